@@ -1,0 +1,348 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test compares the oracle with an independent definition (brute force on
+tiny inputs, a library routine, a closed form, a published table), chosen so
+that a dropped term, a wrong sign or index, or a transposed operand anywhere in
+``oracle/oracle.cpp`` fails at least one of them.  No GPU is used.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16(t):
+    """Round to bf16 (library cast, nearest-even) and back to float64."""
+    return torch.as_tensor(t).to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+
+def read_table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                a, b = line.split()
+                rows.append((a, b))
+    return rows
+
+
+# ------------------------------------------------------------------ codecs
+def test_e2m1_table_matches_ocp():
+    for code, val in read_table("e2m1_values.txt"):
+        got = oracle.e2m1_value(int(code))
+        assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), code
+
+
+def test_e8m0_all_codes():
+    for c in range(255):
+        assert oracle.e8m0_value(c) == 2.0 ** (c - 127)
+    assert math.isnan(oracle.e8m0_value(255))
+
+
+def test_e4m3_decode_matches_torch_float8_e4m3fn():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32)
+    for c in range(256):
+        got = oracle.e4m3_value(c)
+        r = ref[c].item()
+        if math.isnan(r):
+            assert math.isnan(got), c
+        else:
+            assert got == r and math.copysign(1, got) == math.copysign(1, r), c
+
+
+def test_e4m3_encode_matches_torch_cast():
+    rng = np.random.default_rng(3)
+    vals = list(rng.standard_normal(4000) * 60.0) + list(rng.standard_normal(1000) * 0.01)
+    # every exact midpoint between consecutive finite codes (ties go to the even code)
+    pos = [oracle.e4m3_value(c) for c in range(0x7F)]
+    vals += [(a + b) / 2 for a, b in zip(pos[:-1], pos[1:])]
+    vals += [-v for v in vals[-126:]] + [0.0, -0.0, 448.0, 449.0, 463.9, 470.0, 1e6, -1e6, 2.0 ** -10]
+    t = torch.tensor(vals, dtype=torch.float32)
+    ref = t.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    for v, r in zip(t.tolist(), ref.tolist()):
+        got = oracle.e4m3_encode(v)
+        if r & 0x7F == 0:  # zero: sign of zero is immaterial for the product
+            assert got & 0x7F == 0, v
+        else:
+            assert got == r, (v, got, r)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(5)
+    vals = rng.standard_normal(3000).astype(np.float32)
+    bits = rng.integers(0, 2**32, 2000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    bits = bits[np.isfinite(bits)]
+    # exact ties: low 16 bits == 0x8000
+    ties = (rng.integers(0, 2**16, 500, dtype=np.uint32) << 16 | 0x8000).astype(np.uint32).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    allv = np.concatenate([vals, bits, ties])
+    ref = torch.from_numpy(allv).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    for v, r in zip(allv.tolist(), ref.tolist()):
+        assert oracle.to_bf16_bits(v) == r, v
+    assert oracle.to_bf16_bits(float("nan")) & 0x7FC0 == 0x7FC0
+
+
+def ref_mxfp8(v):
+    """OCP MX v1.0 MXFP8 conversion via torch: X = 2^(floor(log2 amax) - 8),
+    elements = float8_e4m3fn(clamp(v / X))."""
+    v = torch.as_tensor(v, dtype=torch.float32).view(-1, 32)
+    amax = v.abs().amax(dim=1)
+    _, e = torch.frexp(amax)
+    sexp = torch.where(amax > 0, (e - 1 - 8).clamp(-127, 127), torch.full_like(e, -127))
+    scaled = torch.ldexp(v, -sexp[:, None].to(torch.float32))
+    q = scaled.clamp(-448, 448).to(torch.float8_e4m3fn)
+    deq = q.to(torch.float32) * torch.pow(2.0, sexp.to(torch.float32))[:, None]
+    return deq.view(-1), q.view(torch.uint8).view(-1), (sexp + 127).to(torch.uint8)
+
+
+def test_mxfp8_block_quantisation_matches_reference():
+    g = torch.Generator().manual_seed(11)
+    v = torch.randn(64 * 32, generator=g) * torch.logspace(-3, 3, 64).repeat_interleave(32)
+    v[:32] = 0.0                                  # all-zero block
+    v[32:64] = 0.25                               # amax exactly a power of two
+    v[64:96] = torch.randn(32, generator=g) * 1e-30  # tiny block
+    deq, codes, scales = oracle.mxfp8(v)
+    rdeq, rcodes, rscales = ref_mxfp8(v)
+    assert torch.equal(scales, rscales)
+    nz = rcodes & 0x7F != 0
+    assert torch.equal(codes[nz], rcodes[nz])
+    assert torch.all(codes[~nz] & 0x7F == 0)
+    assert torch.equal(deq, rdeq)
+
+
+# ------------------------------------------------------------------ router
+def brute_topk(logits, k):
+    """Rank by (value desc, index asc) with NaN last, via Python's sort."""
+    out = []
+    for row in logits.tolist():
+        key = lambda e: (1, 0.0, e) if math.isnan(row[e]) else (0, -row[e], e)
+        out.append(sorted(range(len(row)), key=key)[:k])
+    return torch.tensor(out, dtype=torch.int32)
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 16, 4), (9, 896, 16), (33, 56, 1), (5, 7, 7)])
+def test_route_ids_brute_force(T, E, k):
+    logits = W.separated_logits(0, f"r{T}", T, E, k)
+    ids, w = oracle.route(logits, k)
+    assert torch.equal(ids, brute_topk(logits, k))
+    # weights: library softmax over the selected logits, float64
+    sel = torch.gather(logits.double(), 1, ids.long())
+    ref = torch.softmax(sel, dim=1)
+    assert torch.allclose(w.double(), ref, atol=2e-6, rtol=0)
+    assert torch.allclose(w.double().sum(1), torch.ones(T, dtype=torch.float64), atol=1e-5)
+
+
+def test_route_ties_nan_and_signed_zero():
+    # quantised logits: many exact ties; the lower index must win
+    g = torch.Generator().manual_seed(2)
+    logits = (torch.randn(40, 24, generator=g) * 4).round() / 4
+    logits[0, :] = 1.0                      # all equal -> first k indices, weights 1/k
+    logits[1, :] = float("nan")             # all NaN -> first k indices
+    logits[2, :5] = float("nan")            # NaNs rank below every number
+    logits[3, :] = -1.0
+    logits[3, 7] = -0.0
+    logits[3, 3] = 0.0                      # +0 == -0: index 3 before 7
+    ids, w = oracle.route(logits, 6)
+    assert torch.equal(ids, brute_topk(logits, 6))
+    assert torch.equal(ids[0], torch.arange(6, dtype=torch.int32))
+    assert torch.allclose(w[0], torch.full((6,), 1 / 6))
+    assert ids[3, 0] == 3 and ids[3, 1] == 7
+    assert not any(int(e) < 5 for e in ids[2])
+
+
+def test_route_weight_ratio_closed_form():
+    logits = torch.full((1, 10), -50.0)
+    logits[0, 4] = 1.0
+    logits[0, 8] = 1.0 - 0.7
+    ids, w = oracle.route(logits, 2)
+    assert ids.tolist() == [[4, 8]]
+    assert abs(w[0, 0].item() / w[0, 1].item() - math.exp(0.7)) < 1e-5
+
+
+# ----------------------------------------------------------------- permute
+@pytest.mark.parametrize("R,E", [(256, 16), (4096, 896), (1000, 56), (7, 3), (0, 5)])
+def test_permute_invariants_and_stable_sort(R, E):
+    g = torch.Generator().manual_seed(R + E)
+    ids = torch.randint(0, E, (R,), generator=g, dtype=torch.int32)
+    if R > 10:
+        ids[: R // 3] = E - 1                   # one heavy expert, others possibly empty
+    offsets, sorted_row, row_pos = oracle.permute(ids, E)
+    counts = torch.bincount(ids.long(), minlength=E)
+    assert offsets[0] == 0 and torch.equal(offsets[1:].long() - offsets[:-1].long(), counts)
+    # library stable sort defines the unique stable permutation
+    ref = torch.from_numpy(np.argsort(ids.numpy(), kind="stable").astype(np.int32))
+    assert torch.equal(sorted_row, ref)
+    assert torch.equal(row_pos[sorted_row.long()], torch.arange(R, dtype=torch.int32))
+
+
+# ------------------------------------------------------------ whole layer
+def dense_reference(inp, k, act_quant=False, norm=True):
+    """Brute force: evaluate EVERY expert on EVERY token in float64 (bf16 at the
+    storage points), mask with the token's top-k, weight and sum."""
+    cfg = inp["cfg"]
+    f = lambda n: inp[n].to(torch.float64)
+    if cfg.mxfp4:
+        table = torch.tensor([float(v) for _, v in read_table("e2m1_values.txt")], dtype=torch.float64)
+
+        def deq(codes, scales, N, K):
+            c = codes.view(cfg.E, N, K // 2).long()
+            lo, hi = c & 15, c >> 4
+            el = torch.stack([table[lo], table[hi]], dim=-1).view(cfg.E, N, K)
+            sc = torch.pow(2.0, scales.view(cfg.E, N, K // 32).double() - 127)
+            return el * sc.repeat_interleave(32, dim=2)
+
+        W1, W3 = deq(inp["w1q"], inp["s1"], cfg.I, cfg.l), deq(inp["w3q"], inp["s3"], cfg.I, cfg.l)
+        W2 = deq(inp["w2q"], inp["s2"], cfg.l, cfg.I)
+    else:
+        W1, W3, W2 = f("w1"), f("w3"), f("w2")
+    aq = (lambda v: ref_mxfp8(v.float())[0].double().view(v.shape)) if act_quant else (lambda v: v)
+    x = f("x")
+    if cfg.rows_mode:
+        z = x
+        gates = torch.zeros(cfg.T, cfg.E, dtype=torch.float64)
+        gates[torch.arange(cfg.T), inp["ids"].view(-1).long()] = inp["weights"].view(-1).double()
+    else:
+        z = bf16(x @ f("w_in").T)
+        logits = inp["logits"]
+        sel = brute_topk(logits, k).long()
+        wsel = torch.softmax(torch.gather(logits.double(), 1, sel), dim=1)
+        gates = torch.zeros(cfg.T, cfg.E, dtype=torch.float64)
+        gates.scatter_(1, sel, wsel)
+    za = aq(z)
+    c = torch.zeros(cfg.T, cfg.l, dtype=torch.float64)
+    for e in range(cfg.E):
+        H = bf16(F.silu(za @ W1[e].T) * (za @ W3[e].T))
+        Y = bf16(aq(H) @ W2[e].T)
+        c += gates[:, e:e + 1] * Y
+    if cfg.rows_mode:
+        return bf16(c)
+    if norm and "norm_w" in inp:
+        rh = bf16(c / torch.sqrt((c * c).mean(dim=1, keepdim=True) + cfg.eps) * f("norm_w"))
+    else:
+        rh = bf16(c)
+    y = rh @ f("w_out").T
+    for s in range(cfg.S):
+        hs = bf16(F.silu(x @ f("ws1")[s].T) * (x @ f("ws3")[s].T))
+        y = y + hs @ f("ws2")[s].T
+    return bf16(y)
+
+
+def assert_close(got, ref, max_rel=2e-2, mae=1e-3):
+    got, ref = got.double(), ref.double()
+    floor = 0.1 * ref.pow(2).mean().sqrt()
+    rel = (got - ref).abs() / torch.maximum(ref.abs(), floor)
+    assert rel.max().item() <= max_rel, rel.max().item()
+    assert (got - ref).abs().mean().item() <= mae, (got - ref).abs().mean().item()
+
+
+SMALL = [
+    dict(T=13, d=96, l=64, E=6, k=3, S=2, I=32, Is=48),
+    dict(T=20, d=64, l=96, E=5, k=2, S=1, I=64, Is=32),
+    dict(T=9, d=128, l=64, E=4, k=4, S=0, I=96, Is=0),      # k = E: dense softmax mixture
+]
+
+
+@pytest.mark.parametrize("dims", SMALL)
+@pytest.mark.parametrize("norm", ["ones", "random", "none"])
+def test_layer_matches_dense_brute_force(dims, norm):
+    cfg = W.custom(**dims)
+    inp = W.make_inputs(cfg, norm_w=norm)
+    out = oracle.run(inp)
+    ref = dense_reference(inp, cfg.k)
+    assert_close(out["y"], ref, max_rel=1e-2, mae=2e-4)
+
+
+def test_layer_intermediates_layout():
+    cfg = W.custom(T=11, d=64, l=64, E=5, k=2, S=1, I=32, Is=32)
+    inp = W.make_inputs(cfg)
+    out = oracle.run(inp, intermediates=True)
+    x = inp["x"].double()
+    assert torch.equal(out["z"].double(), bf16(x @ inp["w_in"].double().T))
+    # H/Y are in sorted order: position p holds row sorted_row[p] = t*k + j
+    for p in range(cfg.T * cfg.k):
+        r = int(out["sorted_row"][p])
+        t, e = r // cfg.k, int(out["ids"].view(-1)[r])
+        zt = out["z"][t].double()
+        h = bf16(F.silu(zt @ inp["w1"][e].double().T) * (zt @ inp["w3"][e].double().T))
+        assert (out["H"][p].double() - h).abs().max() <= 1e-2 * h.abs().max()
+    # sampled-token evaluation equals the full evaluation
+    sub = oracle.run(inp, eval_tokens=[3, 0, 10])
+    assert torch.equal(sub["y"], out["y"][[3, 0, 10]])
+
+
+def test_textbook_swiglu_special_case():
+    # E = k = 1, S = 0, d = l, W_in = W_out = identity, no norm: y = SwiGLU(x)
+    cfg = W.custom(T=16, d=64, l=64, E=1, k=1, S=0, I=96, Is=0, norm=False)
+    inp = W.make_inputs(cfg)
+    eye = torch.eye(64, dtype=torch.bfloat16)
+    inp["w_in"], inp["w_out"] = eye, eye
+    out = oracle.run(inp)
+    x = inp["x"].double()
+    H = bf16(F.silu(x @ inp["w1"][0].double().T) * (x @ inp["w3"][0].double().T))
+    ref = bf16(H @ inp["w2"][0].double().T)
+    assert_close(out["y"], ref, max_rel=1e-2, mae=1e-4)
+
+
+def test_zero_expert_down_proj_leaves_shared_only():
+    cfg = W.custom(T=10, d=96, l=64, E=6, k=3, S=2, I=32, Is=48)
+    inp = W.make_inputs(cfg)
+    inp["w2"] = torch.zeros_like(inp["w2"])
+    out = oracle.run(inp)
+    x = inp["x"].double()
+    y = torch.zeros(cfg.T, cfg.d, dtype=torch.float64)
+    for s in range(cfg.S):
+        hs = bf16(F.silu(x @ inp["ws1"][s].double().T) * (x @ inp["ws3"][s].double().T))
+        y += hs @ inp["ws2"][s].double().T
+    assert_close(out["y"], bf16(y), max_rel=1e-2, mae=1e-4)
+
+
+def test_identical_experts_make_routing_irrelevant():
+    cfg = W.custom(T=12, d=64, l=64, E=5, k=2, S=1, I=32, Is=32)
+    inp = W.make_inputs(cfg)
+    for n in ("w1", "w3", "w2"):
+        inp[n] = inp[n][:1].expand_as(inp[n]).contiguous()
+    a = oracle.run(inp)["y"]
+    inp["logits"] = W.separated_logits(7, "other", cfg.T, cfg.E, cfg.k)
+    b = oracle.run(inp)["y"]
+    assert_close(a, b, max_rel=1e-2, mae=1e-4)
+
+
+def test_rows_mode_matches_dense_brute_force():
+    cfg = W.custom(T=300, d=0, l=64, E=7, k=1, S=0, I=32, Is=0, rows_mode=True, norm=False, zipf_s=1.1)
+    inp = W.make_inputs(cfg)
+    out = oracle.run(inp)
+    assert_close(out["y"], dense_reference(inp, 1), max_rel=1e-2, mae=1e-4)
+
+
+@pytest.mark.parametrize("act_quant", [True, False])
+def test_mxfp4_layer_matches_dense_brute_force(act_quant):
+    cfg = W.custom(T=10, d=96, l=64, E=5, k=2, S=1, I=64, Is=32, mxfp4=True)
+    inp = W.make_inputs(cfg)
+    out = oracle.run(inp, act_quant=act_quant)
+    ref = dense_reference(inp, cfg.k, act_quant=act_quant)
+    # a flipped bf16 rounding of an input to the MXFP8 quantiser can move one
+    # element by one e4m3 step (1/8 relative), hence the looser bound here
+    assert_close(out["y"], ref, max_rel=5e-2, mae=2e-3)
+
+
+def test_page_moe_shape():
+    facts = dict((a, int(b)) for a, b in read_table("moe_shape.txt"))
+    cfg = W.CONFIGS["prefill"]
+    assert (cfg.E, cfg.k, cfg.S) == (facts["routed_experts"], facts["top_k"], facts["shared_experts"])
+    dec = W.CONFIGS["decode"]
+    assert (dec.d, dec.l) == (facts["latent_example_in"], facts["latent_example_out"])
+    logits = W.separated_logits(0, "shape", 4, facts["routed_experts"], facts["top_k"])
+    ids, w = oracle.route(logits, facts["top_k"])
+    for row in ids.tolist():
+        assert len(set(row)) == facts["top_k"]
+        assert all(0 <= e < facts["routed_experts"] for e in row)

@@ -1,0 +1,191 @@
+"""Seeded synthetic inputs for the LatentMoE layer.
+
+This module only draws random numbers and lays them out; it holds none of the
+layer's arithmetic.  Both the CPU oracle (``oracle/``) and the HIP path consume
+what it returns, so it is the single source of inputs for parity tests and the
+bench.
+
+Shapes follow the LatentMoE feed-forward of Kimi K3 as described by the
+TokenSpeed AgentX post ("Model architecture": 16 of 896 routed experts plus two
+shared experts) and the vLLM Kimi K3 post (section 1, "LatentMoE: Dimensionality
+Reduction at the Routing Inlet, Restoration at the Outlet": 512 -> 256 latent
+example).
+
+Every tensor gets its own torch generator seeded from (seed, tensor name), so a
+tensor does not change when another one is added or resized.  ``device`` picks
+the generator: the CPU and GPU generators give different (but each
+deterministic) values; a test always hands the same tensors to both sides.
+
+Weight layout is ``[out, in]`` (reduction dim contiguous):
+  w_in [l,d]; w1, w3 [E,I,l]; w2 [E,l,I]; w_out [d,l];
+  ws1, ws3 [S,Is,d]; ws2 [S,d,Is]; norm_w [l].
+MXFP4 experts: codes packed two per byte (even K index in the low nibble)
+  w1q, w3q [E,I,l/2] u8 with e8m0 scales s1, s3 [E,I,l/32];
+  w2q [E,l,I/2] u8 with s2 [E,l,I/32].
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import Optional
+
+import torch
+
+BF16 = torch.bfloat16
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    T: int            # tokens (rows in rows mode)
+    d: int            # hidden width (0 in rows mode)
+    l: int            # latent width
+    E: int            # routed experts (local experts in rows mode)
+    k: int            # experts per token (1 in rows mode)
+    S: int            # shared experts
+    I: int            # routed SwiGLU intermediate
+    Is: int           # shared SwiGLU intermediate
+    rows_mode: bool = False   # expert-parallel share: ids + weights given, no projections
+    mxfp4: bool = False       # routed expert weights in MXFP4
+    norm: bool = True         # routed-latent RMSNorm with gain 1
+    eps: float = 1e-6
+    zipf_s: float = 0.0       # rows mode: Zipf exponent of the expert load
+    seed: int = 0
+
+
+CONFIGS = {
+    # 64 tokens, d=512 -> latent 256, 16 experts top-4, one shared expert, I=128
+    "tiny": LayerConfig("tiny", T=64, d=512, l=256, E=16, k=4, S=1, I=128, Is=128),
+    # decode batch of 256 tokens, 512 -> 256 latent, 896 experts top-16 + 2 shared, I=256
+    "decode": LayerConfig("decode", T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256),
+    # prefill: 8192 tokens, 7168 -> 2048 latent, 896 experts top-16 + 2 shared, I=512
+    "prefill": LayerConfig("prefill", T=8192, d=7168, l=2048, E=896, k=16, S=2, I=512, Is=512),
+    # one expert-parallel rank's share: 56 local experts, 16384 received rows, Zipf(1.1) load
+    "ep_share": LayerConfig("ep_share", T=16384, d=0, l=2048, E=56, k=1, S=0, I=512, Is=0,
+                            rows_mode=True, norm=False, zipf_s=1.1),
+    # prefill shape at 16384 tokens with MXFP4 routed experts
+    "prefill_mxfp4": LayerConfig("prefill_mxfp4", T=16384, d=7168, l=2048, E=896, k=16, S=2,
+                                 I=512, Is=512, mxfp4=True),
+}
+
+
+def _gen(seed: int, name: str, device) -> torch.Generator:
+    h = hashlib.sha256(f"{seed}:{name}".encode()).digest()
+    g = torch.Generator(device=device)
+    g.manual_seed(int.from_bytes(h[:8], "little") & ((1 << 63) - 1))
+    return g
+
+
+def normal_bf16(seed, name, shape, std, device="cpu", mean=0.0) -> torch.Tensor:
+    """N(mean, std) drawn in fp32, stored as bf16 (round-to-nearest-even cast)."""
+    g = _gen(seed, name, device)
+    t = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    if mean != 0.0:
+        t.add_(mean)
+    return t.to(BF16)
+
+
+def separated_logits(seed, name, T, E, k, device="cpu", min_gap=1e-3) -> torch.Tensor:
+    """fp32 N(0,1) router logits, each token redrawn until the k+1 largest values
+    are pairwise at least ``min_gap`` apart (so top-k is unambiguous)."""
+    g = _gen(seed, name, device)
+    out = torch.randn(T, E, generator=g, device=device, dtype=torch.float32)
+    kk = min(k + 1, E)
+    for _ in range(1000):
+        top = torch.topk(out, kk, dim=1).values
+        bad = (top[:, :-1] - top[:, 1:] < min_gap).any(dim=1) if kk > 1 else \
+            torch.zeros(T, dtype=torch.bool, device=device)
+        nbad = int(bad.sum())
+        if nbad == 0:
+            return out
+        out[bad] = torch.randn(nbad, E, generator=g, device=device, dtype=torch.float32)
+    raise RuntimeError("could not draw separated logits")
+
+
+def zipf_ids(seed, name, R, E, s, device="cpu") -> torch.Tensor:
+    """R i.i.d. expert ids whose load follows Zipf(s) over ranks 1..E; the rank ->
+    expert id map is a seeded permutation."""
+    g = _gen(seed, name, "cpu")
+    ranks = torch.arange(1, E + 1, dtype=torch.float64)
+    p = ranks.pow(-s)
+    p /= p.sum()
+    draws = torch.multinomial(p, R, replacement=True, generator=g)
+    perm = torch.randperm(E, generator=g)
+    return perm[draws].to(torch.int32).to(device)
+
+
+def uniform_weights(seed, name, shape, device="cpu") -> torch.Tensor:
+    """fp32 combine weights drawn from U(0, 1]."""
+    g = _gen(seed, name, device)
+    u = torch.rand(*shape, generator=g, device=device, dtype=torch.float32)
+    return 1.0 - u
+
+
+# Magnitude distribution of the MXFP4 element codes drawn below.  The codes
+# 0..7 are the non-negative e2m1 encodings; the probabilities roughly follow a
+# Gaussian block scaled so its max lands near the top code.  They are input
+# structure only (no encoder is involved).
+_E2M1_CODE_PROBS = [0.08, 0.15, 0.15, 0.14, 0.13, 0.20, 0.10, 0.05]
+
+
+def mxfp4_weights(seed, name, E, N, K, device="cpu"):
+    """Random MXFP4 weight matrix [E,N,K]: packed e2m1 codes [E,N,K/2] (even K in
+    the low nibble) and e8m0 scales [E,N,K/32] around 2^-7 (codes 119..121), so
+    the dequantised values have a spread near N(0, 0.02)."""
+    assert K % 32 == 0
+    g = _gen(seed, name + ".codes", "cpu")
+    mag = torch.multinomial(torch.tensor(_E2M1_CODE_PROBS), E * N * K, replacement=True,
+                            generator=g).to(torch.uint8)
+    sign = torch.randint(0, 2, (E * N * K,), generator=g, dtype=torch.uint8) << 3
+    codes = (mag | sign).view(E, N, K // 2, 2)
+    packed = (codes[..., 0] | (codes[..., 1] << 4)).contiguous()
+    gs = _gen(seed, name + ".scales", "cpu")
+    scales = (119 + torch.multinomial(torch.tensor([0.25, 0.5, 0.25]), E * N * (K // 32),
+                                      replacement=True, generator=gs)).to(torch.uint8)
+    return packed.to(device), scales.view(E, N, K // 32).contiguous().to(device)
+
+
+def make_inputs(cfg: LayerConfig, device="cpu", norm_w: Optional[str] = None) -> dict:
+    """All inputs of one layer call for ``cfg``.
+
+    norm_w: None -> the config's default (ones if cfg.norm else absent),
+            "ones", "random" (N(1, 0.1)) or "none".
+    """
+    s = cfg.seed
+    inp = {"cfg": cfg}
+    if cfg.rows_mode:
+        inp["x"] = normal_bf16(s, "x", (cfg.T, cfg.l), 1.0, device)
+        inp["ids"] = zipf_ids(s, "ids", cfg.T, cfg.E, cfg.zipf_s, device).view(cfg.T, 1)
+        inp["weights"] = uniform_weights(s, "weights", (cfg.T, 1), device)
+    else:
+        inp["x"] = normal_bf16(s, "x", (cfg.T, cfg.d), 1.0, device)
+        inp["logits"] = separated_logits(s, "logits", cfg.T, cfg.E, cfg.k, device)
+        inp["w_in"] = normal_bf16(s, "w_in", (cfg.l, cfg.d), 0.02, device)
+        inp["w_out"] = normal_bf16(s, "w_out", (cfg.d, cfg.l), 0.02, device)
+        if cfg.S > 0:
+            inp["ws1"] = normal_bf16(s, "ws1", (cfg.S, cfg.Is, cfg.d), 0.02, device)
+            inp["ws3"] = normal_bf16(s, "ws3", (cfg.S, cfg.Is, cfg.d), 0.02, device)
+            inp["ws2"] = normal_bf16(s, "ws2", (cfg.S, cfg.d, cfg.Is), 0.02, device)
+    if cfg.mxfp4:
+        inp["w1q"], inp["s1"] = mxfp4_weights(s, "w1", cfg.E, cfg.I, cfg.l, device)
+        inp["w3q"], inp["s3"] = mxfp4_weights(s, "w3", cfg.E, cfg.I, cfg.l, device)
+        inp["w2q"], inp["s2"] = mxfp4_weights(s, "w2", cfg.E, cfg.l, cfg.I, device)
+    else:
+        inp["w1"] = normal_bf16(s, "w1", (cfg.E, cfg.I, cfg.l), 0.02, device)
+        inp["w3"] = normal_bf16(s, "w3", (cfg.E, cfg.I, cfg.l), 0.02, device)
+        inp["w2"] = normal_bf16(s, "w2", (cfg.E, cfg.l, cfg.I), 0.02, device)
+    mode = norm_w or ("ones" if cfg.norm else "none")
+    if mode == "ones":
+        inp["norm_w"] = torch.ones(cfg.l, dtype=BF16, device=device)
+    elif mode == "random":
+        inp["norm_w"] = normal_bf16(s, "norm_w", (cfg.l,), 0.1, device, mean=1.0)
+    elif mode != "none":
+        raise ValueError(mode)
+    return inp
+
+
+def custom(name="custom", **kw) -> LayerConfig:
+    """A LayerConfig with explicit fields (for ragged and edge-case tests)."""
+    return LayerConfig(name=name, **kw)
