@@ -1,0 +1,194 @@
+/*
+ * latent_moe.h — C ABI of the MI355X (gfx950) LatentMoE feed-forward layer.
+ *
+ * The layer (vLLM Kimi K3 post, "Kimi K3 Inference Backend Evolution", section
+ * 1 "LatentMoE: Dimensionality Reduction at the Routing Inlet, Restoration at
+ * the Outlet"; TokenSpeed AgentX post, "Model architecture"):
+ *
+ *   z    = x W_in^T                              latent down-projection [T,l]
+ *   ids, w = top-k of E router logits, softmax over the k                 [T,k]
+ *   H    = silu(z W1_e^T) * (z W3_e^T)           routed SwiGLU expert, in latent
+ *   Y    = H W2_e^T                              per (token, slot) row
+ *   c    = sum_j w[t,j] Y[t,j]                   weighted combine (fp32)
+ *   rhat = c / sqrt(mean(c^2) + eps) * gain      routed-latent RMSNorm (optional;
+ *                                                vLLM post section 6 "Latent MoE
+ *                                                Tail"; TokenSpeed Day-0 post,
+ *                                                "Iris and communication")
+ *   hs   = silu(x Ws1^T) * (x Ws3^T)             S shared experts, hidden width
+ *   y    = rhat W_out^T + hs Ws2^T               latent up-projection + shared
+ *
+ * bf16 storage (round to nearest even) at z, H, Y, rhat, hs and y; every
+ * GEMM accumulates in fp32.  The MXFP4 expert format runs "w4a8" (TokenSpeed
+ * Day-0 post, "TensorRT-LLM Stable LatentMoE"): activations entering each
+ * expert GEMM are quantised to MXFP8 (OCP MX v1.0 e4m3fn + one e8m0 scale per
+ * 32 along K) and multiplied on CDNA4's block-scaled MFMA.
+ *
+ * Conventions shared by every call
+ *  - All tensors are row-major and contiguous; weights are [out, in] (the
+ *    reduction dimension is the contiguous one).  bf16 is passed as its 16-bit
+ *    pattern (void*).  Every device pointer must be 16-byte aligned.
+ *  - Device buffers (inputs, outputs, workspaces) are owned by the caller; the
+ *    library never allocates or frees device memory.  The plan is a small host
+ *    object owned by the library (see latent_moe_free).
+ *  - All work is enqueued on the caller's HIP stream (hipStream_t passed as
+ *    void*; NULL = the default stream).  No call synchronises the stream or
+ *    copies device data to the host; results are valid once the stream reaches
+ *    the enqueued work.
+ *  - Return value: LMOE_OK, or an error code.  On LMOE_EINVAL and
+ *    LMOE_EUNSUPPORTED nothing was enqueued.  LMOE_EHIP reports a HIP launch
+ *    error (some earlier kernels of the call may have been enqueued).  A
+ *    device-side fault surfaces at the caller's next synchronisation.
+ *    latent_moe_last_error() gives a one-line reason for the last failure on
+ *    the calling thread.
+ *  - All element offsets are computed in 64 bits.
+ */
+#ifndef LATENT_MOE_H
+#define LATENT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { LMOE_OK = 0, LMOE_EINVAL = 1, LMOE_EUNSUPPORTED = 2, LMOE_EHIP = 3 };
+enum { LMOE_WFMT_BF16 = 0, LMOE_WFMT_MXFP4 = 1 };
+
+/* Limits of this build. */
+#define LMOE_MAX_EXPERTS_LOGITS 1024 /* E in logits mode (router keeps E/64 logits per lane) */
+#define LMOE_MAX_EXPERTS 4096        /* E in ids mode */
+#define LMOE_MAX_TOPK 64             /* k (one lane per selected expert) */
+#define LMOE_MAX_SHARED 4            /* S */
+
+typedef struct latent_moe_plan latent_moe_plan; /* opaque, host memory */
+
+/*
+ * Routing: router top-k/softmax (TokenSpeed AgentX post, "Model architecture":
+ * each token picks k of E routed experts) and the per-expert permutation a
+ * grouped-GEMM MoE builds (TokenSpeed Day-0 post, "Gluon kernels on AMD GPUs >
+ * Stable LatentMoE": route sorting and gather buffers).
+ *
+ * Logits mode (logits != NULL, ids_in == NULL): for each token t,
+ *   topk_ids[t,0..k-1] = the k experts with the largest logits, listed in the
+ *   order (logit descending, expert index ascending); IEEE comparison, so +0
+ *   and -0 tie and the lower index wins; NaN ranks below every number.
+ *   topk_w[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)   (fp32).
+ * Ids mode (logits == NULL, ids_in != NULL): the caller supplies the expert
+ *   of every row and its combine weight (one expert-parallel rank's received
+ *   rows: k must be 1); topk_ids/topk_w, if not NULL, receive copies.
+ * Both modes then build the stable counting sort of the rows r = t*k + j by
+ * expert:  offsets[e] = number of rows with expert < e (E+1 entries,
+ * offsets[E] = T*k);  sorted_row[p] = r, the p-th row in (expert, r)
+ * ascending order;  row_pos[r] = p, its inverse.
+ *
+ * Arguments (device pointers unless noted):
+ *   T           tokens (rows in ids mode), 0 <= T, T*k < 2^31
+ *   E, k        experts and experts per token: 1 <= k <= min(E, 64);
+ *               E <= 1024 in logits mode, E <= 4096 in ids mode
+ *   logits      fp32 [T,E] or NULL
+ *   ids_in      int32 [T,k], values in [0,E), or NULL
+ *   weights_in  fp32 [T,k] (ids mode only)
+ *   topk_ids    int32 [T,k] out (logits mode: required)
+ *   topk_w      fp32 [T,k] out (logits mode: required)
+ *   sorted_row  int32 [T*k] out
+ *   row_pos     int32 [T*k] out
+ *   offsets     int32 [E+1] out
+ *   workspace   >= latent_moe_route_workspace_size(T,E,k) bytes; holds the
+ *               grouped-GEMM tile tables that latent_moe_forward reads
+ * On success *out_plan receives a new plan that borrows (does not copy) the
+ * output and workspace pointers: they must stay valid and unmodified for
+ * every latent_moe_forward that uses the plan.  T == 0 is valid (nothing is
+ * enqueued; forward then does nothing).
+ */
+typedef struct {
+  int64_t T;
+  int32_t E, k;
+  const float* logits;
+  const int32_t* ids_in;
+  const float* weights_in;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* sorted_row;
+  int32_t* row_pos;
+  int32_t* offsets;
+  void* workspace;
+  size_t workspace_bytes;
+} lmoe_route_args;
+
+int latent_moe_route(const lmoe_route_args* args, void* hip_stream, latent_moe_plan** out_plan);
+
+/*
+ * Forward: down-projection, routed SwiGLU experts on grouped MFMA GEMMs,
+ * gather-weight-accumulate combine with optional RMSNorm, shared experts, and
+ * the up-projection (the formulas at the top of this file), using the routing
+ * in `plan`.
+ *
+ * Dimensions: d (hidden), l (latent), I (routed intermediate), Is (shared
+ * intermediate) are multiples of 64; 0 <= S <= 4 shared experts; wfmt is
+ * LMOE_WFMT_BF16 or LMOE_WFMT_MXFP4.
+ * Arguments (device pointers, bf16 unless noted):
+ *   x        [T,d]          hidden states (rows mode: latent rows [T,l])
+ *   w_in     [l,d]          latent down-projection; NULL selects rows mode
+ *   w1, w3   [E,I,l]        routed gate / up projections
+ *                           (MXFP4: u8 [E,I,l/2], two e2m1 codes per byte, even
+ *                           K index in the low nibble)
+ *   w2       [E,l,I]        routed down projection (MXFP4: u8 [E,l,I/2])
+ *   s1, s3   u8 [E,I,l/32]  e8m0 block scales (MXFP4 only, else NULL)
+ *   s2       u8 [E,l,I/32]
+ *   norm_w   [l]            routed-latent RMSNorm gain, or NULL for no norm
+ *   norm_eps                RMSNorm epsilon
+ *   w_out    [d,l]          latent up-projection; NULL iff w_in is NULL
+ *   ws1, ws3 [S,Is,d]       shared experts' gate / up (NULL iff S == 0)
+ *   ws2      [S,d,Is]       shared experts' down projection
+ *   y        [T,d] out      layer output.  Rows mode (one expert-parallel
+ *                           rank's share; plan from ids mode, k == 1, S == 0):
+ *                           y [T,l] = w[r] * Y[r], rows in received order.
+ *   workspace >= latent_moe_forward_workspace_size(...) bytes (intermediates
+ *             z, hs, H, Y, rhat and the MXFP8 activation copies)
+ * Inputs are read-only; y and the workspace are written.  x, the weights and
+ * y must not overlap the workspace.
+ */
+typedef struct {
+  int32_t d, l, I, S, Is;
+  int32_t wfmt;
+  float norm_eps;
+  const void* x;
+  const void* w_in;
+  const void* w1;
+  const void* w3;
+  const void* w2;
+  const uint8_t* s1;
+  const uint8_t* s3;
+  const uint8_t* s2;
+  const void* norm_w;
+  const void* w_out;
+  const void* ws1;
+  const void* ws3;
+  const void* ws2;
+  void* y;
+  void* workspace;
+  size_t workspace_bytes;
+} lmoe_forward_args;
+
+int latent_moe_forward(const latent_moe_plan* plan, const lmoe_forward_args* args, void* hip_stream);
+
+/* Releases a plan (host memory only; NULL is a no-op).  Device buffers the
+ * plan borrowed remain the caller's. */
+void latent_moe_free(latent_moe_plan* plan);
+
+/* Workspace sizes in bytes (0 on invalid dimensions).  rows_mode != 0 sizes
+ * for an ids-mode plan with no projections. */
+size_t latent_moe_route_workspace_size(int64_t T, int32_t E, int32_t k);
+size_t latent_moe_forward_workspace_size(int64_t T, int32_t E, int32_t k, int32_t d, int32_t l,
+                                         int32_t I, int32_t S, int32_t Is, int32_t wfmt,
+                                         int32_t rows_mode);
+
+/* One-line reason for the last non-OK status returned on this thread. */
+const char* latent_moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATENT_MOE_H */

@@ -1,0 +1,225 @@
+"""Python binding of the LatentMoE HIP library (``liblatent_moe.so``).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch provides device memory (outputs, workspaces) and the stream.
+The C entry points keep their names (``latent_moe_route``,
+``latent_moe_forward``, ``latent_moe_free``); ``route`` and ``forward`` are
+thin tensor-level wrappers around them.
+
+The library must have been built (``python -m latentmoe_expert_layer_amd.build``
+or ``__graft_entry__.build()``); importing this module fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblatent_moe.so")
+
+LMOE_OK, LMOE_EINVAL, LMOE_EUNSUPPORTED, LMOE_EHIP = 0, 1, 2, 3
+LMOE_WFMT_BF16, LMOE_WFMT_MXFP4 = 0, 1
+_ERRNAMES = {1: "LMOE_EINVAL", 2: "LMOE_EUNSUPPORTED", 3: "LMOE_EHIP"}
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class RouteArgs(ctypes.Structure):
+    _fields_ = [("T", _i64), ("E", _i32), ("k", _i32), ("logits", _vp), ("ids_in", _vp),
+                ("weights_in", _vp), ("topk_ids", _vp), ("topk_w", _vp), ("sorted_row", _vp),
+                ("row_pos", _vp), ("offsets", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
+class ForwardArgs(ctypes.Structure):
+    _fields_ = [("d", _i32), ("l", _i32), ("I", _i32), ("S", _i32), ("Is", _i32), ("wfmt", _i32),
+                ("norm_eps", _f32), ("x", _vp), ("w_in", _vp), ("w1", _vp), ("w3", _vp), ("w2", _vp),
+                ("s1", _vp), ("s3", _vp), ("s2", _vp), ("norm_w", _vp), ("w_out", _vp), ("ws1", _vp),
+                ("ws3", _vp), ("ws2", _vp), ("y", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
+class LatentMoeError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{_ERRNAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
+                          "(python -m latentmoe_expert_layer_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.latent_moe_route.argtypes = [ctypes.POINTER(RouteArgs), _vp, ctypes.POINTER(_vp)]
+    L.latent_moe_route.restype = ctypes.c_int
+    L.latent_moe_forward.argtypes = [_vp, ctypes.POINTER(ForwardArgs), _vp]
+    L.latent_moe_forward.restype = ctypes.c_int
+    L.latent_moe_free.argtypes = [_vp]
+    L.latent_moe_free.restype = None
+    L.latent_moe_route_workspace_size.argtypes = [_i64, _i32, _i32]
+    L.latent_moe_route_workspace_size.restype = _sz
+    L.latent_moe_forward_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
+    L.latent_moe_forward_workspace_size.restype = _sz
+    L.latent_moe_last_error.argtypes = []
+    L.latent_moe_last_error.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------- raw C calls
+def latent_moe_route(args: RouteArgs, stream: int = 0):
+    """Calls the C entry point; returns the plan handle (int)."""
+    plan = _vp()
+    rc = lib.latent_moe_route(ctypes.byref(args), _vp(stream), ctypes.byref(plan))
+    _check(rc)
+    return plan.value
+
+
+def latent_moe_forward(plan: int, args: ForwardArgs, stream: int = 0):
+    _check(lib.latent_moe_forward(_vp(plan), ctypes.byref(args), _vp(stream)))
+
+
+def latent_moe_free(plan: Optional[int]):
+    lib.latent_moe_free(_vp(plan))
+
+
+def latent_moe_last_error() -> str:
+    return lib.latent_moe_last_error().decode()
+
+
+def _check(rc):
+    if rc != LMOE_OK:
+        raise LatentMoeError(rc, latent_moe_last_error())
+
+
+def route_workspace_size(T, E, k) -> int:
+    return lib.latent_moe_route_workspace_size(T, E, k)
+
+
+def forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt=LMOE_WFMT_BF16, rows_mode=False) -> int:
+    return lib.latent_moe_forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt, int(rows_mode))
+
+
+# ------------------------------------------------------------ tensor wrappers
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+@dataclass
+class Routing:
+    """Routing outputs (device tensors) and the library plan that borrows them."""
+    T: int
+    E: int
+    k: int
+    topk_ids: Optional[torch.Tensor]
+    topk_w: Optional[torch.Tensor]
+    sorted_row: torch.Tensor
+    row_pos: torch.Tensor
+    offsets: torch.Tensor
+    workspace: torch.Tensor
+    plan: Optional[int]
+    keep: list = field(default_factory=list)
+
+    def free(self):
+        if self.plan is not None:
+            latent_moe_free(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def route(logits: Optional[torch.Tensor] = None, k: int = 1, *, ids: Optional[torch.Tensor] = None,
+          weights: Optional[torch.Tensor] = None, E: Optional[int] = None, stream=None,
+          workspace: Optional[torch.Tensor] = None) -> Routing:
+    """Router top-k/softmax (logits mode) or given ids/weights (ids mode), then
+    the per-expert permutation.  Returns a Routing holding the outputs and plan."""
+    if logits is not None:
+        T, E = logits.shape
+        dev = logits.device
+    else:
+        if ids is None or E is None:
+            raise ValueError("ids mode needs ids and E")
+        T = ids.shape[0]
+        dev = ids.device
+    R = T * k
+    ws_bytes = route_workspace_size(T, E, k)
+    if ws_bytes == 0:
+        raise LatentMoeError(LMOE_EINVAL, f"invalid route dims T={T} E={E} k={k}")
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    topk_ids = torch.empty(T, k, dtype=torch.int32, device=dev) if logits is not None else None
+    topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if logits is not None else None
+    sorted_row = torch.empty(R, dtype=torch.int32, device=dev)
+    row_pos = torch.empty(R, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    a = RouteArgs(T=T, E=E, k=k, logits=_p(logits), ids_in=_p(ids), weights_in=_p(weights),
+                  topk_ids=_p(topk_ids), topk_w=_p(topk_w), sorted_row=_p(sorted_row),
+                  row_pos=_p(row_pos), offsets=_p(offsets), workspace=_p(workspace),
+                  workspace_bytes=workspace.numel())
+    plan = latent_moe_route(a, _stream(stream))
+    keep = [t for t in (logits, ids, weights) if t is not None]
+    return Routing(T, E, k, topk_ids, topk_w, sorted_row, row_pos, offsets, workspace, plan, keep)
+
+
+def forward(routing: Routing, x: torch.Tensor, w1, w3, w2, *, w_in=None, w_out=None, ws1=None, ws3=None,
+            ws2=None, norm_w=None, eps: float = 1e-6, s1=None, s3=None, s2=None, mxfp4: bool = False,
+            y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+            I: Optional[int] = None) -> torch.Tensor:
+    """One LatentMoE forward on the routed rows; returns y (bf16)."""
+    rows = w_in is None
+    T = routing.T
+    if rows:
+        d, l = 0, x.shape[1]
+    else:
+        l, d = w_in.shape
+    if I is None:
+        I = w1.shape[1]
+    S = 0 if ws1 is None else ws1.shape[0]
+    Is = 0 if ws1 is None else ws1.shape[1]
+    wfmt = LMOE_WFMT_MXFP4 if mxfp4 else LMOE_WFMT_BF16
+    ws_bytes = forward_workspace_size(T, routing.E, routing.k, d, l, I, S, Is, wfmt, rows)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty(T, l if rows else d, dtype=torch.bfloat16, device=x.device)
+    a = ForwardArgs(d=d, l=l, I=I, S=S, Is=Is, wfmt=wfmt, norm_eps=eps, x=_p(x), w_in=_p(w_in),
+                    w1=_p(w1), w3=_p(w3), w2=_p(w2), s1=_p(s1), s3=_p(s3), s2=_p(s2), norm_w=_p(norm_w),
+                    w_out=_p(w_out), ws1=_p(ws1), ws3=_p(ws3), ws2=_p(ws2), y=_p(y),
+                    workspace=_p(workspace), workspace_bytes=workspace.numel())
+    latent_moe_forward(routing.plan, a, _stream(stream))
+    return y
+
+
+def run_layer(inp: dict, stream=None, norm=True):
+    """Route + forward for a ``workloads.make_inputs`` dict whose tensors are on the GPU."""
+    cfg = inp["cfg"]
+    if cfg.rows_mode:
+        r = route(ids=inp["ids"], weights=inp["weights"], E=cfg.E, k=1, stream=stream)
+        y = forward(r, inp["x"], inp["w1"], inp["w3"], inp["w2"], stream=stream)
+        return r, y
+    r = route(inp["logits"], cfg.k, stream=stream)
+    mx = cfg.mxfp4
+    y = forward(r, inp["x"], inp.get("w1q" if mx else "w1"), inp.get("w3q" if mx else "w3"),
+                inp.get("w2q" if mx else "w2"), w_in=inp["w_in"], w_out=inp["w_out"], ws1=inp.get("ws1"),
+                ws3=inp.get("ws3"), ws2=inp.get("ws2"), norm_w=inp.get("norm_w") if norm else None,
+                eps=cfg.eps, s1=inp.get("s1"), s3=inp.get("s3"), s2=inp.get("s2"), mxfp4=mx, I=cfg.I,
+                stream=stream)
+    return r, y

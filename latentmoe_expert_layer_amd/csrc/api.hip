@@ -1,0 +1,350 @@
+// C ABI of the LatentMoE layer: argument validation, workspace carve-up and
+// kernel launches.  No device memory is allocated and no host<->device copy or
+// stream synchronisation happens here: every length that only the device knows
+// (per-expert row counts, tile counts) stays on the device (the AgentX
+// InferenceX v3 write-up, SGLang/TRT-LLM engine fixes: per-step device-to-host
+// length syncs create decode bubbles).
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/latent_moe.h"
+#include "kernels.h"
+
+using lmoe::Tile;
+
+struct latent_moe_plan {
+  int64_t T;
+  int32_t E, k;
+  int ids_mode;
+  const int32_t* ids;
+  const float* w;
+  const int32_t* sorted_row;
+  const int32_t* row_pos;
+  const int32_t* offsets;
+  Tile* tiles_s;
+  int32_t* n_s;
+  int64_t max_s;
+  Tile* tiles_t;
+  int32_t* n_t;
+  int64_t max_t;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(LMOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Route workspace: [n_s][n_t] counters, then the two tile tables.
+struct RouteLayout {
+  size_t n_s, n_t, tiles_s, tiles_t, total;
+  int64_t max_s, max_t;
+};
+
+RouteLayout route_layout(int64_t T, int32_t E, int32_t k) {
+  RouteLayout L{};
+  const int64_t R = T * k;
+  L.max_s = lmoe::max_tiles(R, E, lmoe::kSkinnyBM);
+  L.max_t = lmoe::max_tiles(R, E, lmoe::kTiledBM);
+  size_t off = 0;
+  L.n_s = off;
+  off = align_up(off + 4);
+  L.n_t = off;
+  off = align_up(off + 4);
+  L.tiles_s = off;
+  off = align_up(off + size_t(L.max_s) * sizeof(Tile));
+  L.tiles_t = off;
+  off = align_up(off + size_t(L.max_t) * sizeof(Tile));
+  L.total = off;
+  return L;
+}
+
+// Forward workspace: bf16 intermediates z, hs, H, Y, rhat (and MXFP8 copies).
+struct FwdLayout {
+  size_t z, hs, H, Y, rhat, total;
+};
+
+FwdLayout fwd_layout(int64_t T, int32_t k, int32_t l, int32_t I, int32_t S, int32_t Is, bool rows) {
+  FwdLayout L{};
+  const int64_t R = T * k;
+  size_t off = 0;
+  L.z = off;
+  off = align_up(off + (rows ? 0 : size_t(T) * l * 2));
+  L.hs = off;
+  off = align_up(off + size_t(T) * S * Is * 2);
+  L.H = off;
+  off = align_up(off + size_t(R) * I * 2);
+  L.Y = off;
+  off = align_up(off + size_t(R) * l * 2);
+  L.rhat = off;
+  off = align_up(off + (rows ? 0 : size_t(T) * l * 2));
+  L.total = off;
+  return L;
+}
+
+int check_route_dims(int64_t T, int32_t E, int32_t k, bool ids_mode) {
+  if (T < 0) return fail(LMOE_EINVAL, "T=%lld < 0", (long long)T);
+  if (k < 1 || k > LMOE_MAX_TOPK) return fail(LMOE_EINVAL, "k=%d outside [1,%d]", k, LMOE_MAX_TOPK);
+  if (E < k) return fail(LMOE_EINVAL, "E=%d < k=%d", E, k);
+  if (T * int64_t(k) >= (int64_t(1) << 31)) return fail(LMOE_EINVAL, "T*k=%lld >= 2^31", (long long)(T * k));
+  if (!ids_mode && E > LMOE_MAX_EXPERTS_LOGITS)
+    return fail(LMOE_EUNSUPPORTED, "E=%d > %d in logits mode", E, LMOE_MAX_EXPERTS_LOGITS);
+  if (E > LMOE_MAX_EXPERTS || lmoe::permute_waves(E) == 0)
+    return fail(LMOE_EUNSUPPORTED, "E=%d > %d", E, LMOE_MAX_EXPERTS);
+  return LMOE_OK;
+}
+
+int check_fwd_dims(const latent_moe_plan* p, const lmoe_forward_args* a, bool rows) {
+  if (a->l <= 0 || a->l % 64) return fail(LMOE_EINVAL, "l=%d is not a positive multiple of 64", a->l);
+  if (a->I <= 0 || a->I % 64) return fail(LMOE_EINVAL, "I=%d is not a positive multiple of 64", a->I);
+  if (a->l > 4096) return fail(LMOE_EUNSUPPORTED, "l=%d > 4096", a->l);
+  if (a->S < 0 || a->S > LMOE_MAX_SHARED) return fail(LMOE_EINVAL, "S=%d outside [0,%d]", a->S, LMOE_MAX_SHARED);
+  if (a->wfmt != LMOE_WFMT_BF16 && a->wfmt != LMOE_WFMT_MXFP4) return fail(LMOE_EINVAL, "unknown wfmt %d", a->wfmt);
+  if (a->wfmt == LMOE_WFMT_MXFP4) return fail(LMOE_EUNSUPPORTED, "MXFP4 expert weights are not built yet");
+  if (rows) {
+    if (a->w_out) return fail(LMOE_EINVAL, "rows mode (w_in == NULL) needs w_out == NULL");
+    if (p->k != 1) return fail(LMOE_EINVAL, "rows mode needs k == 1 (got %d)", p->k);
+    if (a->S != 0) return fail(LMOE_EINVAL, "rows mode has no shared experts (S=%d)", a->S);
+  } else {
+    if (!a->w_out) return fail(LMOE_EINVAL, "w_out is NULL but w_in is not");
+    if (a->d <= 0 || a->d % 64) return fail(LMOE_EINVAL, "d=%d is not a positive multiple of 64", a->d);
+    if (a->S > 0 && (a->Is <= 0 || a->Is % 64))
+      return fail(LMOE_EINVAL, "Is=%d is not a positive multiple of 64", a->Is);
+  }
+  return LMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* latent_moe_last_error(void) { return g_err.c_str(); }
+
+size_t latent_moe_route_workspace_size(int64_t T, int32_t E, int32_t k) {
+  if (T < 0 || k < 1 || E < k || E > LMOE_MAX_EXPERTS) return 0;
+  return route_layout(T, E, k).total;
+}
+
+size_t latent_moe_forward_workspace_size(int64_t T, int32_t E, int32_t k, int32_t d, int32_t l, int32_t I,
+                                         int32_t S, int32_t Is, int32_t wfmt, int32_t rows_mode) {
+  (void)E;
+  (void)d;
+  if (T < 0 || k < 1 || l <= 0 || I <= 0 || S < 0 || (S > 0 && Is <= 0)) return 0;
+  if (wfmt != LMOE_WFMT_BF16 && wfmt != LMOE_WFMT_MXFP4) return 0;
+  return fwd_layout(T, k, l, I, S, rows_mode ? 0 : Is, rows_mode != 0).total;
+}
+
+int latent_moe_route(const lmoe_route_args* a, void* hip_stream, latent_moe_plan** out_plan) {
+  if (!a || !out_plan) return fail(LMOE_EINVAL, "NULL args or out_plan");
+  *out_plan = nullptr;
+  const bool ids_mode = a->ids_in != nullptr;
+  if ((a->logits != nullptr) == ids_mode) return fail(LMOE_EINVAL, "give exactly one of logits and ids_in");
+  int rc = check_route_dims(a->T, a->E, a->k, ids_mode);
+  if (rc) return rc;
+  if (ids_mode) {
+    if (!a->weights_in) return fail(LMOE_EINVAL, "ids mode needs weights_in");
+    if (a->k != 1) return fail(LMOE_EINVAL, "ids mode needs k == 1 (got %d)", a->k);
+  } else if (!a->topk_ids || !a->topk_w) {
+    return fail(LMOE_EINVAL, "logits mode needs topk_ids and topk_w");
+  }
+  if (!a->sorted_row || !a->row_pos || !a->offsets) return fail(LMOE_EINVAL, "NULL permutation output");
+  const void* ptrs[] = {a->logits, a->ids_in, a->weights_in, a->topk_ids, a->topk_w,
+                        a->sorted_row, a->row_pos, a->offsets, a->workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(LMOE_EINVAL, "device pointer %p is not 16-byte aligned", q);
+  const RouteLayout L = route_layout(a->T, a->E, a->k);
+  if (!a->workspace || a->workspace_bytes < L.total)
+    return fail(LMOE_EINVAL, "route workspace too small: %zu < %zu", a->workspace_bytes, L.total);
+
+  latent_moe_plan* p = new (std::nothrow) latent_moe_plan();
+  if (!p) return fail(LMOE_EINVAL, "out of host memory");
+  char* ws = static_cast<char*>(a->workspace);
+  p->T = a->T;
+  p->E = a->E;
+  p->k = a->k;
+  p->ids_mode = ids_mode;
+  p->ids = ids_mode ? a->ids_in : a->topk_ids;
+  p->w = ids_mode ? a->weights_in : a->topk_w;
+  p->sorted_row = a->sorted_row;
+  p->row_pos = a->row_pos;
+  p->offsets = a->offsets;
+  p->n_s = reinterpret_cast<int32_t*>(ws + L.n_s);
+  p->n_t = reinterpret_cast<int32_t*>(ws + L.n_t);
+  p->tiles_s = reinterpret_cast<Tile*>(ws + L.tiles_s);
+  p->tiles_t = reinterpret_cast<Tile*>(ws + L.tiles_t);
+  p->max_s = L.max_s;
+  p->max_t = L.max_t;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int64_t R = a->T * a->k;
+  if (R > 0) {
+    hipError_t e;
+    if (ids_mode) {
+      if (a->topk_ids || a->topk_w) {
+        e = lmoe::launch_copy_ids(a->ids_in, a->weights_in, R, a->topk_ids, a->topk_w, s);
+        if (e != hipSuccess) {
+          delete p;
+          return hip_fail(e, "copy_ids");
+        }
+      }
+    } else {
+      e = lmoe::launch_router(a->logits, a->T, a->E, a->k, a->topk_ids, a->topk_w, s);
+      if (e != hipSuccess) {
+        delete p;
+        return hip_fail(e, "router");
+      }
+    }
+    e = lmoe::launch_permute(p->ids, R, a->E, a->offsets, a->sorted_row, a->row_pos, p->tiles_s, p->n_s,
+                             p->tiles_t, p->n_t, s);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "permute");
+    }
+  }
+  *out_plan = p;
+  return LMOE_OK;
+}
+
+int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, void* hip_stream) {
+  if (!p || !a) return fail(LMOE_EINVAL, "NULL plan or args");
+  const bool rows = a->w_in == nullptr;
+  if (rows && !p->ids_mode) return fail(LMOE_EINVAL, "rows mode (w_in == NULL) needs an ids-mode plan");
+  int rc = check_fwd_dims(p, a, rows);
+  if (rc) return rc;
+  if (!a->x || !a->w1 || !a->w3 || !a->w2 || !a->y) return fail(LMOE_EINVAL, "NULL x, expert weight or y");
+  if (a->S > 0 && (!a->ws1 || !a->ws3 || !a->ws2)) return fail(LMOE_EINVAL, "S > 0 needs ws1, ws3 and ws2");
+  const void* ptrs[] = {a->x, a->w_in, a->w1, a->w3, a->w2, a->s1, a->s3, a->s2, a->norm_w,
+                        a->w_out, a->ws1, a->ws3, a->ws2, a->y, a->workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(LMOE_EINVAL, "device pointer %p is not 16-byte aligned", q);
+  const int64_t T = p->T, R = p->T * p->k;
+  const int32_t S = rows ? 0 : a->S;
+  const FwdLayout L = fwd_layout(T, p->k, a->l, a->I, S, S ? a->Is : 0, rows);
+  if (!a->workspace || a->workspace_bytes < L.total)
+    return fail(LMOE_EINVAL, "forward workspace too small: %zu < %zu", a->workspace_bytes, L.total);
+  if (T == 0) return LMOE_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(a->workspace);
+  uint16_t* z = reinterpret_cast<uint16_t*>(ws + L.z);
+  uint16_t* hs = reinterpret_cast<uint16_t*>(ws + L.hs);
+  uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.H);
+  uint16_t* Y = reinterpret_cast<uint16_t*>(ws + L.Y);
+  uint16_t* rhat = reinterpret_cast<uint16_t*>(ws + L.rhat);
+  const uint16_t* x = static_cast<const uint16_t*>(a->x);
+  const int64_t d = a->d, l = a->l, I = a->I, Is = a->Is;
+  hipError_t e;
+
+  // 1. latent down-projection, and the shared experts' gate/up on x
+  if (!rows) {
+    lmoe::DenseGemm g{};
+    g.M = int(T);
+    g.N = int(l);
+    g.nseg = 1;
+    g.seg[0] = lmoe::GemmSeg{x, d, static_cast<const uint16_t*>(a->w_in), nullptr, d, int(d)};
+    g.gated = false;
+    g.C = z;
+    g.ldc = l;
+    if ((e = lmoe::launch_dense_gemm(g, s)) != hipSuccess) return hip_fail(e, "down-proj");
+    if (S > 0) {
+      lmoe::DenseGemm h{};
+      h.M = int(T);
+      h.N = int(S * Is);
+      h.nseg = 1;
+      h.seg[0] = lmoe::GemmSeg{x, d, static_cast<const uint16_t*>(a->ws1), static_cast<const uint16_t*>(a->ws3),
+                               d, int(d)};
+      h.gated = true;
+      h.C = hs;
+      h.ldc = S * Is;
+      if ((e = lmoe::launch_dense_gemm(h, s)) != hipSuccess) return hip_fail(e, "shared gate/up");
+    }
+  }
+
+  // 2-3. routed experts: grouped FC1 (gated) and FC2 over the permuted rows
+  const bool skinny = R <= int64_t(32) * p->E;
+  lmoe::GroupedGemm f1{};
+  f1.N = int(I);
+  f1.K = int(l);
+  f1.A = rows ? x : z;
+  f1.lda = l;
+  f1.a_rows = p->sorted_row;
+  f1.a_row_div = p->k;
+  f1.B = static_cast<const uint16_t*>(a->w1);
+  f1.B3 = static_cast<const uint16_t*>(a->w3);
+  f1.ldb = l;
+  f1.b_estride = I * l;
+  f1.gated = true;
+  f1.C = H;
+  f1.ldc = I;
+  f1.tiles = skinny ? p->tiles_s : p->tiles_t;
+  f1.ntiles = skinny ? p->n_s : p->n_t;
+  f1.max_tiles = skinny ? p->max_s : p->max_t;
+  e = skinny ? lmoe::launch_grouped_skinny(f1, s) : lmoe::launch_grouped_tiled(f1, s);
+  if (e != hipSuccess) return hip_fail(e, "expert FC1");
+
+  lmoe::GroupedGemm f2 = f1;
+  f2.N = int(l);
+  f2.K = int(I);
+  f2.A = H;
+  f2.lda = I;
+  f2.a_rows = nullptr;
+  f2.a_row_div = 1;
+  f2.B = static_cast<const uint16_t*>(a->w2);
+  f2.B3 = nullptr;
+  f2.ldb = I;
+  f2.b_estride = l * I;
+  f2.gated = false;
+  f2.C = Y;
+  f2.ldc = l;
+  e = skinny ? lmoe::launch_grouped_skinny(f2, s) : lmoe::launch_grouped_tiled(f2, s);
+  if (e != hipSuccess) return hip_fail(e, "expert FC2");
+
+  // 4. weighted combine (+ RMSNorm); rows mode writes the weighted rows out
+  if (rows) {
+    e = lmoe::launch_combine(Y, p->row_pos, p->w, R, 1, int(l), nullptr, 0.0f, static_cast<uint16_t*>(a->y), s);
+    if (e != hipSuccess) return hip_fail(e, "combine");
+    return LMOE_OK;
+  }
+  e = lmoe::launch_combine(Y, p->row_pos, p->w, T, p->k, int(l), static_cast<const uint16_t*>(a->norm_w),
+                           a->norm_eps, rhat, s);
+  if (e != hipSuccess) return hip_fail(e, "combine");
+
+  // 5. latent up-projection, K-concatenated with the shared experts' down-proj
+  lmoe::DenseGemm u{};
+  u.M = int(T);
+  u.N = int(d);
+  u.nseg = 1 + S;
+  u.seg[0] = lmoe::GemmSeg{rhat, l, static_cast<const uint16_t*>(a->w_out), nullptr, l, int(l)};
+  for (int i = 0; i < S; ++i)
+    u.seg[1 + i] = lmoe::GemmSeg{hs + i * Is, S * Is, static_cast<const uint16_t*>(a->ws2) + i * d * Is, nullptr,
+                                 Is, int(Is)};
+  u.gated = false;
+  u.C = static_cast<uint16_t*>(a->y);
+  u.ldc = d;
+  if ((e = lmoe::launch_dense_gemm(u, s)) != hipSuccess) return hip_fail(e, "up-proj");
+  return LMOE_OK;
+}
+
+void latent_moe_free(latent_moe_plan* p) { delete p; }
+
+}  // extern "C"

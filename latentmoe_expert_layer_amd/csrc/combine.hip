@@ -1,0 +1,122 @@
+// Gather-weight-accumulate combine of the routed expert outputs, fused with
+// the routed-latent RMSNorm.
+//
+// The combine merges a token's expert contributions while still in the
+// latent (vLLM Kimi K3 post, section 1, LatentMoE dataflow: the all-to-all
+// combine aggregates the low-dimensional tensors); the RMSNorm of the reduced
+// routed latent precedes the up-projection (vLLM post, section 6 "Latent MoE
+// Tail"; TokenSpeed Day-0 post, "Iris and communication", which also keeps a
+// whole routed row in one workgroup so the norm's sum stays local — here one
+// wave owns one row).
+//
+//   c[t]   = sum_{j<k} w[t,j] * Y[row_pos[t*k+j]]     fp32, j ascending
+//   out[t] = bf16(c * (1/sqrt(mean(c^2) + eps)) * gain)  or bf16(c) without gain
+#include "common.h"
+#include "kernels.h"
+
+namespace lmoe {
+
+namespace {
+
+template <int VEC>
+struct VecT;
+template <>
+struct VecT<8> { typedef uint4 type; };
+template <>
+struct VecT<4> { typedef uint2 type; };
+template <>
+struct VecT<2> { typedef uint32_t type; };
+template <>
+struct VecT<1> { typedef uint16_t type; };
+
+template <int VEC>
+__device__ __forceinline__ void unpack(const typename VecT<VEC>::type& v, float* f) {
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) f[i] = bf16_to_f32(h[i]);
+}
+
+constexpr int kRowsInFlight = 8;
+
+// One wave per token row; lane owns VEC contiguous elements of every
+// 64*VEC-wide chunk.  The fp32 row is parked in LDS between the two passes
+// (weighted sum + sum of squares, then scale and store).
+template <int VEC>
+__global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__ Y, const int32_t* __restrict__ row_pos,
+                                                      const float* __restrict__ w, int64_t T, int k, int l,
+                                                      const bf16_t* __restrict__ gain, float eps,
+                                                      bf16_t* __restrict__ out) {
+  typedef typename VecT<VEC>::type V;
+  extern __shared__ float crow[];  // [4][l]
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t t = int64_t(blockIdx.x) * 4 + wid;
+  if (t >= T) return;
+  float* c = crow + wid * l;
+  float ss = 0.0f;
+  for (int base = 0; base < l; base += 64 * VEC) {
+    const int col = base + lane * VEC;
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += kRowsInFlight) {
+      V v[kRowsInFlight];
+      float wj[kRowsInFlight];
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        if (j0 + u < k) {
+          const int64_t r = t * k + j0 + u;
+          const int64_t p = row_pos[r];
+          wj[u] = w[r];
+          v[u] = *reinterpret_cast<const V*>(Y + p * l + col);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        if (j0 + u < k) {
+          float f[VEC];
+          unpack<VEC>(v[u], f);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[i] += wj[u] * f[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      c[col + i] = acc[i];
+      ss += acc[i] * acc[i];
+    }
+  }
+  float scale = 1.0f;
+  if (gain) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    scale = 1.0f / sqrtf(ss / float(l) + eps);
+  }
+  for (int base = 0; base < l; base += 64 * VEC) {
+    const int col = base + lane * VEC;
+    uint16_t o[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      float v = c[col + i];
+      if (gain) v = v * scale * bf16_to_f32(gain[col + i]);
+      o[i] = f32_to_bf16(v);
+    }
+    *reinterpret_cast<V*>(out + t * l + col) = *reinterpret_cast<const V*>(o);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t* Y, const int32_t* row_pos, const float* w, int64_t T, int k, int l,
+                          const uint16_t* gain, float eps, uint16_t* out, hipStream_t s) {
+  const dim3 grid{uint32_t((T + 3) / 4)}, block{256};
+  const size_t lds = size_t(4) * l * sizeof(float);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  if (l % 512 == 0) combine_kernel<8><<<grid, block, lds, s>>>(Y, row_pos, w, T, k, l, gain, eps, out);
+  else if (l % 256 == 0) combine_kernel<4><<<grid, block, lds, s>>>(Y, row_pos, w, T, k, l, gain, eps, out);
+  else if (l % 128 == 0) combine_kernel<2><<<grid, block, lds, s>>>(Y, row_pos, w, T, k, l, gain, eps, out);
+  else combine_kernel<1><<<grid, block, lds, s>>>(Y, row_pos, w, T, k, l, gain, eps, out);
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

@@ -1,0 +1,57 @@
+// Device-side helpers shared by the LatentMoE HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// 16x16x32 bf16 MFMA: D(16x16 f32) = A(16x32) * B(32x16) + C.
+// Operand layout (lane l): A row l%16, K elements 8*(l/16) .. +8; B column
+// l%16, the same K elements.  Result: lane l holds column l%16 of rows
+// 4*(l/16) .. +4.
+__device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Workgroup id -> logical tile id such that consecutive logical ids share an
+// XCD (the hardware deals workgroups to the 8 XCDs round robin), which keeps
+// tiles that reuse the same operand rows in one L2.
+__device__ __forceinline__ uint32_t xcd_swizzle(uint32_t b, uint32_t nb) {
+  const uint32_t full = (nb / 8u) * 8u;
+  if (b >= full) return b;
+  return (b % 8u) * (nb / 8u) + b / 8u;
+}
+
+}  // namespace lmoe

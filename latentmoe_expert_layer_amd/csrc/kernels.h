@@ -1,0 +1,87 @@
+// Host-side launchers of the LatentMoE HIP kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+// One grouped-GEMM m-tile: rows [row_start, row_start + nrows) of one expert's
+// segment in the permuted (expert-major) row order.
+struct Tile {
+  int32_t expert;
+  int32_t row_start;
+  int32_t nrows;
+  int32_t pad;
+};
+
+// Row-tile granularities of the tile tables that routing builds.
+constexpr int kSkinnyBM = 16;   // weight-streaming (decode-shaped) kernel
+constexpr int kTiledBM = 128;   // LDS-tiled (prefill-shaped) kernel
+
+inline int64_t max_tiles(int64_t rows, int64_t E, int bm) {
+  return rows / bm + (rows < E ? rows : E) + 1;
+}
+
+// ---- router / permute -------------------------------------------------------
+hipError_t launch_router(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
+                         hipStream_t s);
+hipError_t launch_copy_ids(const int32_t* ids_in, const float* w_in, int64_t n, int32_t* ids,
+                           float* w, hipStream_t s);
+// Stable counting sort of R rows by expert plus the two tile tables.
+hipError_t launch_permute(const int32_t* ids, int64_t R, int E, int32_t* offsets, int32_t* sorted_row,
+                          int32_t* row_pos, Tile* tiles_skinny, int32_t* n_skinny, Tile* tiles_tiled,
+                          int32_t* n_tiled, hipStream_t s);
+int permute_waves(int E);  // 0 if E is too large
+
+// ---- GEMMs --------------------------------------------------------------------
+// C[M,N] (bf16) = sum over segments of A_s[M,K_s] * B_s[N,K_s]^T, fp32 accumulate.
+// gated: C = silu(A B^T) * (A B3^T) with B = gate rows, B3 = up rows.
+struct GemmSeg {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  const uint16_t* B3;
+  int64_t ldb;
+  int K;
+};
+
+struct DenseGemm {
+  int M, N;
+  int nseg;
+  GemmSeg seg[1 + 4];
+  bool gated;
+  uint16_t* C;
+  int64_t ldc;
+};
+hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
+
+// Grouped over experts: for each tile (expert e, rows p in the tile):
+//   C[p, :] = A[row(p)] * B_e^T  (gated: silu(A B_e^T) * (A B3_e^T)),
+//   row(p) = a_rows ? a_rows[p] / a_row_div : p,   B_e = B + e * b_estride.
+struct GroupedGemm {
+  int N, K;
+  const uint16_t* A;
+  int64_t lda;
+  const int32_t* a_rows;
+  int a_row_div;
+  const uint16_t* B;
+  const uint16_t* B3;
+  int64_t ldb;
+  int64_t b_estride;
+  bool gated;
+  uint16_t* C;
+  int64_t ldc;
+  const Tile* tiles;
+  const int32_t* ntiles;
+  int64_t max_tiles;
+};
+hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s);
+
+// ---- combine ----------------------------------------------------------------
+// out[t] = bf16(RMSNorm(sum_j w[t,j] Y[row_pos[t*k+j]]))   (norm skipped if gain == NULL)
+hipError_t launch_combine(const uint16_t* Y, const int32_t* row_pos, const float* w, int64_t T, int k,
+                          int l, const uint16_t* gain, float eps, uint16_t* out, hipStream_t s);
+
+}  // namespace lmoe

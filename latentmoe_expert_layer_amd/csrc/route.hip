@@ -1,0 +1,294 @@
+// Router (top-k + softmax) and the stable per-expert permutation.
+//
+// Router: each token picks k of E routed experts (TokenSpeed AgentX post,
+// "Model architecture": 16 of 896), ranked by (logit descending, expert index
+// ascending); the combine weights are the softmax over the k selected logits.
+// Permutation: the route sorting / gather metadata that a grouped-GEMM MoE
+// builds (TokenSpeed Day-0 post, "Gluon kernels on AMD GPUs > Stable
+// LatentMoE"), here a stable counting sort of rows r = t*k + j by expert.
+#include "common.h"
+#include "kernels.h"
+
+namespace lmoe {
+
+// ----------------------------------------------------------------- router ---
+// A logit and its expert index packed into one 64-bit key whose unsigned
+// order is the ranking order: high word = the float mapped to an order-
+// preserving unsigned (+0 and -0 both map to the same key, every NaN maps to
+// 0, below -inf), low word = ~index so that the lower index wins ties.  An
+// empty slot is key 0, below every real entry (whose low word is > 0).
+__device__ __forceinline__ uint64_t rank_key(float v, uint32_t e) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t key;
+  if ((u & 0x7fffffffu) > 0x7f800000u) {
+    key = 0u;                                  // NaN
+  } else {
+    if (u == 0x80000000u) u = 0u;              // -0 -> +0
+    key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return (uint64_t(key) << 32) | uint64_t(0xffffffffu - e);
+}
+
+__device__ __forceinline__ float key_value(uint64_t k) {
+  uint32_t key = uint32_t(k >> 32);
+  uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;  // key 0 -> NaN
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor(uint32_t(v), off, kWave);
+    uint32_t hi = __shfl_xor(uint32_t(v >> 32), off, kWave);
+    uint64_t o = (uint64_t(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// One wave per token; lane l holds logits e = l + 64*j (coalesced rows).
+// k rounds: a wave-wide max of the lanes' current best keys picks the next
+// expert; only the owning lane rescans its VPL candidates.
+template <int VPL>
+__global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                     int k, int32_t* __restrict__ ids,
+                                                     float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + t * int64_t(E);
+  uint64_t cand[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int e = lane + 64 * j;
+    cand[j] = (e < E) ? rank_key(row[e], uint32_t(e)) : 0ull;
+  }
+  uint64_t best = 0;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) best = cand[j] > best ? cand[j] : best;
+
+  uint64_t mine = 0;  // lane i keeps the i-th selected key
+  for (int i = 0; i < k; ++i) {
+    const uint64_t top = wave_max_u64(best);
+    if (lane == i) mine = top;
+    if (best == top) {
+      best = 0;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        if (cand[j] == top) cand[j] = 0;
+        best = cand[j] > best ? cand[j] : best;
+      }
+    }
+  }
+  const float v = key_value(mine);
+  const float vmax = __shfl(v, 0, kWave);
+  float ex = (lane < k) ? expf(v - vmax) : 0.0f;
+  float sum = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+  if (lane < k) {
+    ids[t * k + lane] = int32_t(0xffffffffu - uint32_t(mine));
+    w[t * k + lane] = ex / sum;
+  }
+}
+
+hipError_t launch_router(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
+                         hipStream_t s) {
+  const dim3 grid{uint32_t((T + 3) / 4)}, block{256};
+  if (E <= 128) router_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 256) router_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 512) router_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  else router_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+__global__ void copy_ids_kernel(const int32_t* __restrict__ ids_in, const float* __restrict__ w_in,
+                                int64_t n, int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) {
+    if (ids) ids[i] = ids_in[i];
+    if (w) w[i] = w_in[i];
+  }
+}
+
+hipError_t launch_copy_ids(const int32_t* ids_in, const float* w_in, int64_t n, int32_t* ids, float* w,
+                           hipStream_t s) {
+  copy_ids_kernel<<<dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s>>>(ids_in, w_in, n, ids, w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- permute ---
+constexpr int kPermThreads = 1024;
+
+// Expert ids outside [0, E) (invalid input) are clamped so that every write
+// stays inside the caller's buffers; valid ids are unchanged.
+__device__ __forceinline__ int32_t clamp_id(int32_t id, int E) { return min(max(id, 0), E - 1); }
+constexpr int kPermLdsBudget = 150 * 1024;
+
+int permute_waves(int E) {
+  // per-wave histograms [waves][E] plus two (E+1) scan arrays in LDS
+  const int64_t fixed = 2 * int64_t(E + 1) * 4 + 64 * 4;
+  for (int w = 16; w >= 1; w >>= 1)
+    if (int64_t(w) * E * 4 + fixed <= kPermLdsBudget) return w;
+  return 0;
+}
+
+// Exclusive scan of a[0..n) in LDS by a 1024-thread block (n <= 16 * 1024);
+// returns the total.  Each thread scans a contiguous run, then the run sums
+// are scanned across lanes and waves.
+__device__ int block_exclusive_scan(int32_t* a, int n, int32_t* wave_sums) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int per = (n + kPermThreads - 1) / kPermThreads;
+  const int b = tid * per, e = min(n, b + per);
+  int32_t run = 0;
+  for (int i = b; i < e; ++i) run += a[i];
+  int32_t incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int32_t o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_sums[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    int32_t v = lane < kPermThreads / 64 ? wave_sums[lane] : 0;
+    int32_t iv = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int32_t o = __shfl_up(iv, off, kWave);
+      if (lane >= off) iv += o;
+    }
+    if (lane < kPermThreads / 64) wave_sums[lane] = iv - v;  // exclusive
+    if (lane == kPermThreads / 64 - 1) wave_sums[kPermThreads / 64] = iv;
+  }
+  __syncthreads();
+  int32_t base = wave_sums[wid] + incl - run;
+  for (int i = b; i < e; ++i) {
+    const int32_t c = a[i];
+    a[i] = base;
+    base += c;
+  }
+  const int32_t total = wave_sums[kPermThreads / 64];
+  __syncthreads();
+  return total;
+}
+
+// Tile table of granularity bm: every expert's segment split into runs of at
+// most bm rows.  cnt/tstart are LDS scratch of E+1 entries.
+__device__ void emit_tiles(const int32_t* off, int E, int bm, int32_t* tstart, int32_t* wave_sums,
+                           Tile* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+  for (int e = threadIdx.x; e < E; e += kPermThreads) tstart[e] = (off[e + 1] - off[e] + bm - 1) / bm;
+  __syncthreads();
+  const int32_t total = block_exclusive_scan(tstart, E, wave_sums);
+  for (int e = threadIdx.x; e < E; e += kPermThreads) {
+    const int32_t cnt = off[e + 1] - off[e];
+    int32_t t = tstart[e];
+    for (int32_t r = 0; r < cnt; r += bm, ++t) {
+      Tile tl;
+      tl.expert = e;
+      tl.row_start = off[e] + r;
+      tl.nrows = min(bm, cnt - r);
+      tl.pad = 0;
+      tiles[t] = tl;
+    }
+  }
+  if (threadIdx.x == 0) *ntiles = total;
+  __syncthreads();
+}
+
+// One 1024-thread workgroup.  Wave w owns the contiguous row chunk
+// [w*C, (w+1)*C).  (1) per-wave LDS histograms; (2) per expert, prefix over
+// waves; (3) exclusive scan over experts -> offsets; (4) each wave walks its
+// chunk 64 rows at a time: lanes with equal expert find each other with
+// ballots over the id bits, take consecutive slots in lane order, and the
+// group's lowest lane advances the running base.  Rows keep their order
+// within an expert (stable), so the result is unique.
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int E, int nwaves, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_row, int32_t* __restrict__ row_pos, Tile* __restrict__ tiles_a,
+    int32_t* __restrict__ n_a, Tile* __restrict__ tiles_b, int32_t* __restrict__ n_b) {
+  extern __shared__ int32_t lds[];
+  int32_t* hist = lds;                          // [nwaves][E]
+  int32_t* off = hist + int64_t(nwaves) * E;    // [E+1]
+  int32_t* tmp = off + (E + 1);                 // [E+1]
+  int32_t* wave_sums = tmp + (E + 1);           // [64]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+
+  for (int i = tid; i < nwaves * E; i += kPermThreads) hist[i] = 0;
+  __syncthreads();
+
+  const int64_t chunk = ((R + nwaves - 1) / nwaves + 63) / 64 * 64;
+  const int64_t r0 = int64_t(wid) * chunk, r1 = min(R, r0 + chunk);
+  if (wid < nwaves) {
+    for (int64_t r = r0 + lane; r < r1; r += 64) atomicAdd(&hist[wid * E + clamp_id(ids[r], E)], 1);
+  }
+  __syncthreads();
+
+  for (int e = tid; e < E; e += kPermThreads) {
+    int32_t run = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      const int32_t c = hist[w * E + e];
+      hist[w * E + e] = run;
+      run += c;
+    }
+    off[e] = run;
+  }
+  __syncthreads();
+  block_exclusive_scan(off, E, wave_sums);
+  for (int e = tid; e < E; e += kPermThreads) offsets[e] = off[e];
+  if (tid == 0) {
+    off[E] = int32_t(R);
+    offsets[E] = int32_t(R);
+  }
+  for (int i = tid; i < nwaves * E; i += kPermThreads) hist[i] += off[i % E];
+  __syncthreads();
+
+  if (wid < nwaves) {
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int64_t base_r = r0; base_r < r1; base_r += 64) {
+      const int64_t r = base_r + lane;
+      const bool valid = r < r1;
+      const int32_t id = valid ? clamp_id(ids[r], E) : 0;
+      uint64_t peers = ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (id >> b) & 1;
+        const uint64_t m = ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      int32_t base = 0;
+      if (valid) base = hist[wid * E + id];
+      const int rank = __popcll(peers & below);
+      if (valid && rank == 0) hist[wid * E + id] = base + __popcll(peers);
+      if (valid) {
+        const int32_t p = base + rank;
+        sorted_row[p] = int32_t(r);
+        row_pos[r] = p;
+      }
+    }
+  }
+  __syncthreads();
+  emit_tiles(off, E, kSkinnyBM, tmp, wave_sums, tiles_a, n_a);
+  emit_tiles(off, E, kTiledBM, tmp, wave_sums, tiles_b, n_b);
+}
+
+hipError_t launch_permute(const int32_t* ids, int64_t R, int E, int32_t* offsets, int32_t* sorted_row,
+                          int32_t* row_pos, Tile* tiles_a, int32_t* n_a, Tile* tiles_b, int32_t* n_b,
+                          hipStream_t s) {
+  const int nw = permute_waves(E);
+  if (nw == 0) return hipErrorInvalidValue;
+  const size_t lds = (size_t(nw) * E + 2 * size_t(E + 1) + 64) * 4;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)permute_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPermLdsBudget + 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  permute_kernel<<<dim3(1), dim3(kPermThreads), lds, s>>>(ids, R, E, nw, offsets, sorted_row, row_pos,
+                                                          tiles_a, n_a, tiles_b, n_b);
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

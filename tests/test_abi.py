@@ -1,0 +1,103 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, sizes workspaces, and rejects invalid arguments before
+any launch (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "latent_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(latent_moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("latent_moe_route", "latent_moe_forward", "latent_moe_free"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import latentmoe_expert_layer_amd as lm
+    lib = ctypes.CDLL(lm.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_oracle_is_not_linked_into_the_product():
+    import latentmoe_expert_layer_amd as lm
+    with open(lm.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"lmoe_oracle" not in blob
+
+
+def test_workspace_sizes():
+    import latentmoe_expert_layer_amd as lm
+    a = lm.route_workspace_size(8192, 896, 16)
+    b = lm.route_workspace_size(256, 896, 16)
+    assert a > b > 0
+    assert lm.route_workspace_size(-1, 896, 16) == 0
+    assert lm.route_workspace_size(10, 4, 8) == 0          # k > E
+    f = lm.forward_workspace_size(8192, 896, 16, 7168, 2048, 512, 2, 512)
+    # z + hs + H + Y + rhat in bf16
+    need = 2 * (8192 * 2048 + 8192 * 1024 + 131072 * 512 + 131072 * 2048 + 8192 * 2048)
+    assert need <= f <= need + 16 * 256
+    r = lm.forward_workspace_size(16384, 56, 1, 0, 2048, 512, 0, 0, rows_mode=True)
+    assert 2 * (16384 * 512 + 16384 * 2048) <= r
+
+
+def _route_args(lm, **kw):
+    base = dict(T=4, E=16, k=4, logits=16, ids_in=None, weights_in=None, topk_ids=32, topk_w=48,
+                sorted_row=64, row_pos=80, offsets=96, workspace=112, workspace_bytes=1 << 20)
+    base.update(kw)
+    return lm.RouteArgs(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), 1), (dict(k=65, E=100), 1), (dict(E=3), 1), (dict(T=-1), 1),
+    (dict(logits=None), 1),                               # neither logits nor ids
+    (dict(ids_in=128, weights_in=144), 1),                # both logits and ids
+    (dict(logits=None, ids_in=128, weights_in=None, k=1), 1),
+    (dict(logits=None, ids_in=128, weights_in=144, k=2), 1),
+    (dict(topk_ids=None), 1), (dict(sorted_row=None), 1),
+    (dict(logits=17), 1),                                 # misaligned
+    (dict(workspace_bytes=16), 1),                        # workspace too small
+    (dict(E=2000, k=4), 2),                               # logits mode E limit
+    (dict(logits=None, ids_in=128, weights_in=144, k=1, E=5000), 2),
+])
+def test_route_rejects_invalid_arguments(kw, code):
+    import latentmoe_expert_layer_amd as lm
+    with pytest.raises(lm.LatentMoeError) as ei:
+        lm.latent_moe_route(_route_args(lm, **kw))
+    assert ei.value.code == code, lm.latent_moe_last_error()
+    assert lm.latent_moe_last_error()
+
+
+def test_route_with_empty_batch_needs_no_launch():
+    import latentmoe_expert_layer_amd as lm
+    plan = lm.latent_moe_route(_route_args(lm, T=0))
+    assert plan
+    fa = lm.ForwardArgs(d=512, l=256, I=128, S=1, Is=128, wfmt=0, norm_eps=1e-6, x=16, w_in=32, w1=48,
+                        w3=64, w2=80, w_out=96, ws1=112, ws3=128, ws2=144, y=160, workspace=176,
+                        workspace_bytes=1 << 20)
+    lm.latent_moe_forward(plan, fa)                       # T == 0: OK, nothing enqueued
+    for bad, code in [(dict(l=100), 1), (dict(I=0), 1), (dict(d=65), 1), (dict(S=5), 1),
+                      (dict(Is=32), 1), (dict(wfmt=7), 1), (dict(w_out=None), 1), (dict(x=None), 1),
+                      (dict(ws2=None), 1), (dict(y=8), 1),
+                      (dict(l=8192), 2)]:
+        args = lm.ForwardArgs(**{**{f: getattr(fa, f) for f, _ in fa._fields_}, **bad})
+        with pytest.raises(lm.LatentMoeError) as ei:
+            lm.latent_moe_forward(plan, args)
+        assert ei.value.code == code, (bad, lm.latent_moe_last_error())
+    # rows mode needs an ids-mode plan
+    args = lm.ForwardArgs(**{**{f: getattr(fa, f) for f, _ in fa._fields_}, "w_in": None, "w_out": None})
+    with pytest.raises(lm.LatentMoeError):
+        lm.latent_moe_forward(plan, args)
+    lm.latent_moe_free(plan)
+    lm.latent_moe_free(None)

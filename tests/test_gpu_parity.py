@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Routing ids, permutation and offsets must be bit-exact; combine weights within
+2e-6; bf16 layer outputs within max relative error 2e-2 (relative to
+max(|o|, 0.1 * rms(o))) and mean absolute error 1e-3.  Workspaces and outputs
+are poisoned with NaN before every call, so an unwritten read fails.
+"""
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.parity import assert_parity, log, poison_, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+lm = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global lm
+    import latentmoe_expert_layer_amd as m  # fails loudly if the library is not built
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lm = m
+    yield
+
+
+def gpu_route(logits=None, k=1, **kw):
+    T = logits.shape[0] if logits is not None else kw["ids"].shape[0]
+    E = logits.shape[1] if logits is not None else kw["E"]
+    ws = poison_(torch.empty(lm.route_workspace_size(T, E, k), dtype=torch.uint8, device="cuda"))
+    r = lm.route(logits, k, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def check_routing(r, logits_or_ids, k, E, weights=None):
+    if weights is None:
+        ids_ref, w_ref = oracle.route(logits_or_ids.cpu(), k)
+        assert torch.equal(r.topk_ids.cpu(), ids_ref), "router ids differ"
+        dw = (r.topk_w.cpu().double() - w_ref.double()).abs().max().item()
+        assert dw <= 2e-6, f"combine weights differ by {dw}"
+    else:
+        ids_ref, w_ref = logits_or_ids.cpu(), weights.cpu()
+    off, srow, rpos = oracle.permute(ids_ref, E)
+    assert torch.equal(r.offsets.cpu(), off), "offsets differ"
+    assert torch.equal(r.sorted_row.cpu(), srow), "sorted_row differs"
+    assert torch.equal(r.row_pos.cpu(), rpos), "row_pos differs"
+    return ids_ref, w_ref
+
+
+# ------------------------------------------------------------------ routing
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+def test_route_bit_exact(name):
+    cfg = W.CONFIGS[name]
+    log(f"route {name}: T={cfg.T} E={cfg.E} k={cfg.k}")
+    logits = W.separated_logits(cfg.seed, "logits", cfg.T, cfg.E, cfg.k, device="cuda")
+    r = gpu_route(logits, cfg.k)
+    check_routing(r, logits, cfg.k, cfg.E)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 16, 4), (37, 64, 64), (300, 1024, 16), (129, 7, 3), (1000, 896, 1)])
+def test_route_ties_nan_ragged(T, E, k):
+    log(f"route ties T={T} E={E} k={k}")
+    g = torch.Generator().manual_seed(T * 7 + E)
+    logits = (torch.randn(T, E, generator=g) * 3).round() / 4     # many exact ties
+    logits[0, : min(E, 5)] = float("nan")
+    if T > 2:
+        logits[1, :] = -0.0
+        logits[1, E // 2] = 0.0
+        logits[2, :] = float("-inf")
+    r = gpu_route(logits.cuda(), k)
+    ids_ref, _ = oracle.route(logits, k)
+    assert torch.equal(r.topk_ids.cpu(), ids_ref)
+    off, srow, rpos = oracle.permute(ids_ref, E)
+    assert torch.equal(r.offsets.cpu(), off)
+    assert torch.equal(r.sorted_row.cpu(), srow)
+    assert torch.equal(r.row_pos.cpu(), rpos)
+
+
+@pytest.mark.parametrize("R,E,heavy", [(16384, 56, False), (5000, 4096, False), (777, 13, True), (64, 1, False)])
+def test_permute_ids_mode(R, E, heavy):
+    log(f"permute ids R={R} E={E} heavy={heavy}")
+    ids = W.zipf_ids(0, "ids", R, E, 1.1).view(R, 1)
+    if heavy:
+        ids[: R // 2] = 5
+    w = W.uniform_weights(0, "w", (R, 1))
+    r = gpu_route(None, 1, ids=ids.cuda(), weights=w.cuda(), E=E)
+    check_routing(r, ids.view(-1), 1, E, weights=w)
+
+
+# -------------------------------------------------------------------- layer
+def run_gpu_layer(inp_dev, norm=True):
+    cfg = inp_dev["cfg"]
+    T = cfg.T
+    wfmt = lm.LMOE_WFMT_MXFP4 if cfg.mxfp4 else lm.LMOE_WFMT_BF16
+    if cfg.rows_mode:
+        r = gpu_route(None, 1, ids=inp_dev["ids"], weights=inp_dev["weights"], E=cfg.E)
+        nbytes = lm.forward_workspace_size(T, cfg.E, 1, 0, cfg.l, cfg.I, 0, 0, wfmt, True)
+        ws = poison_(torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
+        y = poison_(torch.empty(T, cfg.l, dtype=torch.bfloat16, device="cuda"))
+        lm.forward(r, inp_dev["x"], inp_dev["w1"], inp_dev["w3"], inp_dev["w2"], y=y, workspace=ws)
+        torch.cuda.synchronize()
+        return r, y
+    r = gpu_route(inp_dev["logits"], cfg.k)
+    nbytes = lm.forward_workspace_size(T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is, wfmt, False)
+    ws = poison_(torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
+    y = poison_(torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda"))
+    mx = cfg.mxfp4
+    lm.forward(r, inp_dev["x"], inp_dev["w1q" if mx else "w1"], inp_dev["w3q" if mx else "w3"],
+               inp_dev["w2q" if mx else "w2"], w_in=inp_dev["w_in"], w_out=inp_dev["w_out"],
+               ws1=inp_dev.get("ws1"), ws3=inp_dev.get("ws3"), ws2=inp_dev.get("ws2"),
+               norm_w=inp_dev.get("norm_w") if norm else None, eps=cfg.eps, s1=inp_dev.get("s1"),
+               s3=inp_dev.get("s3"), s2=inp_dev.get("s2"), mxfp4=mx, I=cfg.I, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    return r, y
+
+
+SMALL_LAYERS = [
+    ("tiny", None),
+    ("decode", None),
+    # ragged: T not a tile multiple, experts with 0 rows, one expert above a 128-row tile
+    ("ragged_a", dict(T=203, d=192, l=128, E=9, k=3, S=1, I=64, Is=192)),
+    ("ragged_b", dict(T=77, d=128, l=320, E=40, k=8, S=2, I=192, Is=64)),
+    ("no_shared", dict(T=150, d=256, l=256, E=4, k=2, S=0, I=128, Is=0)),
+    ("single_token", dict(T=1, d=128, l=64, E=16, k=4, S=1, I=64, Is=64)),
+    # enough rows per expert (>32 on average) to take the LDS-tiled grouped path
+    ("tiled_path", dict(T=600, d=256, l=512, E=8, k=2, S=1, I=256, Is=128)),
+]
+
+
+@pytest.mark.parametrize("name,dims", SMALL_LAYERS, ids=[n for n, _ in SMALL_LAYERS])
+@pytest.mark.parametrize("norm", ["ones", "random", "none"])
+def test_layer_parity_small(name, dims, norm):
+    cfg = W.CONFIGS[name] if dims is None else W.custom(name, **dims)
+    log(f"layer {name} norm={norm}: {cfg}")
+    inp = W.make_inputs(cfg, norm_w=norm)
+    ref = oracle.run(inp)
+    r, y = run_gpu_layer(to_device(inp))
+    check_routing(r, inp["logits"], cfg.k, cfg.E)
+    assert_parity(y.cpu(), ref["y"])
+
+
+def test_layer_deterministic_and_empty():
+    cfg = W.CONFIGS["decode"]
+    inp = to_device(W.make_inputs(cfg))
+    _, y1 = run_gpu_layer(inp)
+    _, y2 = run_gpu_layer(inp)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "repeat runs differ"
+    # T = 0 is a no-op
+    empty = W.custom("empty", T=0, d=512, l=256, E=16, k=4, S=1, I=128, Is=128)
+    e_inp = W.make_inputs(empty)
+    e_inp = to_device(e_inp)
+    r = lm.route(e_inp["logits"], 4)
+    y = lm.forward(r, e_inp["x"], e_inp["w1"], e_inp["w3"], e_inp["w2"], w_in=e_inp["w_in"],
+                   w_out=e_inp["w_out"], ws1=e_inp["ws1"], ws3=e_inp["ws3"], ws2=e_inp["ws2"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, 512)
+
+
+def test_rows_mode_ep_share_sampled():
+    cfg = W.CONFIGS["ep_share"]
+    log(f"ep_share rows mode: {cfg}")
+    inp_dev = W.make_inputs(cfg, device="cuda")
+    r, y = run_gpu_layer(inp_dev)
+    inp = to_host(inp_dev)
+    check_routing(r, inp["ids"].view(-1), 1, cfg.E, weights=inp["weights"])
+    # sample rows: the first and last rows of the heaviest and lightest experts, plus a spread
+    off, srow, _ = oracle.permute(inp["ids"], cfg.E)
+    off, srow = off.long(), srow.long()
+    counts = off[1:] - off[:-1]
+    pick = set(range(0, cfg.T, cfg.T // 48))
+    for e in (int(counts.argmax()), int(counts.argmin())):
+        if counts[e] > 0:
+            pick |= {int(srow[off[e]]), int(srow[off[e + 1] - 1])}
+    pick = sorted(pick)
+    ref = oracle.layer(inp, inp["ids"], inp["weights"], eval_tokens=pick)["y"]
+    assert_parity(y.cpu()[pick], ref)
+
+
+@pytest.mark.parametrize("name", ["prefill"])
+def test_layer_full_size_sampled(name):
+    cfg = W.CONFIGS[name]
+    log(f"full-size {name}: {cfg}")
+    inp_dev = W.make_inputs(cfg, device="cuda")
+    r, y = run_gpu_layer(inp_dev)
+    ids_ref, w_ref = check_routing(r, inp_dev["logits"], cfg.k, cfg.E)
+    inp = to_host(inp_dev)
+    del inp_dev
+    # first and last token of every 1024-token span, plus a spread
+    pick = sorted({0, cfg.T - 1} | set(range(0, cfg.T, 1024)) | set(range(1023, cfg.T, 1024))
+                  | set(range(37, cfg.T, 997)))
+    ref = oracle.layer(inp, ids_ref, w_ref, eval_tokens=pick)["y"]
+    assert_parity(y.cpu()[pick], ref)
