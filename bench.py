@@ -1,0 +1,275 @@
+"""Throughput bench of the LatentMoE layer on one MI355X.
+
+One step = route (router top-k/softmax + permutation) + forward (down-proj,
+shared experts, grouped expert FC1/FC2, combine + RMSNorm, up-proj) over one
+batch of synthetic tokens, all through the C ABI.  Inputs are resident in HBM
+before the timed region.  Several copies of every input (weights included)
+are cycled through, so the expert weights are streamed from HBM rather than
+re-read from the 256 MB last-level cache.
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (its
+duration from HIP events recorded on the layer's stream around that kernel in
+every timed step) and the CPU oracle's throughput on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|...]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+LLC_BYTES = 256 << 20          # MI355X Infinity Cache
+METRIC = "LatentMoE layer tokens/s at 1 GPU; grouped-GEMM TFLOP/s as % MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0 = enough to beat the LLC)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle budget (0 = skip)")
+    ap.add_argument("--no-stage-events", action="store_true")
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the bench needs for its own events."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(ctypes.c_void_p(b))
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "latentmoe_expert_layer_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp_host, budget_s):
+    """The oracle (as it stands) on this host's cores: whole route + layer
+    passes over the same workload until the budget is used."""
+    import oracle
+    import torch
+    cores = oracle.num_threads()
+    # sample: whole batches; the oracle's route and layer over all T tokens
+    done, t0 = 0, time.perf_counter()
+    while True:
+        out = oracle.run(inp_host)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 50:
+            break
+    del out, torch
+    return {"value": done * cfg.T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} full route+forward pass(es) of the {cfg.name} batch ({cfg.T} tokens) "
+                      f"in {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is built and "
+              "measured on a single MI355X", file=sys.stderr)
+        return 2
+    import torch
+
+    import latentmoe_expert_layer_amd as lm
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = W.CONFIGS[args.workload]
+    if cfg.rows_mode or cfg.mxfp4:
+        raise SystemExit("bench workloads: tiny, decode, prefill")
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # ---------------- inputs: several resident copies, distinct seeds
+    wbytes = 3 * cfg.E * cfg.I * cfg.l * 2
+    copies = args.copies or max(2, min(8, -(-2 * LLC_BYTES // max(wbytes, 1))))
+    sets = []
+    for c in range(copies):
+        inp = W.make_inputs(W.LayerConfig(**{**cfg.__dict__, "seed": c}), device="cuda")
+        T, E, k = cfg.T, cfg.E, cfg.k
+        R = T * k
+        rws = torch.empty(lm.route_workspace_size(T, E, k), dtype=torch.uint8, device="cuda")
+        fws = torch.empty(lm.forward_workspace_size(T, E, k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is),
+                          dtype=torch.uint8, device="cuda")
+        out = dict(topk_ids=torch.empty(T, k, dtype=torch.int32, device="cuda"),
+                   topk_w=torch.empty(T, k, dtype=torch.float32, device="cuda"),
+                   sorted_row=torch.empty(R, dtype=torch.int32, device="cuda"),
+                   row_pos=torch.empty(R, dtype=torch.int32, device="cuda"),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                   y=torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda"))
+        P = lambda t: None if t is None else t.data_ptr()
+        ra = lm.RouteArgs(T=T, E=E, k=k, logits=P(inp["logits"]), topk_ids=P(out["topk_ids"]),
+                          topk_w=P(out["topk_w"]), sorted_row=P(out["sorted_row"]), row_pos=P(out["row_pos"]),
+                          offsets=P(out["offsets"]), workspace=P(rws), workspace_bytes=rws.numel())
+        fa = lm.ForwardArgs(d=cfg.d, l=cfg.l, I=cfg.I, S=cfg.S, Is=cfg.Is, wfmt=0, norm_eps=cfg.eps,
+                            x=P(inp["x"]), w_in=P(inp["w_in"]), w1=P(inp["w1"]), w3=P(inp["w3"]),
+                            w2=P(inp["w2"]), norm_w=P(inp.get("norm_w")), w_out=P(inp["w_out"]),
+                            ws1=P(inp.get("ws1")), ws3=P(inp.get("ws3")), ws2=P(inp.get("ws2")),
+                            y=P(out["y"]), workspace=P(fws), workspace_bytes=fws.numel())
+        sets.append(dict(inp=inp, rws=rws, fws=fws, out=out, ra=ra, fa=fa))
+    torch.cuda.synchronize()
+
+    n_ev = lm.N_STAGE_EVENTS
+    use_events = not args.no_stage_events
+
+    def step(i, events=None):
+        s = sets[i % copies]
+        plan = lm.latent_moe_route(s["ra"], stream)
+        if events is not None:
+            lm.latent_moe_plan_set_stage_events(plan, events)
+        lm.latent_moe_forward(plan, s["fa"], stream)
+        lm.latent_moe_free(plan)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-step stage events: one set per timed step, read after the region
+    ev_sets = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)] if use_events else None
+    t_start, t_end = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hip.record(t_start, stream)
+    for i in range(args.steps):
+        step(i, ev_sets[i] if use_events else None)
+    hip.record(t_end, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = hip.elapsed_ms(t_start, t_end)
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = cfg.T * args.steps / (total_ms / 1e3)
+
+    stages = {}
+    if use_events:
+        for j, name in enumerate(lm.STAGES):
+            vals = [hip.elapsed_ms(ev[j], ev[j + 1]) for ev in ev_sets]
+            stages[name] = 1e3 * sum(vals) / len(vals)
+        fwd = [hip.elapsed_ms(ev[0], ev[n_ev - 1]) for ev in ev_sets]
+        stages["forward_total"] = 1e3 * sum(fwd) / len(fwd)
+
+    # ---------------- algorithmic work (per launch, averaged over the copies)
+    T, E, k, d, l, I, S, Is = cfg.T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is
+    R = T * k
+    touched = sum(int(((s["out"]["offsets"][1:] - s["out"]["offsets"][:-1]) > 0).sum()) for s in sets) / copies
+    fc1_bytes = touched * 2 * I * l * 2 + T * l * 2 + R * I * 2
+    fc2_bytes = touched * l * I * 2 + R * I * 2 + R * l * 2
+    fc1_flop = 2.0 * R * l * 2 * I
+    fc2_flop = 2.0 * R * I * l
+    dense_flop = 2.0 * T * d * (l + 2 * S * Is) + 2.0 * T * (l + S * Is) * d
+    layer_flop = fc1_flop + fc2_flop + dense_flop
+    dense_bytes = 2 * (T * d + (l + 2 * S * Is) * d + T * l + T * S * Is + d * (l + S * Is) + T * d)
+    route_bytes = T * E * 4 + R * (4 + 4 + 4 + 4 + 4)
+    combine_bytes = R * l * 2 + T * l * 2 + R * 8
+    layer_bytes = fc1_bytes + fc2_bytes + dense_bytes + route_bytes + combine_bytes
+
+    roofline = None
+    if use_events:
+        dom = max(("fc1", "fc2"), key=lambda n: stages[n])
+        dom_bytes = fc1_bytes if dom == "fc1" else fc2_bytes
+        dom_flop = fc1_flop if dom == "fc1" else fc2_flop
+        dur_s = stages[dom] / 1e6
+        ai = dom_flop / dom_bytes
+        bound = "hbm" if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+        kern = "grouped_gemm"
+        traffic = measured_traffic(f"{dom}", cfg.name, source_hash("gemm.hip"))
+        if bound == "hbm":
+            achieved = dom_bytes / dur_s / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                        "kernel": f"{kern} ({dom})", "algorithmic_bytes_per_launch": int(dom_bytes),
+                        "avg_launch_us": round(stages[dom], 2)}
+        else:
+            achieved = dom_flop / dur_s / 1e12
+            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                        "kernel": f"{kern} ({dom})", "algorithmic_flop_per_launch": dom_flop,
+                        "avg_launch_us": round(stages[dom], 2)}
+
+    extra = {
+        "copies_cycled": copies,
+        "wall_s": round(wall, 3),
+        "stage_us": {n: round(v, 2) for n, v in stages.items()},
+        "layer_tflops": round(layer_flop / (ms_per_step / 1e3) / 1e12, 2),
+        "layer_hbm_gbs": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "layer_hbm_frac": round(layer_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_algorithmic_bytes": int(layer_bytes),
+        "touched_experts": touched,
+    }
+    if use_events:
+        for n, fl, by in (("fc1", fc1_flop, fc1_bytes), ("fc2", fc2_flop, fc2_bytes)):
+            us = stages[n]
+            extra[f"{n}_tflops"] = round(fl / us / 1e6, 2)
+            extra[f"{n}_mfma_frac"] = round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4)
+            extra[f"{n}_hbm_frac"] = round(by / us / 1e3 / HBM_PEAK_GBS, 4)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        from tests.parity import to_host
+        cpu = cpu_baseline(cfg, to_host(sets[0]["inp"]), args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights, gap-separated N(0,1) logits)",
+        "config": {"workload": f"{cfg.name}: T={T} tokens, d={d} -> latent {l}, E={E} top-{k} + {S} shared, "
+                               f"SwiGLU I={I}, shared I={Is}, RMSNorm on", "T": T, "d": d, "latent": l, "E": E,
+                   "k": k, "shared": S, "I": I, "Is": Is},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

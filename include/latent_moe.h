@@ -98,8 +98,9 @@ typedef struct latent_moe_plan latent_moe_plan; /* opaque, host memory */
  *               grouped-GEMM tile tables that latent_moe_forward reads
  * On success *out_plan receives a new plan that borrows (does not copy) the
  * output and workspace pointers: they must stay valid and unmodified for
- * every latent_moe_forward that uses the plan.  T == 0 is valid (nothing is
- * enqueued; forward then does nothing).
+ * every latent_moe_forward that uses the plan.  T == 0 is valid: no pointer
+ * is read or checked, nothing is enqueued, and forward with that plan only
+ * validates its dimensions and does nothing.
  */
 typedef struct {
   int64_t T;
@@ -176,6 +177,18 @@ int latent_moe_forward(const latent_moe_plan* plan, const lmoe_forward_args* arg
 /* Releases a plan (host memory only; NULL is a no-op).  Device buffers the
  * plan borrowed remain the caller's. */
 void latent_moe_free(latent_moe_plan* plan);
+
+/* Optional stage timing (profiling aid, no effect on results).  With n ==
+ * LMOE_N_STAGE_EVENTS caller-created hipEvent_t handles (passed as void*),
+ * every later latent_moe_forward on this plan records events[0] before its
+ * first kernel and events[i] after stage i: 1 down-projection, 2 shared
+ * experts' gate/up, 3 expert FC1, 4 expert FC2, 5 combine (+ RMSNorm),
+ * 6 up-projection (stages a call does not run are recorded back to back).
+ * events == NULL (or n == 0) turns recording off.  The events are borrowed:
+ * they must outlive their use.  Returns LMOE_EINVAL for a NULL plan or
+ * another n. */
+#define LMOE_N_STAGE_EVENTS 7
+int latent_moe_plan_set_stage_events(latent_moe_plan* plan, void* const* events, int n);
 
 /* Workspace sizes in bytes (0 on invalid dimensions).  rows_mode != 0 sizes
  * for an ids-mode plan with no projections. */

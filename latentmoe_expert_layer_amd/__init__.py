@@ -62,6 +62,8 @@ def _load():
     L.latent_moe_route_workspace_size.restype = _sz
     L.latent_moe_forward_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
     L.latent_moe_forward_workspace_size.restype = _sz
+    L.latent_moe_plan_set_stage_events.argtypes = [_vp, ctypes.POINTER(_vp), ctypes.c_int]
+    L.latent_moe_plan_set_stage_events.restype = ctypes.c_int
     L.latent_moe_last_error.argtypes = []
     L.latent_moe_last_error.restype = ctypes.c_char_p
     return L
@@ -85,6 +87,19 @@ def latent_moe_forward(plan: int, args: ForwardArgs, stream: int = 0):
 
 def latent_moe_free(plan: Optional[int]):
     lib.latent_moe_free(_vp(plan))
+
+
+N_STAGE_EVENTS = 7
+STAGES = ("down_proj", "shared_gate_up", "fc1", "fc2", "combine", "up_proj")
+
+
+def latent_moe_plan_set_stage_events(plan: int, events):
+    """events: sequence of N_STAGE_EVENTS hipEvent_t handles (ints), or None."""
+    if events is None:
+        _check(lib.latent_moe_plan_set_stage_events(_vp(plan), None, 0))
+        return
+    arr = (_vp * len(events))(*events)
+    _check(lib.latent_moe_plan_set_stage_events(_vp(plan), arr, len(events)))
 
 
 def latent_moe_last_error() -> str:

