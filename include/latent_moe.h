@@ -183,7 +183,8 @@ void latent_moe_free(latent_moe_plan* plan);
  * every later latent_moe_forward on this plan records events[0] before its
  * first kernel and events[i] after stage i: 1 down-projection, 2 shared
  * experts' gate/up, 3 expert FC1, 4 expert FC2, 5 combine (+ RMSNorm),
- * 6 up-projection (stages a call does not run are recorded back to back).
+ * 6 up-projection (stages a call does not run, or runs fused into the
+ * previous stage's kernel, are recorded back to back).
  * events == NULL (or n == 0) turns recording off.  The events are borrowed:
  * they must outlive their use.  Returns LMOE_EINVAL for a NULL plan or
  * another n. */

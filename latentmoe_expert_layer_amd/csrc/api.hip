@@ -272,31 +272,35 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
 
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "event");
   // 1. latent down-projection, and the shared experts' gate/up on x
+  const bool small = T <= lmoe::kSmallM;
   if (!rows) {
-    lmoe::DenseGemm g{};
-    g.M = int(T);
-    g.N = int(l);
-    g.nseg = 1;
-    g.seg[0] = lmoe::GemmSeg{x, d, static_cast<const uint16_t*>(a->w_in), nullptr, d, int(d)};
-    g.gated = false;
-    g.C = z;
-    g.ldc = l;
-    if ((e = lmoe::launch_dense_gemm(g, s)) != hipSuccess) return hip_fail(e, "down-proj");
-  }
-  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event");
-  if (!rows) {
-    if (S > 0) {
-      lmoe::DenseGemm h{};
-      h.M = int(T);
-      h.N = int(S * Is);
-      h.nseg = 1;
-      h.seg[0] = lmoe::GemmSeg{x, d, static_cast<const uint16_t*>(a->ws1), static_cast<const uint16_t*>(a->ws3),
-                               d, int(d)};
-      h.gated = true;
-      h.C = hs;
-      h.ldc = S * Is;
-      if ((e = lmoe::launch_dense_gemm(h, s)) != hipSuccess) return hip_fail(e, "shared gate/up");
+    lmoe::DenseGemm g[2] = {};
+    g[0].M = int(T);
+    g[0].N = int(l);
+    g[0].nseg = 1;
+    g[0].seg[0] = lmoe::GemmSeg{x, d, static_cast<const uint16_t*>(a->w_in), nullptr, d, int(d)};
+    g[0].gated = false;
+    g[0].C = z;
+    g[0].ldc = l;
+    g[1].M = int(T);
+    g[1].N = int(S * Is);
+    g[1].nseg = 1;
+    g[1].seg[0] = lmoe::GemmSeg{x, d, static_cast<const uint16_t*>(a->ws1), static_cast<const uint16_t*>(a->ws3),
+                                d, int(d)};
+    g[1].gated = true;
+    g[1].C = hs;
+    g[1].ldc = S * Is;
+    if (small) {
+      // one launch for both: they read the same rows of x
+      if ((e = lmoe::launch_small_dense(g, S > 0 ? 2 : 1, s)) != hipSuccess) return hip_fail(e, "down-proj");
+      if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event");
+    } else {
+      if ((e = lmoe::launch_dense_gemm(g[0], s)) != hipSuccess) return hip_fail(e, "down-proj");
+      if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event");
+      if (S > 0 && (e = lmoe::launch_dense_gemm(g[1], s)) != hipSuccess) return hip_fail(e, "shared gate/up");
     }
+  } else if ((e = mark(1)) != hipSuccess) {
+    return hip_fail(e, "event");
   }
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event");
 
@@ -366,7 +370,8 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   u.gated = false;
   u.C = static_cast<uint16_t*>(a->y);
   u.ldc = d;
-  if ((e = lmoe::launch_dense_gemm(u, s)) != hipSuccess) return hip_fail(e, "up-proj");
+  e = small ? lmoe::launch_small_dense(&u, 1, s) : lmoe::launch_dense_gemm(u, s);
+  if (e != hipSuccess) return hip_fail(e, "up-proj");
   if ((e = mark(6)) != hipSuccess) return hip_fail(e, "event");
   return LMOE_OK;
 }

@@ -36,11 +36,13 @@ __device__ __forceinline__ void unpack(const typename VecT<VEC>::type& v, float*
   for (int i = 0; i < VEC; ++i) f[i] = bf16_to_f32(h[i]);
 }
 
-constexpr int kRowsInFlight = 8;
+constexpr int kRowsInFlight = 16;
 
 // One wave per token row; lane owns VEC contiguous elements of every
-// 64*VEC-wide chunk.  The fp32 row is parked in LDS between the two passes
-// (weighted sum + sum of squares, then scale and store).
+// 64*VEC-wide chunk.  Lane j < k first fetches the j-th slot's row position
+// and weight; each chunk then keeps 16 rows' loads in flight.  The fp32 row
+// is parked in LDS between the two passes (weighted sum + sum of squares,
+// then scale and store).
 template <int VEC>
 __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__ Y, const int32_t* __restrict__ row_pos,
                                                       const float* __restrict__ w, int64_t T, int k, int l,
@@ -52,6 +54,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
   const int64_t t = int64_t(blockIdx.x) * 4 + wid;
   if (t >= T) return;
   float* c = crow + wid * l;
+  int32_t my_p = 0;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_p = row_pos[t * k + lane];
+    my_w = w[t * k + lane];
+  }
   float ss = 0.0f;
   for (int base = 0; base < l; base += 64 * VEC) {
     const int col = base + lane * VEC;
@@ -60,23 +68,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
     for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
     for (int j0 = 0; j0 < k; j0 += kRowsInFlight) {
       V v[kRowsInFlight];
-      float wj[kRowsInFlight];
+      // loads past the last slot re-read slot k-1 (no branch, so all of
+      // them are in flight together); their values are not used
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u) {
-        if (j0 + u < k) {
-          const int64_t r = t * k + j0 + u;
-          const int64_t p = row_pos[r];
-          wj[u] = w[r];
-          v[u] = *reinterpret_cast<const V*>(Y + p * l + col);
-        }
+        const int64_t p = __builtin_amdgcn_readlane(my_p, min(j0 + u, k - 1));
+        v[u] = *reinterpret_cast<const V*>(Y + p * l + col);
       }
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u) {
         if (j0 + u < k) {
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j0 + u));
           float f[VEC];
           unpack<VEC>(v[u], f);
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[i] += wj[u] * f[i];
+          for (int i = 0; i < VEC; ++i) acc[i] += wj * f[i];
         }
       }
     }

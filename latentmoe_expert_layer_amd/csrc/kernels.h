@@ -55,6 +55,11 @@ struct DenseGemm {
   int64_t ldc;
 };
 hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
+// Few-row variant (M <= kSmallM): 16-row tiles, K split across the 4 waves of
+// a workgroup; up to two sub-GEMMs with the same M in one launch.  Every N is
+// a multiple of 32.
+constexpr int kSmallM = 512;
+hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s);
 
 // Grouped over experts: for each tile (expert e, rows p in the tile):
 //   C[p, :] = A[row(p)] * B_e^T  (gated: silu(A B_e^T) * (A B3_e^T)),

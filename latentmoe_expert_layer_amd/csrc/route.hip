@@ -35,15 +35,34 @@ __device__ __forceinline__ float key_value(uint64_t k) {
   return __uint_as_float(u);
 }
 
+// DPP move of a 32-bit value; lanes without a source (or outside row_mask)
+// read 0, the identity of an unsigned max.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = dpp_move<CTRL, ROW_MASK>(uint32_t(v));
+  const uint32_t hi = dpp_move<CTRL, ROW_MASK>(uint32_t(v >> 32));
+  const uint64_t o = (uint64_t(hi) << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Wave-wide max of a 64-bit key with DPP row operations: butterflies inside
+// each quad, shifts inside each 16-lane row, then the row broadcasts; the
+// full maximum ends in lane 63 and is read back as a wave-uniform value.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor(uint32_t(v), off, kWave);
-    uint32_t hi = __shfl_xor(uint32_t(v >> 32), off, kWave);
-    uint64_t o = (uint64_t(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0xb1>(v);        // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4e>(v);        // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x114>(v);       // row_shr:4
+  v = dpp_max_step<0x118>(v);       // row_shr:8
+  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), 63));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63));
+  return (uint64_t(hi) << 32) | lo;
 }
 
 // One wave per token; lane l holds logits e = l + 64*j (coalesced rows).
@@ -57,11 +76,16 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + t * int64_t(E);
+  // all VPL loads are issued unconditionally (clamped index) so that they are
+  // in flight together; slots past E are then emptied
+  float v[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
   uint64_t cand[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int e = lane + 64 * j;
-    cand[j] = (e < E) ? rank_key(row[e], uint32_t(e)) : 0ull;
+    cand[j] = (e < E) ? rank_key(v[j], uint32_t(e)) : 0ull;
   }
   uint64_t best = 0;
 #pragma unroll
@@ -80,9 +104,9 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
       }
     }
   }
-  const float v = key_value(mine);
-  const float vmax = __shfl(v, 0, kWave);
-  float ex = (lane < k) ? expf(v - vmax) : 0.0f;
+  const float lv = key_value(mine);
+  const float vmax = __shfl(lv, 0, kWave);
+  float ex = (lane < k) ? expf(lv - vmax) : 0.0f;
   float sum = ex;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, kWave);
@@ -219,8 +243,18 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 
   const int64_t chunk = ((R + nwaves - 1) / nwaves + 63) / 64 * 64;
   const int64_t r0 = int64_t(wid) * chunk, r1 = min(R, r0 + chunk);
+  // ids are read kBatch rows per lane at a time with clamped (in-bounds)
+  // indices, so a batch's loads are in flight together
+  constexpr int kBatch = 8;
   if (wid < nwaves) {
-    for (int64_t r = r0 + lane; r < r1; r += 64) atomicAdd(&hist[wid * E + clamp_id(ids[r], E)], 1);
+    for (int64_t rb = r0; rb < r1; rb += 64 * kBatch) {
+      int32_t idv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) idv[u] = ids[min(rb + 64 * u + lane, R - 1)];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (rb + 64 * u + lane < r1) atomicAdd(&hist[wid * E + clamp_id(idv[u], E)], 1);
+    }
   }
   __syncthreads();
 
@@ -247,10 +281,17 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t base_r = r0; base_r < r1; base_r += 64) {
+    for (int64_t rb = r0; rb < r1; rb += 64 * kBatch) {
+      int32_t idv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) idv[u] = ids[min(rb + 64 * u + lane, R - 1)];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+      const int64_t base_r = rb + 64 * u;
+      if (base_r >= r1) break;
       const int64_t r = base_r + lane;
       const bool valid = r < r1;
-      const int32_t id = valid ? clamp_id(ids[r], E) : 0;
+      const int32_t id = valid ? clamp_id(idv[u], E) : 0;
       uint64_t peers = ballot(valid);
       for (int b = 0; b < nbits; ++b) {
         const bool bit = (id >> b) & 1;
@@ -265,6 +306,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
         const int32_t p = base + rank;
         sorted_row[p] = int32_t(r);
         row_pos[r] = p;
+      }
       }
     }
   }

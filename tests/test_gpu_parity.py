@@ -127,6 +127,8 @@ SMALL_LAYERS = [
     ("single_token", dict(T=1, d=128, l=64, E=16, k=4, S=1, I=64, Is=64)),
     # enough rows per expert (>32 on average) to take the LDS-tiled grouped path
     ("tiled_path", dict(T=600, d=256, l=512, E=8, k=2, S=1, I=256, Is=128)),
+    # LDS-tiled dense projections with a ragged last row tile, odd latent width
+    ("mid_ragged", dict(T=1000, d=320, l=192, E=24, k=4, S=2, I=128, Is=64)),
 ]
 
 
