@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0 = enough to beat the LLC)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle budget (0 = skip)")
     ap.add_argument("--no-stage-events", action="store_true")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="graph: each copy's route+forward captured once in a HIP graph and replayed")
     return ap.parse_args()
 
 
@@ -174,23 +176,62 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # per-step stage events: one set per timed step, read after the region
-    ev_sets = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)] if use_events else None
-    t_start, t_end = hip.event(), hip.event()
-    torch.cuda.synchronize()
+    mode = args.mode
+    graphs = []
+    if mode == "graph":
+        try:
+            cap = torch.cuda.Stream()
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    cs = torch.cuda.current_stream().cuda_stream
+                    plan = lm.latent_moe_route(sets[c]["ra"], cs)
+                    lm.latent_moe_forward(plan, sets[c]["fa"], cs)
+                    lm.latent_moe_free(plan)
+                graphs.append(g)
+            for i in range(args.warmup):
+                graphs[i % copies].replay()
+            torch.cuda.synchronize()
+        except Exception as exc:  # capture unsupported here: time eager launches instead
+            print(f"graph capture failed ({exc}); timing eager launches", file=sys.stderr)
+            mode, graphs = "eager", []
+            torch.cuda.synchronize()
+
+    def timed(run_steps, with_events):
+        """K steps between two events on the layer's stream; eager steps may
+        carry one set of stage events each (read after the region)."""
+        ev_sets = [[hip.event() for _ in range(n_ev)] for _ in range(args.steps)] if with_events else None
+        t0, t1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(t0, stream)
+        run_steps(ev_sets)
+        hip.record(t1, stream)
+        torch.cuda.synchronize()
+        return hip.elapsed_ms(t0, t1), ev_sets
+
+    def eager_steps(ev_sets):
+        for i in range(args.steps):
+            step(i, ev_sets[i] if ev_sets is not None else None)
+
+    def graph_steps(_):
+        for i in range(args.steps):
+            graphs[i % copies].replay()
+
     wall0 = time.perf_counter()
-    hip.record(t_start, stream)
-    for i in range(args.steps):
-        step(i, ev_sets[i] if use_events else None)
-    hip.record(t_end, stream)
-    torch.cuda.synchronize()
+    if mode == "graph":
+        total_ms, _ = timed(graph_steps, False)
+    else:
+        total_ms, _ = timed(eager_steps, False)
     wall = time.perf_counter() - wall0
-    total_ms = hip.elapsed_ms(t_start, t_end)
     ms_per_step = total_ms / args.steps
     tokens_per_s = cfg.T * args.steps / (total_ms / 1e3)
 
-    stages = {}
+    # kernel durations: a second timed region of eager steps, each carrying the
+    # library's stage events (events inside a replayed graph cannot be timed)
+    stages, eager_ms = {}, None
     if use_events:
+        eager_total, ev_sets = timed(eager_steps, True)
+        eager_ms = eager_total / args.steps
         for j, name in enumerate(lm.STAGES):
             vals = [hip.elapsed_ms(ev[j], ev[j + 1]) for ev in ev_sets]
             stages[name] = 1e3 * sum(vals) / len(vals)
@@ -236,6 +277,8 @@ def main():
                         "avg_launch_us": round(stages[dom], 2)}
 
     extra = {
+        "mode": mode,
+        "eager_ms_per_step_with_stage_events": None if eager_ms is None else round(eager_ms, 5),
         "copies_cycled": copies,
         "wall_s": round(wall, 3),
         "stage_us": {n: round(v, 2) for n, v in stages.items()},

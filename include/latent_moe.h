@@ -126,8 +126,9 @@ int latent_moe_route(const lmoe_route_args* args, void* hip_stream, latent_moe_p
  * in `plan`.
  *
  * Dimensions: d (hidden), l (latent), I (routed intermediate), Is (shared
- * intermediate) are multiples of 64; 0 <= S <= 4 shared experts; wfmt is
- * LMOE_WFMT_BF16 or LMOE_WFMT_MXFP4.
+ * intermediate) are multiples of 64 (l and I multiples of 128 with MXFP4
+ * weights); l <= 4096; 0 <= S <= 4 shared experts; wfmt is LMOE_WFMT_BF16
+ * or LMOE_WFMT_MXFP4.
  * Arguments (device pointers, bf16 unless noted):
  *   x        [T,d]          hidden states (rows mode: latent rows [T,l])
  *   w_in     [l,d]          latent down-projection; NULL selects rows mode

@@ -83,10 +83,11 @@ RouteLayout route_layout(int64_t T, int32_t E, int32_t k) {
 
 // Forward workspace: bf16 intermediates z, hs, H, Y, rhat (and MXFP8 copies).
 struct FwdLayout {
-  size_t z, hs, H, Y, rhat, total;
+  size_t z, hs, H, Y, rhat, zq, zs, hq, hsc, total;
 };
 
-FwdLayout fwd_layout(int64_t T, int32_t k, int32_t l, int32_t I, int32_t S, int32_t Is, bool rows) {
+FwdLayout fwd_layout(int64_t T, int32_t k, int32_t l, int32_t I, int32_t S, int32_t Is, bool rows,
+                     bool mx = false) {
   FwdLayout L{};
   const int64_t R = T * k;
   size_t off = 0;
@@ -100,6 +101,15 @@ FwdLayout fwd_layout(int64_t T, int32_t k, int32_t l, int32_t I, int32_t S, int3
   off = align_up(off + size_t(R) * l * 2);
   L.rhat = off;
   off = align_up(off + (rows ? 0 : size_t(T) * l * 2));
+  // MXFP8 copies of the expert-GEMM activations (MXFP4 weights only)
+  L.zq = off;
+  off = align_up(off + (mx ? size_t(T) * l : 0));
+  L.zs = off;
+  off = align_up(off + (mx ? size_t(T) * (l / 32) : 0));
+  L.hq = off;
+  off = align_up(off + (mx ? size_t(R) * I : 0));
+  L.hsc = off;
+  off = align_up(off + (mx ? size_t(R) * (I / 32) : 0));
   L.total = off;
   return L;
 }
@@ -122,7 +132,11 @@ int check_fwd_dims(const latent_moe_plan* p, const lmoe_forward_args* a, bool ro
   if (a->l > 4096) return fail(LMOE_EUNSUPPORTED, "l=%d > 4096", a->l);
   if (a->S < 0 || a->S > LMOE_MAX_SHARED) return fail(LMOE_EINVAL, "S=%d outside [0,%d]", a->S, LMOE_MAX_SHARED);
   if (a->wfmt != LMOE_WFMT_BF16 && a->wfmt != LMOE_WFMT_MXFP4) return fail(LMOE_EINVAL, "unknown wfmt %d", a->wfmt);
-  if (a->wfmt == LMOE_WFMT_MXFP4) return fail(LMOE_EUNSUPPORTED, "MXFP4 expert weights are not built yet");
+  if (a->wfmt == LMOE_WFMT_MXFP4) {
+    if (a->l % 128 || a->I % 128)
+      return fail(LMOE_EINVAL, "MXFP4 experts need l and I multiples of 128 (got %d, %d)", a->l, a->I);
+    if (!a->s1 || !a->s3 || !a->s2) return fail(LMOE_EINVAL, "MXFP4 experts need scales s1, s3 and s2");
+  }
   if (rows) {
     if (a->w_out) return fail(LMOE_EINVAL, "rows mode (w_in == NULL) needs w_out == NULL");
     if (p->k != 1) return fail(LMOE_EINVAL, "rows mode needs k == 1 (got %d)", p->k);
@@ -153,7 +167,7 @@ size_t latent_moe_forward_workspace_size(int64_t T, int32_t E, int32_t k, int32_
   (void)d;
   if (T < 0 || k < 1 || l <= 0 || I <= 0 || S < 0 || (S > 0 && Is <= 0)) return 0;
   if (wfmt != LMOE_WFMT_BF16 && wfmt != LMOE_WFMT_MXFP4) return 0;
-  return fwd_layout(T, k, l, I, S, rows_mode ? 0 : Is, rows_mode != 0).total;
+  return fwd_layout(T, k, l, I, S, rows_mode ? 0 : Is, rows_mode != 0, wfmt == LMOE_WFMT_MXFP4).total;
 }
 
 int latent_moe_route(const lmoe_route_args* a, void* hip_stream, latent_moe_plan** out_plan) {
@@ -252,7 +266,8 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
     if (q && !aligned16(q)) return fail(LMOE_EINVAL, "device pointer %p is not 16-byte aligned", q);
   const int64_t T = p->T, R = p->T * p->k;
   const int32_t S = rows ? 0 : a->S;
-  const FwdLayout L = fwd_layout(T, p->k, a->l, a->I, S, S ? a->Is : 0, rows);
+  const bool mx = a->wfmt == LMOE_WFMT_MXFP4;
+  const FwdLayout L = fwd_layout(T, p->k, a->l, a->I, S, S ? a->Is : 0, rows, mx);
   if (!a->workspace || a->workspace_bytes < L.total)
     return fail(LMOE_EINVAL, "forward workspace too small: %zu < %zu", a->workspace_bytes, L.total);
 
@@ -305,45 +320,92 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "event");
 
   // 2-3. routed experts: grouped FC1 (gated) and FC2 over the permuted rows
-  const bool skinny = R <= int64_t(32) * p->E;
-  lmoe::GroupedGemm f1{};
-  f1.N = int(I);
-  f1.K = int(l);
-  f1.A = rows ? x : z;
-  f1.lda = l;
-  f1.a_rows = p->sorted_row;
-  f1.a_row_div = p->k;
-  f1.B = static_cast<const uint16_t*>(a->w1);
-  f1.B3 = static_cast<const uint16_t*>(a->w3);
-  f1.ldb = l;
-  f1.b_estride = I * l;
-  f1.gated = true;
-  f1.C = H;
-  f1.ldc = I;
-  f1.tiles = skinny ? p->tiles_s : p->tiles_t;
-  f1.ntiles = skinny ? p->n_s : p->n_t;
-  f1.max_tiles = skinny ? p->max_s : p->max_t;
-  e = skinny ? lmoe::launch_grouped_skinny(f1, s) : lmoe::launch_grouped_tiled(f1, s);
-  if (e != hipSuccess) return hip_fail(e, "expert FC1");
-  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "event");
+  if (mx) {
+    // w4a8: MXFP8 activations x MXFP4 weights on the block-scaled MFMA
+    uint8_t* zq = reinterpret_cast<uint8_t*>(ws + L.zq);
+    uint8_t* zs = reinterpret_cast<uint8_t*>(ws + L.zs);
+    uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+    uint8_t* hsc = reinterpret_cast<uint8_t*>(ws + L.hsc);
+    if ((e = lmoe::launch_quant_mxfp8(rows ? x : z, T, int(l), zq, zs, s)) != hipSuccess)
+      return hip_fail(e, "quantise expert inputs");
+    lmoe::GroupedMx m1{};
+    m1.N = int(I);
+    m1.K = int(l);
+    m1.A = zq;
+    m1.As = zs;
+    m1.a_rows = p->sorted_row;
+    m1.a_row_div = p->k;
+    m1.B = static_cast<const uint8_t*>(a->w1);
+    m1.Bs = a->s1;
+    m1.B3 = static_cast<const uint8_t*>(a->w3);
+    m1.B3s = a->s3;
+    m1.gated = true;
+    m1.C = H;
+    m1.ldc = I;
+    m1.tiles = p->tiles_t;
+    m1.ntiles = p->n_t;
+    m1.max_tiles = p->max_t;
+    if ((e = lmoe::launch_grouped_mx(m1, s)) != hipSuccess) return hip_fail(e, "expert FC1 (MXFP4)");
+    if ((e = mark(3)) != hipSuccess) return hip_fail(e, "event");
+    if ((e = lmoe::launch_quant_mxfp8(H, R, int(I), hq, hsc, s)) != hipSuccess)
+      return hip_fail(e, "quantise FC1 output");
+    lmoe::GroupedMx m2 = m1;
+    m2.N = int(l);
+    m2.K = int(I);
+    m2.A = hq;
+    m2.As = hsc;
+    m2.a_rows = nullptr;
+    m2.a_row_div = 1;
+    m2.B = static_cast<const uint8_t*>(a->w2);
+    m2.Bs = a->s2;
+    m2.B3 = nullptr;
+    m2.B3s = nullptr;
+    m2.gated = false;
+    m2.C = Y;
+    m2.ldc = l;
+    if ((e = lmoe::launch_grouped_mx(m2, s)) != hipSuccess) return hip_fail(e, "expert FC2 (MXFP4)");
+    if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
+  } else {
+    const bool skinny = R <= int64_t(32) * p->E;
+    lmoe::GroupedGemm f1{};
+    f1.N = int(I);
+    f1.K = int(l);
+    f1.A = rows ? x : z;
+    f1.lda = l;
+    f1.a_rows = p->sorted_row;
+    f1.a_row_div = p->k;
+    f1.B = static_cast<const uint16_t*>(a->w1);
+    f1.B3 = static_cast<const uint16_t*>(a->w3);
+    f1.ldb = l;
+    f1.b_estride = I * l;
+    f1.gated = true;
+    f1.C = H;
+    f1.ldc = I;
+    f1.tiles = skinny ? p->tiles_s : p->tiles_t;
+    f1.ntiles = skinny ? p->n_s : p->n_t;
+    f1.max_tiles = skinny ? p->max_s : p->max_t;
+    e = skinny ? lmoe::launch_grouped_skinny(f1, s) : lmoe::launch_grouped_tiled(f1, s);
+    if (e != hipSuccess) return hip_fail(e, "expert FC1");
+    if ((e = mark(3)) != hipSuccess) return hip_fail(e, "event");
 
-  lmoe::GroupedGemm f2 = f1;
-  f2.N = int(l);
-  f2.K = int(I);
-  f2.A = H;
-  f2.lda = I;
-  f2.a_rows = nullptr;
-  f2.a_row_div = 1;
-  f2.B = static_cast<const uint16_t*>(a->w2);
-  f2.B3 = nullptr;
-  f2.ldb = I;
-  f2.b_estride = l * I;
-  f2.gated = false;
-  f2.C = Y;
-  f2.ldc = l;
-  e = skinny ? lmoe::launch_grouped_skinny(f2, s) : lmoe::launch_grouped_tiled(f2, s);
-  if (e != hipSuccess) return hip_fail(e, "expert FC2");
-  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
+    lmoe::GroupedGemm f2 = f1;
+    f2.N = int(l);
+    f2.K = int(I);
+    f2.A = H;
+    f2.lda = I;
+    f2.a_rows = nullptr;
+    f2.a_row_div = 1;
+    f2.B = static_cast<const uint16_t*>(a->w2);
+    f2.B3 = nullptr;
+    f2.ldb = I;
+    f2.b_estride = l * I;
+    f2.gated = false;
+    f2.C = Y;
+    f2.ldc = l;
+    e = skinny ? lmoe::launch_grouped_skinny(f2, s) : lmoe::launch_grouped_tiled(f2, s);
+    if (e != hipSuccess) return hip_fail(e, "expert FC2");
+    if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
+  }
 
   // 4. weighted combine (+ RMSNorm); rows mode writes the weighted rows out
   if (rows) {

@@ -22,7 +22,7 @@ namespace lmoe {
 namespace {
 
 constexpr int kBK = 64;          // K per LDS stage
-constexpr int kLdsK = kBK + 8;   // padded LDS row (bf16): 144 B, conflict-free 16 B reads
+constexpr int kLdsK = kBK + 8;   // padded LDS row (bf16): 144 B
 
 struct TiledArgs {
   int M, N;
@@ -40,25 +40,39 @@ struct TiledArgs {
 
 __device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATED, bool GROUPED>
-__global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void tiled_gemm_kernel(TiledArgs g) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int BNT = GATED ? 2 * BN : BN;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int CPR = kBK / 8;                 // 16-byte chunks per row per stage
-  constexpr int A_CH = BM * CPR / NT;
-  constexpr int B_CH = BNT * CPR / NT;
-  static_assert(BM * CPR % NT == 0 && BNT * CPR % NT == 0, "tile/threads mismatch");
-  static_assert(FM >= 1 && FN >= 1, "wave tile too small");
+// 32x32x16 bf16 MFMA: D(32x32 f32) = A(32x16) * B(16x32) + C.  Lane l feeds A
+// row l%32 and B column l%32 with K elements 8*(l/32) .. +8; it receives
+// column l%32 of rows 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Macro tile: 256 rows x 256 B rows (plain: 256 output columns; gated: 128
+// gate + 128 up rows -> 128 output columns), K staged 64 at a time through a
+// double-buffered LDS (2 x 72 KB).  4 waves; WAVES_M x (4/WAVES_M) layout:
+//  * WAVES_M = 4: wave tile 64 x 256, so a grouped tile with few rows leaves
+//    whole waves idle (they skip their MFMAs but still help load) -- an
+//    expert's up-to-256 rows read its weights once;
+//  * WAVES_M = 2: wave tile 128 x 128, less LDS traffic for dense GEMMs.
+// Each wave keeps 16 32x32 accumulators (256 fp32 per lane).  Partial N tiles
+// clamp their B rows and mask their stores.
+template <int WAVES_M, bool GATED, bool GROUPED>
+__global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(TiledArgs g) {
+  constexpr int BM = 256, BR = 256;                 // A rows, B rows per tile
+  constexpr int NOUT = GATED ? 128 : 256;           // output columns per tile
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BR / WAVES_N;
+  constexpr int FM = WM / 32, FN = WN / 32;         // 32x32 subtiles per wave
+  constexpr int CPR = kBK / 8;                      // 16-byte chunks per row
+  constexpr int A_CH = BM * CPR / 256, B_CH = BR * CPR / 256;
 
   extern __shared__ uint4 lds_u4[];
   bf16_t* As = reinterpret_cast<bf16_t*>(lds_u4);  // [2][BM][kLdsK]
-  bf16_t* Bs = As + 2 * BM * kLdsK;                 // [2][BNT][kLdsK]
+  bf16_t* Bs = As + 2 * BM * kLdsK;                 // [2][BR][kLdsK]
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
-  const int tiles_n = g.N / BN;
+  const int tiles_n = (g.N + NOUT - 1) / NOUT;
   const uint32_t lt = xcd_swizzle(blockIdx.x, gridDim.x);
   const int tn = int(lt % uint32_t(tiles_n));
   const int tm = int(lt / uint32_t(tiles_n));
@@ -73,17 +87,25 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void tiled_gemm_kernel(Tiled
     row0 = tm * BM;
     nrows = min(BM, g.M - row0);
   }
-  const int n0 = tn * BN;
+  const int n0 = tn * NOUT;
+  const bool active = wm * WM < nrows;  // this wave has rows to compute
 
-  f32x4 acc[FM][FN];
-  f32x4 acc3[GATED ? FM : 1][GATED ? FN : 1];
+  // B-tile row of this wave's n-subtile j (gated: first half gate, second up)
+  auto brow = [&](int j) -> int {
+    if constexpr (GATED) {
+      return j < FN / 2 ? wn * (WN / 2) + j * 32 : BR / 2 + wn * (WN / 2) + (j - FN / 2) * 32;
+    } else {
+      return wn * WN + j * 32;
+    }
+  };
+
+  f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (GATED) acc3[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   for (int s = 0; s < g.nseg; ++s) {
     const GemmSeg sg = g.seg[s];
@@ -91,9 +113,8 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void tiled_gemm_kernel(Tiled
     const bf16_t* bp[B_CH];
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * NT, r = c / CPR, kc = c % CPR;
-      const int rr = min(r, nrows - 1);
-      int64_t src = int64_t(row0) + rr;
+      const int c = tid + i * 256, r = c / CPR, kc = c % CPR;
+      int64_t src = int64_t(row0) + min(r, nrows - 1);
       if constexpr (GROUPED) {
         if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
       }
@@ -101,10 +122,10 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void tiled_gemm_kernel(Tiled
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NT, r = c / CPR, kc = c % CPR;
-      const bf16_t* base = (GATED && r >= BN) ? sg.B3 : sg.B;
-      const int rn = (GATED && r >= BN) ? r - BN : r;
-      bp[i] = base + int64_t(expert) * g.b_estride + int64_t(n0 + rn) * sg.ldb + kc * 8;
+      const int c = tid + i * 256, r = c / CPR, kc = c % CPR;
+      const bool up = GATED && r >= BR / 2;
+      const int rn = min(n0 + (up ? r - BR / 2 : r), g.N - 1);
+      bp[i] = (up ? sg.B3 : sg.B) + int64_t(expert) * g.b_estride + int64_t(rn) * sg.ldb + kc * 8;
     }
     const int nk = sg.K / kBK;
     uint4 ra[A_CH], rb[B_CH];
@@ -114,12 +135,12 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void tiled_gemm_kernel(Tiled
     for (int i = 0; i < B_CH; ++i) rb[i] = ldg16(bp[i]);
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * NT;
+      const int c = tid + i * 256;
       *reinterpret_cast<uint4*>(&As[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NT;
+      const int c = tid + i * 256;
       *reinterpret_cast<uint4*>(&Bs[(c / CPR) * kLdsK + (c % CPR) * 8]) = rb[i];
     }
     __syncthreads();
@@ -133,44 +154,36 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void tiled_gemm_kernel(Tiled
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) rb[i] = ldg16(bp[i] + koff);
       }
-      const bf16_t* Ab = As + buf * BM * kLdsK;
-      const bf16_t* Bb = Bs + buf * BNT * kLdsK;
+      if (active) {
+        const bf16_t* Ab = As + buf * BM * kLdsK;
+        const bf16_t* Bb = Bs + buf * BR * kLdsK;
 #pragma unroll
-      for (int ks = 0; ks < kBK / 32; ++ks) {
-        const int kof = ks * 32 + (lane >> 4) * 8;
-        bf16x8 af[FM], bf[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ab[(wm * WM + i * 16 + (lane & 15)) * kLdsK + kof]));
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bf[j] = as_bf16x8(*reinterpret_cast<const uint4*>(&Bb[(wn * WN + j * 16 + (lane & 15)) * kLdsK + kof]));
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
-        if constexpr (GATED) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            bf[j] = as_bf16x8(
-                *reinterpret_cast<const uint4*>(&Bb[(BN + wn * WN + j * 16 + (lane & 15)) * kLdsK + kof]));
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+          const int kof = ks * 16 + (lane >> 5) * 8;
+          bf16x8 af[FM];
 #pragma unroll
           for (int i = 0; i < FM; ++i)
+            af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ab[(wm * WM + i * 32 + (lane & 31)) * kLdsK + kof]));
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc3[i][j] = mfma_16x16x32(af[i], bf[j], acc3[i][j]);
+          for (int j = 0; j < FN; ++j) {
+            const bf16x8 bf =
+                as_bf16x8(*reinterpret_cast<const uint4*>(&Bb[(brow(j) + (lane & 31)) * kLdsK + kof]));
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[i][j] = mfma_32x32x16(af[i], bf, acc[i][j]);
+          }
         }
       }
       if (kt + 1 < nk) {
         bf16_t* An = As + (buf ^ 1) * BM * kLdsK;
-        bf16_t* Bn = Bs + (buf ^ 1) * BNT * kLdsK;
+        bf16_t* Bn = Bs + (buf ^ 1) * BR * kLdsK;
 #pragma unroll
         for (int i = 0; i < A_CH; ++i) {
-          const int c = tid + i * NT;
+          const int c = tid + i * 256;
           *reinterpret_cast<uint4*>(&An[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) {
-          const int c = tid + i * NT;
+          const int c = tid + i * 256;
           *reinterpret_cast<uint4*>(&Bn[(c / CPR) * kLdsK + (c % CPR) * 8]) = rb[i];
         }
       }
@@ -179,46 +192,50 @@ __global__ __launch_bounds__(64 * WAVES_M* WAVES_N) void tiled_gemm_kernel(Tiled
   }
 
   // Epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores.
-  constexpr int CLD = BN + 8;
-  bf16_t* Cs = As;  // BM * CLD <= 2 * (BM + BNT) * kLdsK
+  constexpr int CLD = NOUT + 8;
+  static_assert(BM * CLD <= 2 * (BM + BR) * kLdsK, "epilogue staging fits in the LDS buffers");
+  bf16_t* Cs = As;
+  if (active) {
+    constexpr int JO = GATED ? FN / 2 : FN;       // output subtiles per wave
+    constexpr int WO = GATED ? WN / 2 : WN;       // output columns per wave
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < JO; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wm * WM + i * 16 + (lane >> 4) * 4 + r;
-        const int col = wn * WN + j * 16 + (lane & 15);
-        float v = acc[i][j][r];
-        if constexpr (GATED) v = silu_mul(v, acc3[i][j][r]);
-        Cs[row * CLD + col] = f32_to_bf16(v);
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int col = wn * WO + j * 32 + (lane & 31);
+          float x = acc[i][j][v];
+          if constexpr (GATED) x = silu_mul(x, acc[i][j + FN / 2][v]);
+          Cs[row * CLD + col] = f32_to_bf16(x);
+        }
+  }
   __syncthreads();
-  constexpr int OCPR = BN / 8;
-  for (int c = tid; c < BM * OCPR; c += NT) {
+  constexpr int OCPR = NOUT / 8;
+  for (int c = tid; c < BM * OCPR; c += 256) {
     const int row = c / OCPR, cc = c % OCPR;
-    if (row < nrows) {
+    if (row < nrows && n0 + cc * 8 < g.N) {
       *reinterpret_cast<uint4*>(g.C + (int64_t(row0) + row) * g.ldc + n0 + cc * 8) =
           *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
     }
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATED, bool GROUPED>
+template <int WAVES_M, bool GATED, bool GROUPED>
 hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s) {
-  constexpr int BNT = GATED ? 2 * BN : BN;
-  const size_t lds = size_t(2) * (BM + BNT) * kLdsK * sizeof(bf16_t);
-  static_assert(size_t(BM) * (BN + 8) <= size_t(2) * (BM + BNT) * kLdsK, "epilogue staging fits");
-  auto kern = tiled_gemm_kernel<BM, BN, WAVES_M, WAVES_N, GATED, GROUPED>;
+  constexpr int NOUT = GATED ? 128 : 256;
+  const size_t lds = size_t(2) * (256 + 256) * kLdsK * sizeof(bf16_t);
+  auto kern = tiled_gemm_kernel<WAVES_M, GATED, GROUPED>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int64_t nblk = mtiles * (a.N / BN);
+  const int64_t nblk = mtiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
-  kern<<<dim3(uint32_t(nblk)), dim3(64 * WAVES_M * WAVES_N), lds, s>>>(a);
+  kern<<<dim3{uint32_t(nblk)}, dim3{256}, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -434,11 +451,9 @@ hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
   a.b_estride = 0;
   a.C = d.C;
   a.ldc = d.ldc;
-  constexpr int BM = 128;
-  const int64_t mt = (d.M + BM - 1) / BM;
-  if (d.gated) return run_tiled<BM, 64, 2, 2, true, false>(a, mt, s);
-  if (d.N % 128 == 0) return run_tiled<BM, 128, 2, 2, false, false>(a, mt, s);
-  return run_tiled<BM, 64, 2, 2, false, false>(a, mt, s);
+  const int64_t mt = (d.M + 255) / 256;
+  if (d.gated) return run_tiled<2, true, false>(a, mt, s);
+  return run_tiled<2, false, false>(a, mt, s);
 }
 
 hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s) {
@@ -454,10 +469,9 @@ hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s) {
   a.ntiles = g.ntiles;
   a.C = g.C;
   a.ldc = g.ldc;
-  static_assert(kTiledBM == 128, "tile table granularity");
-  if (g.gated) return run_tiled<128, 64, 2, 2, true, true>(a, g.max_tiles, s);
-  if (g.N % 128 == 0) return run_tiled<128, 128, 2, 2, false, true>(a, g.max_tiles, s);
-  return run_tiled<128, 64, 2, 2, false, true>(a, g.max_tiles, s);
+  static_assert(kTiledBM == 256, "tile table granularity");
+  if (g.gated) return run_tiled<4, true, true>(a, g.max_tiles, s);
+  return run_tiled<4, false, true>(a, g.max_tiles, s);
 }
 
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s) {

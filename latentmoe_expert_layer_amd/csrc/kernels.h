@@ -17,7 +17,7 @@ struct Tile {
 
 // Row-tile granularities of the tile tables that routing builds.
 constexpr int kSkinnyBM = 16;   // weight-streaming (decode-shaped) kernel
-constexpr int kTiledBM = 128;   // LDS-tiled (prefill-shaped) kernel
+constexpr int kTiledBM = 256;   // LDS-tiled (prefill-shaped) kernel
 
 inline int64_t max_tiles(int64_t rows, int64_t E, int bm) {
   return rows / bm + (rows < E ? rows : E) + 1;
@@ -83,6 +83,32 @@ struct GroupedGemm {
 };
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s);
+
+// ---- MXFP4 (w4a8) expert path ------------------------------------------------
+// bf16 [rows, K] -> MXFP8 e4m3 codes [rows, K] + e8m0 scales [rows, K/32].
+hipError_t launch_quant_mxfp8(const uint16_t* src, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+// Grouped block-scaled GEMM: MXFP8 activations (rows gathered as in
+// GroupedGemm) x MXFP4 weights [E, N, K/2] with scales [E, N, K/32]; bf16
+// output (gated: SwiGLU of gate and up).  Tiles from the 256-row table.
+struct GroupedMx {
+  int N, K;
+  const uint8_t* A;
+  const uint8_t* As;
+  const int32_t* a_rows;
+  int a_row_div;
+  const uint8_t* B;
+  const uint8_t* Bs;
+  const uint8_t* B3;
+  const uint8_t* B3s;
+  bool gated;
+  uint16_t* C;
+  int64_t ldc;
+  const Tile* tiles;
+  const int32_t* ntiles;
+  int64_t max_tiles;
+};
+hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s);
 
 // ---- combine ----------------------------------------------------------------
 // out[t] = bf16(RMSNorm(sum_j w[t,j] Y[row_pos[t*k+j]]))   (norm skipped if gain == NULL)

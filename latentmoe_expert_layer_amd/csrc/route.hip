@@ -42,32 +42,51 @@ __device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROW_MASK, 0xf, false));
 }
 
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
-  const uint32_t lo = dpp_move<CTRL, ROW_MASK>(uint32_t(v));
-  const uint32_t hi = dpp_move<CTRL, ROW_MASK>(uint32_t(v >> 32));
-  const uint64_t o = (uint64_t(hi) << 32) | lo;
-  return o > v ? o : v;
+// Wave-wide max of an unsigned 32-bit value with DPP row operations:
+// butterflies inside each quad, shifts inside each 16-lane row, then the row
+// broadcasts; the maximum ends in lane 63 and is returned wave-uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_move<0xb1>(v));        // quad_perm [1,0,3,2]
+  v = max(v, dpp_move<0x4e>(v));        // quad_perm [2,3,0,1]
+  v = max(v, dpp_move<0x114>(v));       // row_shr:4
+  v = max(v, dpp_move<0x118>(v));       // row_shr:8
+  v = max(v, dpp_move<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
+  v = max(v, dpp_move<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
 }
 
-// Wave-wide max of a 64-bit key with DPP row operations: butterflies inside
-// each quad, shifts inside each 16-lane row, then the row broadcasts; the
-// full maximum ends in lane 63 and is read back as a wave-uniform value.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = dpp_max_step<0xb1>(v);        // quad_perm [1,0,3,2]
-  v = dpp_max_step<0x4e>(v);        // quad_perm [2,3,0,1]
-  v = dpp_max_step<0x114>(v);       // row_shr:4
-  v = dpp_max_step<0x118>(v);       // row_shr:8
-  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), 63));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63));
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), lane));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), lane));
   return (uint64_t(hi) << 32) | lo;
 }
 
+// In-register bitonic sort of N keys, descending (N a power of two; all
+// indices are compile-time constants, so the keys stay in registers).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&a)[N]) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int p = i ^ j;
+        if (p > i) {
+          const bool desc = (i & k) == 0;
+          const uint64_t x = a[i], y = a[p];
+          const bool swap = desc ? (x < y) : (x > y);
+          a[i] = swap ? y : x;
+          a[p] = swap ? x : y;
+        }
+      }
+}
+
 // One wave per token; lane l holds logits e = l + 64*j (coalesced rows).
-// k rounds: a wave-wide max of the lanes' current best keys picks the next
-// expert; only the owning lane rescans its VPL candidates.
+// Each lane sorts its VPL keys once; then each of the k rounds takes the
+// wave-wide maximum of the lanes' current heads: a 32-bit max of the value
+// word, and only when several lanes tie on it, a second max of the index
+// word.  The winning lane pops its head.
 template <int VPL>
 __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                      int k, int32_t* __restrict__ ids,
@@ -87,21 +106,26 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
     const int e = lane + 64 * j;
     cand[j] = (e < E) ? rank_key(v[j], uint32_t(e)) : 0ull;
   }
-  uint64_t best = 0;
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) best = cand[j] > best ? cand[j] : best;
+  sort_desc<VPL>(cand);
 
   uint64_t mine = 0;  // lane i keeps the i-th selected key
   for (int i = 0; i < k; ++i) {
-    const uint64_t top = wave_max_u64(best);
+    const uint64_t head = cand[0];
+    const uint32_t hi = uint32_t(head >> 32);
+    const uint32_t mh = wave_max_u32(hi);
+    uint64_t tied = ballot(hi == mh);
+    if (__popcll(tied) > 1) {  // equal values on several lanes: lowest index wins
+      const uint32_t lo = (hi == mh) ? uint32_t(head) : 0u;
+      const uint32_t ml = wave_max_u32(lo);
+      tied = ballot(hi == mh && uint32_t(head) == ml);
+    }
+    const int winner = __ffsll(static_cast<unsigned long long>(tied)) - 1;
+    const uint64_t top = readlane_u64(head, winner);
     if (lane == i) mine = top;
-    if (best == top) {
-      best = 0;
+    if (lane == winner) {
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) {
-        if (cand[j] == top) cand[j] = 0;
-        best = cand[j] > best ? cand[j] : best;
-      }
+      for (int j = 0; j + 1 < VPL; ++j) cand[j] = cand[j + 1];
+      cand[VPL - 1] = 0;
     }
   }
   const float lv = key_value(mine);

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.parity import assert_parity, log, poison_, to_device, to_host
+from tests.parity import assert_parity, assert_rowwise, log, poison_, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -195,3 +195,79 @@ def test_layer_full_size_sampled(name):
                   | set(range(37, cfg.T, 997)))
     ref = oracle.layer(inp, ids_ref, w_ref, eval_tokens=pick)["y"]
     assert_parity(y.cpu()[pick], ref)
+
+
+def test_graph_replay_matches_eager():
+    """route + forward captured in a HIP graph: every replay (with eager work
+    and synchronisations in between) equals the eager result bit for bit."""
+    cfg = W.CONFIGS["decode"]
+    inp = to_device(W.make_inputs(cfg))
+    _, y_ref = run_gpu_layer(inp)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    rws = torch.empty(lm.route_workspace_size(T, E, k), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(lm.forward_workspace_size(T, E, k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is),
+                      dtype=torch.uint8, device="cuda")
+    bufs = dict(ids=torch.empty(T, k, dtype=torch.int32, device="cuda"),
+                w=torch.empty(T, k, dtype=torch.float32, device="cuda"),
+                srow=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+                rpos=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+                off=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                y=torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda"))
+    P = lambda t: None if t is None else t.data_ptr()
+    ra = lm.RouteArgs(T=T, E=E, k=k, logits=P(inp["logits"]), topk_ids=P(bufs["ids"]), topk_w=P(bufs["w"]),
+                      sorted_row=P(bufs["srow"]), row_pos=P(bufs["rpos"]), offsets=P(bufs["off"]),
+                      workspace=P(rws), workspace_bytes=rws.numel())
+    fa = lm.ForwardArgs(d=cfg.d, l=cfg.l, I=cfg.I, S=cfg.S, Is=cfg.Is, wfmt=0, norm_eps=cfg.eps,
+                        x=P(inp["x"]), w_in=P(inp["w_in"]), w1=P(inp["w1"]), w3=P(inp["w3"]), w2=P(inp["w2"]),
+                        norm_w=P(inp["norm_w"]), w_out=P(inp["w_out"]), ws1=P(inp["ws1"]), ws3=P(inp["ws3"]),
+                        ws2=P(inp["ws2"]), y=P(bufs["y"]), workspace=P(fws), workspace_bytes=fws.numel())
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        s = torch.cuda.current_stream().cuda_stream
+        plan = lm.latent_moe_route(ra, s)
+        lm.latent_moe_forward(plan, fa, s)
+        lm.latent_moe_free(plan)
+    for rep in range(3):
+        poison_(fws)
+        poison_(bufs["y"])
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["y"].view(torch.int16), y_ref.view(torch.int16)), f"replay {rep} differs"
+        del junk
+
+
+MX_LAYERS = [
+    ("mx_small", dict(T=203, d=192, l=256, E=9, k=3, S=1, I=128, Is=64, mxfp4=True)),
+    ("mx_ragged", dict(T=77, d=128, l=384, E=40, k=8, S=2, I=256, Is=64, mxfp4=True)),
+    ("mx_heavy", dict(T=700, d=256, l=128, E=4, k=2, S=0, I=384, Is=0, mxfp4=True)),
+]
+
+
+@pytest.mark.parametrize("name,dims", MX_LAYERS, ids=[n for n, _ in MX_LAYERS])
+def test_mxfp4_layer_parity_small(name, dims):
+    """w4a8: MXFP8 activations x MXFP4 weights vs an oracle with the same
+    dequantised weights and the same activation quantisation (5e-2)."""
+    cfg = W.custom(name, **dims)
+    log(f"mxfp4 layer {name}: {cfg}")
+    inp = W.make_inputs(cfg)
+    ref = oracle.run(inp, act_quant=True)
+    r, y = run_gpu_layer(to_device(inp))
+    check_routing(r, inp["logits"], cfg.k, cfg.E)
+    assert_rowwise(y.cpu(), ref["y"])
+
+
+def test_mxfp4_full_size_sampled():
+    cfg = W.CONFIGS["prefill_mxfp4"]
+    log(f"full-size {cfg.name}: {cfg}")
+    inp_dev = W.make_inputs(cfg, device="cuda")
+    r, y = run_gpu_layer(inp_dev)
+    ids_ref, w_ref = check_routing(r, inp_dev["logits"], cfg.k, cfg.E)
+    inp = to_host(inp_dev)
+    del inp_dev
+    pick = sorted({0, cfg.T - 1} | set(range(0, cfg.T, 2048)) | set(range(2047, cfg.T, 2048))
+                  | set(range(101, cfg.T, 1999)))
+    ref = oracle.layer(inp, ids_ref, w_ref, eval_tokens=pick, act_quant=True)["y"]
+    assert_rowwise(y.cpu()[pick], ref)

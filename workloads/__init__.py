@@ -133,18 +133,27 @@ _E2M1_CODE_PROBS = [0.08, 0.15, 0.15, 0.14, 0.13, 0.20, 0.10, 0.05]
 def mxfp4_weights(seed, name, E, N, K, device="cpu"):
     """Random MXFP4 weight matrix [E,N,K]: packed e2m1 codes [E,N,K/2] (even K in
     the low nibble) and e8m0 scales [E,N,K/32] around 2^-7 (codes 119..121), so
-    the dequantised values have a spread near N(0, 0.02)."""
+    the dequantised values have a spread near N(0, 0.02).  Codes are drawn by
+    inverting the categorical CDF on uniform draws, in chunks."""
     assert K % 32 == 0
-    g = _gen(seed, name + ".codes", "cpu")
-    mag = torch.multinomial(torch.tensor(_E2M1_CODE_PROBS), E * N * K, replacement=True,
-                            generator=g).to(torch.uint8)
-    sign = torch.randint(0, 2, (E * N * K,), generator=g, dtype=torch.uint8) << 3
-    codes = (mag | sign).view(E, N, K // 2, 2)
-    packed = (codes[..., 0] | (codes[..., 1] << 4)).contiguous()
-    gs = _gen(seed, name + ".scales", "cpu")
-    scales = (119 + torch.multinomial(torch.tensor([0.25, 0.5, 0.25]), E * N * (K // 32),
-                                      replacement=True, generator=gs)).to(torch.uint8)
-    return packed.to(device), scales.view(E, N, K // 32).contiguous().to(device)
+    cdf = torch.tensor(_E2M1_CODE_PROBS, dtype=torch.float64).cumsum(0)
+    cdf = (cdf / cdf[-1]).to(torch.float32).to(device)
+    g = _gen(seed, name + ".codes", device)
+    nbytes = E * N * K // 2
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    chunk = 1 << 25
+    for b0 in range(0, nbytes, chunk):
+        n = min(chunk, nbytes - b0)
+        u = torch.rand(2 * n, generator=g, device=device)
+        mag = torch.searchsorted(cdf, u, right=True).clamp_(max=7).to(torch.uint8)
+        sign = (torch.rand(2 * n, generator=g, device=device) < 0.5).to(torch.uint8) << 3
+        codes = (mag | sign).view(n, 2)
+        packed[b0:b0 + n] = codes[:, 0] | (codes[:, 1] << 4)
+    gs = _gen(seed, name + ".scales", device)
+    scdf = torch.tensor([0.25, 0.75], dtype=torch.float32, device=device)
+    us = torch.rand(E * N * (K // 32), generator=gs, device=device)
+    scales = (119 + torch.searchsorted(scdf, us, right=True)).to(torch.uint8)
+    return packed.view(E, N, K // 2), scales.view(E, N, K // 32)
 
 
 def make_inputs(cfg: LayerConfig, device="cpu", norm_w: Optional[str] = None) -> dict:
