@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the w4a8 expert GEMMs issue at the fp8 rate)
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 METRIC = "LatentMoE layer tokens/s at 1 GPU; grouped-GEMM TFLOP/s as % MFMA peak"
 
@@ -94,23 +95,29 @@ def measured_traffic(kernel, workload, src_hash):
 
 
 def cpu_baseline(cfg, inp_host, budget_s):
-    """The oracle (as it stands) on this host's cores: whole route + layer
-    passes over the same workload until the budget is used."""
+    """The oracle (as it stands) on this host's cores: routing and permutation
+    of the whole batch, then the layer on consecutive token chunks (the whole
+    batch at a time when it has <= 256 tokens) until the budget is used."""
     import oracle
-    import torch
     cores = oracle.num_threads()
-    # sample: whole batches; the oracle's route and layer over all T tokens
-    done, t0 = 0, time.perf_counter()
+    t0 = time.perf_counter()
+    if cfg.rows_mode:
+        ids, w = inp_host["ids"], inp_host["weights"]
+    else:
+        ids, w = oracle.route(inp_host["logits"], cfg.k)
+    oracle.permute(ids, cfg.E)
+    chunk = min(cfg.T, 256)
+    done = 0
     while True:
-        out = oracle.run(inp_host)
-        done += 1
+        toks = [(done + i) % cfg.T for i in range(chunk)]
+        oracle.layer(inp_host, ids, w, eval_tokens=toks)
+        done += chunk
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 50:
+        if el >= budget_s or done >= 50 * cfg.T:
             break
-    del out, torch
-    return {"value": done * cfg.T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} full route+forward pass(es) of the {cfg.name} batch ({cfg.T} tokens) "
-                      f"in {el:.1f} s"}
+    return {"value": done / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"route + permute of the whole {cfg.name} batch ({cfg.T} tokens), then the layer on "
+                      f"{done} tokens in chunks of {chunk}, {el:.1f} s in total"}
 
 
 def main():
@@ -127,35 +134,43 @@ def main():
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
     cfg = W.CONFIGS[args.workload]
-    if cfg.rows_mode or cfg.mxfp4:
-        raise SystemExit("bench workloads: tiny, decode, prefill")
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
 
     # ---------------- inputs: several resident copies, distinct seeds
-    wbytes = 3 * cfg.E * cfg.I * cfg.l * 2
-    copies = args.copies or max(2, min(8, -(-2 * LLC_BYTES // max(wbytes, 1))))
+    wbytes = (3 * cfg.E * cfg.I * cfg.l) * (0.53 if cfg.mxfp4 else 2)
+    copies = args.copies or max(2, min(8, -(-2 * LLC_BYTES // max(int(wbytes), 1))))
+    wfmt = lm.LMOE_WFMT_MXFP4 if cfg.mxfp4 else lm.LMOE_WFMT_BF16
+    P = lambda t: None if t is None else t.data_ptr()
     sets = []
     for c in range(copies):
         inp = W.make_inputs(W.LayerConfig(**{**cfg.__dict__, "seed": c}), device="cuda")
         T, E, k = cfg.T, cfg.E, cfg.k
         R = T * k
         rws = torch.empty(lm.route_workspace_size(T, E, k), dtype=torch.uint8, device="cuda")
-        fws = torch.empty(lm.forward_workspace_size(T, E, k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is),
-                          dtype=torch.uint8, device="cuda")
+        fws = torch.empty(max(256, lm.forward_workspace_size(T, E, k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is, wfmt,
+                                                            cfg.rows_mode)), dtype=torch.uint8, device="cuda")
         out = dict(topk_ids=torch.empty(T, k, dtype=torch.int32, device="cuda"),
                    topk_w=torch.empty(T, k, dtype=torch.float32, device="cuda"),
                    sorted_row=torch.empty(R, dtype=torch.int32, device="cuda"),
                    row_pos=torch.empty(R, dtype=torch.int32, device="cuda"),
                    offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
-                   y=torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda"))
-        P = lambda t: None if t is None else t.data_ptr()
-        ra = lm.RouteArgs(T=T, E=E, k=k, logits=P(inp["logits"]), topk_ids=P(out["topk_ids"]),
-                          topk_w=P(out["topk_w"]), sorted_row=P(out["sorted_row"]), row_pos=P(out["row_pos"]),
-                          offsets=P(out["offsets"]), workspace=P(rws), workspace_bytes=rws.numel())
-        fa = lm.ForwardArgs(d=cfg.d, l=cfg.l, I=cfg.I, S=cfg.S, Is=cfg.Is, wfmt=0, norm_eps=cfg.eps,
-                            x=P(inp["x"]), w_in=P(inp["w_in"]), w1=P(inp["w1"]), w3=P(inp["w3"]),
-                            w2=P(inp["w2"]), norm_w=P(inp.get("norm_w")), w_out=P(inp["w_out"]),
+                   y=torch.empty(T, cfg.l if cfg.rows_mode else cfg.d, dtype=torch.bfloat16, device="cuda"))
+        if cfg.rows_mode:
+            ra = lm.RouteArgs(T=T, E=E, k=k, ids_in=P(inp["ids"]), weights_in=P(inp["weights"]),
+                              sorted_row=P(out["sorted_row"]), row_pos=P(out["row_pos"]),
+                              offsets=P(out["offsets"]), workspace=P(rws), workspace_bytes=rws.numel())
+        else:
+            ra = lm.RouteArgs(T=T, E=E, k=k, logits=P(inp["logits"]), topk_ids=P(out["topk_ids"]),
+                              topk_w=P(out["topk_w"]), sorted_row=P(out["sorted_row"]),
+                              row_pos=P(out["row_pos"]), offsets=P(out["offsets"]), workspace=P(rws),
+                              workspace_bytes=rws.numel())
+        mx = cfg.mxfp4
+        fa = lm.ForwardArgs(d=cfg.d, l=cfg.l, I=cfg.I, S=cfg.S, Is=cfg.Is, wfmt=wfmt, norm_eps=cfg.eps,
+                            x=P(inp["x"]), w_in=P(inp.get("w_in")), w1=P(inp["w1q" if mx else "w1"]),
+                            w3=P(inp["w3q" if mx else "w3"]), w2=P(inp["w2q" if mx else "w2"]),
+                            s1=P(inp.get("s1")), s3=P(inp.get("s3")), s2=P(inp.get("s2")),
+                            norm_w=P(inp.get("norm_w")), w_out=P(inp.get("w_out")),
                             ws1=P(inp.get("ws1")), ws3=P(inp.get("ws3")), ws2=P(inp.get("ws2")),
                             y=P(out["y"]), workspace=P(fws), workspace_bytes=fws.numel())
         sets.append(dict(inp=inp, rws=rws, fws=fws, out=out, ra=ra, fa=fa))
@@ -242,13 +257,14 @@ def main():
     T, E, k, d, l, I, S, Is = cfg.T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is
     R = T * k
     touched = sum(int(((s["out"]["offsets"][1:] - s["out"]["offsets"][:-1]) > 0).sum()) for s in sets) / copies
-    fc1_bytes = touched * 2 * I * l * 2 + T * l * 2 + R * I * 2
-    fc2_bytes = touched * l * I * 2 + R * I * 2 + R * l * 2
+    wb = 0.5 + 1 / 32 if cfg.mxfp4 else 2        # bytes per expert weight element (MXFP4: code + scale share)
+    fc1_bytes = touched * 2 * I * l * wb + T * l * 2 + R * I * 2
+    fc2_bytes = touched * l * I * wb + R * I * 2 + R * l * 2
     fc1_flop = 2.0 * R * l * 2 * I
     fc2_flop = 2.0 * R * I * l
-    dense_flop = 2.0 * T * d * (l + 2 * S * Is) + 2.0 * T * (l + S * Is) * d
+    dense_flop = 0.0 if cfg.rows_mode else 2.0 * T * d * (l + 2 * S * Is) + 2.0 * T * (l + S * Is) * d
     layer_flop = fc1_flop + fc2_flop + dense_flop
-    dense_bytes = 2 * (T * d + (l + 2 * S * Is) * d + T * l + T * S * Is + d * (l + S * Is) + T * d)
+    dense_bytes = 0 if cfg.rows_mode else 2 * (T * d + (l + 2 * S * Is) * d + T * l + T * S * Is + d * (l + S * Is) + T * d)
     route_bytes = T * E * 4 + R * (4 + 4 + 4 + 4 + 4)
     combine_bytes = R * l * 2 + T * l * 2 + R * 8
     layer_bytes = fc1_bytes + fc2_bytes + dense_bytes + route_bytes + combine_bytes
@@ -260,7 +276,8 @@ def main():
         dom_flop = fc1_flop if dom == "fc1" else fc2_flop
         dur_s = stages[dom] / 1e6
         ai = dom_flop / dom_bytes
-        bound = "hbm" if ai < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+        mfma_peak = FP8_PEAK_TFLOPS if cfg.mxfp4 else BF16_PEAK_TFLOPS
+        bound = "hbm" if ai < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
         kern = "grouped_gemm"
         traffic = measured_traffic(f"{dom}", cfg.name, source_hash("gemm.hip"))
         if bound == "hbm":
@@ -271,8 +288,8 @@ def main():
                         "avg_launch_us": round(stages[dom], 2)}
         else:
             achieved = dom_flop / dur_s / 1e12
-            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+            roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak,
+                        "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4), "traffic": traffic,
                         "kernel": f"{kern} ({dom})", "algorithmic_flop_per_launch": dom_flop,
                         "avg_launch_us": round(stages[dom], 2)}
 
@@ -292,7 +309,7 @@ def main():
         for n, fl, by in (("fc1", fc1_flop, fc1_bytes), ("fc2", fc2_flop, fc2_bytes)):
             us = stages[n]
             extra[f"{n}_tflops"] = round(fl / us / 1e6, 2)
-            extra[f"{n}_mfma_frac"] = round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4)
+            extra[f"{n}_mfma_frac"] = round(fl / us / 1e6 / (FP8_PEAK_TFLOPS if cfg.mxfp4 else BF16_PEAK_TFLOPS), 4)
             extra[f"{n}_hbm_frac"] = round(by / us / 1e3 / HBM_PEAK_GBS, 4)
 
     cpu = None
@@ -303,11 +320,15 @@ def main():
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (experts: MXFP4 weights x MXFP8 activations)" if cfg.mxfp4 else "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights, gap-separated N(0,1) logits)",
-        "config": {"workload": f"{cfg.name}: T={T} tokens, d={d} -> latent {l}, E={E} top-{k} + {S} shared, "
-                               f"SwiGLU I={I}, shared I={Is}, RMSNorm on", "T": T, "d": d, "latent": l, "E": E,
-                   "k": k, "shared": S, "I": I, "Is": Is},
+        "config": {"workload": (f"{cfg.name}: {T} received rows, {E} local experts, latent {l}, SwiGLU I={I}, "
+                                f"Zipf({cfg.zipf_s}) expert load, combine weights given") if cfg.rows_mode else
+                               (f"{cfg.name}: T={T} tokens, d={d} -> latent {l}, E={E} top-{k} + {S} shared, "
+                                f"SwiGLU I={I}, shared I={Is}, RMSNorm on"
+                                + (", MXFP4 experts (w4a8)" if cfg.mxfp4 else "")),
+                   "T": T, "d": d, "latent": l, "E": E, "k": k, "shared": S, "I": I, "Is": Is},
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(line), flush=True)
