@@ -49,22 +49,28 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b
 
 // Macro tile: 256 rows x 256 B rows (plain: 256 output columns; gated: 128
 // gate + 128 up rows -> 128 output columns), K staged 64 at a time through a
-// double-buffered LDS (2 x 72 KB).  4 waves; WAVES_M x (4/WAVES_M) layout:
-//  * WAVES_M = 4: wave tile 64 x 256, so a grouped tile with few rows leaves
-//    whole waves idle (they skip their MFMAs but still help load) -- an
-//    expert's up-to-256 rows read its weights once;
-//  * WAVES_M = 2: wave tile 128 x 128, less LDS traffic for dense GEMMs.
-// Each wave keeps 16 32x32 accumulators (256 fp32 per lane).  Partial N tiles
-// clamp their B rows and mask their stores.
-template <int WAVES_M, bool GATED, bool GROUPED>
-__global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(TiledArgs g) {
+// double-buffered LDS (2 x 72 KB).  8 waves = 2 per SIMD, so one wave's LDS
+// reads and memory instructions overlap the other's MFMAs; WAVES_M x
+// (8/WAVES_M) layout (2 x 4: wave tile 128 x 64; 4 x 2: 64 x 128, which lets a
+// grouped tile with few rows idle whole waves).  Each wave keeps 8 32x32
+// accumulators.  Main loop per 64-wide K stage, with one register set:
+//   MFMAs on the first half of stage k | LDS writes of stage k+1 (loaded one
+//   stage earlier) | global loads of stage k+2 | MFMAs on the second half |
+//   barrier
+// so every global load has a whole stage to arrive.  The K of all segments
+// is one sequence of stages; rows of a partial tile and B rows past N are
+// clamped (loaded but never stored).
+template <int WAVES_M, bool GATED, bool GROUPED, bool SWZ>
+__global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
+  constexpr int NTH = 512;
   constexpr int BM = 256, BR = 256;                 // A rows, B rows per tile
   constexpr int NOUT = GATED ? 128 : 256;           // output columns per tile
-  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WAVES_N = 8 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BR / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;         // 32x32 subtiles per wave
   constexpr int CPR = kBK / 8;                      // 16-byte chunks per row
-  constexpr int A_CH = BM * CPR / 256, B_CH = BR * CPR / 256;
+  constexpr int A_CH = BM * CPR / NTH, B_CH = BR * CPR / NTH;
+  static_assert(!GATED || FN % 2 == 0, "gated waves need matching gate and up subtiles");
 
   extern __shared__ uint4 lds_u4[];
   bf16_t* As = reinterpret_cast<bf16_t*>(lds_u4);  // [2][BM][kLdsK]
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(TiledArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
-  const uint32_t lt = xcd_swizzle(blockIdx.x, gridDim.x);
+  const uint32_t lt = SWZ ? xcd_swizzle(blockIdx.x, gridDim.x) : blockIdx.x;
   const int tn = int(lt % uint32_t(tiles_n));
   const int tm = int(lt / uint32_t(tiles_n));
   int expert = 0, row0, nrows;
@@ -99,6 +105,57 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(TiledArgs g) {
     }
   };
 
+  // per-thread load rows (fixed for the tile): A source row, B row
+  int64_t arow[A_CH];
+  int brw[B_CH];
+  bool bup[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int r = (tid + i * NTH) / CPR;
+    int64_t src = int64_t(row0) + min(r, nrows - 1);
+    if constexpr (GROUPED) {
+      if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
+    }
+    arow[i] = src;
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int r = (tid + i * NTH) / CPR;
+    bup[i] = GATED && r >= BR / 2;
+    brw[i] = min(n0 + (bup[i] ? r - BR / 2 : r), g.N - 1);
+  }
+  const int kc8 = (tid % CPR) * 8;  // this thread's column chunk (same for all its rows)
+
+  int nk = 0;
+  for (int s = 0; s < g.nseg; ++s) nk += g.seg[s].K / kBK;
+
+  uint4 ra[A_CH], rb[B_CH];
+  auto gload = [&](int kt) {
+    int s = 0, base = 0;
+    while (base + g.seg[s].K / kBK <= kt) base += g.seg[s++].K / kBK;
+    const GemmSeg& sg = g.seg[s];
+    const int ko = (kt - base) * kBK + kc8;
+    const int64_t be = int64_t(expert) * g.b_estride;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) ra[i] = ldg16(sg.A + arow[i] * sg.lda + ko);
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) rb[i] = ldg16((bup[i] ? sg.B3 : sg.B) + be + int64_t(brw[i]) * sg.ldb + ko);
+  };
+  auto lstore = [&](int buf) {
+    bf16_t* An = As + buf * BM * kLdsK;
+    bf16_t* Bn = Bs + buf * BR * kLdsK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NTH;
+      *reinterpret_cast<uint4*>(&An[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * NTH;
+      *reinterpret_cast<uint4*>(&Bn[(c / CPR) * kLdsK + (c % CPR) * 8]) = rb[i];
+    }
+  };
+
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -107,88 +164,38 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(TiledArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  for (int s = 0; s < g.nseg; ++s) {
-    const GemmSeg sg = g.seg[s];
-    const bf16_t* ap[A_CH];
-    const bf16_t* bp[B_CH];
+  auto compute = [&](int buf, int ks0, int ks1) {
+    const bf16_t* Ab = As + buf * BM * kLdsK;
+    const bf16_t* Bb = Bs + buf * BR * kLdsK;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * 256, r = c / CPR, kc = c % CPR;
-      int64_t src = int64_t(row0) + min(r, nrows - 1);
-      if constexpr (GROUPED) {
-        if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
+    for (int ks = ks0; ks < ks1; ++ks) {
+      const int kof = ks * 16 + (lane >> 5) * 8;
+      bf16x8 af[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ab[(wm * WM + i * 32 + (lane & 31)) * kLdsK + kof]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const bf16x8 bf = as_bf16x8(*reinterpret_cast<const uint4*>(&Bb[(brow(j) + (lane & 31)) * kLdsK + kof]));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[i][j] = mfma_32x32x16(af[i], bf, acc[i][j]);
       }
-      ap[i] = sg.A + src * sg.lda + kc * 8;
     }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * 256, r = c / CPR, kc = c % CPR;
-      const bool up = GATED && r >= BR / 2;
-      const int rn = min(n0 + (up ? r - BR / 2 : r), g.N - 1);
-      bp[i] = (up ? sg.B3 : sg.B) + int64_t(expert) * g.b_estride + int64_t(rn) * sg.ldb + kc * 8;
-    }
-    const int nk = sg.K / kBK;
-    uint4 ra[A_CH], rb[B_CH];
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = ldg16(ap[i]);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = ldg16(bp[i]);
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(&As[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * 256;
-      *reinterpret_cast<uint4*>(&Bs[(c / CPR) * kLdsK + (c % CPR) * 8]) = rb[i];
-    }
-    __syncthreads();
+  };
 
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) {
-        const int koff = (kt + 1) * kBK;
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) ra[i] = ldg16(ap[i] + koff);
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) rb[i] = ldg16(bp[i] + koff);
-      }
-      if (active) {
-        const bf16_t* Ab = As + buf * BM * kLdsK;
-        const bf16_t* Bb = Bs + buf * BR * kLdsK;
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-          const int kof = ks * 16 + (lane >> 5) * 8;
-          bf16x8 af[FM];
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-            af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ab[(wm * WM + i * 32 + (lane & 31)) * kLdsK + kof]));
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const bf16x8 bf =
-                as_bf16x8(*reinterpret_cast<const uint4*>(&Bb[(brow(j) + (lane & 31)) * kLdsK + kof]));
-#pragma unroll
-            for (int i = 0; i < FM; ++i) acc[i][j] = mfma_32x32x16(af[i], bf, acc[i][j]);
-          }
-        }
-      }
-      if (kt + 1 < nk) {
-        bf16_t* An = As + (buf ^ 1) * BM * kLdsK;
-        bf16_t* Bn = Bs + (buf ^ 1) * BR * kLdsK;
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-          const int c = tid + i * 256;
-          *reinterpret_cast<uint4*>(&An[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-          const int c = tid + i * 256;
-          *reinterpret_cast<uint4*>(&Bn[(c / CPR) * kLdsK + (c % CPR) * 8]) = rb[i];
-        }
-      }
-      __syncthreads();
-    }
+  gload(0);
+  lstore(0);
+  if (nk > 1) gload(1);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (active) compute(buf, 0, kBK / 32);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    if (kt + 2 < nk) gload(kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (active) compute(buf, kBK / 32, kBK / 16);
+    __syncthreads();
   }
 
   // Epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores.
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(TiledArgs g) {
   }
   __syncthreads();
   constexpr int OCPR = NOUT / 8;
-  for (int c = tid; c < BM * OCPR; c += 256) {
+  for (int c = tid; c < BM * OCPR; c += NTH) {
     const int row = c / OCPR, cc = c % OCPR;
     if (row < nrows && n0 + cc * 8 < g.N) {
       *reinterpret_cast<uint4*>(g.C + (int64_t(row0) + row) * g.ldc + n0 + cc * 8) =
@@ -222,11 +229,11 @@ __global__ __launch_bounds__(256, 1) void tiled_gemm_kernel(TiledArgs g) {
   }
 }
 
-template <int WAVES_M, bool GATED, bool GROUPED>
+template <int WAVES_M, bool GATED, bool GROUPED, bool SWZ>
 hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s) {
   constexpr int NOUT = GATED ? 128 : 256;
   const size_t lds = size_t(2) * (256 + 256) * kLdsK * sizeof(bf16_t);
-  auto kern = tiled_gemm_kernel<WAVES_M, GATED, GROUPED>;
+  auto kern = tiled_gemm_kernel<WAVES_M, GATED, GROUPED, SWZ>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -235,7 +242,7 @@ hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s) {
   }
   const int64_t nblk = mtiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
-  kern<<<dim3{uint32_t(nblk)}, dim3{256}, lds, s>>>(a);
+  kern<<<dim3{uint32_t(nblk)}, dim3{512}, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -452,8 +459,8 @@ hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
   a.C = d.C;
   a.ldc = d.ldc;
   const int64_t mt = (d.M + 255) / 256;
-  if (d.gated) return run_tiled<2, true, false>(a, mt, s);
-  return run_tiled<2, false, false>(a, mt, s);
+  if (d.gated) return run_tiled<2, true, false, false>(a, mt, s);
+  return run_tiled<2, false, false, false>(a, mt, s);
 }
 
 hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s) {
@@ -470,8 +477,8 @@ hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s) {
   a.C = g.C;
   a.ldc = g.ldc;
   static_assert(kTiledBM == 256, "tile table granularity");
-  if (g.gated) return run_tiled<4, true, true>(a, g.max_tiles, s);
-  return run_tiled<4, false, true>(a, g.max_tiles, s);
+  if (g.gated) return run_tiled<2, true, true, true>(a, g.max_tiles, s);
+  return run_tiled<2, false, true, true>(a, g.max_tiles, s);
 }
 
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s) {
