@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-stage-events", action="store_true")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: each copy's route+forward captured once in a HIP graph and replayed")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 5 plain device copies of BYTES bytes (the reference kernel that scales the "
+                         "PMC FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     return ap.parse_args()
 
 
@@ -128,11 +131,21 @@ def main():
         return 2
     import torch
 
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
+        return 0
+
     import latentmoe_expert_layer_amd as lm
     import workloads as W
 
-    assert torch.cuda.is_available(), "bench needs a GPU"
-    torch.cuda.set_device(0)
     cfg = W.CONFIGS[args.workload]
     hip = Hip()
     stream = torch.cuda.current_stream().cuda_stream
