@@ -82,39 +82,26 @@ __device__ __forceinline__ void sort_desc(uint64_t (&a)[N]) {
       }
 }
 
-// One wave per token; lane l holds logits e = l + 64*j (coalesced rows).
-// Each lane sorts its VPL keys once; then each of the k rounds takes the
-// wave-wide maximum of the lanes' current heads: a 32-bit max of the value
-// word, and only when several lanes tie on it, a second max of the index
-// word.  The winning lane pops its head.
-template <int VPL>
-__global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ logits, int64_t T, int E,
-                                                     int k, int32_t* __restrict__ ids,
-                                                     float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + t * int64_t(E);
-  // all VPL loads are issued unconditionally (clamped index) so that they are
-  // in flight together; slots past E are then emptied
-  float v[VPL];
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
-  uint64_t cand[VPL];
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) {
-    const int e = lane + 64 * j;
-    cand[j] = (e < E) ? rank_key(v[j], uint32_t(e)) : 0ull;
-  }
-  sort_desc<VPL>(cand);
+// Position of the current lane among the lanes set in a ballot mask.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u)));
+}
 
-  uint64_t mine = 0;  // lane i keeps the i-th selected key
+// Serial selection: each lane sorts its VPL keys once; then each of the k
+// rounds takes the wave-wide maximum of the lanes' current heads (a 32-bit max
+// of the value word and, only when several lanes tie on it, a second max of the
+// index word) and the winning lane pops its head.  Returns the i-th selected
+// key in lane i.
+template <int VPL>
+__device__ __forceinline__ uint64_t select_serial(uint64_t (&cand)[VPL], int k, int lane) {
+  sort_desc<VPL>(cand);
+  uint64_t mine = 0;
   for (int i = 0; i < k; ++i) {
     const uint64_t head = cand[0];
     const uint32_t hi = uint32_t(head >> 32);
     const uint32_t mh = wave_max_u32(hi);
     uint64_t tied = ballot(hi == mh);
-    if (__popcll(tied) > 1) {  // equal values on several lanes: lowest index wins
+    if (__popcll(tied) > 1) {
       const uint32_t lo = (hi == mh) ? uint32_t(head) : 0u;
       const uint32_t ml = wave_max_u32(lo);
       tied = ballot(hi == mh && uint32_t(head) == ml);
@@ -128,6 +115,78 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
       cand[VPL - 1] = 0;
     }
   }
+  return mine;
+}
+
+// One wave per token; lane l holds logits e = l + 64*j (coalesced rows).
+//
+// Threshold selection.  Let tau be the k-th largest of the 64 lane maxima of
+// the value words.  At least k entries (those lane maxima) have a value word
+// >= tau, so every one of the top k does, and the candidate set
+// C = {entries with value word >= tau} contains the answer.  tau comes from a
+// most-significant-bit-first search whose count is one ballot per bit.  For
+// i.i.d. logits C holds about k + 2 entries; they are compacted into LDS and
+// each candidate's rank is the number of candidate keys above its own (keys
+// are unique, so ranks are).  When C exceeds 64 entries (many equal values,
+// NaN floods) the serial selection runs instead; both give the same result.
+template <int VPL>
+__global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                     int k, int32_t* __restrict__ ids,
+                                                     float* __restrict__ w) {
+  __shared__ uint64_t cbuf[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t t = int64_t(blockIdx.x) * 4 + wv;
+  if (t >= T) return;
+  const float* row = logits + t * int64_t(E);
+  // all VPL loads are issued unconditionally (clamped index) so that they are
+  // in flight together; slots past E are then emptied
+  float v[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
+  uint64_t cand[VPL];
+  uint32_t lane_max = 0;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int e = lane + 64 * j;
+    cand[j] = (e < E) ? rank_key(v[j], uint32_t(e)) : 0ull;
+    lane_max = max(lane_max, uint32_t(cand[j] >> 32));
+  }
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = tau | (1u << b);
+    if (__popcll(ballot(lane_max >= c)) >= k) tau = c;
+  }
+  int total = 0;  // wave-uniform candidate count
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const bool is_c = cand[j] != 0 && uint32_t(cand[j] >> 32) >= tau;
+    const uint64_t m = ballot(is_c);
+    if (m != 0) {
+      const int pos = total + lanes_below(m);
+      if (is_c && pos < 64) cbuf[wv][pos] = cand[j];
+      total += __popcll(m);
+    }
+  }
+
+  uint64_t mine;  // lane i < k ends with the i-th selected key
+  if (total <= 64) {
+    // cbuf[wv] is private to this wave, whose LDS accesses complete in order;
+    // the fences only keep the compiler from moving them across each other
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t my = lane < total ? cbuf[wv][lane] : 0ull;
+    int rank = 0;
+    for (int i = 0; i < total; ++i) rank += readlane_u64(my, i) > my ? 1 : 0;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (lane < total && rank < k) cbuf[wv][rank] = my;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    mine = lane < k ? cbuf[wv][lane] : 0ull;
+  } else {
+    mine = select_serial<VPL>(cand, k, lane);
+  }
+
   const float lv = key_value(mine);
   const float vmax = __shfl(lv, 0, kWave);
   float ex = (lane < k) ? expf(lv - vmax) : 0.0f;
@@ -181,67 +240,96 @@ int permute_waves(int E) {
   return 0;
 }
 
-// Exclusive scan of a[0..n) in LDS by a 1024-thread block (n <= 16 * 1024);
-// returns the total.  Each thread scans a contiguous run, then the run sums
-// are scanned across lanes and waves.
-__device__ int block_exclusive_scan(int32_t* a, int n, int32_t* wave_sums) {
+// Exclusive scans of a[0..n) and b[0..n) in LDS by a 1024-thread block
+// (n <= 16 * 1024), both at once; returns the two totals.  Each thread scans a
+// contiguous run, then the run sums are scanned across lanes and waves.  b may
+// be null (a scanned alone).
+struct ScanTotals { int32_t a, b; };
+__device__ ScanTotals block_exclusive_scan2(int32_t* a, int32_t* b, int n, int32_t* wave_sums) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int kW = kPermThreads / 64;
   const int per = (n + kPermThreads - 1) / kPermThreads;
-  const int b = tid * per, e = min(n, b + per);
-  int32_t run = 0;
-  for (int i = b; i < e; ++i) run += a[i];
-  int32_t incl = run;
+  const int i0 = tid * per, i1 = min(n, i0 + per);
+  int32_t ra = 0, rb = 0;
+  for (int i = i0; i < i1; ++i) {
+    ra += a[i];
+    if (b) rb += b[i];
+  }
+  int32_t ia = ra, ib = rb;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    int32_t o = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += o;
+    const int32_t oa = __shfl_up(ia, off, kWave), ob = __shfl_up(ib, off, kWave);
+    if (lane >= off) {
+      ia += oa;
+      ib += ob;
+    }
   }
-  if (lane == 63) wave_sums[wid] = incl;
+  if (lane == 63) {
+    wave_sums[wid] = ia;
+    wave_sums[kW + 1 + wid] = ib;
+  }
   __syncthreads();
   if (wid == 0) {
-    int32_t v = lane < kPermThreads / 64 ? wave_sums[lane] : 0;
-    int32_t iv = v;
+    const int32_t va = lane < kW ? wave_sums[lane] : 0, vb = lane < kW ? wave_sums[kW + 1 + lane] : 0;
+    int32_t xa = va, xb = vb;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      int32_t o = __shfl_up(iv, off, kWave);
-      if (lane >= off) iv += o;
+      const int32_t oa = __shfl_up(xa, off, kWave), ob = __shfl_up(xb, off, kWave);
+      if (lane >= off) {
+        xa += oa;
+        xb += ob;
+      }
     }
-    if (lane < kPermThreads / 64) wave_sums[lane] = iv - v;  // exclusive
-    if (lane == kPermThreads / 64 - 1) wave_sums[kPermThreads / 64] = iv;
+    if (lane < kW) {
+      wave_sums[lane] = xa - va;  // exclusive
+      wave_sums[kW + 1 + lane] = xb - vb;
+    }
+    if (lane == kW - 1) {
+      wave_sums[kW] = xa;
+      wave_sums[2 * kW + 1] = xb;
+    }
   }
   __syncthreads();
-  int32_t base = wave_sums[wid] + incl - run;
-  for (int i = b; i < e; ++i) {
-    const int32_t c = a[i];
-    a[i] = base;
-    base += c;
+  int32_t base_a = wave_sums[wid] + ia - ra, base_b = wave_sums[kW + 1 + wid] + ib - rb;
+  for (int i = i0; i < i1; ++i) {
+    const int32_t ca = a[i];
+    a[i] = base_a;
+    base_a += ca;
+    if (b) {
+      const int32_t cb = b[i];
+      b[i] = base_b;
+      base_b += cb;
+    }
   }
-  const int32_t total = wave_sums[kPermThreads / 64];
+  const ScanTotals tot{wave_sums[kW], wave_sums[2 * kW + 1]};
   __syncthreads();
-  return total;
+  return tot;
 }
 
-// Tile table of granularity bm: every expert's segment split into runs of at
-// most bm rows.  cnt/tstart are LDS scratch of E+1 entries.
-__device__ void emit_tiles(const int32_t* off, int E, int bm, int32_t* tstart, int32_t* wave_sums,
-                           Tile* __restrict__ tiles, int32_t* __restrict__ ntiles) {
-  for (int e = threadIdx.x; e < E; e += kPermThreads) tstart[e] = (off[e + 1] - off[e] + bm - 1) / bm;
-  __syncthreads();
-  const int32_t total = block_exclusive_scan(tstart, E, wave_sums);
+// Tile tables of granularity bm_a and bm_b from the offsets: every expert's
+// segment split into runs of at most bm rows.  ta/tb are LDS scratch of E
+// entries each.
+__device__ void emit_tiles(const int32_t* off, int E, int32_t* ta, int32_t* tb, int32_t* wave_sums,
+                           int bm_a, Tile* __restrict__ tiles_a, int32_t* __restrict__ n_a,
+                           int bm_b, Tile* __restrict__ tiles_b, int32_t* __restrict__ n_b) {
   for (int e = threadIdx.x; e < E; e += kPermThreads) {
     const int32_t cnt = off[e + 1] - off[e];
-    int32_t t = tstart[e];
-    for (int32_t r = 0; r < cnt; r += bm, ++t) {
-      Tile tl;
-      tl.expert = e;
-      tl.row_start = off[e] + r;
-      tl.nrows = min(bm, cnt - r);
-      tl.pad = 0;
-      tiles[t] = tl;
-    }
+    ta[e] = (cnt + bm_a - 1) / bm_a;
+    tb[e] = (cnt + bm_b - 1) / bm_b;
   }
-  if (threadIdx.x == 0) *ntiles = total;
   __syncthreads();
+  const ScanTotals tot = block_exclusive_scan2(ta, tb, E, wave_sums);
+  for (int e = threadIdx.x; e < E; e += kPermThreads) {
+    const int32_t o = off[e], cnt = off[e + 1] - o;
+    int32_t t = ta[e];
+    for (int32_t r = 0; r < cnt; r += bm_a, ++t) tiles_a[t] = Tile{e, o + r, min(bm_a, cnt - r), 0};
+    t = tb[e];
+    for (int32_t r = 0; r < cnt; r += bm_b, ++t) tiles_b[t] = Tile{e, o + r, min(bm_b, cnt - r), 0};
+  }
+  if (threadIdx.x == 0) {
+    *n_a = tot.a;
+    *n_b = tot.b;
+  }
 }
 
 // One 1024-thread workgroup.  Wave w owns the contiguous row chunk
@@ -250,7 +338,8 @@ __device__ void emit_tiles(const int32_t* off, int E, int bm, int32_t* tstart, i
 // chunk 64 rows at a time: lanes with equal expert find each other with
 // ballots over the id bits, take consecutive slots in lane order, and the
 // group's lowest lane advances the running base.  Rows keep their order
-// within an expert (stable), so the result is unique.
+// within an expert (stable), so the result is unique.  A wave's first batch
+// of ids (64 * kBatch rows) stays in registers between (1) and (4).
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t* __restrict__ ids, int64_t R, int E, int nwaves, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_row, int32_t* __restrict__ row_pos, Tile* __restrict__ tiles_a,
@@ -259,7 +348,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   int32_t* hist = lds;                          // [nwaves][E]
   int32_t* off = hist + int64_t(nwaves) * E;    // [E+1]
   int32_t* tmp = off + (E + 1);                 // [E+1]
-  int32_t* wave_sums = tmp + (E + 1);           // [64]
+  int32_t* wave_sums = tmp + (E + 1);           // [2 * (waves + 1)]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 
   for (int i = tid; i < nwaves * E; i += kPermThreads) hist[i] = 0;
@@ -270,14 +359,17 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   // ids are read kBatch rows per lane at a time with clamped (in-bounds)
   // indices, so a batch's loads are in flight together
   constexpr int kBatch = 8;
+  int32_t first[kBatch];
   if (wid < nwaves) {
     for (int64_t rb = r0; rb < r1; rb += 64 * kBatch) {
       int32_t idv[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) idv[u] = ids[min(rb + 64 * u + lane, R - 1)];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
+      for (int u = 0; u < kBatch; ++u) {
+        if (rb == r0) first[u] = idv[u];
         if (rb + 64 * u + lane < r1) atomicAdd(&hist[wid * E + clamp_id(idv[u], E)], 1);
+      }
     }
   }
   __syncthreads();
@@ -292,13 +384,16 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     off[e] = run;
   }
   __syncthreads();
-  block_exclusive_scan(off, E, wave_sums);
-  for (int e = tid; e < E; e += kPermThreads) offsets[e] = off[e];
+  block_exclusive_scan2(off, nullptr, E, wave_sums);
+  for (int e = tid; e < E; e += kPermThreads) {
+    const int32_t o = off[e];
+    offsets[e] = o;
+    for (int w = 0; w < nwaves; ++w) hist[w * E + e] += o;
+  }
   if (tid == 0) {
     off[E] = int32_t(R);
     offsets[E] = int32_t(R);
   }
-  for (int i = tid; i < nwaves * E; i += kPermThreads) hist[i] += off[i % E];
   __syncthreads();
 
   if (wid < nwaves) {
@@ -307,36 +402,40 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int64_t rb = r0; rb < r1; rb += 64 * kBatch) {
       int32_t idv[kBatch];
+      if (rb == r0) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) idv[u] = ids[min(rb + 64 * u + lane, R - 1)];
+        for (int u = 0; u < kBatch; ++u) idv[u] = first[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) idv[u] = ids[min(rb + 64 * u + lane, R - 1)];
+      }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-      const int64_t base_r = rb + 64 * u;
-      if (base_r >= r1) break;
-      const int64_t r = base_r + lane;
-      const bool valid = r < r1;
-      const int32_t id = valid ? clamp_id(idv[u], E) : 0;
-      uint64_t peers = ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = (id >> b) & 1;
-        const uint64_t m = ballot(bit);
-        peers &= bit ? m : ~m;
-      }
-      int32_t base = 0;
-      if (valid) base = hist[wid * E + id];
-      const int rank = __popcll(peers & below);
-      if (valid && rank == 0) hist[wid * E + id] = base + __popcll(peers);
-      if (valid) {
-        const int32_t p = base + rank;
-        sorted_row[p] = int32_t(r);
-        row_pos[r] = p;
-      }
+        const int64_t base_r = rb + 64 * u;
+        if (base_r >= r1) break;
+        const int64_t r = base_r + lane;
+        const bool valid = r < r1;
+        const int32_t id = valid ? clamp_id(idv[u], E) : 0;
+        uint64_t peers = ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+          const bool bit = (id >> b) & 1;
+          const uint64_t m = ballot(bit);
+          peers &= bit ? m : ~m;
+        }
+        int32_t base = 0;
+        if (valid) base = hist[wid * E + id];
+        const int rank = __popcll(peers & below);
+        if (valid && rank == 0) hist[wid * E + id] = base + __popcll(peers);
+        if (valid) {
+          const int32_t p = base + rank;
+          sorted_row[p] = int32_t(r);
+          row_pos[r] = p;
+        }
       }
     }
   }
   __syncthreads();
-  emit_tiles(off, E, kSkinnyBM, tmp, wave_sums, tiles_a, n_a);
-  emit_tiles(off, E, kTiledBM, tmp, wave_sums, tiles_b, n_b);
+  emit_tiles(off, E, tmp, hist, wave_sums, kSkinnyBM, tiles_a, n_a, kTiledBM, tiles_b, n_b);
 }
 
 hipError_t launch_permute(const int32_t* ids, int64_t R, int E, int32_t* offsets, int32_t* sorted_row,

@@ -79,6 +79,46 @@ def test_route_ties_nan_ragged(T, E, k):
     assert torch.equal(r.row_pos.cpu(), rpos)
 
 
+def _threshold_rows(T, E, k, seed):
+    """Logit rows that steer the router's threshold selection into each of its
+    cases: a small candidate set with and without value ties (top, boundary,
+    many top values in one lane), and sets too large for the fast path (many
+    equal values, all equal, NaN floods), plus infinities."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, E, generator=g)
+    x[1, torch.randperm(E, generator=g)[:3]] = x[1].max()                # tie at the top
+    srt = x[2].sort(descending=True)
+    x[2, srt.indices[k]] = srt.values[k - 1]                              # tie across the k-th boundary
+    lane = torch.arange(5, E, 64)
+    x[3, lane] = 10.0 + torch.rand(lane.numel(), generator=g)            # one lane holds the top values
+    x[4, torch.randperm(E, generator=g)[:70]] = 5.0                       # 70 equal maxima
+    x[5, torch.randperm(E, generator=g)[:64]] = 5.0                       # 64 equal maxima
+    x[6, torch.randperm(E, generator=g)[: E // 2]] = float("nan")        # half NaN
+    x[7] = 0.25                                                           # all equal
+    x[8] = float("-inf")
+    x[8, torch.randperm(E, generator=g)[:3]] = torch.randn(3, generator=g)
+    x[9, torch.randperm(E, generator=g)[:2]] = float("inf")
+    for t in range(10, T):                                                # random ties near the top
+        top = x[t].topk(k + 2).indices
+        a, b = top[torch.randint(0, k + 2, (2,), generator=g)]
+        x[t, a] = x[t, b]
+    return x
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 896, 16), (40, 1024, 16), (33, 200, 8), (20, 64, 16), (24, 128, 64)])
+def test_route_threshold_paths(T, E, k):
+    log(f"route threshold paths T={T} E={E} k={k}")
+    logits = _threshold_rows(T, E, k, seed=T + E + k)
+    r = gpu_route(logits.cuda(), k)
+    ids_ref, w_ref = oracle.route(logits, k)
+    got = r.topk_ids.cpu()
+    bad = (got != ids_ref).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, f"router ids differ on rows {bad[:10]}"
+    fin = torch.isfinite(logits.gather(1, ids_ref.long())).all(dim=1)
+    dw = (r.topk_w.cpu().double() - w_ref.double())[fin].abs().max().item()
+    assert dw <= 2e-6, f"combine weights differ by {dw}"
+
+
 @pytest.mark.parametrize("R,E,heavy", [(16384, 56, False), (5000, 4096, False), (777, 13, True), (64, 1, False)])
 def test_permute_ids_mode(R, E, heavy):
     log(f"permute ids R={R} E={E} heavy={heavy}")
