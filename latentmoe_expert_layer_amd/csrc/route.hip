@@ -226,141 +226,99 @@ hipError_t launch_copy_ids(const int32_t* ids_in, const float* w_in, int64_t n, 
 
 // ---------------------------------------------------------------- permute ---
 constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / 64;
 
 // Expert ids outside [0, E) (invalid input) are clamped so that every write
 // stays inside the caller's buffers; valid ids are unchanged.
 __device__ __forceinline__ int32_t clamp_id(int32_t id, int E) { return min(max(id, 0), E - 1); }
 constexpr int kPermLdsBudget = 150 * 1024;
 
+// LDS of the permute kernel: the [E][NW+1] histogram plus the scan scratch.
+static int64_t permute_lds_bytes(int E, int nw) { return (int64_t(E) * (nw + 1) + 64) * 4; }
+
 int permute_waves(int E) {
-  // per-wave histograms [waves][E] plus two (E+1) scan arrays in LDS
-  const int64_t fixed = 2 * int64_t(E + 1) * 4 + 64 * 4;
-  for (int w = 16; w >= 1; w >>= 1)
-    if (int64_t(w) * E * 4 + fixed <= kPermLdsBudget) return w;
+  for (int w = 16; w >= 8; w >>= 1)
+    if (permute_lds_bytes(E, w) <= kPermLdsBudget) return w;
   return 0;
 }
 
-// Exclusive scans of a[0..n) and b[0..n) in LDS by a 1024-thread block
-// (n <= 16 * 1024), both at once; returns the two totals.  Each thread scans a
-// contiguous run, then the run sums are scanned across lanes and waves.  b may
-// be null (a scanned alone).
-struct ScanTotals { int32_t a, b; };
-__device__ ScanTotals block_exclusive_scan2(int32_t* a, int32_t* b, int n, int32_t* wave_sums) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  constexpr int kW = kPermThreads / 64;
-  const int per = (n + kPermThreads - 1) / kPermThreads;
-  const int i0 = tid * per, i1 = min(n, i0 + per);
-  int32_t ra = 0, rb = 0;
-  for (int i = i0; i < i1; ++i) {
-    ra += a[i];
-    if (b) rb += b[i];
-  }
-  int32_t ia = ra, ib = rb;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t oa = __shfl_up(ia, off, kWave), ob = __shfl_up(ib, off, kWave);
-    if (lane >= off) {
-      ia += oa;
-      ib += ob;
-    }
-  }
-  if (lane == 63) {
-    wave_sums[wid] = ia;
-    wave_sums[kW + 1 + wid] = ib;
-  }
-  __syncthreads();
-  if (wid == 0) {
-    const int32_t va = lane < kW ? wave_sums[lane] : 0, vb = lane < kW ? wave_sums[kW + 1 + lane] : 0;
-    int32_t xa = va, xb = vb;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t oa = __shfl_up(xa, off, kWave), ob = __shfl_up(xb, off, kWave);
-      if (lane >= off) {
-        xa += oa;
-        xb += ob;
-      }
-    }
-    if (lane < kW) {
-      wave_sums[lane] = xa - va;  // exclusive
-      wave_sums[kW + 1 + lane] = xb - vb;
-    }
-    if (lane == kW - 1) {
-      wave_sums[kW] = xa;
-      wave_sums[2 * kW + 1] = xb;
-    }
-  }
-  __syncthreads();
-  int32_t base_a = wave_sums[wid] + ia - ra, base_b = wave_sums[kW + 1 + wid] + ib - rb;
-  for (int i = i0; i < i1; ++i) {
-    const int32_t ca = a[i];
-    a[i] = base_a;
-    base_a += ca;
-    if (b) {
-      const int32_t cb = b[i];
-      b[i] = base_b;
-      base_b += cb;
-    }
-  }
-  const ScanTotals tot{wave_sums[kW], wave_sums[2 * kW + 1]};
-  __syncthreads();
-  return tot;
+// Inclusive wave scan (sum) with DPP: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then row 0's total into row 1 and row 2's into row 3, then the
+// total of rows 0-1 into rows 2 and 3.  Lanes without a source read 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int32_t dpp_add(int32_t v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+  v = dpp_add<0x111>(v);        // row_shr:1
+  v = dpp_add<0x112>(v);        // row_shr:2
+  v = dpp_add<0x114>(v);        // row_shr:4
+  v = dpp_add<0x118>(v);        // row_shr:8
+  v = dpp_add<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
-// Tile tables of granularity bm_a and bm_b from the offsets: every expert's
-// segment split into runs of at most bm rows.  ta/tb are LDS scratch of E
-// entries each.
-__device__ void emit_tiles(const int32_t* off, int E, int32_t* ta, int32_t* tb, int32_t* wave_sums,
-                           int bm_a, Tile* __restrict__ tiles_a, int32_t* __restrict__ n_a,
-                           int bm_b, Tile* __restrict__ tiles_b, int32_t* __restrict__ n_b) {
-  for (int e = threadIdx.x; e < E; e += kPermThreads) {
-    const int32_t cnt = off[e + 1] - off[e];
-    ta[e] = (cnt + bm_a - 1) / bm_a;
-    tb[e] = (cnt + bm_b - 1) / bm_b;
+// Exclusive scan of three per-thread values over the 1024-thread block, in
+// thread order; also returns the three totals.  One barrier: every wave
+// scans the 16 wave totals itself.
+struct Scan3 { int32_t x[3], total[3]; };
+__device__ __forceinline__ Scan3 block_exclusive_scan3(const int32_t (&v)[3], int32_t* ws) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int32_t incl[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    incl[c] = wave_incl_scan(v[c]);
+    if (lane == 63) ws[c * kPermWaves + wid] = incl[c];
   }
   __syncthreads();
-  const ScanTotals tot = block_exclusive_scan2(ta, tb, E, wave_sums);
-  for (int e = threadIdx.x; e < E; e += kPermThreads) {
-    const int32_t o = off[e], cnt = off[e + 1] - o;
-    int32_t t = ta[e];
-    for (int32_t r = 0; r < cnt; r += bm_a, ++t) tiles_a[t] = Tile{e, o + r, min(bm_a, cnt - r), 0};
-    t = tb[e];
-    for (int32_t r = 0; r < cnt; r += bm_b, ++t) tiles_b[t] = Tile{e, o + r, min(bm_b, cnt - r), 0};
+  Scan3 r;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int32_t wt = lane < kPermWaves ? ws[c * kPermWaves + lane] : 0;
+    const int32_t wi = wave_incl_scan(wt);
+    const int32_t before = wid == 0 ? 0 : __builtin_amdgcn_readlane(wi, wid - 1);
+    r.x[c] = before + incl[c] - v[c];
+    r.total[c] = __builtin_amdgcn_readlane(wi, kPermWaves - 1);
   }
-  if (threadIdx.x == 0) {
-    *n_a = tot.a;
-    *n_b = tot.b;
-  }
+  return r;
 }
 
-// One 1024-thread workgroup.  Wave w owns the contiguous row chunk
-// [w*C, (w+1)*C).  (1) per-wave LDS histograms; (2) per expert, prefix over
-// waves; (3) exclusive scan over experts -> offsets; (4) each wave walks its
-// chunk 64 rows at a time: lanes with equal expert find each other with
-// ballots over the id bits, take consecutive slots in lane order, and the
-// group's lowest lane advances the running base.  Rows keep their order
-// within an expert (stable), so the result is unique.  A wave's first batch
-// of ids (64 * kBatch rows) stays in registers between (1) and (4).
+// One 1024-thread workgroup; NW waves split the rows into contiguous chunks.
+//  (1) histogram: hist[e][w] = rows of expert e in wave w's chunk (LDS
+//      atomics; the per-expert stride NW+1 is odd, so lanes with different
+//      experts hit different banks);
+//  (2) each thread owns a run of consecutive experts: its row count and its
+//      16-row and 256-row tile counts are scanned over the block in one pass,
+//      giving offsets[e], every (expert, wave) start slot, and the tile
+//      tables' start entries;
+//  (3) each wave walks its chunk 64 rows at a time: lanes with equal expert
+//      find each other with ballots over the id bits, take consecutive slots
+//      in lane order, and the group's lowest lane advances the running start.
+// Rows keep their order within an expert (stable), so the result is unique.
+// A wave's first batch of ids (64 * kBatch rows) stays in registers between
+// (1) and (3).
+template <int NW>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t* __restrict__ ids, int64_t R, int E, int nwaves, int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ ids, int64_t R, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_row, int32_t* __restrict__ row_pos, Tile* __restrict__ tiles_a,
     int32_t* __restrict__ n_a, Tile* __restrict__ tiles_b, int32_t* __restrict__ n_b) {
+  constexpr int S = NW + 1;
   extern __shared__ int32_t lds[];
-  int32_t* hist = lds;                          // [nwaves][E]
-  int32_t* off = hist + int64_t(nwaves) * E;    // [E+1]
-  int32_t* tmp = off + (E + 1);                 // [E+1]
-  int32_t* wave_sums = tmp + (E + 1);           // [2 * (waves + 1)]
+  int32_t* hist = lds;                        // [E][S]
+  int32_t* ws = hist + int64_t(E) * S;        // [3 * kPermWaves]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 
-  for (int i = tid; i < nwaves * E; i += kPermThreads) hist[i] = 0;
+  for (int i = tid; i < E * S; i += kPermThreads) hist[i] = 0;
   __syncthreads();
 
-  const int64_t chunk = ((R + nwaves - 1) / nwaves + 63) / 64 * 64;
+  const int64_t chunk = ((R + NW - 1) / NW + 63) / 64 * 64;
   const int64_t r0 = int64_t(wid) * chunk, r1 = min(R, r0 + chunk);
   // ids are read kBatch rows per lane at a time with clamped (in-bounds)
   // indices, so a batch's loads are in flight together
   constexpr int kBatch = 8;
   int32_t first[kBatch];
-  if (wid < nwaves) {
+  if (wid < NW) {
     for (int64_t rb = r0; rb < r1; rb += 64 * kBatch) {
       int32_t idv[kBatch];
 #pragma unroll
@@ -368,35 +326,51 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         if (rb == r0) first[u] = idv[u];
-        if (rb + 64 * u + lane < r1) atomicAdd(&hist[wid * E + clamp_id(idv[u], E)], 1);
+        if (rb + 64 * u + lane < r1) atomicAdd(&hist[clamp_id(idv[u], E) * S + wid], 1);
       }
     }
   }
   __syncthreads();
 
-  for (int e = tid; e < E; e += kPermThreads) {
-    int32_t run = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      const int32_t c = hist[w * E + e];
-      hist[w * E + e] = run;
-      run += c;
-    }
-    off[e] = run;
+  // (2) experts [e0, e1) belong to this thread
+  const int per = (E + kPermThreads - 1) / kPermThreads;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int32_t run[3] = {0, 0, 0};
+  for (int e = e0; e < e1; ++e) {
+    int32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) c += hist[e * S + w];
+    run[0] += c;
+    run[1] += (c + kSkinnyBM - 1) / kSkinnyBM;
+    run[2] += (c + kTiledBM - 1) / kTiledBM;
   }
-  __syncthreads();
-  block_exclusive_scan2(off, nullptr, E, wave_sums);
-  for (int e = tid; e < E; e += kPermThreads) {
-    const int32_t o = off[e];
+  const Scan3 sc = block_exclusive_scan3(run, ws);
+  int32_t o = sc.x[0], ta = sc.x[1], tb = sc.x[2];
+  for (int e = e0; e < e1; ++e) {
+    int32_t c[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) c[w] = hist[e * S + w];
     offsets[e] = o;
-    for (int w = 0; w < nwaves; ++w) hist[w * E + e] += o;
+    int32_t start = o;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      hist[e * S + w] = start;
+      start += c[w];
+    }
+    const int32_t cnt = start - o;
+    for (int32_t r = 0; r < cnt; r += kSkinnyBM, ++ta) tiles_a[ta] = Tile{e, o + r, min(kSkinnyBM, cnt - r), 0};
+    for (int32_t r = 0; r < cnt; r += kTiledBM, ++tb) tiles_b[tb] = Tile{e, o + r, min(kTiledBM, cnt - r), 0};
+    o = start;
   }
   if (tid == 0) {
-    off[E] = int32_t(R);
     offsets[E] = int32_t(R);
+    *n_a = sc.total[1];
+    *n_b = sc.total[2];
   }
   __syncthreads();
 
-  if (wid < nwaves) {
+  // (3) stable scatter
+  if (wid < NW) {
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -423,9 +397,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
           peers &= bit ? m : ~m;
         }
         int32_t base = 0;
-        if (valid) base = hist[wid * E + id];
+        if (valid) base = hist[id * S + wid];
         const int rank = __popcll(peers & below);
-        if (valid && rank == 0) hist[wid * E + id] = base + __popcll(peers);
+        if (valid && rank == 0) hist[id * S + wid] = base + __popcll(peers);
         if (valid) {
           const int32_t p = base + rank;
           sorted_row[p] = int32_t(r);
@@ -434,26 +408,32 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
       }
     }
   }
-  __syncthreads();
-  emit_tiles(off, E, tmp, hist, wave_sums, kSkinnyBM, tiles_a, n_a, kTiledBM, tiles_b, n_b);
+}
+
+template <int NW>
+static hipError_t launch_permute_nw(const int32_t* ids, int64_t R, int E, int32_t* offsets,
+                                    int32_t* sorted_row, int32_t* row_pos, Tile* tiles_a, int32_t* n_a,
+                                    Tile* tiles_b, int32_t* n_b, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)permute_kernel<NW>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kPermLdsBudget);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  permute_kernel<NW><<<dim3(1), dim3(kPermThreads), size_t(permute_lds_bytes(E, NW)), s>>>(
+      ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b);
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, int64_t R, int E, int32_t* offsets, int32_t* sorted_row,
                           int32_t* row_pos, Tile* tiles_a, int32_t* n_a, Tile* tiles_b, int32_t* n_b,
                           hipStream_t s) {
-  const int nw = permute_waves(E);
-  if (nw == 0) return hipErrorInvalidValue;
-  const size_t lds = (size_t(nw) * E + 2 * size_t(E + 1) + 64) * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)permute_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPermLdsBudget + 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  switch (permute_waves(E)) {
+    case 16: return launch_permute_nw<16>(ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b, s);
+    case 8: return launch_permute_nw<8>(ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b, s);
+    default: return hipErrorInvalidValue;
   }
-  permute_kernel<<<dim3(1), dim3(kPermThreads), lds, s>>>(ids, R, E, nw, offsets, sorted_row, row_pos,
-                                                          tiles_a, n_a, tiles_b, n_b);
-  return hipGetLastError();
 }
 
 }  // namespace lmoe
