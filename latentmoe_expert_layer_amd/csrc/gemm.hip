@@ -14,6 +14,8 @@
 //  * skinny_grouped_kernel: decode-shaped grouped GEMMs where every expert
 //    sees a handful of rows and the cost is streaming its weights once; each
 //    wave keeps a whole K chunk of loads in flight and skips LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -105,41 +107,60 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
     }
   };
 
-  // per-thread load rows (fixed for the tile): A source row, B row
-  int64_t arow[A_CH];
-  int brw[B_CH];
-  bool bup[B_CH];
+  // Load cursor.  Thread tid loads, for every stage, the 16-byte chunk kc8 of
+  // A rows i*64 + tid/8 and B rows i*64 + tid/8 (i < A_CH, B_CH).  Gated
+  // tiles take B rows 0..127 from the gate matrix and 128..255 from the up
+  // matrix, so chunks i < B_CH/2 read B and the others B3.  The source
+  // pointers are set once per segment and advance by kBK per stage; stages
+  // are loaded strictly in order.
+  static_assert(NTH / CPR == 64, "64 rows per load chunk");
+  static_assert(!GATED || B_CH % 2 == 0, "gated B chunks split evenly between gate and up");
+  int arow[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int r = (tid + i * NTH) / CPR;
-    int64_t src = int64_t(row0) + min(r, nrows - 1);
+    const int r = i * 64 + tid / CPR;
+    int src = row0 + min(r, nrows - 1);
     if constexpr (GROUPED) {
       if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
     }
     arow[i] = src;
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int r = (tid + i * NTH) / CPR;
-    bup[i] = GATED && r >= BR / 2;
-    brw[i] = min(n0 + (bup[i] ? r - BR / 2 : r), g.N - 1);
   }
   const int kc8 = (tid % CPR) * 8;  // this thread's column chunk (same for all its rows)
 
   int nk = 0;
   for (int s = 0; s < g.nseg; ++s) nk += g.seg[s].K / kBK;
 
-  uint4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int kt) {
-    int s = 0, base = 0;
-    while (base + g.seg[s].K / kBK <= kt) base += g.seg[s++].K / kBK;
+  const bf16_t* pa[A_CH];
+  const bf16_t* pb[B_CH];
+  int lseg = -1, lleft = 0;  // segment of the next stage to load, stages left in it
+  auto set_seg = [&](int s) {
     const GemmSeg& sg = g.seg[s];
-    const int ko = (kt - base) * kBK + kc8;
+    lleft = sg.K / kBK;
     const int64_t be = int64_t(expert) * g.b_estride;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = ldg16(sg.A + arow[i] * sg.lda + ko);
+    for (int i = 0; i < A_CH; ++i) pa[i] = sg.A + int64_t(arow[i]) * sg.lda + kc8;
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = ldg16((bup[i] ? sg.B3 : sg.B) + be + int64_t(brw[i]) * sg.ldb + ko);
+    for (int i = 0; i < B_CH; ++i) {
+      const bool up = GATED && i >= B_CH / 2;
+      const int r = (up ? i - B_CH / 2 : i) * 64 + tid / CPR;
+      pb[i] = (up ? sg.B3 : sg.B) + be + int64_t(min(n0 + r, g.N - 1)) * sg.ldb + kc8;
+    }
+  };
+
+  uint4 ra[A_CH], rb[B_CH];
+  auto gload = [&]() {
+    while (lleft == 0) set_seg(++lseg);
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      if (i * 64 < nrows) ra[i] = ldg16(pa[i]);
+      pa[i] += kBK;
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      rb[i] = ldg16(pb[i]);
+      pb[i] += kBK;
+    }
+    --lleft;
   };
   auto lstore = [&](int buf) {
     bf16_t* An = As + buf * BM * kLdsK;
@@ -147,7 +168,7 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NTH;
-      *reinterpret_cast<uint4*>(&An[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
+      if (i * 64 < nrows) *reinterpret_cast<uint4*>(&An[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
@@ -164,38 +185,54 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  auto compute = [&](int buf, int ks0, int ks1) {
-    const bf16_t* Ab = As + buf * BM * kLdsK;
-    const bf16_t* Bb = Bs + buf * BR * kLdsK;
+  // FA = this wave's 32-row subtiles that hold rows < nrows; the others are
+  // neither read from LDS nor multiplied (a tile's padding rows cost nothing
+  // beyond their clamped A loads, which whole 64-row chunks also skip)
+  auto mainloop = [&](auto fa_c) {
+    constexpr int FA = decltype(fa_c)::value;
+    auto compute = [&](int buf, int ks0, int ks1) {
+      const bf16_t* Ab = As + buf * BM * kLdsK;
+      const bf16_t* Bb = Bs + buf * BR * kLdsK;
 #pragma unroll
-    for (int ks = ks0; ks < ks1; ++ks) {
-      const int kof = ks * 16 + (lane >> 5) * 8;
-      bf16x8 af[FM];
+      for (int ks = ks0; ks < ks1; ++ks) {
+        const int kof = ks * 16 + (lane >> 5) * 8;
+        bf16x8 af[FA > 0 ? FA : 1];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ab[(wm * WM + i * 32 + (lane & 31)) * kLdsK + kof]));
+        for (int i = 0; i < FA; ++i)
+          af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ab[(wm * WM + i * 32 + (lane & 31)) * kLdsK + kof]));
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const bf16x8 bf = as_bf16x8(*reinterpret_cast<const uint4*>(&Bb[(brow(j) + (lane & 31)) * kLdsK + kof]));
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (FA > 0) {
+            const bf16x8 bf = as_bf16x8(*reinterpret_cast<const uint4*>(&Bb[(brow(j) + (lane & 31)) * kLdsK + kof]));
 #pragma unroll
-        for (int i = 0; i < FM; ++i) acc[i][j] = mfma_32x32x16(af[i], bf, acc[i][j]);
+            for (int i = 0; i < FA; ++i) acc[i][j] = mfma_32x32x16(af[i], bf, acc[i][j]);
+          }
+        }
       }
+    };
+    gload();
+    lstore(0);
+    if (nk > 1) gload();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      compute(buf, 0, kBK / 32);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) lstore(buf ^ 1);
+      if (kt + 2 < nk) gload();
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf, kBK / 32, kBK / 16);
+      __syncthreads();
     }
   };
-
-  gload(0);
-  lstore(0);
-  if (nk > 1) gload(1);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (active) compute(buf, 0, kBK / 32);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    if (kt + 2 < nk) gload(kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    if (active) compute(buf, kBK / 32, kBK / 16);
-    __syncthreads();
+  const int fa = active ? min(FM, (nrows - wm * WM + 31) / 32) : 0;
+  static_assert(FM <= 4, "main loop specialisations cover up to 4 row subtiles per wave");
+  switch (fa) {
+    case 0: mainloop(std::integral_constant<int, 0>{}); break;
+    case 1: mainloop(std::integral_constant<int, (FM >= 1 ? 1 : 0)>{}); break;
+    case 2: mainloop(std::integral_constant<int, (FM >= 2 ? 2 : 0)>{}); break;
+    case 3: mainloop(std::integral_constant<int, (FM >= 3 ? 3 : 0)>{}); break;
+    default: mainloop(std::integral_constant<int, FM>{}); break;
   }
 
   // Epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores.
@@ -207,6 +244,7 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
     constexpr int WO = GATED ? WN / 2 : WN;       // output columns per wave
 #pragma unroll
     for (int i = 0; i < FM; ++i)
+      if (i < fa)
 #pragma unroll
       for (int j = 0; j < JO; ++j)
 #pragma unroll
