@@ -62,12 +62,12 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b
 // so every global load has a whole stage to arrive.  The K of all segments
 // is one sequence of stages; rows of a partial tile and B rows past N are
 // clamped (loaded but never stored).
-template <int WAVES_M, bool GATED, bool GROUPED, bool SWZ>
-__global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
-  constexpr int NTH = 512;
+template <int NW, int WAVES_M, bool GATED, bool GROUPED, bool SWZ>
+__global__ __launch_bounds__(NW * 64, 1) void tiled_gemm_kernel(TiledArgs g) {
+  constexpr int NTH = NW * 64;
   constexpr int BM = 256, BR = 256;                 // A rows, B rows per tile
   constexpr int NOUT = GATED ? 128 : 256;           // output columns per tile
-  constexpr int WAVES_N = 8 / WAVES_M;
+  constexpr int WAVES_N = NW / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BR / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;         // 32x32 subtiles per wave
   constexpr int CPR = kBK / 8;                      // 16-byte chunks per row
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
   const bool active = wm * WM < nrows;  // this wave has rows to compute
 
   // B-tile row of this wave's n-subtile j (gated: first half gate, second up)
-  auto brow = [&](int j) -> int {
+  auto brow = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (GATED) {
       return j < FN / 2 ? wn * (WN / 2) + j * 32 : BR / 2 + wn * (WN / 2) + (j - FN / 2) * 32;
     } else {
@@ -113,12 +113,12 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
   // matrix, so chunks i < B_CH/2 read B and the others B3.  The source
   // pointers are set once per segment and advance by kBK per stage; stages
   // are loaded strictly in order.
-  static_assert(NTH / CPR == 64, "64 rows per load chunk");
+  constexpr int RPC = NTH / CPR;                    // rows per load chunk
   static_assert(!GATED || B_CH % 2 == 0, "gated B chunks split evenly between gate and up");
   int arow[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int r = i * 64 + tid / CPR;
+    const int r = i * RPC + tid / CPR;
     int src = row0 + min(r, nrows - 1);
     if constexpr (GROUPED) {
       if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
   const bf16_t* pa[A_CH];
   const bf16_t* pb[B_CH];
   int lseg = -1, lleft = 0;  // segment of the next stage to load, stages left in it
-  auto set_seg = [&](int s) {
+  auto set_seg = [&](int s) __attribute__((always_inline)) {
     const GemmSeg& sg = g.seg[s];
     lleft = sg.K / kBK;
     const int64_t be = int64_t(expert) * g.b_estride;
@@ -142,17 +142,17 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       const bool up = GATED && i >= B_CH / 2;
-      const int r = (up ? i - B_CH / 2 : i) * 64 + tid / CPR;
+      const int r = (up ? i - B_CH / 2 : i) * RPC + tid / CPR;
       pb[i] = (up ? sg.B3 : sg.B) + be + int64_t(min(n0 + r, g.N - 1)) * sg.ldb + kc8;
     }
   };
 
   uint4 ra[A_CH], rb[B_CH];
-  auto gload = [&]() {
+  auto gload = [&]() __attribute__((always_inline)) {
     while (lleft == 0) set_seg(++lseg);
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      if (i * 64 < nrows) ra[i] = ldg16(pa[i]);
+      if (i * RPC < nrows) ra[i] = ldg16(pa[i]);
       pa[i] += kBK;
     }
 #pragma unroll
@@ -162,13 +162,13 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
     }
     --lleft;
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
     bf16_t* An = As + buf * BM * kLdsK;
     bf16_t* Bn = Bs + buf * BR * kLdsK;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NTH;
-      if (i * 64 < nrows) *reinterpret_cast<uint4*>(&An[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
+      if (i * RPC < nrows) *reinterpret_cast<uint4*>(&An[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
@@ -188,9 +188,9 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
   // FA = this wave's 32-row subtiles that hold rows < nrows; the others are
   // neither read from LDS nor multiplied (a tile's padding rows cost nothing
   // beyond their clamped A loads, which whole 64-row chunks also skip)
-  auto mainloop = [&](auto fa_c) {
+  auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
     constexpr int FA = decltype(fa_c)::value;
-    auto compute = [&](int buf, int ks0, int ks1) {
+    auto compute = [&](int buf, int ks0, int ks1) __attribute__((always_inline)) {
       const bf16_t* Ab = As + buf * BM * kLdsK;
       const bf16_t* Bb = Bs + buf * BR * kLdsK;
 #pragma unroll
@@ -226,12 +226,16 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
     }
   };
   const int fa = active ? min(FM, (nrows - wm * WM + 31) / 32) : 0;
-  static_assert(FM <= 4, "main loop specialisations cover up to 4 row subtiles per wave");
+  static_assert(FM <= 8, "main loop specialisations cover up to 8 row subtiles per wave");
   switch (fa) {
     case 0: mainloop(std::integral_constant<int, 0>{}); break;
     case 1: mainloop(std::integral_constant<int, (FM >= 1 ? 1 : 0)>{}); break;
     case 2: mainloop(std::integral_constant<int, (FM >= 2 ? 2 : 0)>{}); break;
     case 3: mainloop(std::integral_constant<int, (FM >= 3 ? 3 : 0)>{}); break;
+    case 4: mainloop(std::integral_constant<int, (FM >= 4 ? 4 : 0)>{}); break;
+    case 5: mainloop(std::integral_constant<int, (FM >= 5 ? 5 : 0)>{}); break;
+    case 6: mainloop(std::integral_constant<int, (FM >= 6 ? 6 : 0)>{}); break;
+    case 7: mainloop(std::integral_constant<int, (FM >= 7 ? 7 : 0)>{}); break;
     default: mainloop(std::integral_constant<int, FM>{}); break;
   }
 
@@ -267,11 +271,11 @@ __global__ __launch_bounds__(512, 1) void tiled_gemm_kernel(TiledArgs g) {
   }
 }
 
-template <int WAVES_M, bool GATED, bool GROUPED, bool SWZ>
+template <int NW, int WAVES_M, bool GATED, bool GROUPED, bool SWZ>
 hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s) {
   constexpr int NOUT = GATED ? 128 : 256;
   const size_t lds = size_t(2) * (256 + 256) * kLdsK * sizeof(bf16_t);
-  auto kern = tiled_gemm_kernel<WAVES_M, GATED, GROUPED, SWZ>;
+  auto kern = tiled_gemm_kernel<NW, WAVES_M, GATED, GROUPED, SWZ>;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -280,7 +284,7 @@ hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s) {
   }
   const int64_t nblk = mtiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
-  kern<<<dim3{uint32_t(nblk)}, dim3{512}, lds, s>>>(a);
+  kern<<<dim3{uint32_t(nblk)}, dim3{uint32_t(NW * 64)}, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -497,8 +501,8 @@ hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
   a.C = d.C;
   a.ldc = d.ldc;
   const int64_t mt = (d.M + 255) / 256;
-  if (d.gated) return run_tiled<2, true, false, false>(a, mt, s);
-  return run_tiled<2, false, false, false>(a, mt, s);
+  if (d.gated) return run_tiled<8, 2, true, false, false>(a, mt, s);
+  return run_tiled<8, 2, false, false, false>(a, mt, s);
 }
 
 hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s) {
@@ -515,8 +519,8 @@ hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s) {
   a.C = g.C;
   a.ldc = g.ldc;
   static_assert(kTiledBM == 256, "tile table granularity");
-  if (g.gated) return run_tiled<2, true, true, true>(a, g.max_tiles, s);
-  return run_tiled<2, false, true, true>(a, g.max_tiles, s);
+  if (g.gated) return run_tiled<8, 2, true, true, true>(a, g.max_tiles, s);
+  return run_tiled<8, 2, false, true, true>(a, g.max_tiles, s);
 }
 
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s) {

@@ -5,6 +5,8 @@
 //   e2m1 weights, two per byte (even K index in the low nibble);
 //   e4m3fn activations (OCP, not the fnuz variant);
 //   one e8m0 scale (2^(code-127)) per 32 consecutive K elements.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -75,6 +77,7 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const bf16_t* __restri
 }
 
 typedef int i32x8v __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 // D(32x32) += (A fp8 x B fp4) with e8m0 scales.  Operand layout (lane l,
 // g = l/32, for one 64-wide K step): A row l%32 holds K [16g, 16g+16) in
@@ -86,9 +89,9 @@ __device__ __forceinline__ f32x16 mfma_mx(const i32x8v& a, const i32x8v& b, int 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0 /*A: fp8 e4m3*/, 4 /*B: fp4 e2m1*/, 0, sa, 0, sb);
 }
 
-constexpr int kMxBK = 128;            // K elements per LDS stage
-constexpr int kMxARow = kMxBK + 16;   // A LDS row stride (bytes)
-constexpr int kMxBRow = kMxBK / 2 + 16;  // B LDS row stride (bytes)
+constexpr int kMxBK = 128;               // K elements per LDS stage
+constexpr int kMxARow = kMxBK + 16;      // A LDS row stride (bytes; fp8)
+constexpr int kMxBRow = kMxBK / 2 + 16;  // B LDS row stride (bytes; packed fp4)
 
 struct MxArgs {
   int N, K;
@@ -100,27 +103,40 @@ struct MxArgs {
   const uint8_t* Bs;      // scales [E, N, K/32]
   const uint8_t* B3;      // gated: up projection
   const uint8_t* B3s;
-  bool gated;
   uint16_t* C;
   int64_t ldc;
   const Tile* tiles;
   const int32_t* ntiles;
 };
 
-// Grouped block-scaled GEMM.  Tile = (expert segment of <= 256 rows, 128 B
-// rows: plain -> 128 output columns, gated -> 64 gate + 64 up -> 64 output
-// columns).  4 waves stacked along M (64 rows each; a wave with no rows
-// skips its MFMAs); K in stages of 128 through a double-buffered LDS.
 template <bool GATED>
-__global__ __launch_bounds__(256, 1) void mx_grouped_kernel(MxArgs g) {
-  constexpr int BM = 256, BR = 128, NOUT = GATED ? 64 : 128;
+constexpr int mx_lds_bytes() {
+  constexpr int stage = 256 * kMxARow + 256 * kMxBRow + 512 * 4;
+  constexpr int epi = 256 * ((GATED ? 128 : 256) + 8) * 2;
+  return 2 * stage > epi ? 2 * stage : epi;
+}
+
+// Grouped block-scaled GEMM.  Macro tile = (expert segment of <= 256 rows,
+// 256 B rows: plain -> 256 output columns; gated -> 128 gate + 128 up rows ->
+// 128 output columns).  8 waves, 2 per SIMD, as 2 x 4 with 128 x 64 wave
+// tiles (4 x 2 scaled 32x32x64 MFMAs per 64-wide K step); K in stages of 128
+// through a double-buffered LDS holding A codes, B codes and both operands'
+// e8m0 scales.  Per stage: MFMAs on the first 64 K | LDS writes of the next
+// stage (loaded one stage earlier) | global loads of the stage after | MFMAs
+// on the second 64 K | barrier.  A wave multiplies only its 32-row subtiles
+// that hold rows of the tile; 64-row A chunks past the tile's rows are not
+// loaded.
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
+  constexpr int NTH = 512, BM = 256, BR = 256, NOUT = GATED ? 128 : 256;
+  constexpr int WAVES_N = 4, WM = 128, WN = 64, FM = 4, FN = 2;
   constexpr int A_STAGE = BM * kMxARow, B_STAGE = BR * kMxBRow;
-  constexpr int AS_STAGE = BM * (kMxBK / 32), BS_STAGE = BR * (kMxBK / 32);
-  constexpr int STAGE = A_STAGE + B_STAGE + AS_STAGE + BS_STAGE;
+  constexpr int STAGE = A_STAGE + B_STAGE + (BM + BR) * 4;
   extern __shared__ uint4 lds_u4[];
   uint8_t* lds = reinterpret_cast<uint8_t*>(lds_u4);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
   const uint32_t lt = xcd_swizzle(blockIdx.x, gridDim.x);
   const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
@@ -128,142 +144,166 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_kernel(MxArgs g) {
   const Tile tl = g.tiles[tm];
   const int row0 = tl.row_start, nrows = tl.nrows, expert = tl.expert;
   const int n0 = tn * NOUT;
-  const bool active = wid * 64 < nrows;
-  const int K = g.K, KB = K / 32;
+  const int K = g.K, KB = K / 32, nk = K / kMxBK;
 
-  // global -> register assignments (per stage): A 256 rows x 128 B = 8 x 16 B
-  // per thread; B 128 rows x 64 B = 2 x 16 B per thread; scales 4 B per row.
-  const uint8_t* ap[8];
-  const uint8_t* asp;
-  const uint8_t* bp[2];
-  const uint8_t* bsp = nullptr;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
+  // Loads per stage: A rows i*64 + tid/8, 16-byte chunk tid%8 (i < 4); B rows
+  // i*128 + tid/4, chunk tid%4 (i < 2; gated: i = 0 gate, i = 1 up); one
+  // 4-byte scale word: A row tid (tid < 256) or B row tid - 256.
+  auto a_src = [&](int r) __attribute__((always_inline)) -> int64_t {
     int64_t src = int64_t(row0) + min(r, nrows - 1);
     if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
-    ap[i] = g.A + src * K + kc * 16;
-  }
-  {
-    int64_t src = int64_t(row0) + min(tid, nrows - 1);
-    if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
-    asp = g.As + src * KB;
-  }
-  auto brow_ptr = [&](int r, const uint8_t* base, const uint8_t* base3, int64_t stride) -> const uint8_t* {
-    const bool up = GATED && r >= BR / 2;
-    const int rn = min(n0 + (up ? r - BR / 2 : r), g.N - 1);
-    return (up ? base3 : base) + (int64_t(expert) * g.N + rn) * stride;
+    return src;
   };
+  auto b_row = [&](int r, bool up) __attribute__((always_inline)) -> int64_t { return int64_t(expert) * g.N + min(n0 + r, g.N - 1); };
+  const uint8_t* pa[4];
+  const uint8_t* pb[2];
+  const uint8_t* ps;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pa[i] = g.A + a_src(i * 64 + tid / 8) * K + (tid % 8) * 16;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i, r = c >> 2, kc = c & 3;
-    bp[i] = brow_ptr(r, g.B, g.B3, K / 2) + kc * 16;
+    const bool up = GATED && i == 1;
+    const int r = (GATED ? 0 : i * 128) + tid / 4;
+    pb[i] = (up ? g.B3 : g.B) + b_row(r, up) * (K / 2) + (tid % 4) * 16;
   }
-  if (tid < BR) bsp = brow_ptr(tid, g.Bs, g.B3s, KB);
+  if (tid < BM) {
+    ps = g.As + a_src(tid) * KB;
+  } else {
+    const int r = tid - BM;
+    const bool up = GATED && r >= BR / 2;
+    ps = (up ? g.B3s : g.Bs) + b_row(up ? r - BR / 2 : r, up) * KB;
+  }
 
-  uint4 ra[8], rb[2];
-  uint32_t rsa = 0, rsb = 0;
-  auto gload = [&](int kt) {
-    const int ko = kt * kMxBK;
+  u32x4v ra[4], rb[2];  // native vectors, so the stage stays in registers
+  uint32_t rs;
+  auto gload = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const uint4*>(ap[i] + ko);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = *reinterpret_cast<const uint4*>(bp[i] + ko / 2);
-    rsa = *reinterpret_cast<const uint32_t*>(asp + ko / 32);
-    if (tid < BR) rsb = *reinterpret_cast<const uint32_t*>(bsp + ko / 32);
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* st = lds + buf * STAGE;
-    uint8_t* sA = st;
-    uint8_t* sB = st + A_STAGE;
-    uint8_t* sAs = sB + B_STAGE;
-    uint8_t* sBs = sAs + AS_STAGE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(sA + (c >> 3) * kMxARow + (c & 7) * 16) = ra[i];
+    for (int i = 0; i < 4; ++i) {
+      if (i * 64 < nrows) ra[i] = *reinterpret_cast<const u32x4v*>(pa[i]);
+      pa[i] += kMxBK;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(sB + (c >> 2) * kMxBRow + (c & 3) * 16) = rb[i];
+      rb[i] = *reinterpret_cast<const u32x4v*>(pb[i]);
+      pb[i] += kMxBK / 2;
     }
-    *reinterpret_cast<uint32_t*>(sAs + tid * 4) = rsa;
-    if (tid < BR) *reinterpret_cast<uint32_t*>(sBs + tid * 4) = rsb;
+    rs = *reinterpret_cast<const uint32_t*>(ps);
+    ps += kMxBK / 32;
+  };
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
+    uint8_t* sA = lds + buf * STAGE;
+    uint8_t* sB = sA + A_STAGE;
+    uint8_t* sS = sB + B_STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i * 64 < nrows) *reinterpret_cast<u32x4v*>(sA + (i * 64 + tid / 8) * kMxARow + (tid % 8) * 16) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4v*>(sB + (i * 128 + tid / 4) * kMxBRow + (tid % 4) * 16) = rb[i];
+    *reinterpret_cast<uint32_t*>(sS + tid * 4) = rs;
   };
 
-  f32x16 acc[2][4];
+  // B-tile row of this wave's n-subtile j (gated: j = 0 gate, j = 1 up)
+  auto brow = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (GATED) return j == 0 ? wn * 32 : BR / 2 + wn * 32;
+    else return wn * WN + j * 32;
+  };
+
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int nk = K / kMxBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int gsel = lane >> 5, rl = lane & 31;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    if (active) {
-      const uint8_t* st = lds + buf * STAGE;
-      const uint8_t* sA = st;
-      const uint8_t* sB = st + A_STAGE;
-      const uint8_t* sAs = sB + B_STAGE;
-      const uint8_t* sBs = sAs + AS_STAGE;
+  auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
+    constexpr int FA = decltype(fa_c)::value;
+    // B fragments first, then A fragments two at a time (each fragment is 8
+    // VGPRs; all four at once would push the 8-wave register budget)
+    auto compute = [&](int buf, int ks) __attribute__((always_inline)) {
+      if constexpr (FA > 0) {
+        const uint8_t* sA = lds + buf * STAGE;
+        const uint8_t* sB = sA + A_STAGE;
+        const uint8_t* sS = sB + B_STAGE;
+        i32x8v bf[FN];
+        int sb[FN];
 #pragma unroll
-      for (int ks = 0; ks < kMxBK / 64; ++ks) {
-        i32x8v af[2];
-        int sa[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = wid * 64 + i * 32 + rl;
-          const uint4 lo = *reinterpret_cast<const uint4*>(sA + r * kMxARow + ks * 64 + 16 * gsel);
-          const uint4 hi = *reinterpret_cast<const uint4*>(sA + r * kMxARow + ks * 64 + 32 + 16 * gsel);
-          af[i] = i32x8v{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-          sa[i] = sAs[r * 4 + ks * 2 + gsel];
+        for (int j = 0; j < FN; ++j) {
+          const int r = brow(j) + rl;
+          const uint4 bw = *reinterpret_cast<const uint4*>(sB + r * kMxBRow + ks * 32 + 16 * gsel);
+          bf[j] = i32x8v{int(bw.x), int(bw.y), int(bw.z), int(bw.w), 0, 0, 0, 0};
+          sb[j] = sS[(BM + r) * 4 + ks * 2 + gsel];
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = j * 32 + rl;
-          const uint4 bw = *reinterpret_cast<const uint4*>(sB + r * kMxBRow + ks * 32 + 16 * gsel);
-          const i32x8v bf = i32x8v{int(bw.x), int(bw.y), int(bw.z), int(bw.w), 0, 0, 0, 0};
-          const int sb = sBs[r * 4 + ks * 2 + gsel];
+        for (int i0 = 0; i0 < FA; i0 += 2) {
+          i32x8v af[2];
+          int sa[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) acc[i][j] = mfma_mx(af[i], bf, sa[i], sb, acc[i][j]);
+          for (int u = 0; u < 2; ++u) {
+            if (i0 + u < FA) {
+              const int r = wm * WM + (i0 + u) * 32 + rl;
+              const uint4 lo = *reinterpret_cast<const uint4*>(sA + r * kMxARow + ks * 64 + 16 * gsel);
+              const uint4 hi = *reinterpret_cast<const uint4*>(sA + r * kMxARow + ks * 64 + 32 + 16 * gsel);
+              af[u] = i32x8v{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+              sa[u] = sS[r * 4 + ks * 2 + gsel];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            if (i0 + u < FA)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) acc[i0 + u][j] = mfma_mx(af[u], bf[j], sa[u], sb[j], acc[i0 + u][j]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    };
+    gload();
+    lstore(0);
+    if (nk > 1) gload();
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      compute(buf, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) lstore(buf ^ 1);
+      if (kt + 2 < nk) gload();
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf, 1);
+      __syncthreads();
+    }
+  };
+  const int fa = wm * WM < nrows ? min(FM, (nrows - wm * WM + 31) / 32) : 0;
+  switch (fa) {
+    case 0: mainloop(std::integral_constant<int, 0>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    case 2: mainloop(std::integral_constant<int, 2>{}); break;
+    case 3: mainloop(std::integral_constant<int, 3>{}); break;
+    default: mainloop(std::integral_constant<int, 4>{}); break;
   }
 
-  // Epilogue (SwiGLU for gated: subtiles 0-1 gate, 2-3 up), bf16 staging in
-  // LDS, then 16-byte row-contiguous stores.
+  // Epilogue (gated: SwiGLU of subtile 0 with its up subtile 1), bf16 staging
+  // in LDS, then 16-byte row-contiguous stores.
   constexpr int CLD = NOUT + 8;
+  static_assert(BM * CLD * 2 <= mx_lds_bytes<GATED>(), "epilogue staging fits");
   bf16_t* Cs = reinterpret_cast<bf16_t*>(lds);
-  static_assert(BM * CLD * 2 <= 2 * STAGE, "epilogue staging fits");
-  if (active) {
-    constexpr int JO = GATED ? 2 : 4;
+  constexpr int JO = GATED ? 1 : FN, WO = GATED ? WN / 2 : WN;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
+    if (i < fa)
 #pragma unroll
       for (int j = 0; j < JO; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = wid * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const int col = j * 32 + rl;
+          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int col = wn * WO + j * 32 + rl;
           float x = acc[i][j][v];
-          if constexpr (GATED) x = silu_mul(x, acc[i][j + 2][v]);
+          if constexpr (GATED) x = silu_mul(x, acc[i][1][v]);
           Cs[row * CLD + col] = f32_to_bf16(x);
         }
-  }
   __syncthreads();
   constexpr int OCPR = NOUT / 8;
-  for (int c = tid; c < BM * OCPR; c += 256) {
+  for (int c = tid; c < BM * OCPR; c += NTH) {
     const int row = c / OCPR, cc = c % OCPR;
     if (row < nrows && n0 + cc * 8 < g.N) {
       *reinterpret_cast<uint4*>(g.C + (int64_t(row0) + row) * g.ldc + n0 + cc * 8) =
@@ -274,9 +314,8 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_kernel(MxArgs g) {
 
 template <bool GATED>
 hipError_t run_mx(const MxArgs& a, int64_t max_tiles, hipStream_t s) {
-  constexpr int NOUT = GATED ? 64 : 128;
-  constexpr int STAGE = 256 * kMxARow + 128 * kMxBRow + 256 * (kMxBK / 32) + 128 * (kMxBK / 32);
-  const size_t lds = size_t(2) * STAGE;
+  constexpr int NOUT = GATED ? 128 : 256;
+  constexpr size_t lds = size_t(mx_lds_bytes<GATED>());
   auto kern = mx_grouped_kernel<GATED>;
   static bool attr = false;
   if (!attr) {
@@ -286,7 +325,7 @@ hipError_t run_mx(const MxArgs& a, int64_t max_tiles, hipStream_t s) {
   }
   const int64_t nblk = max_tiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
-  kern<<<dim3{uint32_t(nblk)}, dim3{256}, lds, s>>>(a);
+  kern<<<dim3{uint32_t(nblk)}, dim3{512}, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -312,7 +351,6 @@ hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s) {
   a.Bs = g.Bs;
   a.B3 = g.B3;
   a.B3s = g.B3s;
-  a.gated = g.gated;
   a.C = g.C;
   a.ldc = g.ldc;
   a.tiles = g.tiles;
