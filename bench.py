@@ -291,8 +291,16 @@ def main():
         ai = dom_flop / dom_bytes
         mfma_peak = FP8_PEAK_TFLOPS if cfg.mxfp4 else BF16_PEAK_TFLOPS
         bound = "hbm" if ai < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
-        kern = "grouped_gemm"
-        traffic = measured_traffic(f"{dom}", cfg.name, source_hash("gemm.hip"))
+        # which kernel ran the grouped GEMMs (the library's own choice: MXFP4
+        # weights -> block-scaled kernel; <= 32 rows per expert on average ->
+        # weight-streaming kernel; otherwise the LDS-tiled kernel)
+        if cfg.mxfp4:
+            kern, src = "mx_grouped_kernel", "mx.hip"
+        elif R <= 32 * E:
+            kern, src = "skinny_grouped_kernel", "skinny.hip"
+        else:
+            kern, src = "tiled_gemm_kernel", "gemm.hip"
+        traffic = measured_traffic(f"{dom}", cfg.name, source_hash(src))
         if bound == "hbm":
             achieved = dom_bytes / dur_s / 1e9
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -46,6 +46,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// 16-byte global load (p 16-byte aligned).
+__device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
 // Workgroup id -> logical tile id such that consecutive logical ids share an
 // XCD (the hardware deals workgroups to the 8 XCDs round robin), which keeps
 // tiles that reuse the same operand rows in one L2.

@@ -11,9 +11,7 @@
 //    "TensorRT-LLM Stable LatentMoE": FC1 with its gate as one gated GEMM,
 //    then FC2).  Grouped tiles come from the device-side tile table, so no
 //    per-expert row count ever reaches the host.
-//  * skinny_grouped_kernel: decode-shaped grouped GEMMs where every expert
-//    sees a handful of rows and the cost is streaming its weights once; each
-//    wave keeps a whole K chunk of loads in flight and skips LDS.
+// (The decode-shaped weight-streaming grouped GEMM is in skinny.hip.)
 #include <type_traits>
 
 #include "common.h"
@@ -39,8 +37,6 @@ struct TiledArgs {
   uint16_t* C;
   int64_t ldc;
 };
-
-__device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // 32x32x16 bf16 MFMA: D(32x32 f32) = A(32x16) * B(16x32) + C.  Lane l feeds A
 // row l%32 and B column l%32 with K elements 8*(l/32) .. +8; it receives
@@ -288,77 +284,6 @@ hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------- skinny grouped ---
-// Block = (m-tile of <= 16 rows, 64*NS output columns); wave w owns NS
-// 16-column subtiles and runs 16x16x32 MFMAs over K in chunks of KCH steps of
-// 32, each chunk's loads issued together (the scheduling barrier keeps the
-// compiler from interleaving them with the MFMAs, which would leave only a few
-// loads in flight per wave).  Blocks take tiles in plain launch order: the
-// hardware deals consecutive blocks to different XCDs, so at any moment all
-// XCDs stream neighbouring weight rows, which measured ~20% faster here than
-// grouping an expert's blocks on one XCD.
-template <bool GATED, int KCH, int NS>
-__global__ __launch_bounds__(256) void skinny_grouped_kernel(GroupedGemm g) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  constexpr int WCOLS = 16 * NS, BCOLS = 4 * WCOLS;
-  const int tiles_n = g.N / BCOLS;
-  const uint32_t lt = blockIdx.x;
-  const int tm = int(lt / uint32_t(tiles_n)), tn = int(lt % uint32_t(tiles_n));
-  if (tm >= *g.ntiles) return;
-  const Tile tl = g.tiles[tm];
-  const int arow = min(lane & 15, tl.nrows - 1);
-  int64_t src = int64_t(tl.row_start) + arow;
-  if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
-  const int kof = (lane >> 4) * 8;
-  const bf16_t* ap = g.A + src * g.lda + kof;
-  const int nb = tn * BCOLS + wid * WCOLS + (lane & 15);
-  const bf16_t* bp[NS];
-  const bf16_t* b3p[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int64_t boff = int64_t(tl.expert) * g.b_estride + int64_t(nb + 16 * j) * g.ldb + kof;
-    bp[j] = g.B + boff;
-    b3p[j] = GATED ? g.B3 + boff : nullptr;
-  }
-  f32x4 acc[NS], acc3[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int kc = 0; kc < g.K; kc += 32 * KCH) {
-    uint4 a[KCH], b[NS][KCH], b3[NS][GATED ? KCH : 1];
-#pragma unroll
-    for (int s = 0; s < KCH; ++s) a[s] = ldg16(ap + kc + s * 32);
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-#pragma unroll
-      for (int s = 0; s < KCH; ++s) {
-        b[j][s] = ldg16(bp[j] + kc + s * 32);
-        if constexpr (GATED) b3[j][s] = ldg16(b3p[j] + kc + s * 32);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < KCH; ++s)
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        acc[j] = mfma_16x16x32(as_bf16x8(a[s]), as_bf16x8(b[j][s]), acc[j]);
-        if constexpr (GATED) acc3[j] = mfma_16x16x32(as_bf16x8(a[s]), as_bf16x8(b3[j][s]), acc3[j]);
-      }
-  }
-#pragma unroll
-  for (int j = 0; j < NS; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = (lane >> 4) * 4 + r;
-      if (row < tl.nrows) {
-        float v = acc[j][r];
-        if constexpr (GATED) v = silu_mul(v, acc3[j][r]);
-        g.C[(int64_t(tl.row_start) + row) * g.ldc + nb + 16 * j] = f32_to_bf16(v);
-      }
-    }
-}
-
 // ------------------------------------------------------- small-M dense split-K ---
 // Dense GEMMs with few rows (decode-sized batches): one 16-row x 32-column
 // output tile per workgroup; the 4 waves split the (segment-concatenated) K
@@ -521,21 +446,6 @@ hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s) {
   static_assert(kTiledBM == 256, "tile table granularity");
   if (g.gated) return run_tiled<8, 2, true, true, true>(a, g.max_tiles, s);
   return run_tiled<8, 2, false, true, true>(a, g.max_tiles, s);
-}
-
-hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s) {
-  const int64_t nblk = g.max_tiles * (g.N / 64);
-  if (nblk <= 0) return hipSuccess;
-  const dim3 grid{uint32_t(nblk)}, block{256};
-  if (g.gated) {
-    if (g.K % 128 == 0) skinny_grouped_kernel<true, 4, 1><<<grid, block, 0, s>>>(g);
-    else skinny_grouped_kernel<true, 2, 1><<<grid, block, 0, s>>>(g);
-  } else {
-    if (g.K % 256 == 0) skinny_grouped_kernel<false, 8, 1><<<grid, block, 0, s>>>(g);
-    else if (g.K % 128 == 0) skinny_grouped_kernel<false, 4, 1><<<grid, block, 0, s>>>(g);
-    else skinny_grouped_kernel<false, 2, 1><<<grid, block, 0, s>>>(g);
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s) {
