@@ -58,8 +58,10 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Route workspace: [n_s][n_t] counters, then the two tile tables.
+static_assert(LMOE_MAX_EXPERTS <= 4096, "the permutation kernels handle at most 4096 experts");
+
 struct RouteLayout {
-  size_t n_s, n_t, tiles_s, tiles_t, total;
+  size_t n_s, n_t, tiles_s, tiles_t, counts, total;
   int64_t max_s, max_t;
 };
 
@@ -77,6 +79,8 @@ RouteLayout route_layout(int64_t T, int32_t E, int32_t k) {
   off = align_up(off + size_t(L.max_s) * sizeof(Tile));
   L.tiles_t = off;
   off = align_up(off + size_t(L.max_t) * sizeof(Tile));
+  L.counts = off;  // per-chunk expert counts of the many-workgroup permutation
+  off = align_up(off + size_t(lmoe::permute_scratch_ints(R, E)) * 4);
   L.total = off;
   return L;
 }
@@ -241,7 +245,7 @@ int latent_moe_route(const lmoe_route_args* a, void* hip_stream, latent_moe_plan
       }
     }
     e = lmoe::launch_permute(p->ids, R, a->E, a->offsets, a->sorted_row, a->row_pos, p->tiles_s, p->n_s,
-                             p->tiles_t, p->n_t, s);
+                             p->tiles_t, p->n_t, reinterpret_cast<int32_t*>(ws + L.counts), s);
     if (e != hipSuccess) {
       delete p;
       return hip_fail(e, "permute");

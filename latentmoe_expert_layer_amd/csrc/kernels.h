@@ -29,9 +29,12 @@ hipError_t launch_router(const float* logits, int64_t T, int E, int k, int32_t* 
 hipError_t launch_copy_ids(const int32_t* ids_in, const float* w_in, int64_t n, int32_t* ids,
                            float* w, hipStream_t s);
 // Stable counting sort of R rows by expert plus the two tile tables.
+// scratch: permute_scratch_ints(R, E) int32 of device memory (may be NULL when
+// that is 0); large batches keep their per-chunk expert counts there.
 hipError_t launch_permute(const int32_t* ids, int64_t R, int E, int32_t* offsets, int32_t* sorted_row,
                           int32_t* row_pos, Tile* tiles_skinny, int32_t* n_skinny, Tile* tiles_tiled,
-                          int32_t* n_tiled, hipStream_t s);
+                          int32_t* n_tiled, int32_t* scratch, hipStream_t s);
+int64_t permute_scratch_ints(int64_t R, int E);
 int permute_waves(int E);  // 0 if E is too large
 
 // ---- GEMMs --------------------------------------------------------------------

@@ -284,6 +284,75 @@ __device__ __forceinline__ Scan3 block_exclusive_scan3(const int32_t (&v)[3], in
   return r;
 }
 
+// Stable scatter of rows [r0, r1) by one wave: walks its rows 64 at a time;
+// lanes with equal expert find each other with ballots over the id bits,
+// take consecutive slots in lane order from the wave's running start
+// hist[id * (NW+1) + wave], and the group's lowest lane advances it.  The
+// first kBatch * 64 ids come in registers.
+constexpr int kPermBatch = 8;
+template <int NW>
+__device__ __forceinline__ void stable_scatter(const int32_t* __restrict__ ids, int64_t R, int E, int64_t r0,
+                                               int64_t r1, const int32_t (&first)[kPermBatch], int32_t* hist,
+                                               int32_t* __restrict__ sorted_row, int32_t* __restrict__ row_pos) {
+  constexpr int S = NW + 1;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t rb = r0; rb < r1; rb += 64 * kPermBatch) {
+    int32_t idv[kPermBatch];
+    if (rb == r0) {
+#pragma unroll
+      for (int u = 0; u < kPermBatch; ++u) idv[u] = first[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kPermBatch; ++u) idv[u] = ids[min(rb + 64 * u + lane, R - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int64_t base_r = rb + 64 * u;
+      if (base_r >= r1) break;
+      const int64_t r = base_r + lane;
+      const bool valid = r < r1;
+      const int32_t id = valid ? clamp_id(idv[u], E) : 0;
+      uint64_t peers = ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (id >> b) & 1;
+        const uint64_t m = ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      int32_t base = 0;
+      if (valid) base = hist[id * S + wid];
+      const int rank = __popcll(peers & below);
+      if (valid && rank == 0) hist[id * S + wid] = base + __popcll(peers);
+      if (valid) {
+        const int32_t p = base + rank;
+        sorted_row[p] = int32_t(r);
+        row_pos[r] = p;
+      }
+    }
+  }
+}
+
+// Per-wave histogram of rows [r0, r1) into hist[id * (NW+1) + wave] (LDS
+// atomics); keeps the first kBatch * 64 ids in registers for the scatter.
+template <int NW>
+__device__ __forceinline__ void wave_histogram(const int32_t* __restrict__ ids, int64_t R, int E, int64_t r0,
+                                               int64_t r1, int32_t (&first)[kPermBatch], int32_t* hist) {
+  constexpr int S = NW + 1;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  for (int64_t rb = r0; rb < r1; rb += 64 * kPermBatch) {
+    int32_t idv[kPermBatch];
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) idv[u] = ids[min(rb + 64 * u + lane, R - 1)];
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      if (rb == r0) first[u] = idv[u];
+      if (rb + 64 * u + lane < r1) atomicAdd(&hist[clamp_id(idv[u], E) * S + wid], 1);
+    }
+  }
+}
+
 // One 1024-thread workgroup; NW waves split the rows into contiguous chunks.
 //  (1) histogram: hist[e][w] = rows of expert e in wave w's chunk (LDS
 //      atomics; the per-expert stride NW+1 is odd, so lanes with different
@@ -314,22 +383,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 
   const int64_t chunk = ((R + NW - 1) / NW + 63) / 64 * 64;
   const int64_t r0 = int64_t(wid) * chunk, r1 = min(R, r0 + chunk);
-  // ids are read kBatch rows per lane at a time with clamped (in-bounds)
-  // indices, so a batch's loads are in flight together
-  constexpr int kBatch = 8;
-  int32_t first[kBatch];
-  if (wid < NW) {
-    for (int64_t rb = r0; rb < r1; rb += 64 * kBatch) {
-      int32_t idv[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) idv[u] = ids[min(rb + 64 * u + lane, R - 1)];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (rb == r0) first[u] = idv[u];
-        if (rb + 64 * u + lane < r1) atomicAdd(&hist[clamp_id(idv[u], E) * S + wid], 1);
-      }
-    }
-  }
+  int32_t first[kPermBatch];
+  if (wid < NW) wave_histogram<NW>(ids, R, E, r0, r1, first, hist);
   __syncthreads();
 
   // (2) experts [e0, e1) belong to this thread
@@ -370,68 +425,176 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   __syncthreads();
 
   // (3) stable scatter
-  if (wid < NW) {
-    int nbits = 1;
-    while ((1 << nbits) < E) ++nbits;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t rb = r0; rb < r1; rb += 64 * kBatch) {
-      int32_t idv[kBatch];
-      if (rb == r0) {
+  if (wid < NW) stable_scatter<NW>(ids, R, E, r0, r1, first, hist, sorted_row, row_pos);
+}
+
+// -------------------------------------------------- permute, large batches ---
+// Above kPermOneWgMaxRows rows one workgroup is too slow (its waves walk
+// R/16 rows each), so the same three phases run over G = ceil(R / kPermChunk)
+// workgroups that each own kPermChunk consecutive rows, with the per-chunk
+// counts in a global scratch array counts[G][E]:
+//   count:   counts[g][e] = rows of expert e in chunk g;
+//   scan:    one workgroup turns every counts[.][e] into its exclusive prefix
+//            over chunks and scans the per-expert totals and tile counts
+//            (offsets, both tile tables);
+//   scatter: chunk g re-reads its ids, splits them over its waves as the
+//            one-workgroup kernel does, and starts expert e's rows at
+//            offsets[e] + counts[g][e].
+// Chunks are consecutive and each keeps its rows in order, so the result is
+// the same stable permutation.
+constexpr int kPermChunk = 4096;
+constexpr int64_t kPermOneWgMaxRows = 8192;
+constexpr int kPermMaxExperts = 4096;  // the scan's threads own at most 4 experts each
+
+int64_t permute_scratch_ints(int64_t R, int E) {
+  if (R <= kPermOneWgMaxRows) return 0;
+  return ((R + kPermChunk - 1) / kPermChunk) * int64_t(E);
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_count_kernel(const int32_t* __restrict__ ids, int64_t R,
+                                                                     int E, int32_t* __restrict__ counts) {
+  extern __shared__ int32_t lds[];  // [E]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPermThreads) lds[e] = 0;
+  __syncthreads();
+  constexpr int PER = kPermChunk / kPermThreads;
+  const int64_t r0 = int64_t(blockIdx.x) * kPermChunk + tid;
+  int32_t v[PER];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) idv[u] = first[u];
-      } else {
+  for (int u = 0; u < PER; ++u) v[u] = ids[min(r0 + int64_t(u) * kPermThreads, R - 1)];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) idv[u] = ids[min(rb + 64 * u + lane, R - 1)];
+  for (int u = 0; u < PER; ++u)
+    if (r0 + int64_t(u) * kPermThreads < R) atomicAdd(&lds[clamp_id(v[u], E)], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermThreads) counts[int64_t(blockIdx.x) * E + e] = lds[e];
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
+    int32_t* __restrict__ counts, int G, int64_t R, int E, int32_t* __restrict__ offsets,
+    Tile* __restrict__ tiles_a, int32_t* __restrict__ n_a, Tile* __restrict__ tiles_b, int32_t* __restrict__ n_b) {
+  __shared__ int32_t ws[3 * kPermWaves];
+  constexpr int kMaxPer = kPermMaxExperts / kPermThreads;
+  constexpr int kG = 16;  // chunk counts loaded together
+  const int tid = threadIdx.x;
+  const int per = (E + kPermThreads - 1) / kPermThreads;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int32_t tot[kMaxPer];
+  int32_t run[3] = {0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q) {
+    const int e = e0 + q;
+    tot[q] = 0;
+    if (e < e1) {
+      int32_t c = 0;
+      for (int g0 = 0; g0 < G; g0 += kG) {
+        int32_t v[kG];
+#pragma unroll
+        for (int u = 0; u < kG; ++u) v[u] = counts[int64_t(min(g0 + u, G - 1)) * E + e];
+#pragma unroll
+        for (int u = 0; u < kG; ++u)
+          if (g0 + u < G) {
+            counts[int64_t(g0 + u) * E + e] = c;
+            c += v[u];
+          }
       }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int64_t base_r = rb + 64 * u;
-        if (base_r >= r1) break;
-        const int64_t r = base_r + lane;
-        const bool valid = r < r1;
-        const int32_t id = valid ? clamp_id(idv[u], E) : 0;
-        uint64_t peers = ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-          const bool bit = (id >> b) & 1;
-          const uint64_t m = ballot(bit);
-          peers &= bit ? m : ~m;
-        }
-        int32_t base = 0;
-        if (valid) base = hist[id * S + wid];
-        const int rank = __popcll(peers & below);
-        if (valid && rank == 0) hist[id * S + wid] = base + __popcll(peers);
-        if (valid) {
-          const int32_t p = base + rank;
-          sorted_row[p] = int32_t(r);
-          row_pos[r] = p;
-        }
-      }
+      tot[q] = c;
+      run[0] += c;
+      run[1] += (c + kSkinnyBM - 1) / kSkinnyBM;
+      run[2] += (c + kTiledBM - 1) / kTiledBM;
     }
   }
+  const Scan3 sc = block_exclusive_scan3(run, ws);
+  int32_t o = sc.x[0], ta = sc.x[1], tb = sc.x[2];
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q) {
+    const int e = e0 + q;
+    if (e < e1) {
+      const int32_t cnt = tot[q];
+      offsets[e] = o;
+      for (int32_t r = 0; r < cnt; r += kSkinnyBM, ++ta) tiles_a[ta] = Tile{e, o + r, min(kSkinnyBM, cnt - r), 0};
+      for (int32_t r = 0; r < cnt; r += kTiledBM, ++tb) tiles_b[tb] = Tile{e, o + r, min(kTiledBM, cnt - r), 0};
+      o += cnt;
+    }
+  }
+  if (tid == 0) {
+    offsets[E] = int32_t(R);
+    *n_a = sc.total[1];
+    *n_b = sc.total[2];
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int E, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_row, int32_t* __restrict__ row_pos) {
+  constexpr int S = NW + 1;
+  extern __shared__ int32_t lds[];  // [E][S]
+  int32_t* hist = lds;
+  const int tid = threadIdx.x, wid = tid >> 6;
+  for (int i = tid; i < E * S; i += kPermThreads) hist[i] = 0;
+  __syncthreads();
+  constexpr int64_t kWaveRows = kPermChunk / NW;
+  static_assert(kWaveRows % 64 == 0, "whole 64-row steps per wave");
+  const int64_t c0 = int64_t(blockIdx.x) * kPermChunk, c1 = min(R, c0 + kPermChunk);
+  const int64_t r0 = min(c1, c0 + wid * kWaveRows), r1 = min(c1, r0 + kWaveRows);
+  int32_t first[kPermBatch];
+  if (wid < NW) wave_histogram<NW>(ids, R, E, r0, r1, first, hist);
+  __syncthreads();
+  for (int e = tid; e < E; e += kPermThreads) {
+    int32_t c[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) c[w] = hist[e * S + w];
+    int32_t start = offsets[e] + counts[int64_t(blockIdx.x) * E + e];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      hist[e * S + w] = start;
+      start += c[w];
+    }
+  }
+  __syncthreads();
+  if (wid < NW) stable_scatter<NW>(ids, R, E, r0, r1, first, hist, sorted_row, row_pos);
 }
 
 template <int NW>
 static hipError_t launch_permute_nw(const int32_t* ids, int64_t R, int E, int32_t* offsets,
                                     int32_t* sorted_row, int32_t* row_pos, Tile* tiles_a, int32_t* n_a,
-                                    Tile* tiles_b, int32_t* n_b, hipStream_t s) {
+                                    Tile* tiles_b, int32_t* n_b, int32_t* scratch, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)permute_kernel<NW>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kPermLdsBudget);
+    hipError_t e = hipFuncSetAttribute((const void*)permute_kernel<NW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPermLdsBudget);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)permute_scatter_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kPermLdsBudget);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  permute_kernel<NW><<<dim3(1), dim3(kPermThreads), size_t(permute_lds_bytes(E, NW)), s>>>(
-      ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b);
+  if (R <= kPermOneWgMaxRows) {
+    permute_kernel<NW><<<dim3(1), dim3(kPermThreads), size_t(permute_lds_bytes(E, NW)), s>>>(
+        ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b);
+    return hipGetLastError();
+  }
+  if (!scratch) return hipErrorInvalidValue;
+  const int64_t G = (R + kPermChunk - 1) / kPermChunk;
+  permute_count_kernel<<<dim3(uint32_t(G)), dim3(kPermThreads), size_t(E) * 4, s>>>(ids, R, E, scratch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  permute_scan_kernel<<<dim3(1), dim3(kPermThreads), 0, s>>>(scratch, int(G), R, E, offsets, tiles_a, n_a, tiles_b,
+                                                             n_b);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  permute_scatter_kernel<NW><<<dim3(uint32_t(G)), dim3(kPermThreads), size_t(permute_lds_bytes(E, NW)), s>>>(
+      ids, R, E, scratch, offsets, sorted_row, row_pos);
   return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, int64_t R, int E, int32_t* offsets, int32_t* sorted_row,
                           int32_t* row_pos, Tile* tiles_a, int32_t* n_a, Tile* tiles_b, int32_t* n_b,
-                          hipStream_t s) {
+                          int32_t* scratch, hipStream_t s) {
   switch (permute_waves(E)) {
-    case 16: return launch_permute_nw<16>(ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b, s);
-    case 8: return launch_permute_nw<8>(ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b, s);
+    case 16:
+      return launch_permute_nw<16>(ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b, scratch, s);
+    case 8:
+      return launch_permute_nw<8>(ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b, scratch, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -119,12 +119,16 @@ def test_route_threshold_paths(T, E, k):
     assert dw <= 2e-6, f"combine weights differ by {dw}"
 
 
-@pytest.mark.parametrize("R,E,heavy", [(16384, 56, False), (5000, 4096, False), (777, 13, True), (64, 1, False)])
+# 8192 rows and below: one workgroup; above: per-chunk counts, scan, scatter
+# over 4096-row chunks (ragged last chunk, 4096 experts with 8-wave histograms)
+@pytest.mark.parametrize("R,E,heavy", [(16384, 56, False), (5000, 4096, False), (777, 13, True), (64, 1, False),
+                                       (8192, 896, False), (8193, 896, False), (12289, 3, True), (20000, 4096, False),
+                                       (262144, 896, False)])
 def test_permute_ids_mode(R, E, heavy):
     log(f"permute ids R={R} E={E} heavy={heavy}")
     ids = W.zipf_ids(0, "ids", R, E, 1.1).view(R, 1)
     if heavy:
-        ids[: R // 2] = 5
+        ids[: R // 2] = min(5, E - 1)
     w = W.uniform_weights(0, "w", (R, 1))
     r = gpu_route(None, 1, ids=ids.cuda(), weights=w.cuda(), E=E)
     check_routing(r, ids.view(-1), 1, E, weights=w)
