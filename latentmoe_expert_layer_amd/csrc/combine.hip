@@ -111,11 +111,55 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
   }
 }
 
+// k == 1 without a norm (one expert-parallel rank's share): out[r] =
+// bf16(w[r] * Y[row_pos[r]]), the weighted un-permutation of the received
+// rows.  One wave per row; lane owns VEC contiguous elements of each
+// 64*VEC-wide chunk, and up to 8 chunks' loads are in flight together.
+template <int VEC>
+__global__ __launch_bounds__(256) void unpermute_kernel(const bf16_t* __restrict__ Y, const int32_t* __restrict__ row_pos,
+                                                        const float* __restrict__ w, int64_t R, int l,
+                                                        bf16_t* __restrict__ out) {
+  typedef typename VecT<VEC>::type V;
+  constexpr int kChunks = 8;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t r = int64_t(blockIdx.x) * 4 + wid;
+  if (r >= R) return;
+  const int64_t p = row_pos[r];
+  const float wr = w[r];
+  const int nch = l / (64 * VEC);
+  for (int c0 = 0; c0 < nch; c0 += kChunks) {
+    V v[kChunks];
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      const int col = min(c0 + u, nch - 1) * 64 * VEC + lane * VEC;  // past the last chunk: re-read it, unused
+      v[u] = *reinterpret_cast<const V*>(Y + p * l + col);
+    }
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      if (c0 + u < nch) {
+        float f[VEC];
+        unpack<VEC>(v[u], f);
+        uint16_t o[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) o[i] = f32_to_bf16(wr * f[i]);
+        *reinterpret_cast<V*>(out + r * l + (c0 + u) * 64 * VEC + lane * VEC) = *reinterpret_cast<const V*>(o);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* Y, const int32_t* row_pos, const float* w, int64_t T, int k, int l,
                           const uint16_t* gain, float eps, uint16_t* out, hipStream_t s) {
   const dim3 grid{uint32_t((T + 3) / 4)}, block{256};
+  if (k == 1 && !gain) {
+    if (l % 512 == 0) unpermute_kernel<8><<<grid, block, 0, s>>>(Y, row_pos, w, T, l, out);
+    else if (l % 256 == 0) unpermute_kernel<4><<<grid, block, 0, s>>>(Y, row_pos, w, T, l, out);
+    else if (l % 128 == 0) unpermute_kernel<2><<<grid, block, 0, s>>>(Y, row_pos, w, T, l, out);
+    else unpermute_kernel<1><<<grid, block, 0, s>>>(Y, row_pos, w, T, l, out);
+    return hipGetLastError();
+  }
   const size_t lds = size_t(4) * l * sizeof(float);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   if (l % 512 == 0) combine_kernel<8><<<grid, block, lds, s>>>(Y, row_pos, w, T, k, l, gain, eps, out);

@@ -205,6 +205,22 @@ def test_layer_deterministic_and_empty():
     assert y.shape == (0, 512)
 
 
+@pytest.mark.parametrize("R,E,l,I", [(300, 7, 320, 128), (1000, 56, 384, 256), (513, 3, 2048, 512)])
+def test_rows_mode_small(R, E, l, I):
+    """Expert-parallel share at small sizes, every row compared: latent widths
+    that are multiples of 64, 128 and 512 (each vector width of the weighted
+    un-permutation), on the weight-streaming (R <= 32 E) and tiled paths."""
+    cfg = W.custom(f"rows_{R}_{E}_{l}", T=R, d=0, l=l, E=E, k=1, S=0, I=I, Is=0, rows_mode=True, norm=False,
+                   zipf_s=1.1, seed=R)
+    log(f"rows mode small: {cfg}")
+    inp_dev = W.make_inputs(cfg, device="cuda")
+    r, y = run_gpu_layer(inp_dev)
+    inp = to_host(inp_dev)
+    check_routing(r, inp["ids"].view(-1), 1, cfg.E, weights=inp["weights"])
+    ref = oracle.layer(inp, inp["ids"], inp["weights"])["y"]
+    assert_parity(y.cpu(), ref)
+
+
 def test_rows_mode_ep_share_sampled():
     cfg = W.CONFIGS["ep_share"]
     log(f"ep_share rows mode: {cfg}")
