@@ -116,7 +116,7 @@ def cpu_baseline(cfg, inp_host, budget_s):
         oracle.layer(inp_host, ids, w, eval_tokens=toks)
         done += chunk
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 50 * cfg.T:
+        if el >= budget_s or done >= 10000 * cfg.T:
             break
     return {"value": done / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"route + permute of the whole {cfg.name} batch ({cfg.T} tokens), then the layer on "
