@@ -183,9 +183,12 @@ void latent_moe_free(latent_moe_plan* plan);
  * LMOE_N_STAGE_EVENTS caller-created hipEvent_t handles (passed as void*),
  * every later latent_moe_forward on this plan records events[0] before its
  * first kernel and events[i] after stage i: 1 down-projection, 2 shared
- * experts' gate/up, 3 expert FC1, 4 expert FC2, 5 combine (+ RMSNorm),
+ * experts' gate/up (and, with MXFP4 experts, the MXFP8 quantisation of the
+ * FC1 input), 3 expert FC1, 4 expert FC2, 5 combine (+ RMSNorm),
  * 6 up-projection (stages a call does not run, or runs fused into the
- * previous stage's kernel, are recorded back to back).
+ * previous stage's kernel, are recorded back to back).  events[2] and
+ * events[3] are recorded by the FC1 launch itself (hipExtLaunchKernel) at
+ * that kernel's start and end, so stage 3 is the FC1 kernel's own duration.
  * events == NULL (or n == 0) turns recording off.  The events are borrowed:
  * they must outlive their use.  Returns LMOE_EINVAL for a NULL plan or
  * another n. */

@@ -268,20 +268,15 @@ __global__ __launch_bounds__(NW * 64, 1) void tiled_gemm_kernel(TiledArgs g) {
 }
 
 template <int NW, int WAVES_M, bool GATED, bool GROUPED, bool SWZ>
-hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s) {
+hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s, hipEvent_t t0 = nullptr,
+                     hipEvent_t t1 = nullptr) {
   constexpr int NOUT = GATED ? 128 : 256;
   const size_t lds = size_t(2) * (256 + 256) * kLdsK * sizeof(bf16_t);
   auto kern = tiled_gemm_kernel<NW, WAVES_M, GATED, GROUPED, SWZ>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  if (hipError_t e = allow_dynamic_lds((const void*)kern, int(lds)); e != hipSuccess) return e;
   const int64_t nblk = mtiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
-  kern<<<dim3{uint32_t(nblk)}, dim3{uint32_t(NW * 64)}, lds, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{uint32_t(NW * 64)}, lds, s, a, t0, t1);
 }
 
 // ------------------------------------------------------- small-M dense split-K ---
@@ -430,7 +425,7 @@ hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
   return run_tiled<8, 2, false, false, false>(a, mt, s);
 }
 
-hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s) {
+hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   TiledArgs a{};
   a.M = 0;
   a.N = g.N;
@@ -444,8 +439,8 @@ hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s) {
   a.C = g.C;
   a.ldc = g.ldc;
   static_assert(kTiledBM == 256, "tile table granularity");
-  if (g.gated) return run_tiled<8, 2, true, true, true>(a, g.max_tiles, s);
-  return run_tiled<8, 2, false, true, true>(a, g.max_tiles, s);
+  if (g.gated) return run_tiled<8, 2, true, true, true>(a, g.max_tiles, s, t0, t1);
+  return run_tiled<8, 2, false, true, true>(a, g.max_tiles, s, t0, t1);
 }
 
 hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s) {

@@ -1,10 +1,26 @@
 // Host-side launchers of the LatentMoE HIP kernels (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace lmoe {
+
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per (device, kernel); thread-safe.  Host code (defined in api.hip).
+hipError_t allow_dynamic_lds(const void* kernel, int bytes);
+
+// kernel<<<grid, block, lds, s>>>(arg); with t0 / t1 set, the launch goes
+// through hipExtLaunchKernel, which records them at the kernel's own start
+// and end (the expert GEMMs' stage timing).
+template <class Arg>
+hipError_t launch_kernel(const void* kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const Arg& arg,
+                         hipEvent_t t0, hipEvent_t t1) {
+  void* args[] = {const_cast<Arg*>(&arg)};
+  if (t0 || t1) return hipExtLaunchKernel(kernel, grid, block, args, lds, s, t0, t1, 0);
+  return hipLaunchKernel(kernel, grid, block, args, lds, s);
+}
 
 // One grouped-GEMM m-tile: rows [row_start, row_start + nrows) of one expert's
 // segment in the permuted (expert-major) row order.
@@ -84,8 +100,8 @@ struct GroupedGemm {
   const int32_t* ntiles;
   int64_t max_tiles;
 };
-hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s);
-hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // ---- MXFP4 (w4a8) expert path ------------------------------------------------
 // bf16 [rows, K] -> MXFP8 e4m3 codes [rows, K] + e8m0 scales [rows, K/32].
@@ -111,7 +127,7 @@ struct GroupedMx {
   const int32_t* ntiles;
   int64_t max_tiles;
 };
-hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s);
+hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // ---- combine ----------------------------------------------------------------
 // out[t] = bf16(RMSNorm(sum_j w[t,j] Y[row_pos[t*k+j]]))   (norm skipped if gain == NULL)

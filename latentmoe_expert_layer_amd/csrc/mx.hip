@@ -313,20 +313,14 @@ __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
 }
 
 template <bool GATED>
-hipError_t run_mx(const MxArgs& a, int64_t max_tiles, hipStream_t s) {
+hipError_t run_mx(const MxArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   constexpr int NOUT = GATED ? 128 : 256;
   constexpr size_t lds = size_t(mx_lds_bytes<GATED>());
   auto kern = mx_grouped_kernel<GATED>;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  if (hipError_t e = allow_dynamic_lds((const void*)kern, int(lds)); e != hipSuccess) return e;
   const int64_t nblk = max_tiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
-  kern<<<dim3{uint32_t(nblk)}, dim3{512}, lds, s>>>(a);
-  return hipGetLastError();
+  return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512}, lds, s, a, t0, t1);
 }
 
 }  // namespace
@@ -339,7 +333,7 @@ hipError_t launch_quant_mxfp8(const uint16_t* src, int64_t rows, int K, uint8_t*
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s) {
+hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   MxArgs a{};
   a.N = g.N;
   a.K = g.K;
@@ -355,7 +349,7 @@ hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s) {
   a.ldc = g.ldc;
   a.tiles = g.tiles;
   a.ntiles = g.ntiles;
-  return g.gated ? run_mx<true>(a, g.max_tiles, s) : run_mx<false>(a, g.max_tiles, s);
+  return g.gated ? run_mx<true>(a, g.max_tiles, s, t0, t1) : run_mx<false>(a, g.max_tiles, s, t0, t1);
 }
 
 }  // namespace lmoe

@@ -559,16 +559,9 @@ template <int NW>
 static hipError_t launch_permute_nw(const int32_t* ids, int64_t R, int E, int32_t* offsets,
                                     int32_t* sorted_row, int32_t* row_pos, Tile* tiles_a, int32_t* n_a,
                                     Tile* tiles_b, int32_t* n_b, int32_t* scratch, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)permute_kernel<NW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPermLdsBudget);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)permute_scatter_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kPermLdsBudget);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  if (hipError_t e = allow_dynamic_lds((const void*)permute_kernel<NW>, kPermLdsBudget); e != hipSuccess) return e;
+  if (hipError_t e = allow_dynamic_lds((const void*)permute_scatter_kernel<NW>, kPermLdsBudget); e != hipSuccess)
+    return e;
   if (R <= kPermOneWgMaxRows) {
     permute_kernel<NW><<<dim3(1), dim3(kPermThreads), size_t(permute_lds_bytes(E, NW)), s>>>(
         ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b);

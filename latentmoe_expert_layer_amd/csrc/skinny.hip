@@ -85,19 +85,19 @@ __global__ __launch_bounds__(256) void skinny_grouped_kernel(GroupedGemm g) {
 
 }  // namespace
 
-hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s) {
+hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const int64_t nblk = g.max_tiles * (g.N / 64);
   if (nblk <= 0) return hipSuccess;
   const dim3 grid{uint32_t(nblk)}, block{256};
+  const void* kern;
   if (g.gated) {
-    if (g.K % 128 == 0) skinny_grouped_kernel<true, 4, 1><<<grid, block, 0, s>>>(g);
-    else skinny_grouped_kernel<true, 2, 1><<<grid, block, 0, s>>>(g);
+    kern = g.K % 128 == 0 ? (const void*)skinny_grouped_kernel<true, 4, 1> : (const void*)skinny_grouped_kernel<true, 2, 1>;
   } else {
-    if (g.K % 256 == 0) skinny_grouped_kernel<false, 8, 1><<<grid, block, 0, s>>>(g);
-    else if (g.K % 128 == 0) skinny_grouped_kernel<false, 4, 1><<<grid, block, 0, s>>>(g);
-    else skinny_grouped_kernel<false, 2, 1><<<grid, block, 0, s>>>(g);
+    kern = g.K % 256 == 0   ? (const void*)skinny_grouped_kernel<false, 8, 1>
+           : g.K % 128 == 0 ? (const void*)skinny_grouped_kernel<false, 4, 1>
+                            : (const void*)skinny_grouped_kernel<false, 2, 1>;
   }
-  return hipGetLastError();
+  return launch_kernel(kern, grid, block, 0, s, g, t0, t1);
 }
 
 }  // namespace lmoe
