@@ -117,8 +117,8 @@ FwdLayout fwd_layout(int64_t T, int32_t k, int32_t l, int32_t I, int32_t S, int3
   off = align_up(off + (rows ? 0 : size_t(T) * l * 2));
   L.hs = off;
   off = align_up(off + size_t(T) * S * Is * 2);
-  L.H = off;
-  off = align_up(off + size_t(R) * I * 2);
+  L.H = off;  // bf16 H (MXFP4 experts: FC1 writes it only as MXFP8, below)
+  off = align_up(off + (mx ? 0 : size_t(R) * I * 2));
   L.Y = off;
   off = align_up(off + size_t(R) * l * 2);
   L.rhat = off;
@@ -365,15 +365,17 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
     m1.B3 = static_cast<const uint8_t*>(a->w3);
     m1.B3s = a->s3;
     m1.gated = true;
-    m1.C = H;
+    m1.C = nullptr;
     m1.ldc = I;
+    m1.Cq = hq;    // FC1's epilogue writes H already quantised to MXFP8 (FC2's operand)
+    m1.Cqs = hsc;
     m1.tiles = p->tiles_t;
     m1.ntiles = p->n_t;
     m1.max_tiles = p->max_t;
     if ((e = lmoe::launch_grouped_mx(m1, s, fc1_t0, fc1_t1)) != hipSuccess) return hip_fail(e, "expert FC1 (MXFP4)");
-    if ((e = lmoe::launch_quant_mxfp8(H, R, int(I), hq, hsc, s)) != hipSuccess)
-      return hip_fail(e, "quantise FC1 output");
     lmoe::GroupedMx m2 = m1;
+    m2.Cq = nullptr;
+    m2.Cqs = nullptr;
     m2.N = int(l);
     m2.K = int(I);
     m2.A = hq;

@@ -109,7 +109,9 @@ hipError_t launch_quant_mxfp8(const uint16_t* src, int64_t rows, int K, uint8_t*
                               hipStream_t s);
 // Grouped block-scaled GEMM: MXFP8 activations (rows gathered as in
 // GroupedGemm) x MXFP4 weights [E, N, K/2] with scales [E, N, K/32]; bf16
-// output (gated: SwiGLU of gate and up).  Tiles from the 256-row table.
+// output (gated: SwiGLU of gate and up), or with Cq set the output rounded to
+// bf16 and then MXFP8-quantised as launch_quant_mxfp8 would.  Tiles from the
+// 256-row table.
 struct GroupedMx {
   int N, K;
   const uint8_t* A;
@@ -123,6 +125,8 @@ struct GroupedMx {
   bool gated;
   uint16_t* C;
   int64_t ldc;
+  uint8_t* Cq = nullptr;   // non-NULL: output written as MXFP8 codes [rows, N] (row stride ldc)
+  uint8_t* Cqs = nullptr;  //   and e8m0 scales [rows, N/32]; C is then not written
   const Tile* tiles;
   const int32_t* ntiles;
   int64_t max_tiles;

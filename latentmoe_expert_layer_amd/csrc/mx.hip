@@ -37,18 +37,11 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
   return sign | (uint32_t(e + 7) << 3) | q;           // a < 448 keeps the code <= 0x7E
 }
 
-// MXFP8 quantisation of bf16 rows [rows, K] -> e4m3 codes [rows, K] and e8m0
-// scales [rows, K/32]: scale exponent = floor(log2 amax) - 8 (clamped to
-// e8m0's range; an all-zero block gets code 0), elements = e4m3(v / 2^exp).
-// One thread per 32-element block.
-__global__ __launch_bounds__(256) void quant_mxfp8_kernel(const bf16_t* __restrict__ src, int64_t nblocks,
-                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (b >= nblocks) return;
-  const uint4* p = reinterpret_cast<const uint4*>(src + b * 32);
-  uint4 raw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) raw[i] = p[i];
+// MXFP8 quantisation of one 32-element block (OCP MX: one shared e8m0 scale
+// per 32 elements): scale exponent = floor(log2 amax) - 8 (clamped to e8m0's
+// range; an all-zero block gets code 0), elements = e4m3(v / 2^exp).  raw
+// holds the block's 32 bf16 values; codes receives 32 e4m3 bytes.
+__device__ __forceinline__ uint8_t quant_block32(const uint4 (&raw)[4], uint4 (&codes)[2]) {
   const bf16_t* h = reinterpret_cast<const bf16_t*>(raw);
   float amax = 0.0f;
 #pragma unroll
@@ -61,7 +54,6 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const bf16_t* __restri
     const int fl = ebits ? ebits - 127 : -127;
     sexp = max(-127, min(127, fl - 8));
   }
-  scales[b] = uint8_t(sexp + 127);
   const float inv = __uint_as_float(uint32_t(127 - sexp) << 23);  // 2^-sexp, exact (|sexp| <= 126 here)
   uint32_t out[8];
 #pragma unroll
@@ -71,9 +63,26 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const bf16_t* __restri
     for (int i = 0; i < 4; ++i) word |= e4m3_rne(bf16_to_f32(h[w * 4 + i]) * inv) << (8 * i);
     out[w] = word;
   }
-  uint4* q = reinterpret_cast<uint4*>(codes + b * 32);
-  q[0] = uint4{out[0], out[1], out[2], out[3]};
-  q[1] = uint4{out[4], out[5], out[6], out[7]};
+  codes[0] = uint4{out[0], out[1], out[2], out[3]};
+  codes[1] = uint4{out[4], out[5], out[6], out[7]};
+  return uint8_t(sexp + 127);
+}
+
+// MXFP8 quantisation of bf16 rows [rows, K] -> e4m3 codes [rows, K] and e8m0
+// scales [rows, K/32], one thread per 32-element block.
+__global__ __launch_bounds__(256) void quant_mxfp8_kernel(const bf16_t* __restrict__ src, int64_t nblocks,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint4* p = reinterpret_cast<const uint4*>(src + b * 32);
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = p[i];
+  uint4 q[2];
+  scales[b] = quant_block32(raw, q);
+  uint4* dst = reinterpret_cast<uint4*>(codes + b * 32);
+  dst[0] = q[0];
+  dst[1] = q[1];
 }
 
 typedef int i32x8v __attribute__((ext_vector_type(8)));
@@ -105,6 +114,8 @@ struct MxArgs {
   const uint8_t* B3s;
   uint16_t* C;
   int64_t ldc;
+  uint8_t* Cq;            // non-NULL: the output is written MXFP8-quantised (codes [rows, N], ldc)
+  uint8_t* Cqs;           //   with e8m0 scales [rows, N/32] (row stride ldc/32), and C is not written
   const Tile* tiles;
   const int32_t* ntiles;
 };
@@ -302,6 +313,26 @@ __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
           Cs[row * CLD + col] = f32_to_bf16(x);
         }
   __syncthreads();
+  if (g.Cq) {
+    // quantised output (the next GEMM's MXFP8 operand): one thread per
+    // (row, 32-column block) of the bf16 tile staged above
+    constexpr int BPR = NOUT / 32;
+    for (int c = tid; c < BM * BPR; c += NTH) {
+      const int row = c / BPR, b = c % BPR, col = n0 + b * 32;
+      if (row < nrows && col < g.N) {
+        uint4 raw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const uint4*>(&Cs[row * CLD + b * 32 + i * 8]);
+        uint4 q[2];
+        const int64_t r = int64_t(row0) + row;
+        g.Cqs[r * (g.ldc / 32) + col / 32] = quant_block32(raw, q);
+        uint4* dst = reinterpret_cast<uint4*>(g.Cq + r * g.ldc + col);
+        dst[0] = q[0];
+        dst[1] = q[1];
+      }
+    }
+    return;
+  }
   constexpr int OCPR = NOUT / 8;
   for (int c = tid; c < BM * OCPR; c += NTH) {
     const int row = c / OCPR, cc = c % OCPR;
@@ -347,6 +378,8 @@ hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s, hipEvent_t t0, h
   a.B3s = g.B3s;
   a.C = g.C;
   a.ldc = g.ldc;
+  a.Cq = g.Cq;
+  a.Cqs = g.Cqs;
   a.tiles = g.tiles;
   a.ntiles = g.ntiles;
   return g.gated ? run_mx<true>(a, g.max_tiles, s, t0, t1) : run_mx<false>(a, g.max_tiles, s, t0, t1);
