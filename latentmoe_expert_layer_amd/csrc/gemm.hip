@@ -77,12 +77,20 @@ __global__ __launch_bounds__(NW * 64, 1) void tiled_gemm_kernel(TiledArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
-  const uint32_t lt = SWZ ? xcd_swizzle(blockIdx.x, gridDim.x) : blockIdx.x;
+  // Grouped launches size the grid for an upper bound on the tile count; the
+  // blocks past the device-side count exit at once, and the XCD-aware order
+  // is taken over the real blocks only (over the whole padded grid it would
+  // put every real tile on the first few XCDs and leave the others idle).
+  uint32_t nreal = gridDim.x;
+  if constexpr (GROUPED) {
+    nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
+    if (blockIdx.x >= nreal) return;
+  }
+  const uint32_t lt = SWZ ? xcd_swizzle(blockIdx.x, nreal) : blockIdx.x;
   const int tn = int(lt % uint32_t(tiles_n));
   const int tm = int(lt / uint32_t(tiles_n));
   int expert = 0, row0, nrows;
   if constexpr (GROUPED) {
-    if (tm >= *g.ntiles) return;
     const Tile tl = g.tiles[tm];
     expert = tl.expert;
     row0 = tl.row_start;

@@ -149,9 +149,13 @@ __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
-  const uint32_t lt = xcd_swizzle(blockIdx.x, gridDim.x);
+  // the grid covers an upper bound on the tile count: blocks past the
+  // device-side count exit, and the XCD-aware order spans the real blocks
+  // only, so they spread over every XCD
+  const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
+  if (blockIdx.x >= nreal) return;
+  const uint32_t lt = xcd_swizzle(blockIdx.x, nreal);
   const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
-  if (tm >= *g.ntiles) return;
   const Tile tl = g.tiles[tm];
   const int row0 = tl.row_start, nrows = tl.nrows, expert = tl.expert;
   const int n0 = tn * NOUT;
