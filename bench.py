@@ -113,7 +113,7 @@ def cpu_baseline(cfg, inp_host, budget_s):
     done = 0
     while True:
         toks = [(done + i) % cfg.T for i in range(chunk)]
-        oracle.layer(inp_host, ids, w, eval_tokens=toks)
+        oracle.layer(inp_host, ids, w, eval_tokens=toks, act_quant=not cfg.w4a16)
         done += chunk
         el = time.perf_counter() - t0
         if el >= budget_s or done >= 10000 * cfg.T:
@@ -153,7 +153,7 @@ def main():
     # ---------------- inputs: several resident copies, distinct seeds
     wbytes = (3 * cfg.E * cfg.I * cfg.l) * (0.53 if cfg.mxfp4 else 2)
     copies = args.copies or max(2, min(8, -(-2 * LLC_BYTES // max(int(wbytes), 1))))
-    wfmt = lm.LMOE_WFMT_MXFP4 if cfg.mxfp4 else lm.LMOE_WFMT_BF16
+    wfmt = (lm.LMOE_WFMT_MXFP4_W4A16 if cfg.w4a16 else lm.LMOE_WFMT_MXFP4) if cfg.mxfp4 else lm.LMOE_WFMT_BF16
     P = lambda t: None if t is None else t.data_ptr()
     sets = []
     for c in range(copies):
@@ -289,12 +289,16 @@ def main():
         dom_flop = fc1_flop if dom == "fc1" else fc2_flop
         dur_s = stages[dom] / 1e6
         ai = dom_flop / dom_bytes
-        mfma_peak = FP8_PEAK_TFLOPS if cfg.mxfp4 else BF16_PEAK_TFLOPS
+        fp8 = cfg.mxfp4 and not cfg.w4a16   # w4a8 issues at the fp8 rate; w4a16 multiplies in bf16
+        mfma_peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
         bound = "hbm" if ai < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
         # which kernel ran the grouped GEMMs (the library's own choice: MXFP4
-        # weights -> block-scaled kernel; <= 32 rows per expert on average ->
-        # weight-streaming kernel; otherwise the LDS-tiled kernel)
-        if cfg.mxfp4:
+        # w4a8 -> block-scaled kernel; MXFP4 w4a16 -> its weight-streaming
+        # kernel; <= 32 rows per expert on average -> weight-streaming kernel;
+        # otherwise the LDS-tiled kernel)
+        if cfg.mxfp4 and cfg.w4a16:
+            kern, src = "skinny_w4a16_kernel", "skinny.hip"
+        elif cfg.mxfp4:
             kern, src = "mx_grouped_kernel", "mx.hip"
         elif R <= 32 * E:
             kern, src = "skinny_grouped_kernel", "skinny.hip"
@@ -330,7 +334,8 @@ def main():
         for n, fl, by in (("fc1", fc1_flop, fc1_bytes), ("fc2", fc2_flop, fc2_bytes)):
             us = stages[n]
             extra[f"{n}_tflops"] = round(fl / us / 1e6, 2)
-            extra[f"{n}_mfma_frac"] = round(fl / us / 1e6 / (FP8_PEAK_TFLOPS if cfg.mxfp4 else BF16_PEAK_TFLOPS), 4)
+            extra[f"{n}_mfma_frac"] = round(fl / us / 1e6 / (FP8_PEAK_TFLOPS if cfg.mxfp4 and not cfg.w4a16
+                                                              else BF16_PEAK_TFLOPS), 4)
             extra[f"{n}_hbm_frac"] = round(by / us / 1e3 / HBM_PEAK_GBS, 4)
 
     cpu = None
@@ -342,13 +347,15 @@ def main():
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 (experts: MXFP4 weights x MXFP8 activations)" if cfg.mxfp4 else "bf16",
+        "dtype": ("bf16 (experts: MXFP4 weights upcast to bf16, bf16 activations)" if cfg.w4a16 else
+                  "bf16 (experts: MXFP4 weights x MXFP8 activations)") if cfg.mxfp4 else "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights, gap-separated N(0,1) logits)",
         "config": {"workload": (f"{cfg.name}: {T} received rows, {E} local experts, latent {l}, SwiGLU I={I}, "
                                 f"Zipf({cfg.zipf_s}) expert load, combine weights given") if cfg.rows_mode else
                                (f"{cfg.name}: T={T} tokens, d={d} -> latent {l}, E={E} top-{k} + {S} shared, "
                                 f"SwiGLU I={I}, shared I={Is}, RMSNorm on"
-                                + (", MXFP4 experts (w4a8)" if cfg.mxfp4 else "")),
+                                + ((", MXFP4 experts (w4a16)" if cfg.w4a16 else ", MXFP4 experts (w4a8)")
+                                   if cfg.mxfp4 else "")),
                    "T": T, "d": d, "latent": l, "E": E, "k": k, "shared": S, "I": I, "Is": Is},
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }

@@ -18,10 +18,12 @@
  *   y    = rhat W_out^T + hs Ws2^T               latent up-projection + shared
  *
  * bf16 storage (round to nearest even) at z, H, Y, rhat, hs and y; every
- * GEMM accumulates in fp32.  The MXFP4 expert format runs "w4a8" (TokenSpeed
- * Day-0 post, "TensorRT-LLM Stable LatentMoE"): activations entering each
- * expert GEMM are quantised to MXFP8 (OCP MX v1.0 e4m3fn + one e8m0 scale per
- * 32 along K) and multiplied on CDNA4's block-scaled MFMA.
+ * GEMM accumulates in fp32.  MXFP4 expert weights (OCP MX v1.0 e2m1 + one
+ * e8m0 scale per 32 along K) run either "w4a8" (TokenSpeed Day-0 post,
+ * "TensorRT-LLM Stable LatentMoE"): activations entering each expert GEMM are
+ * quantised to MXFP8 (e4m3fn + e8m0 per 32) and multiplied on CDNA4's
+ * block-scaled MFMA; or "w4a16": bf16 activations times the exactly upcast
+ * weights on bf16 MFMAs (see the LMOE_WFMT_* values below).
  *
  * Conventions shared by every call
  *  - All tensors are row-major and contiguous; weights are [out, in] (the
@@ -53,7 +55,18 @@ extern "C" {
 #endif
 
 enum { LMOE_OK = 0, LMOE_EINVAL = 1, LMOE_EUNSUPPORTED = 2, LMOE_EHIP = 3 };
-enum { LMOE_WFMT_BF16 = 0, LMOE_WFMT_MXFP4 = 1 };
+/* Routed-expert weight formats (lmoe_forward_args.wfmt):
+ *  LMOE_WFMT_BF16        bf16 weights.
+ *  LMOE_WFMT_MXFP4       MXFP4 weights, "w4a8": the expert GEMMs' activations are
+ *                        quantised to MXFP8 and multiplied on the block-scaled
+ *                        fp8 x fp4 MFMA (the large-batch mode).
+ *  LMOE_WFMT_MXFP4_W4A16 the same MXFP4 weights, "w4a16": activations stay bf16;
+ *                        the weights are upcast to bf16 inside the K loop and
+ *                        multiplied on bf16 MFMAs (the small-batch mode, TokenSpeed
+ *                        Day-0 post, "TensorRT-LLM Stable LatentMoE").  Only
+ *                        decode-shaped batches (T*k <= 32*E): a larger batch
+ *                        returns LMOE_EUNSUPPORTED and nothing is enqueued. */
+enum { LMOE_WFMT_BF16 = 0, LMOE_WFMT_MXFP4 = 1, LMOE_WFMT_MXFP4_W4A16 = 2 };
 
 /* Limits of this build. */
 #define LMOE_MAX_EXPERTS_LOGITS 1024 /* E in logits mode (router keeps E/64 logits per lane) */
@@ -127,16 +140,16 @@ int latent_moe_route(const lmoe_route_args* args, void* hip_stream, latent_moe_p
  *
  * Dimensions: d (hidden), l (latent), I (routed intermediate), Is (shared
  * intermediate) are multiples of 64 (l and I multiples of 128 with MXFP4
- * weights); l <= 4096; 0 <= S <= 4 shared experts; wfmt is LMOE_WFMT_BF16
- * or LMOE_WFMT_MXFP4.
+ * weights); l <= 4096; 0 <= S <= 4 shared experts; wfmt is one of the
+ * LMOE_WFMT_* values.
  * Arguments (device pointers, bf16 unless noted):
  *   x        [T,d]          hidden states (rows mode: latent rows [T,l])
  *   w_in     [l,d]          latent down-projection; NULL selects rows mode
  *   w1, w3   [E,I,l]        routed gate / up projections
- *                           (MXFP4: u8 [E,I,l/2], two e2m1 codes per byte, even
- *                           K index in the low nibble)
+ *                           (either MXFP4 format: u8 [E,I,l/2], two e2m1 codes
+ *                           per byte, even K index in the low nibble)
  *   w2       [E,l,I]        routed down projection (MXFP4: u8 [E,l,I/2])
- *   s1, s3   u8 [E,I,l/32]  e8m0 block scales (MXFP4 only, else NULL)
+ *   s1, s3   u8 [E,I,l/32]  e8m0 block scales (MXFP4 formats only, else NULL)
  *   s2       u8 [E,l,I/32]
  *   norm_w   [l]            routed-latent RMSNorm gain, or NULL for no norm
  *   norm_eps                RMSNorm epsilon
@@ -147,7 +160,7 @@ int latent_moe_route(const lmoe_route_args* args, void* hip_stream, latent_moe_p
  *                           rank's share; plan from ids mode, k == 1, S == 0):
  *                           y [T,l] = w[r] * Y[r], rows in received order.
  *   workspace >= latent_moe_forward_workspace_size(...) bytes (intermediates
- *             z, hs, H, Y, rhat and the MXFP8 activation copies)
+ *             z, hs, H, Y, rhat and, for w4a8, the MXFP8 activation copies)
  * Inputs are read-only; y and the workspace are written.  x, the weights and
  * y must not overlap the workspace.
  */

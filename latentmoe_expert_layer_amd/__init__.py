@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblatent_moe.so")
 
 LMOE_OK, LMOE_EINVAL, LMOE_EUNSUPPORTED, LMOE_EHIP = 0, 1, 2, 3
-LMOE_WFMT_BF16, LMOE_WFMT_MXFP4 = 0, 1
+LMOE_WFMT_BF16, LMOE_WFMT_MXFP4, LMOE_WFMT_MXFP4_W4A16 = 0, 1, 2
 _ERRNAMES = {1: "LMOE_EINVAL", 2: "LMOE_EUNSUPPORTED", 3: "LMOE_EHIP"}
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -196,9 +196,10 @@ def route(logits: Optional[torch.Tensor] = None, k: int = 1, *, ids: Optional[to
 
 def forward(routing: Routing, x: torch.Tensor, w1, w3, w2, *, w_in=None, w_out=None, ws1=None, ws3=None,
             ws2=None, norm_w=None, eps: float = 1e-6, s1=None, s3=None, s2=None, mxfp4: bool = False,
-            y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-            I: Optional[int] = None) -> torch.Tensor:
-    """One LatentMoE forward on the routed rows; returns y (bf16)."""
+            w4a16: bool = False, y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            stream=None, I: Optional[int] = None) -> torch.Tensor:
+    """One LatentMoE forward on the routed rows; returns y (bf16).  mxfp4: the
+    routed weights are MXFP4 codes + scales, run w4a8, or w4a16 if w4a16 is set."""
     rows = w_in is None
     T = routing.T
     if rows:
@@ -209,7 +210,7 @@ def forward(routing: Routing, x: torch.Tensor, w1, w3, w2, *, w_in=None, w_out=N
         I = w1.shape[1]
     S = 0 if ws1 is None else ws1.shape[0]
     Is = 0 if ws1 is None else ws1.shape[1]
-    wfmt = LMOE_WFMT_MXFP4 if mxfp4 else LMOE_WFMT_BF16
+    wfmt = (LMOE_WFMT_MXFP4_W4A16 if w4a16 else LMOE_WFMT_MXFP4) if mxfp4 else LMOE_WFMT_BF16
     ws_bytes = forward_workspace_size(T, routing.E, routing.k, d, l, I, S, Is, wfmt, rows)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=x.device)
@@ -226,15 +227,15 @@ def forward(routing: Routing, x: torch.Tensor, w1, w3, w2, *, w_in=None, w_out=N
 def run_layer(inp: dict, stream=None, norm=True):
     """Route + forward for a ``workloads.make_inputs`` dict whose tensors are on the GPU."""
     cfg = inp["cfg"]
+    mx = cfg.mxfp4
+    wts = dict(s1=inp.get("s1"), s3=inp.get("s3"), s2=inp.get("s2"), mxfp4=mx, w4a16=cfg.w4a16, I=cfg.I)
+    w1, w3, w2 = (inp.get(n + ("q" if mx else "")) for n in ("w1", "w3", "w2"))
     if cfg.rows_mode:
         r = route(ids=inp["ids"], weights=inp["weights"], E=cfg.E, k=1, stream=stream)
-        y = forward(r, inp["x"], inp["w1"], inp["w3"], inp["w2"], stream=stream)
+        y = forward(r, inp["x"], w1, w3, w2, stream=stream, **wts)
         return r, y
     r = route(inp["logits"], cfg.k, stream=stream)
-    mx = cfg.mxfp4
-    y = forward(r, inp["x"], inp.get("w1q" if mx else "w1"), inp.get("w3q" if mx else "w3"),
-                inp.get("w2q" if mx else "w2"), w_in=inp["w_in"], w_out=inp["w_out"], ws1=inp.get("ws1"),
+    y = forward(r, inp["x"], w1, w3, w2, w_in=inp["w_in"], w_out=inp["w_out"], ws1=inp.get("ws1"),
                 ws3=inp.get("ws3"), ws2=inp.get("ws2"), norm_w=inp.get("norm_w") if norm else None,
-                eps=cfg.eps, s1=inp.get("s1"), s3=inp.get("s3"), s2=inp.get("s2"), mxfp4=mx, I=cfg.I,
-                stream=stream)
+                eps=cfg.eps, stream=stream, **wts)
     return r, y

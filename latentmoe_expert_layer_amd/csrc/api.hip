@@ -153,8 +153,9 @@ int check_fwd_dims(const latent_moe_plan* p, const lmoe_forward_args* a, bool ro
   if (a->I <= 0 || a->I % 64) return fail(LMOE_EINVAL, "I=%d is not a positive multiple of 64", a->I);
   if (a->l > 4096) return fail(LMOE_EUNSUPPORTED, "l=%d > 4096", a->l);
   if (a->S < 0 || a->S > LMOE_MAX_SHARED) return fail(LMOE_EINVAL, "S=%d outside [0,%d]", a->S, LMOE_MAX_SHARED);
-  if (a->wfmt != LMOE_WFMT_BF16 && a->wfmt != LMOE_WFMT_MXFP4) return fail(LMOE_EINVAL, "unknown wfmt %d", a->wfmt);
-  if (a->wfmt == LMOE_WFMT_MXFP4) {
+  if (a->wfmt != LMOE_WFMT_BF16 && a->wfmt != LMOE_WFMT_MXFP4 && a->wfmt != LMOE_WFMT_MXFP4_W4A16)
+    return fail(LMOE_EINVAL, "unknown wfmt %d", a->wfmt);
+  if (a->wfmt != LMOE_WFMT_BF16) {
     if (a->l % 128 || a->I % 128)
       return fail(LMOE_EINVAL, "MXFP4 experts need l and I multiples of 128 (got %d, %d)", a->l, a->I);
     if (!a->s1 || !a->s3 || !a->s2) return fail(LMOE_EINVAL, "MXFP4 experts need scales s1, s3 and s2");
@@ -188,7 +189,7 @@ size_t latent_moe_forward_workspace_size(int64_t T, int32_t E, int32_t k, int32_
   (void)E;
   (void)d;
   if (T < 0 || k < 1 || l <= 0 || I <= 0 || S < 0 || (S > 0 && Is <= 0)) return 0;
-  if (wfmt != LMOE_WFMT_BF16 && wfmt != LMOE_WFMT_MXFP4) return 0;
+  if (wfmt != LMOE_WFMT_BF16 && wfmt != LMOE_WFMT_MXFP4 && wfmt != LMOE_WFMT_MXFP4_W4A16) return 0;
   return fwd_layout(T, k, l, I, S, rows_mode ? 0 : Is, rows_mode != 0, wfmt == LMOE_WFMT_MXFP4).total;
 }
 
@@ -289,6 +290,11 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   const int64_t T = p->T, R = p->T * p->k;
   const int32_t S = rows ? 0 : a->S;
   const bool mx = a->wfmt == LMOE_WFMT_MXFP4;
+  const bool w4a16 = a->wfmt == LMOE_WFMT_MXFP4_W4A16;
+  if (w4a16 && R > int64_t(32) * p->E)
+    return fail(LMOE_EUNSUPPORTED,
+                "MXFP4 w4a16 runs decode-shaped batches only (T*k=%lld > 32*E=%lld); use LMOE_WFMT_MXFP4 (w4a8)",
+                (long long)R, 32LL * p->E);
   const FwdLayout L = fwd_layout(T, p->k, a->l, a->I, S, S ? a->Is : 0, rows, mx);
   if (!a->workspace || a->workspace_bytes < L.total)
     return fail(LMOE_EINVAL, "forward workspace too small: %zu < %zu", a->workspace_bytes, L.total);
@@ -390,6 +396,43 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
     m2.C = Y;
     m2.ldc = l;
     if ((e = lmoe::launch_grouped_mx(m2, s)) != hipSuccess) return hip_fail(e, "expert FC2 (MXFP4)");
+    if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
+  } else if (w4a16) {
+    // w4a16: bf16 activations, MXFP4 weights upcast in the weight-streaming kernel
+    lmoe::GroupedW4 q1{};
+    q1.N = int(I);
+    q1.K = int(l);
+    q1.A = rows ? x : z;
+    q1.lda = l;
+    q1.a_rows = p->sorted_row;
+    q1.a_row_div = p->k;
+    q1.B = static_cast<const uint8_t*>(a->w1);
+    q1.Bs = a->s1;
+    q1.B3 = static_cast<const uint8_t*>(a->w3);
+    q1.B3s = a->s3;
+    q1.gated = true;
+    q1.C = H;
+    q1.ldc = I;
+    q1.tiles = p->tiles_s;
+    q1.ntiles = p->n_s;
+    q1.max_tiles = p->max_s;
+    if ((e = lmoe::launch_grouped_w4a16(q1, s, fc1_t0, fc1_t1)) != hipSuccess)
+      return hip_fail(e, "expert FC1 (MXFP4 w4a16)");
+    lmoe::GroupedW4 q2 = q1;
+    q2.N = int(l);
+    q2.K = int(I);
+    q2.A = H;
+    q2.lda = I;
+    q2.a_rows = nullptr;
+    q2.a_row_div = 1;
+    q2.B = static_cast<const uint8_t*>(a->w2);
+    q2.Bs = a->s2;
+    q2.B3 = nullptr;
+    q2.B3s = nullptr;
+    q2.gated = false;
+    q2.C = Y;
+    q2.ldc = l;
+    if ((e = lmoe::launch_grouped_w4a16(q2, s)) != hipSuccess) return hip_fail(e, "expert FC2 (MXFP4 w4a16)");
     if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
   } else {
     const bool skinny = R <= int64_t(32) * p->E;

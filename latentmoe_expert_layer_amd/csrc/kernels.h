@@ -103,6 +103,29 @@ struct GroupedGemm {
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
+// Grouped, decode-shaped, MXFP4 weights with bf16 activations (w4a16): as
+// GroupedGemm with the skinny tile table, but B / B3 are e2m1 codes [E, N, K/2]
+// (even K in the low nibble) with e8m0 scales Bs / B3s [E, N, K/32], upcast to
+// bf16 in registers.  K is a multiple of 128.
+struct GroupedW4 {
+  int N, K;
+  const uint16_t* A;
+  int64_t lda;
+  const int32_t* a_rows;
+  int a_row_div;
+  const uint8_t* B;
+  const uint8_t* Bs;
+  const uint8_t* B3;
+  const uint8_t* B3s;
+  bool gated;
+  uint16_t* C;
+  int64_t ldc;
+  const Tile* tiles;
+  const int32_t* ntiles;
+  int64_t max_tiles;
+};
+hipError_t launch_grouped_w4a16(const GroupedW4& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+
 // ---- MXFP4 (w4a8) expert path ------------------------------------------------
 // bf16 [rows, K] -> MXFP8 e4m3 codes [rows, K] + e8m0 scales [rows, K/32].
 hipError_t launch_quant_mxfp8(const uint16_t* src, int64_t rows, int K, uint8_t* codes, uint8_t* scales,

@@ -83,7 +83,145 @@ __global__ __launch_bounds__(256) void skinny_grouped_kernel(GroupedGemm g) {
     }
 }
 
+// ------------------------------------------------------ skinny w4a16 (MXFP4) ---
+// TokenSpeed Day-0 post, "TensorRT-LLM Stable LatentMoE": w4a16 keeps the
+// activations in bf16 and is the small-batch mode of the MXFP4 experts.  The
+// layout of skinny_grouped_kernel (16-row tile; NS 16-column subtiles per
+// wave, so a workgroup covers 64*NS columns), with the weights read as e2m1
+// codes and upcast in registers by gfx950's scaled conversion (exact: an e2m1
+// value times a power of two).  K is taken in chunks of 128: lane (n, gq) loads the 16 code bytes
+// of row n at K offset 32*gq of the chunk and their one e8m0 scale, and k-step
+// s of the chunk multiplies codes 8s .. 8s+7 of them, so lane gq of step s
+// covers K = chunk + 32*gq + 8s .. +8; the A fragments take the same K order.
+
+// e8m0 scale code -> the fp32 multiplier 2^(code-127) (code 0: 2^-127, a
+// denormal; 255: NaN), the operand the scaled conversion takes.
+__device__ __forceinline__ float e8m0_multiplier(uint32_t c) {
+  return __uint_as_float(c == 0 ? 0x00400000u : (c == 255 ? 0x7fc00000u : c << 23));
+}
+
+// 8 e2m1 codes (one dword, K ascending from the low nibble) x scale -> bf16x8.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  const bf16x4_t lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const bf16x4_t hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <bool GATED, int NCH, int NS>
+__global__ __launch_bounds__(256) void skinny_w4a16_kernel(GroupedW4 g) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  constexpr int BCOLS = 64 * NS;  // output columns per workgroup (NS 16-column subtiles per wave)
+  const int tiles_n = g.N / BCOLS;
+  const uint32_t lt = blockIdx.x;
+  const int tm = int(lt / uint32_t(tiles_n)), tn = int(lt % uint32_t(tiles_n));
+  if (tm >= *g.ntiles) return;
+  const Tile tl = g.tiles[tm];
+  const int arow = min(lane & 15, tl.nrows - 1);
+  int64_t src = int64_t(tl.row_start) + arow;
+  if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
+  const int gq = lane >> 4;
+  const bf16_t* ap = g.A + src * g.lda + 32 * gq;
+  const int nb = tn * BCOLS + wid * 16 * NS + (lane & 15);  // column of subtile 0
+  const uint8_t* bp[NS];
+  const uint8_t* sp[NS];
+  const uint8_t* b3p[NS];
+  const uint8_t* s3p[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int64_t wrow = int64_t(tl.expert) * g.N + nb + 16 * j;  // weight row of this lane
+    bp[j] = g.B + wrow * (g.K / 2) + 16 * gq;
+    sp[j] = g.Bs + wrow * (g.K / 32);
+    b3p[j] = GATED ? g.B3 + wrow * (g.K / 2) + 16 * gq : nullptr;
+    s3p[j] = GATED ? g.B3s + wrow * (g.K / 32) : nullptr;
+  }
+  f32x4 acc[NS], acc3[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int kc = 0; kc < g.K; kc += 128 * NCH) {
+    uint4 a[NCH][4], b[NS][NCH], b3[NS][GATED ? NCH : 1];
+    uint32_t sc[NS][NCH], sc3[NS][GATED ? NCH : 1];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int k0 = kc + 128 * c;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) a[c][st] = ldg16(ap + k0 + 8 * st);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        b[j][c] = *reinterpret_cast<const uint4*>(bp[j] + k0 / 2);
+        sc[j][c] = *reinterpret_cast<const uint32_t*>(sp[j] + k0 / 32);  // the chunk's 4 scales; byte gq is this lane's
+        if constexpr (GATED) {
+          b3[j][c] = *reinterpret_cast<const uint4*>(b3p[j] + k0 / 2);
+          sc3[j][c] = *reinterpret_cast<const uint32_t*>(s3p[j] + k0 / 32);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const float f = e8m0_multiplier((sc[j][c] >> (8 * gq)) & 0xffu);
+        const uint32_t w[4] = {b[j][c].x, b[j][c].y, b[j][c].z, b[j][c].w};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          acc[j] = mfma_16x16x32(as_bf16x8(a[c][st]), fp4x8_to_bf16(w[st], f), acc[j]);
+        if constexpr (GATED) {
+          const float f3 = e8m0_multiplier((sc3[j][c] >> (8 * gq)) & 0xffu);
+          const uint32_t w3[4] = {b3[j][c].x, b3[j][c].y, b3[j][c].z, b3[j][c].w};
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            acc3[j] = mfma_16x16x32(as_bf16x8(a[c][st]), fp4x8_to_bf16(w3[st], f3), acc3[j]);
+        }
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < NS; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = (lane >> 4) * 4 + r;
+      if (row < tl.nrows) {
+        float v = acc[j][r];
+        if constexpr (GATED) v = silu_mul(v, acc3[j][r]);
+        g.C[(int64_t(tl.row_start) + row) * g.ldc + nb + 16 * j] = f32_to_bf16(v);
+      }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_grouped_w4a16(const GroupedW4& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  // 16-column subtiles per wave: two for the gated FC1 (two weight matrices
+  // per subtile), four for FC2 (measured best at the decode shape), fewer
+  // when N does not divide
+  const int want = g.gated ? 2 : 4;
+  const int ns = want == 4 && g.N % 256 == 0 ? 4 : (g.N % 128 == 0 ? 2 : 1);
+  const int64_t nblk = g.max_tiles * (g.N / (64 * ns));
+  if (nblk <= 0) return hipSuccess;
+  const dim3 grid{uint32_t(nblk)}, block{256};
+  const bool two = g.K % 256 == 0;
+  const void* kern;
+#define LMOE_W4_PICK(NS_)                                                                                 \
+  kern = g.gated ? (two ? (const void*)skinny_w4a16_kernel<true, 2, NS_> : (const void*)skinny_w4a16_kernel<true, 1, NS_>) \
+                 : (two ? (const void*)skinny_w4a16_kernel<false, 2, NS_> : (const void*)skinny_w4a16_kernel<false, 1, NS_>)
+  if (ns == 4) {
+    LMOE_W4_PICK(4);
+  } else if (ns == 2) {
+    LMOE_W4_PICK(2);
+  } else {
+    LMOE_W4_PICK(1);
+  }
+#undef LMOE_W4_PICK
+  return launch_kernel(kern, grid, block, 0, s, g, t0, t1);
+}
 
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const int64_t nblk = g.max_tiles * (g.N / 64);

@@ -50,6 +50,12 @@ def test_workspace_sizes():
     assert need <= f <= need + 16 * 256
     r = lm.forward_workspace_size(16384, 56, 1, 0, 2048, 512, 0, 0, rows_mode=True)
     assert 2 * (16384 * 512 + 16384 * 2048) <= r
+    # MXFP4 w4a16 keeps bf16 intermediates: the bf16 layout; w4a8 adds MXFP8
+    # copies but no bf16 H; unknown formats size to 0
+    bf = lm.forward_workspace_size(256, 896, 16, 512, 256, 256, 2, 256, lm.LMOE_WFMT_BF16)
+    assert lm.forward_workspace_size(256, 896, 16, 512, 256, 256, 2, 256, lm.LMOE_WFMT_MXFP4_W4A16) == bf
+    assert lm.forward_workspace_size(256, 896, 16, 512, 256, 256, 2, 256, lm.LMOE_WFMT_MXFP4) > 0
+    assert lm.forward_workspace_size(256, 896, 16, 512, 256, 256, 2, 256, 3) == 0
 
 
 def _route_args(lm, **kw):

@@ -138,25 +138,26 @@ def test_permute_ids_mode(R, E, heavy):
 def run_gpu_layer(inp_dev, norm=True):
     cfg = inp_dev["cfg"]
     T = cfg.T
-    wfmt = lm.LMOE_WFMT_MXFP4 if cfg.mxfp4 else lm.LMOE_WFMT_BF16
+    mx = cfg.mxfp4
+    wfmt = (lm.LMOE_WFMT_MXFP4_W4A16 if cfg.w4a16 else lm.LMOE_WFMT_MXFP4) if mx else lm.LMOE_WFMT_BF16
+    w1, w3, w2 = (inp_dev[n + ("q" if mx else "")] for n in ("w1", "w3", "w2"))
+    wts = dict(s1=inp_dev.get("s1"), s3=inp_dev.get("s3"), s2=inp_dev.get("s2"), mxfp4=mx, w4a16=cfg.w4a16,
+               I=cfg.I)
     if cfg.rows_mode:
         r = gpu_route(None, 1, ids=inp_dev["ids"], weights=inp_dev["weights"], E=cfg.E)
         nbytes = lm.forward_workspace_size(T, cfg.E, 1, 0, cfg.l, cfg.I, 0, 0, wfmt, True)
         ws = poison_(torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
         y = poison_(torch.empty(T, cfg.l, dtype=torch.bfloat16, device="cuda"))
-        lm.forward(r, inp_dev["x"], inp_dev["w1"], inp_dev["w3"], inp_dev["w2"], y=y, workspace=ws)
+        lm.forward(r, inp_dev["x"], w1, w3, w2, y=y, workspace=ws, **wts)
         torch.cuda.synchronize()
         return r, y
     r = gpu_route(inp_dev["logits"], cfg.k)
     nbytes = lm.forward_workspace_size(T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is, wfmt, False)
     ws = poison_(torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
     y = poison_(torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda"))
-    mx = cfg.mxfp4
-    lm.forward(r, inp_dev["x"], inp_dev["w1q" if mx else "w1"], inp_dev["w3q" if mx else "w3"],
-               inp_dev["w2q" if mx else "w2"], w_in=inp_dev["w_in"], w_out=inp_dev["w_out"],
+    lm.forward(r, inp_dev["x"], w1, w3, w2, w_in=inp_dev["w_in"], w_out=inp_dev["w_out"],
                ws1=inp_dev.get("ws1"), ws3=inp_dev.get("ws3"), ws2=inp_dev.get("ws2"),
-               norm_w=inp_dev.get("norm_w") if norm else None, eps=cfg.eps, s1=inp_dev.get("s1"),
-               s3=inp_dev.get("s3"), s2=inp_dev.get("s2"), mxfp4=mx, I=cfg.I, y=y, workspace=ws)
+               norm_w=inp_dev.get("norm_w") if norm else None, eps=cfg.eps, y=y, workspace=ws, **wts)
     torch.cuda.synchronize()
     return r, y
 
@@ -317,6 +318,60 @@ def test_mxfp4_layer_parity_small(name, dims):
     r, y = run_gpu_layer(to_device(inp))
     check_routing(r, inp["logits"], cfg.k, cfg.E)
     assert_rowwise(y.cpu(), ref["y"])
+
+
+W4A16_LAYERS = [
+    ("decode_w4a16", None),
+    # ragged T, experts without rows, l = 384 (K not a multiple of 256: one 128-wide chunk per batch)
+    ("w4_ragged", dict(T=77, d=128, l=384, E=40, k=8, S=2, I=256, Is=64, mxfp4=True, w4a16=True)),
+    ("w4_small", dict(T=203, d=192, l=256, E=40, k=3, S=1, I=128, Is=64, mxfp4=True, w4a16=True)),
+    ("w4_single", dict(T=1, d=128, l=128, E=16, k=4, S=0, I=128, Is=0, mxfp4=True, w4a16=True)),
+]
+
+
+@pytest.mark.parametrize("name,dims", W4A16_LAYERS, ids=[n for n, _ in W4A16_LAYERS])
+@pytest.mark.parametrize("norm", ["ones", "random"])
+def test_w4a16_layer_parity(name, dims, norm):
+    """w4a16: bf16 activations x MXFP4 weights upcast in the K loop, against the
+    oracle with the same dequantised weights and no activation quantisation.
+    The upcast is exact, so this is the bf16 bar (every element)."""
+    cfg = W.CONFIGS[name] if dims is None else W.custom(name, **dims)
+    log(f"w4a16 layer {name} norm={norm}: {cfg}")
+    inp = W.make_inputs(cfg, norm_w=norm)
+    ref = oracle.run(inp, act_quant=False)
+    r, y = run_gpu_layer(to_device(inp))
+    check_routing(r, inp["logits"], cfg.k, cfg.E)
+    assert_parity(y.cpu(), ref["y"])
+
+
+def test_w4a16_rows_mode():
+    """w4a16 on one expert-parallel rank's received rows (k = 1, Zipf load)."""
+    cfg = W.custom("w4_rows", T=600, d=0, l=256, E=56, k=1, S=0, I=256, Is=0, rows_mode=True, norm=False,
+                   zipf_s=1.1, seed=5, mxfp4=True, w4a16=True)
+    log(f"w4a16 rows mode: {cfg}")
+    inp_dev = W.make_inputs(cfg, device="cuda")
+    r, y = run_gpu_layer(inp_dev)
+    inp = to_host(inp_dev)
+    check_routing(r, inp["ids"].view(-1), 1, cfg.E, weights=inp["weights"])
+    ref = oracle.layer(inp, inp["ids"], inp["weights"], act_quant=False)["y"]
+    assert_parity(y.cpu(), ref)
+
+
+def test_w4a16_rejects_large_batches():
+    """w4a16 serves decode-shaped batches only; a larger one is refused before
+    anything is enqueued (the output keeps its poison)."""
+    cfg = W.custom("w4_big", T=600, d=128, l=128, E=8, k=2, S=0, I=128, Is=0, mxfp4=True, w4a16=True)
+    inp_dev = to_device(W.make_inputs(cfg))
+    r = gpu_route(inp_dev["logits"], cfg.k)
+    y = poison_(torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device="cuda"))
+    before = y.clone()
+    with pytest.raises(lm.LatentMoeError) as ei:
+        lm.forward(r, inp_dev["x"], inp_dev["w1q"], inp_dev["w3q"], inp_dev["w2q"], w_in=inp_dev["w_in"],
+                   w_out=inp_dev["w_out"], s1=inp_dev["s1"], s3=inp_dev["s3"], s2=inp_dev["s2"], mxfp4=True,
+                   w4a16=True, I=cfg.I, y=y)
+    assert ei.value.code == lm.LMOE_EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), before.view(torch.int16))
 
 
 def test_mxfp4_full_size_sampled():

@@ -47,6 +47,7 @@ class LayerConfig:
     Is: int           # shared SwiGLU intermediate
     rows_mode: bool = False   # expert-parallel share: ids + weights given, no projections
     mxfp4: bool = False       # routed expert weights in MXFP4
+    w4a16: bool = False       # with mxfp4: bf16 activations (else MXFP8 activations, w4a8)
     norm: bool = True         # routed-latent RMSNorm with gain 1
     eps: float = 1e-6
     zipf_s: float = 0.0       # rows mode: Zipf exponent of the expert load
@@ -66,6 +67,9 @@ CONFIGS = {
     # prefill shape at 16384 tokens with MXFP4 routed experts
     "prefill_mxfp4": LayerConfig("prefill_mxfp4", T=16384, d=7168, l=2048, E=896, k=16, S=2,
                                  I=512, Is=512, mxfp4=True),
+    # the decode batch with MXFP4 routed experts and bf16 activations (w4a16)
+    "decode_w4a16": LayerConfig("decode_w4a16", T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256,
+                                mxfp4=True, w4a16=True),
 }
 
 
