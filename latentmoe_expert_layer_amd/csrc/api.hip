@@ -397,6 +397,27 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
     m2.ldc = l;
     if ((e = lmoe::launch_grouped_mx(m2, s)) != hipSuccess) return hip_fail(e, "expert FC2 (MXFP4)");
     if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
+  } else if (w4a16 && l == lmoe::kW4MlpWidth && I == lmoe::kW4MlpWidth) {
+    // w4a16 at the 256 x 256 decode shape: FC1, SwiGLU and FC2 in one launch
+    lmoe::W4Mlp m{};
+    m.A = rows ? x : z;
+    m.lda = l;
+    m.a_rows = p->sorted_row;
+    m.a_row_div = p->k;
+    m.W1 = static_cast<const uint8_t*>(a->w1);
+    m.S1 = a->s1;
+    m.W3 = static_cast<const uint8_t*>(a->w3);
+    m.S3 = a->s3;
+    m.W2 = static_cast<const uint8_t*>(a->w2);
+    m.S2 = a->s2;
+    m.Y = Y;
+    m.ldy = l;
+    m.tiles = p->tiles_s;
+    m.ntiles = p->n_s;
+    m.max_tiles = p->max_s;
+    if ((e = lmoe::launch_w4a16_mlp(m, s, fc1_t0, fc1_t1)) != hipSuccess)
+      return hip_fail(e, "expert MLP (MXFP4 w4a16)");
+    if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
   } else if (w4a16) {
     // w4a16: bf16 activations, MXFP4 weights upcast in the weight-streaming kernel
     lmoe::GroupedW4 q1{};

@@ -125,6 +125,28 @@ struct GroupedW4 {
   int64_t max_tiles;
 };
 hipError_t launch_grouped_w4a16(const GroupedW4& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// The whole w4a16 expert MLP (FC1, SwiGLU, FC2) in one launch, for latent =
+// intermediate = 256 (kW4MlpWidth): Y [rows, 256] from A rows gathered as in
+// GroupedGemm and the three MXFP4 matrices; H stays in LDS.
+constexpr int kW4MlpWidth = 256;
+struct W4Mlp {
+  const uint16_t* A;
+  int64_t lda;
+  const int32_t* a_rows;
+  int a_row_div;
+  const uint8_t* W1;
+  const uint8_t* S1;
+  const uint8_t* W3;
+  const uint8_t* S3;
+  const uint8_t* W2;
+  const uint8_t* S2;
+  uint16_t* Y;
+  int64_t ldy;
+  const Tile* tiles;
+  const int32_t* ntiles;
+  int64_t max_tiles;
+};
+hipError_t launch_w4a16_mlp(const W4Mlp& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // ---- MXFP4 (w4a8) expert path ------------------------------------------------
 // bf16 [rows, K] -> MXFP8 e4m3 codes [rows, K] + e8m0 scales [rows, K/32].

@@ -326,6 +326,8 @@ W4A16_LAYERS = [
     ("w4_ragged", dict(T=77, d=128, l=384, E=40, k=8, S=2, I=256, Is=64, mxfp4=True, w4a16=True)),
     ("w4_small", dict(T=203, d=192, l=256, E=40, k=3, S=1, I=128, Is=64, mxfp4=True, w4a16=True)),
     ("w4_single", dict(T=1, d=128, l=128, E=16, k=4, S=0, I=128, Is=0, mxfp4=True, w4a16=True)),
+    # latent = intermediate = 256 (the one-launch expert MLP) with ragged T and experts without rows
+    ("w4_fused_ragged", dict(T=77, d=128, l=256, E=40, k=8, S=2, I=256, Is=64, mxfp4=True, w4a16=True)),
 ]
 
 
