@@ -202,85 +202,82 @@ __global__ __launch_bounds__(256) void skinny_w4a16_kernel(GroupedW4 g) {
 // one sequence and H never leaves the workgroup (TokenSpeed Day-0 post,
 // "TensorRT-LLM Stable LatentMoE": the runner's FC1 then FC2 over the routed
 // tokens).  Wave w owns H columns [64w, 64w+64) and Y columns [64w, 64w+64).
-// Its weight loads form three chunks of 8 code loads (16 B) and 8 scale words:
-//   chunks 0, 1 (FC1): slot i = subtile (i>>2) of the chunk's 32 H columns,
-//     K chunk (i>>1)&1, matrix i&1 (gate, up);
-//   chunk 2 (FC2): slot i = subtile (i>>1) of the wave's 64 Y columns, K
-//     chunk i&1;
-// two chunks are in flight at a time.  The K order within a 128-wide chunk is
-// skinny_w4a16_kernel's, so H and Y are bit-identical to that two-launch path.
+// Its weight loads form six chunks of 4 code loads (16 B) and 4 scale words,
+// two in flight (at 124 registers four workgroups fit per CU, which holds a
+// whole decode batch's tiles at once):
+//   chunks 0..3 (FC1): H columns 32*(c>>1) .. +32 of the wave, K chunk c&1;
+//     slot i = subtile i>>1, matrix i&1 (gate, up);
+//   chunks 4, 5 (FC2): K chunk c-4; slot i = Y subtile i (16 columns).
+// The K order within a 128-wide chunk is skinny_w4a16_kernel's, so H and Y
+// are bit-identical to that two-launch path.
 __global__ __launch_bounds__(256) void skinny_w4a16_mlp_kernel(W4Mlp g) {
   constexpr int L = 256, IM = 256, ZS = L + 8, HS = IM + 8;  // padded LDS rows (bf16)
-  constexpr int N1 = IM / 4 / 32, N2 = L / 4 / 64;           // FC1 chunks, FC2 chunks per wave
-  static_assert(N1 == 2 && N2 == 1, "chunk layout of the 256 x 256 shape");
+  static_assert(L == kW4MlpWidth && IM == kW4MlpWidth, "the chunk layout below is for 256 x 256");
   __shared__ bf16_t Zs[16 * ZS];
   __shared__ bf16_t Hs[16 * HS];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, gq = lane >> 4, n16 = lane & 15;
+  const int lane = threadIdx.x & 63, gq = lane >> 4, n16 = lane & 15;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, so row bases stay scalar
   if (int(blockIdx.x) >= *g.ntiles) return;
   const Tile tl = g.tiles[blockIdx.x];
   const int64_t e1 = int64_t(tl.expert) * IM, e2 = int64_t(tl.expert) * L;
-  auto load = [&](uint4 (&w)[8], uint32_t (&sc)[8], int c) __attribute__((always_inline)) {
-    const bool f1 = c < N1;
+  // code rows are K/2 = 128 bytes and scale rows K/32 = 8 bytes for both
+  // GEMMs; each load is a wave-uniform row base plus a 32-bit lane offset
+  const uint32_t coff = uint32_t(n16) * 128u + 16u * uint32_t(gq), soff = uint32_t(n16) * 8u;
+  auto load = [&](uint4 (&w)[4], uint32_t (&sc)[4], int c) __attribute__((always_inline)) {
+    const bool f1 = c < 4;
+    const int kc = f1 ? (c & 1) : (c - 4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = f1 ? (i >> 2) : (i >> 1), kc = f1 ? ((i >> 1) & 1) : (i & 1);
-      const int64_t row = f1 ? e1 + wid * (IM / 4) + 32 * c + 16 * j + n16 : e2 + wid * (L / 4) + 16 * j + n16;
-      const uint8_t* cb = f1 ? ((i & 1) ? g.W3 : g.W1) : g.W2;
-      const uint8_t* sb = f1 ? ((i & 1) ? g.S3 : g.S1) : g.S2;
-      // code rows are K/2 = 128 bytes and scale rows K/32 = 8 bytes for both GEMMs
-      w[i] = *reinterpret_cast<const uint4*>(cb + row * 128 + 64 * kc + 16 * gq);
-      sc[i] = *reinterpret_cast<const uint32_t*>(sb + row * 8 + 4 * kc);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row0 = f1 ? e1 + wid * (IM / 4) + 32 * (c >> 1) + 16 * (i >> 1) : e2 + wid * (L / 4) + 16 * i;
+      const uint8_t* cb = (f1 ? ((i & 1) ? g.W3 : g.W1) : g.W2) + row0 * 128;
+      const uint8_t* sb = (f1 ? ((i & 1) ? g.S3 : g.S1) : g.S2) + row0 * 8;
+      w[i] = *reinterpret_cast<const uint4*>(cb + (coff + 64u * uint32_t(kc)));
+      sc[i] = *reinterpret_cast<const uint32_t*>(sb + (soff + 4u * uint32_t(kc)));  // byte gq is this lane's
     }
   };
-  auto compute = [&](const uint4 (&w)[8], const uint32_t (&sc)[8], int c) __attribute__((always_inline)) {
-    if (c < N1) {
-      f32x4 ag[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, au[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // FC1: acc[2j] gate and acc[2j+1] up of H subtile j; FC2: acc[j] of Y subtile j
+  f32x4 acc[4];
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
+  for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint4 (&w)[4], const uint32_t (&sc)[4], int c) __attribute__((always_inline)) {
+    const bool f1 = c < 4;
+    const int kc = f1 ? (c & 1) : (c - 4);
+    if (!f1 && kc == 0) __syncthreads();  // every wave's H columns are in LDS
+    const bf16_t* As = f1 ? Zs : Hs;
+    const int AS = f1 ? ZS : HS;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&Zs[n16 * ZS + 128 * kc + 32 * gq + 8 * st]));
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&As[n16 * AS + 128 * kc + 32 * gq + 8 * st]));
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int i0 = j * 4 + kc * 2;
-            const uint32_t wg[4] = {w[i0].x, w[i0].y, w[i0].z, w[i0].w};
-            const uint32_t wu[4] = {w[i0 + 1].x, w[i0 + 1].y, w[i0 + 1].z, w[i0 + 1].w};
-            ag[j] = mfma_16x16x32(a, fp4x8_to_bf16(wg[st], e8m0_multiplier((sc[i0] >> (8 * gq)) & 0xffu)), ag[j]);
-            au[j] = mfma_16x16x32(a, fp4x8_to_bf16(wu[st], e8m0_multiplier((sc[i0 + 1] >> (8 * gq)) & 0xffu)), au[j]);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        acc[i] = mfma_16x16x32(a, fp4x8_to_bf16(ww[st], e8m0_multiplier((sc[i] >> (8 * gq)) & 0xffu)), acc[i]);
+      }
+    }
+    if (kc == 1) {
+      if (f1) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            Hs[(4 * gq + r) * HS + wid * (IM / 4) + 32 * (c >> 1) + 16 * j + n16] =
+                f32_to_bf16(silu_mul(acc[2 * j][r], acc[2 * j + 1][r]));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 4 * gq + r;
+            if (row < tl.nrows)
+              g.Y[(int64_t(tl.row_start) + row) * g.ldy + wid * (L / 4) + 16 * j + n16] = f32_to_bf16(acc[j][r]);
           }
-        }
+      }
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          Hs[(4 * gq + r) * HS + wid * (IM / 4) + 32 * c + 16 * j + n16] = f32_to_bf16(silu_mul(ag[j][r], au[j][r]));
-    } else {
-      __syncthreads();  // every wave's H columns are in LDS
-      f32x4 ay[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&Hs[n16 * HS + 128 * kc + 32 * gq + 8 * st]));
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i0 = j * 2 + kc;
-            const uint32_t ww[4] = {w[i0].x, w[i0].y, w[i0].z, w[i0].w};
-            ay[j] = mfma_16x16x32(a, fp4x8_to_bf16(ww[st], e8m0_multiplier((sc[i0] >> (8 * gq)) & 0xffu)), ay[j]);
-          }
-        }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 4 * gq + r;
-          if (row < tl.nrows)
-            g.Y[(int64_t(tl.row_start) + row) * g.ldy + wid * (L / 4) + 16 * j + n16] = f32_to_bf16(ay[j][r]);
-        }
+      for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  uint4 w0[8], w1[8];
-  uint32_t s0[8], s1[8];
+  uint4 w0[4], w1[4];
+  uint32_t s0[4], s1[4];
   load(w0, s0, 0);
   load(w1, s1, 1);
   // the tile's z rows (gathered) into LDS while the first two chunks load
@@ -294,7 +291,13 @@ __global__ __launch_bounds__(256) void skinny_w4a16_mlp_kernel(W4Mlp g) {
   compute(w0, s0, 0);
   load(w0, s0, 2);
   compute(w1, s1, 1);
+  load(w1, s1, 3);
   compute(w0, s0, 2);
+  load(w0, s0, 4);
+  compute(w1, s1, 3);
+  load(w1, s1, 5);
+  compute(w0, s0, 4);
+  compute(w1, s1, 5);
 }
 
 }  // namespace
