@@ -65,6 +65,10 @@ def lib():
             L.lmoe_oracle_permute.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
             L.lmoe_oracle_permute.restype = None
+            L.lmoe_oracle_router_logits.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+            L.lmoe_oracle_router_logits.restype = None
             L.lmoe_oracle_layer.argtypes = [ctypes.POINTER(_Args)]
             L.lmoe_oracle_layer.restype = ctypes.c_int
             for n in ("lmoe_oracle_e2m1_value", "lmoe_oracle_e8m0_value", "lmoe_oracle_e4m3_value"):
@@ -142,6 +146,28 @@ def route(logits, k: int):
     w = torch.empty(T, k, dtype=torch.float32)
     lib().lmoe_oracle_route(T, E, k, _ptr(logits), _ptr(ids), _ptr(w))
     return ids, w
+
+
+def router_logits(x, w_in, w_r):
+    """Router logits scored on the latent: z = bf16(x W_in^T), logits = z W_r^T
+    in fp32.  w_in None: x is z.  Returns (logits [T,E] float32, z [T,l] bf16)."""
+    x = _cpu(x, torch.bfloat16).view(torch.int16)
+    w_r = _cpu(w_r, torch.bfloat16).view(torch.int16)
+    E, l = w_r.shape
+    T = x.shape[0]
+    if w_in is not None:
+        w_in = _cpu(w_in, torch.bfloat16).view(torch.int16)
+        assert w_in.shape[0] == l
+        d = w_in.shape[1]
+        assert x.shape[1] == d
+    else:
+        d = 0
+        assert x.shape[1] == l
+    logits = torch.empty(T, E, dtype=torch.float32)
+    z = torch.empty(T, l, dtype=torch.bfloat16)
+    lib().lmoe_oracle_router_logits(T, d, l, E, _ptr(x), _ptr(w_in), _ptr(w_r), _ptr(logits),
+                                    _ptr(z.view(torch.int16)))
+    return logits, z
 
 
 def permute(ids, E: int):
@@ -230,12 +256,19 @@ def layer(inp: dict, ids, w, row_pos=None, eval_tokens=None, intermediates=False
 def run(inp: dict, eval_tokens=None, intermediates=False, act_quant=True):
     """Route (or take the given ids) and evaluate the whole layer."""
     cfg = inp["cfg"]
+    logits = None
     if cfg.rows_mode:
         ids, w = _cpu(inp["ids"], torch.int32), _cpu(inp["weights"], torch.float32)
+    elif inp.get("w_r") is not None:
+        # the router scores the latent z (logits computed, not given)
+        logits, _ = router_logits(inp["x"], inp["w_in"], inp["w_r"])
+        ids, w = route(logits, cfg.k)
     else:
         ids, w = route(inp["logits"], cfg.k)
     offsets, sorted_row, row_pos = permute(ids, cfg.E)
     out = layer(inp, ids, w, row_pos=row_pos, eval_tokens=eval_tokens,
                 intermediates=intermediates, act_quant=act_quant)
     out.update(ids=ids, w=w, offsets=offsets, sorted_row=sorted_row, row_pos=row_pos)
+    if logits is not None:
+        out["logits"] = logits
     return out

@@ -29,7 +29,8 @@
 //
 // Readings where the pages are silent (each one is listed in the design notes):
 //  * router: top-k by (logit desc, expert index asc), NaN below every number;
-//    combine weights = softmax over the k selected logits;
+//    combine weights = softmax over the k selected logits; when the logits
+//    are computed here, the gate scores the bf16 latent z in fp32;
 //  * permutation: stable counting sort of rows r = t*k + j by expert;
 //  * "SiTU" gate read as SwiGLU: silu(W1 a) * (W3 a), silu(g) = g / (1 + e^-g);
 //  * shared experts are SwiGLU FFNs on the hidden state x, added inside the
@@ -224,6 +225,35 @@ void lmoe_oracle_route(int64_t T, int32_t E, int32_t k, const float* logits, int
     for (int32_t j = 0; j < k; ++j) {
       ids[t * k + j] = order[j];
       w[t * k + j] = ex[j] / sum;
+    }
+  }
+}
+
+// ------------------------------------------------------------ router logits
+// [vLLM-K3] section 1: the latent down-projection sits in front of the
+// router, so the router scores the latent: z = bf16(x W_in^T) (the same z the
+// layer computes), then logits[t,e] = z_t . W_r[e] as one fp32 dot product in
+// ascending K order, not rounded (the router's top-k decides on these fp32
+// values).  w_in == NULL: x already holds z [T,l].  z_out (optional) receives
+// z [T,l] as bf16.
+void lmoe_oracle_router_logits(int64_t T, int32_t d, int32_t l, int32_t E, const uint16_t* x,
+                               const uint16_t* w_in, const uint16_t* w_r, float* logits, uint16_t* z_out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    std::vector<float> xv(w_in ? d : l), z(l), wrow(std::max(d, l));
+    if (w_in) {
+      bf16_row(x + t * d, xv.data(), d);
+      for (int64_t i = 0; i < l; ++i) {
+        bf16_row(w_in + i * d, wrow.data(), d);
+        z[i] = bf16_round(dot(xv.data(), wrow.data(), d));
+      }
+    } else {
+      bf16_row(x + t * l, z.data(), l);
+    }
+    if (z_out) for (int64_t i = 0; i < l; ++i) z_out[t * l + i] = to_bf16(z[i]);
+    for (int64_t e = 0; e < E; ++e) {
+      bf16_row(w_r + e * l, wrow.data(), l);
+      logits[t * E + e] = dot(z.data(), wrow.data(), l);
     }
   }
 }

@@ -213,7 +213,8 @@ def dense_reference(inp, k, act_quant=False, norm=True):
         gates[torch.arange(cfg.T), inp["ids"].view(-1).long()] = inp["weights"].view(-1).double()
     else:
         z = bf16(x @ f("w_in").T)
-        logits = inp["logits"]
+        # router gate on the latent (float64), or the given logits
+        logits = z @ f("w_r").T if "w_r" in inp else inp["logits"]
         sel = brute_topk(logits, k).long()
         wsel = torch.softmax(torch.gather(logits.double(), 1, sel), dim=1)
         gates = torch.zeros(cfg.T, cfg.E, dtype=torch.float64)
@@ -333,6 +334,71 @@ def test_mxfp4_layer_matches_dense_brute_force(act_quant):
     # a flipped bf16 rounding of an input to the MXFP8 quantiser can move one
     # element by one e4m3 step (1/8 relative), hence the looser bound here
     assert_close(out["y"], ref, max_rel=5e-2, mae=2e-3)
+
+
+# ----------------------------------------------------------- router gate
+def test_router_logits_integer_exact():
+    """Small-integer operands make every product and partial sum exact in fp32,
+    so the logits must equal integer matrix products bit for bit: a transposed
+    gate, a wrong row or a dropped term changes them."""
+    g = torch.Generator().manual_seed(5)
+    T, d, l, E = 11, 64, 96, 40
+    x = torch.randint(-2, 3, (T, d), generator=g)
+    w_in = torch.randint(-2, 3, (l, d), generator=g)
+    w_r = torch.randint(-3, 4, (E, l), generator=g)
+    zi = x.long() @ w_in.long().T                   # |z| <= 256: exact in bf16
+    logits, z = oracle.router_logits(x.to(torch.bfloat16), w_in.to(torch.bfloat16), w_r.to(torch.bfloat16))
+    assert torch.equal(z.to(torch.int64), zi)
+    assert torch.equal(logits.to(torch.int64), zi @ w_r.long().T)
+    assert torch.equal(logits, logits.round())
+    # the latent given directly (no down-projection)
+    l2, z2 = oracle.router_logits(zi.to(torch.bfloat16), None, w_r.to(torch.bfloat16))
+    assert torch.equal(l2, logits) and torch.equal(z2, z)
+
+
+def test_router_logits_score_the_rounded_latent():
+    """The gate reads z after its bf16 rounding: latents 257 and 259 (not bf16
+    values) are scored as 256 and 260 (round to nearest, ties to even)."""
+    d, l, E = 64, 64, 64
+    x = torch.zeros(2, d)
+    x[0, 0], x[0, 1] = 256.0, 1.0
+    x[1, 0], x[1, 1] = 256.0, 3.0
+    w_in = torch.zeros(l, d)
+    w_in[0, 0] = w_in[0, 1] = 1.0
+    w_in[1, 0] = 1.0
+    w_in[1, 1] = 1.0
+    eye = torch.eye(E, l)
+    logits, z = oracle.router_logits(x.to(torch.bfloat16), w_in.to(torch.bfloat16), eye.to(torch.bfloat16))
+    assert logits[0, :2].tolist() == [256.0, 256.0]
+    assert logits[1, :2].tolist() == [260.0, 260.0]
+    assert torch.equal(logits[:, 2:], torch.zeros(2, E - 2))
+
+
+def separate_latent_routing(inp, min_gap=1e-3, rounds=100):
+    """Redraw x rows until every token's float64 latent logits have their k+1
+    largest values at least min_gap apart (the fp32 rounding of the oracle then
+    cannot reorder them)."""
+    cfg = inp["cfg"]
+    for r in range(rounds):
+        z = bf16(inp["x"].double() @ inp["w_in"].double().T)
+        top = torch.topk(z @ inp["w_r"].double().T, cfg.k + 1, dim=1).values
+        bad = ((top[:, :-1] - top[:, 1:]) < min_gap).any(dim=1).nonzero().flatten()
+        if bad.numel() == 0:
+            return inp
+        inp["x"][bad] = W.normal_bf16(cfg.seed, f"x.redraw{r}", (bad.numel(), cfg.d), 1.0)
+    raise RuntimeError("could not separate the latent router logits")
+
+
+@pytest.mark.parametrize("dims", SMALL[:2])
+def test_layer_with_router_gate_matches_dense_brute_force(dims):
+    cfg = W.custom(router_gemm=True, **dims)
+    inp = separate_latent_routing(W.make_inputs(cfg))
+    out = oracle.run(inp)
+    ref = dense_reference(inp, cfg.k)
+    assert_close(out["y"], ref, max_rel=1e-2, mae=2e-4)
+    # the oracle's logits are the float64 gate products up to fp32 rounding
+    z = bf16(inp["x"].double() @ inp["w_in"].double().T)
+    assert (out["logits"].double() - z @ inp["w_r"].double().T).abs().max() < 1e-5
 
 
 def test_page_moe_shape():

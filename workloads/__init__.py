@@ -17,7 +17,7 @@ the generator: the CPU and GPU generators give different (but each
 deterministic) values; a test always hands the same tensors to both sides.
 
 Weight layout is ``[out, in]`` (reduction dim contiguous):
-  w_in [l,d]; w1, w3 [E,I,l]; w2 [E,l,I]; w_out [d,l];
+  w_in [l,d]; w1, w3 [E,I,l]; w2 [E,l,I]; w_out [d,l]; w_r [E,l] (router gate);
   ws1, ws3 [S,Is,d]; ws2 [S,d,Is]; norm_w [l].
 MXFP4 experts: codes packed two per byte (even K index in the low nibble)
   w1q, w3q [E,I,l/2] u8 with e8m0 scales s1, s3 [E,I,l/32];
@@ -48,6 +48,7 @@ class LayerConfig:
     rows_mode: bool = False   # expert-parallel share: ids + weights given, no projections
     mxfp4: bool = False       # routed expert weights in MXFP4
     w4a16: bool = False       # with mxfp4: bf16 activations (else MXFP8 activations, w4a8)
+    router_gemm: bool = False # logits computed from the latent by a gate w_r [E,l] (else given)
     norm: bool = True         # routed-latent RMSNorm with gain 1
     eps: float = 1e-6
     zipf_s: float = 0.0       # rows mode: Zipf exponent of the expert load
@@ -89,6 +90,21 @@ def normal_bf16(seed, name, shape, std, device="cpu", mean=0.0) -> torch.Tensor:
     if mean != 0.0:
         t.add_(mean)
     return t.to(BF16)
+
+
+def router_gate_std(d: int, l: int) -> float:
+    """Std of the router gate's entries that gives logits of unit variance when
+    x ~ N(0,1) and w_in ~ N(0, 0.02) (the latent then has variance d * 0.02^2)."""
+    return 1.0 / (l * d * 0.02 ** 2) ** 0.5
+
+
+def grid_bf16(seed, name, shape, levels: int, step: float, device="cpu") -> torch.Tensor:
+    """Integers drawn uniformly from [-levels, levels], times ``step`` (a power of
+    two), stored as bf16: values on a coarse grid, so that sums of their
+    products are exact in fp32 while the magnitudes stay small."""
+    g = _gen(seed, name, device)
+    t = torch.randint(-levels, levels + 1, tuple(shape), generator=g, device=device, dtype=torch.int32)
+    return (t.to(torch.float32) * step).to(BF16)
 
 
 def separated_logits(seed, name, T, E, k, device="cpu", min_gap=1e-3) -> torch.Tensor:
@@ -174,7 +190,12 @@ def make_inputs(cfg: LayerConfig, device="cpu", norm_w: Optional[str] = None) ->
         inp["weights"] = uniform_weights(s, "weights", (cfg.T, 1), device)
     else:
         inp["x"] = normal_bf16(s, "x", (cfg.T, cfg.d), 1.0, device)
-        inp["logits"] = separated_logits(s, "logits", cfg.T, cfg.E, cfg.k, device)
+        if cfg.router_gemm:
+            # gate on the latent, scaled so that the logits are about N(0,1)
+            # (z = x w_in^T has variance d * 0.02^2)
+            inp["w_r"] = normal_bf16(s, "w_r", (cfg.E, cfg.l), router_gate_std(cfg.d, cfg.l), device)
+        else:
+            inp["logits"] = separated_logits(s, "logits", cfg.T, cfg.E, cfg.k, device)
         inp["w_in"] = normal_bf16(s, "w_in", (cfg.l, cfg.d), 0.02, device)
         inp["w_out"] = normal_bf16(s, "w_out", (cfg.d, cfg.l), 0.02, device)
         if cfg.S > 0:
