@@ -7,6 +7,9 @@
  *
  *   z    = x W_in^T                              latent down-projection [T,l]
  *   ids, w = top-k of E router logits, softmax over the k                 [T,k]
+ *                                                (logits given, or computed
+ *                                                as z W_router^T: see
+ *                                                latent_moe_layer)
  *   H    = silu(z W1_e^T) * (z W3_e^T)           routed SwiGLU expert, in latent
  *   Y    = H W2_e^T                              per (token, slot) row
  *   c    = sum_j w[t,j] Y[t,j]                   weighted combine (fp32)
@@ -187,6 +190,35 @@ typedef struct {
 } lmoe_forward_args;
 
 int latent_moe_forward(const latent_moe_plan* plan, const lmoe_forward_args* args, void* hip_stream);
+
+/*
+ * The whole layer from the hidden states alone: the router's logits are
+ * computed from the latent (vLLM Kimi K3 post, section 1: the latent
+ * down-projection is inserted in front of the router), then routing and the
+ * forward run as above, in one call:
+ *   z      = x W_in^T                  (bf16, as in latent_moe_forward)
+ *   logits = z W_router^T              fp32 [T,E], one fp32 accumulation per
+ *                                      entry, not rounded
+ *   routing of `logits` as latent_moe_route in logits mode, then the rest of
+ *   latent_moe_forward on that routing.
+ * Arguments:
+ *   route     as for latent_moe_route, with logits == NULL and ids_in == NULL;
+ *             topk_ids and topk_w are required (E <= 1024)
+ *   w_router  bf16 [E,l] router gate (device)
+ *   logits    fp32 [T,E] out (device): the computed logits
+ *   fwd       as for latent_moe_forward; w_in must not be NULL (no rows mode)
+ *   plan_io   in/out.  *plan_io == NULL: a new plan is returned in it (free it
+ *             with latent_moe_free).  Otherwise it must be a plan from an
+ *             earlier latent_moe_layer call: it is refilled in place (its stage
+ *             events are kept) and no host memory is allocated.
+ * Errors as for the other calls; on LMOE_EINVAL and LMOE_EUNSUPPORTED nothing
+ * was enqueued and *plan_io is unchanged.  On LMOE_EHIP a plan allocated by
+ * this call is freed and *plan_io is set to NULL (a reused plan stays the
+ * caller's).  With stage events set, stage 2 (events[1] -> events[2]) also
+ * covers the gate GEMM, the top-k and the permutation.
+ */
+int latent_moe_layer(const lmoe_route_args* route, const void* w_router, float* logits,
+                     const lmoe_forward_args* fwd, void* hip_stream, latent_moe_plan** plan_io);
 
 /* Releases a plan (host memory only; NULL is a no-op).  Device buffers the
  * plan borrowed remain the caller's. */

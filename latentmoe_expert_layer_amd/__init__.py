@@ -3,8 +3,8 @@
 Argument marshalling only: every step of the layer runs in the library's HIP
 kernels.  torch provides device memory (outputs, workspaces) and the stream.
 The C entry points keep their names (``latent_moe_route``,
-``latent_moe_forward``, ``latent_moe_free``); ``route`` and ``forward`` are
-thin tensor-level wrappers around them.
+``latent_moe_forward``, ``latent_moe_layer``, ``latent_moe_free``); ``route``,
+``forward`` and ``layer`` are thin tensor-level wrappers around them.
 
 The library must have been built (``python -m latentmoe_expert_layer_amd.build``
 or ``__graft_entry__.build()``); importing this module fails loudly otherwise.
@@ -56,6 +56,9 @@ def _load():
     L.latent_moe_route.restype = ctypes.c_int
     L.latent_moe_forward.argtypes = [_vp, ctypes.POINTER(ForwardArgs), _vp]
     L.latent_moe_forward.restype = ctypes.c_int
+    L.latent_moe_layer.argtypes = [ctypes.POINTER(RouteArgs), _vp, _vp, ctypes.POINTER(ForwardArgs), _vp,
+                                   ctypes.POINTER(_vp)]
+    L.latent_moe_layer.restype = ctypes.c_int
     L.latent_moe_free.argtypes = [_vp]
     L.latent_moe_free.restype = None
     L.latent_moe_route_workspace_size.argtypes = [_i64, _i32, _i32]
@@ -83,6 +86,17 @@ def latent_moe_route(args: RouteArgs, stream: int = 0):
 
 def latent_moe_forward(plan: int, args: ForwardArgs, stream: int = 0):
     _check(lib.latent_moe_forward(_vp(plan), ctypes.byref(args), _vp(stream)))
+
+
+def latent_moe_layer(route_args: RouteArgs, w_router: int, logits: int, fwd_args: ForwardArgs,
+                     stream: int = 0, plan: Optional[int] = None) -> int:
+    """Calls the C entry point; returns the plan handle (``plan`` is refilled
+    in place when given)."""
+    h = _vp(plan)
+    rc = lib.latent_moe_layer(ctypes.byref(route_args), _vp(w_router), _vp(logits), ctypes.byref(fwd_args),
+                              _vp(stream), ctypes.byref(h))
+    _check(rc)
+    return h.value
 
 
 def latent_moe_free(plan: Optional[int]):
@@ -148,6 +162,7 @@ class Routing:
     workspace: torch.Tensor
     plan: Optional[int]
     keep: list = field(default_factory=list)
+    logits: Optional[torch.Tensor] = None  # computed by ``layer`` (the router gate)
 
     def free(self):
         if self.plan is not None:
@@ -224,6 +239,54 @@ def forward(routing: Routing, x: torch.Tensor, w1, w3, w2, *, w_in=None, w_out=N
     return y
 
 
+def layer(x: torch.Tensor, w_r: torch.Tensor, k: int, w1, w3, w2, *, w_in, w_out, ws1=None, ws3=None,
+          ws2=None, norm_w=None, eps: float = 1e-6, s1=None, s3=None, s2=None, mxfp4: bool = False,
+          w4a16: bool = False, y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+          route_workspace: Optional[torch.Tensor] = None, stream=None, I: Optional[int] = None,
+          routing: Optional[Routing] = None):
+    """The whole layer from x alone (``latent_moe_layer``): the router's logits
+    are z W_r^T on the latent.  Returns (Routing with .logits, y).  Passing the
+    Routing of an earlier call with the same shapes reuses its buffers and plan."""
+    T, dev = x.shape[0], x.device
+    E, l = w_r.shape
+    d = w_in.shape[1]
+    if I is None:
+        I = w1.shape[1]
+    S = 0 if ws1 is None else ws1.shape[0]
+    Is = 0 if ws1 is None else ws1.shape[1]
+    wfmt = (LMOE_WFMT_MXFP4_W4A16 if w4a16 else LMOE_WFMT_MXFP4) if mxfp4 else LMOE_WFMT_BF16
+    R = T * k
+    if routing is None:
+        rws = route_workspace_size(T, E, k)
+        if rws == 0:
+            raise LatentMoeError(LMOE_EINVAL, f"invalid route dims T={T} E={E} k={k}")
+        if route_workspace is None:
+            route_workspace = torch.empty(rws, dtype=torch.uint8, device=dev)
+        routing = Routing(T, E, k, torch.empty(T, k, dtype=torch.int32, device=dev),
+                          torch.empty(T, k, dtype=torch.float32, device=dev),
+                          torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.int32, device=dev),
+                          torch.empty(E + 1, dtype=torch.int32, device=dev), route_workspace, None,
+                          logits=torch.empty(T, E, dtype=torch.float32, device=dev))
+    elif (routing.T, routing.E, routing.k) != (T, E, k) or routing.logits is None:
+        raise ValueError("the Routing passed in is not from a layer call of this shape")
+    if workspace is None:
+        ws_bytes = forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt, False)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    ra = RouteArgs(T=T, E=E, k=k, logits=None, ids_in=None, weights_in=None, topk_ids=_p(routing.topk_ids),
+                   topk_w=_p(routing.topk_w), sorted_row=_p(routing.sorted_row), row_pos=_p(routing.row_pos),
+                   offsets=_p(routing.offsets), workspace=_p(routing.workspace),
+                   workspace_bytes=routing.workspace.numel())
+    fa = ForwardArgs(d=d, l=l, I=I, S=S, Is=Is, wfmt=wfmt, norm_eps=eps, x=_p(x), w_in=_p(w_in),
+                     w1=_p(w1), w3=_p(w3), w2=_p(w2), s1=_p(s1), s3=_p(s3), s2=_p(s2), norm_w=_p(norm_w),
+                     w_out=_p(w_out), ws1=_p(ws1), ws3=_p(ws3), ws2=_p(ws2), y=_p(y),
+                     workspace=_p(workspace), workspace_bytes=workspace.numel())
+    routing.plan = latent_moe_layer(ra, _p(w_r), _p(routing.logits), fa, _stream(stream), routing.plan)
+    routing.keep = [workspace]
+    return routing, y
+
+
 def run_layer(inp: dict, stream=None, norm=True):
     """Route + forward for a ``workloads.make_inputs`` dict whose tensors are on the GPU."""
     cfg = inp["cfg"]
@@ -234,6 +297,10 @@ def run_layer(inp: dict, stream=None, norm=True):
         r = route(ids=inp["ids"], weights=inp["weights"], E=cfg.E, k=1, stream=stream)
         y = forward(r, inp["x"], w1, w3, w2, stream=stream, **wts)
         return r, y
+    if inp.get("w_r") is not None:
+        return layer(inp["x"], inp["w_r"], cfg.k, w1, w3, w2, w_in=inp["w_in"], w_out=inp["w_out"],
+                     ws1=inp.get("ws1"), ws3=inp.get("ws3"), ws2=inp.get("ws2"),
+                     norm_w=inp.get("norm_w") if norm else None, eps=cfg.eps, stream=stream, **wts)
     r = route(inp["logits"], cfg.k, stream=stream)
     y = forward(r, inp["x"], w1, w3, w2, w_in=inp["w_in"], w_out=inp["w_out"], ws1=inp.get("ws1"),
                 ws3=inp.get("ws3"), ws2=inp.get("ws2"), norm_w=inp.get("norm_w") if norm else None,

@@ -48,6 +48,7 @@ struct latent_moe_plan {
   Tile* tiles_t;
   int32_t* n_t;
   int64_t max_t;
+  int32_t* counts;  // per-chunk expert counts of the many-workgroup permutation
   hipEvent_t events[LMOE_N_STAGE_EVENTS];
   bool timing;
 };
@@ -173,43 +174,21 @@ int check_fwd_dims(const latent_moe_plan* p, const lmoe_forward_args* a, bool ro
   return LMOE_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-const char* latent_moe_last_error(void) { return g_err.c_str(); }
-
-size_t latent_moe_route_workspace_size(int64_t T, int32_t E, int32_t k) {
-  if (T < 0 || k < 1 || E < k || E > LMOE_MAX_EXPERTS) return 0;
-  return route_layout(T, E, k).total;
-}
-
-size_t latent_moe_forward_workspace_size(int64_t T, int32_t E, int32_t k, int32_t d, int32_t l, int32_t I,
-                                         int32_t S, int32_t Is, int32_t wfmt, int32_t rows_mode) {
-  (void)E;
-  (void)d;
-  if (T < 0 || k < 1 || l <= 0 || I <= 0 || S < 0 || (S > 0 && Is <= 0)) return 0;
-  if (wfmt != LMOE_WFMT_BF16 && wfmt != LMOE_WFMT_MXFP4 && wfmt != LMOE_WFMT_MXFP4_W4A16) return 0;
-  return fwd_layout(T, k, l, I, S, rows_mode ? 0 : Is, rows_mode != 0, wfmt == LMOE_WFMT_MXFP4).total;
-}
-
-int latent_moe_route(const lmoe_route_args* a, void* hip_stream, latent_moe_plan** out_plan) {
-  if (!a || !out_plan) return fail(LMOE_EINVAL, "NULL args or out_plan");
-  *out_plan = nullptr;
-  const bool ids_mode = a->ids_in != nullptr;
+// ------------------------------------------------------------------ routing
+// Checks the routing arguments; nothing is enqueued.  gate: the logits come
+// from latent_moe_layer's router gate, so args->logits and ids_in are NULL.
+int route_check(const lmoe_route_args* a, bool gate) {
+  const bool ids_mode = !gate && a->ids_in != nullptr;
   int rc = check_route_dims(a->T, a->E, a->k, ids_mode);
   if (rc) return rc;
-  if (a->T == 0) {  // empty batch: nothing is read, written or enqueued
-    latent_moe_plan* p = new (std::nothrow) latent_moe_plan();
-    if (!p) return fail(LMOE_EINVAL, "out of host memory");
-    p->T = 0;
-    p->E = a->E;
-    p->k = a->k;
-    p->ids_mode = ids_mode;
-    *out_plan = p;
-    return LMOE_OK;
+  if (a->T == 0) return LMOE_OK;  // empty batch: no pointer is read or checked
+  if (gate) {
+    if (a->logits || a->ids_in)
+      return fail(LMOE_EINVAL, "latent_moe_layer computes the logits: route logits and ids_in must be NULL");
+  } else if ((a->logits != nullptr) == ids_mode) {
+    return fail(LMOE_EINVAL, "give exactly one of logits and ids_in");
   }
-  if ((a->logits != nullptr) == ids_mode) return fail(LMOE_EINVAL, "give exactly one of logits and ids_in");
   if (ids_mode) {
     if (!a->weights_in) return fail(LMOE_EINVAL, "ids mode needs weights_in");
     if (a->k != 1) return fail(LMOE_EINVAL, "ids mode needs k == 1 (got %d)", a->k);
@@ -221,17 +200,21 @@ int latent_moe_route(const lmoe_route_args* a, void* hip_stream, latent_moe_plan
                         a->sorted_row, a->row_pos, a->offsets, a->workspace};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(LMOE_EINVAL, "device pointer %p is not 16-byte aligned", q);
-  const RouteLayout L = route_layout(a->T, a->E, a->k);
-  if (!a->workspace || a->workspace_bytes < L.total)
-    return fail(LMOE_EINVAL, "route workspace too small: %zu < %zu", a->workspace_bytes, L.total);
+  const size_t need = route_layout(a->T, a->E, a->k).total;
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(LMOE_EINVAL, "route workspace too small: %zu < %zu", a->workspace_bytes, need);
+  return LMOE_OK;
+}
 
-  latent_moe_plan* p = new (std::nothrow) latent_moe_plan();
-  if (!p) return fail(LMOE_EINVAL, "out of host memory");
-  char* ws = static_cast<char*>(a->workspace);
+// Fills the routing part of a plan from checked arguments (host only).
+void fill_plan(latent_moe_plan* p, const lmoe_route_args* a, bool ids_mode) {
   p->T = a->T;
   p->E = a->E;
   p->k = a->k;
   p->ids_mode = ids_mode;
+  if (a->T == 0) return;
+  const RouteLayout L = route_layout(a->T, a->E, a->k);
+  char* ws = static_cast<char*>(a->workspace);
   p->ids = ids_mode ? a->ids_in : a->topk_ids;
   p->w = ids_mode ? a->weights_in : a->topk_w;
   p->sorted_row = a->sorted_row;
@@ -241,41 +224,35 @@ int latent_moe_route(const lmoe_route_args* a, void* hip_stream, latent_moe_plan
   p->n_t = reinterpret_cast<int32_t*>(ws + L.n_t);
   p->tiles_s = reinterpret_cast<Tile*>(ws + L.tiles_s);
   p->tiles_t = reinterpret_cast<Tile*>(ws + L.tiles_t);
+  p->counts = reinterpret_cast<int32_t*>(ws + L.counts);
   p->max_s = L.max_s;
   p->max_t = L.max_t;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const int64_t R = a->T * a->k;
-  if (R > 0) {
-    hipError_t e;
-    if (ids_mode) {
-      if (a->topk_ids || a->topk_w) {
-        e = lmoe::launch_copy_ids(a->ids_in, a->weights_in, R, a->topk_ids, a->topk_w, s);
-        if (e != hipSuccess) {
-          delete p;
-          return hip_fail(e, "copy_ids");
-        }
-      }
-    } else {
-      e = lmoe::launch_router(a->logits, a->T, a->E, a->k, a->topk_ids, a->topk_w, s);
-      if (e != hipSuccess) {
-        delete p;
-        return hip_fail(e, "router");
-      }
+// Router top-k/softmax over `logits` (or the id copy in ids mode), then the
+// permutation and the tile tables.
+int route_enqueue(const latent_moe_plan* p, const lmoe_route_args* a, const float* logits, hipStream_t s) {
+  const int64_t R = p->T * p->k;
+  if (R == 0) return LMOE_OK;
+  hipError_t e;
+  if (p->ids_mode) {
+    if (a->topk_ids || a->topk_w) {
+      e = lmoe::launch_copy_ids(a->ids_in, a->weights_in, R, a->topk_ids, a->topk_w, s);
+      if (e != hipSuccess) return hip_fail(e, "copy_ids");
     }
-    e = lmoe::launch_permute(p->ids, R, a->E, a->offsets, a->sorted_row, a->row_pos, p->tiles_s, p->n_s,
-                             p->tiles_t, p->n_t, reinterpret_cast<int32_t*>(ws + L.counts), s);
-    if (e != hipSuccess) {
-      delete p;
-      return hip_fail(e, "permute");
-    }
+  } else {
+    e = lmoe::launch_router(logits, p->T, p->E, p->k, a->topk_ids, a->topk_w, s);
+    if (e != hipSuccess) return hip_fail(e, "router");
   }
-  *out_plan = p;
+  e = lmoe::launch_permute(p->ids, R, p->E, a->offsets, a->sorted_row, a->row_pos, p->tiles_s, p->n_s,
+                           p->tiles_t, p->n_t, p->counts, s);
+  if (e != hipSuccess) return hip_fail(e, "permute");
   return LMOE_OK;
 }
 
-int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, void* hip_stream) {
-  if (!p || !a) return fail(LMOE_EINVAL, "NULL plan or args");
+// ------------------------------------------------------------------ forward
+// Checks the forward arguments against the plan; nothing is enqueued.
+int fwd_check(const latent_moe_plan* p, const lmoe_forward_args* a) {
   const bool rows = a->w_in == nullptr;
   if (rows && !p->ids_mode) return fail(LMOE_EINVAL, "rows mode (w_in == NULL) needs an ids-mode plan");
   int rc = check_fwd_dims(p, a, rows);
@@ -287,22 +264,49 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
                         a->w_out, a->ws1, a->ws3, a->ws2, a->y, a->workspace};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(LMOE_EINVAL, "device pointer %p is not 16-byte aligned", q);
-  const int64_t T = p->T, R = p->T * p->k;
-  const int32_t S = rows ? 0 : a->S;
-  const bool mx = a->wfmt == LMOE_WFMT_MXFP4;
-  const bool w4a16 = a->wfmt == LMOE_WFMT_MXFP4_W4A16;
-  if (w4a16 && R > int64_t(32) * p->E)
+  const int64_t R = p->T * p->k;
+  if (a->wfmt == LMOE_WFMT_MXFP4_W4A16 && R > int64_t(32) * p->E)
     return fail(LMOE_EUNSUPPORTED,
                 "MXFP4 w4a16 runs decode-shaped batches only (T*k=%lld > 32*E=%lld); use LMOE_WFMT_MXFP4 (w4a8)",
                 (long long)R, 32LL * p->E);
-  const FwdLayout L = fwd_layout(T, p->k, a->l, a->I, S, S ? a->Is : 0, rows, mx);
-  if (!a->workspace || a->workspace_bytes < L.total)
-    return fail(LMOE_EINVAL, "forward workspace too small: %zu < %zu", a->workspace_bytes, L.total);
+  const int32_t S = rows ? 0 : a->S;
+  const size_t need = fwd_layout(p->T, p->k, a->l, a->I, S, S ? a->Is : 0, rows, a->wfmt == LMOE_WFMT_MXFP4).total;
+  if (!a->workspace || a->workspace_bytes < need)
+    return fail(LMOE_EINVAL, "forward workspace too small: %zu < %zu", a->workspace_bytes, need);
+  return LMOE_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  auto mark = [&](int i) -> hipError_t {
-    return p->timing ? hipEventRecord(p->events[i], s) : hipSuccess;
-  };
+struct FwdCtx {
+  const latent_moe_plan* p;
+  const lmoe_forward_args* a;
+  hipStream_t s;
+  bool rows, mx, w4a16, small;
+  int32_t S;
+  FwdLayout L;
+};
+
+FwdCtx fwd_ctx(const latent_moe_plan* p, const lmoe_forward_args* a, hipStream_t s) {
+  FwdCtx c{};
+  c.p = p;
+  c.a = a;
+  c.s = s;
+  c.rows = a->w_in == nullptr;
+  c.mx = a->wfmt == LMOE_WFMT_MXFP4;
+  c.w4a16 = a->wfmt == LMOE_WFMT_MXFP4_W4A16;
+  c.small = p->T <= lmoe::kSmallM;
+  c.S = c.rows ? 0 : a->S;
+  c.L = fwd_layout(p->T, p->k, a->l, a->I, c.S, c.S ? a->Is : 0, c.rows, c.mx);
+  return c;
+}
+
+// Stage 1 (and 2 at large T): the latent down-projection and the shared
+// experts' gate/up on x.
+int fwd_front(const FwdCtx& c) {
+  const latent_moe_plan* p = c.p;
+  const lmoe_forward_args* a = c.a;
+  const hipStream_t s = c.s;
+  const FwdLayout& L = c.L;
+  auto mark = [&](int i) -> hipError_t { return p->timing ? hipEventRecord(p->events[i], s) : hipSuccess; };
   char* ws = static_cast<char*>(a->workspace);
   uint16_t* z = reinterpret_cast<uint16_t*>(ws + L.z);
   uint16_t* hs = reinterpret_cast<uint16_t*>(ws + L.hs);
@@ -310,12 +314,14 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   uint16_t* Y = reinterpret_cast<uint16_t*>(ws + L.Y);
   uint16_t* rhat = reinterpret_cast<uint16_t*>(ws + L.rhat);
   const uint16_t* x = static_cast<const uint16_t*>(a->x);
+  const int64_t T = p->T, R = p->T * p->k;
   const int64_t d = a->d, l = a->l, I = a->I, Is = a->Is;
+  const int32_t S = c.S;
+  const bool rows = c.rows, mx = c.mx, w4a16 = c.w4a16, small = c.small;
+  (void)R, (void)H, (void)Y, (void)rhat, (void)hs, (void)z, (void)mx, (void)w4a16;
   hipError_t e;
-
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "event");
   // 1. latent down-projection, and the shared experts' gate/up on x
-  const bool small = T <= lmoe::kSmallM;
   if (!rows) {
     lmoe::DenseGemm g[2] = {};
     g[0].M = int(T);
@@ -345,6 +351,29 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   } else if ((e = mark(1)) != hipSuccess) {
     return hip_fail(e, "event");
   }
+  return LMOE_OK;
+}
+
+// Stages 3-6: routed experts, combine (+ RMSNorm), up-projection.
+int fwd_back(const FwdCtx& c) {
+  const latent_moe_plan* p = c.p;
+  const lmoe_forward_args* a = c.a;
+  const hipStream_t s = c.s;
+  const FwdLayout& L = c.L;
+  auto mark = [&](int i) -> hipError_t { return p->timing ? hipEventRecord(p->events[i], s) : hipSuccess; };
+  char* ws = static_cast<char*>(a->workspace);
+  uint16_t* z = reinterpret_cast<uint16_t*>(ws + L.z);
+  uint16_t* hs = reinterpret_cast<uint16_t*>(ws + L.hs);
+  uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.H);
+  uint16_t* Y = reinterpret_cast<uint16_t*>(ws + L.Y);
+  uint16_t* rhat = reinterpret_cast<uint16_t*>(ws + L.rhat);
+  const uint16_t* x = static_cast<const uint16_t*>(a->x);
+  const int64_t T = p->T, R = p->T * p->k;
+  const int64_t d = a->d, l = a->l, I = a->I, Is = a->Is;
+  const int32_t S = c.S;
+  const bool rows = c.rows, mx = c.mx, w4a16 = c.w4a16, small = c.small;
+  (void)R, (void)H, (void)Y, (void)rhat, (void)hs, (void)z, (void)mx, (void)w4a16;
+  hipError_t e;
   // FC1's stage events are recorded by the launch itself, at the kernel's
   // start and end (the roofline figure of the grouped GEMM is that kernel's
   // own duration)
@@ -526,6 +555,109 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   if ((e = mark(6)) != hipSuccess) return hip_fail(e, "event");
   return LMOE_OK;
 }
+
+
+}  // namespace
+
+extern "C" {
+
+const char* latent_moe_last_error(void) { return g_err.c_str(); }
+
+size_t latent_moe_route_workspace_size(int64_t T, int32_t E, int32_t k) {
+  if (T < 0 || k < 1 || E < k || E > LMOE_MAX_EXPERTS) return 0;
+  return route_layout(T, E, k).total;
+}
+
+size_t latent_moe_forward_workspace_size(int64_t T, int32_t E, int32_t k, int32_t d, int32_t l, int32_t I,
+                                         int32_t S, int32_t Is, int32_t wfmt, int32_t rows_mode) {
+  (void)E;
+  (void)d;
+  if (T < 0 || k < 1 || l <= 0 || I <= 0 || S < 0 || (S > 0 && Is <= 0)) return 0;
+  if (wfmt != LMOE_WFMT_BF16 && wfmt != LMOE_WFMT_MXFP4 && wfmt != LMOE_WFMT_MXFP4_W4A16) return 0;
+  return fwd_layout(T, k, l, I, S, rows_mode ? 0 : Is, rows_mode != 0, wfmt == LMOE_WFMT_MXFP4).total;
+}
+
+int latent_moe_route(const lmoe_route_args* a, void* hip_stream, latent_moe_plan** out_plan) {
+  if (!a || !out_plan) return fail(LMOE_EINVAL, "NULL args or out_plan");
+  *out_plan = nullptr;
+  int rc = route_check(a, false);
+  if (rc) return rc;
+  latent_moe_plan* p = new (std::nothrow) latent_moe_plan();
+  if (!p) return fail(LMOE_EINVAL, "out of host memory");
+  const bool ids_mode = a->ids_in != nullptr;
+  fill_plan(p, a, ids_mode);
+  if ((rc = route_enqueue(p, a, a->logits, static_cast<hipStream_t>(hip_stream))) != LMOE_OK) {
+    delete p;
+    return rc;
+  }
+  *out_plan = p;
+  return LMOE_OK;
+}
+
+int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, void* hip_stream) {
+  if (!p || !a) return fail(LMOE_EINVAL, "NULL plan or args");
+  int rc = fwd_check(p, a);
+  if (rc) return rc;
+  if (p->T == 0) return LMOE_OK;
+  const FwdCtx c = fwd_ctx(p, a, static_cast<hipStream_t>(hip_stream));
+  if ((rc = fwd_front(c)) != LMOE_OK) return rc;
+  return fwd_back(c);
+}
+
+int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logits, const lmoe_forward_args* f,
+                     void* hip_stream, latent_moe_plan** plan_io) {
+  if (!r || !f || !plan_io) return fail(LMOE_EINVAL, "NULL route args, forward args or plan_io");
+  int rc = route_check(r, true);
+  if (rc) return rc;
+  if (!f->w_in) return fail(LMOE_EINVAL, "latent_moe_layer needs the projections (w_in != NULL)");
+  latent_moe_plan q{};
+  fill_plan(&q, r, false);
+  if ((rc = fwd_check(&q, f)) != LMOE_OK) return rc;
+  if (r->T > 0) {
+    if (!w_router || !logits) return fail(LMOE_EINVAL, "NULL w_router or logits");
+    if (!aligned16(w_router) || !aligned16(logits))
+      return fail(LMOE_EINVAL, "w_router and logits must be 16-byte aligned");
+  }
+  latent_moe_plan* p = *plan_io;
+  const bool fresh = p == nullptr;
+  if (fresh) {
+    p = new (std::nothrow) latent_moe_plan();
+    if (!p) return fail(LMOE_EINVAL, "out of host memory");
+  } else {
+    q.timing = p->timing;  // a reused plan keeps its stage events
+    for (int i = 0; i < LMOE_N_STAGE_EVENTS; ++i) q.events[i] = p->events[i];
+  }
+  *p = q;
+  *plan_io = p;
+  if (q.T == 0) return LMOE_OK;
+
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const FwdCtx c = fwd_ctx(p, f, s);
+  auto drop = [&](int code) {
+    if (fresh) {
+      delete p;
+      *plan_io = nullptr;
+    }
+    return code;
+  };
+  if ((rc = fwd_front(c)) != LMOE_OK) return drop(rc);
+  // the router gate on the latent z (in the forward workspace): fp32 logits
+  lmoe::DenseGemm g{};
+  g.M = int(q.T);
+  g.N = q.E;
+  g.nseg = 1;
+  g.seg[0] = lmoe::GemmSeg{reinterpret_cast<const uint16_t*>(static_cast<const char*>(f->workspace) + c.L.z), f->l,
+                           static_cast<const uint16_t*>(w_router), nullptr, f->l, f->l};
+  g.gated = false;
+  g.Cf = logits;
+  g.ldc = q.E;
+  const hipError_t e = c.small ? lmoe::launch_small_dense(&g, 1, s) : lmoe::launch_dense_gemm(g, s);
+  if (e != hipSuccess) return drop(hip_fail(e, "router gate"));
+  if ((rc = route_enqueue(p, r, logits, s)) != LMOE_OK) return drop(rc);
+  if ((rc = fwd_back(c)) != LMOE_OK) return drop(rc);
+  return LMOE_OK;
+}
+
 
 void latent_moe_free(latent_moe_plan* p) { delete p; }
 

@@ -35,6 +35,7 @@ struct TiledArgs {
   const Tile* tiles;
   const int32_t* ntiles;
   uint16_t* C;
+  float* Cf;  // F32OUT: fp32 output
   int64_t ldc;
 };
 
@@ -57,9 +58,12 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b
 //   barrier
 // so every global load has a whole stage to arrive.  The K of all segments
 // is one sequence of stages; rows of a partial tile and B rows past N are
-// clamped (loaded but never stored).
-template <int NW, int WAVES_M, bool GATED, bool GROUPED, bool SWZ>
+// clamped (loaded but never stored).  F32OUT (plain GEMMs): fp32 results are
+// stored straight from the accumulators (32 consecutive columns per half-wave
+// and row), any N.
+template <int NW, int WAVES_M, bool GATED, bool GROUPED, bool SWZ, bool F32OUT = false>
 __global__ __launch_bounds__(NW * 64, 1) void tiled_gemm_kernel(TiledArgs g) {
+  static_assert(!F32OUT || (!GATED && !GROUPED), "fp32 output is for plain dense GEMMs");
   constexpr int NTH = NW * 64;
   constexpr int BM = 256, BR = 256;                 // A rows, B rows per tile
   constexpr int NOUT = GATED ? 128 : 256;           // output columns per tile
@@ -243,6 +247,22 @@ __global__ __launch_bounds__(NW * 64, 1) void tiled_gemm_kernel(TiledArgs g) {
     default: mainloop(std::integral_constant<int, FM>{}); break;
   }
 
+  if constexpr (F32OUT) {
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        if (i < fa)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+              const int col = n0 + wn * WN + j * 32 + (lane & 31);
+              if (row < nrows && col < g.N) g.Cf[(int64_t(row0) + row) * g.ldc + col] = acc[i][j][v];
+            }
+    }
+    return;
+  }
   // Epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores.
   constexpr int CLD = NOUT + 8;
   static_assert(BM * CLD <= 2 * (BM + BR) * kLdsK, "epilogue staging fits in the LDS buffers");
@@ -275,12 +295,12 @@ __global__ __launch_bounds__(NW * 64, 1) void tiled_gemm_kernel(TiledArgs g) {
   }
 }
 
-template <int NW, int WAVES_M, bool GATED, bool GROUPED, bool SWZ>
+template <int NW, int WAVES_M, bool GATED, bool GROUPED, bool SWZ, bool F32OUT = false>
 hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s, hipEvent_t t0 = nullptr,
                      hipEvent_t t1 = nullptr) {
   constexpr int NOUT = GATED ? 128 : 256;
   const size_t lds = size_t(2) * (256 + 256) * kLdsK * sizeof(bf16_t);
-  auto kern = tiled_gemm_kernel<NW, WAVES_M, GATED, GROUPED, SWZ>;
+  auto kern = tiled_gemm_kernel<NW, WAVES_M, GATED, GROUPED, SWZ, F32OUT>;
   if (hipError_t e = allow_dynamic_lds((const void*)kern, int(lds)); e != hipSuccess) return e;
   const int64_t nblk = mtiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
@@ -294,13 +314,15 @@ hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s, hipEvent
 // flight, and the partial sums are added in LDS in wave order
 // (deterministic).  Up to two independent sub-GEMMs (e.g. the latent
 // down-projection and the shared experts' gated gate/up projection, which
-// read the same x) share one launch.
+// read the same x) share one launch.  With an fp32 output (Cf), N may be
+// ragged: B rows past N are clamped (loaded, never stored).
 struct SplitKPart {
   int N;
   int nseg;
   GemmSeg seg[5];
   int gated;
   uint16_t* C;
+  float* Cf;
   int64_t ldc;
 };
 struct SplitKArgs {
@@ -320,14 +342,17 @@ constexpr int kSkBatch = 4;  // 32-wide K steps whose loads are issued together
 template <bool GATED>
 __device__ __forceinline__ void splitk_accumulate(const SplitKPart& P, int64_t arow, int ncol, int kof, int st0,
                                                   int st1, f32x4 (&acc)[kSkNS], f32x4 (&acc3)[kSkNS]) {
+  int brow[kSkNS];
+#pragma unroll
+  for (int j = 0; j < kSkNS; ++j) brow[j] = min(ncol + 16 * j, P.N - 1);
   int base = 0;
   for (int s = 0; s < P.nseg; ++s) {
     const GemmSeg sg = P.seg[s];
     const int ns = sg.K / 32;
     const int lo = max(st0, base), hi = min(st1, base + ns);
     const bf16_t* ap = sg.A + arow * sg.lda + kof;
-    const bf16_t* bp = sg.B + int64_t(ncol) * sg.ldb + kof;
-    const bf16_t* b3p = GATED ? sg.B3 + int64_t(ncol) * sg.ldb + kof : nullptr;
+    const bf16_t* bp = sg.B + kof;
+    const bf16_t* b3p = GATED ? sg.B3 + kof : nullptr;
     for (int c0 = lo; c0 < hi; c0 += kSkBatch) {
       const int cnt = min(kSkBatch, hi - c0);
       uint4 a[kSkBatch], b[kSkNS][kSkBatch], b3[kSkNS][GATED ? kSkBatch : 1];
@@ -337,8 +362,8 @@ __device__ __forceinline__ void splitk_accumulate(const SplitKPart& P, int64_t a
         a[u] = ldg16(ap + k);
 #pragma unroll
         for (int j = 0; j < kSkNS; ++j) {
-          b[j][u] = ldg16(bp + int64_t(16 * j) * sg.ldb + k);
-          if constexpr (GATED) b3[j][u] = ldg16(b3p + int64_t(16 * j) * sg.ldb + k);
+          b[j][u] = ldg16(bp + int64_t(brow[j]) * sg.ldb + k);
+          if constexpr (GATED) b3[j][u] = ldg16(b3p + int64_t(brow[j]) * sg.ldb + k);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -363,7 +388,7 @@ __global__ __launch_bounds__(256) void splitk_dense_kernel(SplitKArgs g) {
   const int pi = (g.nparts > 1 && int(blockIdx.x) >= g.nblk0) ? 1 : 0;
   const int bb = int(blockIdx.x) - (pi ? g.nblk0 : 0);
   const SplitKPart& P = g.part[pi];
-  const int tiles_n = P.N / (16 * kSkNS);
+  const int tiles_n = (P.N + 16 * kSkNS - 1) / (16 * kSkNS);
   const int tm = bb / tiles_n, tn = bb % tiles_n;
   const int row0 = tm * 16, nrows = min(16, g.M - row0);
   const int64_t arow = row0 + min(lane & 15, nrows - 1);
@@ -406,7 +431,9 @@ __global__ __launch_bounds__(256) void splitk_dense_kernel(SplitKArgs g) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = (lane >> 4) * 4 + r;
-        if (row < nrows) {
+        if (P.Cf) {
+          if (row < nrows && ncol + 16 * j < P.N) P.Cf[(int64_t(row0) + row) * P.ldc + ncol + 16 * j] = acc[j][r];
+        } else if (row < nrows) {
           float v = acc[j][r];
           if (gated) v = silu_mul(v, acc3[j][r]);
           P.C[(int64_t(row0) + row) * P.ldc + ncol + 16 * j] = f32_to_bf16(v);
@@ -427,8 +454,13 @@ hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
   a.a_row_div = 1;
   a.b_estride = 0;
   a.C = d.C;
+  a.Cf = d.Cf;
   a.ldc = d.ldc;
   const int64_t mt = (d.M + 255) / 256;
+  if (d.Cf) {
+    if (d.gated) return hipErrorInvalidValue;
+    return run_tiled<8, 2, false, false, false, true>(a, mt, s);
+  }
   if (d.gated) return run_tiled<8, 2, true, false, false>(a, mt, s);
   return run_tiled<8, 2, false, false, false>(a, mt, s);
 }
@@ -464,8 +496,10 @@ hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s)
     for (int j = 0; j < d.nseg; ++j) P.seg[j] = d.seg[j];
     P.gated = d.gated ? 1 : 0;
     P.C = d.C;
+    P.Cf = d.Cf;
     P.ldc = d.ldc;
-    const int64_t nb = int64_t((d.M + 15) / 16) * (d.N / (16 * kSkNS));
+    if (d.Cf && d.gated) return hipErrorInvalidValue;
+    const int64_t nb = int64_t((d.M + 15) / 16) * ((d.N + 16 * kSkNS - 1) / (16 * kSkNS));
     if (i == 0) a.nblk0 = int(nb);
     nblk += nb;
   }

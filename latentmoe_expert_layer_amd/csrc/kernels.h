@@ -65,18 +65,21 @@ struct GemmSeg {
   int K;
 };
 
+// Cf != NULL (plain GEMMs only): C is written as fp32 to Cf (C is ignored), and
+// N may be any positive number; otherwise N is a multiple of 8 (tiled) or 32
+// (few-row).
 struct DenseGemm {
   int M, N;
   int nseg;
   GemmSeg seg[1 + 4];
   bool gated;
   uint16_t* C;
+  float* Cf;
   int64_t ldc;
 };
 hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
 // Few-row variant (M <= kSmallM): 16-row tiles, K split across the 4 waves of
-// a workgroup; up to two sub-GEMMs with the same M in one launch.  Every N is
-// a multiple of 32.
+// a workgroup; up to two sub-GEMMs with the same M in one launch.
 constexpr int kSmallM = 512;
 hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s);
 

@@ -119,3 +119,41 @@ def test_forward_rejects_bad_pointers():
     # pointer checks' inputs on an ids-mode plan whose route call fails first
     with pytest.raises(lm.LatentMoeError):
         lm.latent_moe_route(_route_args(lm, T=4, logits=None, ids_in=128, weights_in=144, k=2))
+
+
+def _layer_fwd(lm, **kw):
+    base = dict(d=512, l=256, I=128, S=1, Is=128, wfmt=0, norm_eps=1e-6, x=16, w_in=32, w1=48, w3=64, w2=80,
+                w_out=96, ws1=112, ws3=128, ws2=144, y=160, workspace=176, workspace_bytes=1 << 24)
+    base.update(kw)
+    return lm.ForwardArgs(**base)
+
+
+@pytest.mark.parametrize("rkw,fkw,gate,logits,code", [
+    (dict(), dict(), 192, 208, 1),                              # route logits given: the layer computes them
+    (dict(logits=None, ids_in=128, weights_in=144, k=1), dict(), 192, 208, 1),
+    (dict(logits=None, topk_ids=None), dict(), 192, 208, 1),
+    (dict(logits=None), dict(w_in=None, w_out=None), 192, 208, 1),   # no rows mode
+    (dict(logits=None), dict(), None, 208, 1),                  # no gate
+    (dict(logits=None), dict(), 192, None, 1),                  # no logits buffer
+    (dict(logits=None), dict(), 200, 208, 1),                   # misaligned gate
+    (dict(logits=None), dict(l=100), 192, 208, 1),
+    (dict(logits=None), dict(workspace_bytes=64), 192, 208, 1),
+    (dict(logits=None, workspace_bytes=16), dict(), 192, 208, 1),
+    (dict(logits=None, E=2000), dict(), 192, 208, 2),           # the router's E limit
+])
+def test_layer_rejects_invalid_arguments(rkw, fkw, gate, logits, code):
+    import latentmoe_expert_layer_amd as lm
+    with pytest.raises(lm.LatentMoeError) as ei:
+        lm.latent_moe_layer(_route_args(lm, **rkw), gate, logits, _layer_fwd(lm, **fkw))
+    assert ei.value.code == code, lm.latent_moe_last_error()
+
+
+def test_layer_with_empty_batch_returns_and_reuses_a_plan():
+    import latentmoe_expert_layer_amd as lm
+    ra = _route_args(lm, T=0, logits=None)
+    plan = lm.latent_moe_layer(ra, None, None, _layer_fwd(lm))
+    assert plan
+    assert lm.latent_moe_layer(ra, None, None, _layer_fwd(lm), plan=plan) == plan
+    with pytest.raises(lm.LatentMoeError):                      # dims are checked even when empty
+        lm.latent_moe_layer(ra, None, None, _layer_fwd(lm, l=100), plan=plan)
+    lm.latent_moe_free(plan)

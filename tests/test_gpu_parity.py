@@ -388,3 +388,187 @@ def test_mxfp4_full_size_sampled():
                   | set(range(101, cfg.T, 1999)))
     ref = oracle.layer(inp, ids_ref, w_ref, eval_tokens=pick, act_quant=True)["y"]
     assert_rowwise(y.cpu()[pick], ref)
+
+
+# ------------------------------------------- the whole layer with the router gate
+def gate_routing(cfg):
+    """Poisoned output buffers of latent_moe_layer for ``cfg``."""
+    T, E, k = cfg.T, cfg.E, cfg.k
+    dev = "cuda"
+    return lm.Routing(T, E, k, poison_(torch.empty(T, k, dtype=torch.int32, device=dev)),
+                      poison_(torch.empty(T, k, dtype=torch.float32, device=dev)),
+                      poison_(torch.empty(T * k, dtype=torch.int32, device=dev)),
+                      poison_(torch.empty(T * k, dtype=torch.int32, device=dev)),
+                      poison_(torch.empty(E + 1, dtype=torch.int32, device=dev)),
+                      poison_(torch.empty(lm.route_workspace_size(T, E, k), dtype=torch.uint8, device=dev)),
+                      None, logits=poison_(torch.empty(T, E, dtype=torch.float32, device=dev)))
+
+
+def run_gpu_gate_layer(inp_dev, routing=None):
+    cfg = inp_dev["cfg"]
+    mx = cfg.mxfp4
+    wfmt = (lm.LMOE_WFMT_MXFP4_W4A16 if cfg.w4a16 else lm.LMOE_WFMT_MXFP4) if mx else lm.LMOE_WFMT_BF16
+    w1, w3, w2 = (inp_dev[n + ("q" if mx else "")] for n in ("w1", "w3", "w2"))
+    nbytes = lm.forward_workspace_size(cfg.T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is, wfmt, False)
+    ws = poison_(torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
+    y = poison_(torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device="cuda"))
+    r, y = lm.layer(inp_dev["x"], inp_dev["w_r"], cfg.k, w1, w3, w2, w_in=inp_dev["w_in"], w_out=inp_dev["w_out"],
+                    ws1=inp_dev.get("ws1"), ws3=inp_dev.get("ws3"), ws2=inp_dev.get("ws2"),
+                    norm_w=inp_dev.get("norm_w"), eps=cfg.eps, s1=inp_dev.get("s1"), s3=inp_dev.get("s3"),
+                    s2=inp_dev.get("s2"), mxfp4=mx, w4a16=cfg.w4a16, I=cfg.I, y=y, workspace=ws,
+                    routing=routing if routing is not None else gate_routing(cfg))
+    torch.cuda.synchronize()
+    return r, y
+
+
+def grid_gate_inputs(cfg, step_r):
+    """make_inputs with x, W_in and the gate on coarse grids (integers in [-4,4]
+    times 1/4, 1/64 and step_r): the down-projection's products are multiples
+    of 2^-8 and the gate's of 2^-8 * step_r, and every partial sum, in any
+    order, stays below 2^24 such units, so z, the logits and hence the routing
+    (ties included) are exact on both sides."""
+    inp = W.make_inputs(cfg, device="cuda")
+    inp["x"] = W.grid_bf16(cfg.seed, "x.grid", (cfg.T, cfg.d), 4, 0.25, "cuda")
+    inp["w_in"] = W.grid_bf16(cfg.seed, "w_in.grid", (cfg.l, cfg.d), 4, 1 / 64, "cuda")
+    inp["w_r"] = W.grid_bf16(cfg.seed, "w_r.grid", (cfg.E, cfg.l), 4, step_r, "cuda")
+    x, wi, wr = (inp[n].double() for n in ("x", "w_in", "w_r"))
+    wiT, wrT = wi.T.contiguous(), wr.T.contiguous()
+    assert (x.abs() @ wiT.abs()).max().item() < 2 ** 16
+    z = (x @ wiT).float().to(torch.bfloat16).double()
+    assert (z.abs() @ wrT.abs()).max().item() < 2 ** 16 * step_r
+    return inp
+
+
+GATE_LAYERS = [
+    ("gate_tiny", dict(T=64, d=512, l=256, E=16, k=4, S=1, I=128, Is=128)),
+    ("gate_decode", dict(T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256)),
+    # E not a multiple of the 32-column gate tile, experts without rows
+    ("gate_ragged", dict(T=77, d=192, l=128, E=200, k=8, S=1, I=64, Is=64)),
+    ("gate_single", dict(T=1, d=128, l=64, E=33, k=5, S=0, I=64, Is=0)),
+    # more than 512 tokens: the LDS-tiled gate GEMM, ragged row and column tiles
+    ("gate_tiled", dict(T=1000, d=256, l=192, E=300, k=6, S=1, I=128, Is=64)),
+    ("gate_w4a16", dict(T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256, mxfp4=True, w4a16=True)),
+]
+
+
+@pytest.mark.parametrize("name,dims", GATE_LAYERS, ids=[n for n, _ in GATE_LAYERS])
+def test_gate_layer_exact_grid(name, dims):
+    """latent_moe_layer on exact-sum inputs: logits, ids (ties included),
+    weights and the permutation as for the given-logits path, y at the bf16 bar."""
+    cfg = W.custom(name, router_gemm=True, **dims)
+    log(f"gate layer {name}: {cfg}")
+    inp_dev = grid_gate_inputs(cfg, 1 / 16)
+    r, y = run_gpu_gate_layer(inp_dev)
+    inp = to_host(inp_dev)
+    ref = oracle.run(inp, act_quant=False)
+    assert torch.equal(r.logits.cpu(), ref["logits"]), "gate logits differ"
+    check_routing(r, ref["logits"], cfg.k, cfg.E)
+    assert_parity(y.cpu(), ref["y"])
+
+
+def test_gate_layer_continuous_inputs():
+    """The bench's input distribution (x ~ N(0,1), W_in ~ N(0,0.02), gate scaled
+    for unit-variance logits), where sums are not exact: fp32 summation order
+    and one-ulp bf16 flips of z elements move logits by a few 1e-3, so the
+    logits are compared within 1e-2; tokens whose oracle logits have their k-th
+    and (k+1)-th largest values more than 2e-2 apart select the same experts;
+    every token's GPU ids are the top-k (value desc, index asc) of the GPU's
+    own logits; outputs of identically routed tokens meet the bf16 bar."""
+    cfg = W.custom("gate_cont", router_gemm=True, T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256)
+    log(f"gate layer continuous: {cfg}")
+    inp_dev = W.make_inputs(cfg, device="cuda")
+    r, y = run_gpu_gate_layer(inp_dev)
+    inp = to_host(inp_dev)
+    ref = oracle.run(inp)
+    g, o = r.logits.cpu().double(), ref["logits"].double()
+    tol = 1e-2
+    err = (g - o).abs().max().item()
+    log(f"  logits: max |gpu - oracle| = {err:.3e}")
+    assert err <= tol
+    top = torch.topk(o, cfg.k + 1, dim=1).values
+    sep = (top[:, cfg.k - 1] - top[:, cfg.k]) > 2 * tol
+    gi, oi = r.topk_ids.cpu(), ref["ids"]
+    same = (gi == oi).all(dim=1)
+    same_set = (gi.sort(dim=1).values == oi.sort(dim=1).values).all(dim=1)
+    assert bool(same_set[sep].all()), "well-separated tokens select different experts"
+    order = torch.sort(g, dim=1, descending=True, stable=True).indices[:, :cfg.k]
+    assert torch.equal(gi.long(), order), "GPU ids are not the top-k of the GPU logits"
+    pick = same.nonzero().flatten()
+    log(f"  {int(sep.sum())} tokens separated at the k-th boundary, {pick.numel()} of {cfg.T} routed identically")
+    assert pick.numel() >= 0.9 * cfg.T
+    assert_parity(y.cpu()[pick], ref["y"][pick])
+
+
+def test_gate_layer_prefill_sampled():
+    """Prefill shape (8192 tokens, d=7168, latent 2048): the LDS-tiled gate at
+    full size; logits, ids and outputs on sampled tokens, the permutation by
+    the properties of a stable counting sort of the GPU's ids."""
+    cfg = W.custom("gate_prefill", router_gemm=True, T=8192, d=7168, l=2048, E=896, k=16, S=2, I=512, Is=512)
+    log(f"gate layer prefill: {cfg}")
+    inp_dev = grid_gate_inputs(cfg, 1 / 64)
+    r, y = run_gpu_gate_layer(inp_dev)
+    inp = to_host(inp_dev)
+    del inp_dev
+    T, E, k = cfg.T, cfg.E, cfg.k
+    pick = sorted({0, T - 1} | set(range(0, T, 512)) | set(range(255, T, 512)) | set(range(37, T, 997)))
+    lg, _ = oracle.router_logits(inp["x"][pick], inp["w_in"], inp["w_r"])
+    assert torch.equal(r.logits.cpu()[pick], lg), "gate logits differ"
+    ids_p, w_p = oracle.route(lg, k)
+    assert torch.equal(r.topk_ids.cpu()[pick], ids_p), "router ids differ"
+    assert (r.topk_w.cpu()[pick].double() - w_p.double()).abs().max().item() <= 2e-6
+    gi = r.topk_ids.cpu().view(-1).long()
+    assert bool(((gi >= 0) & (gi < E)).all())
+    off = torch.zeros(E + 1, dtype=torch.int64)
+    off[1:] = torch.bincount(gi, minlength=E).cumsum(0)
+    assert torch.equal(r.offsets.cpu().long(), off)
+    srt = torch.sort(gi, stable=True).indices
+    assert torch.equal(r.sorted_row.cpu().long(), srt)
+    rp = torch.empty_like(srt)
+    rp[srt] = torch.arange(srt.numel())
+    assert torch.equal(r.row_pos.cpu().long(), rp)
+    ids_full = torch.zeros(T, k, dtype=torch.int32)
+    w_full = torch.zeros(T, k, dtype=torch.float32)
+    ids_full[pick], w_full[pick] = ids_p, w_p          # the oracle reads only the evaluated tokens' rows
+    ref = oracle.layer(inp, ids_full, w_full, eval_tokens=pick)["y"]
+    assert_parity(y.cpu()[pick], ref)
+
+
+def test_gate_layer_plan_reuse_and_graph_replay():
+    """A Routing (plan + buffers) reused by a second call gives that call's
+    result; latent_moe_layer captured in a HIP graph equals the eager result on
+    every replay."""
+    cfg = W.custom("gate_reuse", router_gemm=True, T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256)
+    log(f"gate layer reuse/graph: {cfg}")
+    inp = grid_gate_inputs(cfg, 1 / 16)
+    other = dict(inp)
+    other["x"] = W.grid_bf16(cfg.seed + 1, "x.grid", (cfg.T, cfg.d), 4, 0.25, "cuda")
+    r0, y0 = run_gpu_gate_layer(other)
+    r1, y1 = run_gpu_gate_layer(inp)
+    logits1 = r1.logits.clone()
+    plan = r1.plan
+    r1b, y1b = run_gpu_gate_layer(other, routing=r1)       # same buffers and plan, other input
+    assert r1b.plan == plan
+    assert torch.equal(y1b.view(torch.int16), y0.view(torch.int16))
+    assert torch.equal(r1b.topk_ids, r0.topk_ids) and torch.equal(r1b.logits, r0.logits)
+
+    ws = torch.empty(lm.forward_workspace_size(cfg.T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device="cuda")
+    rg = gate_routing(cfg)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    args = dict(w_in=inp["w_in"], w_out=inp["w_out"], ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"],
+                norm_w=inp["norm_w"], eps=cfg.eps, y=y, workspace=ws, routing=rg)
+    with torch.cuda.graph(g, stream=cap):
+        lm.layer(inp["x"], inp["w_r"], cfg.k, inp["w1"], inp["w3"], inp["w2"], **args)
+    for rep in range(3):
+        poison_(ws)
+        poison_(y)
+        poison_(rg.logits)
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), f"replay {rep} differs"
+        assert torch.equal(rg.logits, logits1), f"replay {rep}: logits differ"
+        del junk
