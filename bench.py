@@ -106,6 +106,9 @@ def cpu_baseline(cfg, inp_host, budget_s):
     t0 = time.perf_counter()
     if cfg.rows_mode:
         ids, w = inp_host["ids"], inp_host["weights"]
+    elif cfg.router_gemm:
+        logits, _ = oracle.router_logits(inp_host["x"], inp_host["w_in"], inp_host["w_r"])
+        ids, w = oracle.route(logits, cfg.k)
     else:
         ids, w = oracle.route(inp_host["logits"], cfg.k)
     oracle.permute(ids, cfg.E)
@@ -119,7 +122,8 @@ def cpu_baseline(cfg, inp_host, budget_s):
         if el >= budget_s or done >= 10000 * cfg.T:
             break
     return {"value": done / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"route + permute of the whole {cfg.name} batch ({cfg.T} tokens), then the layer on "
+            "sample": f"{'router gate + ' if cfg.router_gemm else ''}route + permute of the whole {cfg.name} "
+                      f"batch ({cfg.T} tokens), then the layer on "
                       f"{done} tokens in chunks of {chunk}, {el:.1f} s in total"}
 
 
@@ -169,7 +173,13 @@ def main():
                    row_pos=torch.empty(R, dtype=torch.int32, device="cuda"),
                    offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
                    y=torch.empty(T, cfg.l if cfg.rows_mode else cfg.d, dtype=torch.bfloat16, device="cuda"))
-        if cfg.rows_mode:
+        logits = None
+        if cfg.router_gemm:   # latent_moe_layer: the logits are computed from the latent
+            logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+            ra = lm.RouteArgs(T=T, E=E, k=k, topk_ids=P(out["topk_ids"]), topk_w=P(out["topk_w"]),
+                              sorted_row=P(out["sorted_row"]), row_pos=P(out["row_pos"]),
+                              offsets=P(out["offsets"]), workspace=P(rws), workspace_bytes=rws.numel())
+        elif cfg.rows_mode:
             ra = lm.RouteArgs(T=T, E=E, k=k, ids_in=P(inp["ids"]), weights_in=P(inp["weights"]),
                               sorted_row=P(out["sorted_row"]), row_pos=P(out["row_pos"]),
                               offsets=P(out["offsets"]), workspace=P(rws), workspace_bytes=rws.numel())
@@ -186,14 +196,31 @@ def main():
                             norm_w=P(inp.get("norm_w")), w_out=P(inp.get("w_out")),
                             ws1=P(inp.get("ws1")), ws3=P(inp.get("ws3")), ws2=P(inp.get("ws2")),
                             y=P(out["y"]), workspace=P(fws), workspace_bytes=fws.numel())
-        sets.append(dict(inp=inp, rws=rws, fws=fws, out=out, ra=ra, fa=fa))
+        sets.append(dict(inp=inp, rws=rws, fws=fws, out=out, ra=ra, fa=fa, logits=logits, plan=None))
     torch.cuda.synchronize()
 
     n_ev = lm.N_STAGE_EVENTS
     use_events = not args.no_stage_events
 
+    def run_call(s, strm, events=None):
+        """One layer call on copy s: latent_moe_layer (its plan reused across
+        calls) or latent_moe_route + latent_moe_forward."""
+        if cfg.router_gemm:
+            if s["plan"] is not None:
+                lm.latent_moe_plan_set_stage_events(s["plan"], events)
+            s["plan"] = lm.latent_moe_layer(s["ra"], P(s["inp"]["w_r"]), P(s["logits"]), s["fa"], strm, s["plan"])
+            return
+        plan = lm.latent_moe_route(s["ra"], strm)
+        if events is not None:
+            lm.latent_moe_plan_set_stage_events(plan, events)
+        lm.latent_moe_forward(plan, s["fa"], strm)
+        lm.latent_moe_free(plan)
+
     def step(i, events=None):
         s = sets[i % copies]
+        if cfg.router_gemm:
+            run_call(s, stream, events)
+            return
         plan = lm.latent_moe_route(s["ra"], stream)
         if events is not None:
             lm.latent_moe_plan_set_stage_events(plan, events)
@@ -217,10 +244,7 @@ def main():
             for c in range(copies):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
-                    cs = torch.cuda.current_stream().cuda_stream
-                    plan = lm.latent_moe_route(sets[c]["ra"], cs)
-                    lm.latent_moe_forward(plan, sets[c]["fa"], cs)
-                    lm.latent_moe_free(plan)
+                    run_call(sets[c], torch.cuda.current_stream().cuda_stream)
                 graphs.append(g)
             for i in range(args.warmup):
                 graphs[i % copies].replay()
@@ -284,6 +308,9 @@ def main():
     layer_flop = fc1_flop + fc2_flop + dense_flop
     dense_bytes = 0 if cfg.rows_mode else 2 * (T * d + (l + 2 * S * Is) * d + T * l + T * S * Is + d * (l + S * Is) + T * d)
     route_bytes = T * E * 4 + R * (4 + 4 + 4 + 4 + 4)
+    if cfg.router_gemm:   # the gate GEMM: z and the gate in, fp32 logits out
+        layer_flop += 2.0 * T * l * E
+        route_bytes += T * l * 2 + E * l * 2 + T * E * 4
     combine_bytes = R * l * 2 + T * l * 2 + R * 8
     layer_bytes = fc1_bytes + fc2_bytes + dense_bytes + route_bytes + combine_bytes
 
@@ -313,8 +340,9 @@ def main():
             kern, src = "skinny_w4a16_kernel", "skinny.hip"
         elif cfg.mxfp4:
             kern, src = "mx_grouped_kernel", "mx.hip"
-        elif R <= 32 * E:
-            kern, src = "skinny_grouped_kernel", "skinny.hip"
+        elif R <= 32 * E:   # LDS-staged weight loads when the GEMM's K is a multiple of 128
+            kern = "skinny_lds_kernel" if (l if dom == "fc1" else I) % 128 == 0 else "skinny_grouped_kernel"
+            src = "skinny.hip"
         else:
             kern, src = "tiled_gemm_kernel", "gemm.hip"
         traffic = measured_traffic(f"{dom}", cfg.name, source_hash(src))
@@ -344,6 +372,9 @@ def main():
         "layer_algorithmic_bytes": int(layer_bytes),
         "touched_experts": touched,
     }
+    if cfg.router_gemm:
+        extra["stage_note"] = ("shared_gate_up also covers the router gate GEMM, the top-k and the permutation "
+                               "(latent_moe_layer runs them between the down-projection and FC1)")
     if use_events:
         for n, fl, by in (("fc1", fc1_flop, fc1_bytes), ("fc2", fc2_flop, fc2_bytes)):
             us = stages[n]
@@ -367,11 +398,15 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": ("bf16 (experts: MXFP4 weights upcast to bf16, bf16 activations)" if cfg.w4a16 else
                   "bf16 (experts: MXFP4 weights x MXFP8 activations)") if cfg.mxfp4 else "bf16",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights, gap-separated N(0,1) logits)",
+        "data": ("synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights, router gate "
+                 "N(0, 1/sqrt(latent*d*0.02^2)) on the latent)" if cfg.router_gemm else
+                 "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights, gap-separated N(0,1) logits)"),
         "config": {"workload": (f"{cfg.name}: {T} received rows, {E} local experts, latent {l}, SwiGLU I={I}, "
                                 f"Zipf({cfg.zipf_s}) expert load, combine weights given") if cfg.rows_mode else
                                (f"{cfg.name}: T={T} tokens, d={d} -> latent {l}, E={E} top-{k} + {S} shared, "
                                 f"SwiGLU I={I}, shared I={Is}, RMSNorm on"
+                                + (", logits computed by the router gate on the latent (latent_moe_layer)"
+                                   if cfg.router_gemm else "")
                                 + ((", MXFP4 experts (w4a16)" if cfg.w4a16 else ", MXFP4 experts (w4a8)")
                                    if cfg.mxfp4 else "")),
                    "T": T, "d": d, "latent": l, "E": E, "k": k, "shared": S, "I": I, "Is": Is},

@@ -71,6 +71,9 @@ CONFIGS = {
     # the decode batch with MXFP4 routed experts and bf16 activations (w4a16)
     "decode_w4a16": LayerConfig("decode_w4a16", T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256,
                                 mxfp4=True, w4a16=True),
+    # the decode shape with the router's logits computed from the latent (gate [E,l])
+    "decode_gate": LayerConfig("decode_gate", T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256,
+                               router_gemm=True),
 }
 
 
