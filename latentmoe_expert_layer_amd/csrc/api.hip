@@ -642,12 +642,13 @@ int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logi
   };
   if ((rc = fwd_front(c)) != LMOE_OK) return drop(rc);
   // the router gate on the latent z (in the forward workspace): fp32 logits
+  const uint16_t* z = reinterpret_cast<const uint16_t*>(static_cast<const char*>(f->workspace) + c.L.z);
+  const uint16_t* wr = static_cast<const uint16_t*>(w_router);
   lmoe::DenseGemm g{};
   g.M = int(q.T);
   g.N = q.E;
   g.nseg = 1;
-  g.seg[0] = lmoe::GemmSeg{reinterpret_cast<const uint16_t*>(static_cast<const char*>(f->workspace) + c.L.z), f->l,
-                           static_cast<const uint16_t*>(w_router), nullptr, f->l, f->l};
+  g.seg[0] = lmoe::GemmSeg{z, f->l, wr, nullptr, f->l, f->l};
   g.gated = false;
   g.Cf = logits;
   g.ldc = q.E;
@@ -657,7 +658,6 @@ int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logi
   if ((rc = fwd_back(c)) != LMOE_OK) return drop(rc);
   return LMOE_OK;
 }
-
 
 void latent_moe_free(latent_moe_plan* p) { delete p; }
 

@@ -118,7 +118,7 @@ __device__ __forceinline__ uint64_t select_serial(uint64_t (&cand)[VPL], int k, 
   return mine;
 }
 
-// One wave per token; lane l holds logits e = l + 64*j (coalesced rows).
+// Selection of one token's top k by a wave.
 //
 // Threshold selection.  Let tau be the k-th largest of the 64 lane maxima of
 // the value words.  At least k entries (those lane maxima) have a value word
@@ -129,20 +129,12 @@ __device__ __forceinline__ uint64_t select_serial(uint64_t (&cand)[VPL], int k, 
 // each candidate's rank is the number of candidate keys above its own (keys
 // are unique, so ranks are).  When C exceeds 64 entries (many equal values,
 // NaN floods) the serial selection runs instead; both give the same result.
+// route_row: selection, softmax and output of one token whose logits the wave
+// holds (lane l: v[j] = logit l + 64j, any value for l + 64j >= E).  cb: 64
+// keys of LDS private to the wave.
 template <int VPL>
-__global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ logits, int64_t T, int E,
-                                                     int k, int32_t* __restrict__ ids,
-                                                     float* __restrict__ w) {
-  __shared__ uint64_t cbuf[4][64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t t = int64_t(blockIdx.x) * 4 + wv;
-  if (t >= T) return;
-  const float* row = logits + t * int64_t(E);
-  // all VPL loads are issued unconditionally (clamped index) so that they are
-  // in flight together; slots past E are then emptied
-  float v[VPL];
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
+__device__ __forceinline__ void route_row(const float (&v)[VPL], int E, int k, int lane, uint64_t* cb,
+                                          int32_t* __restrict__ ids_row, float* __restrict__ w_row) {
   uint64_t cand[VPL];
   uint32_t lane_max = 0;
 #pragma unroll
@@ -163,26 +155,26 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
     const uint64_t m = ballot(is_c);
     if (m != 0) {
       const int pos = total + lanes_below(m);
-      if (is_c && pos < 64) cbuf[wv][pos] = cand[j];
+      if (is_c && pos < 64) cb[pos] = cand[j];
       total += __popcll(m);
     }
   }
 
   uint64_t mine;  // lane i < k ends with the i-th selected key
   if (total <= 64) {
-    // cbuf[wv] is private to this wave, whose LDS accesses complete in order;
-    // the fences only keep the compiler from moving them across each other
+    // cb is private to this wave, whose LDS accesses complete in order; the
+    // fences only keep the compiler from moving them across each other
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    const uint64_t my = lane < total ? cbuf[wv][lane] : 0ull;
+    const uint64_t my = lane < total ? cb[lane] : 0ull;
     int rank = 0;
     for (int i = 0; i < total; ++i) rank += readlane_u64(my, i) > my ? 1 : 0;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    if (lane < total && rank < k) cbuf[wv][rank] = my;
+    if (lane < total && rank < k) cb[rank] = my;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    mine = lane < k ? cbuf[wv][lane] : 0ull;
+    mine = lane < k ? cb[lane] : 0ull;
   } else {
     mine = select_serial<VPL>(cand, k, lane);
   }
@@ -194,9 +186,27 @@ __global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ l
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, kWave);
   if (lane < k) {
-    ids[t * k + lane] = int32_t(0xffffffffu - uint32_t(mine));
-    w[t * k + lane] = ex / sum;
+    ids_row[lane] = int32_t(0xffffffffu - uint32_t(mine));
+    w_row[lane] = ex / sum;
   }
+}
+
+// One wave per token; lane l holds logits e = l + 64*j (coalesced rows).
+template <int VPL>
+__global__ __launch_bounds__(256) void router_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                     int k, int32_t* __restrict__ ids,
+                                                     float* __restrict__ w) {
+  __shared__ uint64_t cbuf[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t t = int64_t(blockIdx.x) * 4 + wv;
+  if (t >= T) return;
+  const float* row = logits + t * int64_t(E);
+  // all VPL loads are issued unconditionally (clamped index) so that they are
+  // in flight together; slots past E are emptied by route_row
+  float v[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
+  route_row<VPL>(v, E, k, lane, cbuf[wv], ids + t * k, w + t * k);
 }
 
 hipError_t launch_router(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,

@@ -445,8 +445,13 @@ GATE_LAYERS = [
     # E not a multiple of the 32-column gate tile, experts without rows
     ("gate_ragged", dict(T=77, d=192, l=128, E=200, k=8, S=1, I=64, Is=64)),
     ("gate_single", dict(T=1, d=128, l=64, E=33, k=5, S=0, I=64, Is=0)),
+    # latent 192 (no fused gate + top-k kernel for it): the split-K gate GEMM, then the router
+    ("gate_splitk", dict(T=150, d=128, l=192, E=100, k=4, S=1, I=64, Is=64)),
     # more than 512 tokens: the LDS-tiled gate GEMM, ragged row and column tiles
     ("gate_tiled", dict(T=1000, d=256, l=192, E=300, k=6, S=1, I=128, Is=64)),
+    # the fused gate + top-k kernel at E = 1024; latent 512 takes the split-K gate
+    ("gate_wide", dict(T=45, d=256, l=256, E=1024, k=8, S=0, I=64, Is=0)),
+    ("gate_l512", dict(T=45, d=256, l=512, E=1000, k=8, S=0, I=64, Is=0)),
     ("gate_w4a16", dict(T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256, mxfp4=True, w4a16=True)),
 ]
 
