@@ -307,6 +307,230 @@ hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s, hipEvent
   return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{uint32_t(NW * 64)}, lds, s, a, t0, t1);
 }
 
+// ---------------------------------------------- grouped, B two stages ahead ---
+// Grouped expert GEMMs on tiles of at most kTiledBM = 192 rows (the routing's
+// cut): 192 rows x 256 B rows (gated: 128 gate + 128 up), 8 waves as 2 x 4
+// with 96 x 64 wave tiles, K staged 64 at a time through two LDS buffers as
+// in tiled_gemm_kernel.  The smaller accumulator set (96 instead of 128
+// registers per lane) pays for a second register set for B, so B is loaded
+// two stages ahead of its LDS write (A, from a cached activation matrix, one
+// stage ahead): at prefill ~146 rows per expert leave the kernel waiting on
+// the weight stream, and the deeper B pipeline keeps twice as much of it in
+// flight.  The results are bit-identical to tiled_gemm_kernel's (the same
+// MFMAs in the same K order).  Needs K a multiple of 128 and >= 256.
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
+  constexpr int NTH = 512, BM = kTiledBM, BR = 256, NOUT = GATED ? 128 : 256;
+  constexpr int WAVES_N = 4, WM = BM / 2, WN = BR / WAVES_N;
+  constexpr int FM = WM / 32, FN = WN / 32, CPR = kBK / 8, RPC = NTH / CPR;
+  constexpr int A_CH = BM / RPC, B_CH = BR / RPC;
+  static_assert(BM % RPC == 0 && WM % 32 == 0, "tile shape");
+  static_assert(!GATED || B_CH % 2 == 0, "gated B chunks split evenly between gate and up");
+  extern __shared__ uint4 lds_u4[];
+  bf16_t* As = reinterpret_cast<bf16_t*>(lds_u4);  // [2][BM][kLdsK]
+  bf16_t* Bs = As + 2 * BM * kLdsK;                 // [2][BR][kLdsK]
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const int tiles_n = (g.N + NOUT - 1) / NOUT;
+  // grid sized for the host's upper bound; XCD-aware order over the real count
+  const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
+  if (blockIdx.x >= nreal) return;
+  const uint32_t lt = xcd_swizzle(blockIdx.x, nreal);
+  const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
+  const Tile tl = g.tiles[tm];
+  const int expert = tl.expert, row0 = tl.row_start, nrows = min(tl.nrows, BM);
+  const int n0 = tn * NOUT;
+  const bool active = wm * WM < nrows;
+  auto brow = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (GATED) return j < FN / 2 ? wn * (WN / 2) + j * 32 : BR / 2 + wn * (WN / 2) + (j - FN / 2) * 32;
+    else return wn * WN + j * 32;
+  };
+  // thread tid loads the 16-byte chunk kc8 of A rows i*64 + tid/8 and of B
+  // rows i*64 + tid/8 (gated: chunks i < B_CH/2 from the gate matrix)
+  const int kc8 = (tid % CPR) * 8;
+  const bf16_t* pa[A_CH];
+  const bf16_t* pb[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    int src = row0 + min(i * RPC + tid / CPR, nrows - 1);
+    if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
+    pa[i] = g.A + int64_t(src) * g.lda + kc8;
+  }
+  const int64_t be = int64_t(expert) * g.b_estride;
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const bool up = GATED && i >= B_CH / 2;
+    const int r = (up ? i - B_CH / 2 : i) * RPC + tid / CPR;
+    pb[i] = (up ? g.B3 : g.B) + be + int64_t(min(n0 + r, g.N - 1)) * g.ldb + kc8;
+  }
+  const int nk = g.K / kBK;
+  uint4 ra[A_CH], rbx[B_CH], rby[B_CH];  // A one stage ahead; B stages alternate between X and Y
+  auto load_a = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      if (i * RPC < nrows) ra[i] = ldg16(pa[i]);
+      pa[i] += kBK;
+    }
+  };
+  // (separate code for the two B sets: a lambda taking either set by
+  // reference would move them to memory)
+  auto load_bx = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      rbx[i] = ldg16(pb[i]);
+      pb[i] += kBK;
+    }
+  };
+  auto load_by = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      rby[i] = ldg16(pb[i]);
+      pb[i] += kBK;
+    }
+  };
+  auto store_a = [&](int buf) __attribute__((always_inline)) {
+    bf16_t* An = As + buf * BM * kLdsK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NTH;
+      if (i * RPC < nrows) *reinterpret_cast<uint4*>(&An[(c / CPR) * kLdsK + (c % CPR) * 8]) = ra[i];
+    }
+  };
+  auto store_bx = [&](int buf) __attribute__((always_inline)) {
+    bf16_t* Bn = Bs + buf * BR * kLdsK;
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * NTH;
+      *reinterpret_cast<uint4*>(&Bn[(c / CPR) * kLdsK + (c % CPR) * 8]) = rbx[i];
+    }
+  };
+  auto store_by = [&](int buf) __attribute__((always_inline)) {
+    bf16_t* Bn = Bs + buf * BR * kLdsK;
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * NTH;
+      *reinterpret_cast<uint4*>(&Bn[(c / CPR) * kLdsK + (c % CPR) * 8]) = rby[i];
+    }
+  };
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
+    constexpr int FA = decltype(fa_c)::value;
+    auto compute = [&](int buf, int ks0, int ks1) __attribute__((always_inline)) {
+      const bf16_t* Ab = As + buf * BM * kLdsK;
+      const bf16_t* Bb = Bs + buf * BR * kLdsK;
+#pragma unroll
+      for (int ks = ks0; ks < ks1; ++ks) {
+        const int kof = ks * 16 + (lane >> 5) * 8;
+        bf16x8 af[FA > 0 ? FA : 1];
+#pragma unroll
+        for (int i = 0; i < FA; ++i)
+          af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ab[(wm * WM + i * 32 + (lane & 31)) * kLdsK + kof]));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (FA > 0) {
+            const bf16x8 bf = as_bf16x8(*reinterpret_cast<const uint4*>(&Bb[(brow(j) + (lane & 31)) * kLdsK + kof]));
+#pragma unroll
+            for (int i = 0; i < FA; ++i) acc[i][j] = mfma_32x32x16(af[i], bf, acc[i][j]);
+          }
+        }
+      }
+    };
+    // step k: MFMAs on stage k (buffer k&1) around the LDS writes of stage
+    // k+1 (A from ra, B from set X for even k, Y for odd k) and the loads of
+    // A(k+2) and B(k+3) into the set just written out; which writes and loads
+    // a step has is fixed per call site, so no load sits behind a branch
+    auto step = [&](int buf, bool y, bool st, bool la, bool lb) __attribute__((always_inline)) {
+      compute(buf, 0, kBK / 32);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st) {
+        store_a(buf ^ 1);
+        if (y) store_by(buf ^ 1);
+        else store_bx(buf ^ 1);
+      }
+      if (la) load_a();
+      if (lb) {
+        if (y) load_by();
+        else load_bx();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf, kBK / 32, kBK / 16);
+      __syncthreads();
+    };
+    load_a();
+    load_bx();  // stage 0
+    store_a(0);
+    store_bx(0);
+    load_a();
+    load_bx();  // stage 1
+    load_by();  // B of stage 2
+    __syncthreads();
+    for (int kt = 0; kt < nk - 4; kt += 2) {
+      step(0, false, true, true, true);
+      step(1, true, true, true, true);
+    }
+    step(0, false, true, true, true);    // k = nk-4: loads A(nk-2), B(nk-1)
+    step(1, true, true, true, false);    // k = nk-3: loads A(nk-1)
+    step(0, false, true, false, false);  // k = nk-2: writes stage nk-1
+    step(1, true, false, false, false);  // k = nk-1
+  };
+  const int fa = active ? min(FM, (nrows - wm * WM + 31) / 32) : 0;
+  static_assert(FM == 3, "main loop specialisations cover up to 3 row subtiles per wave");
+  switch (fa) {
+    case 0: mainloop(std::integral_constant<int, 0>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    case 2: mainloop(std::integral_constant<int, 2>{}); break;
+    case 3: mainloop(std::integral_constant<int, 3>{}); break;
+    default: mainloop(std::integral_constant<int, FM>{}); break;  // (unreached; in this form the
+  }                                                                // register allocator does not spill)
+
+  // Epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores.
+  constexpr int CLD = NOUT + 8;
+  static_assert(BM * CLD <= 2 * (BM + BR) * kLdsK, "epilogue staging fits in the LDS buffers");
+  bf16_t* Cs = As;
+  if (active) {
+    constexpr int JO = GATED ? FN / 2 : FN, WO = GATED ? WN / 2 : WN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      if (i < fa)
+#pragma unroll
+        for (int j = 0; j < JO; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int col = wn * WO + j * 32 + (lane & 31);
+            float x = acc[i][j][v];
+            if constexpr (GATED) x = silu_mul(x, acc[i][j + FN / 2][v]);
+            Cs[row * CLD + col] = f32_to_bf16(x);
+          }
+  }
+  __syncthreads();
+  constexpr int OCPR = NOUT / 8;
+  for (int c = tid; c < BM * OCPR; c += NTH) {
+    const int row = c / OCPR, cc = c % OCPR;
+    if (row < nrows && n0 + cc * 8 < g.N) {
+      *reinterpret_cast<uint4*>(g.C + (int64_t(row0) + row) * g.ldc + n0 + cc * 8) =
+          *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
+    }
+  }
+}
+
+template <bool GATED>
+hipError_t run_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  constexpr int NOUT = GATED ? 128 : 256;
+  const size_t lds = size_t(2) * (kTiledBM + 256) * kLdsK * sizeof(bf16_t);
+  auto kern = grouped_tiled_kernel<GATED>;
+  if (hipError_t e = allow_dynamic_lds((const void*)kern, int(lds)); e != hipSuccess) return e;
+  const int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
+  if (nblk <= 0) return hipSuccess;
+  return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512u}, lds, s, g, t0, t1);
+}
+
 // ------------------------------------------------------- small-M dense split-K ---
 // Dense GEMMs with few rows (decode-sized batches): one 16-row x 32-column
 // output tile per workgroup; the 4 waves split the (segment-concatenated) K
@@ -466,6 +690,9 @@ hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
 }
 
 hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  // routing cuts tiles at kTiledBM rows; both kernels take tiles of up to 192 rows
+  static_assert(kTiledBM <= 192, "tile table granularity");
+  if (g.K % 128 == 0 && g.K >= 256) return g.gated ? run_grouped<true>(g, s, t0, t1) : run_grouped<false>(g, s, t0, t1);
   TiledArgs a{};
   a.M = 0;
   a.N = g.N;
@@ -478,7 +705,6 @@ hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t 
   a.ntiles = g.ntiles;
   a.C = g.C;
   a.ldc = g.ldc;
-  static_assert(kTiledBM == 256, "tile table granularity");
   if (g.gated) return run_tiled<8, 2, true, true, true>(a, g.max_tiles, s, t0, t1);
   return run_tiled<8, 2, false, true, true>(a, g.max_tiles, s, t0, t1);
 }

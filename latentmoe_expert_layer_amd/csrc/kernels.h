@@ -33,7 +33,7 @@ struct Tile {
 
 // Row-tile granularities of the tile tables that routing builds.
 constexpr int kSkinnyBM = 16;   // weight-streaming (decode-shaped) kernel
-constexpr int kTiledBM = 256;   // LDS-tiled (prefill-shaped) kernel
+constexpr int kTiledBM = 192;   // LDS-tiled (prefill-shaped) kernels: a tile holds <= 192 rows
 
 inline int64_t max_tiles(int64_t rows, int64_t E, int bm) {
   return rows / bm + (rows < E ? rows : E) + 1;

@@ -174,6 +174,8 @@ SMALL_LAYERS = [
     ("tiled_path", dict(T=600, d=256, l=512, E=8, k=2, S=1, I=256, Is=128)),
     # LDS-tiled dense projections with a ragged last row tile, odd latent width
     ("mid_ragged", dict(T=1000, d=320, l=192, E=24, k=4, S=2, I=128, Is=64)),
+    # weight-streaming experts over several K batches: FC1 K = 512 (two of 256), FC2 K = 384 (three of 128)
+    ("skinny_wide", dict(T=100, d=256, l=512, E=64, k=4, S=1, I=384, Is=128)),
 ]
 
 
