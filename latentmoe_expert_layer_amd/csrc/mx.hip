@@ -120,10 +120,10 @@ struct MxArgs {
   const int32_t* ntiles;
 };
 
-template <bool GATED>
+template <bool GATED, int BM = 256>
 constexpr int mx_lds_bytes() {
-  constexpr int stage = 256 * kMxARow + 256 * kMxBRow + 512 * 4;
-  constexpr int epi = 256 * ((GATED ? 128 : 256) + 8) * 2;
+  constexpr int stage = BM * kMxARow + 256 * kMxBRow + 512 * 4;  // one scale word per thread
+  constexpr int epi = BM * ((GATED ? 128 : 256) + 8) * 2;
   return 2 * stage > epi ? 2 * stage : epi;
 }
 
@@ -137,12 +137,22 @@ constexpr int mx_lds_bytes() {
 // on the second 64 K | barrier.  A wave multiplies only its 32-row subtiles
 // that hold rows of the tile; 64-row A chunks past the tile's rows are not
 // loaded.
-template <bool GATED>
+//
+// DEEP (K >= 512): tiles of at most kTiledBM = 192 rows (the routing's cut),
+// 96 x 64 wave tiles, and a second register set for the weight codes and the
+// scale words, so those are loaded two stages ahead of their LDS write (the
+// activation codes, from a cached matrix, one stage ahead): the accumulators
+// this frees (96 instead of 128 registers per lane) pay for it, and twice as
+// much of the weight stream is in flight per CU.  The same MFMAs in the same
+// K order: bit-identical results.
+template <bool GATED, bool DEEP = false>
 __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
-  constexpr int NTH = 512, BM = 256, BR = 256, NOUT = GATED ? 128 : 256;
-  constexpr int WAVES_N = 4, WM = 128, WN = 64, FM = 4, FN = 2;
+  constexpr int NTH = 512, BM = DEEP ? kTiledBM : 256, BR = 256, NOUT = GATED ? 128 : 256;
+  constexpr int WAVES_N = 4, WM = BM / 2, WN = 64, FM = WM / 32, FN = 2;
+  constexpr int A_CH = BM / 64;  // A rows i*64 + tid/8 per thread and stage
+  static_assert(BM % 64 == 0 && BM + BR <= NTH, "tile shape");
   constexpr int A_STAGE = BM * kMxARow, B_STAGE = BR * kMxBRow;
-  constexpr int STAGE = A_STAGE + B_STAGE + (BM + BR) * 4;
+  constexpr int STAGE = A_STAGE + B_STAGE + NTH * 4;  // scale words: one slot per thread
   extern __shared__ uint4 lds_u4[];
   uint8_t* lds = reinterpret_cast<uint8_t*>(lds_u4);
 
@@ -170,33 +180,42 @@ __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
     return src;
   };
   auto b_row = [&](int r, bool up) __attribute__((always_inline)) -> int64_t { return int64_t(expert) * g.N + min(n0 + r, g.N - 1); };
-  const uint8_t* pa[4];
+  const uint8_t* pa[A_CH];
   const uint8_t* pb[2];
   const uint8_t* ps;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pa[i] = g.A + a_src(i * 64 + tid / 8) * K + (tid % 8) * 16;
+  for (int i = 0; i < A_CH; ++i) pa[i] = g.A + a_src(i * 64 + tid / 8) * K + (tid % 8) * 16;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const bool up = GATED && i == 1;
     const int r = (GATED ? 0 : i * 128) + tid / 4;
     pb[i] = (up ? g.B3 : g.B) + b_row(r, up) * (K / 2) + (tid % 4) * 16;
   }
+  // scale words: A row tid (tid < BM) or B row tid - BM (tid < BM + BR);
+  // threads past that (DEEP) re-read B row 0's word into a slot nobody reads
+  const bool has_scale = tid < BM + BR;
   if (tid < BM) {
     ps = g.As + a_src(tid) * KB;
   } else {
-    const int r = tid - BM;
+    const int r = has_scale ? tid - BM : 0;
     const bool up = GATED && r >= BR / 2;
     ps = (up ? g.B3s : g.Bs) + b_row(up ? r - BR / 2 : r, up) * KB;
   }
 
-  u32x4v ra[4], rb[2];  // native vectors, so the stage stays in registers
+  u32x4v ra[A_CH], rb[2];  // native vectors, so the stage stays in registers
   uint32_t rs;
-  auto gload = [&]() __attribute__((always_inline)) {
+  u32x4v rb2[DEEP ? 2 : 1];  // DEEP: the second set of weight codes and scale word
+  uint32_t rs2;
+  // DEEP loads every A chunk (rows past the tile repeat its last row): with
+  // no branch around them the two-ahead pipeline keeps its registers
+  auto gload_a = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i * 64 < nrows) ra[i] = *reinterpret_cast<const u32x4v*>(pa[i]);
+    for (int i = 0; i < A_CH; ++i) {
+      if (DEEP || i * 64 < nrows) ra[i] = *reinterpret_cast<const u32x4v*>(pa[i]);
       pa[i] += kMxBK;
     }
+  };
+  auto gload_b = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       rb[i] = *reinterpret_cast<const u32x4v*>(pb[i]);
@@ -205,16 +224,42 @@ __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
     rs = *reinterpret_cast<const uint32_t*>(ps);
     ps += kMxBK / 32;
   };
-  auto lstore = [&](int buf) __attribute__((always_inline)) {
+  auto gload_b2 = [&]() __attribute__((always_inline)) {  // (separate code: a lambda taking
+#pragma unroll                                              //  either set by reference would
+    for (int i = 0; i < 2; ++i) {                           //  move the sets to memory)
+      rb2[i] = *reinterpret_cast<const u32x4v*>(pb[i]);
+      pb[i] += kMxBK / 2;
+    }
+    rs2 = *reinterpret_cast<const uint32_t*>(ps);
+    ps += kMxBK / 32;
+  };
+  auto gload = [&]() __attribute__((always_inline)) {
+    gload_a();
+    gload_b();
+  };
+  auto lstore_a = [&](int buf) __attribute__((always_inline)) {
     uint8_t* sA = lds + buf * STAGE;
-    uint8_t* sB = sA + A_STAGE;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i)
+      if (DEEP || i * 64 < nrows) *reinterpret_cast<u32x4v*>(sA + (i * 64 + tid / 8) * kMxARow + (tid % 8) * 16) = ra[i];
+  };
+  auto lstore_b = [&](int buf) __attribute__((always_inline)) {
+    uint8_t* sB = lds + buf * STAGE + A_STAGE;
     uint8_t* sS = sB + B_STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i * 64 < nrows) *reinterpret_cast<u32x4v*>(sA + (i * 64 + tid / 8) * kMxARow + (tid % 8) * 16) = ra[i];
-#pragma unroll
     for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4v*>(sB + (i * 128 + tid / 4) * kMxBRow + (tid % 4) * 16) = rb[i];
-    *reinterpret_cast<uint32_t*>(sS + tid * 4) = rs;
+    if (DEEP || has_scale) *reinterpret_cast<uint32_t*>(sS + tid * 4) = rs;
+  };
+  auto lstore_b2 = [&](int buf) __attribute__((always_inline)) {
+    uint8_t* sB = lds + buf * STAGE + A_STAGE;
+    uint8_t* sS = sB + B_STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4v*>(sB + (i * 128 + tid / 4) * kMxBRow + (tid % 4) * 16) = rb2[i];
+    if (DEEP || has_scale) *reinterpret_cast<uint32_t*>(sS + tid * 4) = rs2;
+  };
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
+    lstore_a(buf);
+    lstore_b(buf);
   };
 
   // B-tile row of this wave's n-subtile j (gated: j = 0 gate, j = 1 up)
@@ -273,19 +318,57 @@ __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
         }
       }
     };
-    gload();
-    lstore(0);
-    if (nk > 1) gload();
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      compute(buf, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nk) lstore(buf ^ 1);
-      if (kt + 2 < nk) gload();
-      __builtin_amdgcn_sched_barrier(0);
-      compute(buf, 1);
+    if constexpr (DEEP) {
+      // step k: MFMAs on stage k (buffer k&1) around the LDS writes of stage
+      // k+1 (weights from set 1 for even k, set 2 for odd k) and the loads of
+      // A(k+2) and of the weights of stage k+3 into the set just written out;
+      // each call site has a fixed set of writes and loads, so no load sits
+      // behind a branch.  Needs nk even, >= 4.
+      auto step = [&](int buf, bool second, bool st, bool la, bool lb) __attribute__((always_inline)) {
+        compute(buf, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st) {
+          lstore_a(buf ^ 1);
+          if (second) lstore_b2(buf ^ 1);
+          else lstore_b(buf ^ 1);
+        }
+        if (la) gload_a();
+        if (lb) {
+          if (second) gload_b2();
+          else gload_b();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf, 1);
+        __syncthreads();
+      };
+      gload();
+      lstore(0);
+      gload();     // stage 1: A -> ra, weights -> set 1
+      gload_b2();  // weights of stage 2 -> set 2
       __syncthreads();
+      for (int kt = 0; kt < nk - 4; kt += 2) {
+        step(0, false, true, true, true);
+        step(1, true, true, true, true);
+      }
+      step(0, false, true, true, true);    // k = nk-4: loads A(nk-2), weights(nk-1)
+      step(1, true, true, true, false);    // k = nk-3: loads A(nk-1)
+      step(0, false, true, false, false);  // k = nk-2: writes stage nk-1
+      step(1, true, false, false, false);
+    } else {
+      gload();
+      lstore(0);
+      if (nk > 1) gload();
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        compute(buf, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) lstore(buf ^ 1);
+        if (kt + 2 < nk) gload();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(buf, 1);
+        __syncthreads();
+      }
     }
   };
   const int fa = wm * WM < nrows ? min(FM, (nrows - wm * WM + 31) / 32) : 0;
@@ -294,13 +377,13 @@ __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
     case 1: mainloop(std::integral_constant<int, 1>{}); break;
     case 2: mainloop(std::integral_constant<int, 2>{}); break;
     case 3: mainloop(std::integral_constant<int, 3>{}); break;
-    default: mainloop(std::integral_constant<int, 4>{}); break;
+    default: mainloop(std::integral_constant<int, FM>{}); break;
   }
 
   // Epilogue (gated: SwiGLU of subtile 0 with its up subtile 1), bf16 staging
   // in LDS, then 16-byte row-contiguous stores.
   constexpr int CLD = NOUT + 8;
-  static_assert(BM * CLD * 2 <= mx_lds_bytes<GATED>(), "epilogue staging fits");
+  static_assert(BM * CLD * 2 <= mx_lds_bytes<GATED, BM>(), "epilogue staging fits");
   bf16_t* Cs = reinterpret_cast<bf16_t*>(lds);
   constexpr int JO = GATED ? 1 : FN, WO = GATED ? WN / 2 : WN;
 #pragma unroll
@@ -347,11 +430,11 @@ __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
   }
 }
 
-template <bool GATED>
+template <bool GATED, bool DEEP>
 hipError_t run_mx(const MxArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   constexpr int NOUT = GATED ? 128 : 256;
-  constexpr size_t lds = size_t(mx_lds_bytes<GATED>());
-  auto kern = mx_grouped_kernel<GATED>;
+  constexpr size_t lds = size_t(mx_lds_bytes<GATED, DEEP ? kTiledBM : 256>());
+  auto kern = mx_grouped_kernel<GATED, DEEP>;
   if (hipError_t e = allow_dynamic_lds((const void*)kern, int(lds)); e != hipSuccess) return e;
   const int64_t nblk = max_tiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
@@ -386,7 +469,12 @@ hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s, hipEvent_t t0, h
   a.Cqs = g.Cqs;
   a.tiles = g.tiles;
   a.ntiles = g.ntiles;
-  return g.gated ? run_mx<true>(a, g.max_tiles, s, t0, t1) : run_mx<false>(a, g.max_tiles, s, t0, t1);
+  // routing cuts tiles at kTiledBM rows, within both kernels' reach; the deep
+  // pipeline needs an even number (>= 4) of 128-wide K stages
+  static_assert(kTiledBM <= 256 && kTiledBM % 64 == 0, "tile table granularity");
+  if (g.K % 256 == 0 && g.K >= 512)
+    return g.gated ? run_mx<true, true>(a, g.max_tiles, s, t0, t1) : run_mx<false, true>(a, g.max_tiles, s, t0, t1);
+  return g.gated ? run_mx<true, false>(a, g.max_tiles, s, t0, t1) : run_mx<false, false>(a, g.max_tiles, s, t0, t1);
 }
 
 }  // namespace lmoe

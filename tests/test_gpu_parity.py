@@ -306,6 +306,8 @@ MX_LAYERS = [
     ("mx_small", dict(T=203, d=192, l=256, E=9, k=3, S=1, I=128, Is=64, mxfp4=True)),
     ("mx_ragged", dict(T=77, d=128, l=384, E=40, k=8, S=2, I=256, Is=64, mxfp4=True)),
     ("mx_heavy", dict(T=700, d=256, l=128, E=4, k=2, S=0, I=384, Is=0, mxfp4=True)),
+    # K = 512 for both GEMMs (the two-stages-ahead pipeline), experts over 192 rows (two tiles each)
+    ("mx_deep", dict(T=400, d=128, l=512, E=3, k=2, S=1, I=512, Is=64, mxfp4=True)),
 ]
 
 
