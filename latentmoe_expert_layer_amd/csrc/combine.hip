@@ -111,6 +111,97 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
   }
 }
 
+// Register-resident form for widths l == WPT * NC * 64 * VEC: a token's row is
+// split over WPT waves of the 256-thread block (WPT divides 4); each wave
+// holds its NC chunks of 64*VEC columns in registers from the weighted sum
+// to the store, keeping 16 loads in flight (16/NC rows at a time).  The
+// sum of squares adds the waves' partial sums in part order through LDS.
+// More and shorter waves than one-wave-per-token, and no LDS round trip of
+// the row.  Every element sums its slots in ascending order.
+template <int VEC, int WPT, int NC>
+__global__ __launch_bounds__(256) void combine_reg_kernel(const bf16_t* __restrict__ Y,
+                                                          const int32_t* __restrict__ row_pos,
+                                                          const float* __restrict__ w, int64_t T, int k, int l,
+                                                          const bf16_t* __restrict__ gain, float eps,
+                                                          bf16_t* __restrict__ out) {
+  static_assert(4 % WPT == 0, "a token's waves share one block");
+  typedef typename VecT<VEC>::type V;
+  constexpr int TPB = 4 / WPT;                              // tokens per block
+  constexpr int RPR = NC >= kRowsInFlight ? 1 : kRowsInFlight / NC;  // rows per round
+  __shared__ float part_ss[4];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t t = int64_t(blockIdx.x) * TPB + wid / WPT;
+  const bool live = t < T;
+  const int col0 = (wid % WPT) * NC * 64 * VEC + lane * VEC;
+  int32_t my_p = 0;
+  float my_w = 0.0f;
+  if (live && lane < k) {
+    my_p = row_pos[t * k + lane];
+    my_w = w[t * k + lane];
+  }
+  float acc[NC][VEC];
+#pragma unroll
+  for (int q = 0; q < NC; ++q)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[q][i] = 0.0f;
+  if (live) {
+    for (int j0 = 0; j0 < k; j0 += RPR) {
+      V v[RPR][NC];
+      // loads past the last slot re-read slot k-1 (no branch, so all of
+      // them are in flight together); their values are not used
+#pragma unroll
+      for (int u = 0; u < RPR; ++u) {
+        const int64_t p = __builtin_amdgcn_readlane(my_p, min(j0 + u, k - 1));
+#pragma unroll
+        for (int q = 0; q < NC; ++q) v[u][q] = *reinterpret_cast<const V*>(Y + p * l + col0 + q * 64 * VEC);
+      }
+#pragma unroll
+      for (int u = 0; u < RPR; ++u) {
+        if (j0 + u < k) {
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j0 + u));
+#pragma unroll
+          for (int q = 0; q < NC; ++q) {
+            float f[VEC];
+            unpack<VEC>(v[u][q], f);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[q][i] += wj * f[i];
+          }
+        }
+      }
+    }
+  }
+  float scale = 1.0f;
+  if (gain) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NC; ++q)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) ss += acc[q][i] * acc[q][i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    if constexpr (WPT > 1) {
+      // every wave of the block reaches the barrier, live or not
+      if (lane == 0) part_ss[wid] = ss;
+      __syncthreads();
+      ss = 0.0f;
+#pragma unroll
+      for (int q = 0; q < WPT; ++q) ss += part_ss[(wid / WPT) * WPT + q];
+    }
+    scale = 1.0f / sqrtf(ss / float(l) + eps);
+  }
+  if (!live) return;
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    const int col = col0 + q * 64 * VEC;
+    float g[VEC];
+    if (gain) unpack<VEC>(*reinterpret_cast<const V*>(gain + col), g);
+    uint16_t o[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[i] = f32_to_bf16(gain ? acc[q][i] * scale * g[i] : acc[q][i]);
+    *reinterpret_cast<V*>(out + t * l + col) = *reinterpret_cast<const V*>(o);
+  }
+}
+
 // k == 1 without a norm (one expert-parallel rank's share): out[r] =
 // bf16(w[r] * Y[row_pos[r]]), the weighted un-permutation of the received
 // rows.  One wave per row; lane owns VEC contiguous elements of each
@@ -160,6 +251,22 @@ hipError_t launch_combine(const uint16_t* Y, const int32_t* row_pos, const float
     else unpermute_kernel<1><<<grid, block, 0, s>>>(Y, row_pos, w, T, l, out);
     return hipGetLastError();
   }
+  // register-resident widths: a token's row over WPT waves, NC chunks each
+#define LMOE_COMBINE_REG(VEC, WPT, NC)                                                                   \
+  if (l == WPT * NC * 64 * VEC) {                                                                        \
+    combine_reg_kernel<VEC, WPT, NC><<<dim3{uint32_t((T + 4 / WPT - 1) / (4 / WPT))}, block, 0, s>>>(   \
+        Y, row_pos, w, T, k, l, gain, eps, out);                                                         \
+    return hipGetLastError();                                                                            \
+  }
+  LMOE_COMBINE_REG(8, 4, 2)  // 4096
+  LMOE_COMBINE_REG(8, 4, 1)  // 2048
+  LMOE_COMBINE_REG(8, 2, 1)  // 1024
+  LMOE_COMBINE_REG(8, 1, 1)  // 512
+  LMOE_COMBINE_REG(4, 1, 1)  // 256
+  LMOE_COMBINE_REG(2, 1, 1)  // 128
+  LMOE_COMBINE_REG(1, 1, 1)  // 64
+#undef LMOE_COMBINE_REG
+  // other widths: one wave per token, the fp32 row parked in LDS
   const size_t lds = size_t(4) * l * sizeof(float);
   if (lds > 64 * 1024) return hipErrorInvalidValue;
   if (l % 512 == 0) combine_kernel<8><<<grid, block, lds, s>>>(Y, row_pos, w, T, k, l, gain, eps, out);

@@ -176,6 +176,12 @@ SMALL_LAYERS = [
     ("mid_ragged", dict(T=1000, d=320, l=192, E=24, k=4, S=2, I=128, Is=64)),
     # weight-streaming experts over several K batches: FC1 K = 512 (two of 256), FC2 K = 384 (three of 128)
     ("skinny_wide", dict(T=100, d=256, l=512, E=64, k=4, S=1, I=384, Is=128)),
+    # wide latents: the combine splits a token's row over 4 or 2 waves (with two
+    # chunks per wave at 4096), slot counts leave the last round part-empty,
+    # and token counts leave the last block part-empty
+    ("latent_4096", dict(T=21, d=64, l=4096, E=8, k=5, S=0, I=64, Is=0)),
+    ("latent_2048", dict(T=70, d=128, l=2048, E=12, k=6, S=1, I=128, Is=64)),
+    ("latent_1024", dict(T=45, d=128, l=1024, E=32, k=19, S=0, I=128, Is=0)),
 ]
 
 
@@ -208,11 +214,12 @@ def test_layer_deterministic_and_empty():
     assert y.shape == (0, 512)
 
 
-@pytest.mark.parametrize("R,E,l,I", [(300, 7, 320, 128), (1000, 56, 384, 256), (513, 3, 2048, 512)])
+@pytest.mark.parametrize("R,E,l,I", [(300, 7, 320, 128), (1000, 56, 384, 256), (513, 3, 2048, 512), (257, 5, 1024, 128)])
 def test_rows_mode_small(R, E, l, I):
     """Expert-parallel share at small sizes, every row compared: latent widths
-    that are multiples of 64, 128 and 512 (each vector width of the weighted
-    un-permutation), on the weight-streaming (R <= 32 E) and tiled paths."""
+    that are multiples of 64, 128, 512, 1024 and 2048 (each vector width and
+    row-piece count of the weighted un-permutation), on the weight-streaming
+    (R <= 32 E) and tiled paths."""
     cfg = W.custom(f"rows_{R}_{E}_{l}", T=R, d=0, l=l, E=E, k=1, S=0, I=I, Is=0, rows_mode=True, norm=False,
                    zipf_s=1.1, seed=R)
     log(f"rows mode small: {cfg}")
