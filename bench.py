@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0 = enough to beat the LLC)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle budget (0 = skip)")
     ap.add_argument("--no-stage-events", action="store_true")
+    ap.add_argument("--api", choices=["layer", "route-forward"], default="layer",
+                    help="where the logits are given: latent_moe_layer (one call, its plan reused) or "
+                         "latent_moe_route + latent_moe_forward")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: each copy's route+forward captured once in a HIP graph and replayed")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -202,13 +205,17 @@ def main():
     n_ev = lm.N_STAGE_EVENTS
     use_events = not args.no_stage_events
 
+    one_call = cfg.router_gemm or (args.api == "layer" and not cfg.rows_mode)
+
     def run_call(s, strm, events=None):
         """One layer call on copy s: latent_moe_layer (its plan reused across
-        calls) or latent_moe_route + latent_moe_forward."""
-        if cfg.router_gemm:
+        calls; with the router gate or the given logits) or latent_moe_route +
+        latent_moe_forward."""
+        if one_call:
             if s["plan"] is not None:
                 lm.latent_moe_plan_set_stage_events(s["plan"], events)
-            s["plan"] = lm.latent_moe_layer(s["ra"], P(s["inp"]["w_r"]), P(s["logits"]), s["fa"], strm, s["plan"])
+            gate = P(s["inp"]["w_r"]) if cfg.router_gemm else None
+            s["plan"] = lm.latent_moe_layer(s["ra"], gate, P(s["logits"]), s["fa"], strm, s["plan"])
             return
         plan = lm.latent_moe_route(s["ra"], strm)
         if events is not None:
@@ -217,15 +224,7 @@ def main():
         lm.latent_moe_free(plan)
 
     def step(i, events=None):
-        s = sets[i % copies]
-        if cfg.router_gemm:
-            run_call(s, stream, events)
-            return
-        plan = lm.latent_moe_route(s["ra"], stream)
-        if events is not None:
-            lm.latent_moe_plan_set_stage_events(plan, events)
-        lm.latent_moe_forward(plan, s["fa"], stream)
-        lm.latent_moe_free(plan)
+        run_call(sets[i % copies], stream, events)
 
     # every copy runs once before the warm-up (untimed), so each one's routing
     # outputs, which the algorithmic byte count below reads, exist however
@@ -362,6 +361,7 @@ def main():
 
     extra = {
         "mode": mode,
+        "api": "latent_moe_layer" if one_call else "latent_moe_route + latent_moe_forward",
         "eager_ms_per_step_with_stage_events": None if eager_ms is None else round(eager_ms, 5),
         "copies_cycled": copies,
         "wall_s": round(wall, 3),
@@ -375,6 +375,9 @@ def main():
     if cfg.router_gemm:
         extra["stage_note"] = ("shared_gate_up also covers the router gate GEMM, the top-k and the permutation "
                                "(latent_moe_layer runs them between the down-projection and FC1)")
+    elif one_call:
+        extra["stage_note"] = ("down_proj also covers the top-k (in the same launch at T <= 512) and "
+                               "shared_gate_up the permutation (latent_moe_layer with the logits given)")
     if use_events:
         for n, fl, by in (("fc1", fc1_flop, fc1_bytes), ("fc2", fc2_flop, fc2_bytes)):
             us = stages[n]

@@ -192,20 +192,26 @@ typedef struct {
 int latent_moe_forward(const latent_moe_plan* plan, const lmoe_forward_args* args, void* hip_stream);
 
 /*
- * The whole layer from the hidden states alone: the router's logits are
- * computed from the latent (vLLM Kimi K3 post, section 1: the latent
- * down-projection is inserted in front of the router), then routing and the
- * forward run as above, in one call:
- *   z      = x W_in^T                  (bf16, as in latent_moe_forward)
- *   logits = z W_router^T              fp32 [T,E], one fp32 accumulation per
+ * The whole layer in one call: routing and the forward as above.  Two ways
+ * to get the routing:
+ *  - with a router gate (w_router != NULL) the logits are computed from the
+ *    latent (vLLM Kimi K3 post, section 1: the latent down-projection is
+ *    inserted in front of the router):
+ *      z      = x W_in^T               (bf16, as in latent_moe_forward)
+ *      logits = z W_router^T           fp32 [T,E], one fp32 accumulation per
  *                                      entry, not rounded
- *   routing of `logits` as latent_moe_route in logits mode, then the rest of
- *   latent_moe_forward on that routing.
+ *    then routing of `logits` as latent_moe_route in logits mode;
+ *  - without one (w_router == NULL) the route arguments give the logits or
+ *    the ids, exactly as for latent_moe_route.  Since the routing then does
+ *    not depend on x, at T <= 512 in logits mode the top-k runs in the same
+ *    launch as the down-projection and the shared experts' gate/up.
+ * The results equal latent_moe_route followed by latent_moe_forward.
  * Arguments:
- *   route     as for latent_moe_route, with logits == NULL and ids_in == NULL;
- *             topk_ids and topk_w are required (E <= 1024)
- *   w_router  bf16 [E,l] router gate (device)
- *   logits    fp32 [T,E] out (device): the computed logits
+ *   route     as for latent_moe_route; with w_router, logits == NULL and
+ *             ids_in == NULL, and topk_ids, topk_w are required (E <= 1024)
+ *   w_router  bf16 [E,l] router gate (device), or NULL
+ *   logits    with w_router: fp32 [T,E] out (device), the computed logits;
+ *             without: must be NULL
  *   fwd       as for latent_moe_forward; w_in must not be NULL (no rows mode)
  *   plan_io   in/out.  *plan_io == NULL: a new plan is returned in it (free it
  *             with latent_moe_free).  Otherwise it must be a plan from an
@@ -215,7 +221,8 @@ int latent_moe_forward(const latent_moe_plan* plan, const lmoe_forward_args* arg
  * was enqueued and *plan_io is unchanged.  On LMOE_EHIP a plan allocated by
  * this call is freed and *plan_io is set to NULL (a reused plan stays the
  * caller's).  With stage events set, stage 2 (events[1] -> events[2]) also
- * covers the gate GEMM, the top-k and the permutation.
+ * covers the gate GEMM (if any), the top-k and the permutation; where the
+ * top-k shares the down-projection's launch it falls in stage 1.
  */
 int latent_moe_layer(const lmoe_route_args* route, const void* w_router, float* logits,
                      const lmoe_forward_args* fwd, void* hip_stream, latent_moe_plan** plan_io);

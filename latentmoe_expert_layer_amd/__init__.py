@@ -239,17 +239,21 @@ def forward(routing: Routing, x: torch.Tensor, w1, w3, w2, *, w_in=None, w_out=N
     return y
 
 
-def layer(x: torch.Tensor, w_r: torch.Tensor, k: int, w1, w3, w2, *, w_in, w_out, ws1=None, ws3=None,
+def layer(x: torch.Tensor, w_r: Optional[torch.Tensor], k: int, w1, w3, w2, *, w_in, w_out, ws1=None, ws3=None,
           ws2=None, norm_w=None, eps: float = 1e-6, s1=None, s3=None, s2=None, mxfp4: bool = False,
           w4a16: bool = False, y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
           route_workspace: Optional[torch.Tensor] = None, stream=None, I: Optional[int] = None,
-          routing: Optional[Routing] = None):
-    """The whole layer from x alone (``latent_moe_layer``): the router's logits
-    are z W_r^T on the latent.  Returns (Routing with .logits, y).  Passing the
-    Routing of an earlier call with the same shapes reuses its buffers and plan."""
+          routing: Optional[Routing] = None, logits: Optional[torch.Tensor] = None):
+    """The whole layer in one call (``latent_moe_layer``).  With a router gate
+    w_r [E,l] the logits are z W_r^T on the latent; with w_r None they are the
+    given ``logits`` [T,E] (fp32).  Returns (Routing with .logits, y).  Passing
+    the Routing of an earlier call with the same shapes reuses its buffers and
+    plan."""
+    if (w_r is None) == (logits is None):
+        raise ValueError("give exactly one of w_r and logits")
     T, dev = x.shape[0], x.device
-    E, l = w_r.shape
-    d = w_in.shape[1]
+    E = w_r.shape[0] if logits is None else logits.shape[1]
+    l, d = w_in.shape
     if I is None:
         I = w1.shape[1]
     S = 0 if ws1 is None else ws1.shape[0]
@@ -266,15 +270,17 @@ def layer(x: torch.Tensor, w_r: torch.Tensor, k: int, w1, w3, w2, *, w_in, w_out
                           torch.empty(T, k, dtype=torch.float32, device=dev),
                           torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.int32, device=dev),
                           torch.empty(E + 1, dtype=torch.int32, device=dev), route_workspace, None,
-                          logits=torch.empty(T, E, dtype=torch.float32, device=dev))
+                          logits=torch.empty(T, E, dtype=torch.float32, device=dev) if logits is None else logits)
     elif (routing.T, routing.E, routing.k) != (T, E, k) or routing.logits is None:
         raise ValueError("the Routing passed in is not from a layer call of this shape")
+    elif logits is not None:
+        routing.logits = logits
     if workspace is None:
         ws_bytes = forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt, False)
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     if y is None:
         y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
-    ra = RouteArgs(T=T, E=E, k=k, logits=None, ids_in=None, weights_in=None, topk_ids=_p(routing.topk_ids),
+    ra = RouteArgs(T=T, E=E, k=k, logits=_p(logits), ids_in=None, weights_in=None, topk_ids=_p(routing.topk_ids),
                    topk_w=_p(routing.topk_w), sorted_row=_p(routing.sorted_row), row_pos=_p(routing.row_pos),
                    offsets=_p(routing.offsets), workspace=_p(routing.workspace),
                    workspace_bytes=routing.workspace.numel())
@@ -282,7 +288,8 @@ def layer(x: torch.Tensor, w_r: torch.Tensor, k: int, w1, w3, w2, *, w_in, w_out
                      w1=_p(w1), w3=_p(w3), w2=_p(w2), s1=_p(s1), s3=_p(s3), s2=_p(s2), norm_w=_p(norm_w),
                      w_out=_p(w_out), ws1=_p(ws1), ws3=_p(ws3), ws2=_p(ws2), y=_p(y),
                      workspace=_p(workspace), workspace_bytes=workspace.numel())
-    routing.plan = latent_moe_layer(ra, _p(w_r), _p(routing.logits), fa, _stream(stream), routing.plan)
+    routing.plan = latent_moe_layer(ra, _p(w_r), None if w_r is None else _p(routing.logits), fa, _stream(stream),
+                                    routing.plan)
     routing.keep = [workspace]
     return routing, y
 

@@ -230,12 +230,15 @@ void fill_plan(latent_moe_plan* p, const lmoe_route_args* a, bool ids_mode) {
 }
 
 // Router top-k/softmax over `logits` (or the id copy in ids mode), then the
-// permutation and the tile tables.
-int route_enqueue(const latent_moe_plan* p, const lmoe_route_args* a, const float* logits, hipStream_t s) {
+// permutation and the tile tables.  router_done: the top-k has already been
+// enqueued (in the down-projection's launch); only the permutation is left.
+int route_enqueue(const latent_moe_plan* p, const lmoe_route_args* a, const float* logits, hipStream_t s,
+                  bool router_done = false) {
   const int64_t R = p->T * p->k;
   if (R == 0) return LMOE_OK;
   hipError_t e;
-  if (p->ids_mode) {
+  if (router_done) {
+  } else if (p->ids_mode) {
     if (a->topk_ids || a->topk_w) {
       e = lmoe::launch_copy_ids(a->ids_in, a->weights_in, R, a->topk_ids, a->topk_w, s);
       if (e != hipSuccess) return hip_fail(e, "copy_ids");
@@ -300,8 +303,9 @@ FwdCtx fwd_ctx(const latent_moe_plan* p, const lmoe_forward_args* a, hipStream_t
 }
 
 // Stage 1 (and 2 at large T): the latent down-projection and the shared
-// experts' gate/up on x.
-int fwd_front(const FwdCtx& c) {
+// experts' gate/up on x.  route (small T only): the router's top-k of these
+// logits runs in the same launch as the GEMMs.
+int fwd_front(const FwdCtx& c, const lmoe_route_args* route = nullptr) {
   const latent_moe_plan* p = c.p;
   const lmoe_forward_args* a = c.a;
   const hipStream_t s = c.s;
@@ -339,7 +343,14 @@ int fwd_front(const FwdCtx& c) {
     g[1].gated = true;
     g[1].C = hs;
     g[1].ldc = S * Is;
-    if (small) {
+    if (small && route) {
+      // one launch for both GEMMs and the router's top-k, which does not
+      // depend on them
+      e = lmoe::launch_small_dense_with_router(g, S > 0 ? 2 : 1, route->logits, T, p->E, p->k, route->topk_ids,
+                                               route->topk_w, s);
+      if (e != hipSuccess) return hip_fail(e, "down-proj + router");
+      if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event");
+    } else if (small) {
       // one launch for both: they read the same rows of x
       if ((e = lmoe::launch_small_dense(g, S > 0 ? 2 : 1, s)) != hipSuccess) return hip_fail(e, "down-proj");
       if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event");
@@ -607,16 +618,24 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
 int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logits, const lmoe_forward_args* f,
                      void* hip_stream, latent_moe_plan** plan_io) {
   if (!r || !f || !plan_io) return fail(LMOE_EINVAL, "NULL route args, forward args or plan_io");
-  int rc = route_check(r, true);
+  // with a router gate the logits are computed here; without one the route
+  // arguments give them (or the ids), as for latent_moe_route
+  const bool gate = w_router != nullptr;
+  int rc = route_check(r, gate);
   if (rc) return rc;
   if (!f->w_in) return fail(LMOE_EINVAL, "latent_moe_layer needs the projections (w_in != NULL)");
+  const bool ids_mode = !gate && r->ids_in != nullptr;
   latent_moe_plan q{};
-  fill_plan(&q, r, false);
+  fill_plan(&q, r, ids_mode);
   if ((rc = fwd_check(&q, f)) != LMOE_OK) return rc;
   if (r->T > 0) {
-    if (!w_router || !logits) return fail(LMOE_EINVAL, "NULL w_router or logits");
-    if (!aligned16(w_router) || !aligned16(logits))
-      return fail(LMOE_EINVAL, "w_router and logits must be 16-byte aligned");
+    if (gate) {
+      if (!logits) return fail(LMOE_EINVAL, "NULL logits (the gate's output)");
+      if (!aligned16(w_router) || !aligned16(logits))
+        return fail(LMOE_EINVAL, "w_router and logits must be 16-byte aligned");
+    } else if (logits) {
+      return fail(LMOE_EINVAL, "without w_router the route arguments give the logits: logits must be NULL");
+    }
   }
   latent_moe_plan* p = *plan_io;
   const bool fresh = p == nullptr;
@@ -640,6 +659,15 @@ int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logi
     }
     return code;
   };
+  if (!gate) {
+    // given logits: at small T the top-k runs in the down-projection's launch
+    // (it reads neither x nor z), leaving only the permutation before the experts
+    const bool fuse = !ids_mode && c.small;
+    if ((rc = fwd_front(c, fuse ? r : nullptr)) != LMOE_OK) return drop(rc);
+    if ((rc = route_enqueue(p, r, r->logits, s, fuse)) != LMOE_OK) return drop(rc);
+    if ((rc = fwd_back(c)) != LMOE_OK) return drop(rc);
+    return LMOE_OK;
+  }
   if ((rc = fwd_front(c)) != LMOE_OK) return drop(rc);
   // the router gate on the latent z (in the forward workspace): fp32 logits
   const uint16_t* z = reinterpret_cast<const uint16_t*>(static_cast<const char*>(f->workspace) + c.L.z);

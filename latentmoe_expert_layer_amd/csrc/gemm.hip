@@ -16,6 +16,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "router_core.h"
 
 namespace lmoe {
 
@@ -606,11 +607,13 @@ __device__ __forceinline__ void splitk_accumulate(const SplitKPart& P, int64_t a
   }
 }
 
-__global__ __launch_bounds__(256) void splitk_dense_kernel(SplitKArgs g) {
+// Split-K workgroup `blk` of the launch (256 threads; every thread reaches
+// the one barrier).
+__device__ __forceinline__ void splitk_block(const SplitKArgs& g, int blk) {
   __shared__ f32x4 red[3][2][kSkNS][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int pi = (g.nparts > 1 && int(blockIdx.x) >= g.nblk0) ? 1 : 0;
-  const int bb = int(blockIdx.x) - (pi ? g.nblk0 : 0);
+  const int pi = (g.nparts > 1 && blk >= g.nblk0) ? 1 : 0;
+  const int bb = blk - (pi ? g.nblk0 : 0);
   const SplitKPart& P = g.part[pi];
   const int tiles_n = (P.N + 16 * kSkNS - 1) / (16 * kSkNS);
   const int tm = bb / tiles_n, tn = bb % tiles_n;
@@ -666,6 +669,32 @@ __global__ __launch_bounds__(256) void splitk_dense_kernel(SplitKArgs g) {
   }
 }
 
+__global__ __launch_bounds__(256) void splitk_dense_kernel(SplitKArgs g) { splitk_block(g, int(blockIdx.x)); }
+
+// Router top-k of T tokens (4 per workgroup, one per wave) in the same launch
+// as the split-K GEMMs, which do not read its output: workgroups [0, nblk)
+// route, the rest are the split-K grid.
+struct FrontRouter {
+  const float* logits;
+  int64_t T;
+  int E, k;
+  int32_t* ids;
+  float* w;
+  int nblk;
+};
+
+template <int VPL>
+__global__ __launch_bounds__(256) void splitk_router_kernel(SplitKArgs g, FrontRouter r) {
+  if (int(blockIdx.x) < r.nblk) {
+    __shared__ uint64_t cbuf[4][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t t = int64_t(blockIdx.x) * 4 + wv;
+    if (t < r.T) route_token<VPL>(r.logits, t, r.E, r.k, lane, cbuf[wv], r.ids, r.w);
+    return;
+  }
+  splitk_block(g, int(blockIdx.x) - r.nblk);
+}
+
 }  // namespace
 
 hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
@@ -709,8 +738,7 @@ hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t 
   return run_tiled<8, 2, false, true, true>(a, g.max_tiles, s, t0, t1);
 }
 
-hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s) {
-  SplitKArgs a{};
+static int64_t splitk_args(const DenseGemm* parts, int nparts, SplitKArgs& a) {
   a.M = parts[0].M;
   a.nparts = nparts;
   int64_t nblk = 0;
@@ -724,13 +752,35 @@ hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s)
     P.C = d.C;
     P.Cf = d.Cf;
     P.ldc = d.ldc;
-    if (d.Cf && d.gated) return hipErrorInvalidValue;
+    if (d.Cf && d.gated) return -1;
     const int64_t nb = int64_t((d.M + 15) / 16) * ((d.N + 16 * kSkNS - 1) / (16 * kSkNS));
     if (i == 0) a.nblk0 = int(nb);
     nblk += nb;
   }
-  if (nblk <= 0) return hipSuccess;
+  return nblk;
+}
+
+hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s) {
+  SplitKArgs a{};
+  const int64_t nblk = splitk_args(parts, nparts, a);
+  if (nblk < 0) return hipErrorInvalidValue;
+  if (nblk == 0) return hipSuccess;
   splitk_dense_kernel<<<dim3{uint32_t(nblk)}, dim3{256}, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_dense_with_router(const DenseGemm* parts, int nparts, const float* logits, int64_t T,
+                                          int E, int k, int32_t* ids, float* w, hipStream_t s) {
+  SplitKArgs a{};
+  const int64_t nblk = splitk_args(parts, nparts, a);
+  if (nblk < 0 || E > 1024) return hipErrorInvalidValue;
+  FrontRouter r{logits, T, E, k, ids, w, int((T + 3) / 4)};
+  const dim3 grid{uint32_t(nblk + r.nblk)}, block{256};
+  if (grid.x == 0) return hipSuccess;
+  if (E <= 128) splitk_router_kernel<2><<<grid, block, 0, s>>>(a, r);
+  else if (E <= 256) splitk_router_kernel<4><<<grid, block, 0, s>>>(a, r);
+  else if (E <= 512) splitk_router_kernel<8><<<grid, block, 0, s>>>(a, r);
+  else splitk_router_kernel<16><<<grid, block, 0, s>>>(a, r);
   return hipGetLastError();
 }
 

@@ -133,7 +133,11 @@ def _layer_fwd(lm, **kw):
     (dict(logits=None, ids_in=128, weights_in=144, k=1), dict(), 192, 208, 1),
     (dict(logits=None, topk_ids=None), dict(), 192, 208, 1),
     (dict(logits=None), dict(w_in=None, w_out=None), 192, 208, 1),   # no rows mode
-    (dict(logits=None), dict(), None, 208, 1),                  # no gate
+    (dict(logits=None), dict(), None, 208, 1),                  # no gate and no logits
+    (dict(), dict(), None, 208, 1),                             # logits given: no logits output
+    (dict(logits=None), dict(), None, None, 1),                 # neither gate, logits nor ids
+    (dict(), dict(w_in=None, w_out=None), None, None, 1),       # given logits, still no rows mode
+    (dict(E=2000), dict(), None, None, 2),                      # given logits: the router's E limit
     (dict(logits=None), dict(), 192, None, 1),                  # no logits buffer
     (dict(logits=None), dict(), 200, 208, 1),                   # misaligned gate
     (dict(logits=None), dict(l=100), 192, 208, 1),

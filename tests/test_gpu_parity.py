@@ -588,3 +588,59 @@ def test_gate_layer_plan_reuse_and_graph_replay():
         assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), f"replay {rep} differs"
         assert torch.equal(rg.logits, logits1), f"replay {rep}: logits differ"
         del junk
+
+
+GIVEN_LOGITS_LAYERS = [
+    ("decode", None),                                                     # top-k beside the down-projection
+    ("tiny", None),                                                       # E = 16 (2 logits per lane)
+    ("ragged_b", dict(T=77, d=128, l=320, E=40, k=8, S=2, I=192, Is=64)),  # ragged T, one shared-free part
+    ("no_shared", dict(T=150, d=256, l=256, E=4, k=2, S=0, I=128, Is=0)),   # only the down-projection
+    ("mid_ragged", dict(T=1000, d=320, l=192, E=24, k=4, S=2, I=128, Is=64)),  # T > 512: separate launches
+    ("mx_small", dict(T=203, d=192, l=256, E=9, k=3, S=1, I=128, Is=64, mxfp4=True)),
+    ("decode_w4a16", None),
+]
+
+
+@pytest.mark.parametrize("name,dims", GIVEN_LOGITS_LAYERS, ids=[n for n, _ in GIVEN_LOGITS_LAYERS])
+def test_layer_with_given_logits_equals_route_then_forward(name, dims):
+    """latent_moe_layer without a gate (the logits given) equals
+    latent_moe_route + latent_moe_forward bit for bit: routing, permutation,
+    offsets and y; then the oracle bar on y.  Captured in a graph with its
+    plan reused, every replay gives the same y."""
+    cfg = W.CONFIGS[name] if dims is None else W.custom(name, **dims)
+    log(f"layer with given logits {name}: {cfg}")
+    inp = W.make_inputs(cfg)
+    inp_dev = to_device(inp)
+    r_ref, y_ref = run_gpu_layer(inp_dev)
+    mx = cfg.mxfp4
+    w1, w3, w2 = (inp_dev[n + ("q" if mx else "")] for n in ("w1", "w3", "w2"))
+    wts = dict(s1=inp_dev.get("s1"), s3=inp_dev.get("s3"), s2=inp_dev.get("s2"), mxfp4=mx, w4a16=cfg.w4a16,
+               I=cfg.I, w_in=inp_dev["w_in"], w_out=inp_dev["w_out"], ws1=inp_dev.get("ws1"),
+               ws3=inp_dev.get("ws3"), ws2=inp_dev.get("ws2"), norm_w=inp_dev.get("norm_w"), eps=cfg.eps)
+    r, y = lm.layer(inp_dev["x"], None, cfg.k, w1, w3, w2, logits=inp_dev["logits"], **wts)
+    torch.cuda.synchronize()
+    for f in ("topk_ids", "topk_w", "sorted_row", "row_pos", "offsets"):
+        assert torch.equal(getattr(r, f), getattr(r_ref, f)), f
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    check_routing(r, inp["logits"], cfg.k, cfg.E)
+    ref = oracle.run(inp, act_quant=mx and not cfg.w4a16)
+    if mx and not cfg.w4a16:
+        assert_rowwise(y.cpu(), ref["y"])
+    else:
+        assert_parity(y.cpu(), ref["y"])
+
+    y2 = torch.empty_like(y)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        lm.layer(inp_dev["x"], None, cfg.k, w1, w3, w2, logits=inp_dev["logits"], y=y2, workspace=r.keep[0],
+                 routing=r, **wts)
+    for rep in range(3):
+        poison_(r.keep[0])
+        poison_(y2)
+        junk = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y2.view(torch.int16), y_ref.view(torch.int16)), f"replay {rep} differs"
+        del junk
