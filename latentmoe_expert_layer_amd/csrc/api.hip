@@ -346,8 +346,14 @@ int fwd_front(const FwdCtx& c, const lmoe_route_args* route = nullptr) {
     if (small && route) {
       // one launch for both GEMMs and the router's top-k, which does not
       // depend on them
-      e = lmoe::launch_small_dense_with_router(g, S > 0 ? 2 : 1, route->logits, T, p->E, p->k, route->topk_ids,
-                                               route->topk_w, s);
+      lmoe::FrontRoute fr{};
+      fr.logits = route->logits;
+      fr.T = T;
+      fr.E = p->E;
+      fr.k = p->k;
+      fr.ids = route->topk_ids;
+      fr.w = route->topk_w;
+      e = lmoe::launch_small_dense_with_router(g, S > 0 ? 2 : 1, fr, s);
       if (e != hipSuccess) return hip_fail(e, "down-proj + router");
       if ((e = mark(1)) != hipSuccess) return hip_fail(e, "event");
     } else if (small) {

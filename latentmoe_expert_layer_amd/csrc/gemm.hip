@@ -672,27 +672,18 @@ __device__ __forceinline__ void splitk_block(const SplitKArgs& g, int blk) {
 __global__ __launch_bounds__(256) void splitk_dense_kernel(SplitKArgs g) { splitk_block(g, int(blockIdx.x)); }
 
 // Router top-k of T tokens (4 per workgroup, one per wave) in the same launch
-// as the split-K GEMMs, which do not read its output: workgroups [0, nblk)
+// as the split-K GEMMs, which do not read its output: workgroups [0, nrb)
 // route, the rest are the split-K grid.
-struct FrontRouter {
-  const float* logits;
-  int64_t T;
-  int E, k;
-  int32_t* ids;
-  float* w;
-  int nblk;
-};
-
 template <int VPL>
-__global__ __launch_bounds__(256) void splitk_router_kernel(SplitKArgs g, FrontRouter r) {
-  if (int(blockIdx.x) < r.nblk) {
+__global__ __launch_bounds__(256) void splitk_router_kernel(SplitKArgs g, FrontRoute r, int nrb) {
+  if (int(blockIdx.x) < nrb) {
     __shared__ uint64_t cbuf[4][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t t = int64_t(blockIdx.x) * 4 + wv;
     if (t < r.T) route_token<VPL>(r.logits, t, r.E, r.k, lane, cbuf[wv], r.ids, r.w);
     return;
   }
-  splitk_block(g, int(blockIdx.x) - r.nblk);
+  splitk_block(g, int(blockIdx.x) - nrb);
 }
 
 }  // namespace
@@ -769,18 +760,17 @@ hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_small_dense_with_router(const DenseGemm* parts, int nparts, const float* logits, int64_t T,
-                                          int E, int k, int32_t* ids, float* w, hipStream_t s) {
+hipError_t launch_small_dense_with_router(const DenseGemm* parts, int nparts, const FrontRoute& r, hipStream_t s) {
   SplitKArgs a{};
   const int64_t nblk = splitk_args(parts, nparts, a);
-  if (nblk < 0 || E > 1024) return hipErrorInvalidValue;
-  FrontRouter r{logits, T, E, k, ids, w, int((T + 3) / 4)};
-  const dim3 grid{uint32_t(nblk + r.nblk)}, block{256};
+  if (nblk < 0 || r.E > 1024) return hipErrorInvalidValue;
+  const int nrb = int((r.T + 3) / 4);
+  const dim3 grid{uint32_t(nblk + nrb)}, block{256};
   if (grid.x == 0) return hipSuccess;
-  if (E <= 128) splitk_router_kernel<2><<<grid, block, 0, s>>>(a, r);
-  else if (E <= 256) splitk_router_kernel<4><<<grid, block, 0, s>>>(a, r);
-  else if (E <= 512) splitk_router_kernel<8><<<grid, block, 0, s>>>(a, r);
-  else splitk_router_kernel<16><<<grid, block, 0, s>>>(a, r);
+  if (r.E <= 128) splitk_router_kernel<2><<<grid, block, 0, s>>>(a, r, nrb);
+  else if (r.E <= 256) splitk_router_kernel<4><<<grid, block, 0, s>>>(a, r, nrb);
+  else if (r.E <= 512) splitk_router_kernel<8><<<grid, block, 0, s>>>(a, r, nrb);
+  else splitk_router_kernel<16><<<grid, block, 0, s>>>(a, r, nrb);
   return hipGetLastError();
 }
 

@@ -84,8 +84,14 @@ constexpr int kSmallM = 512;
 hipError_t launch_small_dense(const DenseGemm* parts, int nparts, hipStream_t s);
 // The same GEMMs with the router's top-k of T tokens (as launch_router, E <=
 // 1024) in the same launch: the router's workgroups run beside the GEMM's.
-hipError_t launch_small_dense_with_router(const DenseGemm* parts, int nparts, const float* logits, int64_t T,
-                                          int E, int k, int32_t* ids, float* w, hipStream_t s);
+struct FrontRoute {
+  const float* logits;
+  int64_t T;
+  int E, k;
+  int32_t* ids;
+  float* w;
+};
+hipError_t launch_small_dense_with_router(const DenseGemm* parts, int nparts, const FrontRoute& r, hipStream_t s);
 
 // Grouped over experts: for each tile (expert e, rows p in the tile):
 //   C[p, :] = A[row(p)] * B_e^T  (gated: silu(A B_e^T) * (A B3_e^T)),

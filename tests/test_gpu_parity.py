@@ -590,6 +590,29 @@ def test_gate_layer_plan_reuse_and_graph_replay():
         del junk
 
 
+def test_layer_given_logits_on_zeroed_buffers():
+    """The decode shape through latent_moe_layer with the logits given (the
+    top-k in the down-projection's launch), on routing buffers and a route
+    workspace that start zeroed, a fresh plan and then the same plan again:
+    equal to route + forward bit for bit (every routing output is written)."""
+    cfg = W.CONFIGS["decode"]
+    log(f"given logits on zeroed buffers: {cfg}")
+    inp = to_device(W.make_inputs(cfg))
+    r_ref, y_ref = run_gpu_layer(inp)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    z = lambda *shape, dt=torch.int32: torch.zeros(*shape, dtype=dt, device="cuda")
+    routing = lm.Routing(T, E, k, z(T, k), z(T, k, dt=torch.float32), z(T * k), z(T * k), z(E + 1),
+                         z(lm.route_workspace_size(T, E, k), dt=torch.uint8), None, logits=inp["logits"])
+    for call in range(2):   # a fresh plan, then the same plan again
+        r, y = lm.layer(inp["x"], None, k, inp["w1"], inp["w3"], inp["w2"], w_in=inp["w_in"], w_out=inp["w_out"],
+                        ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], norm_w=inp["norm_w"], eps=cfg.eps,
+                        logits=inp["logits"], routing=routing)
+        torch.cuda.synchronize()
+        for f in ("topk_ids", "topk_w", "sorted_row", "row_pos", "offsets"):
+            assert torch.equal(getattr(r, f), getattr(r_ref, f)), f"call {call}: {f}"
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), f"call {call}: y differs"
+
+
 GIVEN_LOGITS_LAYERS = [
     ("decode", None),                                                     # top-k beside the down-projection
     ("tiny", None),                                                       # E = 16 (2 logits per lane)
