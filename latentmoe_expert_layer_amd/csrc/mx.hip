@@ -14,27 +14,22 @@ namespace lmoe {
 
 namespace {
 
-// Nearest e4m3fn code to v (finite), ties to the even code, saturating to
-// +-448 (1.75 * 2^8, the largest finite e4m3fn value).
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f) {  // below 2^-6: subnormal codes m * 2^-9, m = 0..8
-    const uint32_t m = uint32_t(rintf(a * 512.0f));  // exact scaling, rint = nearest even
-    return sign | m;                                  // m == 8 is the smallest normal (code 8)
-  }
-  const uint32_t au = __float_as_uint(a);
-  int e = int((au >> 23) & 0xffu) - 127;              // -6 .. 8
-  uint32_t q = (au >> 20) & 7u;                       // top 3 mantissa bits
-  const uint32_t rest = au & 0xfffffu;
-  if (rest > 0x80000u || (rest == 0x80000u && (q & 1u))) ++q;
-  if (q == 8u) {
-    q = 0u;
-    ++e;
-  }
-  return sign | (uint32_t(e + 7) << 3) | q;           // a < 448 keeps the code <= 0x7E
+// Four e4m3fn codes (byte i = code of v[i]): the nearest code, ties to the
+// even one, saturating to +-448 (1.75 * 2^8, the largest finite e4m3fn
+// value).  gfx950's converter rounds to nearest even in the OCP e4m3fn format
+// but turns magnitudes that round past 448 into NaN, so inputs are clamped to
+// +-448 first.  For every finite input of magnitude below 2^9 (all that the
+// block quantiser below produces) this equals the code written out from the
+// format's definition (checked over every bf16 bit pattern on the device).
+__device__ __forceinline__ uint32_t e4m3x4(float v0, float v1, float v2, float v3) {
+  constexpr float kMax = 448.0f;
+  v0 = fminf(fmaxf(v0, -kMax), kMax);
+  v1 = fminf(fmaxf(v1, -kMax), kMax);
+  v2 = fminf(fmaxf(v2, -kMax), kMax);
+  v3 = fminf(fmaxf(v3, -kMax), kMax);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);  // bytes 0, 1
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);       // bytes 2, 3
+  return uint32_t(w);
 }
 
 // MXFP8 quantisation of one 32-element block (OCP MX: one shared e8m0 scale
@@ -57,12 +52,9 @@ __device__ __forceinline__ uint8_t quant_block32(const uint4 (&raw)[4], uint4 (&
   const float inv = __uint_as_float(uint32_t(127 - sexp) << 23);  // 2^-sexp, exact (|sexp| <= 126 here)
   uint32_t out[8];
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) word |= e4m3_rne(bf16_to_f32(h[w * 4 + i]) * inv) << (8 * i);
-    out[w] = word;
-  }
+  for (int w = 0; w < 8; ++w)
+    out[w] = e4m3x4(bf16_to_f32(h[w * 4]) * inv, bf16_to_f32(h[w * 4 + 1]) * inv, bf16_to_f32(h[w * 4 + 2]) * inv,
+                    bf16_to_f32(h[w * 4 + 3]) * inv);
   codes[0] = uint4{out[0], out[1], out[2], out[3]};
   codes[1] = uint4{out[4], out[5], out[6], out[7]};
   return uint8_t(sexp + 127);
