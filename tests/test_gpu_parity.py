@@ -619,6 +619,12 @@ GIVEN_LOGITS_LAYERS = [
     ("ragged_b", dict(T=77, d=128, l=320, E=40, k=8, S=2, I=192, Is=64)),  # ragged T, one shared-free part
     ("no_shared", dict(T=150, d=256, l=256, E=4, k=2, S=0, I=128, Is=0)),   # only the down-projection
     ("mid_ragged", dict(T=1000, d=320, l=192, E=24, k=4, S=2, I=128, Is=64)),  # T > 512: separate launches
+    # weight-streaming experts: ragged T and three 64-column groups
+    ("skinny_ragged", dict(T=77, d=128, l=256, E=40, k=8, S=2, I=192, Is=64)),
+    # latent 128 (one K chunk), ~19 rows per expert: experts over several 16-row tiles
+    ("skinny_heavy", dict(T=200, d=128, l=128, E=64, k=6, S=1, I=128, Is=64)),
+    # the top-k beside the down-projection at its limit (512 tokens), T*k = 8192 = 32 E rows
+    ("skinny_max", dict(T=512, d=64, l=256, E=256, k=16, S=0, I=64, Is=0)),
     ("mx_small", dict(T=203, d=192, l=256, E=9, k=3, S=1, I=128, Is=64, mxfp4=True)),
     ("decode_w4a16", None),
 ]
