@@ -161,3 +161,16 @@ def test_layer_with_empty_batch_returns_and_reuses_a_plan():
     with pytest.raises(lm.LatentMoeError):                      # dims are checked even when empty
         lm.latent_moe_layer(ra, None, None, _layer_fwd(lm, l=100), plan=plan)
     lm.latent_moe_free(plan)
+
+
+def test_layer_binding_takes_exactly_one_of_gate_and_logits():
+    """lm.layer: the router gate and given logits exclude each other (checked
+    before any device work)."""
+    import torch
+    import latentmoe_expert_layer_amd as lm
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    w = torch.zeros(8, 32, 64, dtype=torch.bfloat16)
+    for w_r, logits in ((None, None), (torch.zeros(8, 64, dtype=torch.bfloat16), torch.zeros(4, 8))):
+        with pytest.raises(ValueError):
+            lm.layer(x, w_r, 2, w, w, w, w_in=torch.zeros(64, 64, dtype=torch.bfloat16),
+                     w_out=torch.zeros(64, 64, dtype=torch.bfloat16), logits=logits)
