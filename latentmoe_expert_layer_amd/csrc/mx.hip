@@ -7,6 +7,8 @@
 //   one e8m0 scale (2^(code-127)) per 32 consecutive K elements.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -137,26 +139,19 @@ constexpr int mx_lds_bytes() {
 // this frees (96 instead of 128 registers per lane) pay for it, and twice as
 // much of the weight stream is in flight per CU.  The same MFMAs in the same
 // K order: bit-identical results.
-template <bool GATED, bool DEEP = false>
-__global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
+// One macro tile: lt = m-tile * tiles_n + n-tile (in the XCD-aware order).
+template <bool GATED, bool DEEP>
+__device__ __forceinline__ void mx_tile(const MxArgs& g, uint32_t lt, uint8_t* lds) {
   constexpr int NTH = 512, BM = DEEP ? kTiledBM : 256, BR = 256, NOUT = GATED ? 128 : 256;
   constexpr int WAVES_N = 4, WM = BM / 2, WN = 64, FM = WM / 32, FN = 2;
   constexpr int A_CH = BM / 64;  // A rows i*64 + tid/8 per thread and stage
   static_assert(BM % 64 == 0 && BM + BR <= NTH, "tile shape");
   constexpr int A_STAGE = BM * kMxARow, B_STAGE = BR * kMxBRow;
   constexpr int STAGE = A_STAGE + B_STAGE + NTH * 4;  // scale words: one slot per thread
-  extern __shared__ uint4 lds_u4[];
-  uint8_t* lds = reinterpret_cast<uint8_t*>(lds_u4);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
-  // the grid covers an upper bound on the tile count: blocks past the
-  // device-side count exit, and the XCD-aware order spans the real blocks
-  // only, so they spread over every XCD
-  const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
-  if (blockIdx.x >= nreal) return;
-  const uint32_t lt = xcd_swizzle(blockIdx.x, nreal);
   const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
   const Tile tl = g.tiles[tm];
   const int row0 = tl.row_start, nrows = tl.nrows, expert = tl.expert;
@@ -422,14 +417,44 @@ __global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
   }
 }
 
-template <bool GATED, bool DEEP>
+// The grid covers an upper bound on the tile count: blocks past the
+// device-side count exit, and the XCD-aware order spans the real tiles only,
+// so they spread over every XCD.  PERSIST: one workgroup per CU takes tiles
+// b, b + grid, ... (block b stays on its XCD, so the order keeps its
+// meaning); a tile's output stores drain while the next tile's loads and
+// MFMAs run.
+template <bool GATED, bool DEEP, bool PERSIST>
+__global__ __launch_bounds__(512, 1) void mx_grouped_kernel(MxArgs g) {
+  extern __shared__ uint4 lds_u4[];
+  uint8_t* lds = reinterpret_cast<uint8_t*>(lds_u4);
+  constexpr int NOUT = GATED ? 128 : 256;
+  const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t((g.N + NOUT - 1) / NOUT);
+  if constexpr (PERSIST) {
+    for (uint32_t b = blockIdx.x; b < nreal; b += gridDim.x) {
+      mx_tile<GATED, DEEP>(g, xcd_swizzle(b, nreal), lds);
+      __syncthreads();  // the next tile's first stage reuses the LDS the epilogue read
+    }
+  } else {
+    if (blockIdx.x >= nreal) return;
+    mx_tile<GATED, DEEP>(g, xcd_swizzle(blockIdx.x, nreal), lds);
+  }
+}
+
+template <bool GATED, bool DEEP, bool PERSIST>
 hipError_t run_mx(const MxArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   constexpr int NOUT = GATED ? 128 : 256;
   constexpr size_t lds = size_t(mx_lds_bytes<GATED, DEEP ? kTiledBM : 256>());
-  auto kern = mx_grouped_kernel<GATED, DEEP>;
+  auto kern = mx_grouped_kernel<GATED, DEEP, PERSIST>;
   if (hipError_t e = allow_dynamic_lds((const void*)kern, int(lds)); e != hipSuccess) return e;
-  const int64_t nblk = max_tiles * ((a.N + NOUT - 1) / NOUT);
+  int64_t nblk = max_tiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
+  if (PERSIST) {
+    int dev = 0, ncu = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+    if (hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev); e != hipSuccess)
+      return e;
+    nblk = std::min<int64_t>(nblk, ncu);  // one workgroup per CU (its LDS and registers allow no more)
+  }
   return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512}, lds, s, a, t0, t1);
 }
 
@@ -464,9 +489,14 @@ hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s, hipEvent_t t0, h
   // routing cuts tiles at kTiledBM rows, within both kernels' reach; the deep
   // pipeline needs an even number (>= 4) of 128-wide K stages
   static_assert(kTiledBM <= 256 && kTiledBM % 64 == 0, "tile table granularity");
+  // FC2 (plain, bf16 output) writes 2 bytes per output against a short K:
+  // in the deep form its stores get the persistent grid, to drain behind the
+  // next tile (the 256-row form has no registers to spare for it)
   if (g.K % 256 == 0 && g.K >= 512)
-    return g.gated ? run_mx<true, true>(a, g.max_tiles, s, t0, t1) : run_mx<false, true>(a, g.max_tiles, s, t0, t1);
-  return g.gated ? run_mx<true, false>(a, g.max_tiles, s, t0, t1) : run_mx<false, false>(a, g.max_tiles, s, t0, t1);
+    return g.gated ? run_mx<true, true, false>(a, g.max_tiles, s, t0, t1)
+                   : run_mx<false, true, true>(a, g.max_tiles, s, t0, t1);
+  return g.gated ? run_mx<true, false, false>(a, g.max_tiles, s, t0, t1)
+                 : run_mx<false, false, false>(a, g.max_tiles, s, t0, t1);
 }
 
 }  // namespace lmoe
