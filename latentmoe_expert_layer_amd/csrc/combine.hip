@@ -262,7 +262,7 @@ hipError_t launch_combine(const uint16_t* Y, const int32_t* row_pos, const float
   LMOE_COMBINE_REG(8, 4, 1)  // 2048
   LMOE_COMBINE_REG(8, 2, 1)  // 1024
   LMOE_COMBINE_REG(8, 1, 1)  // 512
-  LMOE_COMBINE_REG(4, 1, 1)  // 256
+  LMOE_COMBINE_REG(1, 4, 1)  // 256
   LMOE_COMBINE_REG(2, 1, 1)  // 128
   LMOE_COMBINE_REG(1, 1, 1)  // 64
 #undef LMOE_COMBINE_REG
