@@ -118,6 +118,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
     int32_t* __restrict__ counts, int G, int64_t R, int E, int32_t* __restrict__ offsets,
     Tile* __restrict__ tiles_a, int32_t* __restrict__ n_a, Tile* __restrict__ tiles_b, int32_t* __restrict__ n_b) {
   __shared__ int32_t ws[3 * kPermWaves];
+  __shared__ int32_t s_off[kPermMaxExperts + 1], s_ta[kPermMaxExperts + 1], s_tb[kPermMaxExperts + 1];
   constexpr int kMaxPer = kPermMaxExperts / kPermThreads;
   constexpr int kG = 16;  // chunk counts loaded together
   const int tid = threadIdx.x;
@@ -149,6 +150,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
     }
   }
   const Scan3 sc = block_exclusive_scan3<kPermWaves>(run, ws);
+  // each expert's row offset and first entry in both tile tables, in LDS
   int32_t o = sc.x[0], ta = sc.x[1], tb = sc.x[2];
 #pragma unroll
   for (int q = 0; q < kMaxPer; ++q) {
@@ -156,16 +158,41 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
     if (e < e1) {
       const int32_t cnt = tot[q];
       offsets[e] = o;
-      for (int32_t r = 0; r < cnt; r += kSkinnyBM, ++ta) tiles_a[ta] = Tile{e, o + r, min(kSkinnyBM, cnt - r), 0};
-      for (int32_t r = 0; r < cnt; r += kTiledBM, ++tb) tiles_b[tb] = Tile{e, o + r, min(kTiledBM, cnt - r), 0};
+      s_off[e] = o;
+      s_ta[e] = ta;
+      s_tb[e] = tb;
       o += cnt;
+      ta += (cnt + kSkinnyBM - 1) / kSkinnyBM;
+      tb += (cnt + kTiledBM - 1) / kTiledBM;
     }
   }
+  const int32_t na = sc.total[1], nb = sc.total[2];
   if (tid == 0) {
     offsets[E] = int32_t(R);
-    *n_a = sc.total[1];
-    *n_b = sc.total[2];
+    s_off[E] = int32_t(R);
+    s_ta[E] = na;
+    s_tb[E] = nb;
+    *n_a = na;
+    *n_b = nb;
   }
+  __syncthreads();
+  // the tables' entries over the whole workgroup (a heavy expert's many tiles
+  // are not left to one thread): entry i belongs to the last expert whose
+  // first entry is <= i
+  auto fill = [&](Tile* __restrict__ tiles, const int32_t* first, int32_t n, int bm) {
+    for (int32_t i = tid; i < n; i += kPermThreads) {
+      int lo = 0, hi = E;  // first[lo] <= i < first[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (first[mid] <= i) lo = mid;
+        else hi = mid;
+      }
+      const int32_t j = i - first[lo], cnt = s_off[lo + 1] - s_off[lo];
+      tiles[i] = Tile{lo, s_off[lo] + j * bm, min(bm, cnt - j * bm), 0};
+    }
+  };
+  fill(tiles_a, s_ta, na, kSkinnyBM);
+  fill(tiles_b, s_tb, nb, kTiledBM);
 }
 
 template <int NW>
