@@ -13,6 +13,14 @@ namespace lmoe {
 // Expert ids outside [0, E) (invalid input) are clamped so that every write
 // stays inside the caller's buffers; valid ids are unchanged.
 __device__ __forceinline__ int32_t clamp_id(int32_t id, int E) { return min(max(id, 0), E - 1); }
+
+// Workgroup barrier that orders LDS only: the waves' global stores may still
+// be in flight (unlike __syncthreads, which waits for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 // LDS of the one-workgroup permutation: the [E][NW+1] histogram plus the
 // scan scratch.
 inline int64_t permute_lds_bytes(int E, int nw) { return (int64_t(E) * (nw + 1) + 64) * 4; }

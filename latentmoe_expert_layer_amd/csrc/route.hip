@@ -88,6 +88,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 // Chunks are consecutive and each keeps its rows in order, so the result is
 // the same stable permutation.
 constexpr int kPermChunk = 4096;
+// the scan leaves an expert's tile-table entries to the whole workgroup when
+// it has more 16-row tiles than this (up to kPermHeavyMax such experts)
+constexpr int kPermSerialTiles = 64;
+constexpr int kPermHeavyMax = 1024;
 constexpr int64_t kPermOneWgMaxRows = 8192;
 constexpr int kPermMaxExperts = 4096;  // the scan's threads own at most 4 experts each
 
@@ -118,10 +122,15 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
     int32_t* __restrict__ counts, int G, int64_t R, int E, int32_t* __restrict__ offsets,
     Tile* __restrict__ tiles_a, int32_t* __restrict__ n_a, Tile* __restrict__ tiles_b, int32_t* __restrict__ n_b) {
   __shared__ int32_t ws[3 * kPermWaves];
-  __shared__ int32_t s_off[kPermMaxExperts + 1], s_ta[kPermMaxExperts + 1], s_tb[kPermMaxExperts + 1];
+  // experts with more than kPermSerialTiles 16-row tiles, whose tile-table
+  // entries the whole workgroup writes: (expert, row offset, rows, first
+  // entry of each table)
+  __shared__ int32_t s_nheavy;
+  __shared__ int32_t s_heavy[kPermHeavyMax][5];
   constexpr int kMaxPer = kPermMaxExperts / kPermThreads;
   constexpr int kG = 16;  // chunk counts loaded together
   const int tid = threadIdx.x;
+  if (tid == 0) s_nheavy = 0;  // ordered before its use by the scan's barrier
   const int per = (E + kPermThreads - 1) / kPermThreads;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int32_t tot[kMaxPer];
@@ -150,7 +159,6 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
     }
   }
   const Scan3 sc = block_exclusive_scan3<kPermWaves>(run, ws);
-  // each expert's row offset and first entry in both tile tables, in LDS
   int32_t o = sc.x[0], ta = sc.x[1], tb = sc.x[2];
 #pragma unroll
   for (int q = 0; q < kMaxPer; ++q) {
@@ -158,41 +166,40 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
     if (e < e1) {
       const int32_t cnt = tot[q];
       offsets[e] = o;
-      s_off[e] = o;
-      s_ta[e] = ta;
-      s_tb[e] = tb;
+      const int32_t na = (cnt + kSkinnyBM - 1) / kSkinnyBM, nb = (cnt + kTiledBM - 1) / kTiledBM;
+      // a long run of entries (a skewed load) is left to the whole workgroup
+      // below, while the list has room
+      const int h = na > kPermSerialTiles ? atomicAdd(&s_nheavy, 1) : kPermHeavyMax;
+      if (h < kPermHeavyMax) {
+        s_heavy[h][0] = e;
+        s_heavy[h][1] = o;
+        s_heavy[h][2] = cnt;
+        s_heavy[h][3] = ta;
+        s_heavy[h][4] = tb;
+        ta += na;
+        tb += nb;
+      } else {
+        for (int32_t r = 0; r < cnt; r += kSkinnyBM, ++ta) tiles_a[ta] = Tile{e, o + r, min(kSkinnyBM, cnt - r), 0};
+        for (int32_t r = 0; r < cnt; r += kTiledBM, ++tb) tiles_b[tb] = Tile{e, o + r, min(kTiledBM, cnt - r), 0};
+      }
       o += cnt;
-      ta += (cnt + kSkinnyBM - 1) / kSkinnyBM;
-      tb += (cnt + kTiledBM - 1) / kTiledBM;
     }
   }
-  const int32_t na = sc.total[1], nb = sc.total[2];
   if (tid == 0) {
     offsets[E] = int32_t(R);
-    s_off[E] = int32_t(R);
-    s_ta[E] = na;
-    s_tb[E] = nb;
-    *n_a = na;
-    *n_b = nb;
+    *n_a = sc.total[1];
+    *n_b = sc.total[2];
   }
-  __syncthreads();
-  // the tables' entries over the whole workgroup (a heavy expert's many tiles
-  // are not left to one thread): entry i belongs to the last expert whose
-  // first entry is <= i
-  auto fill = [&](Tile* __restrict__ tiles, const int32_t* first, int32_t n, int bm) {
-    for (int32_t i = tid; i < n; i += kPermThreads) {
-      int lo = 0, hi = E;  // first[lo] <= i < first[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (first[mid] <= i) lo = mid;
-        else hi = mid;
-      }
-      const int32_t j = i - first[lo], cnt = s_off[lo + 1] - s_off[lo];
-      tiles[i] = Tile{lo, s_off[lo] + j * bm, min(bm, cnt - j * bm), 0};
-    }
-  };
-  fill(tiles_a, s_ta, na, kSkinnyBM);
-  fill(tiles_b, s_tb, nb, kTiledBM);
+  lds_barrier();  // the heavy list; the stores above need not land first
+  const int nh = min(s_nheavy, kPermHeavyMax);
+  for (int h = 0; h < nh; ++h) {
+    const int e = s_heavy[h][0];
+    const int32_t oe = s_heavy[h][1], cnt = s_heavy[h][2], ta0 = s_heavy[h][3], tb0 = s_heavy[h][4];
+    for (int32_t j = tid; j * kSkinnyBM < cnt; j += kPermThreads)
+      tiles_a[ta0 + j] = Tile{e, oe + j * kSkinnyBM, min(kSkinnyBM, cnt - j * kSkinnyBM), 0};
+    for (int32_t j = tid; j * kTiledBM < cnt; j += kPermThreads)
+      tiles_b[tb0 + j] = Tile{e, oe + j * kTiledBM, min(kTiledBM, cnt - j * kTiledBM), 0};
+  }
 }
 
 template <int NW>
