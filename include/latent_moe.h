@@ -71,7 +71,7 @@ enum { LMOE_OK = 0, LMOE_EINVAL = 1, LMOE_EUNSUPPORTED = 2, LMOE_EHIP = 3 };
  *                        returns LMOE_EUNSUPPORTED and nothing is enqueued. */
 enum { LMOE_WFMT_BF16 = 0, LMOE_WFMT_MXFP4 = 1, LMOE_WFMT_MXFP4_W4A16 = 2 };
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define LMOE_MAX_EXPERTS_LOGITS 1024 /* E in logits mode (router keeps E/64 logits per lane) */
 #define LMOE_MAX_EXPERTS 4096        /* E in ids mode */
 #define LMOE_MAX_TOPK 64             /* k (one lane per selected expert) */
