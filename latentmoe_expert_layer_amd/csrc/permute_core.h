@@ -24,6 +24,9 @@ __device__ __forceinline__ void lds_barrier() {
 // LDS of the one-workgroup permutation: the [E][NW+1] histogram plus the
 // scan scratch.
 inline int64_t permute_lds_bytes(int E, int nw) { return (int64_t(E) * (nw + 1) + 64) * 4; }
+// ... plus, for the mask form of the scatter, one 64-bit lane mask per
+// (wave, expert) in front of it.
+inline int64_t permute_masks_bytes(int E, int nw) { return int64_t(nw) * E * 8; }
 
 // Inclusive wave scan (sum) with DPP: shifts by 1, 2, 4, 8 inside each
 // 16-lane row, then row 0's total into row 1 and row 2's into row 3, then the
@@ -73,11 +76,17 @@ __device__ __forceinline__ Scan3 block_exclusive_scan3(const int32_t (&v)[3], in
 // take consecutive slots in lane order from the wave's running start
 // hist[id * (NW+1) + wave], and the group's lowest lane advances it.  The
 // first kBatch * 64 ids come in registers.
+// MASKS: the lanes with equal expert find each other through the wave's own
+// LDS mask of that expert instead: every lane ORs in its lane bit (OR does
+// not depend on the order), one read gives the group's lanes, and the group's
+// lowest lane clears the mask again.  The same ranks, in far fewer
+// instructions than one ballot per id bit.
 constexpr int kPermBatch = 8;
-template <int NW>
+template <int NW, bool MASKS = false>
 __device__ __forceinline__ void stable_scatter(const int32_t* __restrict__ ids, int64_t R, int E, int64_t r0,
                                                int64_t r1, const int32_t (&first)[kPermBatch], int32_t* hist,
-                                               int32_t* __restrict__ sorted_row, int32_t* __restrict__ row_pos) {
+                                               int32_t* __restrict__ sorted_row, int32_t* __restrict__ row_pos,
+                                               uint64_t* masks = nullptr) {
   constexpr int S = NW + 1;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int nbits = 1;
@@ -99,16 +108,30 @@ __device__ __forceinline__ void stable_scatter(const int32_t* __restrict__ ids, 
       const int64_t r = base_r + lane;
       const bool valid = r < r1;
       const int32_t id = valid ? clamp_id(idv[u], E) : 0;
-      uint64_t peers = ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = (id >> b) & 1;
-        const uint64_t m = ballot(bit);
-        peers &= bit ? m : ~m;
+      uint64_t peers;
+      if constexpr (MASKS) {
+        uint64_t* mk = masks + int64_t(wid) * E + id;  // this wave's mask of the lane's expert
+        if (valid) atomicOr(reinterpret_cast<unsigned long long*>(mk), 1ull << lane);
+        // the wave's LDS accesses complete in order; this only keeps the
+        // compiler from moving the read above the ORs
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        peers = valid ? *mk : 0ull;
+      } else {
+        peers = ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+          const bool bit = (id >> b) & 1;
+          const uint64_t m = ballot(bit);
+          peers &= bit ? m : ~m;
+        }
       }
       int32_t base = 0;
       if (valid) base = hist[id * S + wid];
       const int rank = __popcll(peers & below);
-      if (valid && rank == 0) hist[id * S + wid] = base + __popcll(peers);
+      if (valid && rank == 0) {
+        hist[id * S + wid] = base + __popcll(peers);
+        if constexpr (MASKS) masks[int64_t(wid) * E + id] = 0ull;  // after every lane's read above
+      }
       if (valid) {
         const int32_t p = base + rank;
         sorted_row[p] = int32_t(r);
@@ -152,8 +175,9 @@ __device__ __forceinline__ void wave_histogram(const int32_t* __restrict__ ids, 
 // Rows keep their order within an expert (stable), so the result is unique.
 // A wave's first batch of ids (64 * kBatch rows) stays in registers between
 // (1) and (3).
-// lds: permute_lds_bytes(E, NW) bytes.
-template <int NW, int NTHREADS>
+// lds: permute_lds_bytes(E, NW) bytes (MASKS: permute_masks_bytes(E, NW) more,
+// 8-byte aligned).
+template <int NW, int NTHREADS, bool MASKS = false>
 __device__ __forceinline__ void permute_block(const int32_t* __restrict__ ids, int64_t R, int E,
                                               int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_row,
                                               int32_t* __restrict__ row_pos, Tile* __restrict__ tiles_a,
@@ -161,10 +185,13 @@ __device__ __forceinline__ void permute_block(const int32_t* __restrict__ ids, i
                                               int32_t* __restrict__ n_b, int32_t* lds) {
   static_assert(NW <= NTHREADS / 64, "the row-splitting waves belong to the block");
   constexpr int S = NW + 1;
-  int32_t* hist = lds;                        // [E][S]
-  int32_t* ws = hist + int64_t(E) * S;        // [3 * NTHREADS / 64]
+  uint64_t* masks = reinterpret_cast<uint64_t*>(lds);                      // MASKS: [NW][E]
+  int32_t* hist = lds + (MASKS ? int64_t(NW) * E * 2 : 0);                 // [E][S]
+  int32_t* ws = hist + int64_t(E) * S;                                      // [3 * NTHREADS / 64]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 
+  if constexpr (MASKS)
+    for (int i = tid; i < NW * E; i += NTHREADS) masks[i] = 0ull;
   for (int i = tid; i < E * S; i += NTHREADS) hist[i] = 0;
   __syncthreads();
 
@@ -212,7 +239,7 @@ __device__ __forceinline__ void permute_block(const int32_t* __restrict__ ids, i
   __syncthreads();
 
   // (3) stable scatter
-  if (wid < NW) stable_scatter<NW>(ids, R, E, r0, r1, first, hist, sorted_row, row_pos);
+  if (wid < NW) stable_scatter<NW, MASKS>(ids, R, E, r0, r1, first, hist, sorted_row, row_pos, masks);
 }
 
 }  // namespace lmoe

@@ -64,13 +64,14 @@ int permute_waves(int E) {
 }
 
 // Small batches: one 1024-thread workgroup (permute_block).
-template <int NW>
+template <int NW, bool MASKS = false>
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t* __restrict__ ids, int64_t R, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_row, int32_t* __restrict__ row_pos, Tile* __restrict__ tiles_a,
     int32_t* __restrict__ n_a, Tile* __restrict__ tiles_b, int32_t* __restrict__ n_b) {
-  extern __shared__ int32_t lds[];
-  permute_block<NW, kPermThreads>(ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b, lds);
+  extern __shared__ uint64_t lds64[];
+  permute_block<NW, kPermThreads, MASKS>(ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b,
+                                         reinterpret_cast<int32_t*>(lds64));
 }
 
 // -------------------------------------------------- permute, large batches ---
@@ -242,6 +243,15 @@ static hipError_t launch_permute_nw(const int32_t* ids, int64_t R, int E, int32_
   if (hipError_t e = allow_dynamic_lds((const void*)permute_scatter_kernel<NW>, kPermLdsBudget); e != hipSuccess)
     return e;
   if (R <= kPermOneWgMaxRows) {
+    // the mask form of the scatter (8 row-splitting waves) where its masks fit
+    const int64_t mlds = permute_masks_bytes(E, 8) + permute_lds_bytes(E, 8);
+    if (mlds <= kPermLdsBudget) {
+      if (hipError_t e = allow_dynamic_lds((const void*)permute_kernel<8, true>, kPermLdsBudget); e != hipSuccess)
+        return e;
+      permute_kernel<8, true><<<dim3(1), dim3(kPermThreads), size_t(mlds), s>>>(ids, R, E, offsets, sorted_row,
+                                                                                  row_pos, tiles_a, n_a, tiles_b, n_b);
+      return hipGetLastError();
+    }
     permute_kernel<NW><<<dim3(1), dim3(kPermThreads), size_t(permute_lds_bytes(E, NW)), s>>>(
         ids, R, E, offsets, sorted_row, row_pos, tiles_a, n_a, tiles_b, n_b);
     return hipGetLastError();
