@@ -203,14 +203,17 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
   }
 }
 
-template <int NW>
+template <int NW, bool MASKS = false>
 __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t R, int E, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_row, int32_t* __restrict__ row_pos) {
   constexpr int S = NW + 1;
-  extern __shared__ int32_t lds[];  // [E][S]
-  int32_t* hist = lds;
+  extern __shared__ uint64_t lds64[];  // MASKS: [NW][E] lane masks, then [E][S]
+  uint64_t* masks = lds64;
+  int32_t* hist = reinterpret_cast<int32_t*>(lds64 + (MASKS ? int64_t(NW) * E : 0));
   const int tid = threadIdx.x, wid = tid >> 6;
+  if constexpr (MASKS)
+    for (int i = tid; i < NW * E; i += kPermThreads) masks[i] = 0ull;
   for (int i = tid; i < E * S; i += kPermThreads) hist[i] = 0;
   __syncthreads();
   constexpr int64_t kWaveRows = kPermChunk / NW;
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
     }
   }
   __syncthreads();
-  if (wid < NW) stable_scatter<NW>(ids, R, E, r0, r1, first, hist, sorted_row, row_pos);
+  if (wid < NW) stable_scatter<NW, MASKS>(ids, R, E, r0, r1, first, hist, sorted_row, row_pos, masks);
 }
 
 template <int NW>
@@ -264,6 +267,13 @@ static hipError_t launch_permute_nw(const int32_t* ids, int64_t R, int E, int32_
   permute_scan_kernel<<<dim3(1), dim3(kPermThreads), 0, s>>>(scratch, int(G), R, E, offsets, tiles_a, n_a, tiles_b,
                                                              n_b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t mlds = permute_masks_bytes(E, 8) + permute_lds_bytes(E, 8);
+  if (mlds <= kPermLdsBudget) {  // the mask form of the scatter where its masks fit
+    if ((e = allow_dynamic_lds((const void*)permute_scatter_kernel<8, true>, kPermLdsBudget)) != hipSuccess) return e;
+    permute_scatter_kernel<8, true><<<dim3(uint32_t(G)), dim3(kPermThreads), size_t(mlds), s>>>(
+        ids, R, E, scratch, offsets, sorted_row, row_pos);
+    return hipGetLastError();
+  }
   permute_scatter_kernel<NW><<<dim3(uint32_t(G)), dim3(kPermThreads), size_t(permute_lds_bytes(E, NW)), s>>>(
       ids, R, E, scratch, offsets, sorted_row, row_pos);
   return hipGetLastError();
