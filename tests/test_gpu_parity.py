@@ -120,10 +120,12 @@ def test_route_threshold_paths(T, E, k):
 
 
 # 8192 rows and below: one workgroup; above: per-chunk counts, scan, scatter
-# over 4096-row chunks (ragged last chunk, 4096 experts with 8-wave histograms)
+# over 4096-row chunks (ragged last chunk, 4096 experts with 8-wave histograms); the
+# scatter's lane-mask form holds up to E = 1533, the ballot form above it
 @pytest.mark.parametrize("R,E,heavy", [(16384, 56, False), (5000, 4096, False), (777, 13, True), (64, 1, False),
                                        (8192, 896, False), (8193, 896, False), (12289, 3, True), (20000, 4096, False),
-                                       (262144, 896, False)])
+                                       (262144, 896, False), (3000, 1533, False), (3000, 1534, True),
+                                       (9000, 1533, True), (9000, 1534, False)])
 def test_permute_ids_mode(R, E, heavy):
     log(f"permute ids R={R} E={E} heavy={heavy}")
     ids = W.zipf_ids(0, "ids", R, E, 1.1).view(R, 1)
