@@ -48,7 +48,8 @@ class _Args(ctypes.Structure):
         ("row_pos", ctypes.c_void_p), ("n_eval", ctypes.c_int64),
         ("eval_tokens", ctypes.c_void_p), ("y", ctypes.c_void_p), ("z", ctypes.c_void_p),
         ("hs", ctypes.c_void_p), ("rhat", ctypes.c_void_p), ("H", ctypes.c_void_p),
-        ("Y", ctypes.c_void_p),
+        ("Y", ctypes.c_void_p), ("korder", ctypes.c_int32), ("zq", ctypes.c_void_p),
+        ("zqs", ctypes.c_void_p), ("hq", ctypes.c_void_p), ("hqs", ctypes.c_void_p),
     ]
 
 
@@ -64,7 +65,7 @@ def lib():
             L.lmoe_oracle_route.restype = None
             L.lmoe_oracle_permute.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-            L.lmoe_oracle_permute.restype = None
+            L.lmoe_oracle_permute.restype = ctypes.c_int
             L.lmoe_oracle_router_logits.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -83,6 +84,8 @@ def lib():
             L.lmoe_oracle_mxfp8.restype = None
             L.lmoe_oracle_num_threads.argtypes = []
             L.lmoe_oracle_num_threads.restype = ctypes.c_int
+            L.lmoe_oracle_set_num_threads.argtypes = [ctypes.c_int]
+            L.lmoe_oracle_set_num_threads.restype = None
             _lib = L
     return _lib
 
@@ -137,6 +140,11 @@ def num_threads() -> int:
     return lib().lmoe_oracle_num_threads()
 
 
+def set_num_threads(n: int) -> None:
+    """Sets the OpenMP threads of the oracle's later parallel loops."""
+    lib().lmoe_oracle_set_num_threads(int(n))
+
+
 # ------------------------------------------------------------- layer steps
 def route(logits, k: int):
     """Top-k ids [T,k] int32 and softmax weights [T,k] float32."""
@@ -177,17 +185,26 @@ def permute(ids, E: int):
     offsets = torch.empty(E + 1, dtype=torch.int32)
     sorted_row = torch.empty(R, dtype=torch.int32)
     row_pos = torch.empty(R, dtype=torch.int32)
-    lib().lmoe_oracle_permute(R, E, _ptr(ids), _ptr(offsets), _ptr(sorted_row), _ptr(row_pos))
+    if R and (int(ids.min()) < 0 or int(ids.max()) >= E):
+        raise ValueError(f"expert ids outside [0, {E})")
+    if lib().lmoe_oracle_permute(R, E, _ptr(ids), _ptr(offsets), _ptr(sorted_row), _ptr(row_pos)) != 0:
+        raise ValueError(f"expert ids outside [0, {E})")
     return offsets, sorted_row, row_pos
 
 
 def layer(inp: dict, ids, w, row_pos=None, eval_tokens=None, intermediates=False,
-          act_quant=True, eps=None):
+          act_quant=True, eps=None, korder=0):
     """Evaluate the layer for ``inp`` (a ``workloads.make_inputs`` dict) given the
     routing (ids, w).  Returns {"y": ..., and the intermediates if asked}.
 
-    eval_tokens: optional 1-D list of token indices; then y is [len, width] and
-    no intermediates are produced.
+    eval_tokens: optional 1-D list of token indices; then y is [len, width].
+    intermediates: also return z, hs, rhat (token rows), H and Y (bf16) and,
+      for MXFP4 w4a8, the MXFP8 codes/scales of FC1's input (zq, zqs) and of
+      FC2's input (hq, hqs).  With all tokens, H/Y/hq/hqs rows are in sorted
+      order (row_pos needed); with eval_tokens, row i*k + j of them is slot j
+      of eval_tokens[i].
+    korder: 0 = every K reduction in ascending order (the oracle), 1 =
+      descending (a second valid fp32 order, for measuring tolerances).
     """
     cfg = inp["cfg"]
     keep = []
@@ -211,6 +228,7 @@ def layer(inp: dict, ids, w, row_pos=None, eval_tokens=None, intermediates=False
     a.mxfp4 = int(cfg.mxfp4)
     a.act_quant = int(bool(act_quant))
     a.eps = cfg.eps if eps is None else eps
+    a.korder = int(korder)
     a.x = P("x", torch.bfloat16)
     a.w_in, a.w_out = P("w_in", torch.bfloat16), P("w_out", torch.bfloat16)
     a.norm_w = P("norm_w", torch.bfloat16)
@@ -223,29 +241,41 @@ def layer(inp: dict, ids, w, row_pos=None, eval_tokens=None, intermediates=False
     a.ids, a.wts = _ptr(ids), _ptr(w)
     width = cfg.l if cfg.rows_mode else cfg.d
     out = {}
-    if eval_tokens is not None:
+    sampled = eval_tokens is not None
+    if sampled:
         ev = torch.as_tensor(eval_tokens, dtype=torch.int64).contiguous()
         keep.append(ev)
         a.n_eval, a.eval_tokens = ev.numel(), _ptr(ev)
-        y = torch.empty(ev.numel(), width, dtype=torch.bfloat16)
+        nt = ev.numel()
     else:
-        y = torch.empty(cfg.T, width, dtype=torch.bfloat16)
-        if intermediates:
-            R = cfg.T * cfg.k
-            if not cfg.rows_mode:
-                out["z"] = torch.empty(cfg.T, cfg.l, dtype=torch.bfloat16)
-                out["rhat"] = torch.empty(cfg.T, cfg.l, dtype=torch.bfloat16)
-                out["hs"] = torch.empty(cfg.T, cfg.S * cfg.Is, dtype=torch.bfloat16)
-            if row_pos is not None:
-                rp = _cpu(row_pos, torch.int32)
-                keep.append(rp)
-                a.row_pos = _ptr(rp)
-                out["H"] = torch.empty(R, cfg.I, dtype=torch.bfloat16)
-                out["Y"] = torch.empty(R, cfg.l, dtype=torch.bfloat16)
-            for n in ("z", "rhat", "hs", "H", "Y"):
-                if n in out:
-                    setattr(a, n, _ptr(out[n]))
-    a.y = _ptr(y)
+        nt = cfg.T
+    y = torch.empty(nt, width, dtype=torch.bfloat16)
+    if intermediates:
+        nr = nt * cfg.k
+        have_rows = sampled or row_pos is not None
+        if not sampled and row_pos is not None:
+            rp = _cpu(row_pos, torch.int32)
+            keep.append(rp)
+            a.row_pos = _ptr(rp)
+        out["z"] = torch.empty(nt, cfg.l, dtype=torch.bfloat16)
+        if not cfg.rows_mode:
+            out["rhat"] = torch.empty(nt, cfg.l, dtype=torch.bfloat16)
+            out["hs"] = torch.empty(nt, cfg.S * cfg.Is, dtype=torch.bfloat16)
+        if have_rows:
+            out["H"] = torch.empty(nr, cfg.I, dtype=torch.bfloat16)
+            out["Y"] = torch.empty(nr, cfg.l, dtype=torch.bfloat16)
+        for n in ("z", "rhat", "hs", "H", "Y"):
+            if n in out:
+                setattr(a, n, _ptr(out[n].view(torch.int16)))
+        if cfg.mxfp4 and act_quant:
+            out["zq"] = torch.empty(nt, cfg.l, dtype=torch.uint8)
+            out["zqs"] = torch.empty(nt, cfg.l // 32, dtype=torch.uint8)
+            a.zq, a.zqs = _ptr(out["zq"]), _ptr(out["zqs"])
+            if have_rows:
+                out["hq"] = torch.empty(nr, cfg.I, dtype=torch.uint8)
+                out["hqs"] = torch.empty(nr, cfg.I // 32, dtype=torch.uint8)
+                a.hq, a.hqs = _ptr(out["hq"]), _ptr(out["hqs"])
+    a.y = _ptr(y.view(torch.int16))
     rc = lib().lmoe_oracle_layer(ctypes.byref(a))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
@@ -253,7 +283,7 @@ def layer(inp: dict, ids, w, row_pos=None, eval_tokens=None, intermediates=False
     return out
 
 
-def run(inp: dict, eval_tokens=None, intermediates=False, act_quant=True):
+def run(inp: dict, eval_tokens=None, intermediates=False, act_quant=True, korder=0):
     """Route (or take the given ids) and evaluate the whole layer."""
     cfg = inp["cfg"]
     logits = None
@@ -267,7 +297,7 @@ def run(inp: dict, eval_tokens=None, intermediates=False, act_quant=True):
         ids, w = route(inp["logits"], cfg.k)
     offsets, sorted_row, row_pos = permute(ids, cfg.E)
     out = layer(inp, ids, w, row_pos=row_pos, eval_tokens=eval_tokens,
-                intermediates=intermediates, act_quant=act_quant)
+                intermediates=intermediates, act_quant=act_quant, korder=korder)
     out.update(ids=ids, w=w, offsets=offsets, sorted_row=sorted_row, row_pos=row_pos)
     if logits is not None:
         out["logits"] = logits

@@ -95,11 +95,12 @@ float e4m3_value(unsigned code) {
   return s ? -mag : mag;
 }
 
-// Nearest e4m3fn code to v (ties to the even code), saturating to +-448.
-// Written as a search over all finite codes: slow, but its correctness can be
-// read off directly.
+// Nearest e4m3fn code to v (ties to the even code), saturating to +-448;
+// NaN gives the NaN code S.1111.111.  Written as a search over all finite
+// codes: slow, but its correctness can be read off directly.
 unsigned e4m3_encode(float v) {
   unsigned sign = std::signbit(v) ? 0x80u : 0u;
+  if (std::isnan(v)) return sign | 0x7Fu;
   float a = std::fabs(v);
   if (a >= 448.0f) return sign | 0x7Eu;
   unsigned best = 0;
@@ -117,8 +118,21 @@ unsigned e4m3_encode(float v) {
 // MXFP8 (e4m3fn) quantise-dequantise of one 32-element block, per OCP MX:
 // shared exponent = floor(log2(amax)) - 8 (8 = exponent of e4m3's largest
 // normal), clamped to e8m0's range; elements = nearest e4m3 of v / 2^exp.
-// An all-zero block gets scale code 0 and zero elements.
+// An all-zero block gets scale code 0 and zero elements.  A block holding a
+// NaN or an infinity (e4m3fn has no infinity) becomes a NaN block: scale code
+// 255 (e8m0's NaN) and every element code the e4m3fn NaN 0x7F, so all 32
+// values dequantise to NaN.
 void mxfp8_block(const float* v, float* out, uint8_t* codes, uint8_t* scale_code) {
+  bool finite = true;
+  for (int i = 0; i < 32; ++i) finite = finite && std::isfinite(v[i]);
+  if (!finite) {
+    if (scale_code) *scale_code = 255;
+    for (int i = 0; i < 32; ++i) {
+      if (codes) codes[i] = 0x7F;
+      out[i] = NAN;
+    }
+    return;
+  }
   float amax = 0.0f;
   for (int i = 0; i < 32; ++i) amax = std::max(amax, std::fabs(v[i]));
   int sexp;
@@ -140,10 +154,16 @@ void mxfp8_block(const float* v, float* out, uint8_t* codes, uint8_t* scale_code
 
 float silu(float g) { return g / (1.0f + std::exp(-g)); }
 
-// fp32 dot product in ascending index order.
-float dot(const float* a, const float* b, int64_t n) {
+// fp32 dot product in ascending index order, or (rev) in descending order.
+// Both are valid fp32 evaluations of the same sum; the reversed order exists
+// to measure how far two valid orders land apart.
+float dot(const float* a, const float* b, int64_t n, bool rev = false) {
   float acc = 0.0f;
-  for (int64_t i = 0; i < n; ++i) acc += a[i] * b[i];
+  if (rev) {
+    for (int64_t i = n - 1; i >= 0; --i) acc += a[i] * b[i];
+  } else {
+    for (int64_t i = 0; i < n; ++i) acc += a[i] * b[i];
+  }
   return acc;
 }
 
@@ -158,19 +178,31 @@ void weight_row(const void* w, const uint8_t* s, bool mxfp4, int64_t row, int64_
     bf16_row(static_cast<const uint16_t*>(w) + row * K, out, K);
     return;
   }
+  // the 16 e2m1 values, each from e2m1_value (the products below are the
+  // same ones e2m1_value(c) * e8m0_value(scale) gives element by element)
+  static const std::vector<float> table = [] {
+    std::vector<float> t(16);
+    for (unsigned c = 0; c < 16; ++c) t[c] = e2m1_value(c);
+    return t;
+  }();
   const uint8_t* codes = static_cast<const uint8_t*>(w) + row * (K / 2);
   const uint8_t* sc = s + row * (K / 32);
-  for (int64_t i = 0; i < K; ++i) {
-    uint8_t b = codes[i / 2];
-    unsigned c = (i % 2 == 0) ? (b & 0x0Fu) : (b >> 4);
-    out[i] = e2m1_value(c) * e8m0_value(sc[i / 32]);
+  for (int64_t b = 0; b < K; b += 32) {
+    const float scale = e8m0_value(sc[b / 32]);
+    for (int64_t i = b; i < b + 32; ++i) {
+      uint8_t byte = codes[i / 2];
+      unsigned c = (i % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4);
+      out[i] = table[c] * scale;
+    }
   }
 }
 
-void mxfp8_row(float* v, int64_t K) {
+// MXFP8 quantise-dequantise of a row in place; codes [K] and scales [K/32]
+// receive the encoding when not NULL.
+void mxfp8_row(float* v, int64_t K, uint8_t* codes = nullptr, uint8_t* scales = nullptr) {
   float tmp[32];
   for (int64_t b = 0; b < K; b += 32) {
-    mxfp8_block(v + b, tmp, nullptr, nullptr);
+    mxfp8_block(v + b, tmp, codes ? codes + b : nullptr, scales ? scales + b / 32 : nullptr);
     std::memcpy(v + b, tmp, sizeof tmp);
   }
 }
@@ -187,6 +219,8 @@ float lmoe_oracle_e4m3_value(unsigned code) { return e4m3_value(code & 255u); }
 unsigned lmoe_oracle_e4m3_encode(float v) { return e4m3_encode(v); }
 uint16_t lmoe_oracle_to_bf16(float v) { return to_bf16(v); }
 int lmoe_oracle_num_threads(void) { return omp_get_max_threads(); }
+// Threads of the oracle's later parallel loops (called from the caller's thread).
+void lmoe_oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 // MXFP8-quantise n (multiple of 32) floats: dequantised values, codes, scales.
 void lmoe_oracle_mxfp8(const float* v, int64_t n, float* deq, uint8_t* codes, uint8_t* scales) {
@@ -265,8 +299,11 @@ void lmoe_oracle_router_logits(int64_t T, int32_t d, int32_t l, int32_t E, const
 // offsets[e] = number of rows with expert < e (E+1 entries);
 // sorted_row[p] = r (p-th row in expert-major, row-ascending order);
 // row_pos[r] = p (the inverse).
-void lmoe_oracle_permute(int64_t R, int32_t E, const int32_t* ids, int32_t* offsets,
-                         int32_t* sorted_row, int32_t* row_pos) {
+// Returns 0, or 1 (nothing written) if an id lies outside [0, E).
+int lmoe_oracle_permute(int64_t R, int32_t E, const int32_t* ids, int32_t* offsets,
+                        int32_t* sorted_row, int32_t* row_pos) {
+  for (int64_t r = 0; r < R; ++r)
+    if (ids[r] < 0 || ids[r] >= E) return 1;
   std::vector<int64_t> count(E, 0);
   for (int64_t r = 0; r < R; ++r) count[ids[r]] += 1;
   offsets[0] = 0;
@@ -277,6 +314,7 @@ void lmoe_oracle_permute(int64_t R, int32_t E, const int32_t* ids, int32_t* offs
     sorted_row[p] = int32_t(r);
     row_pos[r] = int32_t(p);
   }
+  return 0;
 }
 
 // -------------------------------------------------------------------- layer
@@ -305,11 +343,20 @@ struct lmoe_oracle_args {
   int64_t n_eval;          // number of tokens to evaluate
   const int64_t* eval_tokens;  // which tokens; NULL = all T (then n_eval is ignored)
   uint16_t* y;             // [n_eval or T, d] bf16; rows mode: [.., l]
-  uint16_t* z;             // optional [T,l]      (only when eval_tokens == NULL)
-  uint16_t* hs;            // optional [T,S*Is]
-  uint16_t* rhat;          // optional [T,l]
-  uint16_t* H;             // optional [T*k,I] in sorted order (needs row_pos)
-  uint16_t* Y;             // optional [T*k,l] in sorted order (needs row_pos)
+  // Optional intermediates.  All tokens (eval_tokens == NULL): z, hs, rhat
+  // and zq/zqs by token, H, Y and hq/hqs by sorted position (needs row_pos).
+  // Sampled tokens: row i of z, hs, rhat, zq, zqs belongs to eval_tokens[i],
+  // and row i*k + j of H, Y, hq, hqs to its slot j.
+  uint16_t* z;             // [.., l]     latent (rows mode: the given rows)
+  uint16_t* hs;            // [.., S*Is]  shared experts' SwiGLU output
+  uint16_t* rhat;          // [.., l]     combined routed latent after the norm
+  uint16_t* H;             // [.., I]     routed SwiGLU output (bf16, before any requantisation)
+  uint16_t* Y;             // [.., l]     routed expert output
+  int32_t korder;          // 0: every K reduction in ascending order; 1: descending
+  uint8_t* zq;             // w4a8: MXFP8 codes [.., l] and e8m0 scales [.., l/32] of FC1's input
+  uint8_t* zqs;
+  uint8_t* hq;             // w4a8: MXFP8 codes [.., I] and scales [.., I/32] of FC2's input
+  uint8_t* hqs;
 };
 
 // One token of the LatentMoE layer ([vLLM-K3] section 1 dataflow):
@@ -323,10 +370,13 @@ struct lmoe_oracle_args {
 //  y    = bf16(rhat W_out^T + hs Ws2^T)        up-projection plus shared output
 // Rows mode (expert-parallel share, no projections, k = 1):
 //  y[r] = bf16(w[r] * Y_r) with z = x.
-static void one_token(const lmoe_oracle_args& a, int64_t t, uint16_t* y_row) {
+// oi: the row of the token-indexed intermediates (t, or the index into
+// eval_tokens); sampled: H/Y rows go to oi*k + j instead of row_pos[r].
+static void one_token(const lmoe_oracle_args& a, int64_t t, int64_t oi, bool sampled, uint16_t* y_row) {
   const bool rows = (a.w_in == nullptr);
   const int64_t d = a.d, l = a.l, I = a.I, Is = a.Is;
   const bool aq = a.mxfp4 && a.act_quant;
+  const bool rev = a.korder != 0;
   std::vector<float> xv(rows ? l : d), z(l), wrow(std::max<int64_t>(std::max(d, l), std::max(I, Is)));
 
   // latent down-projection
@@ -336,32 +386,35 @@ static void one_token(const lmoe_oracle_args& a, int64_t t, uint16_t* y_row) {
     bf16_row(a.x + t * d, xv.data(), d);
     for (int64_t i = 0; i < l; ++i) {
       bf16_row(a.w_in + i * d, wrow.data(), d);
-      z[i] = bf16_round(dot(xv.data(), wrow.data(), d));
+      z[i] = bf16_round(dot(xv.data(), wrow.data(), d, rev));
     }
-    if (a.z) for (int64_t i = 0; i < l; ++i) a.z[t * l + i] = to_bf16(z[i]);
   }
+  if (a.z) for (int64_t i = 0; i < l; ++i) a.z[oi * l + i] = to_bf16(z[i]);
 
   // routed experts in the latent, then the weighted combine
   std::vector<float> zin(z), h(I), hin(I), yv(l), c(l, 0.0f);
-  if (aq) mxfp8_row(zin.data(), l);
+  if (aq) mxfp8_row(zin.data(), l, a.zq ? a.zq + oi * l : nullptr, a.zqs ? a.zqs + oi * (l / 32) : nullptr);
   for (int32_t j = 0; j < a.k; ++j) {
     const int64_t r = t * a.k + j;
     const int64_t e = a.ids[r];
     for (int64_t n = 0; n < I; ++n) {
       weight_row(a.w1, a.s1, a.mxfp4, e * I + n, l, wrow.data());
-      float g = dot(zin.data(), wrow.data(), l);
+      float g = dot(zin.data(), wrow.data(), l, rev);
       weight_row(a.w3, a.s3, a.mxfp4, e * I + n, l, wrow.data());
-      float u = dot(zin.data(), wrow.data(), l);
+      float u = dot(zin.data(), wrow.data(), l, rev);
       h[n] = bf16_round(silu(g) * u);
     }
+    // where this slot's H and Y rows are stored
+    const int64_t p = sampled ? oi * a.k + j : (a.row_pos ? int64_t(a.row_pos[r]) : -1);
     hin = h;
-    if (aq) mxfp8_row(hin.data(), I);
+    if (aq)
+      mxfp8_row(hin.data(), I, (a.hq && p >= 0) ? a.hq + p * I : nullptr,
+                (a.hqs && p >= 0) ? a.hqs + p * (I / 32) : nullptr);
     for (int64_t n = 0; n < l; ++n) {
       weight_row(a.w2, a.s2, a.mxfp4, e * l + n, I, wrow.data());
-      yv[n] = bf16_round(dot(hin.data(), wrow.data(), I));
+      yv[n] = bf16_round(dot(hin.data(), wrow.data(), I, rev));
     }
-    if (a.row_pos) {
-      const int64_t p = a.row_pos[r];
+    if (p >= 0) {
       if (a.H) for (int64_t n = 0; n < I; ++n) a.H[p * I + n] = to_bf16(h[n]);
       if (a.Y) for (int64_t n = 0; n < l; ++n) a.Y[p * l + n] = to_bf16(yv[n]);
     }
@@ -377,37 +430,45 @@ static void one_token(const lmoe_oracle_args& a, int64_t t, uint16_t* y_row) {
   std::vector<float> rh(l);
   if (a.norm_w) {
     float ss = 0.0f;
-    for (int64_t n = 0; n < l; ++n) ss += c[n] * c[n];
+    if (rev) {
+      for (int64_t n = l - 1; n >= 0; --n) ss += c[n] * c[n];
+    } else {
+      for (int64_t n = 0; n < l; ++n) ss += c[n] * c[n];
+    }
     const float inv = 1.0f / std::sqrt(ss / float(l) + a.eps);
     for (int64_t n = 0; n < l; ++n) rh[n] = bf16_round(c[n] * inv * from_bf16(a.norm_w[n]));
   } else {
     for (int64_t n = 0; n < l; ++n) rh[n] = bf16_round(c[n]);
   }
-  if (a.rhat) for (int64_t n = 0; n < l; ++n) a.rhat[t * l + n] = to_bf16(rh[n]);
+  if (a.rhat) for (int64_t n = 0; n < l; ++n) a.rhat[oi * l + n] = to_bf16(rh[n]);
 
   // shared experts on the hidden state (intermediates of all S concatenated)
   std::vector<float> hsv(int64_t(a.S) * Is);
   for (int32_t s = 0; s < a.S; ++s) {
     for (int64_t n = 0; n < Is; ++n) {
       bf16_row(a.ws1 + (int64_t(s) * Is + n) * d, wrow.data(), d);
-      float g = dot(xv.data(), wrow.data(), d);
+      float g = dot(xv.data(), wrow.data(), d, rev);
       bf16_row(a.ws3 + (int64_t(s) * Is + n) * d, wrow.data(), d);
-      float u = dot(xv.data(), wrow.data(), d);
+      float u = dot(xv.data(), wrow.data(), d, rev);
       hsv[int64_t(s) * Is + n] = bf16_round(silu(g) * u);
     }
   }
-  if (a.hs) for (int64_t i = 0; i < int64_t(a.S) * Is; ++i) a.hs[t * a.S * Is + i] = to_bf16(hsv[i]);
+  if (a.hs) for (int64_t i = 0; i < int64_t(a.S) * Is; ++i) a.hs[oi * a.S * Is + i] = to_bf16(hsv[i]);
 
   // latent up-projection plus the shared experts' down-projection, one fp32
-  // accumulator per output: latent terms first, then shared experts in order
-  std::vector<float> wo(l), w2s(Is);
+  // accumulator per output over the concatenated K = l + S*Is: latent terms
+  // first, then the shared experts in order (rev: the exact reverse)
+  std::vector<float> wo(l), w2s(int64_t(a.S) * Is);
   for (int64_t o = 0; o < d; ++o) {
     bf16_row(a.w_out + o * l, wo.data(), l);
+    for (int32_t s = 0; s < a.S; ++s) bf16_row(a.ws2 + (int64_t(s) * d + o) * Is, w2s.data() + int64_t(s) * Is, Is);
     float acc = 0.0f;
-    for (int64_t i = 0; i < l; ++i) acc += rh[i] * wo[i];
-    for (int32_t s = 0; s < a.S; ++s) {
-      bf16_row(a.ws2 + (int64_t(s) * d + o) * Is, w2s.data(), Is);
-      for (int64_t i = 0; i < Is; ++i) acc += hsv[int64_t(s) * Is + i] * w2s[i];
+    if (rev) {
+      for (int64_t i = int64_t(a.S) * Is - 1; i >= 0; --i) acc += hsv[i] * w2s[i];
+      for (int64_t i = l - 1; i >= 0; --i) acc += rh[i] * wo[i];
+    } else {
+      for (int64_t i = 0; i < l; ++i) acc += rh[i] * wo[i];
+      for (int64_t i = 0; i < int64_t(a.S) * Is; ++i) acc += hsv[i] * w2s[i];
     }
     y_row[o] = to_bf16(acc);
   }
@@ -421,16 +482,15 @@ int lmoe_oracle_layer(const lmoe_oracle_args* a) {
   if (rows && (a->k != 1 || a->S != 0)) return 1;
   if (a->mxfp4 && (!a->s1 || !a->s3 || !a->s2 || a->l % 32 || a->I % 32)) return 1;
   if (a->S > 0 && (!a->ws1 || !a->ws3 || !a->ws2)) return 1;
-  lmoe_oracle_args args = *a;
-  if (args.eval_tokens) {  // intermediates are laid out over all T tokens
-    args.z = args.hs = args.rhat = args.H = args.Y = nullptr;
-  }
-  const int64_t n = args.eval_tokens ? args.n_eval : args.T;
-  const int64_t ow = rows ? args.l : args.d;
+  for (int64_t r = 0; r < a->T * a->k; ++r)
+    if (a->ids[r] < 0 || a->ids[r] >= a->E) return 1;
+  const bool sampled = a->eval_tokens != nullptr;
+  const int64_t n = sampled ? a->n_eval : a->T;
+  const int64_t ow = rows ? a->l : a->d;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < n; ++i) {
-    const int64_t t = args.eval_tokens ? args.eval_tokens[i] : i;
-    one_token(args, t, args.y + i * ow);
+    const int64_t t = sampled ? a->eval_tokens[i] : i;
+    one_token(*a, t, i, sampled, a->y + i * ow);
   }
   return 0;
 }
