@@ -103,7 +103,10 @@ typedef struct latent_moe_plan latent_moe_plan; /* opaque, host memory */
  *   E, k        experts and experts per token: 1 <= k <= min(E, 64);
  *               E <= 1024 in logits mode, E <= 4096 in ids mode
  *   logits      fp32 [T,E] or NULL
- *   ids_in      int32 [T,k], values in [0,E), or NULL
+ *   ids_in      int32 [T,k], values in [0,E), or NULL.  The values are not
+ *               checked: an id outside [0,E) is a caller error that the
+ *               device code does not report (it is clamped to the nearest
+ *               expert, 0 or E-1, so no access leaves the buffers)
  *   weights_in  fp32 [T,k] (ids mode only)
  *   topk_ids    int32 [T,k] out (logits mode: required)
  *   topk_w      fp32 [T,k] out (logits mode: required)
@@ -253,6 +256,41 @@ size_t latent_moe_route_workspace_size(int64_t T, int32_t E, int32_t k);
 size_t latent_moe_forward_workspace_size(int64_t T, int32_t E, int32_t k, int32_t d, int32_t l,
                                          int32_t I, int32_t S, int32_t Is, int32_t wfmt,
                                          int32_t rows_mode);
+
+/*
+ * Where latent_moe_forward (and latent_moe_layer) keep the layer's
+ * intermediates inside the forward workspace, for inspection and testing.
+ * Every field is a byte offset from the workspace pointer; a field whose bit
+ * is clear in `written` names storage that a forward with these dimensions
+ * does not write.  The contents are valid once the stream has reached the end
+ * of the call, until the workspace is used again.  Rows of H, Y, hq and hsc
+ * are in permuted order: row p holds routed row sorted_row[p] = t*k + j.
+ *   z    bf16 [T,l]      latent (not in rows mode)            LMOE_WS_Z
+ *   hs   bf16 [T,S*Is]   shared experts' SwiGLU output         LMOE_WS_HS
+ *   H    bf16 [T*k,I]    routed SwiGLU output (bf16 and w4a16 experts,
+ *                        except the one-launch w4a16 expert MLP at
+ *                        l = I = 256, which keeps H on chip)   LMOE_WS_H
+ *   Y    bf16 [T*k,l]    routed expert output                  LMOE_WS_Y
+ *   rhat bf16 [T,l]      combined routed latent after the RMSNorm
+ *                        (not in rows mode)                    LMOE_WS_RHAT
+ *   zq, zs  u8 [T,l], [T,l/32]    w4a8: MXFP8 codes and e8m0 scales of
+ *                        FC1's input (z; rows mode: x)         LMOE_WS_ZQ
+ *   hq, hsc u8 [T*k,I], [T*k,I/32] w4a8: MXFP8 codes and scales of H, which
+ *                        FC1 writes in place of the bf16 H     LMOE_WS_HQ
+ * Returns LMOE_OK, or LMOE_EINVAL for invalid dimensions or a NULL `out`
+ * (then *out is unchanged).  Host only; nothing is enqueued.
+ */
+enum { LMOE_WS_Z = 1, LMOE_WS_HS = 2, LMOE_WS_H = 4, LMOE_WS_Y = 8, LMOE_WS_RHAT = 16, LMOE_WS_ZQ = 32,
+       LMOE_WS_HQ = 64 };
+typedef struct {
+  size_t z, hs, H, Y, rhat, zq, zs, hq, hsc;
+  size_t total; /* == latent_moe_forward_workspace_size(...) */
+  uint32_t written; /* LMOE_WS_* bits */
+} lmoe_forward_layout;
+
+int latent_moe_forward_workspace_layout(int64_t T, int32_t E, int32_t k, int32_t d, int32_t l, int32_t I,
+                                        int32_t S, int32_t Is, int32_t wfmt, int32_t rows_mode,
+                                        lmoe_forward_layout* out);
 
 /* One-line reason for the last non-OK status returned on this thread. */
 const char* latent_moe_last_error(void);

@@ -41,6 +41,14 @@ class ForwardArgs(ctypes.Structure):
                 ("ws3", _vp), ("ws2", _vp), ("y", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
 
 
+class ForwardLayout(ctypes.Structure):
+    _fields_ = [("z", _sz), ("hs", _sz), ("H", _sz), ("Y", _sz), ("rhat", _sz), ("zq", _sz), ("zs", _sz),
+                ("hq", _sz), ("hsc", _sz), ("total", _sz), ("written", ctypes.c_uint32)]
+
+
+LMOE_WS_BITS = {"z": 1, "hs": 2, "H": 4, "Y": 8, "rhat": 16, "zq": 32, "hq": 64}
+
+
 class LatentMoeError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"{_ERRNAMES.get(code, code)}: {msg}")
@@ -67,6 +75,9 @@ def _load():
     L.latent_moe_forward_workspace_size.restype = _sz
     L.latent_moe_plan_set_stage_events.argtypes = [_vp, ctypes.POINTER(_vp), ctypes.c_int]
     L.latent_moe_plan_set_stage_events.restype = ctypes.c_int
+    L.latent_moe_forward_workspace_layout.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                      ctypes.POINTER(ForwardLayout)]
+    L.latent_moe_forward_workspace_layout.restype = ctypes.c_int
     L.latent_moe_last_error.argtypes = []
     L.latent_moe_last_error.restype = ctypes.c_char_p
     return L
@@ -133,6 +144,37 @@ def forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt=LMOE_WFMT_BF16, rows_mo
     return lib.latent_moe_forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt, int(rows_mode))
 
 
+def latent_moe_forward_workspace_layout(T, E, k, d, l, I, S, Is, wfmt=LMOE_WFMT_BF16,
+                                        rows_mode=False) -> ForwardLayout:
+    out = ForwardLayout()
+    _check(lib.latent_moe_forward_workspace_layout(T, E, k, d, l, I, S, Is, wfmt, int(rows_mode),
+                                                   ctypes.byref(out)))
+    return out
+
+
+def workspace_views(workspace: torch.Tensor, T, E, k, d, l, I, S, Is, wfmt=LMOE_WFMT_BF16,
+                    rows_mode=False) -> dict:
+    """Typed views of the intermediates a forward wrote into ``workspace``
+    (only those it writes for these dimensions): z, hs, rhat [T, .] and H, Y
+    [T*k, .] in permuted row order as bf16; for w4a8 the MXFP8 codes and
+    scales zq, zs [T, l], [T, l/32] and hq, hsc [T*k, I], [T*k, I/32] as uint8."""
+    L = latent_moe_forward_workspace_layout(T, E, k, d, l, I, S, Is, wfmt, rows_mode)
+    if workspace.numel() < L.total:
+        raise ValueError("workspace smaller than the layout")
+    R = T * k
+    shapes = {"z": (T, l, 2), "hs": (T, S * Is, 2), "H": (R, I, 2), "Y": (R, l, 2), "rhat": (T, l, 2),
+              "zq": (T, l, 1), "zs": (T, l // 32, 1), "hq": (R, I, 1), "hsc": (R, I // 32, 1)}
+    bit_of = {"zs": "zq", "hsc": "hq"}
+    out = {}
+    for name, (rows, cols, nbytes) in shapes.items():
+        if not L.written & LMOE_WS_BITS[bit_of.get(name, name)]:
+            continue
+        off = getattr(L, name)
+        raw = workspace[off: off + rows * cols * nbytes]
+        out[name] = raw.view(torch.bfloat16).view(rows, cols) if nbytes == 2 else raw.view(rows, cols)
+    return out
+
+
 # ------------------------------------------------------------ tensor wrappers
 def _p(t: Optional[torch.Tensor]):
     if t is None:
@@ -146,6 +188,25 @@ def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _guard_owned(stream, owned):
+    """Buffers this binding allocates come from torch's caching allocator on
+    the current stream.  When the work runs on another stream, tell the
+    allocator (record_stream) so that the memory is not handed out again while
+    that stream may still use it; a raw stream handle cannot be recorded, so
+    it is refused when the binding has to allocate."""
+    owned = [t for t in owned if t is not None]
+    if stream is None or not owned:
+        return
+    if hasattr(stream, "cuda_stream"):
+        if stream.cuda_stream != torch.cuda.current_stream().cuda_stream:
+            for t in owned:
+                t.record_stream(stream)
+        return
+    if int(stream) != torch.cuda.current_stream().cuda_stream:
+        raise ValueError("with a raw stream handle other than torch's current stream, pass every output and "
+                         "workspace buffer in (the binding cannot track its own allocations on that stream)")
 
 
 @dataclass
@@ -163,6 +224,7 @@ class Routing:
     plan: Optional[int]
     keep: list = field(default_factory=list)
     logits: Optional[torch.Tensor] = None  # computed by ``layer`` (the router gate)
+    workspace_fwd: Optional[torch.Tensor] = None  # the last forward's workspace
 
     def free(self):
         if self.plan is not None:
@@ -193,6 +255,7 @@ def route(logits: Optional[torch.Tensor] = None, k: int = 1, *, ids: Optional[to
     ws_bytes = route_workspace_size(T, E, k)
     if ws_bytes == 0:
         raise LatentMoeError(LMOE_EINVAL, f"invalid route dims T={T} E={E} k={k}")
+    own_ws = workspace is None
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     topk_ids = torch.empty(T, k, dtype=torch.int32, device=dev) if logits is not None else None
@@ -200,6 +263,7 @@ def route(logits: Optional[torch.Tensor] = None, k: int = 1, *, ids: Optional[to
     sorted_row = torch.empty(R, dtype=torch.int32, device=dev)
     row_pos = torch.empty(R, dtype=torch.int32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    _guard_owned(stream, [workspace if own_ws else None, topk_ids, topk_w, sorted_row, row_pos, offsets])
     a = RouteArgs(T=T, E=E, k=k, logits=_p(logits), ids_in=_p(ids), weights_in=_p(weights),
                   topk_ids=_p(topk_ids), topk_w=_p(topk_w), sorted_row=_p(sorted_row),
                   row_pos=_p(row_pos), offsets=_p(offsets), workspace=_p(workspace),
@@ -227,15 +291,22 @@ def forward(routing: Routing, x: torch.Tensor, w1, w3, w2, *, w_in=None, w_out=N
     Is = 0 if ws1 is None else ws1.shape[1]
     wfmt = (LMOE_WFMT_MXFP4_W4A16 if w4a16 else LMOE_WFMT_MXFP4) if mxfp4 else LMOE_WFMT_BF16
     ws_bytes = forward_workspace_size(T, routing.E, routing.k, d, l, I, S, Is, wfmt, rows)
+    owned = []
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=x.device)
+        owned.append(workspace)
     if y is None:
         y = torch.empty(T, l if rows else d, dtype=torch.bfloat16, device=x.device)
+        owned.append(y)
+    _guard_owned(stream, owned)
     a = ForwardArgs(d=d, l=l, I=I, S=S, Is=Is, wfmt=wfmt, norm_eps=eps, x=_p(x), w_in=_p(w_in),
                     w1=_p(w1), w3=_p(w3), w2=_p(w2), s1=_p(s1), s3=_p(s3), s2=_p(s2), norm_w=_p(norm_w),
                     w_out=_p(w_out), ws1=_p(ws1), ws3=_p(ws3), ws2=_p(ws2), y=_p(y),
                     workspace=_p(workspace), workspace_bytes=workspace.numel())
     latent_moe_forward(routing.plan, a, _stream(stream))
+    # the workspace lives as long as the routing (the last forward's
+    # intermediates stay readable through workspace_views)
+    routing.workspace_fwd = workspace
     return y
 
 
@@ -260,6 +331,7 @@ def layer(x: torch.Tensor, w_r: Optional[torch.Tensor], k: int, w1, w3, w2, *, w
     Is = 0 if ws1 is None else ws1.shape[1]
     wfmt = (LMOE_WFMT_MXFP4_W4A16 if w4a16 else LMOE_WFMT_MXFP4) if mxfp4 else LMOE_WFMT_BF16
     R = T * k
+    fresh_routing = routing is None
     if routing is None:
         rws = route_workspace_size(T, E, k)
         if rws == 0:
@@ -275,11 +347,16 @@ def layer(x: torch.Tensor, w_r: Optional[torch.Tensor], k: int, w1, w3, w2, *, w
         raise ValueError("the Routing passed in is not from a layer call of this shape")
     elif logits is not None:
         routing.logits = logits
+    owned = [routing.topk_ids, routing.topk_w, routing.sorted_row, routing.row_pos, routing.offsets,
+             routing.workspace] if fresh_routing else []
     if workspace is None:
         ws_bytes = forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt, False)
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        owned.append(workspace)
     if y is None:
         y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+        owned.append(y)
+    _guard_owned(stream, owned)
     ra = RouteArgs(T=T, E=E, k=k, logits=_p(logits), ids_in=None, weights_in=None, topk_ids=_p(routing.topk_ids),
                    topk_w=_p(routing.topk_w), sorted_row=_p(routing.sorted_row), row_pos=_p(routing.row_pos),
                    offsets=_p(routing.offsets), workspace=_p(routing.workspace),
@@ -291,6 +368,7 @@ def layer(x: torch.Tensor, w_r: Optional[torch.Tensor], k: int, w1, w3, w2, *, w
     routing.plan = latent_moe_layer(ra, _p(w_r), None if w_r is None else _p(routing.logits), fa, _stream(stream),
                                     routing.plan)
     routing.keep = [workspace]
+    routing.workspace_fwd = workspace
     return routing, y
 
 

@@ -594,6 +594,38 @@ size_t latent_moe_forward_workspace_size(int64_t T, int32_t E, int32_t k, int32_
   return fwd_layout(T, k, l, I, S, rows_mode ? 0 : Is, rows_mode != 0, wfmt == LMOE_WFMT_MXFP4).total;
 }
 
+int latent_moe_forward_workspace_layout(int64_t T, int32_t E, int32_t k, int32_t d, int32_t l, int32_t I,
+                                        int32_t S, int32_t Is, int32_t wfmt, int32_t rows_mode,
+                                        lmoe_forward_layout* out) {
+  if (!out) return fail(LMOE_EINVAL, "NULL out");
+  if (latent_moe_forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt, rows_mode) == 0)
+    return fail(LMOE_EINVAL, "invalid forward dimensions");
+  const bool rows = rows_mode != 0;
+  const bool mx = wfmt == LMOE_WFMT_MXFP4;
+  const int32_t Sx = rows ? 0 : S;
+  const FwdLayout L = fwd_layout(T, k, l, I, Sx, Sx ? Is : 0, rows, mx);
+  lmoe_forward_layout o{};
+  o.z = L.z;
+  o.hs = L.hs;
+  o.H = L.H;
+  o.Y = L.Y;
+  o.rhat = L.rhat;
+  o.zq = L.zq;
+  o.zs = L.zs;
+  o.hq = L.hq;
+  o.hsc = L.hsc;
+  o.total = L.total;
+  uint32_t w = LMOE_WS_Y;
+  if (!rows) w |= LMOE_WS_Z | LMOE_WS_RHAT;
+  if (!rows && Sx > 0) w |= LMOE_WS_HS;
+  const bool fused_w4 = wfmt == LMOE_WFMT_MXFP4_W4A16 && l == lmoe::kW4MlpWidth && I == lmoe::kW4MlpWidth;
+  if (!mx && !fused_w4) w |= LMOE_WS_H;
+  if (mx) w |= LMOE_WS_ZQ | LMOE_WS_HQ;
+  o.written = w;
+  *out = o;
+  return LMOE_OK;
+}
+
 int latent_moe_route(const lmoe_route_args* a, void* hip_stream, latent_moe_plan** out_plan) {
   if (!a || !out_plan) return fail(LMOE_EINVAL, "NULL args or out_plan");
   *out_plan = nullptr;

@@ -36,13 +36,23 @@ __device__ __forceinline__ uint32_t e4m3x4(float v0, float v1, float v2, float v
 
 // MXFP8 quantisation of one 32-element block (OCP MX: one shared e8m0 scale
 // per 32 elements): scale exponent = floor(log2 amax) - 8 (clamped to e8m0's
-// range; an all-zero block gets code 0), elements = e4m3(v / 2^exp).  raw
-// holds the block's 32 bf16 values; codes receives 32 e4m3 bytes.
+// range; an all-zero block gets code 0), elements = e4m3(v / 2^exp).  A block
+// holding a NaN or an infinity (e4m3fn has no infinity) becomes a NaN block:
+// scale code 255 (e8m0's NaN) and every element code 0x7F (e4m3fn's NaN), so
+// NaN reaches the product.  raw holds the block's 32 bf16 values; codes
+// receives 32 e4m3 bytes.
 __device__ __forceinline__ uint8_t quant_block32(const uint4 (&raw)[4], uint4 (&codes)[2]) {
   const bf16_t* h = reinterpret_cast<const bf16_t*>(raw);
-  float amax = 0.0f;
+  // the largest magnitude as a bf16 bit pattern: magnitudes order like their
+  // patterns, infinity is 0x7F80 and every NaN lies above it
+  uint32_t amag = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(bf16_to_f32(h[i])));
+  for (int i = 0; i < 32; ++i) amag = max(amag, uint32_t(h[i]) & 0x7fffu);
+  if (amag >= 0x7f80u) {
+    codes[0] = codes[1] = uint4{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
+    return uint8_t(255);
+  }
+  const float amax = __uint_as_float(amag << 16);
   int sexp = -127;
   if (amax > 0.0f) {
     const uint32_t au = __float_as_uint(amax);

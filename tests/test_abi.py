@@ -174,3 +174,42 @@ def test_layer_binding_takes_exactly_one_of_gate_and_logits():
         with pytest.raises(ValueError):
             lm.layer(x, w_r, 2, w, w, w, w_in=torch.zeros(64, 64, dtype=torch.bfloat16),
                      w_out=torch.zeros(64, 64, dtype=torch.bfloat16), logits=logits)
+
+
+@pytest.mark.parametrize("dims,wfmt,rows", [
+    ((8192, 896, 16, 7168, 2048, 512, 2, 512), 0, False),
+    ((16384, 896, 16, 7168, 2048, 512, 2, 512), 1, False),
+    ((256, 896, 16, 512, 256, 256, 2, 256), 2, False),
+    ((256, 896, 16, 512, 384, 256, 2, 256), 2, False),
+    ((16384, 56, 1, 0, 2048, 512, 0, 0), 0, True),
+    ((16384, 56, 1, 0, 2048, 512, 0, 0), 1, True),
+    ((77, 40, 8, 128, 320, 192, 2, 64), 0, False),
+])
+def test_forward_workspace_layout(dims, wfmt, rows):
+    """The intermediates' regions lie inside the workspace, do not overlap,
+    and the written bits name what each format writes."""
+    import latentmoe_expert_layer_amd as lm
+    T, E, k, d, l, I, S, Is = dims
+    L = lm.latent_moe_forward_workspace_layout(T, E, k, d, l, I, S, Is, wfmt, rows)
+    assert L.total == lm.forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt, rows)
+    R = T * k
+    sizes = {"z": T * l * 2, "hs": T * S * Is * 2, "H": R * I * 2, "Y": R * l * 2, "rhat": T * l * 2,
+             "zq": T * l, "zs": T * l // 32, "hq": R * I, "hsc": R * I // 32}
+    bit = {"zs": "zq", "hsc": "hq"}
+    spans = []
+    for n, nb in sizes.items():
+        if L.written & lm.LMOE_WS_BITS[bit.get(n, n)]:
+            off = getattr(L, n)
+            assert off % 256 == 0 and off + nb <= L.total, n
+            spans.append((off, off + nb, n))
+    spans.sort()
+    for (a0, a1, na), (b0, b1, nb_) in zip(spans, spans[1:]):
+        assert a1 <= b0, (na, nb_)
+    w = L.written
+    assert bool(w & lm.LMOE_WS_BITS["Y"])
+    assert bool(w & lm.LMOE_WS_BITS["z"]) == (not rows)
+    assert bool(w & lm.LMOE_WS_BITS["zq"]) == (wfmt == 1)
+    assert bool(w & lm.LMOE_WS_BITS["H"]) == (wfmt == 0 or (wfmt == 2 and not (l == 256 and I == 256)))
+    with pytest.raises(lm.LatentMoeError):
+        lm.latent_moe_forward_workspace_layout(T, E, 0, d, l, I, S, Is, wfmt, rows)
+

@@ -1,16 +1,19 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Routing ids, permutation and offsets must be bit-exact; combine weights within
-2e-6; bf16 layer outputs within max relative error 2e-2 (relative to
-max(|o|, 0.1 * rms(o))) and mean absolute error 1e-3.  Workspaces and outputs
-are poisoned with NaN before every call, so an unwritten read fails.
+2e-6.  Every intermediate the forward writes (z, hs, H, Y, rhat and, for MXFP4
+w4a8, the MXFP8 codes of the expert GEMMs' inputs) and the output y are
+compared with the oracle's element by element, per column and per kernel tile
+(tests/parity.py states the bars).  Workspaces and outputs are poisoned with
+NaN before every call, so an unwritten read fails.
 """
 import pytest
 import torch
 
 import oracle
 import workloads as W
-from tests.parity import assert_parity, assert_rowwise, log, poison_, to_device, to_host
+from tests.gpu_helpers import check_layer, check_routing, gpu_route, run_gpu_layer
+from tests.parity import assert_parity, assert_w4a8, log, poison_, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -24,30 +27,6 @@ def _lib():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     lm = m
     yield
-
-
-def gpu_route(logits=None, k=1, **kw):
-    T = logits.shape[0] if logits is not None else kw["ids"].shape[0]
-    E = logits.shape[1] if logits is not None else kw["E"]
-    ws = poison_(torch.empty(lm.route_workspace_size(T, E, k), dtype=torch.uint8, device="cuda"))
-    r = lm.route(logits, k, workspace=ws, **kw)
-    torch.cuda.synchronize()
-    return r
-
-
-def check_routing(r, logits_or_ids, k, E, weights=None):
-    if weights is None:
-        ids_ref, w_ref = oracle.route(logits_or_ids.cpu(), k)
-        assert torch.equal(r.topk_ids.cpu(), ids_ref), "router ids differ"
-        dw = (r.topk_w.cpu().double() - w_ref.double()).abs().max().item()
-        assert dw <= 2e-6, f"combine weights differ by {dw}"
-    else:
-        ids_ref, w_ref = logits_or_ids.cpu(), weights.cpu()
-    off, srow, rpos = oracle.permute(ids_ref, E)
-    assert torch.equal(r.offsets.cpu(), off), "offsets differ"
-    assert torch.equal(r.sorted_row.cpu(), srow), "sorted_row differs"
-    assert torch.equal(r.row_pos.cpu(), rpos), "row_pos differs"
-    return ids_ref, w_ref
 
 
 # ------------------------------------------------------------------ routing
@@ -137,33 +116,6 @@ def test_permute_ids_mode(R, E, heavy):
 
 
 # -------------------------------------------------------------------- layer
-def run_gpu_layer(inp_dev, norm=True):
-    cfg = inp_dev["cfg"]
-    T = cfg.T
-    mx = cfg.mxfp4
-    wfmt = (lm.LMOE_WFMT_MXFP4_W4A16 if cfg.w4a16 else lm.LMOE_WFMT_MXFP4) if mx else lm.LMOE_WFMT_BF16
-    w1, w3, w2 = (inp_dev[n + ("q" if mx else "")] for n in ("w1", "w3", "w2"))
-    wts = dict(s1=inp_dev.get("s1"), s3=inp_dev.get("s3"), s2=inp_dev.get("s2"), mxfp4=mx, w4a16=cfg.w4a16,
-               I=cfg.I)
-    if cfg.rows_mode:
-        r = gpu_route(None, 1, ids=inp_dev["ids"], weights=inp_dev["weights"], E=cfg.E)
-        nbytes = lm.forward_workspace_size(T, cfg.E, 1, 0, cfg.l, cfg.I, 0, 0, wfmt, True)
-        ws = poison_(torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
-        y = poison_(torch.empty(T, cfg.l, dtype=torch.bfloat16, device="cuda"))
-        lm.forward(r, inp_dev["x"], w1, w3, w2, y=y, workspace=ws, **wts)
-        torch.cuda.synchronize()
-        return r, y
-    r = gpu_route(inp_dev["logits"], cfg.k)
-    nbytes = lm.forward_workspace_size(T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is, wfmt, False)
-    ws = poison_(torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
-    y = poison_(torch.empty(T, cfg.d, dtype=torch.bfloat16, device="cuda"))
-    lm.forward(r, inp_dev["x"], w1, w3, w2, w_in=inp_dev["w_in"], w_out=inp_dev["w_out"],
-               ws1=inp_dev.get("ws1"), ws3=inp_dev.get("ws3"), ws2=inp_dev.get("ws2"),
-               norm_w=inp_dev.get("norm_w") if norm else None, eps=cfg.eps, y=y, workspace=ws, **wts)
-    torch.cuda.synchronize()
-    return r, y
-
-
 SMALL_LAYERS = [
     ("tiny", None),
     ("decode", None),
@@ -190,20 +142,20 @@ SMALL_LAYERS = [
 @pytest.mark.parametrize("name,dims", SMALL_LAYERS, ids=[n for n, _ in SMALL_LAYERS])
 @pytest.mark.parametrize("norm", ["ones", "random", "none"])
 def test_layer_parity_small(name, dims, norm):
+    """Every token, every intermediate."""
     cfg = W.CONFIGS[name] if dims is None else W.custom(name, **dims)
     log(f"layer {name} norm={norm}: {cfg}")
     inp = W.make_inputs(cfg, norm_w=norm)
-    ref = oracle.run(inp)
-    r, y = run_gpu_layer(to_device(inp))
-    check_routing(r, inp["logits"], cfg.k, cfg.E)
-    assert_parity(y.cpu(), ref["y"])
+    r, y, views = run_gpu_layer(to_device(inp))
+    ids, w = check_routing(r, inp["logits"], cfg.k, cfg.E)
+    check_layer(inp, ids, w, y, views)
 
 
 def test_layer_deterministic_and_empty():
     cfg = W.CONFIGS["decode"]
     inp = to_device(W.make_inputs(cfg))
-    _, y1 = run_gpu_layer(inp)
-    _, y2 = run_gpu_layer(inp)
+    _, y1, _ = run_gpu_layer(inp)
+    _, y2, _ = run_gpu_layer(inp)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "repeat runs differ"
     # T = 0 is a no-op
     empty = W.custom("empty", T=0, d=512, l=256, E=16, k=4, S=1, I=128, Is=128)
@@ -226,47 +178,10 @@ def test_rows_mode_small(R, E, l, I):
                    zipf_s=1.1, seed=R)
     log(f"rows mode small: {cfg}")
     inp_dev = W.make_inputs(cfg, device="cuda")
-    r, y = run_gpu_layer(inp_dev)
+    r, y, views = run_gpu_layer(inp_dev)
     inp = to_host(inp_dev)
     check_routing(r, inp["ids"].view(-1), 1, cfg.E, weights=inp["weights"])
-    ref = oracle.layer(inp, inp["ids"], inp["weights"])["y"]
-    assert_parity(y.cpu(), ref)
-
-
-def test_rows_mode_ep_share_sampled():
-    cfg = W.CONFIGS["ep_share"]
-    log(f"ep_share rows mode: {cfg}")
-    inp_dev = W.make_inputs(cfg, device="cuda")
-    r, y = run_gpu_layer(inp_dev)
-    inp = to_host(inp_dev)
-    check_routing(r, inp["ids"].view(-1), 1, cfg.E, weights=inp["weights"])
-    # sample rows: the first and last rows of the heaviest and lightest experts, plus a spread
-    off, srow, _ = oracle.permute(inp["ids"], cfg.E)
-    off, srow = off.long(), srow.long()
-    counts = off[1:] - off[:-1]
-    pick = set(range(0, cfg.T, cfg.T // 48))
-    for e in (int(counts.argmax()), int(counts.argmin())):
-        if counts[e] > 0:
-            pick |= {int(srow[off[e]]), int(srow[off[e + 1] - 1])}
-    pick = sorted(pick)
-    ref = oracle.layer(inp, inp["ids"], inp["weights"], eval_tokens=pick)["y"]
-    assert_parity(y.cpu()[pick], ref)
-
-
-@pytest.mark.parametrize("name", ["prefill"])
-def test_layer_full_size_sampled(name):
-    cfg = W.CONFIGS[name]
-    log(f"full-size {name}: {cfg}")
-    inp_dev = W.make_inputs(cfg, device="cuda")
-    r, y = run_gpu_layer(inp_dev)
-    ids_ref, w_ref = check_routing(r, inp_dev["logits"], cfg.k, cfg.E)
-    inp = to_host(inp_dev)
-    del inp_dev
-    # first and last token of every 1024-token span, plus a spread
-    pick = sorted({0, cfg.T - 1} | set(range(0, cfg.T, 1024)) | set(range(1023, cfg.T, 1024))
-                  | set(range(37, cfg.T, 997)))
-    ref = oracle.layer(inp, ids_ref, w_ref, eval_tokens=pick)["y"]
-    assert_parity(y.cpu()[pick], ref)
+    check_layer(inp, inp["ids"], inp["weights"], y, views)
 
 
 def test_graph_replay_matches_eager():
@@ -274,7 +189,7 @@ def test_graph_replay_matches_eager():
     and synchronisations in between) equals the eager result bit for bit."""
     cfg = W.CONFIGS["decode"]
     inp = to_device(W.make_inputs(cfg))
-    _, y_ref = run_gpu_layer(inp)
+    _, y_ref, _ = run_gpu_layer(inp)
     T, E, k = cfg.T, cfg.E, cfg.k
     rws = torch.empty(lm.route_workspace_size(T, E, k), dtype=torch.uint8, device="cuda")
     fws = torch.empty(lm.forward_workspace_size(T, E, k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is),
@@ -317,20 +232,24 @@ MX_LAYERS = [
     ("mx_heavy", dict(T=700, d=256, l=128, E=4, k=2, S=0, I=384, Is=0, mxfp4=True)),
     # K = 512 for both GEMMs (the two-stages-ahead pipeline), experts over 192 rows (two tiles each)
     ("mx_deep", dict(T=400, d=128, l=512, E=3, k=2, S=1, I=512, Is=64, mxfp4=True)),
+    # more real tiles than CUs with I % 256 == 0: the persistent FC2 grid runs
+    # several tiles per workgroup (about 8 x 21 row tiles x 8 column tiles)
+    ("mx_many_tiles", dict(T=4096, d=128, l=2048, E=8, k=2, S=0, I=512, Is=0, mxfp4=True)),
 ]
 
 
 @pytest.mark.parametrize("name,dims", MX_LAYERS, ids=[n for n, _ in MX_LAYERS])
 def test_mxfp4_layer_parity_small(name, dims):
     """w4a8: MXFP8 activations x MXFP4 weights vs an oracle with the same
-    dequantised weights and the same activation quantisation (5e-2)."""
+    dequantised weights and the same activation quantisation: the MXFP8 codes
+    of z and H within the code budget, Y, rhat and y element-wise at 5e-2
+    within the flip budget; every token."""
     cfg = W.custom(name, **dims)
     log(f"mxfp4 layer {name}: {cfg}")
     inp = W.make_inputs(cfg)
-    ref = oracle.run(inp, act_quant=True)
-    r, y = run_gpu_layer(to_device(inp))
-    check_routing(r, inp["logits"], cfg.k, cfg.E)
-    assert_rowwise(y.cpu(), ref["y"])
+    r, y, views = run_gpu_layer(to_device(inp))
+    ids, w = check_routing(r, inp["logits"], cfg.k, cfg.E)
+    check_layer(inp, ids, w, y, views)
 
 
 W4A16_LAYERS = [
@@ -353,10 +272,9 @@ def test_w4a16_layer_parity(name, dims, norm):
     cfg = W.CONFIGS[name] if dims is None else W.custom(name, **dims)
     log(f"w4a16 layer {name} norm={norm}: {cfg}")
     inp = W.make_inputs(cfg, norm_w=norm)
-    ref = oracle.run(inp, act_quant=False)
-    r, y = run_gpu_layer(to_device(inp))
-    check_routing(r, inp["logits"], cfg.k, cfg.E)
-    assert_parity(y.cpu(), ref["y"])
+    r, y, views = run_gpu_layer(to_device(inp))
+    ids, w = check_routing(r, inp["logits"], cfg.k, cfg.E)
+    check_layer(inp, ids, w, y, views, act_quant=False)
 
 
 def test_w4a16_rows_mode():
@@ -365,11 +283,10 @@ def test_w4a16_rows_mode():
                    zipf_s=1.1, seed=5, mxfp4=True, w4a16=True)
     log(f"w4a16 rows mode: {cfg}")
     inp_dev = W.make_inputs(cfg, device="cuda")
-    r, y = run_gpu_layer(inp_dev)
+    r, y, views = run_gpu_layer(inp_dev)
     inp = to_host(inp_dev)
     check_routing(r, inp["ids"].view(-1), 1, cfg.E, weights=inp["weights"])
-    ref = oracle.layer(inp, inp["ids"], inp["weights"], act_quant=False)["y"]
-    assert_parity(y.cpu(), ref)
+    check_layer(inp, inp["ids"], inp["weights"], y, views, act_quant=False)
 
 
 def test_w4a16_rejects_large_batches():
@@ -387,20 +304,6 @@ def test_w4a16_rejects_large_batches():
     assert ei.value.code == lm.LMOE_EUNSUPPORTED
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), before.view(torch.int16))
-
-
-def test_mxfp4_full_size_sampled():
-    cfg = W.CONFIGS["prefill_mxfp4"]
-    log(f"full-size {cfg.name}: {cfg}")
-    inp_dev = W.make_inputs(cfg, device="cuda")
-    r, y = run_gpu_layer(inp_dev)
-    ids_ref, w_ref = check_routing(r, inp_dev["logits"], cfg.k, cfg.E)
-    inp = to_host(inp_dev)
-    del inp_dev
-    pick = sorted({0, cfg.T - 1} | set(range(0, cfg.T, 2048)) | set(range(2047, cfg.T, 2048))
-                  | set(range(101, cfg.T, 1999)))
-    ref = oracle.layer(inp, ids_ref, w_ref, eval_tokens=pick, act_quant=True)["y"]
-    assert_rowwise(y.cpu()[pick], ref)
 
 
 # ------------------------------------------- the whole layer with the router gate
@@ -484,14 +387,36 @@ def test_gate_layer_exact_grid(name, dims):
     assert_parity(y.cpu(), ref["y"])
 
 
+def _near_tie_candidates(o, k, tol):
+    """For each token, the expert sets its oracle logits ``o`` allow when every
+    logit may be off by ``tol``: the experts above the k-th largest value by
+    more than 2 tol are sure; the remaining places go to any choice among the
+    experts within 2 tol of it.  Returns a list of lists of frozensets."""
+    import itertools
+    out = []
+    for row in o:
+        kth = torch.topk(row, k).values[-1].item()
+        sure = (row > kth + 2 * tol).nonzero().flatten().tolist()
+        near = ((row >= kth - 2 * tol) & (row <= kth + 2 * tol)).nonzero().flatten().tolist()
+        need = k - len(sure)
+        combos = list(itertools.combinations(near, need))
+        assert len(combos) <= 100000, "too many near-tied experts"
+        out.append([frozenset(sure) | frozenset(c) for c in combos])
+    return out
+
+
 def test_gate_layer_continuous_inputs():
     """The bench's input distribution (x ~ N(0,1), W_in ~ N(0,0.02), gate scaled
     for unit-variance logits), where sums are not exact: fp32 summation order
     and one-ulp bf16 flips of z elements move logits by a few 1e-3, so the
-    logits are compared within 1e-2; tokens whose oracle logits have their k-th
-    and (k+1)-th largest values more than 2e-2 apart select the same experts;
-    every token's GPU ids are the top-k (value desc, index asc) of the GPU's
-    own logits; outputs of identically routed tokens meet the bf16 bar."""
+    logits are compared within 1e-2, and a token whose k-th and (k+1)-th
+    largest logits lie within that noise has more than one correct expert set.
+    From the oracle's logits alone, every token gets the sets they allow
+    (near-tied experts within 2e-2 of the k-th value swapped in and out); the
+    GPU's set must be one of them, its ids the top-k of its own logits, and
+    every token's output meets the bf16 bar against the oracle evaluated with
+    the candidate set the GPU took (its ids ordered and weighted from the
+    oracle's logits)."""
     cfg = W.custom("gate_cont", router_gemm=True, T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256)
     log(f"gate layer continuous: {cfg}")
     inp_dev = W.make_inputs(cfg, device="cuda")
@@ -503,18 +428,29 @@ def test_gate_layer_continuous_inputs():
     err = (g - o).abs().max().item()
     log(f"  logits: max |gpu - oracle| = {err:.3e}")
     assert err <= tol
-    top = torch.topk(o, cfg.k + 1, dim=1).values
-    sep = (top[:, cfg.k - 1] - top[:, cfg.k]) > 2 * tol
-    gi, oi = r.topk_ids.cpu(), ref["ids"]
-    same = (gi == oi).all(dim=1)
-    same_set = (gi.sort(dim=1).values == oi.sort(dim=1).values).all(dim=1)
-    assert bool(same_set[sep].all()), "well-separated tokens select different experts"
+    gi = r.topk_ids.cpu()
     order = torch.sort(g, dim=1, descending=True, stable=True).indices[:, :cfg.k]
     assert torch.equal(gi.long(), order), "GPU ids are not the top-k of the GPU logits"
-    pick = same.nonzero().flatten()
-    log(f"  {int(sep.sum())} tokens separated at the k-th boundary, {pick.numel()} of {cfg.T} routed identically")
-    assert pick.numel() >= 0.9 * cfg.T
-    assert_parity(y.cpu()[pick], ref["y"][pick])
+    cands = _near_tie_candidates(ref["logits"], cfg.k, tol)
+    gsets = [frozenset(row) for row in gi.tolist()]
+    for t in range(cfg.T):
+        assert gsets[t] in cands[t], f"token {t}: the GPU's expert set is not one the oracle's logits allow"
+    # the oracle's reference output per token: its own routing where the GPU
+    # took the oracle's set, else the candidate the GPU took
+    ref_y = ref["y"].clone()
+    other = [t for t in range(cfg.T) if gsets[t] != frozenset(ref["ids"][t].tolist())]
+    log(f"  {cfg.T - len(other)} tokens on the oracle's expert set, {len(other)} on another valid set")
+    if other:
+        lg = ref["logits"].clone()
+        for t in other:
+            keep = torch.zeros(cfg.E, dtype=torch.bool)
+            keep[sorted(gsets[t])] = True
+            lg[t] = torch.where(keep, lg[t], torch.full_like(lg[t], float("-inf")))
+        ids2, w2 = oracle.route(lg, cfg.k)
+        assert all(frozenset(ids2[t].tolist()) == gsets[t] for t in other)
+        alt = oracle.layer(inp, ids2, w2, eval_tokens=other)["y"]
+        ref_y[other] = alt
+    assert_parity(y.cpu(), ref_y)
 
 
 def test_gate_layer_prefill_sampled():
@@ -600,7 +536,7 @@ def test_layer_given_logits_on_zeroed_buffers():
     cfg = W.CONFIGS["decode"]
     log(f"given logits on zeroed buffers: {cfg}")
     inp = to_device(W.make_inputs(cfg))
-    r_ref, y_ref = run_gpu_layer(inp)
+    r_ref, y_ref, _ = run_gpu_layer(inp)
     T, E, k = cfg.T, cfg.E, cfg.k
     z = lambda *shape, dt=torch.int32: torch.zeros(*shape, dtype=dt, device="cuda")
     routing = lm.Routing(T, E, k, z(T, k), z(T, k, dt=torch.float32), z(T * k), z(T * k), z(E + 1),
@@ -642,7 +578,7 @@ def test_layer_with_given_logits_equals_route_then_forward(name, dims):
     log(f"layer with given logits {name}: {cfg}")
     inp = W.make_inputs(cfg)
     inp_dev = to_device(inp)
-    r_ref, y_ref = run_gpu_layer(inp_dev)
+    r_ref, y_ref, _ = run_gpu_layer(inp_dev)
     mx = cfg.mxfp4
     w1, w3, w2 = (inp_dev[n + ("q" if mx else "")] for n in ("w1", "w3", "w2"))
     wts = dict(s1=inp_dev.get("s1"), s3=inp_dev.get("s3"), s2=inp_dev.get("s2"), mxfp4=mx, w4a16=cfg.w4a16,
@@ -656,7 +592,7 @@ def test_layer_with_given_logits_equals_route_then_forward(name, dims):
     check_routing(r, inp["logits"], cfg.k, cfg.E)
     ref = oracle.run(inp, act_quant=mx and not cfg.w4a16)
     if mx and not cfg.w4a16:
-        assert_rowwise(y.cpu(), ref["y"])
+        assert_w4a8(y.cpu(), ref["y"])
     else:
         assert_parity(y.cpu(), ref["y"])
 
