@@ -230,6 +230,33 @@ int latent_moe_forward(const latent_moe_plan* plan, const lmoe_forward_args* arg
 int latent_moe_layer(const lmoe_route_args* route, const void* w_router, float* logits,
                      const lmoe_forward_args* fwd, void* hip_stream, latent_moe_plan** plan_io);
 
+/*
+ * latent_moe_layer for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It computes
+ * exactly what latent_moe_layer computes (the same kernels), except that
+ *  - both workspaces come from a static device array of
+ *    LMOE_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held
+ *    from the first call on that GPU until the process ends: route->workspace
+ *    and fwd->workspace must be NULL and their sizes 0;
+ *  - no plan is created or kept (no host allocation either); stage events do
+ *    not apply.
+ * Limit: latent_moe_route_workspace_size (rounded up to 256 bytes) plus
+ * latent_moe_forward_workspace_size must not exceed the array, else
+ * LMOE_EUNSUPPORTED and nothing is enqueued (64 MiB holds the decode shape,
+ * 256 tokens x top-16 of 896 at latent 256, about 14 times over; a prefill
+ * batch does not fit).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on the
+ * same GPU (other streams, other host threads) race on it and must be
+ * serialised by the caller.  The array keeps the last call's intermediates
+ * (latent_moe_forward_workspace_layout at offset
+ * round_up(latent_moe_route_workspace_size, 256)); no part of it needs to
+ * start at zero.  The work runs on the device of hip_stream (the current
+ * device for NULL).  Other arguments and errors as for latent_moe_layer.
+ */
+#define LMOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int latent_moe_layer_noalloc(const lmoe_route_args* route, const void* w_router, float* logits,
+                             const lmoe_forward_args* fwd, void* hip_stream);
+
 /* Releases a plan (host memory only; NULL is a no-op).  Device buffers the
  * plan borrowed remain the caller's. */
 void latent_moe_free(latent_moe_plan* plan);

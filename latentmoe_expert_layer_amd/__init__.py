@@ -67,6 +67,8 @@ def _load():
     L.latent_moe_layer.argtypes = [ctypes.POINTER(RouteArgs), _vp, _vp, ctypes.POINTER(ForwardArgs), _vp,
                                    ctypes.POINTER(_vp)]
     L.latent_moe_layer.restype = ctypes.c_int
+    L.latent_moe_layer_noalloc.argtypes = [ctypes.POINTER(RouteArgs), _vp, _vp, ctypes.POINTER(ForwardArgs), _vp]
+    L.latent_moe_layer_noalloc.restype = ctypes.c_int
     L.latent_moe_free.argtypes = [_vp]
     L.latent_moe_free.restype = None
     L.latent_moe_route_workspace_size.argtypes = [_i64, _i32, _i32]
@@ -108,6 +110,16 @@ def latent_moe_layer(route_args: RouteArgs, w_router: int, logits: int, fwd_args
                               _vp(stream), ctypes.byref(h))
     _check(rc)
     return h.value
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # LMOE_NOALLOC_SCRATCH_BYTES
+
+
+def latent_moe_layer_noalloc(route_args: RouteArgs, w_router: int, logits: int, fwd_args: ForwardArgs,
+                             stream: int = 0):
+    """Calls the C entry point (workspaces NULL: the library's static scratch)."""
+    _check(lib.latent_moe_layer_noalloc(ctypes.byref(route_args), _vp(w_router), _vp(logits),
+                                        ctypes.byref(fwd_args), _vp(stream)))
 
 
 def latent_moe_free(plan: Optional[int]):

@@ -653,18 +653,21 @@ int latent_moe_forward(const latent_moe_plan* p, const lmoe_forward_args* a, voi
   return fwd_back(c);
 }
 
-int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logits, const lmoe_forward_args* f,
-                     void* hip_stream, latent_moe_plan** plan_io) {
-  if (!r || !f || !plan_io) return fail(LMOE_EINVAL, "NULL route args, forward args or plan_io");
+}  // extern "C"
+
+namespace {
+
+// latent_moe_layer's checks (nothing enqueued on failure).
+int layer_check(const lmoe_route_args* r, const void* w_router, const float* logits, const lmoe_forward_args* f) {
+  if (!r || !f) return fail(LMOE_EINVAL, "NULL route args or forward args");
   // with a router gate the logits are computed here; without one the route
   // arguments give them (or the ids), as for latent_moe_route
   const bool gate = w_router != nullptr;
   int rc = route_check(r, gate);
   if (rc) return rc;
   if (!f->w_in) return fail(LMOE_EINVAL, "latent_moe_layer needs the projections (w_in != NULL)");
-  const bool ids_mode = !gate && r->ids_in != nullptr;
   latent_moe_plan q{};
-  fill_plan(&q, r, ids_mode);
+  fill_plan(&q, r, !gate && r->ids_in != nullptr);
   if ((rc = fwd_check(&q, f)) != LMOE_OK) return rc;
   if (r->T > 0) {
     if (gate) {
@@ -675,6 +678,88 @@ int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logi
       return fail(LMOE_EINVAL, "without w_router the route arguments give the logits: logits must be NULL");
     }
   }
+  return LMOE_OK;
+}
+
+// Enqueues the whole layer with the (checked) arguments into the plan `p`,
+// which has been filled from them.
+int layer_enqueue(latent_moe_plan* p, const lmoe_route_args* r, const void* w_router, float* logits,
+                  const lmoe_forward_args* f, hipStream_t s) {
+  if (p->T == 0) return LMOE_OK;
+  const bool gate = w_router != nullptr;
+  const FwdCtx c = fwd_ctx(p, f, s);
+  int rc;
+  if (!gate) {
+    // given logits: at small T the top-k runs in the down-projection's launch
+    // (it reads neither x nor z), leaving only the permutation before the experts
+    const bool fuse = !p->ids_mode && c.small;
+    if ((rc = fwd_front(c, fuse ? r : nullptr)) != LMOE_OK) return rc;
+    if ((rc = route_enqueue(p, r, r->logits, s, fuse)) != LMOE_OK) return rc;
+    return fwd_back(c);
+  }
+  if ((rc = fwd_front(c)) != LMOE_OK) return rc;
+  // the router gate on the latent z (in the forward workspace): fp32 logits
+  const uint16_t* z = reinterpret_cast<const uint16_t*>(static_cast<const char*>(f->workspace) + c.L.z);
+  const uint16_t* wr = static_cast<const uint16_t*>(w_router);
+  lmoe::DenseGemm g{};
+  g.M = int(p->T);
+  g.N = p->E;
+  g.nseg = 1;
+  g.seg[0] = lmoe::GemmSeg{z, f->l, wr, nullptr, f->l, f->l};
+  g.gated = false;
+  g.Cf = logits;
+  g.ldc = p->E;
+  const hipError_t e = c.small ? lmoe::launch_small_dense(&g, 1, s) : lmoe::launch_dense_gemm(g, s);
+  if (e != hipSuccess) return hip_fail(e, "router gate");
+  if ((rc = route_enqueue(p, r, logits, s)) != LMOE_OK) return rc;
+  return fwd_back(c);
+}
+
+// ---------------------------------------------------- no-allocation variant
+// Both workspaces of latent_moe_layer_noalloc live in this array.  Its name
+// is a host-side stand-in: host code uses only the device address that
+// hipGetSymbolAddress returns for the current device (one copy per GPU).
+static __device__ __align__(256) unsigned char scratch[LMOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on `dev` (looked up once per device,
+// with that device current).
+int scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(LMOE_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(LMOE_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logits, const lmoe_forward_args* f,
+                     void* hip_stream, latent_moe_plan** plan_io) {
+  if (!plan_io) return fail(LMOE_EINVAL, "NULL plan_io");
+  int rc = layer_check(r, w_router, logits, f);
+  if (rc) return rc;
+  latent_moe_plan q{};
+  fill_plan(&q, r, w_router == nullptr && r->ids_in != nullptr);
   latent_moe_plan* p = *plan_io;
   const bool fresh = p == nullptr;
   if (fresh) {
@@ -686,43 +771,47 @@ int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logi
   }
   *p = q;
   *plan_io = p;
-  if (q.T == 0) return LMOE_OK;
-
-  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const FwdCtx c = fwd_ctx(p, f, s);
-  auto drop = [&](int code) {
-    if (fresh) {
-      delete p;
-      *plan_io = nullptr;
-    }
-    return code;
-  };
-  if (!gate) {
-    // given logits: at small T the top-k runs in the down-projection's launch
-    // (it reads neither x nor z), leaving only the permutation before the experts
-    const bool fuse = !ids_mode && c.small;
-    if ((rc = fwd_front(c, fuse ? r : nullptr)) != LMOE_OK) return drop(rc);
-    if ((rc = route_enqueue(p, r, r->logits, s, fuse)) != LMOE_OK) return drop(rc);
-    if ((rc = fwd_back(c)) != LMOE_OK) return drop(rc);
-    return LMOE_OK;
+  rc = layer_enqueue(p, r, w_router, logits, f, static_cast<hipStream_t>(hip_stream));
+  if (rc != LMOE_OK && fresh) {
+    delete p;
+    *plan_io = nullptr;
   }
-  if ((rc = fwd_front(c)) != LMOE_OK) return drop(rc);
-  // the router gate on the latent z (in the forward workspace): fp32 logits
-  const uint16_t* z = reinterpret_cast<const uint16_t*>(static_cast<const char*>(f->workspace) + c.L.z);
-  const uint16_t* wr = static_cast<const uint16_t*>(w_router);
-  lmoe::DenseGemm g{};
-  g.M = int(q.T);
-  g.N = q.E;
-  g.nseg = 1;
-  g.seg[0] = lmoe::GemmSeg{z, f->l, wr, nullptr, f->l, f->l};
-  g.gated = false;
-  g.Cf = logits;
-  g.ldc = q.E;
-  const hipError_t e = c.small ? lmoe::launch_small_dense(&g, 1, s) : lmoe::launch_dense_gemm(g, s);
-  if (e != hipSuccess) return drop(hip_fail(e, "router gate"));
-  if ((rc = route_enqueue(p, r, logits, s)) != LMOE_OK) return drop(rc);
-  if ((rc = fwd_back(c)) != LMOE_OK) return drop(rc);
-  return LMOE_OK;
+  return rc;
+}
+
+int latent_moe_layer_noalloc(const lmoe_route_args* r, const void* w_router, float* logits,
+                             const lmoe_forward_args* f, void* hip_stream) {
+  if (!r || !f) return fail(LMOE_EINVAL, "NULL route args or forward args");
+  if (r->workspace || r->workspace_bytes || f->workspace || f->workspace_bytes)
+    return fail(LMOE_EINVAL, "latent_moe_layer_noalloc takes no workspaces (workspace must be NULL, size 0)");
+  if (r->T < 0) return fail(LMOE_EINVAL, "T=%lld < 0", (long long)r->T);
+  const bool gate = w_router != nullptr;
+  const bool ids_mode = !gate && r->ids_in != nullptr;
+  const size_t rws = latent_moe_route_workspace_size(r->T, r->E, r->k);
+  const size_t fws = latent_moe_forward_workspace_size(r->T, r->E, r->k, f->d, f->l, f->I, f->S, f->Is, f->wfmt,
+                                                       f->w_in == nullptr);
+  if (r->T > 0 && (rws == 0 || fws == 0)) return fail(LMOE_EINVAL, "invalid dimensions");
+  const size_t need = align_up(rws) + fws;
+  if (need > size_t(LMOE_NOALLOC_SCRATCH_BYTES))
+    return fail(LMOE_EUNSUPPORTED, "workspaces need %zu bytes, beyond the %zu-byte scratch of latent_moe_layer_noalloc",
+                need, size_t(LMOE_NOALLOC_SCRATCH_BYTES));
+  const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device of the stream");
+  void* base = nullptr;
+  int rc = scratch_on(dev, &base);
+  if (rc) return rc;
+  lmoe_route_args ra = *r;
+  lmoe_forward_args fa = *f;
+  ra.workspace = base;
+  ra.workspace_bytes = align_up(rws);
+  fa.workspace = static_cast<char*>(base) + align_up(rws);
+  fa.workspace_bytes = fws;
+  if ((rc = layer_check(&ra, w_router, logits, &fa)) != LMOE_OK) return rc;
+  latent_moe_plan p{};  // on the stack: no host allocation, no stage events
+  fill_plan(&p, &ra, ids_mode);
+  return layer_enqueue(&p, &ra, w_router, logits, &fa, s);
 }
 
 void latent_moe_free(latent_moe_plan* p) { delete p; }

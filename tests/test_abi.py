@@ -213,3 +213,32 @@ def test_forward_workspace_layout(dims, wfmt, rows):
     with pytest.raises(lm.LatentMoeError):
         lm.latent_moe_forward_workspace_layout(T, E, 0, d, l, I, S, Is, wfmt, rows)
 
+
+def test_noalloc_rejects_workspaces_and_oversized_batches():
+    """latent_moe_layer_noalloc refuses caller workspaces (EINVAL) and batches
+    whose workspaces exceed its static scratch (EUNSUPPORTED) before any HIP
+    call, so this runs without a GPU; the pointers are never dereferenced."""
+    import latentmoe_expert_layer_amd as lm
+    fake = 1 << 20   # 16-byte aligned stand-in addresses, never read
+    T, E, k, d, l, I, S, Is = 256, 896, 16, 512, 256, 256, 2, 256
+
+    def args(T, ws=None):
+        ra = lm.RouteArgs(T=T, E=E, k=k, logits=fake, topk_ids=fake, topk_w=fake, sorted_row=fake, row_pos=fake,
+                          offsets=fake, workspace=ws, workspace_bytes=0 if ws is None else 1 << 30)
+        fa = lm.ForwardArgs(d=d, l=l, I=I, S=S, Is=Is, wfmt=0, norm_eps=1e-6, x=fake, w_in=fake, w1=fake, w3=fake,
+                            w2=fake, norm_w=fake, w_out=fake, ws1=fake, ws3=fake, ws2=fake, y=fake)
+        return ra, fa
+    ra, fa = args(T, ws=fake)
+    with pytest.raises(lm.LatentMoeError) as ei:
+        lm.latent_moe_layer_noalloc(ra, None, None, fa)
+    assert ei.value.code == lm.LMOE_EINVAL
+    big = 4096
+    need = (lm.route_workspace_size(big, E, k) + 255) // 256 * 256 + lm.forward_workspace_size(big, E, k, d, l, I,
+                                                                                            S, Is)
+    assert need > lm.NOALLOC_SCRATCH_BYTES
+    ra, fa = args(big)
+    with pytest.raises(lm.LatentMoeError) as ei:
+        lm.latent_moe_layer_noalloc(ra, None, None, fa)
+    assert ei.value.code == lm.LMOE_EUNSUPPORTED
+    assert "scratch" in str(ei.value)
+
