@@ -344,13 +344,16 @@ def measure(cfg, args, hip, lm, W, torch, stream, clock=None):
     torch.cuda.synchronize()
 
     n_ev = lm.N_STAGE_EVENTS
-    use_events = not args.no_stage_events
+    use_events = not args.no_stage_events and not cfg.os   # the output-stationary call keeps no plan
     one_call = cfg.router_gemm or (args.api == "layer" and not cfg.rows_mode)
 
     def run_call(s, strm, events=None):
         """One layer call on copy s: latent_moe_layer (its plan reused across
-        calls; with the router gate or the given logits) or latent_moe_route +
-        latent_moe_forward."""
+        calls; with the router gate or the given logits), latent_moe_layer_os,
+        or latent_moe_route + latent_moe_forward."""
+        if cfg.os:
+            lm.latent_moe_layer_os(s["ra"], s["fa"], strm)
+            return
         if one_call:
             if s["plan"] is not None:
                 lm.latent_moe_plan_set_stage_events(s["plan"], events)
@@ -462,7 +465,10 @@ def measure(cfg, args, hip, lm, W, torch, stream, clock=None):
     # ---- algorithmic work (per launch, averaged over the copies)
     T, E, k, d, l, I, S, Is = cfg.T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is
     R = T * k
-    touched = sum(int(((s["out"]["offsets"][1:] - s["out"]["offsets"][:-1]) > 0).sum()) for s in sets) / copies
+    if cfg.os:   # no offsets: count the experts the router picked
+        touched = sum(int(torch.unique(s["out"]["topk_ids"]).numel()) for s in sets) / copies
+    else:
+        touched = sum(int(((s["out"]["offsets"][1:] - s["out"]["offsets"][:-1]) > 0).sum()) for s in sets) / copies
     wb = 0.5 + 1 / 32 if cfg.mxfp4 else 2        # bytes per expert weight element (MXFP4: code + scale share)
     fc1_bytes = touched * 2 * I * l * wb + T * l * 2 + R * I * 2
     fc2_bytes = touched * l * I * wb + R * I * 2 + R * l * 2
@@ -524,7 +530,8 @@ def measure(cfg, args, hip, lm, W, torch, stream, clock=None):
         "step_ms": {"median": round(statistics.median(per_step), 5), "p10": round(pct(per_step, 0.1), 5),
                     "p90": round(pct(per_step, 0.9), 5), "min": round(min(per_step), 5),
                     "max": round(max(per_step), 5)},
-        "api": "latent_moe_layer" if one_call else "latent_moe_route + latent_moe_forward",
+        "api": ("latent_moe_layer_os" if cfg.os else
+                "latent_moe_layer" if one_call else "latent_moe_route + latent_moe_forward"),
         "eager_ms_per_step_with_stage_events": None if eager_ms is None else round(eager_ms, 5),
         "copies_cycled": copies, "wall_s": round(wall, 3),
         "stage_us": {n: round(v, 2) for n, v in stages.items()},
@@ -535,7 +542,9 @@ def measure(cfg, args, hip, lm, W, torch, stream, clock=None):
         "layer_algorithmic_bytes": int(layer_bytes), "layer_algorithmic_flop": layer_flop,
         "touched_experts": touched, "roofline": roofline, "shader_clock": clk,
     }
-    if cfg.router_gemm:
+    if cfg.os:
+        res["stage_note"] = "output-stationary call: no permutation; kernel times from the rocprofv3 trace"
+    elif cfg.router_gemm:
         res["stage_note"] = ("shared_gate_up also covers the router gate GEMM, the top-k and the permutation "
                              "(latent_moe_layer runs them between the down-projection and FC1)")
     elif one_call:
@@ -568,7 +577,8 @@ def describe(cfg):
     return (f"{cfg.name}: T={T} tokens, d={d} -> latent {l}, E={E} top-{k} + {S} shared, "
             f"SwiGLU I={I}, shared I={Is}, RMSNorm on"
             + (", logits computed by the router gate on the latent (latent_moe_layer)" if cfg.router_gemm else "")
-            + ((", MXFP4 experts (w4a16)" if cfg.w4a16 else ", MXFP4 experts (w4a8)") if cfg.mxfp4 else ""))
+            + ((", MXFP4 experts (w4a16)" if cfg.w4a16 else ", MXFP4 experts (w4a8)") if cfg.mxfp4 else "")
+            + (", output-stationary experts (latent_moe_layer_os)" if cfg.os else ""))
 
 
 def main():

@@ -231,6 +231,28 @@ int latent_moe_layer(const lmoe_route_args* route, const void* w_router, float* 
                      const lmoe_forward_args* fwd, void* hip_stream, latent_moe_plan** plan_io);
 
 /*
+ * The whole layer for decode-shaped batches, organised around outputs rather
+ * than experts (TokenSpeed Day-0 post, "Gluon kernels on AMD GPUs > Stable
+ * LatentMoE": no route sorting, row padding or gather buffers).  The router's
+ * top-k and softmax run as in latent_moe_layer (logits given); then each
+ * expert-GEMM workgroup owns output columns of one expert and finds that
+ * expert's (token, slot) rows by scanning topk_ids itself.  No permutation or
+ * tile table is built, H and Y are kept in (token, slot) order, and the
+ * combine reads Y there.  Where latent_moe_layer runs its weight-streaming
+ * kernels (T*k <= 32*E, and always for MXFP4 w4a16) the results are equal to
+ * its results bit for bit: each row meets the same MFMAs in the same K order.
+ * Arguments as for latent_moe_layer with the logits given (w_router NULL):
+ *   route   logits != NULL, ids_in == NULL; topk_ids and topk_w receive the
+ *           routing; sorted_row, row_pos, offsets and workspace are not used
+ *   fwd     as for latent_moe_forward; the forward workspace holds z, hs,
+ *           H and Y (rows r = t*k + j) and rhat (same size and layout offsets)
+ * Limits (else LMOE_EUNSUPPORTED, nothing enqueued): T <= 512, T*k <= 8192;
+ * bf16 experts with l and I multiples of 128, or MXFP4 w4a16 experts with
+ * l = I = 256; E <= 1024.  No plan is created.
+ */
+int latent_moe_layer_os(const lmoe_route_args* route, const lmoe_forward_args* fwd, void* hip_stream);
+
+/*
  * latent_moe_layer for callers that cannot allocate: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  It computes
  * exactly what latent_moe_layer computes (the same kernels), except that

@@ -67,6 +67,8 @@ def _load():
     L.latent_moe_layer.argtypes = [ctypes.POINTER(RouteArgs), _vp, _vp, ctypes.POINTER(ForwardArgs), _vp,
                                    ctypes.POINTER(_vp)]
     L.latent_moe_layer.restype = ctypes.c_int
+    L.latent_moe_layer_os.argtypes = [ctypes.POINTER(RouteArgs), ctypes.POINTER(ForwardArgs), _vp]
+    L.latent_moe_layer_os.restype = ctypes.c_int
     L.latent_moe_layer_noalloc.argtypes = [ctypes.POINTER(RouteArgs), _vp, _vp, ctypes.POINTER(ForwardArgs), _vp]
     L.latent_moe_layer_noalloc.restype = ctypes.c_int
     L.latent_moe_free.argtypes = [_vp]
@@ -110,6 +112,11 @@ def latent_moe_layer(route_args: RouteArgs, w_router: int, logits: int, fwd_args
                               _vp(stream), ctypes.byref(h))
     _check(rc)
     return h.value
+
+
+def latent_moe_layer_os(route_args: RouteArgs, fwd_args: ForwardArgs, stream: int = 0):
+    """Calls the C entry point (output-stationary decode layer)."""
+    _check(lib.latent_moe_layer_os(ctypes.byref(route_args), ctypes.byref(fwd_args), _vp(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # LMOE_NOALLOC_SCRATCH_BYTES
@@ -382,6 +389,41 @@ def layer(x: torch.Tensor, w_r: Optional[torch.Tensor], k: int, w1, w3, w2, *, w
     routing.keep = [workspace]
     routing.workspace_fwd = workspace
     return routing, y
+
+
+def layer_os(x: torch.Tensor, logits: torch.Tensor, k: int, w1, w3, w2, *, w_in, w_out, ws1=None, ws3=None,
+             ws2=None, norm_w=None, eps: float = 1e-6, s1=None, s3=None, s2=None, w4a16: bool = False,
+             y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+             I: Optional[int] = None):
+    """The output-stationary decode layer (``latent_moe_layer_os``): returns
+    (topk_ids, topk_w, y, workspace); H and Y in the workspace are in
+    (token, slot) order."""
+    T, dev = x.shape[0], x.device
+    E = logits.shape[1]
+    l, d = w_in.shape
+    if I is None:
+        I = w1.shape[1]
+    S = 0 if ws1 is None else ws1.shape[0]
+    Is = 0 if ws1 is None else ws1.shape[1]
+    wfmt = LMOE_WFMT_MXFP4_W4A16 if w4a16 else LMOE_WFMT_BF16
+    topk_ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    topk_w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    owned = [topk_ids, topk_w]
+    if workspace is None:
+        workspace = torch.empty(max(forward_workspace_size(T, E, k, d, l, I, S, Is, wfmt, False), 256),
+                                dtype=torch.uint8, device=dev)
+        owned.append(workspace)
+    if y is None:
+        y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+        owned.append(y)
+    _guard_owned(stream, owned)
+    ra = RouteArgs(T=T, E=E, k=k, logits=_p(logits), topk_ids=_p(topk_ids), topk_w=_p(topk_w))
+    fa = ForwardArgs(d=d, l=l, I=I, S=S, Is=Is, wfmt=wfmt, norm_eps=eps, x=_p(x), w_in=_p(w_in), w1=_p(w1),
+                     w3=_p(w3), w2=_p(w2), s1=_p(s1), s3=_p(s3), s2=_p(s2), norm_w=_p(norm_w), w_out=_p(w_out),
+                     ws1=_p(ws1), ws3=_p(ws3), ws2=_p(ws2), y=_p(y), workspace=_p(workspace),
+                     workspace_bytes=workspace.numel())
+    latent_moe_layer_os(ra, fa, _stream(stream))
+    return topk_ids, topk_w, y, workspace
 
 
 def run_layer(inp: dict, stream=None, norm=True):

@@ -284,6 +284,7 @@ struct FwdCtx {
   const lmoe_forward_args* a;
   hipStream_t s;
   bool rows, mx, w4a16, small;
+  bool os;  // output-stationary experts: no permutation, H and Y in (token, slot) order
   int32_t S;
   FwdLayout L;
 };
@@ -397,7 +398,62 @@ int fwd_back(const FwdCtx& c) {
   hipEvent_t fc1_t0 = p->timing ? p->events[2] : nullptr, fc1_t1 = p->timing ? p->events[3] : nullptr;
 
   // 2-3. routed experts: grouped FC1 (gated) and FC2 over the permuted rows
-  if (mx) {
+  if (c.os) {
+    // output-stationary: each workgroup finds its expert's rows by scanning
+    // the router's ids; H and Y stay in (token, slot) order
+    if (w4a16) {
+      lmoe::W4Mlp m{};
+      m.A = z;
+      m.lda = l;
+      m.a_row_div = p->k;
+      m.W1 = static_cast<const uint8_t*>(a->w1);
+      m.S1 = a->s1;
+      m.W3 = static_cast<const uint8_t*>(a->w3);
+      m.S3 = a->s3;
+      m.W2 = static_cast<const uint8_t*>(a->w2);
+      m.S2 = a->s2;
+      m.Y = Y;
+      m.ldy = l;
+      m.os_ids = p->ids;
+      m.os_R = R;
+      if ((e = lmoe::launch_w4a16_mlp_os(m, p->E, s, fc1_t0, fc1_t1)) != hipSuccess)
+        return hip_fail(e, "expert MLP (MXFP4 w4a16, output-stationary)");
+    } else {
+      lmoe::GroupedGemm f1{};
+      f1.N = int(I);
+      f1.K = int(l);
+      f1.A = z;
+      f1.lda = l;
+      f1.a_row_div = p->k;
+      f1.B = static_cast<const uint16_t*>(a->w1);
+      f1.B3 = static_cast<const uint16_t*>(a->w3);
+      f1.ldb = l;
+      f1.b_estride = I * l;
+      f1.gated = true;
+      f1.C = H;
+      f1.ldc = I;
+      f1.os_ids = p->ids;
+      f1.os_R = R;
+      if ((e = lmoe::launch_grouped_skinny_os(f1, p->E, s, fc1_t0, fc1_t1)) != hipSuccess)
+        return hip_fail(e, "expert FC1 (output-stationary)");
+      lmoe::GroupedGemm f2 = f1;
+      f2.N = int(l);
+      f2.K = int(I);
+      f2.A = H;
+      f2.lda = I;
+      f2.a_row_div = 1;
+      f2.B = static_cast<const uint16_t*>(a->w2);
+      f2.B3 = nullptr;
+      f2.ldb = I;
+      f2.b_estride = l * I;
+      f2.gated = false;
+      f2.C = Y;
+      f2.ldc = l;
+      if ((e = lmoe::launch_grouped_skinny_os(f2, p->E, s)) != hipSuccess)
+        return hip_fail(e, "expert FC2 (output-stationary)");
+    }
+    if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
+  } else if (mx) {
     // w4a8: MXFP8 activations x MXFP4 weights on the block-scaled MFMA
     uint8_t* zq = reinterpret_cast<uint8_t*>(ws + L.zq);
     uint8_t* zs = reinterpret_cast<uint8_t*>(ws + L.zs);
@@ -550,8 +606,8 @@ int fwd_back(const FwdCtx& c) {
       if ((e = mark(i)) != hipSuccess) return hip_fail(e, "event");
     return LMOE_OK;
   }
-  e = lmoe::launch_combine(Y, p->row_pos, p->w, T, p->k, int(l), static_cast<const uint16_t*>(a->norm_w),
-                           a->norm_eps, rhat, s);
+  e = lmoe::launch_combine(Y, c.os ? nullptr : p->row_pos, p->w, T, p->k, int(l),
+                           static_cast<const uint16_t*>(a->norm_w), a->norm_eps, rhat, s);
   if (e != hipSuccess) return hip_fail(e, "combine");
   if ((e = mark(5)) != hipSuccess) return hip_fail(e, "event");
 
@@ -777,6 +833,45 @@ int latent_moe_layer(const lmoe_route_args* r, const void* w_router, float* logi
     *plan_io = nullptr;
   }
   return rc;
+}
+
+int latent_moe_layer_os(const lmoe_route_args* r, const lmoe_forward_args* f, void* hip_stream) {
+  if (!r || !f) return fail(LMOE_EINVAL, "NULL route args or forward args");
+  if (!r->logits || r->ids_in) return fail(LMOE_EINVAL, "latent_moe_layer_os takes router logits (logits != NULL, ids_in == NULL)");
+  int rc = check_route_dims(r->T, r->E, r->k, false);
+  if (rc) return rc;
+  if (!f->w_in) return fail(LMOE_EINVAL, "latent_moe_layer_os needs the projections (w_in != NULL)");
+  latent_moe_plan q{};
+  q.T = r->T;
+  q.E = r->E;
+  q.k = r->k;
+  q.ids = r->topk_ids;
+  q.w = r->topk_w;
+  if ((rc = fwd_check(&q, f)) != LMOE_OK) return rc;
+  if (r->T == 0) return LMOE_OK;
+  if (r->T > lmoe::kSmallM)
+    return fail(LMOE_EUNSUPPORTED, "latent_moe_layer_os serves decode-shaped batches (T=%lld > %d)",
+                (long long)r->T, lmoe::kSmallM);
+  if (r->T * r->k > lmoe::kOsMaxRows)
+    return fail(LMOE_EUNSUPPORTED, "latent_moe_layer_os: T*k=%lld > %d", (long long)(r->T * r->k), lmoe::kOsMaxRows);
+  if (f->wfmt == LMOE_WFMT_BF16) {
+    if (f->l % 128 || f->I % 128)
+      return fail(LMOE_EUNSUPPORTED, "latent_moe_layer_os with bf16 experts needs l and I multiples of 128");
+  } else if (f->wfmt == LMOE_WFMT_MXFP4_W4A16) {
+    if (f->l != lmoe::kW4MlpWidth || f->I != lmoe::kW4MlpWidth)
+      return fail(LMOE_EUNSUPPORTED, "latent_moe_layer_os with MXFP4 w4a16 experts needs l = I = %d",
+                  lmoe::kW4MlpWidth);
+  } else {
+    return fail(LMOE_EUNSUPPORTED, "latent_moe_layer_os runs bf16 or MXFP4 w4a16 experts");
+  }
+  if (!r->topk_ids || !r->topk_w) return fail(LMOE_EINVAL, "NULL topk_ids or topk_w");
+  if (!aligned16(r->logits) || !aligned16(r->topk_ids) || !aligned16(r->topk_w))
+    return fail(LMOE_EINVAL, "logits, topk_ids and topk_w must be 16-byte aligned");
+  FwdCtx c = fwd_ctx(&q, f, static_cast<hipStream_t>(hip_stream));
+  c.os = true;
+  // the router's top-k runs in the down-projection's launch (small batches)
+  if ((rc = fwd_front(c, r)) != LMOE_OK) return rc;
+  return fwd_back(c);
 }
 
 int latent_moe_layer_noalloc(const lmoe_route_args* r, const void* w_router, float* logits,

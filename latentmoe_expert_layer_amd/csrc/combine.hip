@@ -10,6 +10,7 @@
 // wave owns one row).
 //
 //   c[t]   = sum_{j<k} w[t,j] * Y[row_pos[t*k+j]]     fp32, j ascending
+//            (row_pos == NULL: Y is in (token, slot) order, row t*k+j)
 //   out[t] = bf16(c * (1/sqrt(mean(c^2) + eps)) * gain)  or bf16(c) without gain
 #include "common.h"
 #include "kernels.h"
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
   int32_t my_p = 0;
   float my_w = 0.0f;
   if (lane < k) {
-    my_p = row_pos[t * k + lane];
+    my_p = row_pos ? row_pos[t * k + lane] : int32_t(t * k + lane);
     my_w = w[t * k + lane];
   }
   float ss = 0.0f;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void combine_reg_kernel(const bf16_t* __restri
   int32_t my_p = 0;
   float my_w = 0.0f;
   if (live && lane < k) {
-    my_p = row_pos[t * k + lane];
+    my_p = row_pos ? row_pos[t * k + lane] : int32_t(t * k + lane);
     my_w = w[t * k + lane];
   }
   float acc[NC][VEC];
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const bf16_t* __restrict
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t r = int64_t(blockIdx.x) * 4 + wid;
   if (r >= R) return;
-  const int64_t p = row_pos[r];
+  const int64_t p = row_pos ? int64_t(row_pos[r]) : r;
   const float wr = w[r];
   const int nch = l / (64 * VEC);
   for (int c0 = 0; c0 < nch; c0 += kChunks) {

@@ -112,8 +112,21 @@ struct GroupedGemm {
   const Tile* tiles;
   const int32_t* ntiles;
   int64_t max_tiles;
+  // output-stationary launches (no tile table): the routed expert of every
+  // (token, slot) row r = t*k + j, and the row count
+  const int32_t* os_ids;
+  int64_t os_R;
 };
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// Output-stationary decode (TokenSpeed Day-0 post, "Gluon kernels on AMD GPUs >
+// Stable LatentMoE": organised around outputs, no route sorting, padding or
+// gather buffers): workgroup (expert e, 64 output columns) finds the rows r
+// with os_ids[r] == e by scanning os_ids and computes C[r, cols] =
+// A[r / a_row_div] * B_e^T (gated: SwiGLU) for them, 16 rows at a time, in
+// (token, slot) order.  K a multiple of 128; os_R <= kOsMaxRows.
+constexpr int kOsMaxRows = 8192;
+hipError_t launch_grouped_skinny_os(const GroupedGemm& g, int E, hipStream_t s, hipEvent_t t0 = nullptr,
+                                    hipEvent_t t1 = nullptr);
 hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // Grouped, decode-shaped, MXFP4 weights with bf16 activations (w4a16): as
@@ -158,8 +171,14 @@ struct W4Mlp {
   const Tile* tiles;
   const int32_t* ntiles;
   int64_t max_tiles;
+  const int32_t* os_ids;  // output-stationary launches, as in GroupedGemm
+  int64_t os_R;
 };
 hipError_t launch_w4a16_mlp(const W4Mlp& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// The same MLP output-stationary: one workgroup per expert, rows found by
+// scanning os_ids, Y in (token, slot) order.
+hipError_t launch_w4a16_mlp_os(const W4Mlp& g, int E, hipStream_t s, hipEvent_t t0 = nullptr,
+                               hipEvent_t t1 = nullptr);
 
 // ---- MXFP4 (w4a8) expert path ------------------------------------------------
 // bf16 [rows, K] -> MXFP8 e4m3 codes [rows, K] + e8m0 scales [rows, K/32].
@@ -192,7 +211,8 @@ struct GroupedMx {
 hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // ---- combine ----------------------------------------------------------------
-// out[t] = bf16(RMSNorm(sum_j w[t,j] Y[row_pos[t*k+j]]))   (norm skipped if gain == NULL)
+// out[t] = bf16(RMSNorm(sum_j w[t,j] Y[row_pos[t*k+j]]))   (norm skipped if gain == NULL;
+// row_pos == NULL: Y rows in (token, slot) order)
 hipError_t launch_combine(const uint16_t* Y, const int32_t* row_pos, const float* w, int64_t T, int k,
                           int l, const uint16_t* gain, float eps, uint16_t* out, hipStream_t s);
 

@@ -7,10 +7,94 @@
 // operands go straight from registers into the MFMAs, with no LDS.
 #include "common.h"
 #include "kernels.h"
+#include "permute_core.h"
 
 namespace lmoe {
 
 namespace {
+
+// ------------------------------------------------- output-stationary rows ---
+// The rows of one expert, found without a permutation: thread t of the
+// 256-thread workgroup looks at ids [t*per, t*per + per) (per a multiple of 4,
+// at most 32), keeps a bit mask of the ones equal to the expert, and a block
+// scan of the counts gives each thread the rank of its first match, so the
+// rows come out in ascending r (the order the permutation would give).  Ids
+// past R are -1 and never match.
+struct OsRows {
+  uint32_t mask;  // matches among this thread's ids
+  int32_t pre;    // matches in the threads before this one
+  int32_t n;      // matches in the batch
+  int32_t base;   // first id index of this thread
+};
+
+// The ids this thread looks at, loaded (positions past R read as -1).  Split
+// from the ranking below so that a kernel can issue these loads, then its
+// weight loads (which do not depend on the rows), and rank while both are
+// in flight.
+struct OsIds {
+  int4 v[8];
+  int per, base;
+};
+
+__device__ __forceinline__ OsIds os_load(const int32_t* __restrict__ ids, int64_t R) {
+  OsIds d;
+  d.per = int(((R + 1023) / 1024) * 4);  // ids per thread: 4 * ceil(R / 1024) <= 32
+  d.base = int(threadIdx.x) * d.per;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    d.v[q] = int4{-1, -1, -1, -1};
+    const int64_t r = int64_t(d.base) + 4 * q;
+    if (4 * q < d.per) {
+      if (r + 3 < R) {
+        d.v[q] = *reinterpret_cast<const int4*>(ids + r);
+      } else {
+        if (r < R) d.v[q].x = ids[r];
+        if (r + 1 < R) d.v[q].y = ids[r + 1];
+        if (r + 2 < R) d.v[q].z = ids[r + 2];
+      }
+    }
+  }
+  return d;
+}
+
+__device__ __forceinline__ OsRows os_rank(const OsIds& d, int e, int32_t* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  OsRows o{};
+  o.base = d.base;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    o.mask |= uint32_t(d.v[q].x == e) << (4 * q) | uint32_t(d.v[q].y == e) << (4 * q + 1) |
+              uint32_t(d.v[q].z == e) << (4 * q + 2) | uint32_t(d.v[q].w == e) << (4 * q + 3);
+  const int cnt = __popc(o.mask);
+  const int incl = wave_incl_scan(cnt);
+  if (lane == 63) red[wid] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int v = red[w];
+    before += w < wid ? v : 0;
+    total += v;
+  }
+  o.pre = before + incl - cnt;
+  o.n = total;
+  return o;
+}
+
+// Rows of ranks [c0, c0 + 16) of the scan into lst[0..15].
+__device__ __forceinline__ void os_chunk(const OsRows& o, int c0, int32_t* lst) {
+  const int cnt = __popc(o.mask);
+  if (cnt && o.pre < c0 + 16 && o.pre + cnt > c0) {
+    uint32_t m = o.mask;
+    int rank = o.pre;
+    while (m) {
+      const int b = __builtin_ctz(m);
+      if (rank >= c0 && rank < c0 + 16) lst[rank - c0] = o.base + b;
+      ++rank;
+      m &= m - 1;
+    }
+  }
+}
 
 // ---------------------------------------------------------- skinny grouped ---
 // Block = (m-tile of <= 16 rows, 64*NS output columns); wave w owns NS
@@ -122,60 +206,103 @@ __device__ __forceinline__ f32x4 lds_chunk_mfma(uint4* L, int lane, uint4 v0, ui
   return acc;
 }
 
-template <bool GATED, int NCH>
+// OS: the output-stationary form (no tile table): the grid is experts x
+// column blocks, each workgroup scans the routed ids for its expert's rows
+// and runs them 16 at a time; rows are written at their (token, slot) index.
+template <bool GATED, int NCH, bool OS = false>
 __global__ __launch_bounds__(256) void skinny_lds_kernel(GroupedGemm g) {
   __shared__ uint4 lds[4][16 * 17];
+  __shared__ int32_t os_lst[OS ? 16 : 1];
+  __shared__ int32_t os_red[OS ? 4 : 1];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tiles_n = g.N / 64;
   const int tm = int(blockIdx.x / uint32_t(tiles_n)), tn = int(blockIdx.x % uint32_t(tiles_n));
-  const int ntiles = *g.ntiles;
-  const Tile tl = g.tiles[tm];  // tm < max_tiles: inside the table even past the real count
-  if (tm >= ntiles) return;
-  const int64_t pos = int64_t(tl.row_start) + min(lane & 15, tl.nrows - 1);
-  int32_t sr = 0;
-  if (g.a_rows) sr = g.a_rows[pos];
-  const int64_t wb = int64_t(tl.expert) * g.b_estride + int64_t(tn * 64 + wid * 16) * g.ldb;
-  const int64_t lofs = (lane >> 4) * (g.ldb / 8) + (lane & 15);  // in uint4
-  const uint4* gp = reinterpret_cast<const uint4*>(g.B + wb) + lofs;
-  const uint4* up = GATED ? reinterpret_cast<const uint4*>(g.B3 + wb) + lofs : nullptr;
-  const int64_t rs = 4 * (g.ldb / 8);  // 4 rows, in uint4
-  uint4* L = lds[wid];
-  const bf16_t* ap = nullptr;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
-  for (int kc = 0; kc < g.K; kc += 128 * NCH) {
-    uint4 gv[NCH][4], uv[NCH][GATED ? 4 : 1], a[NCH][4];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        gv[c][j] = gp[j * rs + (kc + 128 * c) / 8];
-        if constexpr (GATED) uv[c][j] = up[j * rs + (kc + 128 * c) / 8];
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    if (kc == 0) ap = g.A + (g.a_rows ? int64_t(sr / g.a_row_div) : pos) * g.lda + (lane >> 4) * 8;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a[c][s] = ldg16(ap + kc + 128 * c + 32 * s);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      acc = lds_chunk_mfma(L, lane, gv[c][0], gv[c][1], gv[c][2], gv[c][3], a[c][0], a[c][1], a[c][2], a[c][3], acc);
-      if constexpr (GATED)
-        acc3 = lds_chunk_mfma(L, lane, uv[c][0], uv[c][1], uv[c][2], uv[c][3], a[c][0], a[c][1], a[c][2], a[c][3],
-                              acc3);
-    }
+  int expert;
+  Tile tl{};
+  OsRows o{};
+  OsIds oid;
+  if constexpr (OS) {
+    expert = tm;
+    oid = os_load(g.os_ids, g.os_R);  // ranked below, once the first weight loads are out
+  } else {
+    const int ntiles = *g.ntiles;
+    tl = g.tiles[tm];  // tm < max_tiles: inside the table even past the real count
+    if (tm >= ntiles) return;
+    expert = tl.expert;
   }
-  const int nb = tn * 64 + wid * 16 + (lane & 15);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = (lane >> 4) * 4 + r;
-    if (row < tl.nrows) {
-      float v = acc[r];
-      if constexpr (GATED) v = silu_mul(v, acc3[r]);
-      g.C[(int64_t(tl.row_start) + row) * g.ldc + nb] = f32_to_bf16(v);
+  for (int c0 = 0;; c0 += 16) {
+    int nrows = 0;
+    int64_t pos = 0;
+    int32_t sr = 0;
+    if constexpr (!OS) {
+      nrows = tl.nrows;
+      pos = int64_t(tl.row_start) + min(lane & 15, tl.nrows - 1);
+      if (g.a_rows) sr = g.a_rows[pos];
     }
+    const int64_t wb = int64_t(expert) * g.b_estride + int64_t(tn * 64 + wid * 16) * g.ldb;
+    const int64_t lofs = (lane >> 4) * (g.ldb / 8) + (lane & 15);  // in uint4
+    const uint4* gp = reinterpret_cast<const uint4*>(g.B + wb) + lofs;
+    const uint4* up = GATED ? reinterpret_cast<const uint4*>(g.B3 + wb) + lofs : nullptr;
+    const int64_t rs = 4 * (g.ldb / 8);  // 4 rows, in uint4
+    uint4* L = lds[wid];
+    const bf16_t* ap = nullptr;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
+    for (int kc = 0; kc < g.K; kc += 128 * NCH) {
+      uint4 gv[NCH][4], uv[NCH][GATED ? 4 : 1], a[NCH][4];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          gv[c][j] = gp[j * rs + (kc + 128 * c) / 8];
+          if constexpr (GATED) uv[c][j] = up[j * rs + (kc + 128 * c) / 8];
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kc == 0) {
+        if constexpr (OS) {
+          // the weights are in flight: rank this expert's rows (first chunk
+          // only), then this chunk's list
+          if (c0 == 0) {
+            o = os_rank(oid, expert, os_red);
+            if (o.n == 0) return;  // the whole workgroup: an expert no row picked
+          }
+          os_chunk(o, c0, os_lst);
+          __syncthreads();
+          nrows = min(16, o.n - c0);
+          sr = os_lst[min(lane & 15, nrows - 1)];
+          ap = g.A + int64_t(sr / g.a_row_div) * g.lda + (lane >> 4) * 8;
+        } else {
+          ap = g.A + (g.a_rows ? int64_t(sr / g.a_row_div) : pos) * g.lda + (lane >> 4) * 8;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a[c][s] = ldg16(ap + kc + 128 * c + 32 * s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        acc = lds_chunk_mfma(L, lane, gv[c][0], gv[c][1], gv[c][2], gv[c][3], a[c][0], a[c][1], a[c][2], a[c][3],
+                             acc);
+        if constexpr (GATED)
+          acc3 = lds_chunk_mfma(L, lane, uv[c][0], uv[c][1], uv[c][2], uv[c][3], a[c][0], a[c][1], a[c][2],
+                                a[c][3], acc3);
+      }
+    }
+    const int nb = tn * 64 + wid * 16 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = (lane >> 4) * 4 + r;
+      if (row < nrows) {
+        float v = acc[r];
+        if constexpr (GATED) v = silu_mul(v, acc3[r]);
+        const int64_t orow = OS ? int64_t(os_lst[row]) : int64_t(tl.row_start) + row;
+        g.C[orow * g.ldc + nb] = f32_to_bf16(v);
+      }
+    }
+    if constexpr (!OS) break;
+    if (c0 + 16 >= o.n) break;
+    __syncthreads();  // every wave is done with this chunk's row list
   }
 }
 
@@ -306,16 +433,31 @@ __global__ __launch_bounds__(256) void skinny_w4a16_kernel(GroupedW4 g) {
 //   chunks 4, 5 (FC2): K chunk c-4; slot i = Y subtile i (16 columns).
 // The K order within a 128-wide chunk is skinny_w4a16_kernel's, so H and Y
 // are bit-identical to that two-launch path.
+// OS: the output-stationary form, one workgroup per expert, its rows found by
+// scanning the routed ids (16 at a time), Y written at (token, slot) rows.
+template <bool OS = false>
 __global__ __launch_bounds__(256) void skinny_w4a16_mlp_kernel(W4Mlp g) {
   constexpr int L = 256, IM = 256, ZS = L + 8, HS = IM + 8;  // padded LDS rows (bf16)
   static_assert(L == kW4MlpWidth && IM == kW4MlpWidth, "the chunk layout below is for 256 x 256");
   __shared__ bf16_t Zs[16 * ZS];
   __shared__ bf16_t Hs[16 * HS];
+  __shared__ int32_t os_lst[OS ? 16 : 1];
+  __shared__ int32_t os_red[OS ? 4 : 1];
   const int lane = threadIdx.x & 63, gq = lane >> 4, n16 = lane & 15;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, so row bases stay scalar
-  if (int(blockIdx.x) >= *g.ntiles) return;
-  const Tile tl = g.tiles[blockIdx.x];
-  const int64_t e1 = int64_t(tl.expert) * IM, e2 = int64_t(tl.expert) * L;
+  int expert;
+  Tile tl{};
+  OsRows o{};
+  OsIds oid;
+  if constexpr (OS) {
+    expert = int(blockIdx.x);
+    oid = os_load(g.os_ids, g.os_R);  // ranked below, once the first weight loads are out
+  } else {
+    if (int(blockIdx.x) >= *g.ntiles) return;
+    tl = g.tiles[blockIdx.x];
+    expert = tl.expert;
+  }
+  const int64_t e1 = int64_t(expert) * IM, e2 = int64_t(expert) * L;
   // code rows are K/2 = 128 bytes and scale rows K/32 = 8 bytes for both
   // GEMMs; each load is a wave-uniform row base plus a 32-bit lane offset
   const uint32_t coff = uint32_t(n16) * 128u + 16u * uint32_t(gq), soff = uint32_t(n16) * 8u;
@@ -331,6 +473,8 @@ __global__ __launch_bounds__(256) void skinny_w4a16_mlp_kernel(W4Mlp g) {
       sc[i] = *reinterpret_cast<const uint32_t*>(sb + (soff + 4u * uint32_t(kc)));  // byte gq is this lane's
     }
   };
+  for (int c0 = 0;; c0 += 16) {
+  int nrows = OS ? 0 : tl.nrows;
   // FC1: acc[2j] gate and acc[2j+1] up of H subtile j; FC2: acc[j] of Y subtile j
   f32x4 acc[4];
 #pragma unroll
@@ -364,8 +508,10 @@ __global__ __launch_bounds__(256) void skinny_w4a16_mlp_kernel(W4Mlp g) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = 4 * gq + r;
-            if (row < tl.nrows)
-              g.Y[(int64_t(tl.row_start) + row) * g.ldy + wid * (L / 4) + 16 * j + n16] = f32_to_bf16(acc[j][r]);
+            if (row < nrows) {
+              const int64_t orow = OS ? int64_t(os_lst[row]) : int64_t(tl.row_start) + row;
+              g.Y[orow * g.ldy + wid * (L / 4) + 16 * j + n16] = f32_to_bf16(acc[j][r]);
+            }
           }
       }
 #pragma unroll
@@ -376,11 +522,27 @@ __global__ __launch_bounds__(256) void skinny_w4a16_mlp_kernel(W4Mlp g) {
   uint32_t s0[4], s1[4];
   load(w0, s0, 0);
   load(w1, s1, 1);
+  if constexpr (OS) {
+    // the first weight chunks are in flight: rank this expert's rows (first
+    // chunk only), then this chunk's list
+    if (c0 == 0) {
+      o = os_rank(oid, expert, os_red);
+      if (o.n == 0) return;
+    }
+    os_chunk(o, c0, os_lst);
+    __syncthreads();
+    nrows = min(16, o.n - c0);
+  }
   // the tile's z rows (gathered) into LDS while the first two chunks load
   for (int i = threadIdx.x; i < 16 * (L / 8); i += 256) {
     const int r = i / (L / 8), cq = i % (L / 8);
-    int64_t src = int64_t(tl.row_start) + min(r, tl.nrows - 1);
-    if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
+    int64_t src;
+    if constexpr (OS) {
+      src = os_lst[min(r, nrows - 1)] / g.a_row_div;
+    } else {
+      src = int64_t(tl.row_start) + min(r, tl.nrows - 1);
+      if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
+    }
     *reinterpret_cast<uint4*>(&Zs[r * ZS + cq * 8]) = ldg16(g.A + src * g.lda + cq * 8);
   }
   __syncthreads();
@@ -394,6 +556,10 @@ __global__ __launch_bounds__(256) void skinny_w4a16_mlp_kernel(W4Mlp g) {
   load(w1, s1, 5);
   compute(w0, s0, 4);
   compute(w1, s1, 5);
+  if constexpr (!OS) break;
+  if (c0 + 16 >= o.n) break;
+  __syncthreads();  // every wave is done with this chunk's rows (Zs, Hs, the list)
+  }
 }
 
 }  // namespace
@@ -425,7 +591,25 @@ hipError_t launch_grouped_w4a16(const GroupedW4& g, hipStream_t s, hipEvent_t t0
 
 hipError_t launch_w4a16_mlp(const W4Mlp& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   if (g.max_tiles <= 0) return hipSuccess;
-  return launch_kernel((const void*)skinny_w4a16_mlp_kernel, dim3{uint32_t(g.max_tiles)}, dim3{256}, 0, s, g, t0, t1);
+  return launch_kernel((const void*)skinny_w4a16_mlp_kernel<false>, dim3{uint32_t(g.max_tiles)}, dim3{256}, 0, s, g,
+                       t0, t1);
+}
+
+hipError_t launch_w4a16_mlp_os(const W4Mlp& g, int E, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (g.os_R <= 0 || E <= 0) return hipSuccess;
+  if (g.os_R > kOsMaxRows || !g.os_ids) return hipErrorInvalidValue;
+  return launch_kernel((const void*)skinny_w4a16_mlp_kernel<true>, dim3{uint32_t(E)}, dim3{256}, 0, s, g, t0, t1);
+}
+
+hipError_t launch_grouped_skinny_os(const GroupedGemm& g, int E, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  if (g.os_R <= 0 || E <= 0) return hipSuccess;
+  if (g.os_R > kOsMaxRows || !g.os_ids || g.K % 128 != 0 || g.N % 64 != 0) return hipErrorInvalidValue;
+  const dim3 grid{uint32_t(int64_t(E) * (g.N / 64))}, block{256};
+  const void* kern = g.gated ? (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<true, 2, true>
+                                               : (const void*)skinny_lds_kernel<true, 1, true>)
+                             : (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<false, 2, true>
+                                               : (const void*)skinny_lds_kernel<false, 1, true>);
+  return launch_kernel(kern, grid, block, 0, s, g, t0, t1);
 }
 
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {

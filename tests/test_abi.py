@@ -242,3 +242,30 @@ def test_noalloc_rejects_workspaces_and_oversized_batches():
     assert ei.value.code == lm.LMOE_EUNSUPPORTED
     assert "scratch" in str(ei.value)
 
+
+def test_output_stationary_layer_refusals():
+    """latent_moe_layer_os refuses what it does not serve before any HIP call
+    (no GPU needed; the stand-in pointers are never read)."""
+    import latentmoe_expert_layer_amd as lm
+    fake = 1 << 20
+    ws_big = 1 << 40
+
+    def args(T=256, E=896, k=16, l=256, I=256, wfmt=0, logits=True):
+        ra = lm.RouteArgs(T=T, E=E, k=k, logits=fake if logits else None, ids_in=None if logits else fake,
+                          weights_in=None if logits else fake, topk_ids=fake, topk_w=fake)
+        fa = lm.ForwardArgs(d=512, l=l, I=I, S=2, Is=256, wfmt=wfmt, norm_eps=1e-6, x=fake, w_in=fake, w1=fake,
+                            w3=fake, w2=fake, s1=fake, s3=fake, s2=fake, norm_w=fake, w_out=fake, ws1=fake,
+                            ws3=fake, ws2=fake, y=fake, workspace=fake, workspace_bytes=ws_big)
+        return ra, fa
+    cases = [(dict(logits=False, k=1), lm.LMOE_EINVAL),
+             (dict(T=600), lm.LMOE_EUNSUPPORTED),                  # beyond a decode batch
+             (dict(T=512, k=17, E=896), lm.LMOE_EUNSUPPORTED),     # T*k > 8192
+             (dict(wfmt=lm.LMOE_WFMT_MXFP4), lm.LMOE_EUNSUPPORTED),
+             (dict(wfmt=lm.LMOE_WFMT_MXFP4_W4A16, l=384), lm.LMOE_EUNSUPPORTED),
+             (dict(l=192, I=128), lm.LMOE_EUNSUPPORTED)]
+    for kw, code in cases:
+        ra, fa = args(**kw)
+        with pytest.raises(lm.LatentMoeError) as ei:
+            lm.latent_moe_layer_os(ra, fa)
+        assert ei.value.code == code, (kw, ei.value)
+

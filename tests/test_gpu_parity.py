@@ -13,7 +13,7 @@ import torch
 import oracle
 import workloads as W
 from tests.gpu_helpers import check_layer, check_routing, gpu_route, run_gpu_layer
-from tests.parity import assert_parity, assert_w4a8, log, poison_, to_device, to_host
+from tests.parity import assert_intermediate, assert_parity, assert_w4a8, log, poison_, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -611,3 +611,63 @@ def test_layer_with_given_logits_equals_route_then_forward(name, dims):
         torch.cuda.synchronize()
         assert torch.equal(y2.view(torch.int16), y_ref.view(torch.int16)), f"replay {rep} differs"
         del junk
+
+
+# ------------------------------------ output-stationary decode (no permutation)
+OS_LAYERS = [
+    ("decode", None),
+    ("decode_w4a16", None),
+    # ragged T, experts without rows
+    ("os_ragged", dict(T=77, d=128, l=256, E=40, k=8, S=2, I=128, Is=64)),
+    # FC1 K = 384 (one 128-wide chunk per batch), FC2 K = 256
+    ("os_l384", dict(T=100, d=256, l=384, E=64, k=4, S=1, I=256, Is=128)),
+    # the row limit: 512 tokens x 16 = 8192 rows (32 ids per scanning thread), 8 chunks of 16 per expert
+    ("os_limit", dict(T=512, d=64, l=256, E=64, k=16, S=0, I=128, Is=0)),
+    # one token (4 ids per scanning thread, most threads empty)
+    ("os_single", dict(T=1, d=128, l=128, E=16, k=4, S=1, I=128, Is=64)),
+    ("os_w4_ragged", dict(T=77, d=128, l=256, E=40, k=8, S=2, I=256, Is=64, mxfp4=True, w4a16=True)),
+]
+
+
+@pytest.mark.parametrize("skew", [False, True], ids=["spread", "skewed"])
+@pytest.mark.parametrize("name,dims", OS_LAYERS, ids=[n for n, _ in OS_LAYERS])
+def test_output_stationary_layer_equals_permuted_path(name, dims, skew):
+    """latent_moe_layer_os against route + forward: routing, y, and H / Y row
+    by row ((token, slot) order against permuted order) bit for bit, then the
+    oracle bar on y.  skewed: four experts get most rows (many 16-row chunks
+    per workgroup)."""
+    cfg = W.CONFIGS[name] if dims is None else W.custom(name, **dims)
+    log(f"output-stationary {name} skew={skew}: {cfg}")
+    inp = W.make_inputs(cfg)
+    if skew:
+        inp["logits"][:, :4] += 6.0
+    inp_dev = to_device(inp)
+    r_ref, y_ref, views_ref = run_gpu_layer(inp_dev)
+    mx = cfg.mxfp4
+    w1, w3, w2 = (inp_dev[n + ("q" if mx else "")] for n in ("w1", "w3", "w2"))
+    wfmt = lm.LMOE_WFMT_MXFP4_W4A16 if mx else lm.LMOE_WFMT_BF16
+    ws = poison_(torch.empty(lm.forward_workspace_size(cfg.T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is,
+                                                       wfmt), dtype=torch.uint8, device="cuda"))
+    y = poison_(torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device="cuda"))
+    ids, w, y, ws = lm.layer_os(inp_dev["x"], inp_dev["logits"], cfg.k, w1, w3, w2, w_in=inp_dev["w_in"],
+                                w_out=inp_dev["w_out"], ws1=inp_dev.get("ws1"), ws3=inp_dev.get("ws3"),
+                                ws2=inp_dev.get("ws2"), norm_w=inp_dev.get("norm_w"), eps=cfg.eps,
+                                s1=inp_dev.get("s1"), s3=inp_dev.get("s3"), s2=inp_dev.get("s2"), w4a16=mx,
+                                I=cfg.I, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, r_ref.topk_ids) and torch.equal(w, r_ref.topk_w), "routing differs"
+    views = lm.workspace_views(ws, cfg.T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is, wfmt)
+    rp = r_ref.row_pos.long()
+    if mx or cfg.T * cfg.k <= 32 * cfg.E:
+        # the permuted path ran the weight-streaming kernels: same MFMAs, same K order
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), "y differs from the permuted path"
+        for n in ("H", "Y"):
+            if n in views:
+                assert torch.equal(views[n].view(torch.int16), views_ref[n][rp].view(torch.int16)), f"{n} differs"
+    else:
+        # the permuted path ran the LDS-tiled kernels (another MFMA shape and K order)
+        for n in ("H", "Y"):
+            assert_intermediate(views[n].cpu(), views_ref[n][rp].cpu(), n)
+    ref = oracle.run(inp, act_quant=False)
+    assert torch.equal(ids.cpu(), ref["ids"])
+    assert_parity(y.cpu(), ref["y"])

@@ -53,6 +53,7 @@ class LayerConfig:
     eps: float = 1e-6
     zipf_s: float = 0.0       # rows mode: Zipf exponent of the expert load
     seed: int = 0
+    os: bool = False          # run through the output-stationary layer call (same inputs)
 
 
 CONFIGS = {
@@ -71,6 +72,10 @@ CONFIGS = {
     # the decode batch with MXFP4 routed experts and bf16 activations (w4a16)
     "decode_w4a16": LayerConfig("decode_w4a16", T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256,
                                 mxfp4=True, w4a16=True),
+    # the decode batches through the output-stationary layer call (no permutation)
+    "decode_os": LayerConfig("decode_os", T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256, os=True),
+    "decode_w4a16_os": LayerConfig("decode_w4a16_os", T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256,
+                                   mxfp4=True, w4a16=True, os=True),
     # the decode shape with the router's logits computed from the latent (gate [E,l])
     "decode_gate": LayerConfig("decode_gate", T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256,
                                router_gemm=True),
