@@ -40,7 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the w4a8 expert GEMMs issue at the fp8 rate)
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 METRIC = "LatentMoE layer tokens/s at 1 GPU; grouped-GEMM TFLOP/s as % MFMA peak"
-DEFAULT_EXTRA = "decode,prefill_mxfp4,ep_share"
+DEFAULT_EXTRA = "prefill@tiled,decode,decode_os,decode_w4a16,decode_w4a16_os,prefill_mxfp4,ep_share"
 
 
 def parse():
@@ -50,7 +50,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--extra-workloads", default=DEFAULT_EXTRA,
-                    help="comma-separated workloads also measured and reported under extra.workloads ('' = none)")
+                    help="comma-separated workloads also measured and reported under extra.workloads ('' = none); "
+                         "name@rows / name@tiled overrides --wlayout for one of them")
+    ap.add_argument("--wlayout", choices=["tiled", "rows"], default="rows",
+                    help="bf16 expert weights: tile-packed once at load time (latent_moe_pack_weights, outside the "
+                         "timed region) or row-major; shapes the packed layout does not serve stay row-major")
     ap.add_argument("--copies", type=int, default=0, help="input copies cycled (0 = enough to beat the LLC)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle budget (0 = skip)")
     ap.add_argument("--no-stage-events", action="store_true")
@@ -295,10 +299,17 @@ def cpu_single_thread(names, budget_s):
     return out
 
 
-def measure(cfg, args, hip, lm, W, torch, stream, clock=None):
+def packed_layout_serves(cfg):
+    """The tile-packed layout serves bf16 experts with l and I multiples of
+    128, at least 256."""
+    return (not cfg.mxfp4) and cfg.l % 128 == 0 and cfg.I % 128 == 0 and cfg.l >= 256 and cfg.I >= 256
+
+
+def measure(cfg, args, hip, lm, W, torch, stream, clock=None, wlayout="tiled"):
     """Builds the resident input copies of ``cfg``, times K steps (graph
     replays, one event per step boundary), then an eager pass with the
     library's stage events; returns the figures of this workload."""
+    packed = wlayout == "tiled" and packed_layout_serves(cfg)
     wbytes = (3 * cfg.E * cfg.I * cfg.l) * (0.53 if cfg.mxfp4 else 2)
     copies = args.copies or max(2, min(8, -(-2 * LLC_BYTES // max(int(wbytes), 1))))
     wfmt = (lm.LMOE_WFMT_MXFP4_W4A16 if cfg.w4a16 else lm.LMOE_WFMT_MXFP4) if cfg.mxfp4 else lm.LMOE_WFMT_BF16
@@ -306,6 +317,9 @@ def measure(cfg, args, hip, lm, W, torch, stream, clock=None):
     sets = []
     for c in range(copies):
         inp = W.make_inputs(W.LayerConfig(**{**cfg.__dict__, "seed": c}), device="cuda")
+        if packed:   # load-time layout change of the expert weights (same values)
+            for n in ("w1", "w3", "w2"):
+                inp[n] = lm.pack_weights(inp[n])
         T, E, k = cfg.T, cfg.E, cfg.k
         R = T * k
         rws = torch.empty(lm.route_workspace_size(T, E, k), dtype=torch.uint8, device="cuda")
@@ -339,7 +353,8 @@ def measure(cfg, args, hip, lm, W, torch, stream, clock=None):
                             s1=P(inp.get("s1")), s3=P(inp.get("s3")), s2=P(inp.get("s2")),
                             norm_w=P(inp.get("norm_w")), w_out=P(inp.get("w_out")),
                             ws1=P(inp.get("ws1")), ws3=P(inp.get("ws3")), ws2=P(inp.get("ws2")),
-                            y=P(out["y"]), workspace=P(fws), workspace_bytes=fws.numel())
+                            y=P(out["y"]), workspace=P(fws), workspace_bytes=fws.numel(),
+                            wlayout=lm.LMOE_WLAYOUT_TILED if packed else lm.LMOE_WLAYOUT_ROWS)
         sets.append(dict(inp=inp, rws=rws, fws=fws, out=out, ra=ra, fa=fa, logits=logits, plan=None))
     torch.cuda.synchronize()
 
@@ -527,6 +542,8 @@ def measure(cfg, args, hip, lm, W, torch, stream, clock=None):
 
     res = {
         "ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s, "mode": mode,
+        "expert_weight_layout": ("tile-packed at load time (latent_moe_pack_weights)" if packed else
+                                 "MXFP4 codes + scales" if cfg.mxfp4 else "row-major [E, N, K]"),
         "step_ms": {"median": round(statistics.median(per_step), 5), "p10": round(pct(per_step, 0.1), 5),
                     "p90": round(pct(per_step, 0.9), 5), "min": round(min(per_step), 5),
                     "max": round(max(per_step), 5)},
@@ -609,7 +626,7 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     clock = None if args.no_clock else ClockSampler()
 
-    main_res = measure(cfg, args, hip, lm, W, torch, stream, clock)
+    main_res = measure(cfg, args, hip, lm, W, torch, stream, clock, args.wlayout)
     print(f"# {cfg.name}: {main_res['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
 
     cpu = None
@@ -621,17 +638,18 @@ def main():
     torch.cuda.empty_cache()
 
     others = {}
-    for name in [n for n in args.extra_workloads.split(",") if n and n != cfg.name]:
+    for key in [n for n in args.extra_workloads.split(",") if n and n != cfg.name]:
+        name, _, lay = key.partition("@")
         ocfg = W.CONFIGS[name]
-        r = measure(ocfg, args, hip, lm, W, torch, stream, clock)
+        r = measure(ocfg, args, hip, lm, W, torch, stream, clock, lay or args.wlayout)
         r.pop("_sets")
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         r["config"] = describe(ocfg)
         r["ms_per_step"] = round(r["ms_per_step"], 5)
         r["tokens_per_s"] = round(r["tokens_per_s"], 1)
-        others[name] = r
-        print(f"# {name}: {r['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+        others[key] = r
+        print(f"# {key}: {r['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
 
     single = None
     if args.cpu_seconds > 0:
@@ -655,7 +673,8 @@ def main():
                  "N(0, 1/sqrt(latent*d*0.02^2)) on the latent)" if cfg.router_gemm else
                  "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights, gap-separated N(0,1) logits)"),
         "config": {"workload": describe(cfg), "T": T, "d": cfg.d, "latent": cfg.l, "E": cfg.E, "k": cfg.k,
-                   "shared": cfg.S, "I": cfg.I, "Is": cfg.Is},
+                   "shared": cfg.S, "I": cfg.I, "Is": cfg.Is,
+                   "expert_weight_layout": main_res.get("expert_weight_layout")},
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(line), flush=True)

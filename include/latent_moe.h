@@ -70,6 +70,14 @@ enum { LMOE_OK = 0, LMOE_EINVAL = 1, LMOE_EUNSUPPORTED = 2, LMOE_EHIP = 3 };
  *                        decode-shaped batches (T*k <= 32*E): a larger batch
  *                        returns LMOE_EUNSUPPORTED and nothing is enqueued. */
 enum { LMOE_WFMT_BF16 = 0, LMOE_WFMT_MXFP4 = 1, LMOE_WFMT_MXFP4_W4A16 = 2 };
+/* Storage of bf16 routed-expert weights (lmoe_forward_args.wlayout):
+ *  LMOE_WLAYOUT_ROWS   row-major [E, N, K] (the layout every shape below names).
+ *  LMOE_WLAYOUT_TILED  tile-packed by latent_moe_pack_weights: the same values
+ *                      in 128-row x 64-column blocks, each 16 KB contiguous,
+ *                      so the expert GEMMs stream contiguous blocks.  Only for
+ *                      LMOE_WFMT_BF16 with l and I multiples of 128, at least
+ *                      256; results equal the row-major layout's bit for bit. */
+enum { LMOE_WLAYOUT_ROWS = 0, LMOE_WLAYOUT_TILED = 1 };
 
 /* Limits of this library. */
 #define LMOE_MAX_EXPERTS_LOGITS 1024 /* E in logits mode (router keeps E/64 logits per lane) */
@@ -167,6 +175,9 @@ int latent_moe_route(const lmoe_route_args* args, void* hip_stream, latent_moe_p
  *                           y [T,l] = w[r] * Y[r], rows in received order.
  *   workspace >= latent_moe_forward_workspace_size(...) bytes (intermediates
  *             z, hs, H, Y, rhat and, for w4a8, the MXFP8 activation copies)
+ *   wlayout  LMOE_WLAYOUT_ROWS, or LMOE_WLAYOUT_TILED for bf16 w1, w3, w2
+ *            packed by latent_moe_pack_weights (see LMOE_WLAYOUT_*); a shape
+ *            the packed layout does not serve returns LMOE_EUNSUPPORTED
  * Inputs are read-only; y and the workspace are written.  x, the weights and
  * y must not overlap the workspace.
  */
@@ -190,6 +201,7 @@ typedef struct {
   void* y;
   void* workspace;
   size_t workspace_bytes;
+  int32_t wlayout; /* LMOE_WLAYOUT_*: how bf16 w1, w3, w2 are stored (0 = row-major) */
 } lmoe_forward_args;
 
 int latent_moe_forward(const latent_moe_plan* plan, const lmoe_forward_args* args, void* hip_stream);
@@ -278,6 +290,21 @@ int latent_moe_layer_os(const lmoe_route_args* route, const lmoe_forward_args* f
 #define LMOE_NOALLOC_SCRATCH_BYTES (64u << 20)
 int latent_moe_layer_noalloc(const lmoe_route_args* route, const void* w_router, float* logits,
                              const lmoe_forward_args* fwd, void* hip_stream);
+
+/*
+ * Packs one bf16 routed-expert weight matrix [E, N, K] (w1 or w3: N = I,
+ * K = l; w2: N = l, K = I) into the tile-packed layout LMOE_WLAYOUT_TILED:
+ * element (e, n, k) moves to
+ *   (((e * N/128 + n/128) * K/64 + k/64) * 128 + n%128) * 64 + k%64,
+ * so that the 64 K columns of 128 consecutive rows of one expert are one
+ * contiguous 16 KB block.  A load-time step (the expert GEMMs read each such
+ * block whole in one pipeline stage); the values are copied unchanged.
+ *   src, dst  device, bf16, E*N*K elements each, 16-byte aligned, not
+ *             overlapping; dst is written, src only read
+ *   N         a multiple of 128;  K a multiple of 64;  E >= 1
+ * Enqueued on hip_stream; LMOE_EINVAL on invalid arguments (nothing enqueued).
+ */
+int latent_moe_pack_weights(const void* src, void* dst, int32_t E, int32_t N, int32_t K, void* hip_stream);
 
 /* Releases a plan (host memory only; NULL is a no-op).  Device buffers the
  * plan borrowed remain the caller's. */

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "liblatent_moe.so")
 
 LMOE_OK, LMOE_EINVAL, LMOE_EUNSUPPORTED, LMOE_EHIP = 0, 1, 2, 3
 LMOE_WFMT_BF16, LMOE_WFMT_MXFP4, LMOE_WFMT_MXFP4_W4A16 = 0, 1, 2
+LMOE_WLAYOUT_ROWS, LMOE_WLAYOUT_TILED = 0, 1
 _ERRNAMES = {1: "LMOE_EINVAL", 2: "LMOE_EUNSUPPORTED", 3: "LMOE_EHIP"}
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -38,7 +39,8 @@ class ForwardArgs(ctypes.Structure):
     _fields_ = [("d", _i32), ("l", _i32), ("I", _i32), ("S", _i32), ("Is", _i32), ("wfmt", _i32),
                 ("norm_eps", _f32), ("x", _vp), ("w_in", _vp), ("w1", _vp), ("w3", _vp), ("w2", _vp),
                 ("s1", _vp), ("s3", _vp), ("s2", _vp), ("norm_w", _vp), ("w_out", _vp), ("ws1", _vp),
-                ("ws3", _vp), ("ws2", _vp), ("y", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+                ("ws3", _vp), ("ws2", _vp), ("y", _vp), ("workspace", _vp), ("workspace_bytes", _sz),
+                ("wlayout", _i32)]
 
 
 class ForwardLayout(ctypes.Structure):
@@ -71,6 +73,8 @@ def _load():
     L.latent_moe_layer_os.restype = ctypes.c_int
     L.latent_moe_layer_noalloc.argtypes = [ctypes.POINTER(RouteArgs), _vp, _vp, ctypes.POINTER(ForwardArgs), _vp]
     L.latent_moe_layer_noalloc.restype = ctypes.c_int
+    L.latent_moe_pack_weights.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp]
+    L.latent_moe_pack_weights.restype = ctypes.c_int
     L.latent_moe_free.argtypes = [_vp]
     L.latent_moe_free.restype = None
     L.latent_moe_route_workspace_size.argtypes = [_i64, _i32, _i32]
@@ -117,6 +121,23 @@ def latent_moe_layer(route_args: RouteArgs, w_router: int, logits: int, fwd_args
 def latent_moe_layer_os(route_args: RouteArgs, fwd_args: ForwardArgs, stream: int = 0):
     """Calls the C entry point (output-stationary decode layer)."""
     _check(lib.latent_moe_layer_os(ctypes.byref(route_args), ctypes.byref(fwd_args), _vp(stream)))
+
+
+def latent_moe_pack_weights(src: int, dst: int, E: int, N: int, K: int, stream: int = 0):
+    """Calls the C entry point (bf16 [E,N,K] -> tile-packed layout)."""
+    _check(lib.latent_moe_pack_weights(_vp(src), _vp(dst), E, N, K, _vp(stream)))
+
+
+def pack_weights(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """Tile-packed copy of a bf16 expert weight tensor [E, N, K] (a new tensor
+    of the same shape whose storage is in LMOE_WLAYOUT_TILED order)."""
+    if w.dtype != torch.bfloat16 or w.dim() != 3 or not w.is_contiguous():
+        raise ValueError("pack_weights takes a contiguous bf16 [E, N, K] tensor")
+    out = torch.empty_like(w)
+    _guard_owned(stream, [out])
+    E, N, K = w.shape
+    latent_moe_pack_weights(w.data_ptr(), out.data_ptr(), E, N, K, _stream(stream))
+    return out
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # LMOE_NOALLOC_SCRATCH_BYTES
@@ -295,7 +316,7 @@ def route(logits: Optional[torch.Tensor] = None, k: int = 1, *, ids: Optional[to
 def forward(routing: Routing, x: torch.Tensor, w1, w3, w2, *, w_in=None, w_out=None, ws1=None, ws3=None,
             ws2=None, norm_w=None, eps: float = 1e-6, s1=None, s3=None, s2=None, mxfp4: bool = False,
             w4a16: bool = False, y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            stream=None, I: Optional[int] = None) -> torch.Tensor:
+            stream=None, I: Optional[int] = None, wlayout: int = LMOE_WLAYOUT_ROWS) -> torch.Tensor:
     """One LatentMoE forward on the routed rows; returns y (bf16).  mxfp4: the
     routed weights are MXFP4 codes + scales, run w4a8, or w4a16 if w4a16 is set."""
     rows = w_in is None
@@ -321,7 +342,7 @@ def forward(routing: Routing, x: torch.Tensor, w1, w3, w2, *, w_in=None, w_out=N
     a = ForwardArgs(d=d, l=l, I=I, S=S, Is=Is, wfmt=wfmt, norm_eps=eps, x=_p(x), w_in=_p(w_in),
                     w1=_p(w1), w3=_p(w3), w2=_p(w2), s1=_p(s1), s3=_p(s3), s2=_p(s2), norm_w=_p(norm_w),
                     w_out=_p(w_out), ws1=_p(ws1), ws3=_p(ws3), ws2=_p(ws2), y=_p(y),
-                    workspace=_p(workspace), workspace_bytes=workspace.numel())
+                    workspace=_p(workspace), workspace_bytes=workspace.numel(), wlayout=wlayout)
     latent_moe_forward(routing.plan, a, _stream(stream))
     # the workspace lives as long as the routing (the last forward's
     # intermediates stay readable through workspace_views)
@@ -333,7 +354,8 @@ def layer(x: torch.Tensor, w_r: Optional[torch.Tensor], k: int, w1, w3, w2, *, w
           ws2=None, norm_w=None, eps: float = 1e-6, s1=None, s3=None, s2=None, mxfp4: bool = False,
           w4a16: bool = False, y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
           route_workspace: Optional[torch.Tensor] = None, stream=None, I: Optional[int] = None,
-          routing: Optional[Routing] = None, logits: Optional[torch.Tensor] = None):
+          routing: Optional[Routing] = None, logits: Optional[torch.Tensor] = None,
+          wlayout: int = LMOE_WLAYOUT_ROWS):
     """The whole layer in one call (``latent_moe_layer``).  With a router gate
     w_r [E,l] the logits are z W_r^T on the latent; with w_r None they are the
     given ``logits`` [T,E] (fp32).  Returns (Routing with .logits, y).  Passing
@@ -383,7 +405,7 @@ def layer(x: torch.Tensor, w_r: Optional[torch.Tensor], k: int, w1, w3, w2, *, w
     fa = ForwardArgs(d=d, l=l, I=I, S=S, Is=Is, wfmt=wfmt, norm_eps=eps, x=_p(x), w_in=_p(w_in),
                      w1=_p(w1), w3=_p(w3), w2=_p(w2), s1=_p(s1), s3=_p(s3), s2=_p(s2), norm_w=_p(norm_w),
                      w_out=_p(w_out), ws1=_p(ws1), ws3=_p(ws3), ws2=_p(ws2), y=_p(y),
-                     workspace=_p(workspace), workspace_bytes=workspace.numel())
+                     workspace=_p(workspace), workspace_bytes=workspace.numel(), wlayout=wlayout)
     routing.plan = latent_moe_layer(ra, _p(w_r), None if w_r is None else _p(routing.logits), fa, _stream(stream),
                                     routing.plan)
     routing.keep = [workspace]
@@ -394,7 +416,7 @@ def layer(x: torch.Tensor, w_r: Optional[torch.Tensor], k: int, w1, w3, w2, *, w
 def layer_os(x: torch.Tensor, logits: torch.Tensor, k: int, w1, w3, w2, *, w_in, w_out, ws1=None, ws3=None,
              ws2=None, norm_w=None, eps: float = 1e-6, s1=None, s3=None, s2=None, w4a16: bool = False,
              y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
-             I: Optional[int] = None):
+             I: Optional[int] = None, wlayout: int = LMOE_WLAYOUT_ROWS):
     """The output-stationary decode layer (``latent_moe_layer_os``): returns
     (topk_ids, topk_w, y, workspace); H and Y in the workspace are in
     (token, slot) order."""
@@ -421,7 +443,7 @@ def layer_os(x: torch.Tensor, logits: torch.Tensor, k: int, w1, w3, w2, *, w_in,
     fa = ForwardArgs(d=d, l=l, I=I, S=S, Is=Is, wfmt=wfmt, norm_eps=eps, x=_p(x), w_in=_p(w_in), w1=_p(w1),
                      w3=_p(w3), w2=_p(w2), s1=_p(s1), s3=_p(s3), s2=_p(s2), norm_w=_p(norm_w), w_out=_p(w_out),
                      ws1=_p(ws1), ws3=_p(ws3), ws2=_p(ws2), y=_p(y), workspace=_p(workspace),
-                     workspace_bytes=workspace.numel())
+                     workspace_bytes=workspace.numel(), wlayout=wlayout)
     latent_moe_layer_os(ra, fa, _stream(stream))
     return topk_ids, topk_w, y, workspace
 

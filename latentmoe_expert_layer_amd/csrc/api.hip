@@ -161,6 +161,13 @@ int check_fwd_dims(const latent_moe_plan* p, const lmoe_forward_args* a, bool ro
       return fail(LMOE_EINVAL, "MXFP4 experts need l and I multiples of 128 (got %d, %d)", a->l, a->I);
     if (!a->s1 || !a->s3 || !a->s2) return fail(LMOE_EINVAL, "MXFP4 experts need scales s1, s3 and s2");
   }
+  if (a->wlayout != LMOE_WLAYOUT_ROWS && a->wlayout != LMOE_WLAYOUT_TILED)
+    return fail(LMOE_EINVAL, "unknown wlayout %d", a->wlayout);
+  if (a->wlayout == LMOE_WLAYOUT_TILED &&
+      (a->wfmt != LMOE_WFMT_BF16 || a->l % 128 || a->I % 128 || a->l < 256 || a->I < 256))
+    return fail(LMOE_EUNSUPPORTED,
+                "the tile-packed weight layout serves bf16 experts with l and I multiples of 128, >= 256 "
+                "(got wfmt %d, l %d, I %d)", a->wfmt, a->l, a->I);
   if (rows) {
     if (a->w_out) return fail(LMOE_EINVAL, "rows mode (w_in == NULL) needs w_out == NULL");
     if (p->k != 1) return fail(LMOE_EINVAL, "rows mode needs k == 1 (got %d)", p->k);
@@ -434,6 +441,7 @@ int fwd_back(const FwdCtx& c) {
       f1.ldc = I;
       f1.os_ids = p->ids;
       f1.os_R = R;
+      f1.packed = a->wlayout == LMOE_WLAYOUT_TILED;
       if ((e = lmoe::launch_grouped_skinny_os(f1, p->E, s, fc1_t0, fc1_t1)) != hipSuccess)
         return hip_fail(e, "expert FC1 (output-stationary)");
       lmoe::GroupedGemm f2 = f1;
@@ -576,6 +584,7 @@ int fwd_back(const FwdCtx& c) {
     f1.tiles = skinny ? p->tiles_s : p->tiles_t;
     f1.ntiles = skinny ? p->n_s : p->n_t;
     f1.max_tiles = skinny ? p->max_s : p->max_t;
+    f1.packed = a->wlayout == LMOE_WLAYOUT_TILED;
     e = skinny ? lmoe::launch_grouped_skinny(f1, s, fc1_t0, fc1_t1) : lmoe::launch_grouped_tiled(f1, s, fc1_t0, fc1_t1);
     if (e != hipSuccess) return hip_fail(e, "expert FC1");
 
@@ -679,6 +688,21 @@ int latent_moe_forward_workspace_layout(int64_t T, int32_t E, int32_t k, int32_t
   if (mx) w |= LMOE_WS_ZQ | LMOE_WS_HQ;
   o.written = w;
   *out = o;
+  return LMOE_OK;
+}
+
+int latent_moe_pack_weights(const void* src, void* dst, int32_t E, int32_t N, int32_t K, void* hip_stream) {
+  if (!src || !dst) return fail(LMOE_EINVAL, "NULL src or dst");
+  if (E < 1 || N < 1 || K < 1 || N % lmoe::kPackRows || K % 64)
+    return fail(LMOE_EINVAL, "pack: E=%d N=%d K=%d (N a multiple of %d, K of 64)", E, N, K, lmoe::kPackRows);
+  if (!aligned16(src) || !aligned16(dst)) return fail(LMOE_EINVAL, "pack: pointers must be 16-byte aligned");
+  const size_t bytes = size_t(E) * size_t(N) * size_t(K) * 2;
+  const char* a = static_cast<const char*>(src);
+  const char* b = static_cast<const char*>(dst);
+  if (a < b + bytes && b < a + bytes) return fail(LMOE_EINVAL, "pack: src and dst overlap");
+  const hipError_t e = lmoe::launch_pack_weights(static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), E,
+                                                 N, K, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_fail(e, "pack weights");
   return LMOE_OK;
 }
 

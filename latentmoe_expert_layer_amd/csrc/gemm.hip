@@ -24,6 +24,24 @@ namespace {
 
 constexpr int kBK = 64;          // K per LDS stage
 constexpr int kLdsK = kBK + 8;   // padded LDS row (bf16): 144 B
+static_assert(kBK == 64, "a tile-packed block holds 64 K columns: one stage");
+
+// [E, N, K] row-major -> tile-packed (kernels.h), one 16-byte chunk (8
+// elements along K) per thread, threads in packed order so the writes are
+// contiguous; each read is 16 bytes of a row.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                          int64_t nchunks, int N, int K) {
+  const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;  // packed chunk index
+  if (q >= nchunks) return;
+  const int kq = int(q % 8);                                   // chunk within the block's 64 columns
+  const int64_t rest = q / 8;
+  const int rin = int(rest % kPackRows);                       // row within the 128-row block
+  const int64_t blk = rest / kPackRows;                        // (e, n/128, k/64) block
+  const int kb = int(blk % (K / 64));
+  const int64_t en = blk / (K / 64);                           // e * N/128 + n/128
+  const int64_t row = en * kPackRows + rin;                    // e * N + n
+  dst[q] = src[(row * K + int64_t(kb) * 64) / 8 + kq];
+}
 
 struct TiledArgs {
   int M, N;
@@ -319,7 +337,9 @@ hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s, hipEvent
 // the weight stream, and the deeper B pipeline keeps twice as much of it in
 // flight.  The results are bit-identical to tiled_gemm_kernel's (the same
 // MFMAs in the same K order).  Needs K a multiple of 128 and >= 256.
-template <bool GATED>
+// PACKED: the weights are in the tile-packed layout (kernels.h): a stage's
+// 128-row block of B is 16 KB of contiguous memory.
+template <bool GATED, bool PACKED = false>
 __global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
   constexpr int NTH = 512, BM = kTiledBM, BR = 256, NOUT = GATED ? 128 : 256;
   constexpr int WAVES_N = 4, WM = BM / 2, WN = BR / WAVES_N;
@@ -362,8 +382,15 @@ __global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
   for (int i = 0; i < B_CH; ++i) {
     const bool up = GATED && i >= B_CH / 2;
     const int r = (up ? i - B_CH / 2 : i) * RPC + tid / CPR;
-    pb[i] = (up ? g.B3 : g.B) + be + int64_t(min(n0 + r, g.N - 1)) * g.ldb + kc8;
+    const int n = min(n0 + r, g.N - 1);
+    if constexpr (PACKED) {
+      pb[i] = (up ? g.B3 : g.B) + be + int64_t(n / kPackRows) * g.K * kPackRows + (n % kPackRows) * kBK + kc8;
+    } else {
+      pb[i] = (up ? g.B3 : g.B) + be + int64_t(n) * g.ldb + kc8;
+    }
   }
+  // B advances one stage: kBK columns of a row, or one packed block
+  constexpr int BSTEP = PACKED ? kPackRows * kBK : kBK;
   const int nk = g.K / kBK;
   uint4 ra[A_CH], rbx[B_CH], rby[B_CH];  // A one stage ahead; B stages alternate between X and Y
   auto load_a = [&]() __attribute__((always_inline)) {
@@ -379,14 +406,14 @@ __global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       rbx[i] = ldg16(pb[i]);
-      pb[i] += kBK;
+      pb[i] += BSTEP;
     }
   };
   auto load_by = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       rby[i] = ldg16(pb[i]);
-      pb[i] += kBK;
+      pb[i] += BSTEP;
     }
   };
   auto store_a = [&](int buf) __attribute__((always_inline)) {
@@ -521,11 +548,11 @@ __global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
   }
 }
 
-template <bool GATED>
+template <bool GATED, bool PACKED>
 hipError_t run_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   constexpr int NOUT = GATED ? 128 : 256;
   const size_t lds = size_t(2) * (kTiledBM + 256) * kLdsK * sizeof(bf16_t);
-  auto kern = grouped_tiled_kernel<GATED>;
+  auto kern = grouped_tiled_kernel<GATED, PACKED>;
   if (hipError_t e = allow_dynamic_lds((const void*)kern, int(lds)); e != hipSuccess) return e;
   const int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
@@ -709,10 +736,24 @@ hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
   return run_tiled<8, 2, false, false, false>(a, mt, s);
 }
 
+hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int E, int N, int K, hipStream_t s) {
+  if (E <= 0 || N % kPackRows || K % 64) return hipErrorInvalidValue;
+  const int64_t nchunks = int64_t(E) * N * (K / 8);
+  const int64_t nblk = (nchunks + 255) / 256;
+  if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
+  pack_weights_kernel<<<dim3{uint32_t(nblk)}, dim3{256}, 0, s>>>(reinterpret_cast<const uint4*>(src),
+                                                                  reinterpret_cast<uint4*>(dst), nchunks, N, K);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   // routing cuts tiles at kTiledBM rows; both kernels take tiles of up to 192 rows
   static_assert(kTiledBM <= 192, "tile table granularity");
-  if (g.K % 128 == 0 && g.K >= 256) return g.gated ? run_grouped<true>(g, s, t0, t1) : run_grouped<false>(g, s, t0, t1);
+  if (g.K % 128 == 0 && g.K >= 256) {
+    if (g.packed) return g.gated ? run_grouped<true, true>(g, s, t0, t1) : run_grouped<false, true>(g, s, t0, t1);
+    return g.gated ? run_grouped<true, false>(g, s, t0, t1) : run_grouped<false, false>(g, s, t0, t1);
+  }
+  if (g.packed) return hipErrorInvalidValue;  // the tile-packed layout needs the kernel above
   TiledArgs a{};
   a.M = 0;
   a.N = g.N;

@@ -96,6 +96,14 @@ hipError_t launch_small_dense_with_router(const DenseGemm* parts, int nparts, co
 // Grouped over experts: for each tile (expert e, rows p in the tile):
 //   C[p, :] = A[row(p)] * B_e^T  (gated: silu(A B_e^T) * (A B3_e^T)),
 //   row(p) = a_rows ? a_rows[p] / a_row_div : p,   B_e = B + e * b_estride.
+// Tile-packed bf16 expert weights (latent_moe_pack_weights): element (e, n, k)
+// of an [E, N, K] matrix sits at
+//   (((e * N/kPackRows + n/kPackRows) * K/64 + k/64) * kPackRows + n%kPackRows) * 64 + k%64,
+// so the 64 K columns of 128 consecutive rows that a tile's stage reads are
+// one 16 KB block.  N a multiple of kPackRows, K of 64.
+constexpr int kPackRows = 128;
+hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int E, int N, int K, hipStream_t s);
+
 struct GroupedGemm {
   int N, K;
   const uint16_t* A;
@@ -116,6 +124,7 @@ struct GroupedGemm {
   // (token, slot) row r = t*k + j, and the row count
   const int32_t* os_ids;
   int64_t os_R;
+  bool packed;  // B and B3 in the tile-packed layout (b_estride = N*K, ldb unused)
 };
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Output-stationary decode (TokenSpeed Day-0 post, "Gluon kernels on AMD GPUs >

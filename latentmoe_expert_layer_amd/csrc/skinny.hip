@@ -209,7 +209,9 @@ __device__ __forceinline__ f32x4 lds_chunk_mfma(uint4* L, int lane, uint4 v0, ui
 // OS: the output-stationary form (no tile table): the grid is experts x
 // column blocks, each workgroup scans the routed ids for its expert's rows
 // and runs them 16 at a time; rows are written at their (token, slot) index.
-template <bool GATED, int NCH, bool OS = false>
+// PACKED: the weights are in the tile-packed layout (kernels.h); a lane's 16
+// bytes (row n, K k..k+7) are the same elements, at another address.
+template <bool GATED, int NCH, bool OS = false, bool PACKED = false>
 __global__ __launch_bounds__(256) void skinny_lds_kernel(GroupedGemm g) {
   __shared__ uint4 lds[4][16 * 17];
   __shared__ int32_t os_lst[OS ? 16 : 1];
@@ -240,11 +242,24 @@ __global__ __launch_bounds__(256) void skinny_lds_kernel(GroupedGemm g) {
       pos = int64_t(tl.row_start) + min(lane & 15, tl.nrows - 1);
       if (g.a_rows) sr = g.a_rows[pos];
     }
-    const int64_t wb = int64_t(expert) * g.b_estride + int64_t(tn * 64 + wid * 16) * g.ldb;
-    const int64_t lofs = (lane >> 4) * (g.ldb / 8) + (lane & 15);  // in uint4
+    // lane (row 4j + lane/16 of the wave's 16, 16-byte column lane%16 of a
+    // 128-wide K chunk); uint4 offsets: rs per 4 rows, ks(k) for chunk k
+    int64_t wb, lofs, rs;
+    if constexpr (PACKED) {
+      const int nb0 = tn * 64 + wid * 16;  // 16 rows inside one 128-row block
+      wb = int64_t(expert) * g.b_estride + int64_t(nb0 / kPackRows) * g.K * kPackRows + (nb0 % kPackRows) * 64;
+      lofs = int64_t((lane & 15) >> 3) * (kPackRows * 8) + (lane >> 4) * 8 + (lane & 7);
+      rs = 4 * 8;
+    } else {
+      wb = int64_t(expert) * g.b_estride + int64_t(tn * 64 + wid * 16) * g.ldb;
+      lofs = (lane >> 4) * (g.ldb / 8) + (lane & 15);
+      rs = 4 * (g.ldb / 8);
+    }
+    auto ks = [&](int k) __attribute__((always_inline)) -> int64_t {
+      return PACKED ? int64_t(k / 64) * (kPackRows * 8) : int64_t(k / 8);
+    };
     const uint4* gp = reinterpret_cast<const uint4*>(g.B + wb) + lofs;
     const uint4* up = GATED ? reinterpret_cast<const uint4*>(g.B3 + wb) + lofs : nullptr;
-    const int64_t rs = 4 * (g.ldb / 8);  // 4 rows, in uint4
     uint4* L = lds[wid];
     const bf16_t* ap = nullptr;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
@@ -254,8 +269,8 @@ __global__ __launch_bounds__(256) void skinny_lds_kernel(GroupedGemm g) {
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          gv[c][j] = gp[j * rs + (kc + 128 * c) / 8];
-          if constexpr (GATED) uv[c][j] = up[j * rs + (kc + 128 * c) / 8];
+          gv[c][j] = gp[j * rs + ks(kc + 128 * c)];
+          if constexpr (GATED) uv[c][j] = up[j * rs + ks(kc + 128 * c)];
         }
       __builtin_amdgcn_sched_barrier(0);
       if (kc == 0) {
@@ -605,10 +620,18 @@ hipError_t launch_grouped_skinny_os(const GroupedGemm& g, int E, hipStream_t s, 
   if (g.os_R <= 0 || E <= 0) return hipSuccess;
   if (g.os_R > kOsMaxRows || !g.os_ids || g.K % 128 != 0 || g.N % 64 != 0) return hipErrorInvalidValue;
   const dim3 grid{uint32_t(int64_t(E) * (g.N / 64))}, block{256};
-  const void* kern = g.gated ? (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<true, 2, true>
-                                               : (const void*)skinny_lds_kernel<true, 1, true>)
-                             : (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<false, 2, true>
-                                               : (const void*)skinny_lds_kernel<false, 1, true>);
+  const void* kern;
+  if (g.packed) {
+    kern = g.gated ? (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<true, 2, true, true>
+                                     : (const void*)skinny_lds_kernel<true, 1, true, true>)
+                   : (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<false, 2, true, true>
+                                     : (const void*)skinny_lds_kernel<false, 1, true, true>);
+  } else {
+    kern = g.gated ? (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<true, 2, true>
+                                     : (const void*)skinny_lds_kernel<true, 1, true>)
+                   : (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<false, 2, true>
+                                     : (const void*)skinny_lds_kernel<false, 1, true>);
+  }
   return launch_kernel(kern, grid, block, 0, s, g, t0, t1);
 }
 
@@ -617,7 +640,13 @@ hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t
   if (nblk <= 0) return hipSuccess;
   const dim3 grid{uint32_t(nblk)}, block{256};
   const void* kern;
-  if (g.gated) {
+  if (g.packed) {
+    if (g.K % 128) return hipErrorInvalidValue;  // the tile-packed layout runs on the LDS-staged kernel
+    kern = g.gated ? (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<true, 2, false, true>
+                                     : (const void*)skinny_lds_kernel<true, 1, false, true>)
+                   : (g.K % 256 == 0 ? (const void*)skinny_lds_kernel<false, 2, false, true>
+                                     : (const void*)skinny_lds_kernel<false, 1, false, true>);
+  } else if (g.gated) {
     kern = g.K % 256 == 0   ? (const void*)skinny_lds_kernel<true, 2>
            : g.K % 128 == 0 ? (const void*)skinny_lds_kernel<true, 1>
                             : (const void*)skinny_grouped_kernel<true, 2, 1>;

@@ -269,3 +269,29 @@ def test_output_stationary_layer_refusals():
             lm.latent_moe_layer_os(ra, fa)
         assert ei.value.code == code, (kw, ei.value)
 
+
+def test_tile_packed_layout_refusals():
+    """The tile-packed weight layout is refused where no kernel reads it, and
+    the pack call validates its arguments, before any HIP call (no GPU)."""
+    import latentmoe_expert_layer_amd as lm
+    fake = 1 << 20
+    ws_big = 1 << 40
+
+    def fwd(wfmt=0, l=256, I=256, wlayout=lm.LMOE_WLAYOUT_TILED):
+        return lm.ForwardArgs(d=512, l=l, I=I, S=2, Is=256, wfmt=wfmt, norm_eps=1e-6, x=fake, w_in=fake, w1=fake,
+                              w3=fake, w2=fake, s1=fake, s3=fake, s2=fake, norm_w=fake, w_out=fake, ws1=fake,
+                              ws3=fake, ws2=fake, y=fake, workspace=fake, workspace_bytes=ws_big, wlayout=wlayout)
+    ra = lm.RouteArgs(T=256, E=896, k=16, logits=fake, topk_ids=fake, topk_w=fake)
+    for kw, code in [(dict(wfmt=lm.LMOE_WFMT_MXFP4), lm.LMOE_EUNSUPPORTED),
+                     (dict(l=192, I=256), lm.LMOE_EUNSUPPORTED),
+                     (dict(l=256, I=128), lm.LMOE_EUNSUPPORTED),
+                     (dict(wlayout=7), lm.LMOE_EINVAL)]:
+        with pytest.raises(lm.LatentMoeError) as ei:
+            lm.latent_moe_layer_os(ra, fwd(**kw))
+        assert ei.value.code == code, kw
+    for args in [(fake, fake, 2, 100, 64), (fake, fake, 2, 128, 96), (fake, fake + 8, 1, 128, 64),
+                 (fake, fake + 1024, 4, 128, 64)]:   # N, K not multiples; misaligned; overlapping
+        with pytest.raises(lm.LatentMoeError) as ei:
+            lm.latent_moe_pack_weights(*args)
+        assert ei.value.code == lm.LMOE_EINVAL, args
+

@@ -671,3 +671,82 @@ def test_output_stationary_layer_equals_permuted_path(name, dims, skew):
     ref = oracle.run(inp, act_quant=False)
     assert torch.equal(ids.cpu(), ref["ids"])
     assert_parity(y.cpu(), ref["y"])
+
+
+# ------------------------------------------------ tile-packed expert weights
+def packed_reference(w):
+    """The tile-packed order written with torch: [E, N/128, 128, K/64, 64] ->
+    [E, N/128, K/64, 128, 64]."""
+    E, N, K = w.shape
+    return w.view(E, N // 128, 128, K // 64, 64).permute(0, 1, 3, 2, 4).contiguous().view(E, N, K)
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 128, 64), (5, 256, 384), (896, 512, 2048), (7, 2048, 512)])
+def test_pack_weights_matches_the_layout_formula(E, N, K):
+    g = torch.Generator(device="cuda").manual_seed(E + N + K)
+    w = torch.randn(E, N, K, generator=g, device="cuda").to(torch.bfloat16)
+    got = lm.pack_weights(w)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), packed_reference(w).view(torch.int16))
+
+
+PACKED_LAYERS = [
+    ("decode", None),                                                               # weight-streaming kernels
+    ("packed_ragged", dict(T=77, d=128, l=384, E=40, k=8, S=2, I=256, Is=64)),     # FC1 K = 384: one chunk per batch
+    ("packed_tiled", dict(T=600, d=256, l=512, E=8, k=2, S=1, I=256, Is=128)),     # LDS-tiled grouped kernel
+    ("packed_tiled_wide", dict(T=1500, d=256, l=2048, E=16, k=4, S=1, I=512, Is=256)),
+]
+
+
+def _pack_inputs(inp_dev):
+    out = dict(inp_dev)
+    for n in ("w1", "w3", "w2"):
+        out[n] = lm.pack_weights(inp_dev[n])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,dims", PACKED_LAYERS, ids=[n for n, _ in PACKED_LAYERS])
+def test_tile_packed_weights_give_identical_results(name, dims):
+    """The same layer with the expert weights tile-packed: routing, y and every
+    intermediate bit for bit equal to the row-major run; then the oracle bar."""
+    cfg = W.CONFIGS[name] if dims is None else W.custom(name, **dims)
+    log(f"tile-packed weights {name}: {cfg}")
+    inp = W.make_inputs(cfg)
+    inp_dev = to_device(inp)
+    r_ref, y_ref, views_ref = run_gpu_layer(inp_dev)
+    pk = _pack_inputs(inp_dev)
+    wts = dict(w_in=pk["w_in"], w_out=pk["w_out"], ws1=pk.get("ws1"), ws3=pk.get("ws3"), ws2=pk.get("ws2"),
+               norm_w=pk.get("norm_w"), eps=cfg.eps, wlayout=lm.LMOE_WLAYOUT_TILED)
+    r = gpu_route(pk["logits"], cfg.k)
+    ws = poison_(torch.empty(lm.forward_workspace_size(cfg.T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is),
+                             dtype=torch.uint8, device="cuda"))
+    y = poison_(torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device="cuda"))
+    lm.forward(r, pk["x"], pk["w1"], pk["w3"], pk["w2"], y=y, workspace=ws, **wts)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), "y differs with packed weights"
+    views = lm.workspace_views(ws, cfg.T, cfg.E, cfg.k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is)
+    for n in ("z", "hs", "H", "Y", "rhat"):
+        if n in views:
+            assert torch.equal(views[n].view(torch.int16), views_ref[n].view(torch.int16)), n
+    if cfg.T <= 512 and cfg.T * cfg.k <= 8192:   # the output-stationary call reads packed weights too
+        ids, w, y_os, _ = lm.layer_os(pk["x"], pk["logits"], cfg.k, pk["w1"], pk["w3"], pk["w2"], **wts)
+        torch.cuda.synchronize()
+        assert torch.equal(y_os.view(torch.int16), y_ref.view(torch.int16)), "output-stationary y differs"
+    ref = oracle.run(inp)
+    assert_parity(y.cpu(), ref["y"])
+
+
+def test_tile_packed_weights_rows_mode():
+    """One expert-parallel rank's share (rows mode, LDS-tiled kernels) with
+    packed weights: identical to the row-major run."""
+    cfg = W.custom("packed_rows", T=3000, d=0, l=2048, E=56, k=1, S=0, I=512, Is=0, rows_mode=True, norm=False,
+                   zipf_s=1.1, seed=2)
+    inp_dev = W.make_inputs(cfg, device="cuda")
+    r_ref, y_ref, views_ref = run_gpu_layer(inp_dev)
+    pk = _pack_inputs(inp_dev)
+    r = gpu_route(None, 1, ids=pk["ids"], weights=pk["weights"], E=cfg.E)
+    y = poison_(torch.empty(cfg.T, cfg.l, dtype=torch.bfloat16, device="cuda"))
+    lm.forward(r, pk["x"], pk["w1"], pk["w3"], pk["w2"], y=y, wlayout=lm.LMOE_WLAYOUT_TILED)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
