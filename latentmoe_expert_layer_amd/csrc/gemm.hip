@@ -3,6 +3,8 @@
 // All operands are "[rows, K]" with K contiguous (activations [M,K], weights
 // [N,K] in the [out, in] layout), so C = A * B^T reads both operands along K.
 //
+//  * ring_dense_kernel: the dense projections at prefill (bf16 outputs),
+//    K streamed through a five-slot LDS ring by direct-to-LDS loads.
 //  * tiled_gemm_kernel: LDS double-buffered macro tiles for the dense
 //    projections (latent down-proj fused with the shared experts' gate/up,
 //    and the latent up-proj K-concatenated with the shared experts' down
@@ -713,9 +715,244 @@ __global__ __launch_bounds__(256) void splitk_router_kernel(SplitKArgs g, FrontR
   splitk_block(g, int(blockIdx.x) - nrb);
 }
 
+// ---------------------------------------------------- dense, five-slot ring ---
+// Dense projections on 256 x 256 output tiles (gated: 128 gate + 128 up B
+// rows), 8 waves as 2 x 4 with 128 x 64 wave tiles, as tiled_gemm_kernel, but
+// K goes through LDS in 32-wide stages that global_load_lds_dwordx4 writes
+// straight into a ring of five slots (no register staging; three stages in
+// flight behind the one being computed).  One barrier per stage: each wave
+// first waits for its own loads of stage s+1, so after the barrier stage s+1
+// is visible to all and the slot of stage s-1 is free for stage s+4.  Inside
+// a stage the second 16-K half's fragments are read while the first half's
+// MFMAs run, and the next stage's first-half fragments while the second
+// half's run.  A slot row is 64 B (32 bf16); its four 16-byte chunks sit
+// XOR-swizzled by (row / 4) % 4, so the 16 lanes of each ds_read_b128 phase
+// (16 consecutive rows, one chunk) hit 16 distinct 4-bank groups.  The MFMAs
+// and their K order are tiled_gemm_kernel's: the results are bit-identical.
+constexpr int kRingBK = 32;                 // K per stage
+constexpr int kRingRow = kRingBK * 2;       // bytes per slot row
+constexpr int kRingSlots = 5;
+constexpr int kRingStage = (256 + 256) * kRingRow;
+constexpr int kRingLds = kRingSlots * kRingStage;  // 160 KiB: all of a CU's LDS
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from gptr land at
+// LDS byte lds_base + 16 l.  Inline asm, so the compiler sees no LDS write that
+// it would order before every later LDS read (it cannot tell the ring slots
+// apart); the kernel orders them itself with vmcnt waits and barriers.
+__device__ __forceinline__ void g2lds16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void ring_dense_kernel(DenseGemm g) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = 256, BR = 256, NOUT = GATED ? 128 : 256, WAVES_N = 4, WM = BM / 2, WN = 64;
+  constexpr int FM = WM / 32, FN = 2, NS = kRingSlots, BK = kRingBK, ROWB = kRingRow;
+  constexpr int A_BYTES = BM * ROWB, STAGE = kRingStage;
+  constexpr int L = 4;  // 1 KB load instructions per wave and stage: 2 of A, 2 of B
+  extern __shared__ uint4 lds_u4[];
+  char* lds = reinterpret_cast<char*>(lds_u4);
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const int tiles_n = (g.N + NOUT - 1) / NOUT;
+  const uint32_t lt = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
+  const int row0 = tm * BM, nrows = min(BM, g.M - row0), n0 = tn * NOUT;
+  // wave w loads A and B rows 16w .. 16w+15 and 16(w+8) .. +15 of each stage;
+  // lane l: row l/4 of those 16, slot chunk l%4, global chunk (l%4)^((l/16)%4)
+  const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  int a_row[2], b_row[2];
+  bool b_up[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wid + 8 * i) * 16 + lrow;
+    a_row[i] = row0 + min(r, nrows - 1);
+    if constexpr (GATED) {
+      b_up[i] = r >= BR / 2;
+      b_row[i] = min(n0 + (b_up[i] ? r - BR / 2 : r), g.N - 1);
+    } else {
+      b_up[i] = false;
+      b_row[i] = min(n0 + r, g.N - 1);
+    }
+  }
+  const bf16_t* pa[2];
+  const bf16_t* pb[2];
+  auto set_seg = [&](const GemmSeg& sg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      pa[i] = reinterpret_cast<const bf16_t*>(sg.A) + int64_t(a_row[i]) * sg.lda + lchunk * 8;
+      pb[i] = reinterpret_cast<const bf16_t*>(b_up[i] ? sg.B3 : sg.B) + int64_t(b_row[i]) * sg.ldb + lchunk * 8;
+    }
+  };
+  set_seg(g.seg[0]);
+  int nk = 0;
+#pragma unroll
+  for (int q = 0; q < 5; ++q)
+    if (q < g.nseg) nk += g.seg[q].K / BK;
+  int ls = 0, lk = g.seg[0].K / BK;  // loader: segment, stages left in it
+  const int fr = lane & 31, sw = (fr >> 2) & 3;
+  const int off0 = fr * ROWB + (((lane >> 5) + 0) ^ sw) * 16;  // K 0..15 of a stage
+  const int off1 = fr * ROWB + (((lane >> 5) + 2) ^ sw) * 16;  // K 16..31
+  auto brow = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (GATED) return j == 0 ? wn * 32 : BR / 2 + wn * 32;
+    else return wn * WN + j * 32;
+  };
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
+    constexpr int FA = decltype(fa_c)::value;
+    bf16x8 a0[FA > 0 ? FA : 1], b0[FN], a1[FA > 0 ? FA : 1], b1[FN];
+    auto issue = [&](int stage) __attribute__((always_inline)) {
+      const uint32_t sb = uint32_t(__builtin_amdgcn_readfirstlane(int(lds0 + (stage % NS) * STAGE)));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        g2lds16(pa[i], sb + (wid + 8 * i) * 1024);
+        g2lds16(pb[i], sb + A_BYTES + (wid + 8 * i) * 1024);
+        pa[i] += BK;
+        pb[i] += BK;
+      }
+      if (--lk == 0 && ls + 1 < g.nseg) {
+        ++ls;
+        switch (ls) {  // (static indices: the arguments stay in the kernarg segment)
+          case 1: set_seg(g.seg[1]); lk = g.seg[1].K / BK; break;
+          case 2: set_seg(g.seg[2]); lk = g.seg[2].K / BK; break;
+          case 3: set_seg(g.seg[3]); lk = g.seg[3].K / BK; break;
+          default: set_seg(g.seg[4]); lk = g.seg[4].K / BK; break;
+        }
+      }
+    };
+    auto rd = [&](int stage, int off, bf16x8* af, bf16x8* bf) __attribute__((always_inline)) {
+      const char* sb = lds + (stage % NS) * STAGE;
+#pragma unroll
+      for (int i = 0; i < FA; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(sb + (wm * WM + i * 32) * ROWB + off));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bf[j] = as_bf16x8(*reinterpret_cast<const uint4*>(sb + A_BYTES + brow(j) * ROWB + off));
+    };
+    auto mm = [&](bf16x8* af, bf16x8* bf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FA; ++i) acc[i][j] = mfma_32x32x16(af[i], bf[j], acc[i][j]);
+    };
+    // stage s: W = stages allowed in flight behind stage s+1 at the top wait
+    // (-1: there is no stage s+1); ISSUE: load stage s+NS-1
+    auto step = [&](int s, auto w_c, auto issue_c) __attribute__((always_inline)) {
+      constexpr int W = decltype(w_c)::value;
+      constexpr bool ISSUE = decltype(issue_c)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (W >= 0) {
+        wait_vmcnt<W * L>();
+        __builtin_amdgcn_s_barrier();
+      }
+      if constexpr (ISSUE) issue(s + NS - 1);
+      if constexpr (FA > 0) {
+        rd(s, off1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (W >= 0) rd(s + 1, off0, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(a1, b1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int p = 0; p < NS - 1; ++p) issue(p);
+    wait_vmcnt<(NS - 2) * L>();
+    __builtin_amdgcn_s_barrier();
+    if constexpr (FA > 0) rd(0, off0, a0, b0);
+    int s = 0;
+    for (; s <= nk - NS; ++s) step(s, std::integral_constant<int, NS - 3>{}, std::true_type{});
+    static_assert(NS == 5, "the tail below drains a five-slot ring");
+    step(s, std::integral_constant<int, 2>{}, std::false_type{});
+    step(s + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    step(s + 2, std::integral_constant<int, 0>{}, std::false_type{});
+    step(s + 3, std::integral_constant<int, -1>{}, std::false_type{});
+  };
+  const int fa = max(0, min(FM, (nrows - wm * WM + 31) / 32));
+  switch (fa) {
+    case 0: mainloop(std::integral_constant<int, 0>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    case 2: mainloop(std::integral_constant<int, 2>{}); break;
+    case 3: mainloop(std::integral_constant<int, 3>{}); break;
+    default: mainloop(std::integral_constant<int, 4>{}); break;
+  }
+  __syncthreads();
+  // epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores
+  constexpr int CLD = NOUT + 8;
+  static_assert(BM * CLD * 2 <= kRingLds, "epilogue staging fits in the ring");
+  bf16_t* Cs = reinterpret_cast<bf16_t*>(lds);
+  constexpr int JO = GATED ? 1 : FN, WO = GATED ? 32 : WN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    if (i < fa)
+#pragma unroll
+      for (int j = 0; j < JO; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int col = wn * WO + j * 32 + (lane & 31);
+          float x = acc[i][j][v];
+          if constexpr (GATED) x = silu_mul(x, acc[i][1][v]);
+          Cs[row * CLD + col] = f32_to_bf16(x);
+        }
+  __syncthreads();
+  constexpr int OCPR = NOUT / 8;
+  for (int c = tid; c < BM * OCPR; c += 512) {
+    const int row = c / OCPR, cc = c % OCPR;
+    if (row < nrows && n0 + cc * 8 < g.N)
+      *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(g.C) + (int64_t(row0) + row) * g.ldc + n0 + cc * 8) =
+          *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
+  }
+#endif
+}
+
+// The ring kernel takes bf16 outputs and segments whose K are multiples of
+// 32, at least 4 stages in all.
+bool ring_fits(const DenseGemm& d) {
+  if (d.Cf || d.nseg < 1 || d.nseg > 5 || d.M <= 0 || d.N <= 0) return false;
+  int nk = 0;
+  for (int i = 0; i < d.nseg; ++i) {
+    if (d.seg[i].K <= 0 || d.seg[i].K % kRingBK) return false;
+    nk += d.seg[i].K / kRingBK;
+  }
+  return nk >= kRingSlots - 1;
+}
+
+template <bool GATED>
+hipError_t run_ring(const DenseGemm& d, hipStream_t s) {
+  constexpr int NOUT = GATED ? 128 : 256;
+  auto kern = ring_dense_kernel<GATED>;
+  if (hipError_t e = allow_dynamic_lds((const void*)kern, kRingLds); e != hipSuccess) return e;
+  const int64_t nblk = int64_t((d.M + 255) / 256) * ((d.N + NOUT - 1) / NOUT);
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3{uint32_t(nblk)}, dim3{512u}, kRingLds, s, d);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
+  if (ring_fits(d)) return d.gated ? run_ring<true>(d, s) : run_ring<false>(d, s);
   TiledArgs a{};
   a.M = d.M;
   a.N = d.N;
