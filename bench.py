@@ -40,7 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the w4a8 expert GEMMs issue at the fp8 rate)
 LLC_BYTES = 256 << 20          # MI355X Infinity Cache
 METRIC = "LatentMoE layer tokens/s at 1 GPU; grouped-GEMM TFLOP/s as % MFMA peak"
-DEFAULT_EXTRA = "prefill@tiled,decode,decode_os,decode_w4a16,decode_w4a16_os,prefill_mxfp4,ep_share"
+DEFAULT_EXTRA = "prefill@tiled,prefill_bf16_16k,decode,decode_os,decode_w4a16,decode_w4a16_os,prefill_mxfp4,prefill_w4a16,ep_share"
 
 
 def parse():
@@ -223,15 +223,18 @@ class ClockSampler:
 def grouped_kernel(cfg, dom, fused_mlp):
     """Which kernel runs the grouped GEMM ``dom`` (the library's own choice:
     MXFP4 w4a8 -> block-scaled kernel; MXFP4 w4a16 -> its weight-streaming
-    kernels; <= 32 rows per expert on average -> weight-streaming kernel;
-    otherwise the LDS-tiled grouped kernel when K is a multiple of 128 and at
-    least 256, else the general tiled kernel)."""
+    kernels at <= 32 rows per expert on average, else the LDS-tiled grouped
+    kernel in its MXFP4 form; bf16 at <= 32 rows per expert on average ->
+    weight-streaming kernel; otherwise the LDS-tiled grouped kernel when K is
+    a multiple of 128 and at least 256, else the general tiled kernel)."""
     R = cfg.T * cfg.k
     K = cfg.l if dom == "fc1" else cfg.I
     if fused_mlp:
         return "skinny_w4a16_mlp_kernel", "skinny.hip"
     if cfg.mxfp4 and cfg.w4a16:
-        return "skinny_w4a16_kernel", "skinny.hip"
+        if R <= 32 * cfg.E:
+            return "skinny_w4a16_kernel", "skinny.hip"
+        return "grouped_tiled_kernel (MXFP4 w4a16)", "gemm.hip"
     if cfg.mxfp4:
         return "mx_grouped_kernel", "mx.hip"
     if R <= 32 * cfg.E:
@@ -505,7 +508,7 @@ def measure(cfg, args, hip, lm, W, torch, stream, clock=None, wlayout="tiled"):
 
     # the library runs the w4a16 expert MLP at latent = intermediate = 256 as
     # one launch (its duration is the FC1 stage; H never reaches HBM)
-    fused_mlp = cfg.mxfp4 and cfg.w4a16 and l == 256 and I == 256
+    fused_mlp = cfg.mxfp4 and cfg.w4a16 and l == 256 and I == 256 and cfg.T * cfg.k <= 32 * cfg.E
     fp8 = cfg.mxfp4 and not cfg.w4a16   # w4a8 issues at the fp8 rate; w4a16 multiplies in bf16
     mfma_peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
     roofline = None

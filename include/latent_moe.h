@@ -65,10 +65,13 @@ enum { LMOE_OK = 0, LMOE_EINVAL = 1, LMOE_EUNSUPPORTED = 2, LMOE_EHIP = 3 };
  *                        fp8 x fp4 MFMA (the large-batch mode).
  *  LMOE_WFMT_MXFP4_W4A16 the same MXFP4 weights, "w4a16": activations stay bf16;
  *                        the weights are upcast to bf16 inside the K loop and
- *                        multiplied on bf16 MFMAs (the small-batch mode, TokenSpeed
- *                        Day-0 post, "TensorRT-LLM Stable LatentMoE").  Only
- *                        decode-shaped batches (T*k <= 32*E): a larger batch
- *                        returns LMOE_EUNSUPPORTED and nothing is enqueued. */
+ *                        multiplied on bf16 MFMAs (TokenSpeed Day-0 post,
+ *                        "TensorRT-LLM Stable LatentMoE" and "Gluon kernels on
+ *                        AMD GPUs > Stable LatentMoE").  Decode-shaped batches
+ *                        (T*k <= 32*E) run weight-streaming kernels; larger ones
+ *                        the tiled expert GEMMs, which upcast a stage's weights
+ *                        on their way into LDS and need l, I >= 256 (else
+ *                        LMOE_EUNSUPPORTED, nothing enqueued). */
 enum { LMOE_WFMT_BF16 = 0, LMOE_WFMT_MXFP4 = 1, LMOE_WFMT_MXFP4_W4A16 = 2 };
 /* Storage of bf16 routed-expert weights (lmoe_forward_args.wlayout):
  *  LMOE_WLAYOUT_ROWS   row-major [E, N, K] (the layout every shape below names).
@@ -251,8 +254,8 @@ int latent_moe_layer(const lmoe_route_args* route, const void* w_router, float* 
  * expert's (token, slot) rows by scanning topk_ids itself.  No permutation or
  * tile table is built, H and Y are kept in (token, slot) order, and the
  * combine reads Y there.  Where latent_moe_layer runs its weight-streaming
- * kernels (T*k <= 32*E, and always for MXFP4 w4a16) the results are equal to
- * its results bit for bit: each row meets the same MFMAs in the same K order.
+ * kernels (T*k <= 32*E) the results are equal to its results bit for bit:
+ * each row meets the same MFMAs in the same K order.
  * Arguments as for latent_moe_layer with the logits given (w_router NULL):
  *   route   logits != NULL, ids_in == NULL; topk_ids and topk_w receive the
  *           routing; sorted_row, row_pos, offsets and workspace are not used

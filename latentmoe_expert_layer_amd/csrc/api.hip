@@ -274,11 +274,9 @@ int fwd_check(const latent_moe_plan* p, const lmoe_forward_args* a) {
                         a->w_out, a->ws1, a->ws3, a->ws2, a->y, a->workspace};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return fail(LMOE_EINVAL, "device pointer %p is not 16-byte aligned", q);
-  const int64_t R = p->T * p->k;
-  if (a->wfmt == LMOE_WFMT_MXFP4_W4A16 && R > int64_t(32) * p->E)
+  if (a->wfmt == LMOE_WFMT_MXFP4_W4A16 && p->T * p->k > int64_t(32) * p->E && (a->l < 256 || a->I < 256))
     return fail(LMOE_EUNSUPPORTED,
-                "MXFP4 w4a16 runs decode-shaped batches only (T*k=%lld > 32*E=%lld); use LMOE_WFMT_MXFP4 (w4a8)",
-                (long long)R, 32LL * p->E);
+                "MXFP4 w4a16 beyond T*k <= 32*E runs the tiled expert GEMMs: l and I >= 256 (got %d, %d)", a->l, a->I);
   const int32_t S = rows ? 0 : a->S;
   const size_t need = fwd_layout(p->T, p->k, a->l, a->I, S, S ? a->Is : 0, rows, a->wfmt == LMOE_WFMT_MXFP4).total;
   if (!a->workspace || a->workspace_bytes < need)
@@ -506,6 +504,45 @@ int fwd_back(const FwdCtx& c) {
     m2.C = Y;
     m2.ldc = l;
     if ((e = lmoe::launch_grouped_mx(m2, s)) != hipSuccess) return hip_fail(e, "expert FC2 (MXFP4)");
+    if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
+  } else if (w4a16 && R > int64_t(32) * p->E) {
+    // w4a16 beyond decode-shaped batches: the tiled grouped GEMMs, weights
+    // upcast to bf16 on their way into LDS
+    lmoe::GroupedGemm t1{};
+    t1.N = int(I);
+    t1.K = int(l);
+    t1.A = rows ? x : z;
+    t1.lda = l;
+    t1.a_rows = p->sorted_row;
+    t1.a_row_div = p->k;
+    t1.B = static_cast<const uint16_t*>(a->w1);
+    t1.B3 = static_cast<const uint16_t*>(a->w3);
+    t1.w4 = true;
+    t1.Bs = a->s1;
+    t1.B3s = a->s3;
+    t1.gated = true;
+    t1.C = H;
+    t1.ldc = I;
+    t1.tiles = p->tiles_t;
+    t1.ntiles = p->n_t;
+    t1.max_tiles = p->max_t;
+    if ((e = lmoe::launch_grouped_tiled(t1, s, fc1_t0, fc1_t1)) != hipSuccess)
+      return hip_fail(e, "expert FC1 (MXFP4 w4a16, tiled)");
+    lmoe::GroupedGemm t2 = t1;
+    t2.N = int(l);
+    t2.K = int(I);
+    t2.A = H;
+    t2.lda = I;
+    t2.a_rows = nullptr;
+    t2.a_row_div = 1;
+    t2.B = static_cast<const uint16_t*>(a->w2);
+    t2.B3 = nullptr;
+    t2.Bs = a->s2;
+    t2.B3s = nullptr;
+    t2.gated = false;
+    t2.C = Y;
+    t2.ldc = l;
+    if ((e = lmoe::launch_grouped_tiled(t2, s)) != hipSuccess) return hip_fail(e, "expert FC2 (MXFP4 w4a16, tiled)");
     if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
   } else if (w4a16 && l == lmoe::kW4MlpWidth && I == lmoe::kW4MlpWidth) {
     // w4a16 at the 256 x 256 decode shape: FC1, SwiGLU and FC2 in one launch

@@ -341,7 +341,14 @@ hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s, hipEvent
 // MFMAs in the same K order).  Needs K a multiple of 128 and >= 256.
 // PACKED: the weights are in the tile-packed layout (kernels.h): a stage's
 // 128-row block of B is 16 KB of contiguous memory.
-template <bool GATED, bool PACKED = false>
+// W4: MXFP4 weights with bf16 activations (w4a16 at prefill size; TokenSpeed
+// Day-0 post, "Gluon kernels on AMD GPUs > Stable LatentMoE": weights upcast
+// in the K loop, activations in bf16): per stage each thread loads the 16 code
+// bytes (32 e2m1 values, one MX block) of one B row's K half and its e8m0
+// scale, two stages ahead, and writes them to LDS as 32 bf16 values (gfx950's
+// scaled conversion: exact, an e2m1 value times a power of two); the MFMA loop
+// is the bf16 one.
+template <bool GATED, bool PACKED = false, bool W4 = false>
 __global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
   constexpr int NTH = 512, BM = kTiledBM, BR = 256, NOUT = GATED ? 128 : 256;
   constexpr int WAVES_N = 4, WM = BM / 2, WN = BR / WAVES_N;
@@ -380,21 +387,36 @@ __global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
     pa[i] = g.A + int64_t(src) * g.lda + kc8;
   }
   const int64_t be = int64_t(expert) * g.b_estride;
+  if constexpr (!W4) {
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const bool up = GATED && i >= B_CH / 2;
-    const int r = (up ? i - B_CH / 2 : i) * RPC + tid / CPR;
-    const int n = min(n0 + r, g.N - 1);
-    if constexpr (PACKED) {
-      pb[i] = (up ? g.B3 : g.B) + be + int64_t(n / kPackRows) * g.K * kPackRows + (n % kPackRows) * kBK + kc8;
-    } else {
-      pb[i] = (up ? g.B3 : g.B) + be + int64_t(n) * g.ldb + kc8;
+    for (int i = 0; i < B_CH; ++i) {
+      const bool up = GATED && i >= B_CH / 2;
+      const int r = (up ? i - B_CH / 2 : i) * RPC + tid / CPR;
+      const int n = min(n0 + r, g.N - 1);
+      if constexpr (PACKED) {
+        pb[i] = (up ? g.B3 : g.B) + be + int64_t(n / kPackRows) * g.K * kPackRows + (n % kPackRows) * kBK + kc8;
+      } else {
+        pb[i] = (up ? g.B3 : g.B) + be + int64_t(n) * g.ldb + kc8;
+      }
     }
+  }
+  // W4: thread tid covers B tile row tid/2 (gated: rows >= 128 from B3), K
+  // half tid%2 of each stage: code bytes qb (16 per stage half), scale qs
+  const uint8_t* qb = nullptr;
+  const uint8_t* qs = nullptr;
+  if constexpr (W4) {
+    const int r = tid >> 1, h = tid & 1;
+    const bool up = GATED && r >= BR / 2;
+    const int n = min(n0 + (up ? r - BR / 2 : r), g.N - 1);
+    const int64_t row = int64_t(expert) * g.N + n;
+    qb = reinterpret_cast<const uint8_t*>(up ? g.B3 : g.B) + row * (g.K / 2) + h * 16;
+    qs = (up ? g.B3s : g.Bs) + row * (g.K / 32) + h;
   }
   // B advances one stage: kBK columns of a row, or one packed block
   constexpr int BSTEP = PACKED ? kPackRows * kBK : kBK;
   const int nk = g.K / kBK;
-  uint4 ra[A_CH], rbx[B_CH], rby[B_CH];  // A one stage ahead; B stages alternate between X and Y
+  uint4 ra[A_CH], rbx[W4 ? 1 : B_CH], rby[W4 ? 1 : B_CH];  // A one stage ahead; B stages alternate X / Y
+  uint32_t sbx = 0, sby = 0;                                  // W4: the e8m0 scale codes of X / Y
   auto load_a = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
@@ -405,18 +427,41 @@ __global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
   // (separate code for the two B sets: a lambda taking either set by
   // reference would move them to memory)
   auto load_bx = [&]() __attribute__((always_inline)) {
+    if constexpr (W4) {
+      rbx[0] = *reinterpret_cast<const uint4*>(qb);
+      sbx = *qs;
+      qb += kBK / 2;
+      qs += kBK / 32;
+    } else {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      rbx[i] = ldg16(pb[i]);
-      pb[i] += BSTEP;
+      for (int i = 0; i < B_CH; ++i) {
+        rbx[i] = ldg16(pb[i]);
+        pb[i] += BSTEP;
+      }
     }
   };
   auto load_by = [&]() __attribute__((always_inline)) {
+    if constexpr (W4) {
+      rby[0] = *reinterpret_cast<const uint4*>(qb);
+      sby = *qs;
+      qb += kBK / 2;
+      qs += kBK / 32;
+    } else {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      rby[i] = ldg16(pb[i]);
-      pb[i] += BSTEP;
+      for (int i = 0; i < B_CH; ++i) {
+        rby[i] = ldg16(pb[i]);
+        pb[i] += BSTEP;
+      }
     }
+  };
+  // W4: 32 e2m1 codes and their scale -> 32 bf16 at B row tid/2, K half tid%2
+  auto store_w4 = [&](bf16_t* Bn, const uint4& q, uint32_t sc) __attribute__((always_inline)) {
+    const float f = e8m0_multiplier(sc);
+    bf16_t* dst = &Bn[(tid >> 1) * kLdsK + (tid & 1) * 32];
+    *reinterpret_cast<bf16x8*>(dst + 0) = fp4x8_to_bf16(q.x, f);
+    *reinterpret_cast<bf16x8*>(dst + 8) = fp4x8_to_bf16(q.y, f);
+    *reinterpret_cast<bf16x8*>(dst + 16) = fp4x8_to_bf16(q.z, f);
+    *reinterpret_cast<bf16x8*>(dst + 24) = fp4x8_to_bf16(q.w, f);
   };
   auto store_a = [&](int buf) __attribute__((always_inline)) {
     bf16_t* An = As + buf * BM * kLdsK;
@@ -428,18 +473,26 @@ __global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
   };
   auto store_bx = [&](int buf) __attribute__((always_inline)) {
     bf16_t* Bn = Bs + buf * BR * kLdsK;
+    if constexpr (W4) {
+      store_w4(Bn, rbx[0], sbx);
+    } else {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NTH;
-      *reinterpret_cast<uint4*>(&Bn[(c / CPR) * kLdsK + (c % CPR) * 8]) = rbx[i];
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + i * NTH;
+        *reinterpret_cast<uint4*>(&Bn[(c / CPR) * kLdsK + (c % CPR) * 8]) = rbx[i];
+      }
     }
   };
   auto store_by = [&](int buf) __attribute__((always_inline)) {
     bf16_t* Bn = Bs + buf * BR * kLdsK;
+    if constexpr (W4) {
+      store_w4(Bn, rby[0], sby);
+    } else {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NTH;
-      *reinterpret_cast<uint4*>(&Bn[(c / CPR) * kLdsK + (c % CPR) * 8]) = rby[i];
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + i * NTH;
+        *reinterpret_cast<uint4*>(&Bn[(c / CPR) * kLdsK + (c % CPR) * 8]) = rby[i];
+      }
     }
   };
   f32x16 acc[FM][FN];
@@ -550,11 +603,11 @@ __global__ __launch_bounds__(512, 1) void grouped_tiled_kernel(GroupedGemm g) {
   }
 }
 
-template <bool GATED, bool PACKED>
+template <bool GATED, bool PACKED, bool W4 = false>
 hipError_t run_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   constexpr int NOUT = GATED ? 128 : 256;
   const size_t lds = size_t(2) * (kTiledBM + 256) * kLdsK * sizeof(bf16_t);
-  auto kern = grouped_tiled_kernel<GATED, PACKED>;
+  auto kern = grouped_tiled_kernel<GATED, PACKED, W4>;
   if (hipError_t e = allow_dynamic_lds((const void*)kern, int(lds)); e != hipSuccess) return e;
   const int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
@@ -986,6 +1039,11 @@ hipError_t launch_pack_weights(const uint16_t* src, uint16_t* dst, int E, int N,
 hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   // routing cuts tiles at kTiledBM rows; both kernels take tiles of up to 192 rows
   static_assert(kTiledBM <= 192, "tile table granularity");
+  if (g.w4) {
+    // (the bf16 fallback below has no MXFP4 form)
+    if (g.packed || g.K % 128 || g.K < 256 || !g.Bs || (g.gated && !g.B3s)) return hipErrorInvalidValue;
+    return g.gated ? run_grouped<true, false, true>(g, s, t0, t1) : run_grouped<false, false, true>(g, s, t0, t1);
+  }
   if (g.K % 128 == 0 && g.K >= 256) {
     if (g.packed) return g.gated ? run_grouped<true, true>(g, s, t0, t1) : run_grouped<false, true>(g, s, t0, t1);
     return g.gated ? run_grouped<true, false>(g, s, t0, t1) : run_grouped<false, false>(g, s, t0, t1);

@@ -125,6 +125,12 @@ struct GroupedGemm {
   const int32_t* os_ids;
   int64_t os_R;
   bool packed;  // B and B3 in the tile-packed layout (b_estride = N*K, ldb unused)
+  // w4a16 (launch_grouped_tiled only): B and B3 point to e2m1 codes [E, N, K/2]
+  // (even K in the low nibble) with e8m0 scales Bs / B3s [E, N, K/32], upcast
+  // to bf16 on their way into LDS; ldb and b_estride are unused
+  bool w4;
+  const uint8_t* Bs;
+  const uint8_t* B3s;
 };
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Output-stationary decode (TokenSpeed Day-0 post, "Gluon kernels on AMD GPUs >

@@ -332,25 +332,6 @@ __global__ __launch_bounds__(256) void skinny_lds_kernel(GroupedGemm g) {
 // s of the chunk multiplies codes 8s .. 8s+7 of them, so lane gq of step s
 // covers K = chunk + 32*gq + 8s .. +8; the A fragments take the same K order.
 
-// e8m0 scale code -> the fp32 multiplier 2^(code-127) (code 0: 2^-127, a
-// denormal; 255: NaN), the operand the scaled conversion takes.
-__device__ __forceinline__ float e8m0_multiplier(uint32_t c) {
-  return __uint_as_float(c == 0 ? 0x00400000u : (c == 255 ? 0x7fc00000u : c << 23));
-}
-
-// 8 e2m1 codes (one dword, K ascending from the low nibble) x scale -> bf16x8.
-__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
-  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
-  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
-  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
-  const bf16x4_t lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
-  const bf16x4_t hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 template <bool GATED, int NCH, int NS>
 __global__ __launch_bounds__(256) void skinny_w4a16_kernel(GroupedW4 g) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;

@@ -29,7 +29,7 @@ def expert_tile_rows(cfg):
     R = cfg.T * cfg.k
     if cfg.mxfp4 and not cfg.w4a16:
         return TILED_BM
-    if cfg.w4a16 or R <= 32 * cfg.E:
+    if R <= 32 * cfg.E:
         return SKINNY_BM
     return TILED_BM
 

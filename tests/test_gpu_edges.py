@@ -106,14 +106,17 @@ TOPS_W4A8 = [30, 60, 90, 120, 150, 180, 210, 240, 254]
 TOPS_W4A16 = [32, 60, 90, 120, 150, 180, 210, 240, 252]
 
 
-@pytest.mark.parametrize("w4a16", [False, True], ids=["w4a8", "w4a16"])
+@pytest.mark.parametrize("fmt", ["w4a8", "w4a16", "w4a16_tiled"])
 @pytest.mark.parametrize("which", ["fc1", "fc2"])
-def test_mxfp4_block_scales_across_the_code_range(w4a16, which):
+def test_mxfp4_block_scales_across_the_code_range(fmt, which):
+    w4a16 = fmt != "w4a8"
     tops = TOPS_W4A16 if w4a16 else TOPS_W4A8
     lo_code = 2 if w4a16 else 0
     E = len(tops)
-    # w4a16 serves decode-shaped batches (at most 32 rows per expert on average)
-    cfg = rows_cfg(f"scales_{which}", 280 if w4a16 else 900, E, 256, 256, w4a16, 31 + (which == "fc2"))
+    # w4a16: 280 rows (at most 32 per expert on average) run the weight-streaming
+    # kernels, 900 rows the tiled ones
+    rows = 280 if fmt == "w4a16" else 900
+    cfg = rows_cfg(f"scales_{which}", rows, E, 256, 256, w4a16, 31 + (which == "fc2"))
     inp = W.make_inputs(cfg)
     ids = inp["ids"].view(-1).long()
     x = inp["x"].float()
@@ -153,11 +156,13 @@ def test_mxfp4_block_scales_across_the_code_range(w4a16, which):
                      budget=W4A8_H_CODE_BUDGET)
 
 
-@pytest.mark.parametrize("w4a16", [False, True], ids=["w4a8", "w4a16"])
-def test_mxfp4_nan_block_scale(w4a16):
+@pytest.mark.parametrize("fmt", ["w4a8", "w4a16", "w4a16_tiled"])
+def test_mxfp4_nan_block_scale(fmt):
     """e8m0 code 255 is NaN: one block of expert 2's W1 carries it, so exactly
-    the rows routed to expert 2 come out NaN."""
-    cfg = rows_cfg("scale_nan", 150 if w4a16 else 300, 5, 256, 256, w4a16, 41)
+    the rows routed to expert 2 come out NaN (w4a16: 150 rows over 5 experts
+    run the weight-streaming kernels, 600 the tiled ones)."""
+    w4a16 = fmt != "w4a8"
+    cfg = rows_cfg("scale_nan", 150 if fmt == "w4a16" else (600 if w4a16 else 300), 5, 256, 256, w4a16, 41)
     inp = W.make_inputs(cfg)
     inp["s1"][2, 7, 3] = 255
     r, y, views = run_gpu_layer(to_device(inp))

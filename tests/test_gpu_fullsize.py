@@ -27,7 +27,7 @@ def _lib():
     yield
 
 
-@pytest.mark.parametrize("name", ["prefill", "prefill_mxfp4"])
+@pytest.mark.parametrize("name", ["prefill", "prefill_bf16_16k", "prefill_mxfp4", "prefill_w4a16"])
 def test_full_size_every_tile(name):
     cfg = W.CONFIGS[name]
     log(f"full-size {name}: {cfg}")

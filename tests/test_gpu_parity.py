@@ -260,6 +260,10 @@ W4A16_LAYERS = [
     ("w4_single", dict(T=1, d=128, l=128, E=16, k=4, S=0, I=128, Is=0, mxfp4=True, w4a16=True)),
     # latent = intermediate = 256 (the one-launch expert MLP) with ragged T and experts without rows
     ("w4_fused_ragged", dict(T=77, d=128, l=256, E=40, k=8, S=2, I=256, Is=64, mxfp4=True, w4a16=True)),
+    # beyond T*k <= 32*E: the tiled expert GEMMs (192-row tiles; ~250 rows per expert, two tiles each)
+    ("w4_tiled", dict(T=1000, d=128, l=256, E=8, k=2, S=1, I=256, Is=64, mxfp4=True, w4a16=True)),
+    # tiled, FC1 over 3 and FC2 over 2 column tiles, ragged tile tails
+    ("w4_tiled_wide", dict(T=701, d=128, l=512, E=6, k=2, S=0, I=384, Is=0, mxfp4=True, w4a16=True)),
 ]
 
 
@@ -277,9 +281,13 @@ def test_w4a16_layer_parity(name, dims, norm):
     check_layer(inp, ids, w, y, views, act_quant=False)
 
 
-def test_w4a16_rows_mode():
-    """w4a16 on one expert-parallel rank's received rows (k = 1, Zipf load)."""
-    cfg = W.custom("w4_rows", T=600, d=0, l=256, E=56, k=1, S=0, I=256, Is=0, rows_mode=True, norm=False,
+@pytest.mark.parametrize("rows", [600, 3000], ids=["weight_streaming", "tiled"])
+def test_w4a16_rows_mode(rows):
+    """w4a16 on one expert-parallel rank's received rows (k = 1, Zipf load):
+    600 rows over 56 experts run the weight-streaming kernels, 3000 rows over
+    8 experts the tiled ones (the heaviest expert spans many tiles)."""
+    E = 56 if rows == 600 else 8
+    cfg = W.custom("w4_rows", T=rows, d=0, l=256, E=E, k=1, S=0, I=256, Is=0, rows_mode=True, norm=False,
                    zipf_s=1.1, seed=5, mxfp4=True, w4a16=True)
     log(f"w4a16 rows mode: {cfg}")
     inp_dev = W.make_inputs(cfg, device="cuda")
@@ -289,8 +297,9 @@ def test_w4a16_rows_mode():
     check_layer(inp, inp["ids"], inp["weights"], y, views, act_quant=False)
 
 
-def test_w4a16_rejects_large_batches():
-    """w4a16 serves decode-shaped batches only; a larger one is refused before
+def test_w4a16_tiled_needs_l_and_I_of_256():
+    """Beyond T*k <= 32*E w4a16 runs the tiled expert GEMMs, which need l and
+    I >= 256; a batch that would need them with l = I = 128 is refused before
     anything is enqueued (the output keeps its poison)."""
     cfg = W.custom("w4_big", T=600, d=128, l=128, E=8, k=2, S=0, I=128, Is=0, mxfp4=True, w4a16=True)
     inp_dev = to_device(W.make_inputs(cfg))

@@ -69,6 +69,12 @@ CONFIGS = {
     # prefill shape at 16384 tokens with MXFP4 routed experts
     "prefill_mxfp4": LayerConfig("prefill_mxfp4", T=16384, d=7168, l=2048, E=896, k=16, S=2,
                                  I=512, Is=512, mxfp4=True),
+    # the 16384-token prefill shape with bf16 routed experts (~293 rows per expert)
+    "prefill_bf16_16k": LayerConfig("prefill_bf16_16k", T=16384, d=7168, l=2048, E=896, k=16, S=2,
+                                    I=512, Is=512),
+    # the 16384-token prefill shape with MXFP4 routed experts and bf16 activations (w4a16)
+    "prefill_w4a16": LayerConfig("prefill_w4a16", T=16384, d=7168, l=2048, E=896, k=16, S=2,
+                                 I=512, Is=512, mxfp4=True, w4a16=True),
     # the decode batch with MXFP4 routed experts and bf16 activations (w4a16)
     "decode_w4a16": LayerConfig("decode_w4a16", T=256, d=512, l=256, E=896, k=16, S=2, I=256, Is=256,
                                 mxfp4=True, w4a16=True),
