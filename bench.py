@@ -212,6 +212,17 @@ class ClockSampler:
             self._stop.set()
             th.join()
 
+    def close(self):
+        """End the amdsmi session (opened in _setup), so nothing of it
+        outlives the run."""
+        if self._read is not None:
+            try:
+                import amdsmi
+                amdsmi.amdsmi_shut_down()
+            except Exception:
+                pass
+            self._read = None
+
     def summary(self):
         if not self.samples:
             return None
@@ -681,6 +692,11 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(line), flush=True)
+    # leave nothing behind: the amdsmi session, then the device memory
+    if clock is not None:
+        clock.close()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return 0
 
 
