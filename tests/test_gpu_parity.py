@@ -128,6 +128,13 @@ SMALL_LAYERS = [
     ("tiled_path", dict(T=600, d=256, l=512, E=8, k=2, S=1, I=256, Is=128)),
     # LDS-tiled dense projections with a ragged last row tile, odd latent width
     ("mid_ragged", dict(T=1000, d=320, l=192, E=24, k=4, S=2, I=128, Is=64)),
+    # dense projections above 512 tokens with short K: d = 64 (two 32-wide
+    # stages) is below the five-slot ring's minimum of four and takes the
+    # two-buffer kernel; the up-projection's three K segments of 64 switch
+    # segments inside the ring's prologue
+    ("short_k", dict(T=700, d=64, l=64, E=8, k=2, S=2, I=64, Is=64)),
+    # the ring's minimum: four stages in all (up-proj 64 + 64), one segment switch
+    ("ring_min", dict(T=530, d=128, l=64, E=6, k=3, S=1, I=128, Is=64)),
     # weight-streaming experts over several K batches: FC1 K = 512 (two of 256), FC2 K = 384 (three of 128)
     ("skinny_wide", dict(T=100, d=256, l=512, E=64, k=4, S=1, I=384, Is=128)),
     # wide latents: the combine splits a token's row over 4 or 2 waves (with two
