@@ -3,8 +3,11 @@
 // All operands are "[rows, K]" with K contiguous (activations [M,K], weights
 // [N,K] in the [out, in] layout), so C = A * B^T reads both operands along K.
 //
-//  * ring_dense_kernel: the dense projections at prefill (bf16 outputs),
-//    K streamed through a five-slot LDS ring by direct-to-LDS loads.
+//  * ring64_dense_kernel: the dense projections at prefill (bf16 outputs,
+//    K a multiple of 64), K streamed through LDS in 64-wide stages by
+//    direct-to-LDS loads of whole 128-byte lines, a ring of half stages.
+//  * ring_dense_kernel: the same with 32-wide stages in a five-slot ring, for
+//    K a multiple of 32 only.
 //  * tiled_gemm_kernel: LDS double-buffered macro tiles for the dense
 //    projections (latent down-proj fused with the shared experts' gate/up,
 //    and the latent up-proj K-concatenated with the shared experts' down
@@ -978,6 +981,293 @@ __global__ __launch_bounds__(512, 1) void ring_dense_kernel(DenseGemm g) {
 #endif
 }
 
+// ------------------------------------- dense, 64-wide stages, half-stage ring ---
+// Dense projections with the tile and wave layout of ring_dense_kernel (256 x
+// 256 output tiles, gated: 128 gate + 128 up B rows; 8 waves as 2 x 4 with 128
+// x 64 wave tiles), but K goes through LDS in 64-wide stages: a row of a
+// stage is 128 bytes, so each direct-to-LDS instruction (8 rows x 128 B) asks
+// L2 for whole 128-byte lines.  With 32-wide stages every request is half a
+// line and the same loads reach ~13 TB/s into LDS across the chip, against
+// ~21 TB/s for whole lines.  A 64-wide stage takes 64 KB, so the 160 KB of LDS
+// is a ring of five 32 KB entries, each holding one operand's half of a stage:
+// stage s keeps A in entry 2s mod 5 and B in entry 2s+1 mod 5.  One barrier
+// per stage, before its last 16-K step: each wave first waits for its LDS reads
+// (lgkmcnt) and for its loads of stage s+1, so after the barrier stage s+1 is
+// visible and both entries of stage s are free.  Under that last step's MFMAs
+// go, in this order, the loads of B(s+2) into stage s's A entry, the reads of
+// stage s+1's first fragments and the loads of A(s+3) into stage s's B entry;
+// in flight behind the stage being computed are 1.5 stages (A two stages
+// ahead, B one).  The waits count on that order (vmcnt is in order: B(s+1) has
+// arrived once at most A(s+2)'s loads remain).  Rows are 128 B with
+// the eight 16-byte chunks XOR-swizzled by (row / 2) mod 8, so the 16 lanes of
+// each ds_read_b128 phase (16 consecutive rows, one chunk) hit 16 distinct
+// 4-bank groups.  Same MFMAs in the same K order as tiled_gemm_kernel: the
+// results are bit-identical.  Needs every segment's K a multiple of 64 and at
+// least 3 stages in all.
+constexpr int kR64BK = 64;                // K per stage
+constexpr int kR64Row = kR64BK * 2;       // bytes per LDS row
+constexpr int kR64Ent = 256 * kR64Row;    // one operand's half of a stage: 32 KB
+constexpr int kR64Lds = 5 * kR64Ent;      // 160 KiB: all of a CU's LDS
+
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = 8, NTH = NW * 64, WAVES_N = 4;
+  constexpr int BM = 256, BR = 256, NOUT = GATED ? 128 : 256, WM = 128, WN = 64;
+  constexpr int FM = WM / 32, FN = WN / 32, BK = kR64BK, ROWB = kR64Row, ENT = kR64Ent;
+  constexpr int LH = 32 / NW;  // 1 KB load instructions per wave and half stage
+  extern __shared__ uint4 lds_u4[];
+  char* lds = reinterpret_cast<char*>(lds_u4);
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const int tiles_n = (g.N + NOUT - 1) / NOUT;
+  const uint32_t lt = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
+  const int row0 = tm * BM, nrows = min(BM, g.M - row0), n0 = tn * NOUT;
+  // wave w loads the 8-row groups w, w+8, w+16, w+24 of each half stage; lane
+  // l: row l/8 of the group into slot chunk l%8, from global chunk
+  // (l%8) ^ ((row/2)%8) (row/2 mod 8 = 4 (group mod 2) + (l/8)/2, and the
+  // group's parity is the wave's)
+  const int lr = lane >> 3;
+  const int gchunk = (lane & 7) ^ ((((wid & 1) << 2) + (lr >> 1)) & 7);
+  int a_row[LH], b_row[LH];
+  bool b_up[LH];
+#pragma unroll
+  for (int i = 0; i < LH; ++i) {
+    const int r = (wid + NW * i) * 8 + lr;
+    a_row[i] = row0 + min(r, nrows - 1);
+    if constexpr (GATED) {
+      b_up[i] = r >= BR / 2;
+      b_row[i] = min(n0 + (b_up[i] ? r - BR / 2 : r), g.N - 1);
+    } else {
+      b_up[i] = false;
+      b_row[i] = min(n0 + r, g.N - 1);
+    }
+  }
+  const bf16_t* pa[LH];
+  const bf16_t* pb[LH];
+  auto set_a = [&](const GemmSeg& sg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LH; ++i) pa[i] = reinterpret_cast<const bf16_t*>(sg.A) + int64_t(a_row[i]) * sg.lda + gchunk * 8;
+  };
+  auto set_b = [&](const GemmSeg& sg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LH; ++i)
+      pb[i] = reinterpret_cast<const bf16_t*>(b_up[i] ? sg.B3 : sg.B) + int64_t(b_row[i]) * sg.ldb + gchunk * 8;
+  };
+  set_a(g.seg[0]);
+  set_b(g.seg[0]);
+  int nk = 0;
+#pragma unroll
+  for (int q = 0; q < 5; ++q)
+    if (q < g.nseg) nk += g.seg[q].K / BK;
+  // the A and B loaders walk the segments separately (A runs a stage ahead)
+  int lsa = 0, lka = g.seg[0].K / BK, lsb = 0, lkb = g.seg[0].K / BK;
+  // fragment reads: row fr of a 32-row block, global chunk 2t + lane/32 for
+  // the 16-K step t of a stage
+  const int fr = lane & 31, fsw = (fr >> 1) & 7, fh = lane >> 5;
+  auto brow = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (GATED) return j == 0 ? wn * 32 : BR / 2 + wn * 32;
+    else return wn * WN + j * 32;
+  };
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  auto ent = [&](int e) __attribute__((always_inline)) -> uint32_t {
+    return uint32_t(__builtin_amdgcn_readfirstlane(int(lds0 + e * ENT)));
+  };
+
+  auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
+    constexpr int FA = decltype(fa_c)::value;
+    bf16x8 af[2][FA > 0 ? FA : 1], bfr[2][FN];
+    // load q of this wave's share of an A (or B) half stage into the entry at eb
+    auto issue_a = [&](uint32_t eb, int q) __attribute__((always_inline)) { g2lds16(pa[q], eb + (wid + NW * q) * 1024); };
+    auto issue_b = [&](uint32_t eb, int q) __attribute__((always_inline)) { g2lds16(pb[q], eb + (wid + NW * q) * 1024); };
+    auto done_a = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < LH; ++i) pa[i] += BK;
+      if (--lka == 0 && lsa + 1 < g.nseg) {
+        ++lsa;
+        switch (lsa) {  // (static indices: the arguments stay in the kernarg segment)
+          case 1: set_a(g.seg[1]); lka = g.seg[1].K / BK; break;
+          case 2: set_a(g.seg[2]); lka = g.seg[2].K / BK; break;
+          case 3: set_a(g.seg[3]); lka = g.seg[3].K / BK; break;
+          default: set_a(g.seg[4]); lka = g.seg[4].K / BK; break;
+        }
+      }
+    };
+    auto done_b = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < LH; ++i) pb[i] += BK;
+      if (--lkb == 0 && lsb + 1 < g.nseg) {
+        ++lsb;
+        switch (lsb) {
+          case 1: set_b(g.seg[1]); lkb = g.seg[1].K / BK; break;
+          case 2: set_b(g.seg[2]); lkb = g.seg[2].K / BK; break;
+          case 3: set_b(g.seg[3]); lkb = g.seg[3].K / BK; break;
+          default: set_b(g.seg[4]); lkb = g.seg[4].K / BK; break;
+        }
+      }
+    };
+    // fragment q (q < FA: A, then the FN of B) of step t, A in entry ea, B in eb
+    auto rd_one = [&](int ea, int eb, int t, int q, int buf) __attribute__((always_inline)) {
+      const int off = fr * ROWB + (((2 * t + fh) ^ fsw) << 4);
+      if (q < FA) af[buf][q] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + ea * ENT + (wm * WM + q * 32) * ROWB + off));
+      else bfr[buf][q - FA] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + eb * ENT + brow(q - FA) * ROWB + off));
+    };
+    // a 16-K step's MFMAs on fragment set buf, with the side items 0 .. nside-1
+    // spread over them in order: MFMA m is followed by items c m .. c m + c - 1,
+    // c = ceil(nside / NM), NM being the MFMA count (all items at once if 0).
+    // The order matters: each wave's vmcnt waits count on its loads of B(s+2)
+    // leaving before those of A(s+3).
+    auto mm = [&](int buf, int nside, auto side) __attribute__((always_inline)) {
+      constexpr int NM = FA * FN;
+      const int c = NM > 0 ? (nside + NM - 1) / NM : 0;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FA; ++i) {
+          acc[i][j] = mfma_32x32x16(af[buf][i], bfr[buf][j], acc[i][j]);
+          const int m = j * FA + i;
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            if (k >= m * c && k < m * c + c && k < nside) side(k);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      if constexpr (NM == 0) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (k < nside) side(k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // stage s: A in entry e0 = 2s mod 5, B in e0+1; stage s+1 in e0+2, e0+3.
+    // W: half stages issued after B(s+1) (the wait before the barrier; -1: no
+    // stage s+1); IB / IA: issue B(s+2) into e0 / A(s+3) into e0+1
+    int e0 = 0;
+    auto step = [&](auto w_c, auto ib_c, auto ia_c) __attribute__((always_inline)) {
+      constexpr int W = decltype(w_c)::value;
+      constexpr bool IB = decltype(ib_c)::value, IA = decltype(ia_c)::value;
+      const int e1 = e0 + 1 >= 5 ? e0 - 4 : e0 + 1;
+      const int e2 = e0 + 2 >= 5 ? e0 - 3 : e0 + 2;
+      const int e3 = e0 + 3 >= 5 ? e0 - 2 : e0 + 3;
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        mm(t & 1, FA + FN, [&](int q) __attribute__((always_inline)) { rd_one(e0, e1, t + 1, q, (t + 1) & 1); });
+      if constexpr (W >= 0) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s are done
+        wait_vmcnt<W * LH>();
+        __builtin_amdgcn_s_barrier();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t b0 = ent(e0), b1 = ent(e1);
+      // side items: the loads of B(s+2), stage s+1's first fragments, the
+      // loads of A(s+3) (A has a step more to arrive)
+      constexpr int NB = IB ? LH : 0, NR = W >= 0 ? FA + FN : 0, NA = IA ? LH : 0;
+      mm(1, NB + NR + NA, [&](int k) __attribute__((always_inline)) {
+        if (k < NB) issue_b(b0, k);
+        else if (k < NB + NR) rd_one(e2, e3, 0, k - NB, 0);
+        else issue_a(b1, k - NB - NR);
+      });
+      if constexpr (IB) done_b();
+      if constexpr (IA) done_a();
+      e0 = e2;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using Im = std::integral_constant<int, -1>;
+    // A(0), B(0), A(1), B(1), A(2) into entries 0..4
+    {
+      const uint32_t base = ent(0);
+#pragma unroll
+      for (int h = 0; h < 5; ++h) {
+#pragma unroll
+        for (int q = 0; q < LH; ++q) {
+          if (h % 2 == 0) issue_a(base + h * ENT, q);
+          else issue_b(base + h * ENT, q);
+        }
+        if (h % 2 == 0) done_a();
+        else done_b();
+      }
+    }
+    wait_vmcnt<3 * LH>();  // stage 0; A(1), B(1), A(2) may be in flight
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int q = 0; q < FA + FN; ++q) rd_one(0, 1, 0, q, 0);
+    int s = 0;
+    for (; s + 3 < nk; ++s) step(I1{}, std::true_type{}, std::true_type{});
+    step(I1{}, std::true_type{}, std::false_type{});   // s = nk-3: B(nk-1)
+    step(I0{}, std::false_type{}, std::false_type{});  // s = nk-2
+    step(Im{}, std::false_type{}, std::false_type{});  // s = nk-1
+  };
+  const int fa = max(0, min(FM, (nrows - wm * WM + 31) / 32));
+  switch (fa) {
+    case 0: mainloop(std::integral_constant<int, 0>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    case 2: mainloop(std::integral_constant<int, 2>{}); break;
+    case 3: mainloop(std::integral_constant<int, 3>{}); break;
+    default: mainloop(std::integral_constant<int, 4>{}); break;
+  }
+  __syncthreads();
+  // epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores
+  constexpr int CLD = NOUT + 8;
+  static_assert(BM * CLD * 2 <= kR64Lds, "epilogue staging fits in the ring");
+  bf16_t* Cs = reinterpret_cast<bf16_t*>(lds);
+  constexpr int JO = GATED ? 1 : FN, WO = GATED ? 32 : WN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    if (i < fa)
+#pragma unroll
+      for (int j = 0; j < JO; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int col = wn * WO + j * 32 + (lane & 31);
+          float x = acc[i][j][v];
+          if constexpr (GATED) x = silu_mul(x, acc[i][1][v]);
+          Cs[row * CLD + col] = f32_to_bf16(x);
+        }
+  __syncthreads();
+  constexpr int OCPR = NOUT / 8;
+  for (int c = tid; c < BM * OCPR; c += NTH) {
+    const int row = c / OCPR, cc = c % OCPR;
+    if (row < nrows && n0 + cc * 8 < g.N)
+      *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(g.C) + (int64_t(row0) + row) * g.ldc + n0 + cc * 8) =
+          *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
+  }
+#endif
+}
+
+// ring64_dense_kernel takes bf16 outputs and segments whose K are multiples
+// of 64, at least 3 stages in all.
+bool ring64_fits(const DenseGemm& d) {
+  if (d.Cf || d.nseg < 1 || d.nseg > 5 || d.M <= 0 || d.N <= 0) return false;
+  int nk = 0;
+  for (int i = 0; i < d.nseg; ++i) {
+    if (d.seg[i].K <= 0 || d.seg[i].K % kR64BK) return false;
+    nk += d.seg[i].K / kR64BK;
+  }
+  return nk >= 3;
+}
+
+template <bool GATED>
+hipError_t run_ring64(const DenseGemm& d, hipStream_t s) {
+  constexpr int NOUT = GATED ? 128 : 256;
+  auto kern = ring64_dense_kernel<GATED>;
+  if (hipError_t e = allow_dynamic_lds((const void*)kern, kR64Lds); e != hipSuccess) return e;
+  const int64_t nblk = int64_t((d.M + 255) / 256) * ((d.N + NOUT - 1) / NOUT);
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3{uint32_t(nblk)}, dim3{512u}, kR64Lds, s, d);
+  return hipGetLastError();
+}
+
 // The ring kernel takes bf16 outputs and segments whose K are multiples of
 // 32, at least 4 stages in all.
 bool ring_fits(const DenseGemm& d) {
@@ -1005,6 +1295,7 @@ hipError_t run_ring(const DenseGemm& d, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
+  if (ring64_fits(d)) return d.gated ? run_ring64<true>(d, s) : run_ring64<false>(d, s);
   if (ring_fits(d)) return d.gated ? run_ring<true>(d, s) : run_ring<false>(d, s);
   TiledArgs a{};
   a.M = d.M;

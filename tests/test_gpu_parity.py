@@ -128,13 +128,19 @@ SMALL_LAYERS = [
     ("tiled_path", dict(T=600, d=256, l=512, E=8, k=2, S=1, I=256, Is=128)),
     # LDS-tiled dense projections with a ragged last row tile, odd latent width
     ("mid_ragged", dict(T=1000, d=320, l=192, E=24, k=4, S=2, I=128, Is=64)),
-    # dense projections above 512 tokens with short K: d = 64 (two 32-wide
-    # stages) is below the five-slot ring's minimum of four and takes the
-    # two-buffer kernel; the up-projection's three K segments of 64 switch
-    # segments inside the ring's prologue
+    # dense projections above 512 tokens with short K: d = 64 (one 64-wide
+    # stage) takes the two-buffer kernel; the up-projection's three K segments
+    # of 64 are the 64-wide ring's minimum of three stages and switch segments
+    # inside its prologue
     ("short_k", dict(T=700, d=64, l=64, E=8, k=2, S=2, I=64, Is=64)),
-    # the ring's minimum: four stages in all (up-proj 64 + 64), one segment switch
+    # K = 128 in all (down-proj, shared gate/up; up-proj 64 + 64 with one
+    # segment switch): two 64-wide stages, below that ring's minimum, so the
+    # 32-wide five-slot ring runs at its own minimum of four stages
     ("ring_min", dict(T=530, d=128, l=64, E=6, k=3, S=1, I=128, Is=64)),
+    # the 64-wide ring at its edges: down-proj K = 192 (three stages), partial
+    # column tiles (N = 320 of 2 x 256, gated N = 192 of 2 x 128, up-proj N =
+    # 192), a ragged last row tile, an up-proj segment switch after 5 stages
+    ("ring64_edges", dict(T=900, d=192, l=320, E=8, k=2, S=1, I=128, Is=192)),
     # weight-streaming experts over several K batches: FC1 K = 512 (two of 256), FC2 K = 384 (three of 128)
     ("skinny_wide", dict(T=100, d=256, l=512, E=64, k=4, S=1, I=384, Is=128)),
     # wide latents: the combine splits a token's row over 4 or 2 waves (with two
