@@ -231,13 +231,15 @@ class ClockSampler:
                 "spec_peak_mhz": 2400}
 
 
-def grouped_kernel(cfg, dom, fused_mlp):
+def grouped_kernel(cfg, dom, fused_mlp, packed=False):
     """Which kernel runs the grouped GEMM ``dom`` (the library's own choice:
     MXFP4 w4a8 -> block-scaled kernel; MXFP4 w4a16 -> its weight-streaming
-    kernels at <= 32 rows per expert on average, else the LDS-tiled grouped
-    kernel in its MXFP4 form; bf16 at <= 32 rows per expert on average ->
-    weight-streaming kernel; otherwise the LDS-tiled grouped kernel when K is
-    a multiple of 128 and at least 256, else the general tiled kernel)."""
+    kernels at <= 32 rows per expert on average, else the register-staged
+    grouped kernel in its MXFP4 form; bf16 at <= 32 rows per expert on average
+    -> weight-streaming kernel; otherwise, tile-packed weights -> the
+    register-staged grouped kernel in its packed form, row-major weights -> the
+    64-wide direct-to-LDS ring when K is a multiple of 64 and at least 192,
+    else the general tiled kernel)."""
     R = cfg.T * cfg.k
     K = cfg.l if dom == "fc1" else cfg.I
     if fused_mlp:
@@ -250,8 +252,10 @@ def grouped_kernel(cfg, dom, fused_mlp):
         return "mx_grouped_kernel", "mx.hip"
     if R <= 32 * cfg.E:
         return ("skinny_lds_kernel" if K % 128 == 0 else "skinny_grouped_kernel"), "skinny.hip"
-    if K % 128 == 0 and K >= 256:
-        return "grouped_tiled_kernel", "gemm.hip"
+    if packed:
+        return "grouped_tiled_kernel (tile-packed)", "gemm.hip"
+    if K % 64 == 0 and K >= 192:
+        return "ring64_grouped_kernel", "gemm.hip"
     return "tiled_gemm_kernel", "gemm.hip"
 
 
@@ -533,7 +537,7 @@ def measure(cfg, args, hip, lm, W, torch, stream, clock=None, wlayout="tiled"):
         dur_s = stages[dom] / 1e6
         ai = dom_flop / dom_bytes
         bound = "hbm" if ai < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
-        kern, src = grouped_kernel(cfg, dom, fused_mlp)
+        kern, src = grouped_kernel(cfg, dom, fused_mlp, packed)
         # the kernel's source with the headers every kernel includes
         traffic = measured_traffic(f"{dom}", cfg.name, source_hash(src, "common.h", "kernels.h"))
         if bound == "hbm":

@@ -3,9 +3,11 @@
 // All operands are "[rows, K]" with K contiguous (activations [M,K], weights
 // [N,K] in the [out, in] layout), so C = A * B^T reads both operands along K.
 //
-//  * ring64_dense_kernel: the dense projections at prefill (bf16 outputs,
-//    K a multiple of 64), K streamed through LDS in 64-wide stages by
-//    direct-to-LDS loads of whole 128-byte lines, a ring of half stages.
+//  * ring64_dense_kernel / ring64_grouped_kernel: the dense projections at
+//    prefill (bf16 outputs) and the prefill-shaped grouped expert GEMMs (bf16
+//    row-major weights), K a multiple of 64, streamed through LDS in 64-wide
+//    stages by direct-to-LDS loads of whole 128-byte lines, a ring of half
+//    stages.
 //  * ring_dense_kernel: the same with 32-wide stages in a five-slot ring, for
 //    K a multiple of 32 only.
 //  * tiled_gemm_kernel: LDS double-buffered macro tiles for the dense
@@ -341,7 +343,9 @@ hipError_t run_tiled(const TiledArgs& a, int64_t mtiles, hipStream_t s, hipEvent
 // stage ahead): at prefill ~146 rows per expert leave the kernel waiting on
 // the weight stream, and the deeper B pipeline keeps twice as much of it in
 // flight.  The results are bit-identical to tiled_gemm_kernel's (the same
-// MFMAs in the same K order).  Needs K a multiple of 128 and >= 256.
+// MFMAs in the same K order).  Needs K a multiple of 128 and >= 256.  It
+// serves the two forms below; row-major bf16 weights go to
+// ring64_grouped_kernel, whose direct-to-LDS stream is faster.
 // PACKED: the weights are in the tile-packed layout (kernels.h): a stage's
 // 128-row block of B is 16 KB of contiguous memory.
 // W4: MXFP4 weights with bf16 activations (w4a16 at prefill size; TokenSpeed
@@ -981,93 +985,60 @@ __global__ __launch_bounds__(512, 1) void ring_dense_kernel(DenseGemm g) {
 #endif
 }
 
-// ------------------------------------- dense, 64-wide stages, half-stage ring ---
-// Dense projections with the tile and wave layout of ring_dense_kernel (256 x
-// 256 output tiles, gated: 128 gate + 128 up B rows; 8 waves as 2 x 4 with 128
-// x 64 wave tiles), but K goes through LDS in 64-wide stages: a row of a
-// stage is 128 bytes, so each direct-to-LDS instruction (8 rows x 128 B) asks
-// L2 for whole 128-byte lines.  With 32-wide stages every request is half a
-// line and the same loads reach ~13 TB/s into LDS across the chip, against
-// ~21 TB/s for whole lines.  A 64-wide stage takes 64 KB, so the 160 KB of LDS
-// is a ring of five 32 KB entries, each holding one operand's half of a stage:
-// stage s keeps A in entry 2s mod 5 and B in entry 2s+1 mod 5.  One barrier
-// per stage, before its last 16-K step: each wave first waits for its LDS reads
+// ------------------------------------------ 64-wide stages, half-stage ring ---
+// The dense projections and the prefill-shaped grouped expert GEMMs on 8
+// waves as 2 x 4 (wave tiles BM/2 x 64 of 32x32x16 bf16 MFMAs; B tiles of 256
+// rows, gated: 128 gate + 128 up), with K going through LDS in 64-wide stages:
+// a row of a stage is 128 bytes, so each direct-to-LDS instruction (8 rows x
+// 128 B) asks L2 for whole 128-byte lines.  With 32-wide stages every request
+// is half a line, and the same loads reach only ~13 TB/s into LDS across the
+// chip against ~21 TB/s for whole lines.  A 64-wide stage takes up to 64 KB,
+// so the 160 KB of LDS is a ring of five 32 KB entries, each holding one
+// operand's half of a stage: the operand issued two stages ahead ("far": A
+// for the dense projections, whose activations and weights both mostly hit
+// L2; B for the grouped GEMMs, whose weights stream from HBM) sits in entry
+// 2s mod 5, the other ("near") in entry 2s+1 mod 5.  One barrier per stage,
+// before its last 16-K step: each wave first waits for its LDS reads
 // (lgkmcnt) and for its loads of stage s+1, so after the barrier stage s+1 is
-// visible and both entries of stage s are free.  Under that last step's MFMAs
-// go, in this order, the loads of B(s+2) into stage s's A entry, the reads of
-// stage s+1's first fragments and the loads of A(s+3) into stage s's B entry;
-// in flight behind the stage being computed are 1.5 stages (A two stages
-// ahead, B one).  The waits count on that order (vmcnt is in order: B(s+1) has
-// arrived once at most A(s+2)'s loads remain).  Rows are 128 B with
-// the eight 16-byte chunks XOR-swizzled by (row / 2) mod 8, so the 16 lanes of
-// each ds_read_b128 phase (16 consecutive rows, one chunk) hit 16 distinct
-// 4-bank groups.  Same MFMAs in the same K order as tiled_gemm_kernel: the
-// results are bit-identical.  Needs every segment's K a multiple of 64 and at
-// least 3 stages in all.
+// visible and both entries of stage s are free.  Under that last step's
+// MFMAs go, in this order, the loads of near(s+2) into stage s's far entry,
+// the reads of stage s+1's first fragments, and the loads of far(s+3) into
+// stage s's near entry: 1.5 stages are in flight behind the one computed.
+// The waits count on that order (vmcnt is in order: near(s+1) has arrived
+// once at most far(s+2)'s loads remain).  Rows are 128 B with the eight
+// 16-byte chunks XOR-swizzled by (row / 2) mod 8, so the 16 lanes of each
+// ds_read_b128 phase (16 consecutive rows, one chunk) hit 16 distinct 4-bank
+// groups.  The MFMAs and their K order are tiled_gemm_kernel's: the results
+// are bit-identical.  Needs K a multiple of 64 in every segment and at least
+// 3 stages in all.
 constexpr int kR64BK = 64;                // K per stage
 constexpr int kR64Row = kR64BK * 2;       // bytes per LDS row
 constexpr int kR64Ent = 256 * kR64Row;    // one operand's half of a stage: 32 KB
 constexpr int kR64Lds = 5 * kR64Ent;      // 160 KiB: all of a CU's LDS
 
-template <bool GATED>
-__global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g) {
-#if defined(__HIP_DEVICE_COMPILE__)
+// Lane l of wave w loads row l/8 of the 8-row groups w, w+8, ... of a half
+// stage, into chunk l%8 of its LDS row, from global chunk (l%8) ^ ((row/2)%8);
+// row/2 mod 8 = 4 (group mod 2) + (l/8)/2, and a group's parity is its wave's.
+__device__ __forceinline__ int ring64_gchunk(int wid, int lane) {
+  return (lane & 7) ^ ((((wid & 1) << 2) + ((lane >> 3) >> 1)) & 7);
+}
+
+// Main loop and epilogue of a 64-wide-ring tile.  pa / pb: this lane's
+// global addresses of its A / B rows at stage 0 (LA = BM/64 and 4 rows);
+// next_a / next_b advance them by one stage (and may switch segments).  The
+// tile's rows row0 .. row0+nrows-1 of C, columns n0 .. of N, are written.
+template <bool GATED, int BM, bool BFAR, class NextA, class NextB>
+__device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, int lane, int tid, int nk, int nrows,
+                                            const bf16_t* (&pa)[BM / 64], const bf16_t* (&pb)[4], NextA next_a,
+                                            NextB next_b, uint16_t* C, int64_t ldc, int64_t row0, int n0, int N) {
   constexpr int NW = 8, NTH = NW * 64, WAVES_N = 4;
-  constexpr int BM = 256, BR = 256, NOUT = GATED ? 128 : 256, WM = 128, WN = 64;
-  constexpr int FM = WM / 32, FN = WN / 32, BK = kR64BK, ROWB = kR64Row, ENT = kR64Ent;
-  constexpr int LH = 32 / NW;  // 1 KB load instructions per wave and half stage
-  extern __shared__ uint4 lds_u4[];
-  char* lds = reinterpret_cast<char*>(lds_u4);
-  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int BR = 256, NOUT = GATED ? 128 : 256, WM = BM / 2, WN = 64;
+  constexpr int FM = WM / 32, FN = WN / 32, ROWB = kR64Row, ENT = kR64Ent;
+  constexpr int LA = BM / 8 / NW, LB = BR / 8 / NW;  // 1 KB loads per wave and A / B half stage
+  constexpr int LF = BFAR ? LB : LA, LN = BFAR ? LA : LB;
+  static_assert(BM % (8 * NW) == 0 && BM * ROWB <= ENT && FM >= 1 && FM <= 4, "tile rows");
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
-  const int tiles_n = (g.N + NOUT - 1) / NOUT;
-  const uint32_t lt = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
-  const int row0 = tm * BM, nrows = min(BM, g.M - row0), n0 = tn * NOUT;
-  // wave w loads the 8-row groups w, w+8, w+16, w+24 of each half stage; lane
-  // l: row l/8 of the group into slot chunk l%8, from global chunk
-  // (l%8) ^ ((row/2)%8) (row/2 mod 8 = 4 (group mod 2) + (l/8)/2, and the
-  // group's parity is the wave's)
-  const int lr = lane >> 3;
-  const int gchunk = (lane & 7) ^ ((((wid & 1) << 2) + (lr >> 1)) & 7);
-  int a_row[LH], b_row[LH];
-  bool b_up[LH];
-#pragma unroll
-  for (int i = 0; i < LH; ++i) {
-    const int r = (wid + NW * i) * 8 + lr;
-    a_row[i] = row0 + min(r, nrows - 1);
-    if constexpr (GATED) {
-      b_up[i] = r >= BR / 2;
-      b_row[i] = min(n0 + (b_up[i] ? r - BR / 2 : r), g.N - 1);
-    } else {
-      b_up[i] = false;
-      b_row[i] = min(n0 + r, g.N - 1);
-    }
-  }
-  const bf16_t* pa[LH];
-  const bf16_t* pb[LH];
-  auto set_a = [&](const GemmSeg& sg) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LH; ++i) pa[i] = reinterpret_cast<const bf16_t*>(sg.A) + int64_t(a_row[i]) * sg.lda + gchunk * 8;
-  };
-  auto set_b = [&](const GemmSeg& sg) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LH; ++i)
-      pb[i] = reinterpret_cast<const bf16_t*>(b_up[i] ? sg.B3 : sg.B) + int64_t(b_row[i]) * sg.ldb + gchunk * 8;
-  };
-  set_a(g.seg[0]);
-  set_b(g.seg[0]);
-  int nk = 0;
-#pragma unroll
-  for (int q = 0; q < 5; ++q)
-    if (q < g.nseg) nk += g.seg[q].K / BK;
-  // the A and B loaders walk the segments separately (A runs a stage ahead)
-  int lsa = 0, lka = g.seg[0].K / BK, lsb = 0, lkb = g.seg[0].K / BK;
-  // fragment reads: row fr of a 32-row block, global chunk 2t + lane/32 for
-  // the 16-K step t of a stage
-  const int fr = lane & 31, fsw = (fr >> 1) & 7, fh = lane >> 5;
+  const int fr = lane & 31, fsw = (fr >> 1) & 7, fh = lane >> 5;  // fragment row, its swizzle, K half
   auto brow = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (GATED) return j == 0 ? wn * 32 : BR / 2 + wn * 32;
     else return wn * WN + j * 32;
@@ -1082,41 +1053,37 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g) {
   auto ent = [&](int e) __attribute__((always_inline)) -> uint32_t {
     return uint32_t(__builtin_amdgcn_readfirstlane(int(lds0 + e * ENT)));
   };
+  // (the LDS address goes to m0, so it must be wave-uniform: readfirstlane)
+  auto issue_a = [&](uint32_t eb, int q) __attribute__((always_inline)) {
+    g2lds16(pa[q], uint32_t(__builtin_amdgcn_readfirstlane(int(eb + (wid + NW * q) * 1024))));
+  };
+  auto issue_b = [&](uint32_t eb, int q) __attribute__((always_inline)) {
+    g2lds16(pb[q], uint32_t(__builtin_amdgcn_readfirstlane(int(eb + (wid + NW * q) * 1024))));
+  };
+  auto issue_far = [&](uint32_t eb, int q) __attribute__((always_inline)) {
+    if constexpr (BFAR) issue_b(eb, q);
+    else issue_a(eb, q);
+  };
+  auto issue_near = [&](uint32_t eb, int q) __attribute__((always_inline)) {
+    if constexpr (BFAR) issue_a(eb, q);
+    else issue_b(eb, q);
+  };
+  auto next_far = [&]() __attribute__((always_inline)) {
+    if constexpr (BFAR) next_b();
+    else next_a();
+  };
+  auto next_near = [&]() __attribute__((always_inline)) {
+    if constexpr (BFAR) next_a();
+    else next_b();
+  };
 
   auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
     constexpr int FA = decltype(fa_c)::value;
     bf16x8 af[2][FA > 0 ? FA : 1], bfr[2][FN];
-    // load q of this wave's share of an A (or B) half stage into the entry at eb
-    auto issue_a = [&](uint32_t eb, int q) __attribute__((always_inline)) { g2lds16(pa[q], eb + (wid + NW * q) * 1024); };
-    auto issue_b = [&](uint32_t eb, int q) __attribute__((always_inline)) { g2lds16(pb[q], eb + (wid + NW * q) * 1024); };
-    auto done_a = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < LH; ++i) pa[i] += BK;
-      if (--lka == 0 && lsa + 1 < g.nseg) {
-        ++lsa;
-        switch (lsa) {  // (static indices: the arguments stay in the kernarg segment)
-          case 1: set_a(g.seg[1]); lka = g.seg[1].K / BK; break;
-          case 2: set_a(g.seg[2]); lka = g.seg[2].K / BK; break;
-          case 3: set_a(g.seg[3]); lka = g.seg[3].K / BK; break;
-          default: set_a(g.seg[4]); lka = g.seg[4].K / BK; break;
-        }
-      }
-    };
-    auto done_b = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < LH; ++i) pb[i] += BK;
-      if (--lkb == 0 && lsb + 1 < g.nseg) {
-        ++lsb;
-        switch (lsb) {
-          case 1: set_b(g.seg[1]); lkb = g.seg[1].K / BK; break;
-          case 2: set_b(g.seg[2]); lkb = g.seg[2].K / BK; break;
-          case 3: set_b(g.seg[3]); lkb = g.seg[3].K / BK; break;
-          default: set_b(g.seg[4]); lkb = g.seg[4].K / BK; break;
-        }
-      }
-    };
-    // fragment q (q < FA: A, then the FN of B) of step t, A in entry ea, B in eb
-    auto rd_one = [&](int ea, int eb, int t, int q, int buf) __attribute__((always_inline)) {
+    // fragment q (q < FA: A, then the FN of B) of the 16-K step t of the
+    // stage whose far operand is in entry ef and near one in en
+    auto rd = [&](int ef, int en, int t, int q, int buf) __attribute__((always_inline)) {
+      const int ea = BFAR ? en : ef, eb = BFAR ? ef : en;
       const int off = fr * ROWB + (((2 * t + fh) ^ fsw) << 4);
       if (q < FA) af[buf][q] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + ea * ENT + (wm * WM + q * 32) * ROWB + off));
       else bfr[buf][q - FA] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + eb * ENT + brow(q - FA) * ROWB + off));
@@ -1124,8 +1091,8 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g) {
     // a 16-K step's MFMAs on fragment set buf, with the side items 0 .. nside-1
     // spread over them in order: MFMA m is followed by items c m .. c m + c - 1,
     // c = ceil(nside / NM), NM being the MFMA count (all items at once if 0).
-    // The order matters: each wave's vmcnt waits count on its loads of B(s+2)
-    // leaving before those of A(s+3).
+    // The order matters: the vmcnt waits count on each wave's loads of
+    // near(s+2) leaving before those of far(s+3).
     auto mm = [&](int buf, int nside, auto side) __attribute__((always_inline)) {
       constexpr int NM = FA * FN;
       const int c = NM > 0 ? (nside + NM - 1) / NM : 0;
@@ -1147,62 +1114,63 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g) {
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    // stage s: A in entry e0 = 2s mod 5, B in e0+1; stage s+1 in e0+2, e0+3.
-    // W: half stages issued after B(s+1) (the wait before the barrier; -1: no
-    // stage s+1); IB / IA: issue B(s+2) into e0 / A(s+3) into e0+1
+    // stage s: far operand in e0 = 2s mod 5, near in e0+1; stage s+1 in e0+2,
+    // e0+3.  W: far half stages issued after near(s+1) (the wait before the
+    // barrier; -1: there is no stage s+1); IN / IF: issue near(s+2) into e0 /
+    // far(s+3) into e0+1
     int e0 = 0;
-    auto step = [&](auto w_c, auto ib_c, auto ia_c) __attribute__((always_inline)) {
+    auto step = [&](auto w_c, auto in_c, auto if_c) __attribute__((always_inline)) {
       constexpr int W = decltype(w_c)::value;
-      constexpr bool IB = decltype(ib_c)::value, IA = decltype(ia_c)::value;
+      constexpr bool IN = decltype(in_c)::value, IF = decltype(if_c)::value;
       const int e1 = e0 + 1 >= 5 ? e0 - 4 : e0 + 1;
       const int e2 = e0 + 2 >= 5 ? e0 - 3 : e0 + 2;
       const int e3 = e0 + 3 >= 5 ? e0 - 2 : e0 + 3;
 #pragma unroll
       for (int t = 0; t < 3; ++t)
-        mm(t & 1, FA + FN, [&](int q) __attribute__((always_inline)) { rd_one(e0, e1, t + 1, q, (t + 1) & 1); });
+        mm(t & 1, FA + FN, [&](int q) __attribute__((always_inline)) { rd(e0, e1, t + 1, q, (t + 1) & 1); });
       if constexpr (W >= 0) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s are done
-        wait_vmcnt<W * LH>();
+        wait_vmcnt<W * LF>();
         __builtin_amdgcn_s_barrier();
       }
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t b0 = ent(e0), b1 = ent(e1);
-      // side items: the loads of B(s+2), stage s+1's first fragments, the
-      // loads of A(s+3) (A has a step more to arrive)
-      constexpr int NB = IB ? LH : 0, NR = W >= 0 ? FA + FN : 0, NA = IA ? LH : 0;
-      mm(1, NB + NR + NA, [&](int k) __attribute__((always_inline)) {
-        if (k < NB) issue_b(b0, k);
-        else if (k < NB + NR) rd_one(e2, e3, 0, k - NB, 0);
-        else issue_a(b1, k - NB - NR);
+      constexpr int NNR = IN ? LN : 0, NRD = W >= 0 ? FA + FN : 0, NFR = IF ? LF : 0;
+      mm(1, NNR + NRD + NFR, [&](int k) __attribute__((always_inline)) {
+        if (k < NNR) issue_near(b0, k);
+        else if (k < NNR + NRD) rd(e2, e3, 0, k - NNR, 0);  // stage s+1's first fragments
+        else issue_far(b1, k - NNR - NRD);
       });
-      if constexpr (IB) done_b();
-      if constexpr (IA) done_a();
+      if constexpr (IN) next_near();
+      if constexpr (IF) next_far();
       e0 = e2;
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using Im = std::integral_constant<int, -1>;
-    // A(0), B(0), A(1), B(1), A(2) into entries 0..4
+    // far(0), near(0), far(1), near(1), far(2) into entries 0..4
     {
       const uint32_t base = ent(0);
 #pragma unroll
       for (int h = 0; h < 5; ++h) {
+        if (h % 2 == 0) {
 #pragma unroll
-        for (int q = 0; q < LH; ++q) {
-          if (h % 2 == 0) issue_a(base + h * ENT, q);
-          else issue_b(base + h * ENT, q);
+          for (int q = 0; q < LF; ++q) issue_far(base + h * ENT, q);
+          next_far();
+        } else {
+#pragma unroll
+          for (int q = 0; q < LN; ++q) issue_near(base + h * ENT, q);
+          next_near();
         }
-        if (h % 2 == 0) done_a();
-        else done_b();
       }
     }
-    wait_vmcnt<3 * LH>();  // stage 0; A(1), B(1), A(2) may be in flight
+    wait_vmcnt<2 * LF + LN>();  // stage 0; far(1), near(1), far(2) may be in flight
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int q = 0; q < FA + FN; ++q) rd_one(0, 1, 0, q, 0);
+    for (int q = 0; q < FA + FN; ++q) rd(0, 1, 0, q, 0);
     int s = 0;
     for (; s + 3 < nk; ++s) step(I1{}, std::true_type{}, std::true_type{});
-    step(I1{}, std::true_type{}, std::false_type{});   // s = nk-3: B(nk-1)
+    step(I1{}, std::true_type{}, std::false_type{});   // s = nk-3: near(nk-1)
     step(I0{}, std::false_type{}, std::false_type{});  // s = nk-2
     step(Im{}, std::false_type{}, std::false_type{});  // s = nk-1
   };
@@ -1211,8 +1179,8 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g) {
     case 0: mainloop(std::integral_constant<int, 0>{}); break;
     case 1: mainloop(std::integral_constant<int, 1>{}); break;
     case 2: mainloop(std::integral_constant<int, 2>{}); break;
-    case 3: mainloop(std::integral_constant<int, 3>{}); break;
-    default: mainloop(std::integral_constant<int, 4>{}); break;
+    case 3: mainloop(std::integral_constant<int, FM >= 3 ? 3 : FM>{}); break;
+    default: mainloop(std::integral_constant<int, FM>{}); break;
   }
   __syncthreads();
   // epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores
@@ -1237,10 +1205,133 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g) {
   constexpr int OCPR = NOUT / 8;
   for (int c = tid; c < BM * OCPR; c += NTH) {
     const int row = c / OCPR, cc = c % OCPR;
-    if (row < nrows && n0 + cc * 8 < g.N)
-      *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(g.C) + (int64_t(row0) + row) * g.ldc + n0 + cc * 8) =
-          *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
+    if (row < nrows && n0 + cc * 8 < N)
+      *reinterpret_cast<uint4*>(C + (row0 + row) * ldc + n0 + cc * 8) = *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
   }
+}
+
+// Dense projections: 256 x 256 tiles over up to five K segments (the A and B
+// loaders walk the segments separately, A a stage ahead of B).
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = 256, BR = 256, NOUT = GATED ? 128 : 256, NW = 8, LA = BM / 64, LB = 4, BK = kR64BK;
+  extern __shared__ uint4 lds_u4[];
+  char* lds = reinterpret_cast<char*>(lds_u4);
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_n = (g.N + NOUT - 1) / NOUT;
+  const uint32_t lt = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
+  const int row0 = tm * BM, nrows = min(BM, g.M - row0), n0 = tn * NOUT;
+  const int lr = lane >> 3, gchunk = ring64_gchunk(wid, lane);
+  int a_row[LA], b_row[LB];
+  bool b_up[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) a_row[i] = row0 + min((wid + NW * i) * 8 + lr, nrows - 1);
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int r = (wid + NW * i) * 8 + lr;
+    b_up[i] = GATED && r >= BR / 2;
+    b_row[i] = min(n0 + (b_up[i] ? r - BR / 2 : r), g.N - 1);
+  }
+  const bf16_t* pa[LA];
+  const bf16_t* pb[LB];
+  auto set_a = [&](const GemmSeg& sg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) pa[i] = reinterpret_cast<const bf16_t*>(sg.A) + int64_t(a_row[i]) * sg.lda + gchunk * 8;
+  };
+  auto set_b = [&](const GemmSeg& sg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+      pb[i] = reinterpret_cast<const bf16_t*>(b_up[i] ? sg.B3 : sg.B) + int64_t(b_row[i]) * sg.ldb + gchunk * 8;
+  };
+  set_a(g.seg[0]);
+  set_b(g.seg[0]);
+  int nk = 0;
+#pragma unroll
+  for (int q = 0; q < 5; ++q)
+    if (q < g.nseg) nk += g.seg[q].K / BK;
+  int lsa = 0, lka = g.seg[0].K / BK, lsb = 0, lkb = g.seg[0].K / BK;
+  auto next_a = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) pa[i] += BK;
+    if (--lka == 0 && lsa + 1 < g.nseg) {
+      ++lsa;
+      switch (lsa) {  // (static indices: the arguments stay in the kernarg segment)
+        case 1: set_a(g.seg[1]); lka = g.seg[1].K / BK; break;
+        case 2: set_a(g.seg[2]); lka = g.seg[2].K / BK; break;
+        case 3: set_a(g.seg[3]); lka = g.seg[3].K / BK; break;
+        default: set_a(g.seg[4]); lka = g.seg[4].K / BK; break;
+      }
+    }
+  };
+  auto next_b = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i) pb[i] += BK;
+    if (--lkb == 0 && lsb + 1 < g.nseg) {
+      ++lsb;
+      switch (lsb) {
+        case 1: set_b(g.seg[1]); lkb = g.seg[1].K / BK; break;
+        case 2: set_b(g.seg[2]); lkb = g.seg[2].K / BK; break;
+        case 3: set_b(g.seg[3]); lkb = g.seg[3].K / BK; break;
+        default: set_b(g.seg[4]); lkb = g.seg[4].K / BK; break;
+      }
+    }
+  };
+  ring64_tile<GATED, BM, false>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0, n0,
+                                g.N);
+#endif
+}
+
+// Grouped expert GEMMs on the routing's tiles of at most kTiledBM = 192 rows
+// (tile table, gathered activation rows, the tile's expert's B), weights two
+// stages ahead.
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = kTiledBM, BR = 256, NOUT = GATED ? 128 : 256, NW = 8, LA = BM / 64, LB = 4, BK = kR64BK;
+  extern __shared__ uint4 lds_u4[];
+  char* lds = reinterpret_cast<char*>(lds_u4);
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_n = (g.N + NOUT - 1) / NOUT;
+  // grid sized for the host's upper bound; XCD-aware order over the real count
+  const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
+  if (blockIdx.x >= nreal) return;
+  const uint32_t lt = xcd_swizzle(blockIdx.x, nreal);
+  const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
+  const Tile tl = g.tiles[tm];
+  const int row0 = tl.row_start, nrows = min(tl.nrows, BM), n0 = tn * NOUT;
+  const int lr = lane >> 3, gchunk = ring64_gchunk(wid, lane);
+  const bf16_t* pa[LA];
+  const bf16_t* pb[LB];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    int src = row0 + min((wid + NW * i) * 8 + lr, nrows - 1);
+    if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
+    pa[i] = reinterpret_cast<const bf16_t*>(g.A) + int64_t(src) * g.lda + gchunk * 8;
+  }
+  const int64_t be = int64_t(tl.expert) * g.b_estride;
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int r = (wid + NW * i) * 8 + lr;
+    const bool up = GATED && r >= BR / 2;
+    const int n = min(n0 + (up ? r - BR / 2 : r), g.N - 1);
+    pb[i] = reinterpret_cast<const bf16_t*>(up ? g.B3 : g.B) + be + int64_t(n) * g.ldb + gchunk * 8;
+  }
+  auto next_a = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LA; ++i) pa[i] += BK;
+  };
+  auto next_b = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i) pb[i] += BK;
+  };
+  ring64_tile<GATED, BM, true>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0,
+                               n0, g.N);
 #endif
 }
 
@@ -1266,6 +1357,17 @@ hipError_t run_ring64(const DenseGemm& d, hipStream_t s) {
   if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3{uint32_t(nblk)}, dim3{512u}, kR64Lds, s, d);
   return hipGetLastError();
+}
+
+template <bool GATED>
+hipError_t run_ring64_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  constexpr int NOUT = GATED ? 128 : 256;
+  auto kern = ring64_grouped_kernel<GATED>;
+  if (hipError_t e = allow_dynamic_lds((const void*)kern, kR64Lds); e != hipSuccess) return e;
+  const int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
+  return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512u}, kR64Lds, s, g, t0, t1);
 }
 
 // The ring kernel takes bf16 outputs and segments whose K are multiples of
@@ -1335,11 +1437,13 @@ hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t 
     if (g.packed || g.K % 128 || g.K < 256 || !g.Bs || (g.gated && !g.B3s)) return hipErrorInvalidValue;
     return g.gated ? run_grouped<true, false, true>(g, s, t0, t1) : run_grouped<false, false, true>(g, s, t0, t1);
   }
-  if (g.K % 128 == 0 && g.K >= 256) {
-    if (g.packed) return g.gated ? run_grouped<true, true>(g, s, t0, t1) : run_grouped<false, true>(g, s, t0, t1);
-    return g.gated ? run_grouped<true, false>(g, s, t0, t1) : run_grouped<false, false>(g, s, t0, t1);
+  if (g.packed) {
+    // the tile-packed layout has only the register-staged form
+    if (g.K % 128 || g.K < 256) return hipErrorInvalidValue;
+    return g.gated ? run_grouped<true, true>(g, s, t0, t1) : run_grouped<false, true>(g, s, t0, t1);
   }
-  if (g.packed) return hipErrorInvalidValue;  // the tile-packed layout needs the kernel above
+  if (g.K % kR64BK == 0 && g.K >= 3 * kR64BK)
+    return g.gated ? run_ring64_grouped<true>(g, s, t0, t1) : run_ring64_grouped<false>(g, s, t0, t1);
   TiledArgs a{};
   a.M = 0;
   a.N = g.N;
