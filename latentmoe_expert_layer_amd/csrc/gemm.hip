@@ -994,18 +994,18 @@ __global__ __launch_bounds__(512, 1) void ring_dense_kernel(DenseGemm g) {
 // is half a line, and the same loads reach only ~13 TB/s into LDS across the
 // chip against ~21 TB/s for whole lines.  A 64-wide stage takes up to 64 KB,
 // so the 160 KB of LDS is a ring of five 32 KB entries, each holding one
-// operand's half of a stage: the operand issued two stages ahead ("far": A
-// for the dense projections, whose activations and weights both mostly hit
-// L2; B for the grouped GEMMs, whose weights stream from HBM) sits in entry
-// 2s mod 5, the other ("near") in entry 2s+1 mod 5.  One barrier per stage,
+// operand's half of a stage: B (the weights, issued two stages ahead: for the
+// grouped GEMMs they stream from HBM, and the dense projections gain 1-2% too)
+// sits in entry 2s mod 5, A (one stage ahead) in entry 2s+1 mod 5.  One
+// barrier per stage,
 // before its last 16-K step: each wave first waits for its LDS reads
 // (lgkmcnt) and for its loads of stage s+1, so after the barrier stage s+1 is
 // visible and both entries of stage s are free.  Under that last step's
-// MFMAs go, in this order, the loads of near(s+2) into stage s's far entry,
-// the reads of stage s+1's first fragments, and the loads of far(s+3) into
-// stage s's near entry: 1.5 stages are in flight behind the one computed.
-// The waits count on that order (vmcnt is in order: near(s+1) has arrived
-// once at most far(s+2)'s loads remain).  Rows are 128 B with the eight
+// MFMAs go, in this order, the loads of A(s+2) into stage s's B entry, the
+// reads of stage s+1's first fragments, and the loads of B(s+3) into stage
+// s's A entry: 1.5 stages are in flight behind the one computed.  The waits
+// count on that order (vmcnt is in order: A(s+1) has arrived once at most
+// B(s+2)'s loads remain).  Rows are 128 B with the eight
 // 16-byte chunks XOR-swizzled by (row / 2) mod 8, so the 16 lanes of each
 // ds_read_b128 phase (16 consecutive rows, one chunk) hit 16 distinct 4-bank
 // groups.  The MFMAs and their K order are tiled_gemm_kernel's: the results
@@ -1027,7 +1027,7 @@ __device__ __forceinline__ int ring64_gchunk(int wid, int lane) {
 // global addresses of its A / B rows at stage 0 (LA = BM/64 and 4 rows);
 // next_a / next_b advance them by one stage (and may switch segments).  The
 // tile's rows row0 .. row0+nrows-1 of C, columns n0 .. of N, are written.
-template <bool GATED, int BM, bool BFAR, class NextA, class NextB>
+template <bool GATED, int BM, class NextA, class NextB>
 __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, int lane, int tid, int nk, int nrows,
                                             const bf16_t* (&pa)[BM / 64], const bf16_t* (&pb)[4], NextA next_a,
                                             NextB next_b, uint16_t* C, int64_t ldc, int64_t row0, int n0, int N) {
@@ -1035,7 +1035,6 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
   constexpr int BR = 256, NOUT = GATED ? 128 : 256, WM = BM / 2, WN = 64;
   constexpr int FM = WM / 32, FN = WN / 32, ROWB = kR64Row, ENT = kR64Ent;
   constexpr int LA = BM / 8 / NW, LB = BR / 8 / NW;  // 1 KB loads per wave and A / B half stage
-  constexpr int LF = BFAR ? LB : LA, LN = BFAR ? LA : LB;
   static_assert(BM % (8 * NW) == 0 && BM * ROWB <= ENT && FM >= 1 && FM <= 4, "tile rows");
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
   const int fr = lane & 31, fsw = (fr >> 1) & 7, fh = lane >> 5;  // fragment row, its swizzle, K half
@@ -1060,30 +1059,13 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
   auto issue_b = [&](uint32_t eb, int q) __attribute__((always_inline)) {
     g2lds16(pb[q], uint32_t(__builtin_amdgcn_readfirstlane(int(eb + (wid + NW * q) * 1024))));
   };
-  auto issue_far = [&](uint32_t eb, int q) __attribute__((always_inline)) {
-    if constexpr (BFAR) issue_b(eb, q);
-    else issue_a(eb, q);
-  };
-  auto issue_near = [&](uint32_t eb, int q) __attribute__((always_inline)) {
-    if constexpr (BFAR) issue_a(eb, q);
-    else issue_b(eb, q);
-  };
-  auto next_far = [&]() __attribute__((always_inline)) {
-    if constexpr (BFAR) next_b();
-    else next_a();
-  };
-  auto next_near = [&]() __attribute__((always_inline)) {
-    if constexpr (BFAR) next_a();
-    else next_b();
-  };
 
   auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
     constexpr int FA = decltype(fa_c)::value;
     bf16x8 af[2][FA > 0 ? FA : 1], bfr[2][FN];
     // fragment q (q < FA: A, then the FN of B) of the 16-K step t of the
-    // stage whose far operand is in entry ef and near one in en
-    auto rd = [&](int ef, int en, int t, int q, int buf) __attribute__((always_inline)) {
-      const int ea = BFAR ? en : ef, eb = BFAR ? ef : en;
+    // stage whose B is in entry eb and A in ea
+    auto rd = [&](int eb, int ea, int t, int q, int buf) __attribute__((always_inline)) {
       const int off = fr * ROWB + (((2 * t + fh) ^ fsw) << 4);
       if (q < FA) af[buf][q] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + ea * ENT + (wm * WM + q * 32) * ROWB + off));
       else bfr[buf][q - FA] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + eb * ENT + brow(q - FA) * ROWB + off));
@@ -1092,7 +1074,7 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
     // spread over them in order: MFMA m is followed by items c m .. c m + c - 1,
     // c = ceil(nside / NM), NM being the MFMA count (all items at once if 0).
     // The order matters: the vmcnt waits count on each wave's loads of
-    // near(s+2) leaving before those of far(s+3).
+    // A(s+2) leaving before those of B(s+3).
     auto mm = [&](int buf, int nside, auto side) __attribute__((always_inline)) {
       constexpr int NM = FA * FN;
       const int c = NM > 0 ? (nside + NM - 1) / NM : 0;
@@ -1114,14 +1096,13 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    // stage s: far operand in e0 = 2s mod 5, near in e0+1; stage s+1 in e0+2,
-    // e0+3.  W: far half stages issued after near(s+1) (the wait before the
-    // barrier; -1: there is no stage s+1); IN / IF: issue near(s+2) into e0 /
-    // far(s+3) into e0+1
+    // stage s: B in e0 = 2s mod 5, A in e0+1; stage s+1 in e0+2, e0+3.  W: B
+    // half stages issued after A(s+1) (the wait before the barrier; -1: there
+    // is no stage s+1); IA / IB: issue A(s+2) into e0 / B(s+3) into e0+1
     int e0 = 0;
-    auto step = [&](auto w_c, auto in_c, auto if_c) __attribute__((always_inline)) {
+    auto step = [&](auto w_c, auto ia_c, auto ib_c) __attribute__((always_inline)) {
       constexpr int W = decltype(w_c)::value;
-      constexpr bool IN = decltype(in_c)::value, IF = decltype(if_c)::value;
+      constexpr bool IA = decltype(ia_c)::value, IB = decltype(ib_c)::value;
       const int e1 = e0 + 1 >= 5 ? e0 - 4 : e0 + 1;
       const int e2 = e0 + 2 >= 5 ? e0 - 3 : e0 + 2;
       const int e3 = e0 + 3 >= 5 ? e0 - 2 : e0 + 3;
@@ -1130,47 +1111,47 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
         mm(t & 1, FA + FN, [&](int q) __attribute__((always_inline)) { rd(e0, e1, t + 1, q, (t + 1) & 1); });
       if constexpr (W >= 0) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s are done
-        wait_vmcnt<W * LF>();
+        wait_vmcnt<W * LB>();
         __builtin_amdgcn_s_barrier();
       }
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t b0 = ent(e0), b1 = ent(e1);
-      constexpr int NNR = IN ? LN : 0, NRD = W >= 0 ? FA + FN : 0, NFR = IF ? LF : 0;
-      mm(1, NNR + NRD + NFR, [&](int k) __attribute__((always_inline)) {
-        if (k < NNR) issue_near(b0, k);
-        else if (k < NNR + NRD) rd(e2, e3, 0, k - NNR, 0);  // stage s+1's first fragments
-        else issue_far(b1, k - NNR - NRD);
+      constexpr int NA = IA ? LA : 0, NRD = W >= 0 ? FA + FN : 0, NB = IB ? LB : 0;
+      mm(1, NA + NRD + NB, [&](int k) __attribute__((always_inline)) {
+        if (k < NA) issue_a(b0, k);
+        else if (k < NA + NRD) rd(e2, e3, 0, k - NA, 0);  // stage s+1's first fragments
+        else issue_b(b1, k - NA - NRD);
       });
-      if constexpr (IN) next_near();
-      if constexpr (IF) next_far();
+      if constexpr (IA) next_a();
+      if constexpr (IB) next_b();
       e0 = e2;
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using Im = std::integral_constant<int, -1>;
-    // far(0), near(0), far(1), near(1), far(2) into entries 0..4
+    // B(0), A(0), B(1), A(1), B(2) into entries 0..4
     {
       const uint32_t base = ent(0);
 #pragma unroll
       for (int h = 0; h < 5; ++h) {
         if (h % 2 == 0) {
 #pragma unroll
-          for (int q = 0; q < LF; ++q) issue_far(base + h * ENT, q);
-          next_far();
+          for (int q = 0; q < LB; ++q) issue_b(base + h * ENT, q);
+          next_b();
         } else {
 #pragma unroll
-          for (int q = 0; q < LN; ++q) issue_near(base + h * ENT, q);
-          next_near();
+          for (int q = 0; q < LA; ++q) issue_a(base + h * ENT, q);
+          next_a();
         }
       }
     }
-    wait_vmcnt<2 * LF + LN>();  // stage 0; far(1), near(1), far(2) may be in flight
+    wait_vmcnt<2 * LB + LA>();  // stage 0; B(1), A(1), B(2) may be in flight
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int q = 0; q < FA + FN; ++q) rd(0, 1, 0, q, 0);
     int s = 0;
     for (; s + 3 < nk; ++s) step(I1{}, std::true_type{}, std::true_type{});
-    step(I1{}, std::true_type{}, std::false_type{});   // s = nk-3: near(nk-1)
+    step(I1{}, std::true_type{}, std::false_type{});   // s = nk-3: A(nk-1)
     step(I0{}, std::false_type{}, std::false_type{});  // s = nk-2
     step(Im{}, std::false_type{}, std::false_type{});  // s = nk-1
   };
@@ -1211,83 +1192,103 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
 }
 
 // Dense projections: 256 x 256 tiles over up to five K segments (the A and B
-// loaders walk the segments separately, A a stage ahead of B).
+// loaders walk the segments separately, B a stage ahead of A).  When the
+// tiles leave a last round of workgroups at most half full, the last nsplit
+// tiles run as two 128-row halves each, so that last round fills the GPU:
+// blocks below nt - nsplit take whole tiles in the XCD-aware order, the
+// 2 nsplit blocks after them the halves (a half tile loads 3/4 of a whole
+// one's operands for 1/2 of its MFMAs).
 template <bool GATED>
-__global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g) {
+__global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g, int nsplit) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int BM = 256, BR = 256, NOUT = GATED ? 128 : 256, NW = 8, LA = BM / 64, LB = 4, BK = kR64BK;
+  constexpr int BR = 256, NOUT = GATED ? 128 : 256, NW = 8, LB = 4, BK = kR64BK;
   extern __shared__ uint4 lds_u4[];
   char* lds = reinterpret_cast<char*>(lds_u4);
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
-  const uint32_t lt = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
-  const int row0 = tm * BM, nrows = min(BM, g.M - row0), n0 = tn * NOUT;
+  const uint32_t nwhole = gridDim.x - 2 * uint32_t(nsplit);  // blocks taking whole tiles
+  uint32_t t;
+  int half = -1;  // -1: a whole tile; else which 128-row half
+  if (blockIdx.x < nwhole) {
+    t = xcd_swizzle(blockIdx.x, nwhole);
+  } else {
+    const uint32_t h = xcd_swizzle(blockIdx.x - nwhole, 2 * uint32_t(nsplit));
+    t = nwhole + h / 2;
+    half = int(h % 2);
+  }
+  const int tn = int(t % uint32_t(tiles_n)), tm = int(t / uint32_t(tiles_n));
+  const int row0 = tm * 256 + (half > 0 ? 128 : 0);
+  const int nrows = min(half >= 0 ? 128 : 256, g.M - row0), n0 = tn * NOUT;
+  if (nrows <= 0) return;  // (the empty second half of a short last row tile)
   const int lr = lane >> 3, gchunk = ring64_gchunk(wid, lane);
-  int a_row[LA], b_row[LB];
+  int b_row[LB];
   bool b_up[LB];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) a_row[i] = row0 + min((wid + NW * i) * 8 + lr, nrows - 1);
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int r = (wid + NW * i) * 8 + lr;
     b_up[i] = GATED && r >= BR / 2;
     b_row[i] = min(n0 + (b_up[i] ? r - BR / 2 : r), g.N - 1);
   }
-  const bf16_t* pa[LA];
-  const bf16_t* pb[LB];
-  auto set_a = [&](const GemmSeg& sg) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) pa[i] = reinterpret_cast<const bf16_t*>(sg.A) + int64_t(a_row[i]) * sg.lda + gchunk * 8;
-  };
-  auto set_b = [&](const GemmSeg& sg) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LB; ++i)
-      pb[i] = reinterpret_cast<const bf16_t*>(b_up[i] ? sg.B3 : sg.B) + int64_t(b_row[i]) * sg.ldb + gchunk * 8;
-  };
-  set_a(g.seg[0]);
-  set_b(g.seg[0]);
   int nk = 0;
 #pragma unroll
   for (int q = 0; q < 5; ++q)
     if (q < g.nseg) nk += g.seg[q].K / BK;
-  int lsa = 0, lka = g.seg[0].K / BK, lsb = 0, lkb = g.seg[0].K / BK;
-  auto next_a = [&]() __attribute__((always_inline)) {
+  auto tile = [&](auto bm_c) __attribute__((always_inline)) {
+    constexpr int BM = decltype(bm_c)::value, LA = BM / 64;
+    int a_row[LA];
 #pragma unroll
-    for (int i = 0; i < LA; ++i) pa[i] += BK;
-    if (--lka == 0 && lsa + 1 < g.nseg) {
-      ++lsa;
-      switch (lsa) {  // (static indices: the arguments stay in the kernarg segment)
-        case 1: set_a(g.seg[1]); lka = g.seg[1].K / BK; break;
-        case 2: set_a(g.seg[2]); lka = g.seg[2].K / BK; break;
-        case 3: set_a(g.seg[3]); lka = g.seg[3].K / BK; break;
-        default: set_a(g.seg[4]); lka = g.seg[4].K / BK; break;
-      }
-    }
-  };
-  auto next_b = [&]() __attribute__((always_inline)) {
+    for (int i = 0; i < LA; ++i) a_row[i] = row0 + min((wid + NW * i) * 8 + lr, nrows - 1);
+    const bf16_t* pa[LA];
+    const bf16_t* pb[LB];
+    auto set_a = [&](const GemmSeg& sg) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < LB; ++i) pb[i] += BK;
-    if (--lkb == 0 && lsb + 1 < g.nseg) {
-      ++lsb;
-      switch (lsb) {
-        case 1: set_b(g.seg[1]); lkb = g.seg[1].K / BK; break;
-        case 2: set_b(g.seg[2]); lkb = g.seg[2].K / BK; break;
-        case 3: set_b(g.seg[3]); lkb = g.seg[3].K / BK; break;
-        default: set_b(g.seg[4]); lkb = g.seg[4].K / BK; break;
+      for (int i = 0; i < LA; ++i) pa[i] = reinterpret_cast<const bf16_t*>(sg.A) + int64_t(a_row[i]) * sg.lda + gchunk * 8;
+    };
+    auto set_b = [&](const GemmSeg& sg) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < LB; ++i)
+        pb[i] = reinterpret_cast<const bf16_t*>(b_up[i] ? sg.B3 : sg.B) + int64_t(b_row[i]) * sg.ldb + gchunk * 8;
+    };
+    set_a(g.seg[0]);
+    set_b(g.seg[0]);
+    int lsa = 0, lka = g.seg[0].K / BK, lsb = 0, lkb = g.seg[0].K / BK;
+    auto next_a = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < LA; ++i) pa[i] += BK;
+      if (--lka == 0 && lsa + 1 < g.nseg) {
+        ++lsa;
+        switch (lsa) {  // (static indices: the arguments stay in the kernarg segment)
+          case 1: set_a(g.seg[1]); lka = g.seg[1].K / BK; break;
+          case 2: set_a(g.seg[2]); lka = g.seg[2].K / BK; break;
+          case 3: set_a(g.seg[3]); lka = g.seg[3].K / BK; break;
+          default: set_a(g.seg[4]); lka = g.seg[4].K / BK; break;
+        }
       }
-    }
+    };
+    auto next_b = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < LB; ++i) pb[i] += BK;
+      if (--lkb == 0 && lsb + 1 < g.nseg) {
+        ++lsb;
+        switch (lsb) {
+          case 1: set_b(g.seg[1]); lkb = g.seg[1].K / BK; break;
+          case 2: set_b(g.seg[2]); lkb = g.seg[2].K / BK; break;
+          case 3: set_b(g.seg[3]); lkb = g.seg[3].K / BK; break;
+          default: set_b(g.seg[4]); lkb = g.seg[4].K / BK; break;
+        }
+      }
+    };
+    ring64_tile<GATED, BM>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0, n0, g.N);
   };
-  ring64_tile<GATED, BM, false>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0, n0,
-                                g.N);
+  if (half >= 0) tile(std::integral_constant<int, 128>{});
+  else tile(std::integral_constant<int, 256>{});
 #endif
 }
 
 // Grouped expert GEMMs on the routing's tiles of at most kTiledBM = 192 rows
-// (tile table, gathered activation rows, the tile's expert's B), weights two
-// stages ahead.
+// (tile table, gathered activation rows, the tile's expert's B).
 template <bool GATED>
 __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -1330,8 +1331,8 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
 #pragma unroll
     for (int i = 0; i < LB; ++i) pb[i] += BK;
   };
-  ring64_tile<GATED, BM, true>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0,
-                               n0, g.N);
+  ring64_tile<GATED, BM>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0, n0,
+                         g.N);
 #endif
 }
 
@@ -1347,15 +1348,33 @@ bool ring64_fits(const DenseGemm& d) {
   return nk >= 3;
 }
 
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <bool GATED>
 hipError_t run_ring64(const DenseGemm& d, hipStream_t s) {
   constexpr int NOUT = GATED ? 128 : 256;
   auto kern = ring64_dense_kernel<GATED>;
   if (hipError_t e = allow_dynamic_lds((const void*)kern, kR64Lds); e != hipSuccess) return e;
-  const int64_t nblk = int64_t((d.M + 255) / 256) * ((d.N + NOUT - 1) / NOUT);
-  if (nblk <= 0) return hipSuccess;
+  const int64_t nt = int64_t((d.M + 255) / 256) * ((d.N + NOUT - 1) / NOUT);
+  if (nt <= 0) return hipSuccess;
+  // one workgroup per CU at a time: split the tiles of a last round that
+  // would be at most half full into 128-row halves
+  const int64_t cus = device_cus(), rest = nt % cus;
+  const int64_t nsplit = rest <= cus / 2 ? rest : 0;
+  const int64_t nblk = nt + nsplit;
   if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3{uint32_t(nblk)}, dim3{512u}, kR64Lds, s, d);
+  hipLaunchKernelGGL(kern, dim3{uint32_t(nblk)}, dim3{512u}, kR64Lds, s, d, int(nsplit));
   return hipGetLastError();
 }
 
