@@ -1026,8 +1026,9 @@ __device__ __forceinline__ int ring64_gchunk(int wid, int lane) {
 // Main loop and epilogue of a 64-wide-ring tile.  pa / pb: this lane's
 // global addresses of its A / B rows at stage 0 (LA = BM/64 and 4 rows);
 // next_a / next_b advance them by one stage (and may switch segments).  The
-// tile's rows row0 .. row0+nrows-1 of C, columns n0 .. of N, are written.
-template <bool GATED, int BM, class NextA, class NextB>
+// tile's rows row0 .. row0+nrows-1 of C, columns n0 .. of N, are written;
+// NT: with nontemporal stores.
+template <bool GATED, int BM, bool NT, class NextA, class NextB>
 __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, int lane, int tid, int nk, int nrows,
                                             const bf16_t* (&pa)[BM / 64], const bf16_t* (&pb)[4], NextA next_a,
                                             NextB next_b, uint16_t* C, int64_t ldc, int64_t row0, int n0, int N) {
@@ -1187,7 +1188,18 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
   for (int c = tid; c < BM * OCPR; c += NTH) {
     const int row = c / OCPR, cc = c % OCPR;
     if (row < nrows && n0 + cc * 8 < N)
-      *reinterpret_cast<uint4*>(C + (row0 + row) * ldc + n0 + cc * 8) = *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
+    {
+      const uint4 val = *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
+      uint4* dst = reinterpret_cast<uint4*>(C + (row0 + row) * ldc + n0 + cc * 8);
+      if constexpr (NT) {
+        __builtin_nontemporal_store(val.x, &dst->x);
+        __builtin_nontemporal_store(val.y, &dst->y);
+        __builtin_nontemporal_store(val.z, &dst->z);
+        __builtin_nontemporal_store(val.w, &dst->w);
+      } else {
+        *dst = val;
+      }
+    }
   }
 }
 
@@ -1218,7 +1230,14 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g, int n
     t = nwhole + h / 2;
     half = int(h % 2);
   }
-  const int tn = int(t % uint32_t(tiles_n)), tm = int(t / uint32_t(tiles_n));
+  // within an XCD's run of tile indices, groups of 4 row tiles x all column
+  // tiles, row tile fastest: the 32 tiles an XCD runs at once are 4 x 8, so
+  // their A and B slices are shared through its L2 (the 16k up-projection
+  // 617 -> 583 us against plain row-major; the down-projection unchanged)
+  constexpr int GM = 4;
+  const int tiles_m = (g.M + 255) / 256;
+  const int first = int(t) / (GM * tiles_n) * GM, gs = min(tiles_m - first, GM), w = int(t) % (GM * tiles_n);
+  const int tm = first + w % gs, tn = w / gs;
   const int row0 = tm * 256 + (half > 0 ? 128 : 0);
   const int nrows = min(half >= 0 ? 128 : 256, g.M - row0), n0 = tn * NOUT;
   if (nrows <= 0) return;  // (the empty second half of a short last row tile)
@@ -1280,7 +1299,8 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g, int n
         }
       }
     };
-    ring64_tile<GATED, BM>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0, n0, g.N);
+    ring64_tile<GATED, BM, false>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0, n0,
+                                  g.N);
   };
   if (half >= 0) tile(std::integral_constant<int, 128>{});
   else tile(std::integral_constant<int, 256>{});
@@ -1288,7 +1308,11 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g, int n
 }
 
 // Grouped expert GEMMs on the routing's tiles of at most kTiledBM = 192 rows
-// (tile table, gathered activation rows, the tile's expert's B).
+// (tile table, gathered activation rows, the tile's expert's B).  FC1 (gated)
+// writes H with nontemporal stores: at prefill its 134 MB of output otherwise
+// pushes the weight stream and the gathered rows out of L2 (FC1 780 -> 745 us
+// in the layer, alternated builds).  For FC2's Y the same hint was a wash (FC2
+// slower by about what the combine that reads Y gained).
 template <bool GATED>
 __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -1331,8 +1355,8 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
 #pragma unroll
     for (int i = 0; i < LB; ++i) pb[i] += BK;
   };
-  ring64_tile<GATED, BM>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0, n0,
-                         g.N);
+  ring64_tile<GATED, BM, GATED>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0,
+                                n0, g.N);
 #endif
 }
 
