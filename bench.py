@@ -233,7 +233,8 @@ class ClockSampler:
 
 def grouped_kernel(cfg, dom, fused_mlp, packed=False):
     """Which kernel runs the grouped GEMM ``dom`` (the library's own choice:
-    MXFP4 w4a8 -> block-scaled kernel; MXFP4 w4a16 -> its weight-streaming
+    MXFP4 w4a8 -> block-scaled kernel (its direct-to-LDS ring form when K is
+    a multiple of 512); MXFP4 w4a16 -> its weight-streaming
     kernels at <= 32 rows per expert on average, else the register-staged
     grouped kernel in its MXFP4 form; bf16 at <= 32 rows per expert on average
     -> weight-streaming kernel; otherwise, tile-packed weights -> the
@@ -249,6 +250,8 @@ def grouped_kernel(cfg, dom, fused_mlp, packed=False):
             return "skinny_w4a16_kernel", "skinny.hip"
         return "grouped_tiled_kernel (MXFP4 w4a16)", "gemm.hip"
     if cfg.mxfp4:
+        if K % 512 == 0:
+            return "mx_ring_kernel", "mx.hip"
         return "mx_grouped_kernel", "mx.hip"
     if R <= 32 * cfg.E:
         return ("skinny_lds_kernel" if K % 128 == 0 else "skinny_grouped_kernel"), "skinny.hip"

@@ -486,6 +486,7 @@ int fwd_back(const FwdCtx& c) {
     m1.tiles = p->tiles_t;
     m1.ntiles = p->n_t;
     m1.max_tiles = p->max_t;
+    m1.a_rows_n = T;
     if ((e = lmoe::launch_grouped_mx(m1, s, fc1_t0, fc1_t1)) != hipSuccess) return hip_fail(e, "expert FC1 (MXFP4)");
     lmoe::GroupedMx m2 = m1;
     m2.Cq = nullptr;
@@ -503,6 +504,7 @@ int fwd_back(const FwdCtx& c) {
     m2.gated = false;
     m2.C = Y;
     m2.ldc = l;
+    m2.a_rows_n = R;
     if ((e = lmoe::launch_grouped_mx(m2, s)) != hipSuccess) return hip_fail(e, "expert FC2 (MXFP4)");
     if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
   } else if (w4a16 && R > int64_t(32) * p->E) {

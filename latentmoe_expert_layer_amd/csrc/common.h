@@ -83,4 +83,22 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct-to-LDS load: lane l's 16 bytes from gptr land at LDS byte
+// lds_base + 16 l.  Inline asm, so the compiler sees no LDS write that
+// it would order before every later LDS read (it cannot tell ring entries
+// apart); the kernels order them with vmcnt waits and barriers.  lds_base goes
+// to m0, so it must be wave-uniform.
+__device__ __forceinline__ void g2lds16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 }  // namespace lmoe

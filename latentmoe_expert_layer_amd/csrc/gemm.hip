@@ -795,23 +795,6 @@ constexpr int kRingSlots = 5;
 constexpr int kRingStage = (256 + 256) * kRingRow;
 constexpr int kRingLds = kRingSlots * kRingStage;  // 160 KiB: all of a CU's LDS
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from gptr land at
-// LDS byte lds_base + 16 l.  Inline asm, so the compiler sees no LDS write that
-// it would order before every later LDS read (it cannot tell the ring slots
-// apart); the kernel orders them itself with vmcnt waits and barriers.
-__device__ __forceinline__ void g2lds16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(N), leaving the other counters alone
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 template <bool GATED>
 __global__ __launch_bounds__(512, 1) void ring_dense_kernel(DenseGemm g) {
 #if defined(__HIP_DEVICE_COMPILE__)

@@ -222,6 +222,7 @@ struct GroupedMx {
   const Tile* tiles;
   const int32_t* ntiles;
   int64_t max_tiles;
+  int64_t a_rows_n = 0;  // rows of A (and As); 0: unknown
 };
 hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 

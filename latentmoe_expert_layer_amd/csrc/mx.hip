@@ -131,6 +131,65 @@ constexpr int mx_lds_bytes() {
   return 2 * stage > epi ? 2 * stage : epi;
 }
 
+// Epilogue of a tile of BM rows whose accumulators are acc (wave tiles
+// BM/2 x 64 of 32x32 fragments, fa of them holding rows): gated, SwiGLU of
+// subtile 0 with its up subtile 1; the bf16 tile is staged in the LDS (free
+// on entry), then written as MXFP8 codes and scales (Cq set) or as bf16, in
+// 16-byte row-contiguous stores.
+template <bool GATED, int BM, int FM, int LDSB>
+__device__ __forceinline__ void mx_epilogue(const MxArgs& g, const f32x16 (&acc)[FM][2], int fa, uint8_t* lds,
+                                            int row0, int nrows, int n0) {
+  constexpr int NTH = 512, NOUT = GATED ? 128 : 256, WAVES_N = 4, WM = BM / 2, WN = 64, FN = 2;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, rl = lane & 31;
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  constexpr int CLD = NOUT + 8;
+  static_assert(BM * CLD * 2 <= LDSB, "epilogue staging fits");
+  bf16_t* Cs = reinterpret_cast<bf16_t*>(lds);
+  constexpr int JO = GATED ? 1 : FN, WO = GATED ? WN / 2 : WN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    if (i < fa)
+#pragma unroll
+      for (int j = 0; j < JO; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int col = wn * WO + j * 32 + rl;
+          float x = acc[i][j][v];
+          if constexpr (GATED) x = silu_mul(x, acc[i][1][v]);
+          Cs[row * CLD + col] = f32_to_bf16(x);
+        }
+  __syncthreads();
+  if (g.Cq) {
+    // quantised output (the next GEMM's MXFP8 operand): one thread per
+    // (row, 32-column block) of the bf16 tile staged above
+    constexpr int BPR = NOUT / 32;
+    for (int c = tid; c < BM * BPR; c += NTH) {
+      const int row = c / BPR, b = c % BPR, col = n0 + b * 32;
+      if (row < nrows && col < g.N) {
+        uint4 raw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const uint4*>(&Cs[row * CLD + b * 32 + i * 8]);
+        uint4 q[2];
+        const int64_t r = int64_t(row0) + row;
+        g.Cqs[r * (g.ldc / 32) + col / 32] = quant_block32(raw, q);
+        uint4* dst = reinterpret_cast<uint4*>(g.Cq + r * g.ldc + col);
+        dst[0] = q[0];
+        dst[1] = q[1];
+      }
+    }
+    return;
+  }
+  constexpr int OCPR = NOUT / 8;
+  for (int c = tid; c < BM * OCPR; c += NTH) {
+    const int row = c / OCPR, cc = c % OCPR;
+    if (row < nrows && n0 + cc * 8 < g.N) {
+      *reinterpret_cast<uint4*>(g.C + (int64_t(row0) + row) * g.ldc + n0 + cc * 8) =
+          *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
+    }
+  }
+}
+
 // Grouped block-scaled GEMM.  Macro tile = (expert segment of <= 256 rows,
 // 256 B rows: plain -> 256 output columns; gated -> 128 gate + 128 up rows ->
 // 128 output columns).  8 waves, 2 per SIMD, as 2 x 4 with 128 x 64 wave
@@ -377,54 +436,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, uint32_t lt, uint8_t* l
     default: mainloop(std::integral_constant<int, FM>{}); break;
   }
 
-  // Epilogue (gated: SwiGLU of subtile 0 with its up subtile 1), bf16 staging
-  // in LDS, then 16-byte row-contiguous stores.
-  constexpr int CLD = NOUT + 8;
-  static_assert(BM * CLD * 2 <= mx_lds_bytes<GATED, BM>(), "epilogue staging fits");
-  bf16_t* Cs = reinterpret_cast<bf16_t*>(lds);
-  constexpr int JO = GATED ? 1 : FN, WO = GATED ? WN / 2 : WN;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-    if (i < fa)
-#pragma unroll
-      for (int j = 0; j < JO; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const int col = wn * WO + j * 32 + rl;
-          float x = acc[i][j][v];
-          if constexpr (GATED) x = silu_mul(x, acc[i][1][v]);
-          Cs[row * CLD + col] = f32_to_bf16(x);
-        }
-  __syncthreads();
-  if (g.Cq) {
-    // quantised output (the next GEMM's MXFP8 operand): one thread per
-    // (row, 32-column block) of the bf16 tile staged above
-    constexpr int BPR = NOUT / 32;
-    for (int c = tid; c < BM * BPR; c += NTH) {
-      const int row = c / BPR, b = c % BPR, col = n0 + b * 32;
-      if (row < nrows && col < g.N) {
-        uint4 raw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const uint4*>(&Cs[row * CLD + b * 32 + i * 8]);
-        uint4 q[2];
-        const int64_t r = int64_t(row0) + row;
-        g.Cqs[r * (g.ldc / 32) + col / 32] = quant_block32(raw, q);
-        uint4* dst = reinterpret_cast<uint4*>(g.Cq + r * g.ldc + col);
-        dst[0] = q[0];
-        dst[1] = q[1];
-      }
-    }
-    return;
-  }
-  constexpr int OCPR = NOUT / 8;
-  for (int c = tid; c < BM * OCPR; c += NTH) {
-    const int row = c / OCPR, cc = c % OCPR;
-    if (row < nrows && n0 + cc * 8 < g.N) {
-      *reinterpret_cast<uint4*>(g.C + (int64_t(row0) + row) * g.ldc + n0 + cc * 8) =
-          *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
-    }
-  }
+  mx_epilogue<GATED, BM, FM, mx_lds_bytes<GATED, BM>()>(g, acc, fa, lds, row0, nrows, n0);
 }
 
 // The grid covers an upper bound on the tile count: blocks past the
@@ -468,6 +480,320 @@ hipError_t run_mx(const MxArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t 
   return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512}, lds, s, a, t0, t1);
 }
 
+
+// ------------------------------------------------ direct-to-LDS ring form ---
+// The deep form's tiles (at most 192 rows; 8 waves as 2 x 4 with 96 x 64 wave
+// tiles) with the operands moved into LDS by direct-to-LDS loads of whole
+// 128-byte lines, as the bf16 ring kernels do, instead of through registers.
+// A stage is 128 K: 192 rows x 128 B of activation codes.  A stage's weight
+// codes are 64 B per row, half a line, so the weights travel in pairs of
+// stages (256 rows x 128 B).  The e8m0 scales (4 bytes per row and stage)
+// travel in groups of four stages: 16 bytes per row, one load per 64 rows.
+// Loaded one stage at a time they would be 4-byte gathers, each asking for 64
+// separate lines: more line requests than all the codes together, and the
+// largest cost of the loads.  LDS slots: three for activation stages, two for
+// weight pairs, two for scale groups (152 KB).  The prologue loads S0 W0 A0
+// A1 W1 A2 (S: a scale group, W: a weight pair, A: a stage's activation
+// codes).  After the barrier of stage s, the stage reloads its activation
+// slot with A(s+3); an odd stage, the last user of its pair, also reloads the
+// pair's slot with the pair (s+3)/2; a stage 4g also loads scale group g+1
+// into the slot group g-1 left.  Codes land three stages before their use,
+// scales four.  One barrier per stage, before its second 64-K step: each wave
+// first waits for its LDS reads (lgkmcnt) and for its loads of stage s+1.
+// vmcnt counts in issue order, so the wait names how many of the wave's
+// newest loads may still be in flight: in the loop, after stage s mod 4 =
+// 0, 1, 2, 3, these are 7 (a pair and A(s+2)), 4 (a scale group and A(s+2)),
+// 7 and 3 (A(s+2)); in the last four stages 7, 3, 0 and none.  After the
+// barrier stage s+1 is visible and the slots stage s freed are refilled while
+// the second step's MFMAs run from registers.  Code rows are 128 B with the
+// 16-byte chunks XOR-swizzled by (row / 2) mod 8.  The MFMAs and their K
+// order are the deep form's: the results are bit-identical.  Needs K a
+// multiple of 512.
+constexpr int kMxrA = kTiledBM * kMxBK;         // one stage's activation codes: 24 KB
+constexpr int kMxrB = 256 * 128;                // a weight pair: 32 KB
+constexpr int kMxrS = 512 * 16;                 // a scale group: 192 + 256 rows (+64 spare) x 16 B
+constexpr int kMxrBOff = 3 * kMxrA;             // weight pair slots
+constexpr int kMxrSOff = kMxrBOff + 2 * kMxrB;  // scale group slots
+constexpr int kMxrLds = kMxrSOff + 2 * kMxrS;   // 152 KiB
+
+// direct-to-LDS loads from a wave-uniform base plus a 32-bit lane offset
+__device__ __forceinline__ void g2lds16_so(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(off), "s"(base) : "memory", "m0");
+}
+
+// One tile.  Operand addresses are 32-bit offsets from wave-uniform bases:
+// the activation codes and scales from A and As (which the host checks to be
+// below 2^31 bytes), the weights from the tile's expert matrices.
+template <bool GATED>
+__device__ __forceinline__ void mx_ring_tile(const MxArgs& g, uint32_t lt, uint8_t* lds, uint32_t lds0) {
+  constexpr int NW = 8, BM = kTiledBM, BR = 256, NOUT = GATED ? 128 : 256, WAVES_N = 4;
+  constexpr int WM = BM / 2, WN = 64, FM = WM / 32, FN = 2, ROWB = 128;
+  constexpr int LA = BM / 8 / NW;   // activation code loads (1 KB each) per wave and stage
+  constexpr int LB = BR / 8 / NW;   // weight code loads per wave and stage pair
+  constexpr int LS = 1;             // scale loads per wave and group
+  static_assert(BM % (8 * NW) == 0 && BM + BR <= NW * 64 && LB == 4, "tile rows");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const int tiles_n = (g.N + NOUT - 1) / NOUT;
+  const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
+  const Tile tl = g.tiles[tm];
+  const int row0 = __builtin_amdgcn_readfirstlane(tl.row_start);
+  const int nrows = __builtin_amdgcn_readfirstlane(tl.nrows);
+  const int expert = __builtin_amdgcn_readfirstlane(tl.expert);
+  const int n0 = tn * NOUT;
+  const int K = g.K, KB = K / 32, nk = K / kMxBK;
+
+  // tile row r's activation row (rows past the tile repeat its last one)
+  auto a_src = [&](int r) __attribute__((always_inline)) -> uint32_t {
+    int src = row0 + min(r, nrows - 1);
+    if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
+    return uint32_t(src);
+  };
+  // LDS weight row r (gated: 128 gate rows, then 128 up rows): its row in the
+  // expert's matrix
+  auto w_row = [&](int r) __attribute__((always_inline)) -> uint32_t {
+    return uint32_t(min(n0 + (GATED && r >= BR / 2 ? r - BR / 2 : r), g.N - 1));
+  };
+  const int64_t wexp = int64_t(expert) * g.N;
+  const uint8_t* wg = g.B + wexp * (K / 2);  // the expert's gate (plain: only) codes
+  const uint8_t* wu = GATED ? g.B3 + wexp * (K / 2) : wg;
+  // Code loads: lane l of wave w takes row 8 (w + 8 q) + l/8 of its operand,
+  // into chunk l%8 of the LDS row, from global chunk (l%8) ^ ((row/2) mod 8);
+  // weight loads q < 2 take rows 0..127 (gated: gate rows), q >= 2 rows
+  // 128..255 (gated: up rows).  Scale loads: lane l of wave w takes the 16
+  // bytes of scale row 64 w + l of [192 activation rows, 256 weight rows,
+  // weight rows 0..63 again (a spare copy that nobody reads)], so each wave's
+  // scale base is uniform.
+  const uint32_t gc = uint32_t(((lane & 7) ^ ((((wid & 1) << 2) + (lane >> 4)) & 7)) * 16);
+  uint32_t oa[LA], ob[LB], os;
+#pragma unroll
+  for (int q = 0; q < LA; ++q) oa[q] = a_src(8 * (wid + NW * q) + (lane >> 3)) * uint32_t(K) + gc;
+#pragma unroll
+  for (int q = 0; q < LB; ++q) ob[q] = w_row(8 * (wid + NW * q) + (lane >> 3)) * uint32_t(K / 2) + gc;
+  const uint8_t* sbase;
+  {
+    const int idx = wid * 64 + lane;
+    if (wid < BM / 64) {
+      sbase = g.As;
+      os = a_src(idx) * uint32_t(KB);
+    } else {
+      const int r = wid < (BM + BR) / 64 ? idx - BM : idx - BM - BR;
+      sbase = (GATED && wid >= (BM + BR / 2) / 64 && wid < (BM + BR) / 64 ? g.B3s : g.Bs) + wexp * KB;
+      os = w_row(r) * uint32_t(KB);
+    }
+  }
+  auto rfl = [](uint32_t v) __attribute__((always_inline)) -> uint32_t {
+    return uint32_t(__builtin_amdgcn_readfirstlane(int(v)));
+  };
+  auto issue_a = [&](int slot, int q) __attribute__((always_inline)) {
+    g2lds16_so(g.A, oa[q], rfl(lds0 + slot * kMxrA + (wid + NW * q) * 1024));
+  };
+  auto next_a = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < LA; ++q) oa[q] += kMxBK;
+  };
+  auto issue_b = [&](int slot, int q) __attribute__((always_inline)) {
+    g2lds16_so(q < LB / 2 ? wg : wu, ob[q], rfl(lds0 + kMxrBOff + slot * kMxrB + (wid + NW * q) * 1024));
+  };
+  auto next_b = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < LB; ++q) ob[q] += kMxBK;  // two stages of packed codes
+  };
+  auto issue_s = [&](int slot) __attribute__((always_inline)) {
+    g2lds16_so(sbase, os, rfl(lds0 + kMxrSOff + slot * kMxrS + wid * 1024));
+    os += 4 * kMxBK / 32;
+  };
+  auto brow = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (GATED) return j == 0 ? wn * 32 : BR / 2 + wn * 32;
+    else return wn * WN + j * 32;
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int fr = lane & 31, fsw = (fr >> 1) & 7, fh = lane >> 5;  // fragment row, its swizzle, K half
+  auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
+    constexpr int FA = decltype(fa_c)::value, FAR = FA > 0 ? FA : 1;
+    // one set of activation fragments, each reloaded after its last MFMA;
+    // two sets of weight fragments (the 64-K step t's set is t)
+    i32x8v af[FAR];
+    int sa[FAR];
+    uint4 bq[2][FN];
+    int sb[2][FN];
+    // Fragments of the 64-K step t of stage s, R = s mod 4: its activation
+    // codes in slot as, its pair in slot bs, its scales in group slot ss.
+    auto rd_a = [&](int as, int ss, int R, int t, int i) __attribute__((always_inline)) {
+      const uint8_t* E = lds + as * kMxrA;
+      const int r = wm * WM + i * 32 + fr;
+      const uint4 lo = *reinterpret_cast<const uint4*>(E + r * ROWB + (((4 * t + fh) ^ fsw) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(E + r * ROWB + (((4 * t + 2 + fh) ^ fsw) << 4));
+      af[i] = i32x8v{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+      sa[i] = lds[kMxrSOff + ss * kMxrS + r * 16 + 4 * R + 2 * t + fh];
+    };
+    auto rd_b = [&](int bs, int ss, int R, int t, int j) __attribute__((always_inline)) {
+      const int r = brow(j) + fr;
+      bq[t][j] = *reinterpret_cast<const uint4*>(lds + kMxrBOff + bs * kMxrB + r * ROWB +
+                                                 (((4 * (R & 1) + 2 * t + fh) ^ fsw) << 4));
+      sb[t][j] = lds[kMxrSOff + ss * kMxrS + (BM + r) * 16 + 4 * R + 2 * t + fh];
+    };
+    // the 64-K step t's MFMAs (activation fragment major).  With rd set, the
+    // fragments of step tn of the stage (as, bs, ss, R) are read under them:
+    // the weight set after the first MFMA, each activation fragment after its
+    // last MFMA.  The nside side items (loads) are spread over the MFMAs in
+    // order: MFMA m is followed by items c m .. c m + c - 1, c = ceil(nside /
+    // NM) (all at once if NM = 0).  The order matters: the waits count on
+    // each wave's loads leaving in the order issued.
+    auto mm = [&](int t, bool rd, int as, int bs, int ss, int R, int tn, int nside, auto side)
+                  __attribute__((always_inline)) {
+      constexpr int NM = FA * FN;
+      const int c = NM > 0 ? (nside + NM - 1) / NM : 0;
+#pragma unroll
+      for (int i = 0; i < FA; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint4 b = bq[t][j];
+          acc[i][j] = mfma_mx(af[i], i32x8v{int(b.x), int(b.y), int(b.z), int(b.w), 0, 0, 0, 0}, sa[i], sb[t][j],
+                              acc[i][j]);
+          const int m = i * FN + j;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k >= m * c && k < m * c + c && k < nside) side(k);
+          if (rd && m == 0)
+#pragma unroll
+            for (int j2 = 0; j2 < FN; ++j2) rd_b(bs, ss, R, tn, j2);
+          if (rd && j == FN - 1) rd_a(as, ss, R, tn, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      if constexpr (NM == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k < nside) side(k);
+        if (rd)
+#pragma unroll
+          for (int j2 = 0; j2 < FN; ++j2) rd_b(bs, ss, R, tn, j2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    static_assert(LS + LB + LA <= 8, "side items");
+    int as0 = 0;  // A(s)'s slot: s mod 3
+    int ss0 = 0;  // stage s's scale group slot
+    // stage s, R = s mod 4.  W: loads allowed in flight at the barrier (-1:
+    // the last stage, no barrier); IA / IB / IS: load A(s+3) / the pair
+    // (s+3)/2 (odd R) / scale group s/4 + 1 (R = 0)
+    auto step = [&](auto r_c, auto w_c, auto ia_c, auto ib_c, auto is_c) __attribute__((always_inline)) {
+      constexpr int R = decltype(r_c)::value, W = decltype(w_c)::value;
+      constexpr bool IA = decltype(ia_c)::value, IB = decltype(ib_c)::value, IS = decltype(is_c)::value;
+      static_assert(!IB || (R & 1), "pairs are reloaded by odd stages");
+      static_assert(!IS || R == 0, "scale groups are loaded by stages 4g");
+      constexpr int BS = R >> 1, BSN = ((R + 1) & 3) >> 1;  // pair slots of stages s and s+1
+      mm(0, true, as0, BS, ss0, R, 1, 0, [&](int) {});
+      if constexpr (W >= 0) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s are done
+        wait_vmcnt<W>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");       // no LDS read moves above the barrier
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int as1 = as0 == 2 ? 0 : as0 + 1, ss1 = R == 3 ? ss0 ^ 1 : ss0;
+      constexpr int NS = IS ? LS : 0, NB = IB ? LB : 0, NA = IA ? LA : 0;
+      mm(1, W >= 0, as1, BSN, ss1, (R + 1) & 3, 0, NS + NB + NA, [&](int k) __attribute__((always_inline)) {
+        if (k < NS) issue_s(ss0 ^ 1);         // scale group s/4 + 1
+        else if (k < NS + NB) issue_b(BS, k - NS);  // the pair (s+3)/2 into the slot of pair s/2
+        else issue_a(as0, k - NS - NB);       // A(s+3) into A(s)'s slot
+      });
+      if constexpr (NB > 0) next_b();
+      if constexpr (NA > 0) next_a();
+      as0 = as1;
+      ss0 = ss1;
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using W7 = std::integral_constant<int, LB + LA>;
+    using W4 = std::integral_constant<int, LS + LA>;
+    using W3 = std::integral_constant<int, LA>;
+    using W0 = std::integral_constant<int, 0>;
+    using Wm = std::integral_constant<int, -1>;
+    issue_s(0);  // S0
+#pragma unroll
+    for (int q = 0; q < LB; ++q) issue_b(0, q);  // W0
+    next_b();
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {  // A0, A1
+#pragma unroll
+      for (int q = 0; q < LA; ++q) issue_a(e, q);
+      next_a();
+    }
+#pragma unroll
+    for (int q = 0; q < LB; ++q) issue_b(1, q);  // W1
+    next_b();
+#pragma unroll
+    for (int q = 0; q < LA; ++q) issue_a(2, q);  // A2
+    next_a();
+    wait_vmcnt<2 * LA + LB>();  // S0, W0 and A0 have landed; A1, W1, A2 may be in flight
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < FN; ++j) rd_b(0, 0, 0, 0, j);
+#pragma unroll
+    for (int i = 0; i < FA; ++i) rd_a(0, 0, 0, 0, i);
+    for (int s = 0; s + 4 < nk; s += 4) {
+      step(I0{}, W7{}, T{}, F{}, T{});
+      step(I1{}, W4{}, T{}, T{}, F{});
+      step(I2{}, W7{}, T{}, F{}, F{});
+      step(I3{}, W3{}, T{}, T{}, F{});
+    }
+    step(I0{}, W7{}, T{}, F{}, F{});  // s = nk-4: A(nk-1)
+    step(I1{}, W3{}, F{}, F{}, F{});
+    step(I2{}, W0{}, F{}, F{}, F{});
+    step(I3{}, Wm{}, F{}, F{}, F{});
+  };
+  const int fa = max(0, min(FM, (nrows - wm * WM + 31) / 32));
+  switch (fa) {
+    case 0: mainloop(std::integral_constant<int, 0>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    case 2: mainloop(std::integral_constant<int, 2>{}); break;
+    default: mainloop(std::integral_constant<int, FM>{}); break;
+  }
+  __syncthreads();
+  mx_epilogue<GATED, BM, FM, kMxrLds>(g, acc, fa, lds, row0, nrows, n0);
+}
+
+// The grid covers an upper bound on the tile count; blocks past the
+// device-side count exit.  (A persistent grid gains nothing here: a block's
+// output stores drain while the next block on its CU starts.)
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void mx_ring_kernel(MxArgs g) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  extern __shared__ uint4 lds_u4[];
+  uint8_t* lds = reinterpret_cast<uint8_t*>(lds_u4);
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
+  constexpr int NOUT = GATED ? 128 : 256;
+  const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t((g.N + NOUT - 1) / NOUT);
+  if (blockIdx.x >= nreal) return;
+  mx_ring_tile<GATED>(g, xcd_swizzle(blockIdx.x, nreal), lds, lds0);
+#endif
+}
+
+template <bool GATED>
+hipError_t run_mx_ring(const MxArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  constexpr int NOUT = GATED ? 128 : 256;
+  auto kern = mx_ring_kernel<GATED>;
+  if (hipError_t e = allow_dynamic_lds((const void*)kern, kMxrLds); e != hipSuccess) return e;
+  const int64_t nblk = max_tiles * ((a.N + NOUT - 1) / NOUT);
+  if (nblk <= 0) return hipSuccess;
+  return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512}, size_t(kMxrLds), s, a, t0, t1);
+}
+
 }  // namespace
 
 hipError_t launch_quant_mxfp8(const uint16_t* src, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
@@ -496,12 +822,16 @@ hipError_t launch_grouped_mx(const GroupedMx& g, hipStream_t s, hipEvent_t t0, h
   a.Cqs = g.Cqs;
   a.tiles = g.tiles;
   a.ntiles = g.ntiles;
-  // routing cuts tiles at kTiledBM rows, within both kernels' reach; the deep
-  // pipeline needs an even number (>= 4) of 128-wide K stages
+  // routing cuts tiles at kTiledBM rows, within every form's reach
   static_assert(kTiledBM <= 256 && kTiledBM % 64 == 0, "tile table granularity");
   // FC2 (plain, bf16 output) writes 2 bytes per output against a short K:
   // in the deep form its stores get the persistent grid, to drain behind the
   // next tile (the 256-row form has no registers to spare for it)
+  // the ring form needs K % 512 == 0 and 32-bit offsets into A, As and an
+  // expert's weights; the deep form an even number (>= 4) of 128-wide stages
+  constexpr int64_t kOff = int64_t(1) << 31;
+  if (g.K % 512 == 0 && g.a_rows_n > 0 && g.a_rows_n * g.K < kOff && int64_t(g.N) * g.K / 2 < kOff)
+    return g.gated ? run_mx_ring<true>(a, g.max_tiles, s, t0, t1) : run_mx_ring<false>(a, g.max_tiles, s, t0, t1);
   if (g.K % 256 == 0 && g.K >= 512)
     return g.gated ? run_mx<true, true, false>(a, g.max_tiles, s, t0, t1)
                    : run_mx<false, true, true>(a, g.max_tiles, s, t0, t1);

@@ -243,10 +243,17 @@ MX_LAYERS = [
     ("mx_small", dict(T=203, d=192, l=256, E=9, k=3, S=1, I=128, Is=64, mxfp4=True)),
     ("mx_ragged", dict(T=77, d=128, l=384, E=40, k=8, S=2, I=256, Is=64, mxfp4=True)),
     ("mx_heavy", dict(T=700, d=256, l=128, E=4, k=2, S=0, I=384, Is=0, mxfp4=True)),
-    # K = 512 for both GEMMs (the two-stages-ahead pipeline), experts over 192 rows (two tiles each)
+    # K = 512 for both GEMMs (the direct-to-LDS ring, four stages: its
+    # prologue and tail only), experts over 192 rows (two tiles each)
     ("mx_deep", dict(T=400, d=128, l=512, E=3, k=2, S=1, I=512, Is=64, mxfp4=True)),
-    # more real tiles than CUs with I % 256 == 0: the persistent FC2 grid runs
-    # several tiles per workgroup (about 8 x 21 row tiles x 8 column tiles)
+    # the ring at K = 1024 (eight stages: one pass of the loop, two scale
+    # groups), ~120-row tiles: the lower waves hold 0..2 fragments of rows
+    ("mx_ring_k1024", dict(T=300, d=128, l=1024, E=5, k=2, S=1, I=1024, Is=64, mxfp4=True)),
+    # K = 768: a multiple of 256 but not of 512, the register-staged deep form
+    # (weights two stages ahead) with its persistent FC2 grid
+    ("mx_deep_k768", dict(T=400, d=128, l=768, E=3, k=2, S=1, I=768, Is=64, mxfp4=True)),
+    # more real tiles than CUs: FC1 at K = 2048 (sixteen stages, four scale
+    # groups), about 8 x 21 row tiles x 4 and x 8 column tiles
     ("mx_many_tiles", dict(T=4096, d=128, l=2048, E=8, k=2, S=0, I=512, Is=0, mxfp4=True)),
 ]
 
