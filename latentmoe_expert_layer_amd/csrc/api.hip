@@ -528,6 +528,7 @@ int fwd_back(const FwdCtx& c) {
     t1.tiles = p->tiles_t;
     t1.ntiles = p->n_t;
     t1.max_tiles = p->max_t;
+    t1.a_rows_n = T;
     if ((e = lmoe::launch_grouped_tiled(t1, s, fc1_t0, fc1_t1)) != hipSuccess)
       return hip_fail(e, "expert FC1 (MXFP4 w4a16, tiled)");
     lmoe::GroupedGemm t2 = t1;
@@ -544,6 +545,7 @@ int fwd_back(const FwdCtx& c) {
     t2.gated = false;
     t2.C = Y;
     t2.ldc = l;
+    t2.a_rows_n = R;
     if ((e = lmoe::launch_grouped_tiled(t2, s)) != hipSuccess) return hip_fail(e, "expert FC2 (MXFP4 w4a16, tiled)");
     if ((e = mark(4)) != hipSuccess) return hip_fail(e, "event");
   } else if (w4a16 && l == lmoe::kW4MlpWidth && I == lmoe::kW4MlpWidth) {

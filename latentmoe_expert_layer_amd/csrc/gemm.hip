@@ -1006,6 +1006,54 @@ __device__ __forceinline__ int ring64_gchunk(int wid, int lane) {
   return (lane & 7) ^ ((((wid & 1) << 2) + ((lane >> 3) >> 1)) & 7);
 }
 
+// Epilogue of a 64-wide-ring tile (BM rows x 256 B rows on 8 waves as 2 x 4,
+// wave tiles BM/2 x 64 in acc, the first fa of a wave's 32-row subtiles
+// holding rows of the tile); the LDS is free on entry.  Gated: SwiGLU of each
+// gate subtile with its up subtile.  Rows row0 .. row0+nrows-1 of C, columns
+// n0 .. (below N), are written; NT: with nontemporal stores.
+template <bool GATED, int BM, bool NT>
+__device__ __forceinline__ void ring64_store(char* lds, const f32x16 (&acc)[BM / 64][2], int fa, int wm, int wn,
+                                             int lane, int tid, uint16_t* C, int64_t ldc, int64_t row0, int nrows,
+                                             int n0, int N) {
+  constexpr int NTH = 512, NOUT = GATED ? 128 : 256, WM = BM / 2, WN = 64, FM = WM / 32, FN = 2;
+  // epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores
+  constexpr int CLD = NOUT + 8;
+  static_assert(BM * CLD * 2 <= kR64Lds, "epilogue staging fits in the ring");
+  bf16_t* Cs = reinterpret_cast<bf16_t*>(lds);
+  constexpr int JO = GATED ? 1 : FN, WO = GATED ? 32 : WN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    if (i < fa)
+#pragma unroll
+      for (int j = 0; j < JO; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int col = wn * WO + j * 32 + (lane & 31);
+          float x = acc[i][j][v];
+          if constexpr (GATED) x = silu_mul(x, acc[i][1][v]);
+          Cs[row * CLD + col] = f32_to_bf16(x);
+        }
+  __syncthreads();
+  constexpr int OCPR = NOUT / 8;
+  for (int c = tid; c < BM * OCPR; c += NTH) {
+    const int row = c / OCPR, cc = c % OCPR;
+    if (row < nrows && n0 + cc * 8 < N)
+    {
+      const uint4 val = *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
+      uint4* dst = reinterpret_cast<uint4*>(C + (row0 + row) * ldc + n0 + cc * 8);
+      if constexpr (NT) {
+        __builtin_nontemporal_store(val.x, &dst->x);
+        __builtin_nontemporal_store(val.y, &dst->y);
+        __builtin_nontemporal_store(val.z, &dst->z);
+        __builtin_nontemporal_store(val.w, &dst->w);
+      } else {
+        *dst = val;
+      }
+    }
+  }
+}
+
 // Main loop and epilogue of a 64-wide-ring tile.  pa / pb: this lane's
 // global addresses of its A / B rows at stage 0 (LA = BM/64 and 4 rows);
 // next_a / next_b advance them by one stage (and may switch segments).  The
@@ -1015,8 +1063,8 @@ template <bool GATED, int BM, bool NT, class NextA, class NextB>
 __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, int lane, int tid, int nk, int nrows,
                                             const bf16_t* (&pa)[BM / 64], const bf16_t* (&pb)[4], NextA next_a,
                                             NextB next_b, uint16_t* C, int64_t ldc, int64_t row0, int n0, int N) {
-  constexpr int NW = 8, NTH = NW * 64, WAVES_N = 4;
-  constexpr int BR = 256, NOUT = GATED ? 128 : 256, WM = BM / 2, WN = 64;
+  constexpr int NW = 8, WAVES_N = 4;
+  constexpr int BR = 256, WM = BM / 2, WN = 64;
   constexpr int FM = WM / 32, FN = WN / 32, ROWB = kR64Row, ENT = kR64Ent;
   constexpr int LA = BM / 8 / NW, LB = BR / 8 / NW;  // 1 KB loads per wave and A / B half stage
   static_assert(BM % (8 * NW) == 0 && BM * ROWB <= ENT && FM >= 1 && FM <= 4, "tile rows");
@@ -1148,42 +1196,7 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
     default: mainloop(std::integral_constant<int, FM>{}); break;
   }
   __syncthreads();
-  // epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores
-  constexpr int CLD = NOUT + 8;
-  static_assert(BM * CLD * 2 <= kR64Lds, "epilogue staging fits in the ring");
-  bf16_t* Cs = reinterpret_cast<bf16_t*>(lds);
-  constexpr int JO = GATED ? 1 : FN, WO = GATED ? 32 : WN;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-    if (i < fa)
-#pragma unroll
-      for (int j = 0; j < JO; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const int col = wn * WO + j * 32 + (lane & 31);
-          float x = acc[i][j][v];
-          if constexpr (GATED) x = silu_mul(x, acc[i][1][v]);
-          Cs[row * CLD + col] = f32_to_bf16(x);
-        }
-  __syncthreads();
-  constexpr int OCPR = NOUT / 8;
-  for (int c = tid; c < BM * OCPR; c += NTH) {
-    const int row = c / OCPR, cc = c % OCPR;
-    if (row < nrows && n0 + cc * 8 < N)
-    {
-      const uint4 val = *reinterpret_cast<const uint4*>(&Cs[row * CLD + cc * 8]);
-      uint4* dst = reinterpret_cast<uint4*>(C + (row0 + row) * ldc + n0 + cc * 8);
-      if constexpr (NT) {
-        __builtin_nontemporal_store(val.x, &dst->x);
-        __builtin_nontemporal_store(val.y, &dst->y);
-        __builtin_nontemporal_store(val.z, &dst->z);
-        __builtin_nontemporal_store(val.w, &dst->w);
-      } else {
-        *dst = val;
-      }
-    }
-  }
+  ring64_store<GATED, BM, NT>(lds, acc, fa, wm, wn, lane, tid, C, ldc, row0, nrows, n0, N);
 }
 
 // Dense projections: 256 x 256 tiles over up to five K segments (the A and B
@@ -1343,6 +1356,272 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
 #endif
 }
 
+// ---------------------------------------- w4a16: MXFP4 weights, 64-wide ring ---
+// Grouped expert GEMMs with MXFP4 weights and bf16 activations at prefill
+// size (TokenSpeed Day-0 post, "Gluon kernels on AMD GPUs > Stable
+// LatentMoE": MXFP4 weights upcast inside the K loop, bf16 activations): the
+// tiles of ring64_grouped_kernel (<= 192 rows x 256 B rows, gated: 128 gate +
+// 128 up; 8 waves as 2 x 4 with 96 x 64 wave tiles of 32x32x16 bf16 MFMAs),
+// with every operand moved into LDS by direct-to-LDS loads of whole 128-byte
+// lines and the weights upcast from LDS to bf16 fragments in registers by
+// gfx950's scaled conversion (exact: an e2m1 value times a power of two).
+// A 64-K stage holds 192 rows x 128 B of activations.  A weight row's codes
+// for one stage are 32 B, a quarter line, so they travel in groups of four
+// stages (256 rows x 128 B), and its e8m0 scales (2 B per stage) in groups
+// of eight stages (16 B per row: one load per 64 rows; waves 4-7 load a copy
+// that nobody reads, so every wave issues the same loads).  LDS: two code
+// group slots (32 KB), two scale group slots (8 KB), two activation slots
+// (24 KB): 128 KB.
+// K order: in the 16-K step t of a stage, lane half h of both operands'
+// fragments holds the stage's K 32 h + 8 t .. +7, so a lane's codes for the
+// whole stage are one 16-byte LDS read, under one MX scale, per B column.
+// Each product is summed once, in another order than the bf16 ring's.
+// Schedule (group g = s / 4 in code slot g % 2, scale group h = s / 8 in
+// scale slot h % 2, A(s) in slot s % 2): the prologue loads S0 G0 A0 A1 S1
+// G1.  After the barrier of stage s (before its last step, whose fragments
+// are already in registers) it loads, in this order: A(s + 2); code group
+// s/4 + 2 on the last stage of a group; scale group s/8 + 2 on the last stage
+// of a scale group.  Past the end a scale group is clamped to the last one (a
+// harmless reload into a slot that is not read again), so the counts stay
+// fixed.  vmcnt counts in issue order: before the barrier of stage s the
+// wave waits for A(s + 1) and lets the groups issued after it fly.  Needs K
+// a multiple of 512.
+constexpr int kW4A = kTiledBM * 128;             // one stage's activations: 24 KB
+constexpr int kW4B = 256 * 128;                  // a code group: 32 KB
+constexpr int kW4S = 8 * 1024;                   // a scale group (and its spare copy)
+// code slots first, so that a fragment read's slot and row offsets fit the
+// LDS instructions' 16-bit immediate offset
+constexpr int kW4BOff = 0;
+constexpr int kW4SOff = kW4BOff + 2 * kW4B;
+constexpr int kW4AOff = kW4SOff + 2 * kW4S;
+constexpr int kW4Lds = kW4AOff + 2 * kW4A;       // 128 KiB
+
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = kTiledBM, BR = 256, NOUT = GATED ? 128 : 256, NW = 8, WAVES_N = 4;
+  constexpr int WM = BM / 2, WN = 64, FM = WM / 32, FN = 2, ROWB = 128;
+  constexpr int LA = BM / 64, LB = 4, LS = 1;
+  static_assert(kW4Lds <= kR64Lds && BM * (NOUT + 8) * 2 <= kW4Lds, "LDS");
+  extern __shared__ uint4 lds_u4[];
+  char* lds = reinterpret_cast<char*>(lds_u4);
+  const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const int tiles_n = (g.N + NOUT - 1) / NOUT;
+  // grid sized for the host's upper bound; XCD-aware order over the real count
+  const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
+  if (blockIdx.x >= nreal) return;
+  const uint32_t lt = xcd_swizzle(blockIdx.x, nreal);
+  const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
+  const Tile tl = g.tiles[tm];
+  const int row0 = tl.row_start, nrows = min(tl.nrows, BM), n0 = tn * NOUT;
+  const int K = g.K, nk = K / 64;
+  const int lr = lane >> 3, gchunk = ring64_gchunk(wid, lane);
+  // Operand addresses: wave-uniform bases (advanced stage by stage) plus
+  // fixed 32-bit lane offsets.  Lane l of wave w loads row 8 (w + 8 q) + l/8
+  // of its operand into chunk l%8 of the LDS row, from global chunk
+  // (l%8) ^ ((row/2) mod 8); weight loads q < 2 take rows 0..127 (gated: the
+  // gate rows), q >= 2 rows 128..255 (gated: the up rows).  Scale loads: lane
+  // l of wave w takes the 16 bytes of weight row 64 (w mod 4) + l.
+  uint32_t oa[LA], ob[LB], os;
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    int src = row0 + min((wid + NW * i) * 8 + lr, nrows - 1);
+    if (g.a_rows) src = g.a_rows[src] / g.a_row_div;
+    oa[i] = uint32_t(src) * uint32_t(g.lda * 2) + uint32_t(gchunk * 16);
+  }
+  // weight row r of the tile (gated: 128 gate rows, then 128 up rows): its
+  // row in the expert's [N, K] matrix
+  auto w_row = [&](int r) __attribute__((always_inline)) -> uint32_t {
+    return uint32_t(min(n0 + (GATED && r >= BR / 2 ? r - BR / 2 : r), g.N - 1));
+  };
+#pragma unroll
+  for (int i = 0; i < LB; ++i) ob[i] = w_row((wid + NW * i) * 8 + lr) * uint32_t(K / 2) + uint32_t(gchunk * 16);
+  os = w_row(64 * (wid & 3) + lane) * uint32_t(K / 32);
+  const int64_t wexp = int64_t(tl.expert) * g.N;
+  const char* abase = reinterpret_cast<const char*>(g.A);
+  const uint8_t* gbase = reinterpret_cast<const uint8_t*>(g.B) + wexp * (K / 2);
+  const uint8_t* ubase = GATED ? reinterpret_cast<const uint8_t*>(g.B3) + wexp * (K / 2) : gbase;
+  const uint8_t* sbase = (GATED && (wid & 3) >= 2 ? g.B3s : g.Bs) + wexp * (K / 32);
+  const int nsg = nk / 8;
+  auto rfl = [](uint32_t v) __attribute__((always_inline)) -> uint32_t {
+    return uint32_t(__builtin_amdgcn_readfirstlane(int(v)));
+  };
+  auto issue_a = [&](int slot, int q) __attribute__((always_inline)) {
+    g2lds16_so(abase, oa[q], rfl(lds0 + kW4AOff + slot * kW4A + (wid + NW * q) * 1024));
+  };
+  auto next_a = [&]() __attribute__((always_inline)) { abase += 128; };
+  auto issue_g = [&](int slot, int q) __attribute__((always_inline)) {
+    g2lds16_so(q < LB / 2 ? gbase : ubase, ob[q], rfl(lds0 + kW4BOff + slot * kW4B + (wid + NW * q) * 1024));
+  };
+  auto next_g = [&]() __attribute__((always_inline)) {  // four stages of packed codes
+    gbase += 128;
+    ubase += 128;
+  };
+  int sg_next = 0;  // the next scale group to load
+  auto issue_s = [&](int slot) __attribute__((always_inline)) {
+    g2lds16_so(sbase + min(sg_next, nsg - 1) * 16, os, rfl(lds0 + kW4SOff + slot * kW4S + wid * 1024));
+    ++sg_next;
+  };
+  auto brow = [&](int j) __attribute__((always_inline)) -> int {
+    if constexpr (GATED) return j == 0 ? wn * 32 : BR / 2 + wn * 32;
+    else return wn * WN + j * 32;
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const int fr = lane & 31, fsw = (fr >> 1) & 7, fh = lane >> 5;  // fragment row, its swizzle, K half
+  auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
+    constexpr int FA = decltype(fa_c)::value, FAR = FA > 0 ? FA : 1;
+    bf16x8 af[2][FAR];  // activation fragments, by step parity
+    uint4 bq[FN];       // a stage's weight codes (the next stage's are read
+    uint32_t bs[FN];    // after the last step's conversion) and scale codes
+    auto rd_a = [&](int aslot, int t, int i, int buf) __attribute__((always_inline)) {
+      const int r = wm * WM + i * 32 + fr;
+      af[buf][i] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + kW4AOff + aslot * kW4A + r * ROWB +
+                                                             (((4 * fh + t) ^ fsw) << 4)));
+    };
+    // stage s's codes and scales, R = s mod 8, in code slot cs / scale slot ss
+    auto rd_b = [&](int cs, int ss, int R, int j) __attribute__((always_inline)) {
+      const int r = brow(j) + fr;
+      bq[j] = *reinterpret_cast<const uint4*>(lds + kW4BOff + cs * kW4B + r * ROWB +
+                                                   (((2 * (R & 3) + fh) ^ fsw) << 4));
+      bs[j] = uint32_t(*reinterpret_cast<const uint8_t*>(lds + kW4SOff + ss * kW4S + r * 16 + 2 * R + fh));
+    };
+    // the 16-K step t's MFMAs on the stage's codes and activation set t & 1,
+    // with the side items 0 .. nside-1 spread over them in order (MFMA m is
+    // followed by items c m .. c m + c - 1, c = ceil(nside / NM); all at once
+    // if NM = 0).  The order matters: the vmcnt waits count on each wave's
+    // loads leaving in the order issued.
+    auto mm = [&](int t, int nside, auto side) __attribute__((always_inline)) {
+      constexpr int NM = FA * FN;
+      const int c = NM > 0 ? (nside + NM - 1) / NM : 0;
+      bf16x8 bf[FN];
+      if constexpr (FA > 0)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const uint4 q = bq[j];
+          const uint32_t w = t == 0 ? q.x : t == 1 ? q.y : t == 2 ? q.z : q.w;
+          bf[j] = fp4x8_to_bf16(w, e8m0_multiplier(bs[j]));
+        }
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FA; ++i) {
+          acc[i][j] = mfma_32x32x16(af[t & 1][i], bf[j], acc[i][j]);
+          const int m = j * FA + i;
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            if (k >= m * c && k < m * c + c && k < nside) side(k);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      if constexpr (NM == 0) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (k < nside) side(k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int ss0 = 0;  // stage s's scale slot
+    // stage s, R = s mod 8 (its A slot is R mod 2), LAST: in the last eight
+    // stages.  W: loads allowed in flight at the barrier (-1: the last stage,
+    // no barrier): those issued after A(s + 1), at stage s - 1
+    auto stage = [&](auto r_c, auto last_c) __attribute__((always_inline)) {
+      constexpr int R = decltype(r_c)::value;
+      constexpr bool LAST = decltype(last_c)::value;
+      constexpr bool IA = !LAST || R < 6, IG = !LAST && (R == 3 || R == 7), IS = !LAST && R == 7;
+      constexpr int W = (LAST && R == 7) ? -1 : R == 0 ? LB + LS : (R == 4 && !LAST) ? LB : 0;
+      constexpr int AS = R & 1, ASN = AS ^ 1;                                // A slots of s and s+1
+      constexpr int CS = R >= 4 ? 1 : 0, CSN = ((R + 1) & 7) >= 4 ? 1 : 0;  // code slots of s and s+1
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        mm(t, FA, [&](int i) __attribute__((always_inline)) { rd_a(AS, t + 1, i, (t + 1) & 1); });
+      if constexpr (W >= 0) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's reads of stage s are done
+        wait_vmcnt<W>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");       // no LDS read moves above the barrier
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int ss1 = R == 7 ? ss0 ^ 1 : ss0;
+      constexpr int NA = IA ? LA : 0, NG = IG ? LB : 0, NS = IS ? LS : 0;
+      constexpr int NRB = (W >= 0 && FA > 0) ? FN : 0, NRA = W >= 0 ? FA : 0;
+      mm(3, NA + NG + NS + NRB + NRA, [&](int k) __attribute__((always_inline)) {
+        if (k < NA) issue_a(AS, k);                        // A(s+2) into A(s)'s slot
+        else if (k < NA + NG) issue_g(CS, k - NA);         // code group s/4 + 2 into group s/4's slot
+        else if (k < NA + NG + NS) issue_s(ss0);           // scale group s/8 + 2 into s/8's slot
+        else if (k < NA + NG + NS + NRB) rd_b(CSN, ss1, (R + 1) & 7, k - NA - NG - NS);
+        else rd_a(ASN, 0, k - NA - NG - NS - NRB, 0);      // stage s+1's first fragments
+      });
+      if constexpr (NA > 0) next_a();
+      if constexpr (NG > 0) next_g();
+      ss0 = ss1;
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    // prologue: S0 G0 A0 A1 S1 G1
+    issue_s(0);
+#pragma unroll
+    for (int q = 0; q < LB; ++q) issue_g(0, q);
+    next_g();
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+#pragma unroll
+      for (int q = 0; q < LA; ++q) issue_a(e, q);
+      next_a();
+    }
+    issue_s(1);
+#pragma unroll
+    for (int q = 0; q < LB; ++q) issue_g(1, q);
+    next_g();
+    wait_vmcnt<LA + LS + LB>();  // S0, G0 and A0 have landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if constexpr (FA > 0)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) rd_b(0, 0, 0, j);
+#pragma unroll
+    for (int i = 0; i < FA; ++i) rd_a(0, 0, i, 0);
+    using std::integral_constant;
+    for (int s = 0; s + 8 < nk; s += 8) {
+      stage(integral_constant<int, 0>{}, F{});
+      stage(integral_constant<int, 1>{}, F{});
+      stage(integral_constant<int, 2>{}, F{});
+      stage(integral_constant<int, 3>{}, F{});
+      stage(integral_constant<int, 4>{}, F{});
+      stage(integral_constant<int, 5>{}, F{});
+      stage(integral_constant<int, 6>{}, F{});
+      stage(integral_constant<int, 7>{}, F{});
+    }
+    stage(integral_constant<int, 0>{}, T{});
+    stage(integral_constant<int, 1>{}, T{});
+    stage(integral_constant<int, 2>{}, T{});
+    stage(integral_constant<int, 3>{}, T{});
+    stage(integral_constant<int, 4>{}, T{});
+    stage(integral_constant<int, 5>{}, T{});
+    stage(integral_constant<int, 6>{}, T{});
+    stage(integral_constant<int, 7>{}, T{});
+  };
+  const int fa = max(0, min(FM, (nrows - wm * WM + 31) / 32));
+  switch (fa) {
+    case 0: mainloop(std::integral_constant<int, 0>{}); break;
+    case 1: mainloop(std::integral_constant<int, 1>{}); break;
+    case 2: mainloop(std::integral_constant<int, 2>{}); break;
+    default: mainloop(std::integral_constant<int, FM>{}); break;
+  }
+  __syncthreads();
+  ring64_store<GATED, BM, GATED>(lds, acc, fa, wm, wn, lane, tid, g.C, g.ldc, row0, nrows, n0, g.N);
+#endif
+}
+
 // ring64_dense_kernel takes bf16 outputs and segments whose K are multiples
 // of 64, at least 3 stages in all.
 bool ring64_fits(const DenseGemm& d) {
@@ -1394,6 +1673,17 @@ hipError_t run_ring64_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0
   if (nblk <= 0) return hipSuccess;
   if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
   return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512u}, kR64Lds, s, g, t0, t1);
+}
+
+template <bool GATED>
+hipError_t run_w4ring_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+  constexpr int NOUT = GATED ? 128 : 256;
+  auto kern = w4ring_grouped_kernel<GATED>;
+  if (hipError_t e = allow_dynamic_lds((const void*)kern, kW4Lds); e != hipSuccess) return e;
+  const int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
+  if (nblk <= 0) return hipSuccess;
+  if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
+  return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512u}, kW4Lds, s, g, t0, t1);
 }
 
 // The ring kernel takes bf16 outputs and segments whose K are multiples of
@@ -1461,6 +1751,11 @@ hipError_t launch_grouped_tiled(const GroupedGemm& g, hipStream_t s, hipEvent_t 
   if (g.w4) {
     // (the bf16 fallback below has no MXFP4 form)
     if (g.packed || g.K % 128 || g.K < 256 || !g.Bs || (g.gated && !g.B3s)) return hipErrorInvalidValue;
+    // K a multiple of 512 and 32-bit offsets into A and an expert's codes:
+    // the direct-to-LDS ring form
+    constexpr int64_t kOff = int64_t(1) << 31;
+    if (g.K % 512 == 0 && g.a_rows_n > 0 && g.a_rows_n * g.lda * 2 < kOff && int64_t(g.N) * g.K / 2 < kOff)
+      return g.gated ? run_w4ring_grouped<true>(g, s, t0, t1) : run_w4ring_grouped<false>(g, s, t0, t1);
     return g.gated ? run_grouped<true, false, true>(g, s, t0, t1) : run_grouped<false, false, true>(g, s, t0, t1);
   }
   if (g.packed) {

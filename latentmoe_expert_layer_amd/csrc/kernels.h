@@ -131,6 +131,9 @@ struct GroupedGemm {
   bool w4;
   const uint8_t* Bs;
   const uint8_t* B3s;
+  // rows of A (0: unknown); the w4a16 ring form addresses A by 32-bit
+  // offsets and is used only when A's rows end below 2^31 bytes
+  int64_t a_rows_n = 0;
 };
 hipError_t launch_grouped_skinny(const GroupedGemm& g, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Output-stationary decode (TokenSpeed Day-0 post, "Gluon kernels on AMD GPUs >

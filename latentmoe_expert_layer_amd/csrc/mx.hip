@@ -516,11 +516,6 @@ constexpr int kMxrBOff = 3 * kMxrA;             // weight pair slots
 constexpr int kMxrSOff = kMxrBOff + 2 * kMxrB;  // scale group slots
 constexpr int kMxrLds = kMxrSOff + 2 * kMxrS;   // 152 KiB
 
-// direct-to-LDS loads from a wave-uniform base plus a 32-bit lane offset
-__device__ __forceinline__ void g2lds16_so(const void* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(off), "s"(base) : "memory", "m0");
-}
-
 // One tile.  Operand addresses are 32-bit offsets from wave-uniform bases:
 // the activation codes and scales from A and As (which the host checks to be
 // below 2^31 bytes), the weights from the tile's expert matrices.

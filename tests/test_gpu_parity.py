@@ -284,6 +284,15 @@ W4A16_LAYERS = [
     ("w4_tiled", dict(T=1000, d=128, l=256, E=8, k=2, S=1, I=256, Is=64, mxfp4=True, w4a16=True)),
     # tiled, FC1 over 3 and FC2 over 2 column tiles, ragged tile tails
     ("w4_tiled_wide", dict(T=701, d=128, l=512, E=6, k=2, S=0, I=384, Is=0, mxfp4=True, w4a16=True)),
+    # K a multiple of 512: the direct-to-LDS ring form.  l = I = 512: eight
+    # 64-K stages (the last-eight-stage tail alone, one scale group)
+    ("w4_ring_k512", dict(T=1000, d=128, l=512, E=8, k=2, S=1, I=512, Is=64, mxfp4=True, w4a16=True)),
+    # FC1 K = 2048 (three full 8-stage blocks + the tail, four scale groups),
+    # FC2 K = 1024 (one block + the tail; the scale group past the end clamped)
+    ("w4_ring_k2048", dict(T=600, d=128, l=2048, E=5, k=2, S=0, I=1024, Is=0, mxfp4=True, w4a16=True)),
+    # FC1 K = 1536 (three scale groups, clamped in the second block), and ~35
+    # rows per expert: the second row of waves has no rows in most tiles
+    ("w4_ring_k1536_sparse", dict(T=700, d=128, l=1536, E=40, k=2, S=1, I=512, Is=64, mxfp4=True, w4a16=True)),
 ]
 
 
