@@ -235,8 +235,9 @@ def grouped_kernel(cfg, dom, fused_mlp, packed=False):
     """Which kernel runs the grouped GEMM ``dom`` (the library's own choice:
     MXFP4 w4a8 -> block-scaled kernel (its direct-to-LDS ring form when K is
     a multiple of 512); MXFP4 w4a16 -> its weight-streaming
-    kernels at <= 32 rows per expert on average, else the register-staged
-    grouped kernel in its MXFP4 form; bf16 at <= 32 rows per expert on average
+    kernels at <= 32 rows per expert on average, else the direct-to-LDS ring
+    with the weights upcast in registers (K a multiple of 512) or the
+    register-staged grouped kernel in its MXFP4 form; bf16 at <= 32 rows per expert on average
     -> weight-streaming kernel; otherwise, tile-packed weights -> the
     register-staged grouped kernel in its packed form, row-major weights -> the
     64-wide direct-to-LDS ring when K is a multiple of 64 and at least 192,
@@ -248,6 +249,8 @@ def grouped_kernel(cfg, dom, fused_mlp, packed=False):
     if cfg.mxfp4 and cfg.w4a16:
         if R <= 32 * cfg.E:
             return "skinny_w4a16_kernel", "skinny.hip"
+        if K % 512 == 0:
+            return "w4ring_grouped_kernel", "gemm.hip"
         return "grouped_tiled_kernel (MXFP4 w4a16)", "gemm.hip"
     if cfg.mxfp4:
         if K % 512 == 0:
