@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import check_layer, check_routing, gpu_route, run_gpu_layer
+from tests.gpu_helpers import check_layer, check_routing, gpu_route, run_gpu_layer, wfmt_of
 from tests.parity import assert_intermediate, assert_parity, assert_w4a8, log, poison_, to_device, to_host
 
 pytestmark = pytest.mark.gpu
@@ -197,15 +197,29 @@ def test_rows_mode_small(R, E, l, I):
     check_layer(inp, inp["ids"], inp["weights"], y, views)
 
 
-def test_graph_replay_matches_eager():
+GRAPH_LAYERS = [
+    ("decode", None),
+    # beyond 512 tokens and 8192 routed rows: the 64-wide ring kernels (dense
+    # and grouped) and the three-launch permutation
+    ("graph_ring", dict(T=3000, d=256, l=512, E=24, k=4, S=1, I=512, Is=128)),
+    # the same with MXFP4 w4a16 experts: the ring form with the weights upcast in registers
+    ("graph_w4ring", dict(T=3000, d=256, l=512, E=24, k=4, S=1, I=512, Is=128, mxfp4=True, w4a16=True)),
+]
+
+
+@pytest.mark.parametrize("name,dims", GRAPH_LAYERS, ids=[n for n, _ in GRAPH_LAYERS])
+def test_graph_replay_matches_eager(name, dims):
     """route + forward captured in a HIP graph: every replay (with eager work
     and synchronisations in between) equals the eager result bit for bit."""
-    cfg = W.CONFIGS["decode"]
+    cfg = W.CONFIGS[name] if dims is None else W.custom(name, **dims)
+    log(f"graph replay {name}: {cfg}")
     inp = to_device(W.make_inputs(cfg))
     _, y_ref, _ = run_gpu_layer(inp)
     T, E, k = cfg.T, cfg.E, cfg.k
+    mx = cfg.mxfp4
+    wfmt = wfmt_of(cfg)
     rws = torch.empty(lm.route_workspace_size(T, E, k), dtype=torch.uint8, device="cuda")
-    fws = torch.empty(lm.forward_workspace_size(T, E, k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is),
+    fws = torch.empty(lm.forward_workspace_size(T, E, k, cfg.d, cfg.l, cfg.I, cfg.S, cfg.Is, wfmt),
                       dtype=torch.uint8, device="cuda")
     bufs = dict(ids=torch.empty(T, k, dtype=torch.int32, device="cuda"),
                 w=torch.empty(T, k, dtype=torch.float32, device="cuda"),
@@ -217,8 +231,10 @@ def test_graph_replay_matches_eager():
     ra = lm.RouteArgs(T=T, E=E, k=k, logits=P(inp["logits"]), topk_ids=P(bufs["ids"]), topk_w=P(bufs["w"]),
                       sorted_row=P(bufs["srow"]), row_pos=P(bufs["rpos"]), offsets=P(bufs["off"]),
                       workspace=P(rws), workspace_bytes=rws.numel())
-    fa = lm.ForwardArgs(d=cfg.d, l=cfg.l, I=cfg.I, S=cfg.S, Is=cfg.Is, wfmt=0, norm_eps=cfg.eps,
-                        x=P(inp["x"]), w_in=P(inp["w_in"]), w1=P(inp["w1"]), w3=P(inp["w3"]), w2=P(inp["w2"]),
+    wq = "q" if mx else ""
+    fa = lm.ForwardArgs(d=cfg.d, l=cfg.l, I=cfg.I, S=cfg.S, Is=cfg.Is, wfmt=wfmt, norm_eps=cfg.eps,
+                        x=P(inp["x"]), w_in=P(inp["w_in"]), w1=P(inp["w1" + wq]), w3=P(inp["w3" + wq]),
+                        w2=P(inp["w2" + wq]), s1=P(inp.get("s1")), s3=P(inp.get("s3")), s2=P(inp.get("s2")),
                         norm_w=P(inp["norm_w"]), w_out=P(inp["w_out"]), ws1=P(inp["ws1"]), ws3=P(inp["ws3"]),
                         ws2=P(inp["ws2"]), y=P(bufs["y"]), workspace=P(fws), workspace_bytes=fws.numel())
     g = torch.cuda.CUDAGraph()
@@ -310,13 +326,16 @@ def test_w4a16_layer_parity(name, dims, norm):
     check_layer(inp, ids, w, y, views, act_quant=False)
 
 
-@pytest.mark.parametrize("rows", [600, 3000], ids=["weight_streaming", "tiled"])
-def test_w4a16_rows_mode(rows):
+@pytest.mark.parametrize("rows,width", [(600, 256), (3000, 256), (3000, 512)],
+                         ids=["weight_streaming", "tiled", "ring"])
+def test_w4a16_rows_mode(rows, width):
     """w4a16 on one expert-parallel rank's received rows (k = 1, Zipf load):
     600 rows over 56 experts run the weight-streaming kernels, 3000 rows over
-    8 experts the tiled ones (the heaviest expert spans many tiles)."""
+    8 experts the tiled ones (the heaviest expert spans many tiles); at
+    latent = intermediate = 512 the tiled GEMMs take the direct-to-LDS ring
+    form, its activation rows gathered straight from the received rows."""
     E = 56 if rows == 600 else 8
-    cfg = W.custom("w4_rows", T=rows, d=0, l=256, E=E, k=1, S=0, I=256, Is=0, rows_mode=True, norm=False,
+    cfg = W.custom("w4_rows", T=rows, d=0, l=width, E=E, k=1, S=0, I=width, Is=0, rows_mode=True, norm=False,
                    zipf_s=1.1, seed=5, mxfp4=True, w4a16=True)
     log(f"w4a16 rows mode: {cfg}")
     inp_dev = W.make_inputs(cfg, device="cuda")
