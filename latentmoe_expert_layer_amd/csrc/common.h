@@ -83,6 +83,19 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t codes, float scale) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// A tile's rows split between its two rows of waves in whole 32-row
+// subtiles, the first row of waves taking the larger half (a 101-row tile:
+// 64 + 37 rows, not 96 + 5), so that a partial tile's time follows its row
+// count: wave row wm's first row (r0) and subtile count (fa, at most fm).
+struct WaveRows {
+  int r0, fa;
+};
+__device__ __forceinline__ WaveRows wave_rows(int wm, int nrows, int fm) {
+  const int ns = (nrows + 31) / 32, s0 = (ns + 1) / 2;
+  if (wm == 0) return WaveRows{0, min(fm, s0)};
+  return WaveRows{32 * s0, max(0, min(fm, ns - s0))};
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Direct-to-LDS load: lane l's 16 bytes from gptr land at LDS byte

@@ -1007,15 +1007,15 @@ __device__ __forceinline__ int ring64_gchunk(int wid, int lane) {
 }
 
 // Epilogue of a 64-wide-ring tile (BM rows x 256 B rows on 8 waves as 2 x 4,
-// wave tiles BM/2 x 64 in acc, the first fa of a wave's 32-row subtiles
-// holding rows of the tile); the LDS is free on entry.  Gated: SwiGLU of each
+// this wave's fa 32-row subtiles from tile row r0 in acc, as wave_rows
+// splits the tile); the LDS is free on entry.  Gated: SwiGLU of each
 // gate subtile with its up subtile.  Rows row0 .. row0+nrows-1 of C, columns
 // n0 .. (below N), are written; NT: with nontemporal stores.
 template <bool GATED, int BM, bool NT>
-__device__ __forceinline__ void ring64_store(char* lds, const f32x16 (&acc)[BM / 64][2], int fa, int wm, int wn,
+__device__ __forceinline__ void ring64_store(char* lds, const f32x16 (&acc)[BM / 64][2], int fa, int r0, int wn,
                                              int lane, int tid, uint16_t* C, int64_t ldc, int64_t row0, int nrows,
                                              int n0, int N) {
-  constexpr int NTH = 512, NOUT = GATED ? 128 : 256, WM = BM / 2, WN = 64, FM = WM / 32, FN = 2;
+  constexpr int NTH = 512, NOUT = GATED ? 128 : 256, WN = 64, FM = BM / 64, FN = 2;
   // epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores
   constexpr int CLD = NOUT + 8;
   static_assert(BM * CLD * 2 <= kR64Lds, "epilogue staging fits in the ring");
@@ -1028,7 +1028,7 @@ __device__ __forceinline__ void ring64_store(char* lds, const f32x16 (&acc)[BM /
       for (int j = 0; j < JO; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int row = r0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const int col = wn * WO + j * 32 + (lane & 31);
           float x = acc[i][j][v];
           if constexpr (GATED) x = silu_mul(x, acc[i][1][v]);
@@ -1069,6 +1069,7 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
   constexpr int LA = BM / 8 / NW, LB = BR / 8 / NW;  // 1 KB loads per wave and A / B half stage
   static_assert(BM % (8 * NW) == 0 && BM * ROWB <= ENT && FM >= 1 && FM <= 4, "tile rows");
   const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const WaveRows wr = wave_rows(wm, nrows, FM);  // this wave row's first tile row and subtiles
   const int fr = lane & 31, fsw = (fr >> 1) & 7, fh = lane >> 5;  // fragment row, its swizzle, K half
   auto brow = [&](int j) __attribute__((always_inline)) -> int {
     if constexpr (GATED) return j == 0 ? wn * 32 : BR / 2 + wn * 32;
@@ -1099,7 +1100,7 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
     // stage whose B is in entry eb and A in ea
     auto rd = [&](int eb, int ea, int t, int q, int buf) __attribute__((always_inline)) {
       const int off = fr * ROWB + (((2 * t + fh) ^ fsw) << 4);
-      if (q < FA) af[buf][q] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + ea * ENT + (wm * WM + q * 32) * ROWB + off));
+      if (q < FA) af[buf][q] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + ea * ENT + (wr.r0 + q * 32) * ROWB + off));
       else bfr[buf][q - FA] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + eb * ENT + brow(q - FA) * ROWB + off));
     };
     // a 16-K step's MFMAs on fragment set buf, with the side items 0 .. nside-1
@@ -1187,7 +1188,7 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
     step(I0{}, std::false_type{}, std::false_type{});  // s = nk-2
     step(Im{}, std::false_type{}, std::false_type{});  // s = nk-1
   };
-  const int fa = max(0, min(FM, (nrows - wm * WM + 31) / 32));
+  const int fa = wr.fa;
   switch (fa) {
     case 0: mainloop(std::integral_constant<int, 0>{}); break;
     case 1: mainloop(std::integral_constant<int, 1>{}); break;
@@ -1196,7 +1197,7 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
     default: mainloop(std::integral_constant<int, FM>{}); break;
   }
   __syncthreads();
-  ring64_store<GATED, BM, NT>(lds, acc, fa, wm, wn, lane, tid, C, ldc, row0, nrows, n0, N);
+  ring64_store<GATED, BM, NT>(lds, acc, fa, wr.r0, wn, lane, tid, C, ldc, row0, nrows, n0, N);
 }
 
 // Dense projections: 256 x 256 tiles over up to five K segments (the A and B
@@ -1418,6 +1419,7 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
   const Tile tl = g.tiles[tm];
   const int row0 = tl.row_start, nrows = min(tl.nrows, BM), n0 = tn * NOUT;
   const int K = g.K, nk = K / 64;
+  const WaveRows wr = wave_rows(wm, nrows, FM);  // this wave row's first tile row and subtiles
   const int lr = lane >> 3, gchunk = ring64_gchunk(wid, lane);
   // Operand addresses: wave-uniform bases (advanced stage by stage) plus
   // fixed 32-bit lane offsets.  Lane l of wave w loads row 8 (w + 8 q) + l/8
@@ -1485,7 +1487,7 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
     uint4 bq[FN];       // a stage's weight codes (the next stage's are read
     uint32_t bs[FN];    // after the last step's conversion) and scale codes
     auto rd_a = [&](int aslot, int t, int i, int buf) __attribute__((always_inline)) {
-      const int r = wm * WM + i * 32 + fr;
+      const int r = wr.r0 + i * 32 + fr;
       af[buf][i] = as_bf16x8(*reinterpret_cast<const uint4*>(lds + kW4AOff + aslot * kW4A + r * ROWB +
                                                              (((4 * fh + t) ^ fsw) << 4)));
     };
@@ -1610,7 +1612,7 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
     stage(integral_constant<int, 6>{}, T{});
     stage(integral_constant<int, 7>{}, T{});
   };
-  const int fa = max(0, min(FM, (nrows - wm * WM + 31) / 32));
+  const int fa = wr.fa;
   switch (fa) {
     case 0: mainloop(std::integral_constant<int, 0>{}); break;
     case 1: mainloop(std::integral_constant<int, 1>{}); break;
@@ -1618,7 +1620,7 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
     default: mainloop(std::integral_constant<int, FM>{}); break;
   }
   __syncthreads();
-  ring64_store<GATED, BM, GATED>(lds, acc, fa, wm, wn, lane, tid, g.C, g.ldc, row0, nrows, n0, g.N);
+  ring64_store<GATED, BM, GATED>(lds, acc, fa, wr.r0, wn, lane, tid, g.C, g.ldc, row0, nrows, n0, g.N);
 #endif
 }
 

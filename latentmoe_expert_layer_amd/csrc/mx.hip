@@ -131,17 +131,17 @@ constexpr int mx_lds_bytes() {
   return 2 * stage > epi ? 2 * stage : epi;
 }
 
-// Epilogue of a tile of BM rows whose accumulators are acc (wave tiles
-// BM/2 x 64 of 32x32 fragments, fa of them holding rows): gated, SwiGLU of
+// Epilogue of a tile of BM rows whose accumulators are acc (this wave's fa
+// 32x32 fragments of rows from tile row r0, x 64 columns): gated, SwiGLU of
 // subtile 0 with its up subtile 1; the bf16 tile is staged in the LDS (free
 // on entry), then written as MXFP8 codes and scales (Cq set) or as bf16, in
 // 16-byte row-contiguous stores.
 template <bool GATED, int BM, int FM, int LDSB>
-__device__ __forceinline__ void mx_epilogue(const MxArgs& g, const f32x16 (&acc)[FM][2], int fa, uint8_t* lds,
+__device__ __forceinline__ void mx_epilogue(const MxArgs& g, const f32x16 (&acc)[FM][2], int fa, int r0, uint8_t* lds,
                                             int row0, int nrows, int n0) {
-  constexpr int NTH = 512, NOUT = GATED ? 128 : 256, WAVES_N = 4, WM = BM / 2, WN = 64, FN = 2;
+  constexpr int NTH = 512, NOUT = GATED ? 128 : 256, WAVES_N = 4, WN = 64, FN = 2;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, rl = lane & 31;
-  const int wm = wid / WAVES_N, wn = wid % WAVES_N;
+  const int wn = wid % WAVES_N;
   constexpr int CLD = NOUT + 8;
   static_assert(BM * CLD * 2 <= LDSB, "epilogue staging fits");
   bf16_t* Cs = reinterpret_cast<bf16_t*>(lds);
@@ -153,7 +153,7 @@ __device__ __forceinline__ void mx_epilogue(const MxArgs& g, const f32x16 (&acc)
       for (int j = 0; j < JO; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int row = r0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const int col = wn * WO + j * 32 + rl;
           float x = acc[i][j][v];
           if constexpr (GATED) x = silu_mul(x, acc[i][1][v]);
@@ -436,7 +436,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& g, uint32_t lt, uint8_t* l
     default: mainloop(std::integral_constant<int, FM>{}); break;
   }
 
-  mx_epilogue<GATED, BM, FM, mx_lds_bytes<GATED, BM>()>(g, acc, fa, lds, row0, nrows, n0);
+  mx_epilogue<GATED, BM, FM, mx_lds_bytes<GATED, BM>()>(g, acc, fa, wm * WM, lds, row0, nrows, n0);
 }
 
 // The grid covers an upper bound on the tile count: blocks past the
@@ -538,6 +538,7 @@ __device__ __forceinline__ void mx_ring_tile(const MxArgs& g, uint32_t lt, uint8
   const int expert = __builtin_amdgcn_readfirstlane(tl.expert);
   const int n0 = tn * NOUT;
   const int K = g.K, KB = K / 32, nk = K / kMxBK;
+  const WaveRows wr = wave_rows(wm, nrows, FM);  // this wave row's first tile row and subtiles
 
   // tile row r's activation row (rows past the tile repeat its last one)
   auto a_src = [&](int r) __attribute__((always_inline)) -> uint32_t {
@@ -625,7 +626,7 @@ __device__ __forceinline__ void mx_ring_tile(const MxArgs& g, uint32_t lt, uint8
     // codes in slot as, its pair in slot bs, its scales in group slot ss.
     auto rd_a = [&](int as, int ss, int R, int t, int i) __attribute__((always_inline)) {
       const uint8_t* E = lds + as * kMxrA;
-      const int r = wm * WM + i * 32 + fr;
+      const int r = wr.r0 + i * 32 + fr;
       const uint4 lo = *reinterpret_cast<const uint4*>(E + r * ROWB + (((4 * t + fh) ^ fsw) << 4));
       const uint4 hi = *reinterpret_cast<const uint4*>(E + r * ROWB + (((4 * t + 2 + fh) ^ fsw) << 4));
       af[i] = i32x8v{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
@@ -752,7 +753,7 @@ __device__ __forceinline__ void mx_ring_tile(const MxArgs& g, uint32_t lt, uint8
     step(I2{}, W0{}, F{}, F{}, F{});
     step(I3{}, Wm{}, F{}, F{}, F{});
   };
-  const int fa = max(0, min(FM, (nrows - wm * WM + 31) / 32));
+  const int fa = wr.fa;
   switch (fa) {
     case 0: mainloop(std::integral_constant<int, 0>{}); break;
     case 1: mainloop(std::integral_constant<int, 1>{}); break;
@@ -760,7 +761,7 @@ __device__ __forceinline__ void mx_ring_tile(const MxArgs& g, uint32_t lt, uint8
     default: mainloop(std::integral_constant<int, FM>{}); break;
   }
   __syncthreads();
-  mx_epilogue<GATED, BM, FM, kMxrLds>(g, acc, fa, lds, row0, nrows, n0);
+  mx_epilogue<GATED, BM, FM, kMxrLds>(g, acc, fa, wr.r0, lds, row0, nrows, n0);
 }
 
 // The grid covers an upper bound on the tile count; blocks past the
