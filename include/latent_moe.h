@@ -69,9 +69,11 @@ enum { LMOE_OK = 0, LMOE_EINVAL = 1, LMOE_EUNSUPPORTED = 2, LMOE_EHIP = 3 };
  *                        "TensorRT-LLM Stable LatentMoE" and "Gluon kernels on
  *                        AMD GPUs > Stable LatentMoE").  Decode-shaped batches
  *                        (T*k <= 32*E) run weight-streaming kernels; larger ones
- *                        the tiled expert GEMMs, which upcast a stage's weights
- *                        on their way into LDS and need l, I >= 256 (else
- *                        LMOE_EUNSUPPORTED, nothing enqueued). */
+ *                        the tiled expert GEMMs, which upcast the weights to
+ *                        bf16 (on their way into LDS, or from LDS into the
+ *                        MFMA operands when K is a multiple of 512) and need
+ *                        l, I >= 256 (else LMOE_EUNSUPPORTED, nothing
+ *                        enqueued). */
 enum { LMOE_WFMT_BF16 = 0, LMOE_WFMT_MXFP4 = 1, LMOE_WFMT_MXFP4_W4A16 = 2 };
 /* Storage of bf16 routed-expert weights (lmoe_forward_args.wlayout):
  *  LMOE_WLAYOUT_ROWS   row-major [E, N, K] (the layout every shape below names).
