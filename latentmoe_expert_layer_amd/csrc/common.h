@@ -55,6 +55,15 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 // 16-byte global load (p 16-byte aligned).
 __device__ __forceinline__ uint4 ldg16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// The same with the nontemporal hint, for data that one pass reads once
+// (expert outputs in the combine, weights streamed at decode, logits): the
+// lines are not kept in the caches for reuse.
+__device__ __forceinline__ uint4 ldnt16(const void* p) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v r = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return uint4{r[0], r[1], r[2], r[3]};
+}
+
 // Workgroup id -> logical tile id such that consecutive logical ids share an
 // XCD (the hardware deals workgroups to the 8 XCDs round robin), which keeps
 // tiles that reuse the same operand rows in one L2.

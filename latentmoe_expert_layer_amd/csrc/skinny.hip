@@ -269,8 +269,10 @@ __global__ __launch_bounds__(256) void skinny_lds_kernel(GroupedGemm g) {
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          gv[c][j] = gp[j * rs + ks(kc + 128 * c)];
-          if constexpr (GATED) uv[c][j] = up[j * rs + ks(kc + 128 * c)];
+          // the weights are read once per step: nontemporal (FC1 42.1 -> 37.8
+          // us, FC2 22.1 -> 20.4 us at decode, traced alternately)
+          gv[c][j] = ldnt16(gp + j * rs + ks(kc + 128 * c));
+          if constexpr (GATED) uv[c][j] = ldnt16(up + j * rs + ks(kc + 128 * c));
         }
       __builtin_amdgcn_sched_barrier(0);
       if (kc == 0) {
