@@ -320,7 +320,8 @@ void latent_moe_free(latent_moe_plan* plan);
  * every later latent_moe_forward on this plan records events[0] before its
  * first kernel and events[i] after stage i: 1 down-projection, 2 shared
  * experts' gate/up (and, with MXFP4 experts, the MXFP8 quantisation of the
- * FC1 input), 3 expert FC1, 4 expert FC2, 5 combine (+ RMSNorm),
+ * FC1 input where the down-projection's kernel does not write it in its
+ * epilogue: rows mode and small T), 3 expert FC1, 4 expert FC2, 5 combine (+ RMSNorm),
  * 6 up-projection (stages a call does not run, or runs fused into the
  * previous stage's kernel, are recorded back to back).  events[2] and
  * events[3] are recorded by the FC1 launch itself (hipExtLaunchKernel) at

@@ -308,6 +308,28 @@ FwdCtx fwd_ctx(const latent_moe_plan* p, const lmoe_forward_args* a, hipStream_t
   return c;
 }
 
+// The latent down-projection z = x W_in^T as a dense GEMM over the forward
+// workspace (MXFP4 w4a8 at large T: with z's MXFP8 copy from the epilogue,
+// when the launch can write it).
+lmoe::DenseGemm down_proj_gemm(const FwdCtx& c) {
+  const lmoe_forward_args* a = c.a;
+  char* ws = static_cast<char*>(a->workspace);
+  lmoe::DenseGemm g{};
+  g.M = int(c.p->T);
+  g.N = int(a->l);
+  g.nseg = 1;
+  g.seg[0] = lmoe::GemmSeg{static_cast<const uint16_t*>(a->x), a->d, static_cast<const uint16_t*>(a->w_in), nullptr,
+                           a->d, int(a->d)};
+  g.gated = false;
+  g.C = reinterpret_cast<uint16_t*>(ws + c.L.z);
+  g.ldc = a->l;
+  if (c.mx && !c.small && lmoe::dense_gemm_quant_fits(g)) {
+    g.Cq = reinterpret_cast<uint8_t*>(ws + c.L.zq);
+    g.Cqs = reinterpret_cast<uint8_t*>(ws + c.L.zs);
+  }
+  return g;
+}
+
 // Stage 1 (and 2 at large T): the latent down-projection and the shared
 // experts' gate/up on x.  route (small T only): the router's top-k of these
 // logits runs in the same launch as the GEMMs.
@@ -334,13 +356,7 @@ int fwd_front(const FwdCtx& c, const lmoe_route_args* route = nullptr) {
   // 1. latent down-projection, and the shared experts' gate/up on x
   if (!rows) {
     lmoe::DenseGemm g[2] = {};
-    g[0].M = int(T);
-    g[0].N = int(l);
-    g[0].nseg = 1;
-    g[0].seg[0] = lmoe::GemmSeg{x, d, static_cast<const uint16_t*>(a->w_in), nullptr, d, int(d)};
-    g[0].gated = false;
-    g[0].C = z;
-    g[0].ldc = l;
+    g[0] = down_proj_gemm(c);
     g[1].M = int(T);
     g[1].N = int(S * Is);
     g[1].nseg = 1;
@@ -465,7 +481,9 @@ int fwd_back(const FwdCtx& c) {
     uint8_t* zs = reinterpret_cast<uint8_t*>(ws + L.zs);
     uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
     uint8_t* hsc = reinterpret_cast<uint8_t*>(ws + L.hsc);
-    if ((e = lmoe::launch_quant_mxfp8(rows ? x : z, T, int(l), zq, zs, s)) != hipSuccess)
+    // (z's copy is written by the down-projection where it can)
+    if ((rows || !down_proj_gemm(c).Cq) &&
+        (e = lmoe::launch_quant_mxfp8(rows ? x : z, T, int(l), zq, zs, s)) != hipSuccess)
       return hip_fail(e, "quantise expert inputs");
     lmoe::GroupedMx m1{};
     m1.N = int(I);

@@ -1014,7 +1014,7 @@ __device__ __forceinline__ int ring64_gchunk(int wid, int lane) {
 template <bool GATED, int BM, bool NT>
 __device__ __forceinline__ void ring64_store(char* lds, const f32x16 (&acc)[BM / 64][2], int fa, int r0, int wn,
                                              int lane, int tid, uint16_t* C, int64_t ldc, int64_t row0, int nrows,
-                                             int n0, int N) {
+                                             int n0, int N, uint8_t* Cq = nullptr, uint8_t* Cqs = nullptr) {
   constexpr int NTH = 512, NOUT = GATED ? 128 : 256, WN = 64, FM = BM / 64, FN = 2;
   // epilogue: stage the bf16 tile in LDS, then 16-byte row-contiguous stores
   constexpr int CLD = NOUT + 8;
@@ -1052,6 +1052,24 @@ __device__ __forceinline__ void ring64_store(char* lds, const f32x16 (&acc)[BM /
       }
     }
   }
+  if (!GATED && Cq) {
+    // the MXFP8 copy: one thread per (row, 32-column block) of the staged tile
+    constexpr int BPR = NOUT / 32;
+    for (int c = tid; c < BM * BPR; c += NTH) {
+      const int row = c / BPR, b = c % BPR, col = n0 + b * 32;
+      if (row < nrows && col < N) {
+        uint4 raw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = *reinterpret_cast<const uint4*>(&Cs[row * CLD + b * 32 + i * 8]);
+        uint4 q[2];
+        const int64_t r = row0 + row;
+        Cqs[r * (ldc / 32) + col / 32] = quant_block32(raw, q);
+        uint4* dst = reinterpret_cast<uint4*>(Cq + r * ldc + col);
+        dst[0] = q[0];
+        dst[1] = q[1];
+      }
+    }
+  }
 }
 
 // Main loop and epilogue of a 64-wide-ring tile.  pa / pb: this lane's
@@ -1062,7 +1080,8 @@ __device__ __forceinline__ void ring64_store(char* lds, const f32x16 (&acc)[BM /
 template <bool GATED, int BM, bool NT, class NextA, class NextB>
 __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, int lane, int tid, int nk, int nrows,
                                             const bf16_t* (&pa)[BM / 64], const bf16_t* (&pb)[4], NextA next_a,
-                                            NextB next_b, uint16_t* C, int64_t ldc, int64_t row0, int n0, int N) {
+                                            NextB next_b, uint16_t* C, int64_t ldc, int64_t row0, int n0, int N,
+                                            uint8_t* Cq = nullptr, uint8_t* Cqs = nullptr) {
   constexpr int NW = 8, WAVES_N = 4;
   constexpr int BR = 256, WM = BM / 2, WN = 64;
   constexpr int FM = WM / 32, FN = WN / 32, ROWB = kR64Row, ENT = kR64Ent;
@@ -1197,7 +1216,7 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
     default: mainloop(std::integral_constant<int, FM>{}); break;
   }
   __syncthreads();
-  ring64_store<GATED, BM, NT>(lds, acc, fa, wr.r0, wn, lane, tid, C, ldc, row0, nrows, n0, N);
+  ring64_store<GATED, BM, NT>(lds, acc, fa, wr.r0, wn, lane, tid, C, ldc, row0, nrows, n0, N, Cq, Cqs);
 }
 
 // Dense projections: 256 x 256 tiles over up to five K segments (the A and B
@@ -1297,7 +1316,7 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g, int n
       }
     };
     ring64_tile<GATED, BM, false>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0, n0,
-                                  g.N);
+                                  g.N, g.Cq, g.Cqs);
   };
   if (half >= 0) tile(std::integral_constant<int, 128>{});
   else tile(std::integral_constant<int, 256>{});
@@ -1636,6 +1655,10 @@ bool ring64_fits(const DenseGemm& d) {
   return nk >= 3;
 }
 
+bool dense_gemm_quant_fits_impl(const DenseGemm& d) {
+  return ring64_fits(d) && !d.gated && d.N % 32 == 0 && d.ldc % 32 == 0;
+}
+
 // compute units of the current device (cached per device)
 int device_cus() {
   static int cus[64] = {};
@@ -1714,7 +1737,10 @@ hipError_t run_ring(const DenseGemm& d, hipStream_t s) {
 
 }  // namespace
 
+bool dense_gemm_quant_fits(const DenseGemm& d) { return dense_gemm_quant_fits_impl(d); }
+
 hipError_t launch_dense_gemm(const DenseGemm& d, hipStream_t s) {
+  if ((d.Cq || d.Cqs) && !dense_gemm_quant_fits_impl(d)) return hipErrorInvalidValue;
   if (ring64_fits(d)) return d.gated ? run_ring64<true>(d, s) : run_ring64<false>(d, s);
   if (ring_fits(d)) return d.gated ? run_ring<true>(d, s) : run_ring<false>(d, s);
   TiledArgs a{};

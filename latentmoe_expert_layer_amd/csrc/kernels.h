@@ -76,8 +76,17 @@ struct DenseGemm {
   uint16_t* C;
   float* Cf;
   int64_t ldc;
+  // optional (dense_gemm_quant_fits): C's MXFP8 copy as well, codes [M, N]
+  // (row stride ldc) and e8m0 scales [M, N/32] (row stride ldc/32), each
+  // 32-column block quantised from the bf16 values written to C
+  uint8_t* Cq = nullptr;
+  uint8_t* Cqs = nullptr;
 };
 hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
+// Whether launch_dense_gemm writes the MXFP8 copy for this GEMM (a plain
+// GEMM on the 64-wide ring with N and ldc multiples of 32); otherwise the
+// caller quantises C itself.
+bool dense_gemm_quant_fits(const DenseGemm& g);
 // Few-row variant (M <= kSmallM): 16-row tiles, K split across the 4 waves of
 // a workgroup; up to two sub-GEMMs with the same M in one launch.
 constexpr int kSmallM = 512;

@@ -16,62 +16,6 @@ namespace lmoe {
 
 namespace {
 
-// Four e4m3fn codes (byte i = code of v[i]): the nearest code, ties to the
-// even one, saturating to +-448 (1.75 * 2^8, the largest finite e4m3fn
-// value).  gfx950's converter rounds to nearest even in the OCP e4m3fn format
-// but turns magnitudes that round past 448 into NaN, so inputs are clamped to
-// +-448 first.  For every finite input of magnitude below 2^9 (all that the
-// block quantiser below produces) this equals the code written out from the
-// format's definition (checked over every bf16 bit pattern on the device).
-__device__ __forceinline__ uint32_t e4m3x4(float v0, float v1, float v2, float v3) {
-  constexpr float kMax = 448.0f;
-  v0 = fminf(fmaxf(v0, -kMax), kMax);
-  v1 = fminf(fmaxf(v1, -kMax), kMax);
-  v2 = fminf(fmaxf(v2, -kMax), kMax);
-  v3 = fminf(fmaxf(v3, -kMax), kMax);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);  // bytes 0, 1
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);       // bytes 2, 3
-  return uint32_t(w);
-}
-
-// MXFP8 quantisation of one 32-element block (OCP MX: one shared e8m0 scale
-// per 32 elements): scale exponent = floor(log2 amax) - 8 (clamped to e8m0's
-// range; an all-zero block gets code 0), elements = e4m3(v / 2^exp).  A block
-// holding a NaN or an infinity (e4m3fn has no infinity) becomes a NaN block:
-// scale code 255 (e8m0's NaN) and every element code 0x7F (e4m3fn's NaN), so
-// NaN reaches the product.  raw holds the block's 32 bf16 values; codes
-// receives 32 e4m3 bytes.
-__device__ __forceinline__ uint8_t quant_block32(const uint4 (&raw)[4], uint4 (&codes)[2]) {
-  const bf16_t* h = reinterpret_cast<const bf16_t*>(raw);
-  // the largest magnitude as a bf16 bit pattern: magnitudes order like their
-  // patterns, infinity is 0x7F80 and every NaN lies above it
-  uint32_t amag = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amag = max(amag, uint32_t(h[i]) & 0x7fffu);
-  if (amag >= 0x7f80u) {
-    codes[0] = codes[1] = uint4{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
-    return uint8_t(255);
-  }
-  const float amax = __uint_as_float(amag << 16);
-  int sexp = -127;
-  if (amax > 0.0f) {
-    const uint32_t au = __float_as_uint(amax);
-    const int ebits = int((au >> 23) & 0xffu);
-    // floor(log2 amax); bf16 subnormals (ebits == 0) are below 2^-126
-    const int fl = ebits ? ebits - 127 : -127;
-    sexp = max(-127, min(127, fl - 8));
-  }
-  const float inv = __uint_as_float(uint32_t(127 - sexp) << 23);  // 2^-sexp, exact (|sexp| <= 126 here)
-  uint32_t out[8];
-#pragma unroll
-  for (int w = 0; w < 8; ++w)
-    out[w] = e4m3x4(bf16_to_f32(h[w * 4]) * inv, bf16_to_f32(h[w * 4 + 1]) * inv, bf16_to_f32(h[w * 4 + 2]) * inv,
-                    bf16_to_f32(h[w * 4 + 3]) * inv);
-  codes[0] = uint4{out[0], out[1], out[2], out[3]};
-  codes[1] = uint4{out[4], out[5], out[6], out[7]};
-  return uint8_t(sexp + 127);
-}
-
 // MXFP8 quantisation of bf16 rows [rows, K] -> e4m3 codes [rows, K] and e8m0
 // scales [rows, K/32], one thread per 32-element block.
 __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const bf16_t* __restrict__ src, int64_t nblocks,
