@@ -171,15 +171,25 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // it would order before every later LDS read (it cannot tell ring entries
 // apart); the kernels order them with vmcnt waits and barriers.  lds_base goes
 // to m0, so it must be wave-uniform.
+template <bool NT = false>
 __device__ __forceinline__ void g2lds16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr) : "memory", "m0");
 }
 
 // The same from a wave-uniform base address plus a 32-bit lane offset (the
 // base in scalar registers, so a kernel keeps one 32-bit register per lane
 // and load instead of a 64-bit address).
+template <bool NT = false>
 __device__ __forceinline__ void g2lds16_so(const void* base, uint32_t off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(off), "s"(base) : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds_base), "v"(off), "s"(base)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(off), "s"(base)
+                 : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N), leaving the other counters alone

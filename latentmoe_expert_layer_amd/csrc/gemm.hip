@@ -1076,8 +1076,10 @@ __device__ __forceinline__ void ring64_store(char* lds, const f32x16 (&acc)[BM /
 // global addresses of its A / B rows at stage 0 (LA = BM/64 and 4 rows);
 // next_a / next_b advance them by one stage (and may switch segments).  The
 // tile's rows row0 .. row0+nrows-1 of C, columns n0 .. of N, are written;
-// NT: with nontemporal stores.
-template <bool GATED, int BM, bool NT, class NextA, class NextB>
+// NT: with nontemporal stores.  B_ONCE: B is read by this tile alone (an
+// expert's only row tile), so its loads carry the nontemporal hint, which
+// leaves L2 to the A rows that every column tile re-reads.
+template <bool GATED, int BM, bool NT, bool B_ONCE, class NextA, class NextB>
 __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, int lane, int tid, int nk, int nrows,
                                             const bf16_t* (&pa)[BM / 64], const bf16_t* (&pb)[4], NextA next_a,
                                             NextB next_b, uint16_t* C, int64_t ldc, int64_t row0, int n0, int N,
@@ -1109,7 +1111,7 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
     g2lds16(pa[q], uint32_t(__builtin_amdgcn_readfirstlane(int(eb + (wid + NW * q) * 1024))));
   };
   auto issue_b = [&](uint32_t eb, int q) __attribute__((always_inline)) {
-    g2lds16(pb[q], uint32_t(__builtin_amdgcn_readfirstlane(int(eb + (wid + NW * q) * 1024))));
+    g2lds16<B_ONCE>(pb[q], uint32_t(__builtin_amdgcn_readfirstlane(int(eb + (wid + NW * q) * 1024))));
   };
 
   auto mainloop = [&](auto fa_c) __attribute__((always_inline)) {
@@ -1315,8 +1317,8 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g, int n
         }
       }
     };
-    ring64_tile<GATED, BM, false>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0, n0,
-                                  g.N, g.Cq, g.Cqs);
+    ring64_tile<GATED, BM, false, false>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0,
+                                         n0, g.N, g.Cq, g.Cqs);
   };
   if (half >= 0) tile(std::integral_constant<int, 128>{});
   else tile(std::integral_constant<int, 256>{});
@@ -1371,8 +1373,14 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
 #pragma unroll
     for (int i = 0; i < LB; ++i) pb[i] += BK;
   };
-  ring64_tile<GATED, BM, GATED>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0,
-                                n0, g.N);
+  // FC1 (gated) only: FC2 was a little slower with it.  (The hint is an
+  // instruction bit: one copy of the tile's code for each form.)
+  if (GATED && tl.solo)
+    ring64_tile<GATED, BM, GATED, true>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C, g.ldc,
+                                        row0, n0, g.N);
+  else
+    ring64_tile<GATED, BM, GATED, false>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C,
+                                         g.ldc, row0, n0, g.N);
 #endif
 }
 
@@ -1474,8 +1482,11 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
     g2lds16_so(abase, oa[q], rfl(lds0 + kW4AOff + slot * kW4A + (wid + NW * q) * 1024));
   };
   auto next_a = [&]() __attribute__((always_inline)) { abase += 128; };
+  const bool b_once = tl.solo != 0;  // the expert's only tile: its codes are read once (nontemporal)
   auto issue_g = [&](int slot, int q) __attribute__((always_inline)) {
-    g2lds16_so(q < LB / 2 ? gbase : ubase, ob[q], rfl(lds0 + kW4BOff + slot * kW4B + (wid + NW * q) * 1024));
+    const uint32_t lb = rfl(lds0 + kW4BOff + slot * kW4B + (wid + NW * q) * 1024);
+    if (b_once) g2lds16_so<true>(q < LB / 2 ? gbase : ubase, ob[q], lb);
+    else g2lds16_so(q < LB / 2 ? gbase : ubase, ob[q], lb);
   };
   auto next_g = [&]() __attribute__((always_inline)) {  // four stages of packed codes
     gbase += 128;

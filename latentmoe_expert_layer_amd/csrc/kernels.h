@@ -28,7 +28,7 @@ struct Tile {
   int32_t expert;
   int32_t row_start;
   int32_t nrows;
-  int32_t pad;
+  int32_t solo;  // 1: the expert's only tile, so the launch reads its weights once
 };
 
 // Row-tile granularities of the tile tables that routing builds.

@@ -227,8 +227,10 @@ __device__ __forceinline__ void permute_block(const int32_t* __restrict__ ids, i
       start += c[w];
     }
     const int32_t cnt = start - o;
-    for (int32_t r = 0; r < cnt; r += kSkinnyBM, ++ta) tiles_a[ta] = Tile{e, o + r, min(kSkinnyBM, cnt - r), 0};
-    for (int32_t r = 0; r < cnt; r += kTiledBM, ++tb) tiles_b[tb] = Tile{e, o + r, min(kTiledBM, cnt - r), 0};
+    for (int32_t r = 0; r < cnt; r += kSkinnyBM, ++ta)
+      tiles_a[ta] = Tile{e, o + r, min(kSkinnyBM, cnt - r), cnt <= kSkinnyBM};
+    for (int32_t r = 0; r < cnt; r += kTiledBM, ++tb)
+      tiles_b[tb] = Tile{e, o + r, min(kTiledBM, cnt - r), cnt <= kTiledBM};
     o = start;
   }
   if (tid == 0) {

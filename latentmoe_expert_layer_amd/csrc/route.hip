@@ -180,8 +180,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
         ta += na;
         tb += nb;
       } else {
-        for (int32_t r = 0; r < cnt; r += kSkinnyBM, ++ta) tiles_a[ta] = Tile{e, o + r, min(kSkinnyBM, cnt - r), 0};
-        for (int32_t r = 0; r < cnt; r += kTiledBM, ++tb) tiles_b[tb] = Tile{e, o + r, min(kTiledBM, cnt - r), 0};
+        for (int32_t r = 0; r < cnt; r += kSkinnyBM, ++ta)
+          tiles_a[ta] = Tile{e, o + r, min(kSkinnyBM, cnt - r), cnt <= kSkinnyBM};
+        for (int32_t r = 0; r < cnt; r += kTiledBM, ++tb)
+          tiles_b[tb] = Tile{e, o + r, min(kTiledBM, cnt - r), cnt <= kTiledBM};
       }
       o += cnt;
     }
@@ -197,9 +199,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
     const int e = s_heavy[h][0];
     const int32_t oe = s_heavy[h][1], cnt = s_heavy[h][2], ta0 = s_heavy[h][3], tb0 = s_heavy[h][4];
     for (int32_t j = tid; j * kSkinnyBM < cnt; j += kPermThreads)
-      tiles_a[ta0 + j] = Tile{e, oe + j * kSkinnyBM, min(kSkinnyBM, cnt - j * kSkinnyBM), 0};
+      tiles_a[ta0 + j] = Tile{e, oe + j * kSkinnyBM, min(kSkinnyBM, cnt - j * kSkinnyBM), cnt <= kSkinnyBM};
     for (int32_t j = tid; j * kTiledBM < cnt; j += kPermThreads)
-      tiles_b[tb0 + j] = Tile{e, oe + j * kTiledBM, min(kTiledBM, cnt - j * kTiledBM), 0};
+      tiles_b[tb0 + j] = Tile{e, oe + j * kTiledBM, min(kTiledBM, cnt - j * kTiledBM), cnt <= kTiledBM};
   }
 }
 
