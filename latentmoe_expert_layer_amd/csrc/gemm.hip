@@ -1343,8 +1343,27 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
   // grid sized for the host's upper bound; XCD-aware order over the real count
   const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
-  if (blockIdx.x >= nreal) return;
-  const uint32_t lt = xcd_swizzle(blockIdx.x, nreal);
+  // FC2 runs on a persistent grid (a multiple of 8 workgroups, one per CU):
+  // each XCD's workgroups walk that XCD's run of the XCD-aware order (the run
+  // xcd_swizzle gives it, then its one remainder tile) in passes of G tiles,
+  // slot j taking tile j of even passes and G-1-j of odd ones, so that a
+  // workgroup alternates between the ends of each pass (with the first and
+  // second row tiles of two-tile experts adjacent in the order, a fixed
+  // stride handed half the workgroups only the larger ones).  A tile's
+  // output stores drain while the next tile's first stages load.
+  constexpr bool PERSIST = !GATED;
+  const uint32_t xcd = blockIdx.x % 8u, slot = blockIdx.x / 8u, G = gridDim.x / 8u, per = nreal / 8u;
+  const uint32_t mine = per + (xcd < nreal % 8u ? 1u : 0u);  // tiles of this XCD's run
+  for (uint32_t pass = 0;; ++pass) {
+  uint32_t lt;
+  if constexpr (PERSIST) {
+    const uint32_t pos = pass * G + ((pass & 1u) ? G - 1u - slot : slot);
+    if (pos >= mine) break;
+    lt = pos < per ? xcd * per + pos : 8u * per + xcd;
+  } else {
+    if (blockIdx.x >= nreal) break;
+    lt = xcd_swizzle(blockIdx.x, nreal);
+  }
   const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
   const Tile tl = g.tiles[tm];
   const int row0 = tl.row_start, nrows = min(tl.nrows, BM), n0 = tn * NOUT;
@@ -1381,6 +1400,9 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
   else
     ring64_tile<GATED, BM, GATED, false>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C,
                                          g.ldc, row0, n0, g.N);
+  if constexpr (!PERSIST) break;
+  __syncthreads();  // the epilogue's LDS reads are done before the next tile's loads land
+  }
 #endif
 }
 
@@ -1705,9 +1727,12 @@ hipError_t run_ring64_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0
   constexpr int NOUT = GATED ? 128 : 256;
   auto kern = ring64_grouped_kernel<GATED>;
   if (hipError_t e = allow_dynamic_lds((const void*)kern, kR64Lds); e != hipSuccess) return e;
-  const int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
+  int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
   if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
+  // FC2: one workgroup per CU, a multiple of 8 (blockIdx mod 8 is the XCD
+  // the hardware deals a workgroup to)
+  if (!GATED) nblk = (device_cus() + 7) / 8 * 8;
   return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512u}, kR64Lds, s, g, t0, t1);
 }
 
