@@ -73,6 +73,23 @@ __device__ __forceinline__ uint32_t xcd_swizzle(uint32_t b, uint32_t nb) {
   return (b % 8u) * (nb / 8u) + b / 8u;
 }
 
+// Persistent grids over the same order: workgroup b (on XCD b mod 8, slot
+// b/8 of the G = grid/8 there; grid a multiple of 8) walks its XCD's run of
+// the order (the run xcd_swizzle gives that XCD, then its one remainder tile)
+// in passes of G tiles, slot j taking tile j of even passes and G-1-j of odd
+// ones, so a workgroup alternates between the ends of a pass.  (A fixed
+// stride hands each slot tiles at one offset in every period of the order:
+// with an expert's two row tiles adjacent in it, half the workgroups got
+// only the larger ones.)  Returns false once the pass is past the run.
+__device__ __forceinline__ bool mirrored_tile(uint32_t b, uint32_t grid, uint32_t nb, uint32_t pass, uint32_t& lt) {
+  const uint32_t xcd = b % 8u, slot = b / 8u, G = grid / 8u, per = nb / 8u;
+  const uint32_t mine = per + (xcd < nb % 8u ? 1u : 0u);
+  const uint32_t pos = pass * G + ((pass & 1u) ? G - 1u - slot : slot);
+  if (pos >= mine) return false;
+  lt = pos < per ? xcd * per + pos : 8u * per + xcd;
+  return true;
+}
+
 // e8m0 scale code -> the fp32 multiplier 2^(code-127) (code 0: 2^-127, a
 // denormal; 255: NaN), the operand the scaled conversion takes.
 __device__ __forceinline__ float e8m0_multiplier(uint32_t c) {

@@ -27,6 +27,19 @@
 
 namespace lmoe {
 
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 namespace {
 
 constexpr int kBK = 64;          // K per LDS stage
@@ -1343,23 +1356,14 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
   // grid sized for the host's upper bound; XCD-aware order over the real count
   const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
-  // FC2 runs on a persistent grid (a multiple of 8 workgroups, one per CU):
-  // each XCD's workgroups walk that XCD's run of the XCD-aware order (the run
-  // xcd_swizzle gives it, then its one remainder tile) in passes of G tiles,
-  // slot j taking tile j of even passes and G-1-j of odd ones, so that a
-  // workgroup alternates between the ends of each pass (with the first and
-  // second row tiles of two-tile experts adjacent in the order, a fixed
-  // stride handed half the workgroups only the larger ones).  A tile's
-  // output stores drain while the next tile's first stages load.
+  // FC2 runs on a persistent grid (one workgroup per CU, in mirrored_tile's
+  // order), so a tile's output stores drain while the next tile's first
+  // stages load.
   constexpr bool PERSIST = !GATED;
-  const uint32_t xcd = blockIdx.x % 8u, slot = blockIdx.x / 8u, G = gridDim.x / 8u, per = nreal / 8u;
-  const uint32_t mine = per + (xcd < nreal % 8u ? 1u : 0u);  // tiles of this XCD's run
   for (uint32_t pass = 0;; ++pass) {
   uint32_t lt;
   if constexpr (PERSIST) {
-    const uint32_t pos = pass * G + ((pass & 1u) ? G - 1u - slot : slot);
-    if (pos >= mine) break;
-    lt = pos < per ? xcd * per + pos : 8u * per + xcd;
+    if (!mirrored_tile(blockIdx.x, gridDim.x, nreal, pass, lt)) break;
   } else {
     if (blockIdx.x >= nreal) break;
     lt = xcd_swizzle(blockIdx.x, nreal);
@@ -1462,8 +1466,16 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
   // grid sized for the host's upper bound; XCD-aware order over the real count
   const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
-  if (blockIdx.x >= nreal) return;
-  const uint32_t lt = xcd_swizzle(blockIdx.x, nreal);
+  // FC2: a persistent grid in mirrored_tile's order (as ring64_grouped_kernel)
+  constexpr bool PERSIST = !GATED;
+  for (uint32_t pass = 0;; ++pass) {
+  uint32_t lt;
+  if constexpr (PERSIST) {
+    if (!mirrored_tile(blockIdx.x, gridDim.x, nreal, pass, lt)) break;
+  } else {
+    if (blockIdx.x >= nreal) break;
+    lt = xcd_swizzle(blockIdx.x, nreal);
+  }
   const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
   const Tile tl = g.tiles[tm];
   const int row0 = tl.row_start, nrows = min(tl.nrows, BM), n0 = tn * NOUT;
@@ -1673,6 +1685,9 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
   }
   __syncthreads();
   ring64_store<GATED, BM, GATED>(lds, acc, fa, wr.r0, wn, lane, tid, g.C, g.ldc, row0, nrows, n0, g.N);
+  if constexpr (!PERSIST) break;
+  __syncthreads();  // the epilogue's LDS reads are done before the next tile's loads land
+  }
 #endif
 }
 
@@ -1690,19 +1705,6 @@ bool ring64_fits(const DenseGemm& d) {
 
 bool dense_gemm_quant_fits_impl(const DenseGemm& d) {
   return ring64_fits(d) && !d.gated && d.N % 32 == 0 && d.ldc % 32 == 0;
-}
-
-// compute units of the current device (cached per device)
-int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
 }
 
 template <bool GATED>
@@ -1741,9 +1743,10 @@ hipError_t run_w4ring_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0
   constexpr int NOUT = GATED ? 128 : 256;
   auto kern = w4ring_grouped_kernel<GATED>;
   if (hipError_t e = allow_dynamic_lds((const void*)kern, kW4Lds); e != hipSuccess) return e;
-  const int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
+  int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
   if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
+  if (!GATED) nblk = (device_cus() + 7) / 8 * 8;  // FC2: the persistent grid
   return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512u}, kW4Lds, s, g, t0, t1);
 }
 

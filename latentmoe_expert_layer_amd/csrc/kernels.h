@@ -83,6 +83,8 @@ struct DenseGemm {
   uint8_t* Cqs = nullptr;
 };
 hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
+// compute units of the current device (cached per device; 256 if unknown)
+int device_cus();
 // Whether launch_dense_gemm writes the MXFP8 copy for this GEMM (a plain
 // GEMM on the 64-wide ring with N and ldc multiples of 32); otherwise the
 // caller quantises C itself.
