@@ -1356,18 +1356,10 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
   // grid sized for the host's upper bound; XCD-aware order over the real count
   const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
-  // FC2 runs on a persistent grid (one workgroup per CU, in mirrored_tile's
-  // order), so a tile's output stores drain while the next tile's first
-  // stages load.
-  constexpr bool PERSIST = !GATED;
-  for (uint32_t pass = 0;; ++pass) {
+  // a persistent grid (one workgroup per CU, in mirrored_tile's order), so a
+  // tile's output stores drain while the next tile's first stages load
   uint32_t lt;
-  if constexpr (PERSIST) {
-    if (!mirrored_tile(blockIdx.x, gridDim.x, nreal, pass, lt)) break;
-  } else {
-    if (blockIdx.x >= nreal) break;
-    lt = xcd_swizzle(blockIdx.x, nreal);
-  }
+  for (uint32_t pass = 0; mirrored_tile(blockIdx.x, gridDim.x, nreal, pass, lt); ++pass) {
   const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
   const Tile tl = g.tiles[tm];
   const int row0 = tl.row_start, nrows = min(tl.nrows, BM), n0 = tn * NOUT;
@@ -1404,7 +1396,6 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
   else
     ring64_tile<GATED, BM, GATED, false>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C,
                                          g.ldc, row0, n0, g.N);
-  if constexpr (!PERSIST) break;
   __syncthreads();  // the epilogue's LDS reads are done before the next tile's loads land
   }
 #endif
@@ -1466,16 +1457,9 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
   const int tiles_n = (g.N + NOUT - 1) / NOUT;
   // grid sized for the host's upper bound; XCD-aware order over the real count
   const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t(tiles_n);
-  // FC2: a persistent grid in mirrored_tile's order (as ring64_grouped_kernel)
-  constexpr bool PERSIST = !GATED;
-  for (uint32_t pass = 0;; ++pass) {
+  // a persistent grid in mirrored_tile's order (as ring64_grouped_kernel)
   uint32_t lt;
-  if constexpr (PERSIST) {
-    if (!mirrored_tile(blockIdx.x, gridDim.x, nreal, pass, lt)) break;
-  } else {
-    if (blockIdx.x >= nreal) break;
-    lt = xcd_swizzle(blockIdx.x, nreal);
-  }
+  for (uint32_t pass = 0; mirrored_tile(blockIdx.x, gridDim.x, nreal, pass, lt); ++pass) {
   const int tn = int(lt % uint32_t(tiles_n)), tm = int(lt / uint32_t(tiles_n));
   const Tile tl = g.tiles[tm];
   const int row0 = tl.row_start, nrows = min(tl.nrows, BM), n0 = tn * NOUT;
@@ -1685,7 +1669,6 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
   }
   __syncthreads();
   ring64_store<GATED, BM, GATED>(lds, acc, fa, wr.r0, wn, lane, tid, g.C, g.ldc, row0, nrows, n0, g.N);
-  if constexpr (!PERSIST) break;
   __syncthreads();  // the epilogue's LDS reads are done before the next tile's loads land
   }
 #endif
@@ -1732,9 +1715,10 @@ hipError_t run_ring64_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0
   int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
   if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
-  // FC2: one workgroup per CU, a multiple of 8 (blockIdx mod 8 is the XCD
-  // the hardware deals a workgroup to)
-  if (!GATED) nblk = (device_cus() + 7) / 8 * 8;
+  // one workgroup per CU, or fewer when the tiles are fewer; a multiple of 8
+  // either way (mirrored_tile: blockIdx mod 8 is the XCD the hardware deals
+  // a workgroup to, and every XCD holds grid/8 of them)
+  nblk = std::min<int64_t>((nblk + 7) / 8 * 8, (device_cus() + 7) / 8 * 8);
   return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512u}, kR64Lds, s, g, t0, t1);
 }
 
@@ -1746,7 +1730,7 @@ hipError_t run_w4ring_grouped(const GroupedGemm& g, hipStream_t s, hipEvent_t t0
   int64_t nblk = g.max_tiles * ((g.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
   if (nblk > int64_t(0x7fffffff)) return hipErrorInvalidValue;
-  if (!GATED) nblk = (device_cus() + 7) / 8 * 8;  // FC2: the persistent grid
+  nblk = std::min<int64_t>((nblk + 7) / 8 * 8, (device_cus() + 7) / 8 * 8);  // the persistent grid
   return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512u}, kW4Lds, s, g, t0, t1);
 }
 

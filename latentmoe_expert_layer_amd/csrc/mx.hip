@@ -708,10 +708,8 @@ __device__ __forceinline__ void mx_ring_tile(const MxArgs& g, uint32_t lt, uint8
   mx_epilogue<GATED, BM, FM, kMxrLds>(g, acc, fa, wr.r0, lds, row0, nrows, n0);
 }
 
-// FC1: the grid covers an upper bound on the tile count; blocks past the
-// device-side count exit.  FC2: a persistent grid (one workgroup per CU) in
-// mirrored_tile's order, so a tile's output stores drain while the next
-// tile's first stages load.
+// A persistent grid (one workgroup per CU) in mirrored_tile's order, so a
+// tile's output stores drain while the next tile's first stages load.
 template <bool GATED>
 __global__ __launch_bounds__(512, 1) void mx_ring_kernel(MxArgs g) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -720,15 +718,10 @@ __global__ __launch_bounds__(512, 1) void mx_ring_kernel(MxArgs g) {
   const uint32_t lds0 = uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
   constexpr int NOUT = GATED ? 128 : 256;
   const uint32_t nreal = uint32_t(*g.ntiles) * uint32_t((g.N + NOUT - 1) / NOUT);
-  if constexpr (GATED) {
-    if (blockIdx.x >= nreal) return;
-    mx_ring_tile<GATED>(g, xcd_swizzle(blockIdx.x, nreal), lds, lds0);
-  } else {
-    uint32_t lt;
-    for (uint32_t pass = 0; mirrored_tile(blockIdx.x, gridDim.x, nreal, pass, lt); ++pass) {
-      mx_ring_tile<GATED>(g, lt, lds, lds0);
-      __syncthreads();  // the epilogue's LDS reads are done before the next tile's loads land
-    }
+  uint32_t lt;
+  for (uint32_t pass = 0; mirrored_tile(blockIdx.x, gridDim.x, nreal, pass, lt); ++pass) {
+    mx_ring_tile<GATED>(g, lt, lds, lds0);
+    __syncthreads();  // the epilogue's LDS reads are done before the next tile's loads land
   }
 #endif
 }
@@ -740,7 +733,7 @@ hipError_t run_mx_ring(const MxArgs& a, int64_t max_tiles, hipStream_t s, hipEve
   if (hipError_t e = allow_dynamic_lds((const void*)kern, kMxrLds); e != hipSuccess) return e;
   int64_t nblk = max_tiles * ((a.N + NOUT - 1) / NOUT);
   if (nblk <= 0) return hipSuccess;
-  if (!GATED) nblk = (device_cus() + 7) / 8 * 8;  // FC2: the persistent grid
+  nblk = std::min<int64_t>((nblk + 7) / 8 * 8, (device_cus() + 7) / 8 * 8);  // the persistent grid
   return launch_kernel((const void*)kern, dim3{uint32_t(nblk)}, dim3{512}, size_t(kMxrLds), s, a, t0, t1);
 }
 
