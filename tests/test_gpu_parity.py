@@ -288,6 +288,30 @@ def test_mxfp4_layer_parity_small(name, dims):
     check_layer(inp, ids, w, y, views)
 
 
+# More tiles than the persistent grid of one workgroup per CU holds, on
+# experts of one and of two row tiles (173..238 rows; 17 of 80 experts fit one
+# tile): every grouped ring kernel takes two or three tiles per workgroup in
+# its mirrored passes, and FC1 runs both its solo-tile (nontemporal weights)
+# and shared-tile code.  143 row tiles x 4 column tiles for FC1 and for FC2
+# (l = 1024).
+MANY_TILE_LAYERS = [
+    ("many_tiles_bf16", dict(T=4096, d=128, l=1024, E=80, k=4, S=0, I=512, Is=0)),
+    ("many_tiles_w4a16", dict(T=4096, d=128, l=1024, E=80, k=4, S=0, I=512, Is=0, mxfp4=True, w4a16=True)),
+    ("many_tiles_w4a8", dict(T=4096, d=128, l=1024, E=80, k=4, S=0, I=512, Is=0, mxfp4=True)),
+]
+
+
+@pytest.mark.parametrize("name,dims", MANY_TILE_LAYERS, ids=[n for n, _ in MANY_TILE_LAYERS])
+def test_many_tiles_parity(name, dims):
+    """Every token, every intermediate, with several tiles per workgroup."""
+    cfg = W.custom(name, **dims)
+    log(f"many-tile layer {name}: {cfg}")
+    inp = W.make_inputs(cfg, norm_w="random")
+    r, y, views = run_gpu_layer(to_device(inp))
+    ids, w = check_routing(r, inp["logits"], cfg.k, cfg.E)
+    check_layer(inp, ids, w, y, views)
+
+
 W4A16_LAYERS = [
     ("decode_w4a16", None),
     # ragged T, experts without rows, l = 384 (K not a multiple of 256: one 128-wide chunk per batch)
