@@ -437,8 +437,8 @@ template <bool OS = false>
 __global__ __launch_bounds__(256) void skinny_w4a16_mlp_kernel(W4Mlp g) {
   constexpr int L = 256, IM = 256, ZS = L + 8, HS = IM + 8;  // padded LDS rows (bf16)
   static_assert(L == kW4MlpWidth && IM == kW4MlpWidth, "the chunk layout below is for 256 x 256");
-  __shared__ bf16_t Zs[16 * ZS];
-  __shared__ bf16_t Hs[16 * HS];
+  __shared__ __attribute__((aligned(16))) bf16_t Zs[16 * ZS];
+  __shared__ __attribute__((aligned(16))) bf16_t Hs[16 * HS];
   __shared__ int32_t os_lst[OS ? 16 : 1];
   __shared__ int32_t os_red[OS ? 4 : 1];
   const int lane = threadIdx.x & 63, gq = lane >> 4, n16 = lane & 15;
@@ -501,16 +501,25 @@ __global__ __launch_bounds__(256) void skinny_w4a16_mlp_kernel(W4Mlp g) {
             Hs[(4 * gq + r) * HS + wid * (IM / 4) + 32 * (c >> 1) + 16 * j + n16] =
                 f32_to_bf16(silu_mul(acc[2 * j][r], acc[2 * j + 1][r]));
       } else {
+        // Y through LDS (the z rows' buffer, free since FC1 ended), so that a
+        // wave writes each of its rows' 128 bytes as one 16-byte-per-lane
+        // store: full lines, not 32-byte pieces
+        bf16_t* Ys = Zs + wid * (L / 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 4 * gq + r;
-            if (row < nrows) {
-              const int64_t orow = OS ? int64_t(os_lst[row]) : int64_t(tl.row_start) + row;
-              g.Y[orow * g.ldy + wid * (L / 4) + 16 * j + n16] = f32_to_bf16(acc[j][r]);
-            }
+          for (int r = 0; r < 4; ++r) Ys[(4 * gq + r) * ZS + 16 * j + n16] = f32_to_bf16(acc[j][r]);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();  // (the wave reads back only its own columns)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int row = 8 * q + (lane >> 3);
+          if (row < nrows) {
+            const int64_t orow = OS ? int64_t(os_lst[row]) : int64_t(tl.row_start) + row;
+            *reinterpret_cast<uint4*>(g.Y + orow * g.ldy + wid * (L / 4) + 8 * (lane & 7)) =
+                *reinterpret_cast<const uint4*>(&Ys[row * ZS + 8 * (lane & 7)]);
           }
+        }
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -589,6 +598,8 @@ hipError_t launch_grouped_w4a16(const GroupedW4& g, hipStream_t s, hipEvent_t t0
 
 hipError_t launch_w4a16_mlp(const W4Mlp& g, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   if (g.max_tiles <= 0) return hipSuccess;
+  // Y rows go out as 16-byte stores
+  if (g.ldy % 8 || reinterpret_cast<uintptr_t>(g.Y) % 16) return hipErrorInvalidValue;
   return launch_kernel((const void*)skinny_w4a16_mlp_kernel<false>, dim3{uint32_t(g.max_tiles)}, dim3{256}, 0, s, g,
                        t0, t1);
 }
@@ -596,6 +607,7 @@ hipError_t launch_w4a16_mlp(const W4Mlp& g, hipStream_t s, hipEvent_t t0, hipEve
 hipError_t launch_w4a16_mlp_os(const W4Mlp& g, int E, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   if (g.os_R <= 0 || E <= 0) return hipSuccess;
   if (g.os_R > kOsMaxRows || !g.os_ids) return hipErrorInvalidValue;
+  if (g.ldy % 8 || reinterpret_cast<uintptr_t>(g.Y) % 16) return hipErrorInvalidValue;
   return launch_kernel((const void*)skinny_w4a16_mlp_kernel<true>, dim3{uint32_t(E)}, dim3{256}, 0, s, g, t0, t1);
 }
 
