@@ -1500,7 +1500,10 @@ __global__ __launch_bounds__(512, 1) void w4ring_grouped_kernel(GroupedGemm g) {
     g2lds16_so(abase, oa[q], rfl(lds0 + kW4AOff + slot * kW4A + (wid + NW * q) * 1024));
   };
   auto next_a = [&]() __attribute__((always_inline)) { abase += 128; };
-  const bool b_once = tl.solo != 0;  // the expert's only tile: its codes are read once (nontemporal)
+  // the weight codes with the nontemporal hint: FC2's always (816-824 ->
+  // 805-807 us at the 16k-token w4a16 shape, traced alternately), FC1's for
+  // an expert's only tile (read once)
+  const bool b_once = !GATED || tl.solo != 0;
   auto issue_g = [&](int slot, int q) __attribute__((always_inline)) {
     const uint32_t lb = rfl(lds0 + kW4BOff + slot * kW4B + (wid + NW * q) * 1024);
     if (b_once) g2lds16_so<true>(q < LB / 2 ? gbase : ubase, ob[q], lb);
