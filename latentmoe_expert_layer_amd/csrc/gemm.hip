@@ -1388,9 +1388,9 @@ __global__ __launch_bounds__(512, 1) void ring64_grouped_kernel(GroupedGemm g) {
 #pragma unroll
     for (int i = 0; i < LB; ++i) pb[i] += BK;
   };
-  // FC1 (gated) only: FC2 was a little slower with it.  (The hint is an
-  // instruction bit: one copy of the tile's code for each form.)
-  if (GATED && tl.solo)
+  // (The hint is an instruction bit: one copy of the tile's code for each
+  // form.)
+  if (tl.solo)
     ring64_tile<GATED, BM, GATED, true>(lds, lds0, wid, lane, tid, g.K / BK, nrows, pa, pb, next_a, next_b, g.C, g.ldc,
                                         row0, n0, g.N);
   else
