@@ -323,6 +323,7 @@ lmoe::DenseGemm down_proj_gemm(const FwdCtx& c) {
   g.gated = false;
   g.C = reinterpret_cast<uint16_t*>(ws + c.L.z);
   g.ldc = a->l;
+  g.stream_c = true;
   if (c.mx && !c.small && lmoe::dense_gemm_quant_fits(g)) {
     g.Cq = reinterpret_cast<uint8_t*>(ws + c.L.zq);
     g.Cqs = reinterpret_cast<uint8_t*>(ws + c.L.zs);
@@ -365,6 +366,7 @@ int fwd_front(const FwdCtx& c, const lmoe_route_args* route = nullptr) {
     g[1].gated = true;
     g[1].C = hs;
     g[1].ldc = S * Is;
+    g[1].stream_c = true;
     if (small && route) {
       // one launch for both GEMMs and the router's top-k, which does not
       // depend on them
@@ -691,6 +693,7 @@ int fwd_back(const FwdCtx& c) {
   u.gated = false;
   u.C = static_cast<uint16_t*>(a->y);
   u.ldc = d;
+  u.stream_c = true;
   e = small ? lmoe::launch_small_dense(&u, 1, s) : lmoe::launch_dense_gemm(u, s);
   if (e != hipSuccess) return hip_fail(e, "up-proj");
   if ((e = mark(6)) != hipSuccess) return hip_fail(e, "event");

@@ -1241,7 +1241,7 @@ __device__ __forceinline__ void ring64_tile(char* lds, uint32_t lds0, int wid, i
 // blocks below nt - nsplit take whole tiles in the XCD-aware order, the
 // 2 nsplit blocks after them the halves (a half tile loads 3/4 of a whole
 // one's operands for 1/2 of its MFMAs).
-template <bool GATED>
+template <bool GATED, bool NT>
 __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g, int nsplit) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BR = 256, NOUT = GATED ? 128 : 256, NW = 8, LB = 4, BK = kR64BK;
@@ -1330,7 +1330,7 @@ __global__ __launch_bounds__(512, 1) void ring64_dense_kernel(DenseGemm g, int n
         }
       }
     };
-    ring64_tile<GATED, BM, false, false>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0,
+    ring64_tile<GATED, BM, NT, false>(lds, lds0, wid, lane, tid, nk, nrows, pa, pb, next_a, next_b, g.C, g.ldc, row0,
                                          n0, g.N, g.Cq, g.Cqs);
   };
   if (half >= 0) tile(std::integral_constant<int, 128>{});
@@ -1696,7 +1696,7 @@ bool dense_gemm_quant_fits_impl(const DenseGemm& d) {
 template <bool GATED>
 hipError_t run_ring64(const DenseGemm& d, hipStream_t s) {
   constexpr int NOUT = GATED ? 128 : 256;
-  auto kern = ring64_dense_kernel<GATED>;
+  auto kern = d.stream_c ? ring64_dense_kernel<GATED, true> : ring64_dense_kernel<GATED, false>;
   if (hipError_t e = allow_dynamic_lds((const void*)kern, kR64Lds); e != hipSuccess) return e;
   const int64_t nt = int64_t((d.M + 255) / 256) * ((d.N + NOUT - 1) / NOUT);
   if (nt <= 0) return hipSuccess;

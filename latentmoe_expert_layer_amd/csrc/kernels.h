@@ -81,6 +81,12 @@ struct DenseGemm {
   // 32-column block quantised from the bf16 values written to C
   uint8_t* Cq = nullptr;
   uint8_t* Cqs = nullptr;
+  // C written with the nontemporal hint (the 64-wide ring form).  The layer
+  // sets it on its dense projections: they are MFMA-bound, and output lines
+  // left dirty in the caches would be written back during the bandwidth-bound
+  // grouped FC1 that follows (its prefill time 728 -> 699 us; the dense
+  // launches +5 us in all, traced alternately)
+  bool stream_c = false;
 };
 hipError_t launch_dense_gemm(const DenseGemm& g, hipStream_t s);
 // compute units of the current device (cached per device; 256 if unknown)
